@@ -1,0 +1,190 @@
+// C ABI of the KDA forward: argument checks, workspace carve-up, launches.
+// Declarations and the contract of every entry point are in include/kda.h.
+#include "../../include/kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "kda_launch.h"
+
+namespace {
+
+constexpr int64_t kChunkTokens = 64;
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct Carve {
+  size_t info, table, seq_off, seq_order, rec, total;
+};
+
+bool sizes_ok(const kda_problem_t* p, bool packed, int64_t* N, int64_t* n_chunk_ub) {
+  if (!p) return false;
+  if (p->batch < 1 || p->seqlen < 0 || p->heads < 1 || p->num_seqs < 0) return false;
+  if (packed) {
+    if (p->batch != 1 || p->num_seqs < 1) return false;
+    *N = p->num_seqs;
+    *n_chunk_ub = (p->seqlen + kChunkTokens - 1) / kChunkTokens + p->num_seqs;
+  } else {
+    if (p->num_seqs != 0 && p->num_seqs != p->batch) return false;
+    *N = p->batch;
+    *n_chunk_ub = p->batch * ((p->seqlen + kChunkTokens - 1) / kChunkTokens);
+  }
+  // grid limits: chunks and scan workgroups must fit the launch dimensions
+  if (*n_chunk_ub > 0x7fffffffLL || *N * (int64_t)p->heads * 8 > 0x7fffffffLL) return false;
+  // int32 token offsets inside the packed table; 64-bit element offsets elsewhere
+  if (packed && p->seqlen > 0x7fffffffLL) return false;
+  return true;
+}
+
+bool dims_supported(const kda_problem_t* p) {
+  return (p->dk == 64 || p->dk == 128) && (p->dv == 64 || p->dv == 128) &&
+         (p->dtype == KDA_BF16 || p->dtype == KDA_F32);
+}
+
+Carve carve(const kda_problem_t* p, int64_t N, int64_t n_chunk_ub) {
+  Carve c;
+  c.info = 0;
+  c.table = c.info + 256;
+  c.seq_off = c.table + align256((size_t)n_chunk_ub * 16);
+  c.seq_order = c.seq_off + align256((size_t)(N + 1) * 4);
+  c.rec = c.seq_order + align256((size_t)N * 4);
+  c.total = c.rec + (size_t)n_chunk_ub * (size_t)p->heads * kda::record_bytes(p->dk, p->dv);
+  return c;
+}
+
+bool misaligned(const void* ptr) { return ptr && (reinterpret_cast<uintptr_t>(ptr) & 15u); }
+
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+  if (!a || !b || an == 0 || bn == 0) return false;
+  uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+int slice_width(const kda_problem_t* p, int64_t N) {
+  const char* env = std::getenv("KDA_SCAN_SLICE");
+  if (env) {
+    int v = std::atoi(env);
+    if ((v == 16 || v == 32 || v == 64) && v <= p->dv) return v;
+  }
+  (void)N;
+  return 32;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_version(void) { return 100; }
+
+const char* kda_status_string(kda_status_t s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: dk/dv must be 64 or 128, dtype bf16 or fp32";
+    case KDA_ERR_BAD_ARG: return "KDA_ERR_BAD_ARG: inconsistent sizes, non-finite scale or bad cu_seqlens";
+    case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: tensor pointers must be 16-byte aligned";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace smaller than kda_fwd_workspace_size()";
+    case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: out or ht overlaps an input";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP launch failed";
+  }
+  return "unknown kda_status_t";
+}
+
+size_t kda_fwd_workspace_size(const kda_problem_t* prob) {
+  if (!prob || !dims_supported(prob)) return 0;
+  int64_t N = 0, ub = 0;
+  // the workspace depends only on sizes; packed mode is the one with num_seqs >= 1 and batch == 1
+  // when the caller passes cu_seqlens, so size for the larger of the two readings
+  bool fixed_ok = sizes_ok(prob, false, &N, &ub);
+  size_t best = 0;
+  if (fixed_ok) best = carve(prob, N, ub).total;
+  int64_t N2 = 0, ub2 = 0;
+  if (sizes_ok(prob, true, &N2, &ub2)) {
+    size_t t2 = carve(prob, N2, ub2).total;
+    if (t2 > best) best = t2;
+  }
+  return best;
+}
+
+kda_status_t kda_fwd_validate(const kda_problem_t* prob, const void* q, const void* k, const void* v,
+                              const float* g, const void* beta, const float* h0,
+                              const int32_t* cu_seqlens, float scale, const void* out, const float* ht,
+                              const void* workspace, size_t workspace_bytes) {
+  if (!prob) return KDA_ERR_NULL;
+  if (!dims_supported(prob)) return KDA_ERR_UNSUPPORTED;
+  const bool packed = cu_seqlens != nullptr;
+  int64_t N = 0, ub = 0;
+  if (!sizes_ok(prob, packed, &N, &ub)) return KDA_ERR_BAD_ARG;
+  if (!std::isfinite(scale)) return KDA_ERR_BAD_ARG;
+  const int64_t toks = prob->batch * prob->seqlen;
+  if (toks > 0 && (!q || !k || !v || !g || !beta || !out)) return KDA_ERR_NULL;
+  if (!workspace) return KDA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(beta) ||
+      misaligned(h0) || misaligned(out) || misaligned(ht) || misaligned(workspace))
+    return KDA_ERR_ALIGN;
+  if (workspace_bytes < carve(prob, N, ub).total) return KDA_ERR_WORKSPACE;
+  const size_t es = prob->dtype == KDA_BF16 ? 2 : 4;
+  const size_t nqk = (size_t)toks * prob->heads * prob->dk;
+  const size_t nv = (size_t)toks * prob->heads * prob->dv;
+  const size_t nst = (size_t)N * prob->heads * prob->dk * prob->dv * 4;
+  struct In { const void* p; size_t n; } ins[] = {
+      {q, nqk * es}, {k, nqk * es}, {v, nv * es}, {g, nqk * 4}, {beta, (size_t)toks * prob->heads * es},
+      {h0, h0 ? nst : 0}, {cu_seqlens, packed ? (size_t)(N + 1) * 4 : 0}, {workspace, workspace_bytes}};
+  for (const In& in : ins) {
+    if (overlap(out, nv * es, in.p, in.n)) return KDA_ERR_ALIAS;
+    if (ht && in.p != h0 && overlap(ht, nst, in.p, in.n)) return KDA_ERR_ALIAS;
+  }
+  if (ht && h0 && ht != h0 && overlap(ht, nst, h0, nst)) return KDA_ERR_ALIAS;
+  if (ht && overlap(ht, nst, out, nv * es)) return KDA_ERR_ALIAS;
+  const char* env = std::getenv("KDA_VALIDATE_CU_SEQLENS");
+  if (packed && env && env[0] == '1') {
+    std::vector<int32_t> host((size_t)N + 1);
+    if (hipMemcpy(host.data(), cu_seqlens, host.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+      return KDA_ERR_HIP;
+    if (host[0] != 0 || host[N] != prob->seqlen) return KDA_ERR_BAD_ARG;
+    for (int64_t i = 0; i < N; ++i)
+      if (host[i + 1] < host[i]) return KDA_ERR_BAD_ARG;
+  }
+  return KDA_OK;
+}
+
+kda_status_t kda_fwd(const kda_problem_t* prob, const void* q, const void* k, const void* v, const float* g,
+                     const void* beta, const float* h0, const int32_t* cu_seqlens, float scale, void* out,
+                     float* ht, void* workspace, size_t workspace_bytes, void* stream) {
+  kda_status_t st = kda_fwd_validate(prob, q, k, v, g, beta, h0, cu_seqlens, scale, out, ht, workspace,
+                                     workspace_bytes);
+  if (st != KDA_OK) return st;
+  const bool packed = cu_seqlens != nullptr;
+  int64_t N = 0, ub = 0;
+  sizes_ok(prob, packed, &N, &ub);
+  Carve c = carve(prob, N, ub);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  kda::ForwardPlan p;
+  p.B = prob->batch;
+  p.T = prob->seqlen;
+  p.N = N;
+  p.T_total = prob->batch * prob->seqlen;
+  p.n_chunk_ub = ub;
+  p.H = prob->heads;
+  p.dk = prob->dk;
+  p.dv = prob->dv;
+  p.dtype = prob->dtype;
+  p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.cu = cu_seqlens;
+  p.scale = scale;
+  p.out = out;
+  p.ht = ht;
+  p.info = reinterpret_cast<int32_t*>(ws + c.info);
+  p.table = ws + c.table;
+  p.seq_off = reinterpret_cast<int32_t*>(ws + c.seq_off);
+  p.seq_order = reinterpret_cast<int32_t*>(ws + c.seq_order);
+  p.rec = ws + c.rec;
+  p.slice = slice_width(prob, N);
+  hipError_t e = kda::launch_forward(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+// Device-side building blocks shared by the KDA forward kernels (gfx950).
+//
+// Fragment conventions (v_mfma_f32_16x16x32_f16, one wave of 64 lanes, lane l):
+//   A operand (16 x 32):  lane l holds A[l % 16][8 * (l / 16) + 0..7]
+//   B operand (32 x 16):  lane l holds B[8 * (l / 16) + 0..7][l % 16]
+//   C/D       (16 x 16):  lane l holds C[4 * (l / 16) + 0..3][l % 16]
+// A 32-wide contraction step is free to use any order of its 32 indices as
+// long as both operands agree.  The kernels use the order pi below, under
+// which the C fragments of two stacked 16-row tiles are, lane for lane and
+// without any data movement, the operand fragment of the next contraction:
+//   slot 8*gq + e  (gq = l/16, e = 0..7)  <->  index 16*(e/4) + 4*gq + (e%4)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunk = 64;      // tokens per chunk
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Index (within a 32-wide step) that slot e of lane-quarter gq stands for.
+__device__ __host__ constexpr int pi_index(int gq, int e) { return 16 * (e >> 2) + 4 * gq + (e & 3); }
+
+__device__ inline f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// 2^x on the hardware exp unit (x <= 0 everywhere it is used: results in [0, 1]).
+__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Shift a value D lanes up inside each row of 16 lanes; lanes with no source get 0.
+template <int D>
+__device__ inline float row_shr(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + D, 0xF, 0xF, true));
+}
+
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (NaN stays NaN).
+__device__ inline uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Load four consecutive elements (bf16 or fp32) as fp32.
+__device__ inline void load4(const uint16_t* p, float* o) {
+  uint2 r = *reinterpret_cast<const uint2*>(p);
+  o[0] = __uint_as_float(r.x << 16);
+  o[1] = __uint_as_float(r.x & 0xffff0000u);
+  o[2] = __uint_as_float(r.y << 16);
+  o[3] = __uint_as_float(r.y & 0xffff0000u);
+}
+__device__ inline void load4(const float* p, float* o) {
+  float4 r = *reinterpret_cast<const float4*>(p);
+  o[0] = r.x; o[1] = r.y; o[2] = r.z; o[3] = r.w;
+}
+__device__ inline float load1(const uint16_t* p) { return bf16_to_f32(*p); }
+__device__ inline float load1(const float* p) { return *p; }
+
+// Store four consecutive elements from fp32 (bf16 rounds to nearest even).
+__device__ inline void store4(uint16_t* p, const float* x) {
+  uint2 r;
+  r.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+  r.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+  *reinterpret_cast<uint2*>(p) = r;
+}
+__device__ inline void store4(float* p, const float* x) {
+  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+
+__device__ inline float wave_max(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+// Per 64-token chunk and head, the chunk factors handed from the chunk kernel
+// to the state-scan kernel.  Every fragment block is stored lane-major so a
+// wave moves it with one 16-byte (or 8-byte) access per lane.
+template <int DK, int DV>
+struct Rec {
+  static constexpr int KSK = DK / 32;  // contraction steps over key channels
+  static constexpr int NTK = DK / 16;  // 16-row tiles of key channels
+  static constexpr int NTV = DV / 16;  // 16-column tiles of value channels
+  // W: A fragments of W [64 x DK], [row block 4][KSK][lane 64] x f16x8 (channels in pi order)
+  static constexpr size_t W = 0;
+  // Q: A fragments of qhat * exp(G), same layout as W
+  static constexpr size_t Q = W + 64 * DK * 2;
+  // KT: A fragments of (khat * exp(G_last - G))^T [DK x 64], [NTK][2][lane] x f16x8 (tokens in pi order)
+  static constexpr size_t KT = Q + 64 * DK * 2;
+  // A: A fragments of the masked intra-chunk attention [64 x 64], [row block 4][2][lane] x f16x8
+  static constexpr size_t A = KT + 64 * DK * 2;
+  // U: C-layout tiles of U * 2^ue [64 x DV], [row block 4][NTV][lane] x f16x4
+  static constexpr size_t U = A + 64 * 64 * 2;
+  // LAM: exp(G_last) per key channel, fp32 [DK]
+  static constexpr size_t LAM = U + 64 * DV * 2;
+  // HDR: { float vmax (max |v| over the chunk), int ue (U scale exponent), pad, pad }
+  static constexpr size_t HDR = LAM + DK * 4;
+  static constexpr size_t BYTES = (HDR + 16 + 255) / 256 * 256;
+};
+
+// One entry of the chunk table.
+struct ChunkEntry {
+  int32_t seq;   // sequence index
+  int32_t len;   // valid tokens in this chunk (1..64)
+  int32_t idx;   // chunk index inside its sequence
+  int32_t pad;
+};
+
+// Token offset of sequence n (packed: cu[n]; fixed-length: n * T).
+__device__ inline int64_t seq_start(const int32_t* cu, int64_t T, int64_t n) {
+  return cu ? (int64_t)cu[n] : n * T;
+}
+__device__ inline int64_t seq_len(const int32_t* cu, int64_t T, int64_t n) {
+  if (!cu) return T;
+  int64_t L = (int64_t)cu[n + 1] - (int64_t)cu[n];
+  return L > 0 ? L : 0;
+}
+
+}  // namespace kda

@@ -1,0 +1,77 @@
+// Kernel instantiations and launch sequence of the KDA forward (gfx950).
+#include "kda_launch.h"
+#include "kda_chunkmap.h"
+#include "kda_prep.h"
+#include "kda_scan.h"
+
+namespace kda {
+
+size_t record_bytes(int dk, int dv) {
+  if (dk == 64 && dv == 64) return Rec<64, 64>::BYTES;
+  if (dk == 64 && dv == 128) return Rec<64, 128>::BYTES;
+  if (dk == 128 && dv == 64) return Rec<128, 64>::BYTES;
+  if (dk == 128 && dv == 128) return Rec<128, 128>::BYTES;
+  return 0;
+}
+
+template <int DK, int DV, typename InT>
+static hipError_t launch_prep(const ForwardPlan& p, hipStream_t stream) {
+  PrepArgs a;
+  a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.beta = p.beta; a.cu = p.cu;
+  a.T = p.T; a.T_total = p.T_total; a.H = p.H;
+  a.info = p.info;
+  a.table = reinterpret_cast<const ChunkEntry*>(p.table);
+  a.rec = p.rec;
+  const size_t smem = PrepSmem<DK, DV>::BYTES;
+  auto kern = chunk_prep_kernel<DK, DV, InT>;
+  hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  dim3 grid((unsigned)p.n_chunk_ub, (unsigned)p.H);
+  hipLaunchKernelGGL(kern, grid, dim3(256), smem, stream, a);
+  return hipGetLastError();
+}
+
+template <int DK, int DV, int NV, typename OutT>
+static hipError_t launch_scan_nv(const ForwardPlan& p, hipStream_t stream) {
+  ScanArgs a;
+  a.h0 = p.h0; a.ht = p.ht; a.out = p.out; a.cu = p.cu;
+  a.T = p.T; a.T_total = p.T_total; a.N = p.N; a.H = p.H; a.n_chunk_ub = p.n_chunk_ub;
+  a.seq_off = p.seq_off; a.seq_order = p.seq_order; a.rec = p.rec; a.scale = p.scale;
+  const size_t smem = ScanSmem<DK, DV, NV>::BYTES;
+  auto kern = state_scan_kernel<DK, DV, NV, OutT>;
+  const int64_t blocks = p.N * (int64_t)p.H * (DV / NV);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), smem, stream, a);
+  return hipGetLastError();
+}
+
+template <int DK, int DV, typename OutT>
+static hipError_t launch_scan(const ForwardPlan& p, hipStream_t stream) {
+  switch (p.slice) {
+    case 16: return launch_scan_nv<DK, DV, 16, OutT>(p, stream);
+    case 64: return launch_scan_nv<DK, DV, 64, OutT>(p, stream);
+    default: return launch_scan_nv<DK, DV, 32, OutT>(p, stream);
+  }
+}
+
+template <int DK, int DV>
+static hipError_t launch_dkdv(const ForwardPlan& p, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  if (p.T_total > 0) {
+    e = (p.dtype == 0) ? launch_prep<DK, DV, uint16_t>(p, stream) : launch_prep<DK, DV, float>(p, stream);
+    if (e != hipSuccess) return e;
+  }
+  return (p.dtype == 0) ? launch_scan<DK, DV, uint16_t>(p, stream) : launch_scan<DK, DV, float>(p, stream);
+}
+
+hipError_t launch_forward(const ForwardPlan& p, hipStream_t stream) {
+  if (p.N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kMapThreads), 0, stream, p.cu, p.T, p.N, p.n_chunk_ub,
+                     p.info, reinterpret_cast<ChunkEntry*>(p.table), p.seq_off, p.seq_order);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.dk == 64 && p.dv == 64) return launch_dkdv<64, 64>(p, stream);
+  if (p.dk == 64 && p.dv == 128) return launch_dkdv<64, 128>(p, stream);
+  if (p.dk == 128 && p.dv == 64) return launch_dkdv<128, 64>(p, stream);
+  return launch_dkdv<128, 128>(p, stream);
+}
+
+}  // namespace kda

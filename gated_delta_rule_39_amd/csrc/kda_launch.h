@@ -1,0 +1,40 @@
+// Host-side launch interface between the C ABI (kda_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct ForwardPlan {
+  // sizes
+  int64_t B, T, N, T_total, n_chunk_ub;
+  int32_t H, dk, dv, dtype;  // dtype: 0 = bf16, 1 = fp32
+  // tensors
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const void* beta;
+  const float* h0;
+  const int32_t* cu;
+  float scale;
+  void* out;
+  float* ht;
+  // workspace carve-up
+  int32_t* info;
+  void* table;
+  int32_t* seq_off;
+  int32_t* seq_order;
+  uint8_t* rec;
+  int32_t slice;  // value columns per scan workgroup (16, 32 or 64)
+};
+
+// Bytes of one per-(chunk, head) record.
+size_t record_bytes(int dk, int dv);
+
+// Enqueue chunk map, chunk kernel and state scan on `stream`.
+hipError_t launch_forward(const ForwardPlan& p, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,286 @@
+// State-scan kernel: the sequential walk over a sequence's chunks, one
+// workgroup per (sequence, head, slice of NV value columns).
+//
+// The value columns of the state evolve independently (the recurrence only
+// mixes key channels), so a head's state is split into DV/NV column slices
+// that walk their chunks in parallel ("Autoresearch on Kimi Delta
+// Attention", section "The optimization trace": the recurrence split across
+// value tiles to expose more independent work).  The state is carried in fp32
+// registers for the whole walk; "Kernel Design Agents (KDA) optimize Kimi
+// Delta Attention (KDA)", section "01 - Results", shows that a bf16 state
+// compounds error along the sequence.  Per chunk (S0 = state at the chunk
+// start, all products on fp16 MFMA with fp32 accumulation):
+//     Delta  = U - W S0                                   (the corrected values)
+//     o      = scale (Qhat*exp(G) S0 + Aqk Delta)         (chunk output, fused here)
+//     S_next = Diag(exp(G_last)) S0 + (Khat*exp(G_last-G))^T Delta
+// Boundaries come from the chunk table (built from cu_seqlens on the device);
+// the walk never drops history.
+//
+// fp16 range: the state is linear in (v, h0).  For beta in [0, 1], g <= 0 and
+// unit keys, every column s of the state obeys ||s_t||^2 <= ||s_{t-1}||^2 + v_t^2,
+// hence ||s_t|| <= B = sqrt(max_col ||h0_col||^2 + L vmax^2) over a sequence of
+// length L, and |Delta| <= vmax + B.  The fp16 copies of S and Delta are taken
+// after an exact power-of-two scale 2^es with 2^es B <= 2^14, so they stay
+// below the fp16 maximum for every legal input; the fp32 state is unscaled.
+#pragma once
+
+#include "kda_device.h"
+
+namespace kda {
+
+struct ScanArgs {
+  const float* h0;
+  float* ht;
+  void* out;
+  const int32_t* cu;
+  int64_t T;
+  int64_t T_total;
+  int64_t N;
+  int32_t H;
+  int64_t n_chunk_ub;
+  const int32_t* seq_off;
+  const int32_t* seq_order;
+  const uint8_t* rec;
+  float scale;
+};
+
+template <int DK, int DV, int NV>
+struct ScanSmem {
+  static constexpr int KSK = DK / 32;
+  static constexpr int NT = NV / 16;
+  static constexpr size_t SB = 0;                              // S fragments [KSK][NT][64] f16x8
+  static constexpr size_t DB = SB + (size_t)KSK * NT * 64 * 16;  // Delta fragments [2][NT][64] f16x8
+  static constexpr size_t CN = DB + (size_t)2 * NT * 64 * 16;    // column norms [4][NV]
+  static constexpr size_t RED = CN + 4 * NV * 4;                 // [8]
+  static constexpr size_t BYTES = RED + 8 * 4;
+};
+
+template <int DK, int DV, int NV>
+struct ChunkRegs {
+  static constexpr int KSK = DK / 32;
+  static constexpr int TPW = DK / 64;  // 16-row state tiles owned by each wave
+  static constexpr int NT = NV / 16;
+  f16x8 wf[KSK];
+  f16x8 qf[KSK];
+  f16x8 af[2];
+  f16x8 kt[TPW][2];
+  f16x4 uf[NT];
+  float4 lam[TPW];
+  int ue;
+};
+
+template <int DK, int DV, int NV>
+__device__ inline void load_chunk(ChunkRegs<DK, DV, NV>& c, const uint8_t* rec, int w, int l, int slice) {
+  using R = Rec<DK, DV>;
+  using CR = ChunkRegs<DK, DV, NV>;
+  const int t = l & 15, gq = l >> 4;
+#pragma unroll
+  for (int s = 0; s < CR::KSK; ++s) {
+    c.wf[s] = *reinterpret_cast<const f16x8*>(rec + R::W + ((size_t)(w * CR::KSK + s) * 64 + l) * 16);
+    c.qf[s] = *reinterpret_cast<const f16x8*>(rec + R::Q + ((size_t)(w * CR::KSK + s) * 64 + l) * 16);
+  }
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+    c.af[s2] = *reinterpret_cast<const f16x8*>(rec + R::A + ((size_t)(w * 2 + s2) * 64 + l) * 16);
+#pragma unroll
+  for (int m = 0; m < CR::TPW; ++m) {
+    const int ct = CR::TPW * w + m;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+      c.kt[m][s2] = *reinterpret_cast<const f16x8*>(rec + R::KT + ((size_t)(ct * 2 + s2) * 64 + l) * 16);
+    c.lam[m] = *reinterpret_cast<const float4*>(rec + R::LAM + (size_t)(16 * ct + 4 * gq) * 4);
+  }
+#pragma unroll
+  for (int nt = 0; nt < CR::NT; ++nt)
+    c.uf[nt] = *reinterpret_cast<const f16x4*>(
+        rec + R::U + ((size_t)(w * R::NTV + slice * CR::NT + nt) * 64 + l) * 8);
+  c.ue = reinterpret_cast<const int32_t*>(rec + R::HDR)[1];
+  (void)t;
+}
+
+template <int DK, int DV, int NV, typename OutT>
+__global__ __launch_bounds__(256) void state_scan_kernel(ScanArgs a) {
+  using R = Rec<DK, DV>;
+  using SM = ScanSmem<DK, DV, NV>;
+  using CR = ChunkRegs<DK, DV, NV>;
+  constexpr int KSK = DK / 32;
+  constexpr int TPW = DK / 64;
+  constexpr int NT = NV / 16;
+  constexpr int NS = DV / NV;
+
+  extern __shared__ __align__(16) uint8_t smem[];
+  f16x8* sb = reinterpret_cast<f16x8*>(smem + SM::SB);
+  uint8_t* db = smem + SM::DB;
+  float* cn = reinterpret_cast<float*>(smem + SM::CN);
+  float* red = reinterpret_cast<float*>(smem + SM::RED);
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, t = l & 15, gq = l >> 4;
+  const int64_t bid = blockIdx.x;
+  const int slice = (int)(bid % NS);
+  const int64_t rest = bid / NS;
+  const int h = (int)(rest % a.H);
+  const int64_t n = a.seq_order[rest / a.H];
+  int64_t c0 = a.seq_off[n], c1 = a.seq_off[n + 1];
+  if (c1 > a.n_chunk_ub) c1 = a.n_chunk_ub;  // only on invalid cu_seqlens
+  if (c0 > c1) c0 = c1;
+  const int64_t L = seq_len(a.cu, a.T, n);
+  const int64_t s0 = seq_start(a.cu, a.T, n);
+  const int col0 = slice * NV;
+
+  // initial state (fp32, C layout: lane holds rows 16*tile + 4gq + r of column col0 + 16nt + t)
+  float S[TPW][NT][4];
+  const size_t sbase = ((size_t)n * a.H + h) * DK * DV;
+#pragma unroll
+  for (int m = 0; m < TPW; ++m)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * (TPW * w + m) + 4 * gq + r;
+        S[m][nt][r] = a.h0 ? a.h0[sbase + (size_t)row * DV + col0 + 16 * nt + t] : 0.f;
+      }
+
+  // power-of-two scale of the fp16 copies from the bound B (see the file comment)
+  float vm = 0.f;
+  for (int64_t c = c0 + tid; c < c1; c += 256)
+    vm = fmaxf(vm, reinterpret_cast<const float*>(a.rec + ((size_t)c * a.H + h) * R::BYTES + R::HDR)[0]);
+  vm = wave_max(vm);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float ss = 0.f;
+#pragma unroll
+    for (int m = 0; m < TPW; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ss = fmaf(S[m][nt][r], S[m][nt][r], ss);
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    if (gq == 0) cn[w * NV + 16 * nt + t] = ss;
+  }
+  if (l == 0) red[w] = vm;
+  __syncthreads();
+  float cmax = 0.f;
+  for (int j = 0; j < NV; ++j) cmax = fmaxf(cmax, cn[j] + cn[NV + j] + cn[2 * NV + j] + cn[3 * NV + j]);
+  const float vmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  int es = 0;
+  {
+    const double b2 = (double)cmax + (double)L * (double)vmax * (double)vmax;
+    if (b2 > 0.0 && b2 < 1e300) es = 14 - (ilogb(sqrt(b2)) + 1);
+    es = es < -250 ? -250 : (es > 250 ? 250 : es);
+  }
+
+  auto write_state = [&]() {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      if (TPW == 2) {
+        f16x8 f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          f[r] = (_Float16)ldexpf(S[0][nt][r], es);
+          f[4 + r] = (_Float16)ldexpf(S[TPW - 1][nt][r], es);
+        }
+        sb[(w * NT + nt) * 64 + l] = f;
+      } else {
+        f16x4 f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) f[r] = (_Float16)ldexpf(S[0][nt][r], es);
+        *reinterpret_cast<f16x4*>(reinterpret_cast<uint8_t*>(sb) +
+                                  (((size_t)(w >> 1) * NT + nt) * 64 + l) * 16 + (w & 1) * 8) = f;
+      }
+    }
+  };
+  write_state();
+  __syncthreads();
+
+  OutT* out = reinterpret_cast<OutT*>(a.out);
+  const float oscale = a.scale;
+  CR cur;
+  if (c0 < c1) load_chunk<DK, DV, NV>(cur, a.rec + ((size_t)c0 * a.H + h) * R::BYTES, w, l, slice);
+  for (int64_t c = c0; c < c1; ++c) {
+    CR nxt;
+    if (c + 1 < c1) load_chunk<DK, DV, NV>(nxt, a.rec + ((size_t)(c + 1) * a.H + h) * R::BYTES, w, l, slice);
+
+    // S0 fragments (B operand of W S0 and, read as A of S0^T, of the output)
+    f16x8 sf[KSK][NT];
+#pragma unroll
+    for (int s = 0; s < KSK; ++s)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sf[s][nt] = sb[(s * NT + nt) * 64 + l];
+
+    // Delta rows 16w..16w+15 (C layout: lane column = value column, rows = tokens 4gq + r)
+    f32x4 oacc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 d = zero4();
+#pragma unroll
+      for (int s = 0; s < KSK; ++s) d = mfma16(cur.wf[s], sf[s][nt], d);
+      f16x4 df;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) df[r] = (_Float16)(ldexpf((float)cur.uf[nt][r], es - cur.ue) - d[r]);
+      *reinterpret_cast<f16x4*>(db + (((size_t)(w >> 1) * NT + nt) * 64 + l) * 16 + (w & 1) * 8) = df;
+      // o^T, inter-chunk part: S0^T (Qhat exp(G))^T
+      f32x4 o = zero4();
+#pragma unroll
+      for (int s = 0; s < KSK; ++s) o = mfma16(sf[s][nt], cur.qf[s], o);
+      oacc[nt] = o;
+    }
+    __syncthreads();
+
+    f16x8 dfr[2][NT];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        dfr[s2][nt] = *reinterpret_cast<const f16x8*>(db + (((size_t)s2 * NT + nt) * 64 + l) * 16);
+
+    // state update on the wave's key-channel rows
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+      const float lam[4] = {cur.lam[m].x, cur.lam[m].y, cur.lam[m].z, cur.lam[m].w};
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        f32x4 u = zero4();
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) u = mfma16(cur.kt[m][s2], dfr[s2][nt], u);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[m][nt][r] = fmaf(lam[r], S[m][nt][r], ldexpf(u[r], -es));
+      }
+    }
+    write_state();
+
+    // o^T, intra-chunk part: Delta^T Aqk^T; then store 4 consecutive value columns per lane
+    const int64_t idx = c - c0;
+    const int64_t rem = L - idx * kChunk;
+    const int len = rem < kChunk ? (int)rem : kChunk;
+    const int i_loc = 16 * w + t;
+    const int64_t tok = s0 + idx * kChunk + i_loc;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 o = oacc[nt];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) o = mfma16(dfr[s2][nt], cur.af[s2], o);
+      if (i_loc < len && tok < a.T_total) {
+        float v4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v4[r] = ldexpf(o[r], -es) * oscale;
+        store4(out + ((size_t)tok * a.H + h) * DV + col0 + 16 * nt + 4 * gq, v4);
+      }
+    }
+    __syncthreads();
+    if (c + 1 < c1) cur = nxt;
+  }
+
+  if (a.ht) {
+#pragma unroll
+    for (int m = 0; m < TPW; ++m)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * (TPW * w + m) + 4 * gq + r;
+          a.ht[sbase + (size_t)row * DV + col0 + 16 * nt + t] = S[m][nt][r];
+        }
+  }
+}
+
+}  // namespace kda

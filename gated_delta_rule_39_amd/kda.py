@@ -1,0 +1,131 @@
+"""Python binding of the KDA forward C ABI (include/kda.h).
+
+Argument marshalling only: every step of the forward runs in the HIP library.
+PyTorch provides device memory and the current stream.  There is no other
+code path: if the library is missing, importing this module fails.
+"""
+import ctypes
+import os
+import re
+
+import torch  # loaded first so the library binds to the HIP runtime torch uses
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "kda.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libkda.so is not built: run __graft_entry__.build() (hipcc, gfx950) first")
+_lib = ctypes.CDLL(LIB_PATH)
+
+KDA_BF16, KDA_F32 = 0, 1
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_BAD_ARG",
+          4: "KDA_ERR_ALIGN", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_ALIAS", 7: "KDA_ERR_HIP"}
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("num_seqs", ctypes.c_int64),
+                ("heads", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_lib.kda_fwd_workspace_size.argtypes = [ctypes.POINTER(Problem)]
+_lib.kda_fwd_workspace_size.restype = ctypes.c_size_t
+_lib.kda_fwd_validate.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                  _P, _P, _P, ctypes.c_size_t]
+_lib.kda_fwd_validate.restype = ctypes.c_int
+_lib.kda_fwd.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
+                         ctypes.c_size_t, _P]
+_lib.kda_fwd.restype = ctypes.c_int
+_lib.kda_status_string.argtypes = [ctypes.c_int]
+_lib.kda_status_string.restype = ctypes.c_char_p
+_lib.kda_version.argtypes = []
+_lib.kda_version.restype = ctypes.c_int
+
+
+class KDAError(RuntimeError):
+    def __init__(self, code):
+        self.code = code
+        super().__init__(_lib.kda_status_string(code).decode())
+
+
+def declared_functions():
+    """Names of the functions include/kda.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(kda_\w+)\s*\(", text, re.M)))
+
+
+def library():
+    return _lib
+
+
+def version():
+    return _lib.kda_version()
+
+
+def make_problem(B, T, H, dk, dv, dtype, num_seqs=0):
+    return Problem(int(B), int(T), int(num_seqs), int(H), int(dk), int(dv), int(dtype))
+
+
+def workspace_size(B, T, H, dk, dv, dtype=KDA_BF16, num_seqs=0):
+    return int(_lib.kda_fwd_workspace_size(ctypes.byref(make_problem(B, T, H, dk, dv, dtype, num_seqs))))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return KDA_BF16
+    if dt == torch.float32:
+        return KDA_F32
+    raise TypeError("q, k, v and beta must be bfloat16 or float32, got %s" % dt)
+
+
+def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, *, out=None, ht=None, workspace=None,
+        output_final_state=True, stream=None):
+    """KDA forward.  Shapes: q, k, g [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H];
+    h0 [N, H, dk, dv] fp32 or None; cu_seqlens int32 [N + 1] (B must be 1) or None.
+    Returns (out [B, T, H, dv] in q's dtype, ht [N, H, dk, dv] fp32 or None)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q.dtype)
+    for name, t_ in (("k", k), ("v", v), ("beta", beta)):
+        if t_.dtype != q.dtype:
+            raise TypeError("%s must have q's dtype" % name)
+    if g.dtype != torch.float32:
+        raise TypeError("g must be float32")
+    tensors = [q, k, v, g, beta] + [x for x in (h0, cu_seqlens, out, ht, workspace) if x is not None]
+    for t_ in tensors:
+        if not t_.is_cuda or not t_.is_contiguous():
+            raise ValueError("all tensors must be contiguous device tensors")
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != (B, T, H):
+        raise ValueError("inconsistent shapes")
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if h0 is not None and (h0.dtype != torch.float32 or tuple(h0.shape) != (N, H, dk, dv)):
+        raise ValueError("h0 must be float32 [N, H, dk, dv]")
+    if scale is None:
+        scale = dk ** -0.5
+    prob = make_problem(B, T, H, dk, dv, code, N if cu_seqlens is not None else 0)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    if ht is None and output_final_state:
+        ht = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    wsb = int(_lib.kda_fwd_workspace_size(ctypes.byref(prob)))
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = _lib.kda_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                      _ptr(cu_seqlens), float(scale), _ptr(out), _ptr(ht), _ptr(workspace),
+                      workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KDAError(rc)
+    return out, ht

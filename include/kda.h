@@ -1,0 +1,138 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward.
+ *
+ * The operation.  Per head and per sequence, with a dk x dv state S:
+ *
+ *     S_t = (I - beta_t khat_t khat_t^T) Diag(exp(g_t)) S_{t-1} + beta_t khat_t v_t^T
+ *     o_t = scale * S_t^T qhat_t
+ *
+ * qhat = q/||q||_2 and khat = k/||k||_2 (a zero vector stays zero), g is a
+ * natural-log gate with one value per key channel (it scales the rows of S),
+ * beta is one scalar per (token, head), and o_t is read after token t's
+ * update.  "Autoresearch on Kimi Delta Attention", section "KDA in one
+ * minute", describes this memory in words (fixed-size state, read the
+ * prediction, write only the correction, per-channel forgetting) and points
+ * to the chunkwise form that turns most of the work into matrix products;
+ * "Kernel Design Agents (KDA) optimize Kimi Delta Attention (KDA)", sections
+ * "01 - Results" and "03 - Reward hacking", fix the interface this header
+ * serves: a forward pass over fixed-length and packed variable-length
+ * (cu_seqlens) batches, with an initial state in and the final state out,
+ * real Q/K L2 norms, boundaries read from cu_seqlens at run time, 64-token
+ * chunks, and a recurrent state that must not be kept in bf16.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are row-major and contiguous; every tensor pointer is 16-byte
+ *     aligned.  All tensor pointers are DEVICE pointers; `prob` is a host
+ *     pointer.  The library never allocates memory: the caller owns every
+ *     buffer, including the workspace.
+ *   - Errors are reported as kda_status_t; nothing is printed and nothing is
+ *     thrown.  A failed call enqueues no work.
+ *   - kda_fwd enqueues its kernels on `stream` and returns without waiting
+ *     for them.  It keeps no pointer after that work completes, holds no
+ *     global state and may be called from several host threads at once.
+ *   - Results are deterministic: the same inputs on the same GPU and build
+ *     give bitwise-equal out and ht.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dtype of q, k, v, beta and out (g, h0 and ht are always fp32). */
+typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype_t;
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,        /* a required pointer is NULL */
+  KDA_ERR_UNSUPPORTED = 2, /* dk/dv not in {64,128} or an unknown dtype */
+  KDA_ERR_BAD_ARG = 3,     /* negative or inconsistent sizes, non-finite scale, bad cu_seqlens */
+  KDA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
+  KDA_ERR_WORKSPACE = 5,   /* workspace smaller than kda_fwd_workspace_size() */
+  KDA_ERR_ALIAS = 6,       /* out or ht overlaps an input (ht == h0 exactly is allowed) */
+  KDA_ERR_HIP = 7          /* a HIP launch reported an error */
+} kda_status_t;
+
+/*
+ * Problem sizes.
+ *   Fixed-length mode (cu_seqlens == NULL): `batch` sequences of `seqlen`
+ *     tokens each; num_seqs must be 0 or equal to batch.
+ *   Packed mode (cu_seqlens != NULL): batch == 1, `seqlen` is the total
+ *     number of tokens and `num_seqs` >= 1 the number of packed sequences.
+ */
+typedef struct {
+  int64_t batch;    /* B */
+  int64_t seqlen;   /* T (per row; total tokens in packed mode) */
+  int64_t num_seqs; /* N */
+  int32_t heads;    /* H >= 1 */
+  int32_t dk;       /* key/query head size: 64 or 128 */
+  int32_t dv;       /* value head size: 64 or 128 */
+  int32_t dtype;    /* kda_dtype_t */
+} kda_problem_t;
+
+/*
+ * Bytes of device workspace kda_fwd needs for `prob` (0 on an invalid
+ * problem).  The workspace holds the chunk table and, per 64-token chunk and
+ * head, the chunk's factors (the WY factors W and U, the decayed queries and
+ * keys, the masked intra-chunk attention and the chunk decay).  Its contents
+ * are scratch: nothing in it needs initialising and nothing survives the call.
+ */
+size_t kda_fwd_workspace_size(const kda_problem_t* prob);
+
+/*
+ * Checks everything kda_fwd checks on the host, without touching the GPU:
+ * sizes, dtype, NULL pointers, alignment, workspace size and overlaps.  With
+ * the environment variable KDA_VALIDATE_CU_SEQLENS=1 it also copies
+ * cu_seqlens to the host (a synchronising copy) and checks cu[0] == 0,
+ * non-decreasing offsets and cu[N] == seqlen.  Arguments as for kda_fwd.
+ */
+kda_status_t kda_fwd_validate(const kda_problem_t* prob, const void* q, const void* k,
+                              const void* v, const float* g, const void* beta, const float* h0,
+                              const int32_t* cu_seqlens, float scale, const void* out,
+                              const float* ht, const void* workspace, size_t workspace_bytes);
+
+/*
+ * KDA forward pass.
+ *
+ *   q, k        [B, T, H, dk]  dtype        queries and keys (any finite magnitude;
+ *                                           normalised inside the kernels)
+ *   v           [B, T, H, dv]  dtype        values
+ *   g           [B, T, H, dk]  fp32         log-gate, finite and <= 0
+ *   beta        [B, T, H]      dtype        write strength in [0, 1]
+ *   h0          [N, H, dk, dv] fp32         initial state, or NULL for zeros
+ *   cu_seqlens  [N + 1]        int32        packed-sequence token offsets (device),
+ *                                           or NULL for fixed-length rows; cu[0] = 0,
+ *                                           non-decreasing, cu[N] = T; empty sequences
+ *                                           are allowed and return ht = h0
+ *   scale                      host float   output scale (1/sqrt(dk) is the usual value)
+ *   out         [B, T, H, dv]  dtype        output (written)
+ *   ht          [N, H, dk, dv] fp32         final state (written), or NULL; may be
+ *                                           exactly h0 for an in-place state update
+ *   workspace   workspace_bytes             device scratch, >= kda_fwd_workspace_size()
+ *   stream                                  hipStream_t to enqueue on (NULL = default)
+ *
+ * Inputs outside the stated domain (g > 0, beta outside [0, 1], non-finite
+ * values) get no accuracy guarantee but never make the kernels read or write
+ * out of bounds.  cu_seqlens is read on the device; its validity is the
+ * caller's precondition (see kda_fwd_validate).
+ */
+kda_status_t kda_fwd(const kda_problem_t* prob, const void* q, const void* k, const void* v,
+                     const float* g, const void* beta, const float* h0,
+                     const int32_t* cu_seqlens, float scale, void* out, float* ht,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* kda_status_string(kda_status_t status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,38 @@
+"""Helpers for GPU tests: move seeded inputs to the device, call the C ABI
+through the binding, and compare with the fp64 oracle."""
+import numpy as np
+
+TOL = 5e-3  # relative RMSE gate on outputs and on the final state
+
+
+def rel_rmse(x, ref):
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    nr = np.linalg.norm(ref)
+    return float(np.linalg.norm(x - ref) / nr) if nr > 0 else float(np.max(np.abs(x)))
+
+
+def to_device(x):
+    import torch
+    dev = torch.device("cuda:0")
+    io = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+    d = dict(q=t(x.q, io), k=t(x.k, io), v=t(x.v, io), g=t(x.g, torch.float32), beta=t(x.beta, io),
+             h0=None if x.h0 is None else t(x.h0, torch.float32),
+             cu_seqlens=None if x.cu_seqlens is None else t(x.cu_seqlens, torch.int32))
+    return d
+
+
+def run_gpu(x, d=None, **kw):
+    import torch
+    import gated_delta_rule_39_amd.kda as kda
+    if d is None:
+        d = to_device(x)
+    out, ht = kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu_seqlens"], x.scale, **kw)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), (None if ht is None else ht.cpu().numpy().astype(np.float64))
+
+
+def run_oracle(x):
+    from oracle import oracle_fwd
+    return oracle_fwd(x.q, x.k, x.v, x.g, x.beta, x.h0, x.cu_seqlens, x.scale)
