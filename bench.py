@@ -1,0 +1,319 @@
+"""Benchmark of the MI355X KDA forward (one GPU).
+
+A step is one kda_fwd over the 8,192-token fixed-length prefill
+(B=1, T=8192, H=32, dk=dv=128, bf16 q/k/v/beta, fp32 gates and state, h0 given),
+with its inputs resident in HBM before the timed region starts.  Prints ONE
+JSON line on stdout; everything else goes to stderr.
+
+The run fails closed: after timing, the output and final state of the timed
+inputs are checked against the fp64 oracle, and then new input contents are
+written into the same buffers and checked again; a failed check reports no
+speed.  The oracle run on the whole batch is also the CPU baseline.
+
+Per-kernel durations come from HIP events that kda_fwd_timed records between
+the library's kernels on the stream they run on.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published (no sparsity)
+TOL = 5e-3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work of one forward (per chunk-head / per token-head figures)
+# ---------------------------------------------------------------------------
+
+def record_bytes(dk, dv):
+    raw = 64 * dk * 2 * 3 + 64 * 64 * 2 + 64 * dv * 2 + dk * 4 + 16
+    return raw
+
+
+def algorithmic_work(x, n_chunks):
+    """Bytes and MFMA flops each kernel must move / do, counting every tensor once
+    (triangular products as triangles).  n_chunks = number of (sequence) chunks."""
+    B, T, H, dk, dv = x.shape
+    toks = B * T
+    N = x.num_seqs
+    es = 2 if x.dtype == "bf16" else 4
+    C = 64
+    ch = n_chunks * H
+    rec = record_bytes(dk, dv)
+    prep_bytes = toks * H * ((2 * dk + dv) * es + dk * 4 + es) + ch * rec
+    state_io = N * H * dk * dv * 4 * (1 + (x.h0 is not None))
+    scan_bytes = ch * (rec - 16) + toks * H * dv * es + state_io
+    tri_incl = C * (C + 1) // 2
+    tri_strict = C * (C - 1) // 2
+    prep_flops = ch * 2 * (tri_strict * dk + tri_incl * dk + tri_incl * dk + tri_incl * dv)
+    scan_flops = ch * 2 * (C * dk * dv * 3 + tri_incl * dv)
+    return dict(prep_bytes=prep_bytes, scan_bytes=scan_bytes, prep_flops=prep_flops, scan_flops=scan_flops)
+
+
+def n_chunks_of(x):
+    return sum((e - s + 63) // 64 for s, e in x.seq_bounds())
+
+
+# ---------------------------------------------------------------------------
+# HIP events through the runtime torch already loaded
+# ---------------------------------------------------------------------------
+
+def hip_runtime():
+    path = None
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64.so" in line:
+                path = line.split()[-1]
+                break
+    if path is None:
+        raise RuntimeError("libamdhip64 is not loaded")
+    hip = ctypes.CDLL(path)
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+def traffic_from_profiles(kernel):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except ValueError:
+        return None
+    if rec.get("source_sha256") != csrc_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def csrc_hash():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "gated_delta_rule_39_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=1, help="benchmark workload index (1 = fixed 8192)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-verify", action="store_true", help="skip parity (then no speed is reported)")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="run only a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: %d bytes read + %d bytes written per copy, 5 copies" % (n, n))
+        return
+
+    import gated_delta_rule_39_amd.kda as kda
+    from workloads import make_config
+
+    t0 = time.time()
+    x = make_config(args.workload)
+    log("workload %s (%s) generated in %.1fs" % (x.name, x.meta.get("description"), time.time() - t0))
+    B, T, H, dk, dv = x.shape
+    io = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+
+    def upload(y):
+        t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+        return dict(q=t(y.q, io), k=t(y.k, io), v=t(y.v, io), g=t(y.g, torch.float32), beta=t(y.beta, io),
+                    h0=None if y.h0 is None else t(y.h0, torch.float32),
+                    cu=None if y.cu_seqlens is None else t(y.cu_seqlens, torch.int32))
+
+    d = upload(x)
+    N = x.num_seqs
+    out = torch.empty((B, T, H, dv), dtype=io, device=dev)
+    ht = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    prob = kda.make_problem(B, T, H, dk, dv, kda.KDA_BF16 if io == torch.bfloat16 else kda.KDA_F32,
+                            N if d["cu"] is not None else 0)
+    lib = kda.library()
+    wsb = int(lib.kda_fwd_workspace_size(ctypes.byref(prob)))
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    P = lambda t_: None if t_ is None else ctypes.c_void_p(t_.data_ptr())
+    argv = [ctypes.byref(prob), P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["h0"]),
+            P(d["cu"]), ctypes.c_float(x.scale), P(out), P(ht), P(ws), ctypes.c_size_t(wsb),
+            ctypes.c_void_p(stream)]
+    lib.kda_fwd_timed.argtypes = list(lib.kda_fwd.argtypes) + [ctypes.c_void_p]
+    lib.kda_fwd_timed.restype = ctypes.c_int
+
+    hip = hip_runtime()
+    K, W = args.steps, args.warmup
+    marks = []
+    for _ in range(K):
+        row = (ctypes.c_void_p * 4)()
+        for j in range(4):
+            e = ctypes.c_void_p()
+            if hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            row[j] = e
+        marks.append(row)
+
+    for _ in range(W):
+        rc = lib.kda_fwd(*argv)
+        if rc:
+            raise kda.KDAError(rc)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    ev0.record()
+    for i in range(K):
+        rc = lib.kda_fwd_timed(*argv, ctypes.cast(marks[i], ctypes.c_void_p))
+        if rc:
+            raise kda.KDAError(rc)
+    ev1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_start
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / K
+
+    def elapsed(a, b):
+        f = ctypes.c_float()
+        hip.hipEventElapsedTime(ctypes.byref(f), a, b)
+        return f.value
+
+    k_map = np.mean([elapsed(m[0], m[1]) for m in marks])
+    k_prep = np.mean([elapsed(m[1], m[2]) for m in marks])
+    k_scan = np.mean([elapsed(m[2], m[3]) for m in marks])
+    for m in marks:
+        for j in range(4):
+            hip.hipEventDestroy(m[j])
+    log("timed %d steps: %.4f ms/step (wall %.4f ms/step); kernels: chunk map %.4f ms, chunk %.4f ms, "
+        "scan %.4f ms" % (K, ms_per_step, 1e3 * t_wall / K, k_map, k_prep, k_scan))
+
+    tokens = B * T
+    value = tokens / (ms_per_step * 1e-3)
+
+    # ---- fail-closed parity: timed inputs, then new contents in the same buffers ----
+    parity = {}
+    cpu_baseline = None
+    ok = True
+    if not args.no_verify:
+        from oracle import oracle_fwd, oracle_threads
+        import oracle.kda_oracle as okm
+        o_gpu = out.float().cpu().numpy()
+        h_gpu = ht.cpu().numpy()
+        t1 = time.perf_counter()
+        ro, rh = oracle_fwd(x.q, x.k, x.v, x.g, x.beta, x.h0, x.cu_seqlens, x.scale)
+        t_or = time.perf_counter() - t1
+        rel = lambda a, b: float(np.linalg.norm(a.astype(np.float64) - b) / np.linalg.norm(b))
+        parity["out_rel_rmse"] = rel(o_gpu, ro)
+        parity["state_rel_rmse"] = rel(h_gpu, rh)
+        reps, t_sum = 1, t_or
+        while not args.no_cpu_baseline and t_sum < 10.0 and reps < 100:  # about 10 s of CPU work
+            t1 = time.perf_counter()
+            oracle_fwd(x.q, x.k, x.v, x.g, x.beta, x.h0, x.cu_seqlens, x.scale)
+            t_sum += time.perf_counter() - t1
+            reps += 1
+        cpu_baseline = {"value": round(tokens * reps / t_sum, 1), "unit": "tokens/s",
+                        "cores": okm.oracle_threads(), "kind": "oracle",
+                        "sample": "the whole timed batch (%d tokens x %d heads), fp64 token-by-token, "
+                                  "%d runs in %.1f s" % (tokens, H, reps, t_sum)}
+        del ro, rh
+        # replay: new contents in the same buffers, same call; check 4 heads against the oracle
+        y = make_config(args.workload, seed=1000 + args.workload)
+        dy = upload(y)
+        for key in ("q", "k", "v", "g", "beta", "h0"):
+            if d[key] is not None:
+                d[key].copy_(dy[key])
+        rc = lib.kda_fwd(*argv)
+        torch.cuda.synchronize()
+        hs = slice(0, 4)
+        ys = lambda a: np.ascontiguousarray(a[:, :, hs]) if a.ndim >= 3 else a
+        ro2, rh2 = oracle_fwd(ys(y.q), ys(y.k), ys(y.v), ys(y.g), np.ascontiguousarray(y.beta[:, :, hs]),
+                              None if y.h0 is None else np.ascontiguousarray(y.h0[:, hs]),
+                              y.cu_seqlens, y.scale)
+        parity["replay_out_rel_rmse"] = rel(out.float().cpu().numpy()[:, :, hs], ro2)
+        parity["replay_state_rel_rmse"] = rel(ht.cpu().numpy()[:, hs], rh2)
+        ok = all(v_ <= TOL for v_ in parity.values()) and rc == 0
+        log("parity: " + json.dumps(parity))
+        if args.no_cpu_baseline:
+            cpu_baseline = None
+
+    nch = n_chunks_of(x)
+    wk = algorithmic_work(x, nch)
+    dominant = "chunk" if k_prep >= k_scan else "scan"
+    dom_bytes = wk["prep_bytes"] if dominant == "chunk" else wk["scan_bytes"]
+    dom_ms = k_prep if dominant == "chunk" else k_scan
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    kname = "chunk_prep_kernel" if dominant == "chunk" else "state_scan_kernel"
+    traffic = traffic_from_profiles(kname)
+    total_flops = wk["prep_flops"] + wk["scan_flops"]
+    res = {
+        "metric": "KDA fwd tokens/s @ H=32,d=128, 8192-token fixed+varlen; % bf16 MFMA peak",
+        "value": round(value, 1) if ok and not args.no_verify else None,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16xf32",
+        "data": "synthetic",
+        "config": {"workload": x.name, "global_batch": B, "seq_len": T, "heads": H, "dk": dk, "dv": dv,
+                   "io_dtype": x.dtype, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": dom_bytes},
+        "kernels_ms": {"chunk_map": round(float(k_map), 5), "chunk_prep": round(float(k_prep), 5),
+                       "state_scan": round(float(k_scan), 5)},
+        "mfma": {"flops_per_step": total_flops,
+                 "frac_of_peak": round(total_flops / (ms_per_step * 1e-3) / (MFMA_F16_PEAK_TFLOPS * 1e12), 5),
+                 "peak_tflops": MFMA_F16_PEAK_TFLOPS},
+        "hbm_frac_whole_step": round((wk["prep_bytes"] + wk["scan_bytes"]) / (ms_per_step * 1e-3) / 1e9
+                                     / HBM_PEAK_GBS, 4),
+        "parity": parity,
+        "cpu_baseline": cpu_baseline,
+    }
+    print(json.dumps(res), flush=True)
+    if not ok:
+        log("PARITY FAILED: no speed reported")
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

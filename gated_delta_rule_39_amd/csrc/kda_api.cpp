@@ -152,9 +152,10 @@ kda_status_t kda_fwd_validate(const kda_problem_t* prob, const void* q, const vo
   return KDA_OK;
 }
 
-kda_status_t kda_fwd(const kda_problem_t* prob, const void* q, const void* k, const void* v, const float* g,
-                     const void* beta, const float* h0, const int32_t* cu_seqlens, float scale, void* out,
-                     float* ht, void* workspace, size_t workspace_bytes, void* stream) {
+static kda_status_t forward(const kda_problem_t* prob, const void* q, const void* k, const void* v,
+                            const float* g, const void* beta, const float* h0, const int32_t* cu_seqlens,
+                            float scale, void* out, float* ht, void* workspace, size_t workspace_bytes,
+                            void* stream, void* const* events) {
   kda_status_t st = kda_fwd_validate(prob, q, k, v, g, beta, h0, cu_seqlens, scale, out, ht, workspace,
                                      workspace_bytes);
   if (st != KDA_OK) return st;
@@ -183,8 +184,24 @@ kda_status_t kda_fwd(const kda_problem_t* prob, const void* q, const void* k, co
   p.seq_order = reinterpret_cast<int32_t*>(ws + c.seq_order);
   p.rec = ws + c.rec;
   p.slice = slice_width(prob, N);
+  for (int i = 0; i < 4; ++i) p.marks[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
   hipError_t e = kda::launch_forward(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status_t kda_fwd(const kda_problem_t* prob, const void* q, const void* k, const void* v, const float* g,
+                     const void* beta, const float* h0, const int32_t* cu_seqlens, float scale, void* out,
+                     float* ht, void* workspace, size_t workspace_bytes, void* stream) {
+  return forward(prob, q, k, v, g, beta, h0, cu_seqlens, scale, out, ht, workspace, workspace_bytes, stream,
+                 nullptr);
+}
+
+kda_status_t kda_fwd_timed(const kda_problem_t* prob, const void* q, const void* k, const void* v,
+                           const float* g, const void* beta, const float* h0, const int32_t* cu_seqlens,
+                           float scale, void* out, float* ht, void* workspace, size_t workspace_bytes,
+                           void* stream, void* const* events) {
+  return forward(prob, q, k, v, g, beta, h0, cu_seqlens, scale, out, ht, workspace, workspace_bytes, stream,
+                 events);
 }
 
 }  // extern "C"

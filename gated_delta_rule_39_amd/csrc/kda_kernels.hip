@@ -52,6 +52,10 @@ static hipError_t launch_scan(const ForwardPlan& p, hipStream_t stream) {
   }
 }
 
+static void mark(const ForwardPlan& p, int i, hipStream_t stream) {
+  if (p.marks[i]) hipEventRecord(p.marks[i], stream);
+}
+
 template <int DK, int DV>
 static hipError_t launch_dkdv(const ForwardPlan& p, hipStream_t stream) {
   hipError_t e = hipSuccess;
@@ -59,13 +63,18 @@ static hipError_t launch_dkdv(const ForwardPlan& p, hipStream_t stream) {
     e = (p.dtype == 0) ? launch_prep<DK, DV, uint16_t>(p, stream) : launch_prep<DK, DV, float>(p, stream);
     if (e != hipSuccess) return e;
   }
-  return (p.dtype == 0) ? launch_scan<DK, DV, uint16_t>(p, stream) : launch_scan<DK, DV, float>(p, stream);
+  mark(p, 2, stream);
+  e = (p.dtype == 0) ? launch_scan<DK, DV, uint16_t>(p, stream) : launch_scan<DK, DV, float>(p, stream);
+  mark(p, 3, stream);
+  return e;
 }
 
 hipError_t launch_forward(const ForwardPlan& p, hipStream_t stream) {
   if (p.N <= 0) return hipSuccess;
+  mark(p, 0, stream);
   hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kMapThreads), 0, stream, p.cu, p.T, p.N, p.n_chunk_ub,
                      p.info, reinterpret_cast<ChunkEntry*>(p.table), p.seq_off, p.seq_order);
+  mark(p, 1, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.dk == 64 && p.dv == 64) return launch_dkdv<64, 64>(p, stream);

@@ -29,6 +29,7 @@ struct ForwardPlan {
   int32_t* seq_order;
   uint8_t* rec;
   int32_t slice;  // value columns per scan workgroup (16, 32 or 64)
+  hipEvent_t marks[4];  // optional timing marks around the kernels (may be null)
 };
 
 // Bytes of one per-(chunk, head) record.

@@ -125,6 +125,20 @@ kda_status_t kda_fwd(const kda_problem_t* prob, const void* q, const void* k, co
                      const int32_t* cu_seqlens, float scale, void* out, float* ht,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * kda_fwd with timing marks for profiling: identical work, plus hipEventRecord
+ * of events[0] before the chunk map, events[1] after it, events[2] after the
+ * chunk kernel and events[3] after the state scan, all on `stream`.
+ * `events` is a host array of 4 hipEvent_t handles created by the caller
+ * (NULL entries are skipped); the elapsed time between consecutive marks is
+ * the duration of each kernel.  Errors as for kda_fwd.
+ */
+kda_status_t kda_fwd_timed(const kda_problem_t* prob, const void* q, const void* k, const void* v,
+                           const float* g, const void* beta, const float* h0,
+                           const int32_t* cu_seqlens, float scale, void* out, float* ht,
+                           void* workspace, size_t workspace_bytes, void* stream,
+                           void* const* events);
+
 /* Human-readable name of a status code (static string). */
 const char* kda_status_string(kda_status_t status);
 
