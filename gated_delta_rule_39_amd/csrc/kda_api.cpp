@@ -1,6 +1,6 @@
 // C ABI of the KDA forward: argument checks, workspace carve-up, launches.
 // Declarations and the contract of every entry point are in include/kda.h.
-#include "../../include/kda.h"
+#include "kda.h"
 
 #include <hip/hip_runtime.h>
 
@@ -71,7 +71,7 @@ int slice_width(const kda_problem_t* p, int64_t N) {
     if ((v == 16 || v == 32 || v == 64) && v <= p->dv) return v;
   }
   (void)N;
-  return 32;
+  return 16;
 }
 
 }  // namespace

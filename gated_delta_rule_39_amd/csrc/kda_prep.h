@@ -212,12 +212,24 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
   if (l == 0) red[w] = vm;
   __syncthreads();  // #1
 #pragma unroll
-  for (int e = 0; e < NE; ++e) {
-    const int ch = 32 * (e >> 3) + pi_index(gq, e & 7);
-    float off = 0.f;
-    for (int b = 0; b < w; ++b) off += btot[b * DK + ch];
-    G[e] += off;
-  }
+  for (int s = 0; s < KSK; ++s)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      // totals of the earlier 16-token blocks, added in block order
+      const int c0 = 32 * s + 16 * hh + 4 * gq;
+      float4 off = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int b = 0; b < 3; ++b) {
+        if (b < w) {
+          const float4 bt4 = *reinterpret_cast<const float4*>(btot + b * DK + c0);
+          off.x += bt4.x; off.y += bt4.y; off.z += bt4.z; off.w += bt4.w;
+        }
+      }
+      G[8 * s + 4 * hh + 0] += off.x;
+      G[8 * s + 4 * hh + 1] += off.y;
+      G[8 * s + 4 * hh + 2] += off.z;
+      G[8 * s + 4 * hh + 3] += off.w;
+    }
   const float vmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const int ue = (vmax > 0.f) ? 12 - (ilogbf(vmax) + 1) : 0;
   __syncthreads();  // #2: btot reads done before the region is reused

@@ -116,11 +116,23 @@ __global__ __launch_bounds__(256) void state_scan_kernel(ScanArgs a) {
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, t = l & 15, gq = l >> 4;
+  // Workgroups are dispatched round-robin over the 8 XCDs (block id mod 8).  The NS
+  // slices of one (sequence, head) share every chunk factor except U, so they are
+  // mapped to block ids with equal residue mod 8: one XCD's L2 serves all of them.
+  const int64_t nblk = (int64_t)gridDim.x;
   const int64_t bid = blockIdx.x;
-  const int slice = (int)(bid % NS);
-  const int64_t rest = bid / NS;
-  const int h = (int)(rest % a.H);
-  const int64_t n = a.seq_order[rest / a.H];
+  int64_t chain, slice_l;
+  if (nblk % (8 * NS) == 0) {
+    const int64_t xcd = bid & 7, k = bid >> 3;
+    slice_l = k % NS;
+    chain = (k / NS) * 8 + xcd;
+  } else {
+    slice_l = bid % NS;
+    chain = bid / NS;
+  }
+  const int slice = (int)slice_l;
+  const int h = (int)(chain % a.H);
+  const int64_t n = a.seq_order[chain / a.H];
   int64_t c0 = a.seq_off[n], c1 = a.seq_off[n + 1];
   if (c1 > a.n_chunk_ub) c1 = a.n_chunk_ub;  // only on invalid cu_seqlens
   if (c0 > c1) c0 = c1;
@@ -194,12 +206,9 @@ __global__ __launch_bounds__(256) void state_scan_kernel(ScanArgs a) {
 
   OutT* out = reinterpret_cast<OutT*>(a.out);
   const float oscale = a.scale;
-  CR cur;
-  if (c0 < c1) load_chunk<DK, DV, NV>(cur, a.rec + ((size_t)c0 * a.H + h) * R::BYTES, w, l, slice);
-  for (int64_t c = c0; c < c1; ++c) {
-    CR nxt;
-    if (c + 1 < c1) load_chunk<DK, DV, NV>(nxt, a.rec + ((size_t)(c + 1) * a.H + h) * R::BYTES, w, l, slice);
 
+  // One chunk step on the factors in `cur`.
+  auto step = [&](const CR& cur, int64_t c) {
     // S0 fragments (B operand of W S0 and, read as A of S0^T, of the output)
     f16x8 sf[KSK][NT];
 #pragma unroll
@@ -267,7 +276,24 @@ __global__ __launch_bounds__(256) void state_scan_kernel(ScanArgs a) {
       }
     }
     __syncthreads();
-    if (c + 1 < c1) cur = nxt;
+  };
+
+  // Ping-pong prefetch: the factors of chunk c+1 are requested (unconditionally; the
+  // last chunk is re-read at the end) before chunk c is processed.
+  auto rec_of = [&](int64_t c) {
+    const int64_t cc = c < c1 ? c : c1 - 1;
+    return a.rec + ((size_t)cc * a.H + h) * R::BYTES;
+  };
+  if (c0 < c1) {
+    CR bufA, bufB;
+    load_chunk<DK, DV, NV>(bufA, rec_of(c0), w, l, slice);
+    for (int64_t c = c0; c < c1; c += 2) {
+      load_chunk<DK, DV, NV>(bufB, rec_of(c + 1), w, l, slice);
+      step(bufA, c);
+      if (c + 1 >= c1) break;
+      load_chunk<DK, DV, NV>(bufA, rec_of(c + 2), w, l, slice);
+      step(bufB, c + 1);
+    }
   }
 
   if (a.ht) {
