@@ -18,7 +18,7 @@ constexpr int64_t kChunkTokens = 64;
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct Carve {
-  size_t info, table, seq_off, seq_order, rec, total;
+  size_t info, table, seq_off, seq_order, defer, rec, total;
 };
 
 bool sizes_ok(const kda_problem_t* p, bool packed, int64_t* N, int64_t* n_chunk_ub) {
@@ -51,7 +51,8 @@ Carve carve(const kda_problem_t* p, int64_t N, int64_t n_chunk_ub) {
   c.table = c.info + 256;
   c.seq_off = c.table + align256((size_t)n_chunk_ub * 16);
   c.seq_order = c.seq_off + align256((size_t)(N + 1) * 4);
-  c.rec = c.seq_order + align256((size_t)N * 4);
+  c.defer = c.seq_order + align256((size_t)N * 4);
+  c.rec = c.defer + align256((size_t)n_chunk_ub * (size_t)p->heads * 4);
   c.total = c.rec + (size_t)n_chunk_ub * (size_t)p->heads * kda::record_bytes(p->dk, p->dv);
   return c;
 }
@@ -183,6 +184,7 @@ static kda_status_t forward(const kda_problem_t* prob, const void* q, const void
   p.seq_off = reinterpret_cast<int32_t*>(ws + c.seq_off);
   p.seq_order = reinterpret_cast<int32_t*>(ws + c.seq_order);
   p.rec = ws + c.rec;
+  p.defer_list = reinterpret_cast<int32_t*>(ws + c.defer);
   p.slice = slice_width(prob, N);
   for (int i = 0; i < 4; ++i) p.marks[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
   hipError_t e = kda::launch_forward(p, static_cast<hipStream_t>(stream));

@@ -8,7 +8,7 @@
 // a sequence may be partial.
 //
 // One workgroup of 1024 threads builds:
-//   info[0]           total number of chunks
+//   info[0]           total number of chunks (info[2], the deferred-chunk count, is zeroed)
 //   table[c]          (sequence, valid length, index inside the sequence) of chunk c
 //   seq_off[n]        first chunk of sequence n (exclusive prefix of chunk counts), seq_off[N] = total
 //   seq_order[i]      sequences ordered by chunk count, longest first (buckets of
@@ -66,6 +66,7 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* _
   if (tid == 0) {
     info[0] = total;
     info[1] = (carry_s > n_chunk_ub) ? 1 : 0;
+    info[2] = 0;  // chunks deferred to the exact chunk kernel
     seq_off[N] = carry_s;
   }
   __syncthreads();

@@ -22,11 +22,24 @@ static hipError_t launch_prep(const ForwardPlan& p, hipStream_t stream) {
   a.info = p.info;
   a.table = reinterpret_cast<const ChunkEntry*>(p.table);
   a.rec = p.rec;
+  a.defer_count = p.info + 2;
+  a.defer_list = p.defer_list;
   const size_t smem = PrepSmem<DK, DV>::BYTES;
-  auto kern = chunk_prep_kernel<DK, DV, InT>;
-  hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  dim3 grid((unsigned)p.n_chunk_ub, (unsigned)p.H);
-  hipLaunchKernelGGL(kern, grid, dim3(256), smem, stream, a);
+  auto fast = chunk_prep_kernel<DK, DV, InT>;
+  auto exact = chunk_prep_exact_kernel<DK, DV, InT>;
+  hipFuncSetAttribute(reinterpret_cast<const void*>(fast), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  hipFuncSetAttribute(reinterpret_cast<const void*>(exact), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  hipLaunchKernelGGL(fast, dim3((unsigned)p.n_chunk_ub, (unsigned)p.H), dim3(256), smem, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the exact variant walks the deferred list (usually empty: its workgroups exit at once)
+  int dev = 0, cus = 0;
+  hipGetDevice(&dev);
+  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int64_t grid = cus > 0 ? cus : 256;
+  const int64_t items = p.n_chunk_ub * (int64_t)p.H;
+  if (grid > items) grid = items;
+  hipLaunchKernelGGL(exact, dim3((unsigned)grid), dim3(256), smem, stream, a);
   return hipGetLastError();
 }
 

@@ -26,17 +26,25 @@
 //  (a) In-chunk cumulative log-gate G, kept in fp32 and in log2 units
 //      (the same section rejects an fp16 table of decays and decays formed
 //      as ratios of cumulative powers that underflow past 126 bits).
-//  (b) Gram matrices L and Aqk on fp16 MFMA.  Every pair factor
-//      exp(G_i - G_j) is split around a reference row r with j <= r <= i as
-//      exp(G_i - G_r) * exp(G_r - G_j): both factors are <= 1, so nothing can
-//      overflow at any gate depth and underflow only drops terms that are
-//      below fp32 range.  Off-diagonal 16x16 tiles use the end of the column
-//      block as r; diagonal tiles use, per 4-token column group, the end of
-//      that group; pairs inside one 4-token group use exp(g) products
-//      (r = j), all on MFMA.
+//  (b) Gram matrices L and Aqk.  Every pair factor exp(G_i - G_j) is split
+//      around a reference row r with j <= r <= i as exp(G_i - G_r) *
+//      exp(G_r - G_j): both factors are <= 1, so nothing overflows at any
+//      gate depth and underflow only drops terms below fp32 range.
+//      Off-diagonal 16x16 tiles (fp16 MFMA) use the end of the column block
+//      as r.  A diagonal tile uses its middle row as r, which puts the
+//      factors in [exp(-D), exp(D)] with D the larger half-span of the tile's
+//      decay; when D <= 80 nats on every channel of all four diagonal tiles
+//      (checked per chunk and head) each tile is one fp32 MFMA product.
+//      Otherwise the chunk is handed to the exact variant of this kernel
+//      (a second launch over the deferred list), which uses per-4-token
+//      column-group references plus exp(g) products inside each group, on
+//      fp16 MFMA, exact at any depth.
 //  (b) Tinv by blocked forward substitution in fp32 (16x16 diagonal blocks by
 //      substitution, off-diagonal blocks by block products).
-//  (b) W and U on fp16 MFMA from Tinv and the LDS-transposed operands.
+//  (b) W and U on fp16 MFMA from Tinv and the exchanged operand fragments.
+//  Transposes (token-major operands of the token contractions) are MFMA
+//  products with an identity matrix: the C fragment of X * I holds, lane for
+//  lane, the operand fragment of X^T, exactly (fp16 values, fp32 sums).
 //
 // fp16 operands: every operand is bounded (|khat|,|qhat| <= 1, all decay
 // factors <= 1, |Tinv| <= 1, |W| rows bounded) except V, which is rescaled
@@ -52,18 +60,23 @@ namespace kda {
 template <int DK, int DV>
 struct PrepSmem {
   static constexpr int KSK = DK / 32;
-  static constexpr int PT = 72;  // pitch (halves) of transposed [*][64] fp16 tiles
+  static constexpr int NTK = DK / 16;
+  static constexpr int NTV = DV / 16;
   static constexpr int LP = 68;  // pitch (floats) of 64x64 fp32 matrices
+  static constexpr int ET_ROWS = 19;
+  static constexpr size_t BTOT = 4 * DK * 4;
   static constexpr size_t YBF = 3 * KSK * 64 * 16;
-  static constexpr size_t BWT = (size_t)DK * PT * 2;
-  static constexpr size_t BUT = (size_t)DV * PT * 2;
-  static constexpr size_t X_BYTES = (YBF > BWT + BUT ? YBF : BWT + BUT);
+  static constexpr size_t BWX = (size_t)NTK * 2 * 64 * 16;
+  static constexpr size_t BUX = (size_t)NTV * 2 * 64 * 16;
+  static_assert(YBF <= BWX, "column operands must not reach the Bu fragments");
+  static constexpr size_t X_A = BTOT > YBF ? BTOT : YBF;
+  static constexpr size_t X_BYTES = X_A > BWX + BUX ? X_A : BWX + BUX;
   static constexpr size_t MAT = 64 * LP * 4;
-  static constexpr size_t KTT = (size_t)DK * PT * 2;
-  static constexpr size_t Z_BYTES = (MAT > KTT ? MAT : KTT);
-  static constexpr size_t X = 0;                  // btot -> YBf -> BwT | BuT
+  static constexpr size_t ETB = (size_t)ET_ROWS * DK * 4;
+  static constexpr size_t Z_BYTES = MAT > ETB ? MAT : ETB;
+  static constexpr size_t X = 0;                  // btot -> column operands | Bu fragments -> Bw^T | Bu
   static constexpr size_t Y = X + X_BYTES;        // L (strict lower) + inverse temporaries (upper)
-  static constexpr size_t Z = Y + MAT;            // K~^T transpose -> Tinv
+  static constexpr size_t Z = Y + MAT;            // decay-factor table -> Tinv
   static constexpr size_t GE = Z + Z_BYTES;       // G (log2 units) at the 16 group ends
   static constexpr size_t BETA = GE + 16 * DK * 4;
   static constexpr size_t RED = BETA + 64 * 4;
@@ -83,37 +96,46 @@ struct PrepArgs {
   const int32_t* info;
   const ChunkEntry* table;
   uint8_t* rec;     // records [n_chunk_ub][H]
+  int32_t* defer_count;  // chunks handed to the exact variant (zeroed by the chunk map)
+  int32_t* defer_list;   // their items chunk * H + head
 };
 
-template <int DK, int DV, typename InT>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
+// Decay-factor table rows (per key channel c, G in log2 units, Gend(p) = G at the end
+// of 4-token group p, block w = tokens 16w..16w+15):
+//   0..3    exp(Gprev(w))                  Gprev(w) = Gend(4w-1), Gprev(0) = 0
+//   4..7    exp(Glast - Gnext(w))          Gnext(w) = Gend(4w+3)
+//   8..10   exp(Gprev(w) - Gnext(b))       (b, w) = (0, 2), (0, 3), (1, 3)
+//   11..14  exp(Gprev(w) - Gmid(w))        Gmid(w) = Gend(4w+1)   (>= 1, used under the guard)
+//   15..18  exp(Gmid(w) - Gnext(w))        (>= 1, used under the guard)
+constexpr float kGuardLog2 = 115.0f;  // 80 nats: half-span limit of the fp32 diagonal path
+
+// One (chunk, head).  EXACT = false: guarded fp32 diagonal tiles, the chunk is deferred
+// when the guard fails.  EXACT = true: per-group references on every diagonal tile.
+template <int DK, int DV, typename InT, bool EXACT>
+__device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, const int h, uint8_t* smem) {
   using R = Rec<DK, DV>;
   using SM = PrepSmem<DK, DV>;
   constexpr int KSK = DK / 32;   // contraction steps over key channels
   constexpr int KSV = DV / 32;
+  constexpr int NTV = DV / 16;
   constexpr int NE = KSK * 8;    // key channels held per lane
   constexpr int NEV = KSV * 8;   // value channels held per lane
-  constexpr int PT = SM::PT;
   constexpr int LP = SM::LP;
 
-  extern __shared__ __align__(16) uint8_t smem[];
   float* btot = reinterpret_cast<float*>(smem + SM::X);            // [4][DK]
   f16x8* ybf = reinterpret_cast<f16x8*>(smem + SM::X);             // [3][KSK][64]
-  _Float16* bwT = reinterpret_cast<_Float16*>(smem + SM::X);       // [DK][PT]
-  _Float16* buT = reinterpret_cast<_Float16*>(smem + SM::X + SM::BWT);  // [DV][PT]
+  uint8_t* bwx = smem + SM::X;                                     // [NTK][2][64] f16x8
+  uint8_t* bux = smem + SM::X + SM::BWX;                           // [NTV][2][64] f16x8
   float* Lm = reinterpret_cast<float*>(smem + SM::Y);              // [64][LP]
-  _Float16* ktT = reinterpret_cast<_Float16*>(smem + SM::Z);       // [DK][PT]
+  float* et = reinterpret_cast<float*>(smem + SM::Z);              // [19][DK]
   float* Tm = reinterpret_cast<float*>(smem + SM::Z);              // [64][LP]
   float* gend = reinterpret_cast<float*>(smem + SM::GE);           // [16][DK]
   float* sbeta = reinterpret_cast<float*>(smem + SM::BETA);        // [64]
-  float* red = reinterpret_cast<float*>(smem + SM::RED);           // [16]
+  float* red = reinterpret_cast<float*>(smem + SM::RED);           // [8]
+  int* guard = reinterpret_cast<int*>(smem + SM::RED) + 8;
 
-  const int chunk = blockIdx.x;
-  const int h = blockIdx.y;
-  if (chunk >= a.info[0]) return;  // uniform for the workgroup
   const ChunkEntry ce = a.table[chunk];
   const int64_t start = seq_start(a.cu, a.T, ce.seq) + (int64_t)ce.idx * kChunk;
-
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int l = tid & 63;
@@ -124,7 +146,27 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
   const bool valid = (i_loc < ce.len) && (tok < a.T_total);
   uint8_t* rec = a.rec + ((size_t)chunk * a.H + h) * R::BYTES;
 
+  // reads the lane's NE channels of row `row` of a [*][DK] fp32 array in LDS
+  auto lane_row = [&](const float* base, int row, float* out) {
+    const float* p = base + row * DK;
+#pragma unroll
+    for (int j = 0; j < 2 * KSK; ++j) {
+      const float4 r4 = *reinterpret_cast<const float4*>(p + 16 * j + 4 * gq);
+      out[4 * j + 0] = r4.x; out[4 * j + 1] = r4.y; out[4 * j + 2] = r4.z; out[4 * j + 3] = r4.w;
+    }
+  };
+
+  // reads the lane's 8 channels of k-step s of row `row` (indices 8 s .. 8 s + 7)
+  auto lane_step = [&](const float* base, int row, int s, float* out8) {
+    const float* p = base + row * DK + 32 * s + 4 * gq;
+    const float4 lo = *reinterpret_cast<const float4*>(p);
+    const float4 hi = *reinterpret_cast<const float4*>(p + 16);
+    out8[0] = lo.x; out8[1] = lo.y; out8[2] = lo.z; out8[3] = lo.w;
+    out8[4] = hi.x; out8[5] = hi.y; out8[6] = hi.z; out8[7] = hi.w;
+  };
+
   // ---------------- (a) loads, norms, cumulative gate ----------------
+  // Lane (token 16w + t, quarter gq) holds channels 32 s + pi_index(gq, e) at index 8 s + e.
   float xq[NE], xk[NE], G[NE], xv[NEV];
   float bt = 0.f;
   {
@@ -135,38 +177,30 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
     const size_t rowk = ((size_t)tok * a.H + h) * DK;
     const size_t rowv = ((size_t)tok * a.H + h) * DV;
 #pragma unroll
-    for (int s = 0; s < KSK; ++s)
+    for (int j = 0; j < 2 * KSK; ++j) {
+      const int c0 = 16 * j + 4 * gq;
+      if (valid) {
+        load4(q + rowk + c0, xq + 4 * j);
+        load4(k + rowk + c0, xk + 4 * j);
+        load4(a.g + rowk + c0, G + 4 * j);
+      } else {
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int c0 = 32 * s + 16 * hh + 4 * gq;
-        float* oq = xq + 8 * s + 4 * hh;
-        float* ok = xk + 8 * s + 4 * hh;
-        float* og = G + 8 * s + 4 * hh;
-        if (valid) {
-          load4(q + rowk + c0, oq);
-          load4(k + rowk + c0, ok);
-          load4(a.g + rowk + c0, og);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) oq[r] = ok[r] = og[r] = 0.f;
-        }
+        for (int r = 0; r < 4; ++r) xq[4 * j + r] = xk[4 * j + r] = G[4 * j + r] = 0.f;
       }
+    }
 #pragma unroll
-    for (int s = 0; s < KSV; ++s)
+    for (int j = 0; j < 2 * KSV; ++j) {
+      if (valid) {
+        load4(v + rowv + 16 * j + 4 * gq, xv + 4 * j);
+      } else {
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int c0 = 32 * s + 16 * hh + 4 * gq;
-        float* ov = xv + 8 * s + 4 * hh;
-        if (valid) {
-          load4(v + rowv + c0, ov);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ov[r] = 0.f;
-        }
+        for (int r = 0; r < 4; ++r) xv[4 * j + r] = 0.f;
       }
+    }
     if (valid) bt = load1(be + (size_t)tok * a.H + h);
   }
   if (gq == 0) sbeta[i_loc] = bt;
+  if (tid == 0) *guard = 0;
 
   // L2 normalisation (4 lanes share a token: lanes t, t+16, t+32, t+48)
   auto normalise = [&](float* x) {
@@ -203,7 +237,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
   }
   if (t == 15) {
 #pragma unroll
-    for (int e = 0; e < NE; ++e) btot[w * DK + 32 * (e >> 3) + pi_index(gq, e & 7)] = G[e];
+    for (int j = 0; j < 2 * KSK; ++j)
+      *reinterpret_cast<float4*>(btot + w * DK + 16 * j + 4 * gq) =
+          make_float4(G[4 * j], G[4 * j + 1], G[4 * j + 2], G[4 * j + 3]);
   }
   float vm = 0.f;
 #pragma unroll
@@ -212,64 +248,129 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
   if (l == 0) red[w] = vm;
   __syncthreads();  // #1
 #pragma unroll
-  for (int s = 0; s < KSK; ++s)
+  for (int j = 0; j < 2 * KSK; ++j) {
+    // totals of the earlier 16-token blocks, added in block order
+    float4 off = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      // totals of the earlier 16-token blocks, added in block order
-      const int c0 = 32 * s + 16 * hh + 4 * gq;
-      float4 off = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int b = 0; b < 3; ++b) {
-        if (b < w) {
-          const float4 bt4 = *reinterpret_cast<const float4*>(btot + b * DK + c0);
-          off.x += bt4.x; off.y += bt4.y; off.z += bt4.z; off.w += bt4.w;
-        }
+    for (int b = 0; b < 3; ++b) {
+      if (b < w) {
+        const float4 bt4 = *reinterpret_cast<const float4*>(btot + b * DK + 16 * j + 4 * gq);
+        off.x += bt4.x; off.y += bt4.y; off.z += bt4.z; off.w += bt4.w;
       }
-      G[8 * s + 4 * hh + 0] += off.x;
-      G[8 * s + 4 * hh + 1] += off.y;
-      G[8 * s + 4 * hh + 2] += off.z;
-      G[8 * s + 4 * hh + 3] += off.w;
     }
+    G[4 * j + 0] += off.x; G[4 * j + 1] += off.y; G[4 * j + 2] += off.z; G[4 * j + 3] += off.w;
+  }
   const float vmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const int ue = (vmax > 0.f) ? 12 - (ilogbf(vmax) + 1) : 0;
-  __syncthreads();  // #2: btot reads done before the region is reused
+  // beta v 2^ue rows in fp16 (|.| < 2^12); the fp32 copy dies here
+  f16x8 vr[KSV];
+#pragma unroll
+  for (int s = 0; s < KSV; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vr[s][e] = (_Float16)(bt * ldexpf(xv[8 * s + e], ue));
   if ((t & 3) == 3) {
 #pragma unroll
-    for (int e = 0; e < NE; ++e) gend[(4 * w + (t >> 2)) * DK + 32 * (e >> 3) + pi_index(gq, e & 7)] = G[e];
+    for (int j = 0; j < 2 * KSK; ++j)
+      *reinterpret_cast<float4*>(gend + (4 * w + (t >> 2)) * DK + 16 * j + 4 * gq) =
+          make_float4(G[4 * j], G[4 * j + 1], G[4 * j + 2], G[4 * j + 3]);
   }
-  __syncthreads();  // #3: group-end gates visible
+  __syncthreads();  // #2: group-end gates visible, block totals consumed
 
-  // reads the lane's NE channels of a group-end row of G
-  auto gend_row = [&](int p, float* out) {
-    const float* row = gend + p * DK;
+  // decay-factor table and the guard of the fp32 diagonal path
+  if (tid < DK) {
+    const int c = tid;
+    auto ge = [&](int p) { return p < 0 ? 0.f : gend[p * DK + c]; };
+    const float glast = ge(15);
+    int bad = 0;
 #pragma unroll
-    for (int s = 0; s < KSK; ++s)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float4 r4 = *reinterpret_cast<const float4*>(row + 32 * s + 16 * hh + 4 * gq);
-        out[8 * s + 4 * hh + 0] = r4.x;
-        out[8 * s + 4 * hh + 1] = r4.y;
-        out[8 * s + 4 * hh + 2] = r4.z;
-        out[8 * s + 4 * hh + 3] = r4.w;
-      }
-  };
-
-  // ---------------- outputs that need only G: Q~, K~^T, lambda, header ----------------
-  {
-    float glast[NE];
-    gend_row(15, glast);
-#pragma unroll
-    for (int s = 0; s < KSK; ++s) {
-      f16x8 qf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[e] = (_Float16)(xq[8 * s + e] * exp2_hw(G[8 * s + e]));
-      *reinterpret_cast<f16x8*>(rec + R::Q + ((size_t)(w * KSK + s) * 64 + l) * 16) = qf;
+    for (int ww = 0; ww < 4; ++ww) {
+      const float gp = ge(4 * ww - 1), gn = ge(4 * ww + 3), gm = ge(4 * ww + 1);
+      et[ww * DK + c] = exp2_hw(gp);
+      et[(4 + ww) * DK + c] = exp2_hw(glast - gn);
+      const float d1 = gp - gm, d2 = gm - gn;
+      if (!(d1 <= kGuardLog2 && d2 <= kGuardLog2)) bad = 1;
+      et[(11 + ww) * DK + c] = exp2_hw(fminf(d1, kGuardLog2));
+      et[(15 + ww) * DK + c] = exp2_hw(fminf(d2, kGuardLog2));
     }
-    // K~ = khat * exp(G_last - G), transposed into LDS [channel][token]
+    et[8 * DK + c] = exp2_hw(ge(7) - ge(3));
+    et[9 * DK + c] = exp2_hw(ge(11) - ge(3));
+    et[10 * DK + c] = exp2_hw(ge(11) - ge(7));
+    if (bad) atomicOr(guard, 1);
+  }
+  // operand bases: rows khat_i exp(G_i - Gprev(w)) and qhat_i exp(G_i - Gprev(w)),
+  // columns khat_j exp(Gnext(w) - G_j); all factors <= 1
+  float XB[NE], QB[NE], YC[NE];
+  {
+    float gp[NE], gn[NE];
+    lane_row(gend, 4 * w + 3, gn);
+    if (w > 0) {
+      lane_row(gend, 4 * w - 1, gp);
+    } else {
+#pragma unroll
+      for (int e = 0; e < NE; ++e) gp[e] = 0.f;
+    }
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
-      const int ch = 32 * (e >> 3) + pi_index(gq, e & 7);
-      ktT[ch * PT + i_loc] = (_Float16)(xk[e] * exp2_hw(glast[e] - G[e]));
+      const float fb = exp2_hw(G[e] - gp[e]);
+      const float fc = exp2_hw(gn[e] - G[e]);
+      XB[e] = xk[e] * fb;
+      QB[e] = xq[e] * fb;
+      YC[e] = xk[e] * fc;
+    }
+  }
+  __syncthreads();  // #3: table and guard visible
+  if (!EXACT) {
+    if (*guard) {  // a diagonal tile spans more decay than the fp32 path covers
+      if (tid == 0) a.defer_list[atomicAdd(a.defer_count, 1)] = chunk * a.H + h;
+      return;  // uniform for the workgroup
+    }
+  }
+
+  // identity fragments: B[k][n] = 1 iff the channel of slot k is 16*hh + n of the step
+  f16x8 ident[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      ident[hh][e] = (_Float16)(((t >> 2) == gq && e == 4 * hh + (t & 3)) ? 1.f : 0.f);
+
+  // ---------------- outputs that need only G ----------------
+  f16x8 bwr[KSK];
+  {
+#pragma unroll
+    for (int s = 0; s < KSK; ++s) {
+      float eS[8], eE[8];
+      lane_step(et, w, s, eS);
+      lane_step(et, 4 + w, s, eE);
+      f16x8 qf, kf, y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qf[e] = (_Float16)(QB[8 * s + e] * eS[e]);          // qhat exp(G)
+        kf[e] = (_Float16)(YC[8 * s + e] * eE[e]);          // khat exp(G_last - G)
+        bwr[s][e] = (_Float16)(bt * XB[8 * s + e] * eS[e]); // beta khat exp(G)
+        y[e] = (_Float16)YC[8 * s + e];
+      }
+      *reinterpret_cast<f16x8*>(rec + R::Q + ((size_t)(w * KSK + s) * 64 + l) * 16) = qf;
+      // K~^T fragments: (K~ I) holds, per lane, key channel 16 ct + t at tokens 16 w + 4 gq + r
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const f32x4 c = mfma16(kf, ident[hh], zero4());
+        const int ct = 2 * s + hh;
+        f16x4 h4 = {(_Float16)c[0], (_Float16)c[1], (_Float16)c[2], (_Float16)c[3]};
+        *reinterpret_cast<f16x4*>(rec + R::KT + ((size_t)(ct * 2 + (w >> 1)) * 64 + l) * 16 + (w & 1) * 8) = h4;
+      }
+      // column-side operands of the off-diagonal Gram tiles (reference = end of block w)
+      if (w < 3) ybf[(w * KSK + s) * 64 + l] = y;
+    }
+    // Bu fragments (beta v 2^ue, rows = value channels, tokens in pi order)
+#pragma unroll
+    for (int s = 0; s < KSV; ++s) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const f32x4 c = mfma16(vr[s], ident[hh], zero4());
+        f16x4 h4 = {(_Float16)c[0], (_Float16)c[1], (_Float16)c[2], (_Float16)c[3]};
+        *reinterpret_cast<f16x4*>(bux + ((size_t)((2 * s + hh) * 2 + (w >> 1)) * 64 + l) * 16 + (w & 1) * 8) = h4;
+      }
     }
     if (tid < DK) reinterpret_cast<float*>(rec + R::LAM)[tid] = exp2_hw(gend[15 * DK + tid]);
     if (tid == 0) {
@@ -277,33 +378,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
       reinterpret_cast<int32_t*>(rec + R::HDR)[1] = ue;
     }
   }
-  // column-side operands of off-diagonal Gram tiles: khat_j * exp(Gend(block j) - G_j)
-  if (w < 3) {
-    float gb[NE];
-    gend_row(4 * w + 3, gb);
-#pragma unroll
-    for (int s = 0; s < KSK; ++s) {
-      f16x8 y;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = (_Float16)(xk[8 * s + e] * exp2_hw(gb[8 * s + e] - G[8 * s + e]));
-      ybf[(w * KSK + s) * 64 + l] = y;
-    }
-  }
-  __syncthreads();  // #4: K~^T and the column operands visible
-
-  // K~^T fragments: row = key channel, contraction over tokens in pi order
-#pragma unroll
-  for (int m = 0; m < R::NTK / 4; ++m) {
-    const int ct = w + 4 * m;
-    const _Float16* row = ktT + (16 * ct + t) * PT;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      f16x4 lo = *reinterpret_cast<const f16x4*>(row + 32 * s2 + 4 * gq);
-      f16x4 hi = *reinterpret_cast<const f16x4*>(row + 32 * s2 + 16 + 4 * gq);
-      f16x8 f = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      *reinterpret_cast<f16x8*>(rec + R::KT + ((size_t)(ct * 2 + s2) * 64 + l) * 16) = f;
-    }
-  }
+  __syncthreads();  // #4: column operands visible
 
   // ---------------- (b) Gram matrices L (row block w) and Aqk^T (column block w) ----------------
   // offL[b]: L tile (w, b) and offA[b]: Aqk^T tile (b, w) for b < w; dL, dA: the diagonal tiles
@@ -311,20 +386,26 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
 #pragma unroll
   for (int b = 0; b < 3; ++b) { offL[b] = zero4(); offA[b] = zero4(); }
 
-  // off-diagonal tiles (w, b), b < w: reference r = end of block b
+  // off-diagonal tiles (w, b), b < w: reference r = end of block b.
+  // Row factor exp(G_i - Gnext(b)) = exp(G_i - Gprev(w)) * exp(Gprev(w) - Gnext(b)).
 #pragma unroll
   for (int b = 0; b < 3; ++b) {
     if (b < w) {
-      float gr[NE];
-      gend_row(4 * b + 3, gr);
+      const int trow = 8 + (b == 0 ? (w == 2 ? 0 : 1) : 2);
 #pragma unroll
       for (int s = 0; s < KSK; ++s) {
+        float fr[8];
+        if (b == w - 1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) fr[e] = 1.f;
+        } else {
+          lane_step(et, trow, s, fr);
+        }
         f16x8 xk8, xq8;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float f = exp2_hw(G[8 * s + e] - gr[8 * s + e]);
-          xk8[e] = (_Float16)(xk[8 * s + e] * f);
-          xq8[e] = (_Float16)(xq[8 * s + e] * f);
+          xk8[e] = (_Float16)(XB[8 * s + e] * fr[e]);
+          xq8[e] = (_Float16)(QB[8 * s + e] * fr[e]);
         }
         const f16x8 yb = ybf[(b * KSK + s) * 64 + l];
         offL[b] = mfma16(xk8, yb, offL[b]);
@@ -332,12 +413,37 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
       }
     }
   }
-  // diagonal tile (w, w), pairs in different 4-token groups: reference = end of the column group
-  {
+
+  if (!EXACT) {
+    // diagonal tile in one fp32 product around the tile's middle row m = 16w + 7:
+    // rows exp(G_i - G_m) = exp(G_i - Gprev) exp(Gprev - G_m),
+    // columns exp(G_m - G_j) = exp(Gnext - G_j) exp(G_m - Gnext)
+#pragma unroll
+    for (int s = 0; s < KSK; ++s) {
+      float er[8], ec[8];
+      lane_step(et, 11 + w, s, er);
+      lane_step(et, 15 + w, s, ec);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xkr = XB[8 * s + e] * er[e], xqr = QB[8 * s + e] * er[e], ykc = YC[8 * s + e] * ec[e];
+        dL = __builtin_amdgcn_mfma_f32_16x16x4f32(xkr, ykc, dL, 0, 0, 0);
+        dA = __builtin_amdgcn_mfma_f32_16x16x4f32(ykc, xqr, dA, 0, 0, 0);
+      }
+    }
+    // keep L strictly below the diagonal and Aqk on and below it
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * gq + r;
+      if (!(row > t)) dL[r] = 0.f;   // L tile: lane column j = t, row i
+      if (!(row <= t)) dA[r] = 0.f;  // Aqk^T tile: lane column i = t, row j
+    }
+  } else {
+    // exact at any gate depth: pairs in different 4-token groups use the end of the
+    // column group as reference; pairs inside a group use products of exp(g)
     const int grp = t >> 2;
     float gown[NE];
-    gend_row(4 * w + grp, gown);
-    f16x8 yg[KSK];  // khat_j * exp(Gend(group j) - G_j), one version per token
+    lane_row(gend, 4 * w + grp, gown);
+    f16x8 yg[KSK];  // khat_j * exp(Gend(group j) - G_j)
 #pragma unroll
     for (int s = 0; s < KSK; ++s)
 #pragma unroll
@@ -345,7 +451,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
 #pragma unroll
     for (int qg = 0; qg < 3; ++qg) {
       float gr[NE];
-      gend_row(4 * w + qg, gr);
+      lane_row(gend, 4 * w + qg, gr);
       const bool col_in = (grp == qg);   // this lane's token as a column of group qg
       const bool row_in = (grp > qg);    // this lane's token as a row after group qg
 #pragma unroll
@@ -362,10 +468,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
         dA = mfma16(ym, xq8, dA);
       }
     }
-  }
-  // diagonal tile, pairs inside one 4-token group at distance d = 1..3: reference r = j,
-  // factor exp(G_i - G_{i-d}) as a product of per-token decays exp(g)
-  {
     f32x4 bandL[3], bandA[3];
 #pragma unroll
     for (int d = 0; d < 3; ++d) { bandL[d] = zero4(); bandA[d] = zero4(); }
@@ -448,19 +550,17 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
       }
     }
   }
-  __syncthreads();  // #5: L complete; column operands and K~^T consumed
+  __syncthreads();  // #5: L complete; column operands and table consumed
 
-  // transposed fp16 operands of the W and U products: beta_j khat_j exp(G_j) and beta_j v_j 2^ue
+  // Bw^T fragments through identity products (rows = key channels, tokens in pi order)
 #pragma unroll
-  for (int e = 0; e < NE; ++e) {
-    const int ch = 32 * (e >> 3) + pi_index(gq, e & 7);
-    bwT[ch * PT + i_loc] = (_Float16)(bt * xk[e] * exp2_hw(G[e]));
-  }
+  for (int s = 0; s < KSK; ++s)
 #pragma unroll
-  for (int e = 0; e < NEV; ++e) {
-    const int ch = 32 * (e >> 3) + pi_index(gq, e & 7);
-    buT[ch * PT + i_loc] = (_Float16)(bt * ldexpf(xv[e], ue));
-  }
+    for (int hh = 0; hh < 2; ++hh) {
+      const f32x4 c = mfma16(bwr[s], ident[hh], zero4());
+      f16x4 h4 = {(_Float16)c[0], (_Float16)c[1], (_Float16)c[2], (_Float16)c[3]};
+      *reinterpret_cast<f16x4*>(bwx + ((size_t)((2 * s + hh) * 2 + (w >> 1)) * 64 + l) * 16 + (w & 1) * 8) = h4;
+    }
 
   // ---------------- (b) Tinv = (I + A)^-1, blocked ----------------
   if (l < 16) {  // diagonal block w, column c = l, forward substitution
@@ -510,17 +610,19 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
 
   // ---------------- (b) W = Tinv Bw (as W^T tiles) and U = Tinv Bu ----------------
   {
-    constexpr int NTK = DK / 16;
-    constexpr int NTV = DV / 16;
     const int nks = (w >= 2) ? 2 : 1;  // Tinv rows of block w vanish beyond column 16w+15
+    // Tinv row 16w + t at the tokens of the pi-ordered slots of step s
     f16x8 tf[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int jb = 32 * s + 8 * gq;
-      const bool keep = ((jb >> 4) <= w);
-      const float* trow = Tm + (16 * w + t) * LP + jb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) tf[s][e] = (_Float16)(keep ? trow[e] : 0.f);
+      const float* trow = Tm + (16 * w + t) * LP + 32 * s + 4 * gq;
+      const float4 lo = *reinterpret_cast<const float4*>(trow);
+      const float4 hi = *reinterpret_cast<const float4*>(trow + 16);
+      const bool klo = (2 * s <= w), khi = (2 * s + 1 <= w);
+      tf[s][0] = (_Float16)(klo ? lo.x : 0.f); tf[s][1] = (_Float16)(klo ? lo.y : 0.f);
+      tf[s][2] = (_Float16)(klo ? lo.z : 0.f); tf[s][3] = (_Float16)(klo ? lo.w : 0.f);
+      tf[s][4] = (_Float16)(khi ? hi.x : 0.f); tf[s][5] = (_Float16)(khi ? hi.y : 0.f);
+      tf[s][6] = (_Float16)(khi ? hi.z : 0.f); tf[s][7] = (_Float16)(khi ? hi.w : 0.f);
     }
 #pragma unroll
     for (int sk = 0; sk < KSK; ++sk) {
@@ -528,8 +630,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         if (s < nks) {
-          const f16x8 a0 = *reinterpret_cast<const f16x8*>(bwT + (32 * sk + t) * PT + 32 * s + 8 * gq);
-          const f16x8 a1 = *reinterpret_cast<const f16x8*>(bwT + (32 * sk + 16 + t) * PT + 32 * s + 8 * gq);
+          const f16x8 a0 = *reinterpret_cast<const f16x8*>(bwx + ((size_t)((2 * sk) * 2 + s) * 64 + l) * 16);
+          const f16x8 a1 = *reinterpret_cast<const f16x8*>(bwx + ((size_t)((2 * sk + 1) * 2 + s) * 64 + l) * 16);
           c0 = mfma16(a0, tf[s], c0);
           c1 = mfma16(a1, tf[s], c1);
         }
@@ -544,14 +646,34 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         if (s < nks) {
-          const f16x8 bfr = *reinterpret_cast<const f16x8*>(buT + (16 * nt + t) * PT + 32 * s + 8 * gq);
+          const f16x8 bfr = *reinterpret_cast<const f16x8*>(bux + ((size_t)(nt * 2 + s) * 64 + l) * 16);
           c = mfma16(tf[s], bfr, c);
         }
       }
       f16x4 uf = {(_Float16)c[0], (_Float16)c[1], (_Float16)c[2], (_Float16)c[3]};
       *reinterpret_cast<f16x4*>(rec + R::U + ((size_t)(w * NTV + nt) * 64 + l) * 8) = uf;
     }
-    (void)NTK;
+  }
+}
+
+// Fast variant, one workgroup per (chunk, head).
+template <int DK, int DV, typename InT>
+__global__ __launch_bounds__(256, 2) void chunk_prep_kernel(PrepArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int chunk = blockIdx.x;
+  if (chunk >= a.info[0]) return;  // uniform for the workgroup
+  prep_item<DK, DV, InT, false>(a, chunk, (int)blockIdx.y, smem);
+}
+
+// Exact variant over the chunks the fast variant deferred.
+template <int DK, int DV, typename InT>
+__global__ __launch_bounds__(256) void chunk_prep_exact_kernel(PrepArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int n = *a.defer_count;
+  for (int i = blockIdx.x; i < n; i += gridDim.x) {
+    const int item = a.defer_list[i];
+    prep_item<DK, DV, InT, true>(a, item / a.H, item % a.H, smem);
+    __syncthreads();  // LDS is rewritten by the next item
   }
 }
 
