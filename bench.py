@@ -98,16 +98,21 @@ def traffic_from_profiles(kernel):
         rec = json.load(open(path))
     except ValueError:
         return None
-    if rec.get("source_sha256") != csrc_hash():
-        return None
     k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    if k is None or k.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    return k.get("hbm_bytes_per_launch")
 
 
-def csrc_hash():
+KERNEL_SOURCES = {"chunk_prep_kernel": ["kda_device.h", "kda_prep.h"],
+                  "state_scan_kernel": ["kda_device.h", "kda_scan.h"]}
+
+
+def kernel_source_hash(kernel):
+    """sha256 over the source files that define `kernel` (counters go stale when they change)."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "gated_delta_rule_39_amd", "csrc")
-    for name in sorted(os.listdir(d)):
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(d, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -182,8 +187,8 @@ def main():
     K, W = args.steps, args.warmup
     marks = []
     for _ in range(K):
-        row = (ctypes.c_void_p * 4)()
-        for j in range(4):
+        row = (ctypes.c_void_p * 5)()
+        for j in range(5):
             e = ctypes.c_void_p()
             if hip.hipEventCreate(ctypes.byref(e)) != 0:
                 raise RuntimeError("hipEventCreate failed")
@@ -216,12 +221,13 @@ def main():
 
     k_map = np.mean([elapsed(m[0], m[1]) for m in marks])
     k_prep = np.mean([elapsed(m[1], m[2]) for m in marks])
-    k_scan = np.mean([elapsed(m[2], m[3]) for m in marks])
+    k_exact = np.mean([elapsed(m[2], m[3]) for m in marks])
+    k_scan = np.mean([elapsed(m[3], m[4]) for m in marks])
     for m in marks:
-        for j in range(4):
+        for j in range(5):
             hip.hipEventDestroy(m[j])
     log("timed %d steps: %.4f ms/step (wall %.4f ms/step); kernels: chunk map %.4f ms, chunk %.4f ms, "
-        "scan %.4f ms" % (K, ms_per_step, 1e3 * t_wall / K, k_map, k_prep, k_scan))
+        "exact chunk %.4f ms, scan %.4f ms" % (K, ms_per_step, 1e3 * t_wall / K, k_map, k_prep, k_exact, k_scan))
 
     tokens = B * T
     value = tokens / (ms_per_step * 1e-3)
@@ -300,7 +306,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": dom_bytes},
         "kernels_ms": {"chunk_map": round(float(k_map), 5), "chunk_prep": round(float(k_prep), 5),
-                       "state_scan": round(float(k_scan), 5)},
+                       "chunk_prep_exact": round(float(k_exact), 5), "state_scan": round(float(k_scan), 5)},
         "mfma": {"flops_per_step": total_flops,
                  "frac_of_peak": round(total_flops / (ms_per_step * 1e-3) / (MFMA_F16_PEAK_TFLOPS * 1e12), 5),
                  "peak_tflops": MFMA_F16_PEAK_TFLOPS},

@@ -14,6 +14,10 @@ size_t record_bytes(int dk, int dv) {
   return 0;
 }
 
+static void mark(const ForwardPlan& p, int i, hipStream_t stream) {
+  if (p.marks[i]) hipEventRecord(p.marks[i], stream);
+}
+
 template <int DK, int DV, typename InT>
 static hipError_t launch_prep(const ForwardPlan& p, hipStream_t stream) {
   PrepArgs a;
@@ -32,6 +36,7 @@ static hipError_t launch_prep(const ForwardPlan& p, hipStream_t stream) {
   hipLaunchKernelGGL(fast, dim3((unsigned)p.n_chunk_ub, (unsigned)p.H), dim3(256), smem, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  mark(p, 2, stream);
   // the exact variant walks the deferred list (usually empty: its workgroups exit at once)
   int dev = 0, cus = 0;
   hipGetDevice(&dev);
@@ -65,20 +70,18 @@ static hipError_t launch_scan(const ForwardPlan& p, hipStream_t stream) {
   }
 }
 
-static void mark(const ForwardPlan& p, int i, hipStream_t stream) {
-  if (p.marks[i]) hipEventRecord(p.marks[i], stream);
-}
-
 template <int DK, int DV>
 static hipError_t launch_dkdv(const ForwardPlan& p, hipStream_t stream) {
   hipError_t e = hipSuccess;
   if (p.T_total > 0) {
     e = (p.dtype == 0) ? launch_prep<DK, DV, uint16_t>(p, stream) : launch_prep<DK, DV, float>(p, stream);
     if (e != hipSuccess) return e;
+  } else {
+    mark(p, 2, stream);
   }
-  mark(p, 2, stream);
-  e = (p.dtype == 0) ? launch_scan<DK, DV, uint16_t>(p, stream) : launch_scan<DK, DV, float>(p, stream);
   mark(p, 3, stream);
+  e = (p.dtype == 0) ? launch_scan<DK, DV, uint16_t>(p, stream) : launch_scan<DK, DV, float>(p, stream);
+  mark(p, 4, stream);
   return e;
 }
 

@@ -30,7 +30,7 @@ struct ForwardPlan {
   uint8_t* rec;
   int32_t* defer_list;  // [n_chunk_ub * H] chunks handed to the exact chunk kernel
   int32_t slice;  // value columns per scan workgroup (16, 32 or 64)
-  hipEvent_t marks[4];  // optional timing marks around the kernels (may be null)
+  hipEvent_t marks[5];  // optional timing marks around the kernels (may be null)
 };
 
 // Bytes of one per-(chunk, head) record.

@@ -1,0 +1,103 @@
+"""Host-side checks of the C ABI (include/kda.h): the library loads, exports every
+declared function, and kda_fwd_validate / kda_fwd_workspace_size return the
+documented status codes.  No GPU is touched: these entry points only inspect
+sizes, pointer values and alignment (addresses below are never dereferenced)."""
+import ctypes
+import math
+
+import pytest
+
+kda = pytest.importorskip("gated_delta_rule_39_amd.kda")
+
+GB = 1 << 30
+OK, NULL, UNSUP, BAD, ALIGN, WS, ALIAS = 0, 1, 2, 3, 4, 5, 6
+
+
+def test_library_exports_every_declared_function():
+    names = kda.declared_functions()
+    assert set(names) >= {"kda_fwd", "kda_fwd_timed", "kda_fwd_validate", "kda_fwd_workspace_size",
+                          "kda_status_string", "kda_version"}
+    lib = kda.library()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert kda.version() >= 100
+    for code in range(8):
+        assert kda.library().kda_status_string(code)
+
+
+def _args(B=1, T=200, H=2, dk=64, dv=64, dtype=kda.KDA_BF16, packed_n=0):
+    prob = kda.make_problem(B, T, H, dk, dv, dtype, packed_n)
+    base = {n: (i + 1) * GB for i, n in enumerate(["q", "k", "v", "g", "beta", "h0", "cu", "out", "ht", "ws"])}
+    wsb = kda.library().kda_fwd_workspace_size(ctypes.byref(prob))
+    return prob, base, wsb
+
+
+def _validate(prob, p, wsb, scale=0.125, cu=False):
+    P = lambda n: None if p.get(n) is None else ctypes.c_void_p(p[n])
+    return kda.library().kda_fwd_validate(ctypes.byref(prob), P("q"), P("k"), P("v"), P("g"), P("beta"), P("h0"),
+                                          P("cu") if cu else None, ctypes.c_float(scale), P("out"), P("ht"),
+                                          P("ws"), ctypes.c_size_t(wsb))
+
+
+def test_valid_fixed_and_packed_problems():
+    prob, p, wsb = _args()
+    assert wsb > 0
+    assert _validate(prob, p, wsb) == OK
+    prob, p, wsb = _args(B=1, T=500, packed_n=7)
+    assert _validate(prob, p, wsb, cu=True) == OK
+    p["h0"] = None
+    p["ht"] = None
+    assert _validate(prob, p, wsb, cu=True) == OK  # NULL h0 and ht are allowed
+
+
+def test_workspace_size_rules():
+    lib = kda.library()
+    size = lambda *a: lib.kda_fwd_workspace_size(ctypes.byref(kda.make_problem(*a)))
+    assert size(1, 8192, 32, 96, 128, 0, 0) == 0  # unsupported head size
+    assert size(1, 8192, 32, 128, 128, 7, 0) == 0  # unknown dtype
+    assert size(1, 8192, 32, 128, 128, 0, 0) > size(1, 4096, 32, 128, 128, 0, 0) > 0
+    assert size(1, 8192, 32, 128, 128, 0, 50) >= size(1, 8192, 32, 128, 128, 0, 0)
+
+
+def test_null_unsupported_and_bad_arguments():
+    prob, p, wsb = _args()
+    for n in ["q", "k", "v", "g", "beta", "out", "ws"]:
+        p2 = dict(p)
+        p2[n] = None
+        assert _validate(prob, p2, wsb) == NULL, n
+    assert kda.library().kda_fwd_validate(None, *([None] * 7), ctypes.c_float(1.0), None, None, None,
+                                          ctypes.c_size_t(0)) == NULL
+    for dk, dv in [(32, 64), (64, 96), (256, 128)]:
+        prob2, p2, _ = _args(dk=dk, dv=dv)
+        assert _validate(prob2, p2, 1 << 40) == UNSUP
+    prob2, p2, w2 = _args(dtype=5)
+    assert _validate(prob2, p2, 1 << 40) == UNSUP
+    assert _validate(prob, p, wsb, scale=math.inf) == BAD
+    assert _validate(prob, p, wsb, scale=math.nan) == BAD
+    prob2, p2, w2 = _args(B=2, T=100, packed_n=3)  # packed mode needs B == 1
+    assert _validate(prob2, p2, 1 << 40, cu=True) == BAD
+    prob2, p2, w2 = _args(B=2, T=100, packed_n=3)  # fixed mode: num_seqs must be 0 or B
+    assert _validate(prob2, p2, 1 << 40) == BAD
+    prob2 = kda.make_problem(1, -5, 2, 64, 64, 0, 0)
+    assert _validate(prob2, p, 1 << 40) == BAD
+
+
+def test_alignment_workspace_and_aliasing():
+    prob, p, wsb = _args()
+    for n in ["q", "v", "g", "h0", "out", "ht", "ws"]:
+        p2 = dict(p)
+        p2[n] += 8
+        assert _validate(prob, p2, wsb) == ALIGN, n
+    assert _validate(prob, p, wsb - 1) == WS
+    p2 = dict(p)
+    p2["out"] = p2["q"] + 1024  # out overlaps q
+    assert _validate(prob, p2, wsb) == ALIAS
+    p2 = dict(p)
+    p2["ht"] = p2["h0"]  # in-place state update is allowed
+    assert _validate(prob, p2, wsb) == OK
+    p2 = dict(p)
+    p2["ht"] = p2["h0"] + 256  # partial overlap is not
+    assert _validate(prob, p2, wsb) == ALIAS
+    p2 = dict(p)
+    p2["ht"] = p2["ws"] + 4096  # state written into the workspace
+    assert _validate(prob, p2, wsb) == ALIAS
