@@ -34,7 +34,7 @@ bool sizes_ok(const kda_problem_t* p, bool packed, int64_t* N, int64_t* n_chunk_
     *n_chunk_ub = p->batch * ((p->seqlen + kChunkTokens - 1) / kChunkTokens);
   }
   // grid limits: chunks and scan workgroups must fit the launch dimensions
-  if (*n_chunk_ub > 0x7fffffffLL || *N * (int64_t)p->heads * 8 > 0x7fffffffLL) return false;
+  if (*n_chunk_ub * (int64_t)p->heads > 0x7fffffffLL || *N * (int64_t)p->heads * 8 > 0x7fffffffLL) return false;
   // int32 token offsets inside the packed table; 64-bit element offsets elsewhere
   if (packed && p->seqlen > 0x7fffffffLL) return false;
   return true;

@@ -33,7 +33,7 @@ static hipError_t launch_prep(const ForwardPlan& p, hipStream_t stream) {
   auto exact = chunk_prep_exact_kernel<DK, DV, InT>;
   hipFuncSetAttribute(reinterpret_cast<const void*>(fast), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   hipFuncSetAttribute(reinterpret_cast<const void*>(exact), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  hipLaunchKernelGGL(fast, dim3((unsigned)p.n_chunk_ub, (unsigned)p.H), dim3(256), smem, stream, a);
+  hipLaunchKernelGGL(fast, dim3((unsigned)(p.n_chunk_ub * p.H)), dim3(256), smem, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   mark(p, 2, stream);

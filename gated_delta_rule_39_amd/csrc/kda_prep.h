@@ -656,13 +656,15 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   }
 }
 
-// Fast variant, one workgroup per (chunk, head).
+// Fast variant, one workgroup per (chunk, head).  The head is the fastest grid
+// index: workgroups that run together read whole token rows (all heads) of q, k,
+// v and g, and write adjacent records.
 template <int DK, int DV, typename InT>
 __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(PrepArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int chunk = blockIdx.x;
+  const int chunk = (int)(blockIdx.x / (unsigned)a.H);
   if (chunk >= a.info[0]) return;  // uniform for the workgroup
-  prep_item<DK, DV, InT, false>(a, chunk, (int)blockIdx.y, smem);
+  prep_item<DK, DV, InT, false>(a, chunk, (int)(blockIdx.x % (unsigned)a.H), smem);
 }
 
 // Exact variant over the chunks the fast variant deferred.

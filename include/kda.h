@@ -63,6 +63,8 @@ typedef enum {
  *     tokens each; num_seqs must be 0 or equal to batch.
  *   Packed mode (cu_seqlens != NULL): batch == 1, `seqlen` is the total
  *     number of tokens and `num_seqs` >= 1 the number of packed sequences.
+ *   Limits (KDA_ERR_BAD_ARG beyond them): (64-token chunks) x heads and
+ *   8 x sequences x heads below 2^31; packed seqlen below 2^31.
  */
 typedef struct {
   int64_t batch;    /* B */
