@@ -184,7 +184,7 @@ static kda_status_t forward(const kda_problem_t* prob, const void* q, const void
   p.seq_off = reinterpret_cast<int32_t*>(ws + c.seq_off);
   p.seq_order = reinterpret_cast<int32_t*>(ws + c.seq_order);
   p.rec = ws + c.rec;
-  p.defer_list = reinterpret_cast<int32_t*>(ws + c.defer);
+  p.defer_mask = reinterpret_cast<uint32_t*>(ws + c.defer);
   p.slice = slice_width(prob, N);
   for (int i = 0; i < 5; ++i) p.marks[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
   hipError_t e = kda::launch_forward(p, static_cast<hipStream_t>(stream));

@@ -26,25 +26,25 @@ static hipError_t launch_prep(const ForwardPlan& p, hipStream_t stream) {
   a.info = p.info;
   a.table = reinterpret_cast<const ChunkEntry*>(p.table);
   a.rec = p.rec;
-  a.defer_count = p.info + 2;
-  a.defer_list = p.defer_list;
+  a.defer_mask = p.defer_mask;
   const size_t smem = PrepSmem<DK, DV>::BYTES;
   auto fast = chunk_prep_kernel<DK, DV, InT>;
   auto exact = chunk_prep_exact_kernel<DK, DV, InT>;
   hipFuncSetAttribute(reinterpret_cast<const void*>(fast), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   hipFuncSetAttribute(reinterpret_cast<const void*>(exact), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  hipLaunchKernelGGL(fast, dim3((unsigned)(p.n_chunk_ub * p.H)), dim3(256), smem, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  mark(p, 2, stream);
-  // the exact variant walks the deferred list (usually empty: its workgroups exit at once)
+  // persistent workgroups, one per compute unit (the LDS footprint admits one)
   int dev = 0, cus = 0;
   hipGetDevice(&dev);
   hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   int64_t grid = cus > 0 ? cus : 256;
   const int64_t items = p.n_chunk_ub * (int64_t)p.H;
   if (grid > items) grid = items;
-  hipLaunchKernelGGL(exact, dim3((unsigned)grid), dim3(256), smem, stream, a);
+  hipLaunchKernelGGL(fast, dim3((unsigned)grid), dim3(kPrepThreads), smem, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  mark(p, 2, stream);
+  // the exact variant walks the deferred items (usually none: its workgroups exit at once)
+  hipLaunchKernelGGL(exact, dim3((unsigned)grid), dim3(kPrepThreads), smem, stream, a);
   return hipGetLastError();
 }
 
@@ -89,7 +89,8 @@ hipError_t launch_forward(const ForwardPlan& p, hipStream_t stream) {
   if (p.N <= 0) return hipSuccess;
   mark(p, 0, stream);
   hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kMapThreads), 0, stream, p.cu, p.T, p.N, p.n_chunk_ub,
-                     p.info, reinterpret_cast<ChunkEntry*>(p.table), p.seq_off, p.seq_order);
+                     p.info, reinterpret_cast<ChunkEntry*>(p.table), p.seq_off, p.seq_order, p.defer_mask,
+                     (p.n_chunk_ub * (int64_t)p.H + 31) / 32);
   mark(p, 1, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -28,7 +28,7 @@ struct ForwardPlan {
   int32_t* seq_off;
   int32_t* seq_order;
   uint8_t* rec;
-  int32_t* defer_list;  // [n_chunk_ub * H] chunks handed to the exact chunk kernel
+  uint32_t* defer_mask;  // bit (chunk * H + head) set: the item goes to the exact chunk kernel
   int32_t slice;  // value columns per scan workgroup (16, 32 or 64)
   hipEvent_t marks[5];  // optional timing marks around the kernels (may be null)
 };

@@ -1,5 +1,5 @@
 // Chunk kernel: everything about a 64-token chunk that does not depend on
-// the recurrent state, for one (chunk, head) per workgroup of 4 waves.
+// the recurrent state, for one (chunk, head) at a time per workgroup.
 //
 // The chunkwise form of the gated delta rule ("Autoresearch on Kimi Delta
 // Attention", section "KDA in one minute": the state moves sequentially
@@ -12,17 +12,27 @@
 //     Aqk_ij = sum_c qhat_ic khat_jc exp(G_ic - G_jc)          (j <= i)
 // so that the scan kernel can finish the chunk with Delta = U - W S0,
 // o = scale (Qhat*exp(G) S0 + Aqk Delta) and
-// S_next = Diag(exp(G_last)) S0 + (Khat*exp(G_last - G))^T Delta.
+// S_next = Diag(exp(G_last)) S0 + (Khat*exp(G_last-G))^T Delta.
 //
 // This kernel produces, per (chunk, head): the fragments of W, Qhat*exp(G),
 // (Khat*exp(G_last-G))^T, Aqk, U (scaled by 2^ue), exp(G_last), max|v| and ue.
 //
+// Work split: a workgroup of 8 waves takes one (chunk, head) at a time; wave
+// (w, hf) holds tokens 16w..16w+15 and one half (hf) of the key and value
+// channels.  Channel-wise steps need no exchange; the two places that sum
+// over all channels (the L2 norms and the Gram matrices) add the two halves'
+// partial sums through LDS.  The workgroups are persistent: while one item is
+// computed, the raw inputs of the next are already on their way into
+// registers, so the HBM latency of the loads is hidden behind the arithmetic.
+//
 // Steps, each exact up to rounding for every legal input:
 //  (a) Real L2 norms of q and k per token ("Kernel Design Agents (KDA)
 //      optimize Kimi Delta Attention (KDA)", section "03 - Reward hacking":
-//      a distribution constant in place of the norm was rejected).  The sum
-//      of squares is taken after an exact power-of-two rescale by the
-//      largest entry, so entries up to the bf16/fp32 maximum cannot overflow.
+//      a distribution constant in place of the norm was rejected).  Each
+//      half's sum of squares is taken after an exact power-of-two rescale by
+//      that half's largest entry, and the halves are brought to a common
+//      exponent before they are added, so entries up to the bf16/fp32
+//      maximum cannot overflow.
 //  (a) In-chunk cumulative log-gate G, kept in fp32 and in log2 units
 //      (the same section rejects an fp16 table of decays and decays formed
 //      as ratios of cumulative powers that underflow past 126 bits).
@@ -36,7 +46,7 @@
 //      decay; when D <= 80 nats on every channel of all four diagonal tiles
 //      (checked per chunk and head) each tile is one fp32 MFMA product.
 //      Otherwise the chunk is handed to the exact variant of this kernel
-//      (a second launch over the deferred list), which uses per-4-token
+//      (a second launch over the deferred items), which uses per-4-token
 //      column-group references plus exp(g) products inside each group, on
 //      fp16 MFMA, exact at any depth.
 //  (b) Tinv by blocked forward substitution in fp32 (16x16 diagonal blocks by
@@ -56,6 +66,8 @@
 #include "kda_device.h"
 
 namespace kda {
+
+constexpr int kPrepThreads = 512;  // 8 waves: 4 token blocks x 2 channel halves
 
 template <int DK, int DV>
 struct PrepSmem {
@@ -78,8 +90,10 @@ struct PrepSmem {
   static constexpr size_t Y = X + X_BYTES;        // L (strict lower) + inverse temporaries (upper)
   static constexpr size_t Z = Y + MAT;            // decay-factor table -> Tinv
   static constexpr size_t GE = Z + Z_BYTES;       // G (log2 units) at the 16 group ends
-  static constexpr size_t BETA = GE + 16 * DK * 4;
-  static constexpr size_t RED = BETA + 64 * 4;
+  static constexpr size_t GP = GE + 16 * DK * 4;  // Gram partial tiles: [L | Aqk^T][block w][tile b][lane] x 4 fp32
+  static constexpr size_t NRM = GP + 2 * 16 * 64 * 16;  // norm partials: [exp | sum][tensor 2][half 2][token 64]
+  static constexpr size_t BETA = NRM + 2 * 2 * 2 * 64 * 4;
+  static constexpr size_t RED = BETA + 64 * 4;    // [8] max |v| per wave, then the guard flag
   static constexpr size_t BYTES = RED + 16 * 4;
 };
 
@@ -96,9 +110,159 @@ struct PrepArgs {
   const int32_t* info;
   const ChunkEntry* table;
   uint8_t* rec;     // records [n_chunk_ub][H]
-  int32_t* defer_count;  // chunks handed to the exact variant (zeroed by the chunk map)
-  int32_t* defer_list;   // their items chunk * H + head
+  uint32_t* defer_mask;  // bit (chunk * H + head): item handed to the exact variant (cleared by the chunk map)
 };
+
+// Four consecutive input elements as loaded (bf16 pairs or fp32).
+template <typename InT> struct Raw4;
+template <> struct Raw4<uint16_t> { using T = uint2; };
+template <> struct Raw4<float> { using T = float4; };
+
+__device__ inline void unpack4(const uint2& r, float* o) {
+  o[0] = __uint_as_float(r.x << 16);
+  o[1] = __uint_as_float(r.x & 0xffff0000u);
+  o[2] = __uint_as_float(r.y << 16);
+  o[3] = __uint_as_float(r.y & 0xffff0000u);
+}
+__device__ inline void unpack4(const float4& r, float* o) { o[0] = r.x; o[1] = r.y; o[2] = r.z; o[3] = r.w; }
+__device__ inline float unpack1(uint16_t b) { return bf16_to_f32(b); }
+__device__ inline float unpack1(float b) { return b; }
+
+// One lane's raw inputs of one (chunk, head): token 16w + t, channels of half hf,
+// in groups of four at 16 j + 4 gq inside the half.
+template <int DK, int DV, typename InT>
+struct RawIn {
+  static constexpr int KH = DK / 64;  // 32-wide key steps per half
+  static constexpr int VH = DV / 64;  // 32-wide value steps per half
+  using V4 = typename Raw4<InT>::T;
+  V4 q[2 * KH], k[2 * KH], v[2 * VH];
+  float4 g[2 * KH];
+  InT beta;
+  bool valid;
+};
+
+// The same inputs as fp32 (g in log2 units): x[4 j + r] is channel (half base) + 16 j + 4 gq + r.
+template <int DK, int DV>
+struct ItemIn {
+  float q[DK / 8], k[DK / 8], g[DK / 8], v[DV / 8];
+  float beta;
+};
+
+// Scalar-unit reads (through the constant cache, counted by lgkmcnt) of data that no
+// kernel of this launch writes: the chunk table and cu_seqlens.  Read this way, the
+// per-item metadata never waits behind the record stores on the vector-memory counter.
+// Both need a wave-uniform address aligned to 4 bytes.
+__device__ __forceinline__ uint32_t sload_u32(const void* p) {
+  uint32_t r;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
+  return r;
+}
+__device__ __forceinline__ uint64_t sload_u64(const void* p) {
+  uint64_t r;
+  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
+  return r;
+}
+__device__ __forceinline__ ChunkEntry ld_entry(const ChunkEntry* p) {
+  const uint64_t sl = sload_u64(p);
+  ChunkEntry e;
+  e.seq = (int32_t)(uint32_t)sl;
+  e.len = (int32_t)(uint32_t)(sl >> 32);
+  e.idx = (int32_t)sload_u32(reinterpret_cast<const int32_t*>(p) + 2);
+  e.pad = 0;
+  return e;
+}
+
+// Element offsets of one lane's inputs of an item (chunk, h).  Lanes past the chunk's
+// end read token 0 instead (the kernel runs only when there are tokens) and are
+// zeroed when unpacked.
+struct RawAt {
+  size_t rowk;  // q, k, g: token row + half base + 4 gq
+  size_t rowv;  // v
+  size_t bidx;  // beta
+  bool valid;
+};
+
+template <int DK, int DV>
+__device__ __forceinline__ RawAt raw_at(const PrepArgs& a, const ChunkEntry& ce, int h) {
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int w = wv & 3, hf = wv >> 2, l = tid & 63, t = l & 15, gq = l >> 4;
+  const int i_loc = 16 * w + t;
+  const int64_t s0 = a.cu ? (int64_t)(int32_t)sload_u32(a.cu + ce.seq) : (int64_t)ce.seq * a.T;
+  const int64_t start = s0 + (int64_t)ce.idx * kChunk;
+  const int64_t tok = start + i_loc;
+  RawAt at;
+  at.valid = (i_loc < ce.len) && (tok >= 0) && (tok < a.T_total);
+  const int64_t tk = at.valid ? tok : 0;
+  at.rowk = ((size_t)tk * a.H + h) * DK + hf * (DK / 2) + 4 * gq;
+  at.rowv = ((size_t)tk * a.H + h) * DV + hf * (DV / 2) + 4 * gq;
+  at.bidx = (size_t)tk * a.H + h;
+  return at;
+}
+
+// Issues one group of an item's loads: 0 = q, k, beta; 1 = g; 2 = v.  The groups are
+// issued at different points of the previous item so that the loads of all compute
+// units do not reach HBM in one burst.
+template <int PART, int DK, int DV, typename InT>
+__device__ __forceinline__ void load_part(RawIn<DK, DV, InT>& r, const PrepArgs& a, const RawAt& at) {
+  using RI = RawIn<DK, DV, InT>;
+  using V4 = typename RI::V4;
+  if (PART == 0) {
+    const InT* q = reinterpret_cast<const InT*>(a.q);
+    const InT* k = reinterpret_cast<const InT*>(a.k);
+#pragma unroll
+    for (int j = 0; j < 2 * RI::KH; ++j) {
+      r.q[j] = *reinterpret_cast<const V4*>(q + at.rowk + 16 * j);
+      r.k[j] = *reinterpret_cast<const V4*>(k + at.rowk + 16 * j);
+    }
+    r.beta = reinterpret_cast<const InT*>(a.beta)[at.bidx];
+    r.valid = at.valid;
+  } else if (PART == 1) {
+#pragma unroll
+    for (int j = 0; j < 2 * RI::KH; ++j) r.g[j] = *reinterpret_cast<const float4*>(a.g + at.rowk + 16 * j);
+  } else {
+    const InT* v = reinterpret_cast<const InT*>(a.v);
+#pragma unroll
+    for (int j = 0; j < 2 * RI::VH; ++j) r.v[j] = *reinterpret_cast<const V4*>(v + at.rowv + 16 * j);
+  }
+}
+
+template <int DK, int DV, typename InT>
+__device__ __forceinline__ void load_raw(RawIn<DK, DV, InT>& r, const PrepArgs& a, const ChunkEntry& ce, int h) {
+  const RawAt at = raw_at<DK, DV>(a, ce, h);
+  load_part<0>(r, a, at);
+  load_part<1>(r, a, at);
+  load_part<2>(r, a, at);
+}
+
+template <int DK, int DV, typename InT>
+__device__ __forceinline__ void unpack_raw(ItemIn<DK, DV>& in, const RawIn<DK, DV, InT>& r) {
+  using RI = RawIn<DK, DV, InT>;
+#pragma unroll
+  for (int j = 0; j < 2 * RI::KH; ++j) {
+    unpack4(r.q[j], in.q + 4 * j);
+    unpack4(r.k[j], in.k + 4 * j);
+    unpack4(r.g[j], in.g + 4 * j);
+  }
+#pragma unroll
+  for (int j = 0; j < 2 * RI::VH; ++j) unpack4(r.v[j], in.v + 4 * j);
+  in.beta = unpack1(r.beta);
+#pragma unroll
+  for (int e = 0; e < DK / 8; ++e) in.g[e] *= kLog2e;  // gates in log2 units
+  // fresh definitions: later uses never wait on the vector-memory counter for them
+#pragma unroll
+  for (int e = 0; e < DK / 8; ++e) asm volatile("" : "+v"(in.q[e]), "+v"(in.k[e]), "+v"(in.g[e]));
+#pragma unroll
+  for (int e = 0; e < DV / 8; ++e) asm volatile("" : "+v"(in.v[e]));
+  asm volatile("" : "+v"(in.beta));
+  if (!r.valid) {
+#pragma unroll
+    for (int e = 0; e < DK / 8; ++e) in.q[e] = in.k[e] = in.g[e] = 0.f;
+#pragma unroll
+    for (int e = 0; e < DV / 8; ++e) in.v[e] = 0.f;
+    in.beta = 0.f;
+  }
+}
 
 // Decay-factor table rows (per key channel c, G in log2 units, Gend(p) = G at the end
 // of 4-token group p, block w = tokens 16w..16w+15):
@@ -108,18 +272,25 @@ struct PrepArgs {
 //   11..14  exp(Gprev(w) - Gmid(w))        Gmid(w) = Gend(4w+1)   (>= 1, used under the guard)
 //   15..18  exp(Gmid(w) - Gnext(w))        (>= 1, used under the guard)
 constexpr float kGuardLog2 = 115.0f;  // 80 nats: half-span limit of the fp32 diagonal path
+constexpr int kNoExp = -1000;         // exponent recorded for an all-zero half row
 
-// One (chunk, head).  EXACT = false: guarded fp32 diagonal tiles, the chunk is deferred
-// when the guard fails.  EXACT = true: per-group references on every diagonal tile.
-template <int DK, int DV, typename InT, bool EXACT>
-__device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, const int h, uint8_t* smem) {
+// One (chunk, head) from its fp32 inputs.  EXACT = false: guarded fp32 diagonal tiles,
+// the chunk is deferred when the guard fails.  EXACT = true: per-group references on
+// every diagonal tile.  Every wave of the workgroup calls it (it holds barriers).
+// `mid(1)` and `mid(2)` run right after barriers #2 and #4 (the persistent kernel
+// issues the next item's remaining loads there).
+template <int DK, int DV, bool EXACT, typename Mid>
+__device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, const int h, ItemIn<DK, DV>& in,
+                                          uint8_t* smem, Mid&& mid) {
   using R = Rec<DK, DV>;
   using SM = PrepSmem<DK, DV>;
   constexpr int KSK = DK / 32;   // contraction steps over key channels
   constexpr int KSV = DV / 32;
   constexpr int NTV = DV / 16;
-  constexpr int NE = KSK * 8;    // key channels held per lane
-  constexpr int NEV = KSV * 8;   // value channels held per lane
+  constexpr int KH = KSK / 2;    // key steps of one channel half
+  constexpr int VH = KSV / 2;    // value steps of one channel half
+  constexpr int NE = KH * 8;     // key channels held per lane
+  constexpr int NEV = VH * 8;    // value channels held per lane
   constexpr int LP = SM::LP;
 
   float* btot = reinterpret_cast<float*>(smem + SM::X);            // [4][DK]
@@ -130,33 +301,37 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   float* et = reinterpret_cast<float*>(smem + SM::Z);              // [19][DK]
   float* Tm = reinterpret_cast<float*>(smem + SM::Z);              // [64][LP]
   float* gend = reinterpret_cast<float*>(smem + SM::GE);           // [16][DK]
+  float* gpl = reinterpret_cast<float*>(smem + SM::GP);            // L partials [4][4][64][4]
+  float* gpa = gpl + 16 * 64 * 4;                                  // Aqk^T partials [4][4][64][4]
+  int* nrm_ex = reinterpret_cast<int*>(smem + SM::NRM);            // [2][2][64]
+  float* nrm_ss = reinterpret_cast<float*>(smem + SM::NRM) + 256;  // [2][2][64]
   float* sbeta = reinterpret_cast<float*>(smem + SM::BETA);        // [64]
   float* red = reinterpret_cast<float*>(smem + SM::RED);           // [8]
   int* guard = reinterpret_cast<int*>(smem + SM::RED) + 8;
 
-  const ChunkEntry ce = a.table[chunk];
-  const int64_t start = seq_start(a.cu, a.T, ce.seq) + (int64_t)ce.idx * kChunk;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
+  const int w = wv & 3;          // token block
+  const int hf = wv >> 2;        // channel half
   const int l = tid & 63;
   const int t = l & 15;
   const int gq = l >> 4;
   const int i_loc = 16 * w + t;  // this lane's token row inside the chunk
-  const int64_t tok = start + i_loc;
-  const bool valid = (i_loc < ce.len) && (tok < a.T_total);
+  const int cb = hf * (DK / 2);  // first key channel of the half
+  const int sb = hf * KH;        // first key step of the half
   uint8_t* rec = a.rec + ((size_t)chunk * a.H + h) * R::BYTES;
 
-  // reads the lane's NE channels of row `row` of a [*][DK] fp32 array in LDS
+  // reads the lane's NE channels (of this half) of row `row` of a [*][DK] fp32 array in LDS
   auto lane_row = [&](const float* base, int row, float* out) {
-    const float* p = base + row * DK;
+    const float* p = base + row * DK + cb;
 #pragma unroll
-    for (int j = 0; j < 2 * KSK; ++j) {
+    for (int j = 0; j < 2 * KH; ++j) {
       const float4 r4 = *reinterpret_cast<const float4*>(p + 16 * j + 4 * gq);
       out[4 * j + 0] = r4.x; out[4 * j + 1] = r4.y; out[4 * j + 2] = r4.z; out[4 * j + 3] = r4.w;
     }
   };
 
-  // reads the lane's 8 channels of k-step s of row `row` (indices 8 s .. 8 s + 7)
+  // reads the lane's 8 channels of (global) k-step s of row `row` (indices 8 s .. 8 s + 7)
   auto lane_step = [&](const float* base, int row, int s, float* out8) {
     const float* p = base + row * DK + 32 * s + 4 * gq;
     const float4 lo = *reinterpret_cast<const float4*>(p);
@@ -165,51 +340,24 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     out8[4] = hi.x; out8[5] = hi.y; out8[6] = hi.z; out8[7] = hi.w;
   };
 
-  // ---------------- (a) loads, norms, cumulative gate ----------------
-  // Lane (token 16w + t, quarter gq) holds channels 32 s + pi_index(gq, e) at index 8 s + e.
-  float xq[NE], xk[NE], G[NE], xv[NEV];
-  float bt = 0.f;
-  {
-    const InT* q = reinterpret_cast<const InT*>(a.q);
-    const InT* k = reinterpret_cast<const InT*>(a.k);
-    const InT* v = reinterpret_cast<const InT*>(a.v);
-    const InT* be = reinterpret_cast<const InT*>(a.beta);
-    const size_t rowk = ((size_t)tok * a.H + h) * DK;
-    const size_t rowv = ((size_t)tok * a.H + h) * DV;
-#pragma unroll
-    for (int j = 0; j < 2 * KSK; ++j) {
-      const int c0 = 16 * j + 4 * gq;
-      if (valid) {
-        load4(q + rowk + c0, xq + 4 * j);
-        load4(k + rowk + c0, xk + 4 * j);
-        load4(a.g + rowk + c0, G + 4 * j);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) xq[4 * j + r] = xk[4 * j + r] = G[4 * j + r] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 2 * KSV; ++j) {
-      if (valid) {
-        load4(v + rowv + 16 * j + 4 * gq, xv + 4 * j);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) xv[4 * j + r] = 0.f;
-      }
-    }
-    if (valid) bt = load1(be + (size_t)tok * a.H + h);
-  }
-  if (gq == 0) sbeta[i_loc] = bt;
+  // ---------------- (a) norms, cumulative gate ----------------
+  // Lane (token 16w + t, quarter gq) holds channels 32 (sb + s) + pi_index(gq, e) at index 8 s + e.
+  float* xq = in.q;
+  float* xk = in.k;
+  float* G = in.g;
+  float* xv = in.v;
+  const float bt = in.beta;
+  if (gq == 0 && hf == 0) sbeta[i_loc] = bt;
   if (tid == 0) *guard = 0;
 
-  // L2 normalisation (4 lanes share a token: lanes t, t+16, t+32, t+48)
-  auto normalise = [&](float* x) {
+  // half-row L2 norm partials (4 lanes share a token: lanes t, t+16, t+32, t+48)
+  auto half_norm = [&](float* x, int which, int& ex) {
     float m = 0.f;
 #pragma unroll
     for (int e = 0; e < NE; ++e) m = fmaxf(m, fabsf(x[e]));
     m = fmaxf(m, __shfl_xor(m, 16, 64));
     m = fmaxf(m, __shfl_xor(m, 32, 64));
-    const int ex = (m > 0.f) ? ilogbf(m) : 0;
+    ex = (m > 0.f) ? ilogbf(m) : kNoExp;
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
@@ -218,17 +366,30 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     }
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
-    const float rinv = (ss > 0.f) ? 1.0f / sqrtf(ss) : 0.f;
-#pragma unroll
-    for (int e = 0; e < NE; ++e) x[e] *= rinv;
+    if (gq == 0) {
+      nrm_ex[(which * 2 + hf) * 64 + i_loc] = ex;
+      nrm_ss[(which * 2 + hf) * 64 + i_loc] = ss;
+    }
+    return ss;
   };
-  normalise(xq);
-  normalise(xk);
+  // both halves at the larger exponent, then x * 2^(ex - exm) / ||row||
+  auto finish_norm = [&](float* x, int which, int ex, float ss) {
+    const int ex_p = nrm_ex[(which * 2 + (hf ^ 1)) * 64 + i_loc];
+    const float ss_p = nrm_ss[(which * 2 + (hf ^ 1)) * 64 + i_loc];
+    const int exm = ex > ex_p ? ex : ex_p;
+    const float tot = ldexpf(ss, 2 * (ex - exm)) + ldexpf(ss_p, 2 * (ex_p - exm));
+    const float f = (tot > 0.f) ? ldexpf(1.0f / sqrtf(tot), ex - exm) : 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) x[e] *= f;
+  };
+  int exq, exk;
+  const float ssq = half_norm(xq, 0, exq);
+  const float ssk = half_norm(xk, 1, exk);
 
   // cumulative log2-gate inside the 16-token block (rows of 16 lanes), then block offsets
 #pragma unroll
   for (int e = 0; e < NE; ++e) {
-    float x = G[e] * kLog2e;
+    float x = G[e];
     x += row_shr<1>(x);
     x += row_shr<2>(x);
     x += row_shr<4>(x);
@@ -237,44 +398,49 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   }
   if (t == 15) {
 #pragma unroll
-    for (int j = 0; j < 2 * KSK; ++j)
-      *reinterpret_cast<float4*>(btot + w * DK + 16 * j + 4 * gq) =
+    for (int j = 0; j < 2 * KH; ++j)
+      *reinterpret_cast<float4*>(btot + w * DK + cb + 16 * j + 4 * gq) =
           make_float4(G[4 * j], G[4 * j + 1], G[4 * j + 2], G[4 * j + 3]);
   }
   float vm = 0.f;
 #pragma unroll
   for (int e = 0; e < NEV; ++e) vm = fmaxf(vm, fabsf(xv[e]));
   vm = wave_max(vm);
-  if (l == 0) red[w] = vm;
-  __syncthreads();  // #1
+  if (l == 0) red[wv] = vm;
+  __syncthreads();  // #1: block totals, norm partials, max |v|
+  finish_norm(xq, 0, exq, ssq);
+  finish_norm(xk, 1, exk, ssk);
 #pragma unroll
-  for (int j = 0; j < 2 * KSK; ++j) {
+  for (int j = 0; j < 2 * KH; ++j) {
     // totals of the earlier 16-token blocks, added in block order
     float4 off = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int b = 0; b < 3; ++b) {
       if (b < w) {
-        const float4 bt4 = *reinterpret_cast<const float4*>(btot + b * DK + 16 * j + 4 * gq);
+        const float4 bt4 = *reinterpret_cast<const float4*>(btot + b * DK + cb + 16 * j + 4 * gq);
         off.x += bt4.x; off.y += bt4.y; off.z += bt4.z; off.w += bt4.w;
       }
     }
     G[4 * j + 0] += off.x; G[4 * j + 1] += off.y; G[4 * j + 2] += off.z; G[4 * j + 3] += off.w;
   }
-  const float vmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const int ue = (vmax > 0.f) ? 12 - (ilogbf(vmax) + 1) : 0;
-  // beta v 2^ue rows in fp16 (|.| < 2^12); the fp32 copy dies here
-  f16x8 vr[KSV];
+  float vmax = red[0];
 #pragma unroll
-  for (int s = 0; s < KSV; ++s)
+  for (int i = 1; i < 8; ++i) vmax = fmaxf(vmax, red[i]);
+  const int ue = (vmax > 0.f) ? 12 - (ilogbf(vmax) + 1) : 0;
+  // beta v 2^ue rows in fp16 (|.| < 2^12)
+  f16x8 vr[VH];
+#pragma unroll
+  for (int s = 0; s < VH; ++s)
 #pragma unroll
     for (int e = 0; e < 8; ++e) vr[s][e] = (_Float16)(bt * ldexpf(xv[8 * s + e], ue));
   if ((t & 3) == 3) {
 #pragma unroll
-    for (int j = 0; j < 2 * KSK; ++j)
-      *reinterpret_cast<float4*>(gend + (4 * w + (t >> 2)) * DK + 16 * j + 4 * gq) =
+    for (int j = 0; j < 2 * KH; ++j)
+      *reinterpret_cast<float4*>(gend + (4 * w + (t >> 2)) * DK + cb + 16 * j + 4 * gq) =
           make_float4(G[4 * j], G[4 * j + 1], G[4 * j + 2], G[4 * j + 3]);
   }
-  __syncthreads();  // #2: group-end gates visible, block totals consumed
+  __syncthreads();  // #2: group-end gates visible, block totals and norm partials consumed
+  mid(1);
 
   // decay-factor table and the guard of the fp32 diagonal path
   if (tid < DK) {
@@ -320,9 +486,12 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   }
   __syncthreads();  // #3: table and guard visible
   if (!EXACT) {
-    if (*guard) {  // a diagonal tile spans more decay than the fp32 path covers
-      if (tid == 0) a.defer_list[atomicAdd(a.defer_count, 1)] = chunk * a.H + h;
-      return;  // uniform for the workgroup
+    // A diagonal tile spans more decay than the fp32 path covers: the item is handed to
+    // the exact variant, which rewrites its record.  This variant still runs to the end
+    // (its record is overwritten), so every item issues the same memory operations.
+    if (*guard && tid == 0) {
+      const int item = chunk * a.H + h;
+      atomicOr(a.defer_mask + (item >> 5), 1u << (item & 31));  // no return value: no wait
     }
   }
 
@@ -335,20 +504,21 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
       ident[hh][e] = (_Float16)(((t >> 2) == gq && e == 4 * hh + (t & 3)) ? 1.f : 0.f);
 
   // ---------------- outputs that need only G ----------------
-  f16x8 bwr[KSK];
+  f16x8 bwr[KH];
   {
 #pragma unroll
-    for (int s = 0; s < KSK; ++s) {
+    for (int sl = 0; sl < KH; ++sl) {
+      const int s = sb + sl;
       float eS[8], eE[8];
       lane_step(et, w, s, eS);
       lane_step(et, 4 + w, s, eE);
       f16x8 qf, kf, y;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        qf[e] = (_Float16)(QB[8 * s + e] * eS[e]);          // qhat exp(G)
-        kf[e] = (_Float16)(YC[8 * s + e] * eE[e]);          // khat exp(G_last - G)
-        bwr[s][e] = (_Float16)(bt * XB[8 * s + e] * eS[e]); // beta khat exp(G)
-        y[e] = (_Float16)YC[8 * s + e];
+        qf[e] = (_Float16)(QB[8 * sl + e] * eS[e]);          // qhat exp(G)
+        kf[e] = (_Float16)(YC[8 * sl + e] * eE[e]);          // khat exp(G_last - G)
+        bwr[sl][e] = (_Float16)(bt * XB[8 * sl + e] * eS[e]); // beta khat exp(G)
+        y[e] = (_Float16)YC[8 * sl + e];
       }
       *reinterpret_cast<f16x8*>(rec + R::Q + ((size_t)(w * KSK + s) * 64 + l) * 16) = qf;
       // K~^T fragments: (K~ I) holds, per lane, key channel 16 ct + t at tokens 16 w + 4 gq + r
@@ -364,12 +534,13 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     }
     // Bu fragments (beta v 2^ue, rows = value channels, tokens in pi order)
 #pragma unroll
-    for (int s = 0; s < KSV; ++s) {
+    for (int svl = 0; svl < VH; ++svl) {
+      const int sv = hf * VH + svl;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const f32x4 c = mfma16(vr[s], ident[hh], zero4());
+        const f32x4 c = mfma16(vr[svl], ident[hh], zero4());
         f16x4 h4 = {(_Float16)c[0], (_Float16)c[1], (_Float16)c[2], (_Float16)c[3]};
-        *reinterpret_cast<f16x4*>(bux + ((size_t)((2 * s + hh) * 2 + (w >> 1)) * 64 + l) * 16 + (w & 1) * 8) = h4;
+        *reinterpret_cast<f16x4*>(bux + ((size_t)((2 * sv + hh) * 2 + (w >> 1)) * 64 + l) * 16 + (w & 1) * 8) = h4;
       }
     }
     if (tid < DK) reinterpret_cast<float*>(rec + R::LAM)[tid] = exp2_hw(gend[15 * DK + tid]);
@@ -379,9 +550,11 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     }
   }
   __syncthreads();  // #4: column operands visible
+  mid(2);
 
   // ---------------- (b) Gram matrices L (row block w) and Aqk^T (column block w) ----------------
-  // offL[b]: L tile (w, b) and offA[b]: Aqk^T tile (b, w) for b < w; dL, dA: the diagonal tiles
+  // Partial sums over this half's channels.  offL[b]: L tile (w, b) and offA[b]: Aqk^T
+  // tile (b, w) for b < w; dL, dA: the diagonal tiles.
   f32x4 offL[3], offA[3], dL = zero4(), dA = zero4();
 #pragma unroll
   for (int b = 0; b < 3; ++b) { offL[b] = zero4(); offA[b] = zero4(); }
@@ -393,7 +566,8 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     if (b < w) {
       const int trow = 8 + (b == 0 ? (w == 2 ? 0 : 1) : 2);
 #pragma unroll
-      for (int s = 0; s < KSK; ++s) {
+      for (int sl = 0; sl < KH; ++sl) {
+        const int s = sb + sl;
         float fr[8];
         if (b == w - 1) {
 #pragma unroll
@@ -404,8 +578,8 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
         f16x8 xk8, xq8;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          xk8[e] = (_Float16)(XB[8 * s + e] * fr[e]);
-          xq8[e] = (_Float16)(QB[8 * s + e] * fr[e]);
+          xk8[e] = (_Float16)(XB[8 * sl + e] * fr[e]);
+          xq8[e] = (_Float16)(QB[8 * sl + e] * fr[e]);
         }
         const f16x8 yb = ybf[(b * KSK + s) * 64 + l];
         offL[b] = mfma16(xk8, yb, offL[b]);
@@ -419,13 +593,14 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     // rows exp(G_i - G_m) = exp(G_i - Gprev) exp(Gprev - G_m),
     // columns exp(G_m - G_j) = exp(Gnext - G_j) exp(G_m - Gnext)
 #pragma unroll
-    for (int s = 0; s < KSK; ++s) {
+    for (int sl = 0; sl < KH; ++sl) {
+      const int s = sb + sl;
       float er[8], ec[8];
       lane_step(et, 11 + w, s, er);
       lane_step(et, 15 + w, s, ec);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float xkr = XB[8 * s + e] * er[e], xqr = QB[8 * s + e] * er[e], ykc = YC[8 * s + e] * ec[e];
+        const float xkr = XB[8 * sl + e] * er[e], xqr = QB[8 * sl + e] * er[e], ykc = YC[8 * sl + e] * ec[e];
         dL = __builtin_amdgcn_mfma_f32_16x16x4f32(xkr, ykc, dL, 0, 0, 0);
         dA = __builtin_amdgcn_mfma_f32_16x16x4f32(ykc, xqr, dA, 0, 0, 0);
       }
@@ -443,11 +618,11 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     const int grp = t >> 2;
     float gown[NE];
     lane_row(gend, 4 * w + grp, gown);
-    f16x8 yg[KSK];  // khat_j * exp(Gend(group j) - G_j)
+    f16x8 yg[KH];  // khat_j * exp(Gend(group j) - G_j)
 #pragma unroll
-    for (int s = 0; s < KSK; ++s)
+    for (int sl = 0; sl < KH; ++sl)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) yg[s][e] = (_Float16)(xk[8 * s + e] * exp2_hw(gown[8 * s + e] - G[8 * s + e]));
+      for (int e = 0; e < 8; ++e) yg[sl][e] = (_Float16)(xk[8 * sl + e] * exp2_hw(gown[8 * sl + e] - G[8 * sl + e]));
 #pragma unroll
     for (int qg = 0; qg < 3; ++qg) {
       float gr[NE];
@@ -455,14 +630,14 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
       const bool col_in = (grp == qg);   // this lane's token as a column of group qg
       const bool row_in = (grp > qg);    // this lane's token as a row after group qg
 #pragma unroll
-      for (int s = 0; s < KSK; ++s) {
+      for (int sl = 0; sl < KH; ++sl) {
         f16x8 xk8, xq8, ym;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float f = row_in ? exp2_hw(G[8 * s + e] - gr[8 * s + e]) : 0.f;
-          xk8[e] = (_Float16)(xk[8 * s + e] * f);
-          xq8[e] = (_Float16)(xq[8 * s + e] * f);
-          ym[e] = col_in ? yg[s][e] : (_Float16)0.f;
+          const float f = row_in ? exp2_hw(G[8 * sl + e] - gr[8 * sl + e]) : 0.f;
+          xk8[e] = (_Float16)(xk[8 * sl + e] * f);
+          xq8[e] = (_Float16)(xq[8 * sl + e] * f);
+          ym[e] = col_in ? yg[sl][e] : (_Float16)0.f;
         }
         dL = mfma16(xk8, ym, dL);
         dA = mfma16(ym, xq8, dA);
@@ -473,15 +648,15 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     for (int d = 0; d < 3; ++d) { bandL[d] = zero4(); bandA[d] = zero4(); }
     float adiag = 0.f;
 #pragma unroll
-    for (int s = 0; s < KSK; ++s) {
+    for (int sl = 0; sl < KH; ++sl) {
       f16x8 kk;
       float al[8], p1[8], p2[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float gi = G[8 * s + e];
+        const float gi = G[8 * sl + e];
         al[e] = exp2_hw(gi - row_shr<1>(gi));   // exp(g_i) (lane t-1 holds token i-1)
-        kk[e] = (_Float16)xk[8 * s + e];
-        adiag = fmaf(xq[8 * s + e], xk[8 * s + e], adiag);
+        kk[e] = (_Float16)xk[8 * sl + e];
+        adiag = fmaf(xq[8 * sl + e], xk[8 * sl + e], adiag);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -491,12 +666,12 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
       f16x8 k1, q1, k2, q2, k3, q3;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        k1[e] = (_Float16)(xk[8 * s + e] * al[e]);
-        q1[e] = (_Float16)(xq[8 * s + e] * al[e]);
-        k2[e] = (_Float16)(xk[8 * s + e] * p1[e]);
-        q2[e] = (_Float16)(xq[8 * s + e] * p1[e]);
-        k3[e] = (_Float16)(xk[8 * s + e] * p2[e]);
-        q3[e] = (_Float16)(xq[8 * s + e] * p2[e]);
+        k1[e] = (_Float16)(xk[8 * sl + e] * al[e]);
+        q1[e] = (_Float16)(xq[8 * sl + e] * al[e]);
+        k2[e] = (_Float16)(xk[8 * sl + e] * p1[e]);
+        q2[e] = (_Float16)(xq[8 * sl + e] * p1[e]);
+        k3[e] = (_Float16)(xk[8 * sl + e] * p2[e]);
+        q3[e] = (_Float16)(xq[8 * sl + e] * p2[e]);
       }
       bandL[0] = mfma16(k1, kk, bandL[0]);
       bandL[1] = mfma16(k2, kk, bandL[1]);
@@ -521,49 +696,81 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     }
   }
 
-  // Aqk A-fragments for row block w: slots (rows of Aqk^T tile (2 s2, w), rows of tile (2 s2 + 1, w))
-  auto aqkT_tile = [&](int b, int r) -> float {
-    float x = 0.f;
+  // tile b (<= w) of this wave's row block of L, or of its column block of Aqk^T
+  auto tileL = [&](int b) -> f32x4 {
+    f32x4 x = dL;
 #pragma unroll
-    for (int bb = 0; bb < 3; ++bb) x = (bb == b && b < w) ? offA[bb][r] : x;
-    return (b == w) ? dA[r] : x;
+    for (int bb = 0; bb < 3; ++bb) x = (bb == b && b < w) ? offL[bb] : x;
+    return x;
   };
+  auto tileA = [&](int b) -> f32x4 {
+    f32x4 x = dA;
 #pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2) {
-    f16x8 f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      f[r] = (_Float16)aqkT_tile(2 * s2, r);
-      f[4 + r] = (_Float16)aqkT_tile(2 * s2 + 1, r);
-    }
-    *reinterpret_cast<f16x8*>(rec + R::A + ((size_t)(w * 2 + s2) * 64 + l) * 16) = f;
-  }
-  // A = diag(beta) L into LDS (blocks (w, b <= w))
+    for (int bb = 0; bb < 3; ++bb) x = (bb == b && b < w) ? offA[bb] : x;
+    return x;
+  };
+  // The two halves' partial tiles meet in LDS: half 0 completes L, half 1 completes Aqk.
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     if (b <= w) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * w + 4 * gq + r;
-        const float lv = (b == w) ? dL[r] : offL[b < 3 ? b : 0][r];
-        Lm[i * LP + 16 * b + t] = sbeta[i] * lv;
-      }
+      float* dst = (hf == 1 ? gpl : gpa) + ((w * 4 + b) * 64 + l) * 4;
+      *reinterpret_cast<f32x4*>(dst) = (hf == 1) ? tileL(b) : tileA(b);
     }
   }
-  __syncthreads();  // #5: L complete; column operands and table consumed
+  __syncthreads();  // #5a: partial tiles visible; every wave is past the column operands
 
+  if (hf == 0) {
+    // A = diag(beta) L into LDS (blocks (w, b <= w))
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (b <= w) {
+        const f32x4 p = *reinterpret_cast<const f32x4*>(gpl + ((w * 4 + b) * 64 + l) * 4);
+        const f32x4 own = tileL(b);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * w + 4 * gq + r;
+          Lm[i * LP + 16 * b + t] = sbeta[i] * (own[r] + p[r]);
+        }
+      }
+    }
+  } else {
+    // Aqk A-fragments for row block w: slots (rows of Aqk^T tile (2 s2, w), rows of tile (2 s2 + 1, w))
+    f32x4 full[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      full[b] = zero4();
+      if (b <= w) {
+        const f32x4 p = *reinterpret_cast<const f32x4*>(gpa + ((w * 4 + b) * 64 + l) * 4);
+        const f32x4 own = tileA(b);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) full[b][r] = own[r] + p[r];
+      }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      f16x8 f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        f[r] = (_Float16)full[2 * s2][r];
+        f[4 + r] = (_Float16)full[2 * s2 + 1][r];
+      }
+      *reinterpret_cast<f16x8*>(rec + R::A + ((size_t)(w * 2 + s2) * 64 + l) * 16) = f;
+    }
+  }
   // Bw^T fragments through identity products (rows = key channels, tokens in pi order)
 #pragma unroll
-  for (int s = 0; s < KSK; ++s)
+  for (int sl = 0; sl < KH; ++sl)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const f32x4 c = mfma16(bwr[s], ident[hh], zero4());
+      const int s = sb + sl;
+      const f32x4 c = mfma16(bwr[sl], ident[hh], zero4());
       f16x4 h4 = {(_Float16)c[0], (_Float16)c[1], (_Float16)c[2], (_Float16)c[3]};
       *reinterpret_cast<f16x4*>(bwx + ((size_t)((2 * s + hh) * 2 + (w >> 1)) * 64 + l) * 16 + (w & 1) * 8) = h4;
     }
+  __syncthreads();  // #5: L complete; table consumed
 
   // ---------------- (b) Tinv = (I + A)^-1, blocked ----------------
-  if (l < 16) {  // diagonal block w, column c = l, forward substitution
+  if (hf == 0 && l < 16) {  // diagonal block w, column c = l, forward substitution
     const int c = l;
     float x[16];
 #pragma unroll
@@ -579,12 +786,13 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   }
   __syncthreads();  // #6
   // levels: Tinv_ab = -Tinv_aa * sum_{c=b}^{a-1} A_ac Tinv_cb, for a - b = 1, 2, 3.
-  // Z_ab goes to the free upper block (b, a) of the L buffer.
+  // Z_ab goes to the free upper block (b, a) of the L buffer.  The blocks of a level are
+  // shared out over the two 256-thread halves of the workgroup.
 #pragma unroll
   for (int lev = 1; lev <= 3; ++lev) {
     const int nblk = 4 - lev;
-    const int r = tid >> 4, col = tid & 15;
-    for (int m = 0; m < nblk; ++m) {
+    const int r = (tid >> 4) & 15, col = tid & 15, m0 = tid >> 8;
+    for (int m = m0; m < nblk; m += 2) {
       const int b = m, aa = m + lev;
       float z = 0.f;
       for (int c = b; c < aa; ++c) {
@@ -596,7 +804,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
       Lm[(16 * b + r) * LP + 16 * aa + col] = z;
     }
     __syncthreads();
-    for (int m = 0; m < nblk; ++m) {
+    for (int m = m0; m < nblk; m += 2) {
       const int b = m, aa = m + lev;
       const float* trow = Tm + (16 * aa + r) * LP + 16 * aa;
       const float* zcol = Lm + (16 * b) * LP + 16 * aa + col;
@@ -625,7 +833,8 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
       tf[s][6] = (_Float16)(khi ? hi.z : 0.f); tf[s][7] = (_Float16)(khi ? hi.w : 0.f);
     }
 #pragma unroll
-    for (int sk = 0; sk < KSK; ++sk) {
+    for (int skl = 0; skl < KH; ++skl) {
+      const int sk = sb + skl;
       f32x4 c0 = zero4(), c1 = zero4();
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -641,7 +850,8 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
       *reinterpret_cast<f16x8*>(rec + R::W + ((size_t)(w * KSK + sk) * 64 + l) * 16) = wf;
     }
 #pragma unroll
-    for (int nt = 0; nt < NTV; ++nt) {
+    for (int ntl = 0; ntl < NTV / 2; ++ntl) {
+      const int nt = hf * (NTV / 2) + ntl;
       f32x4 c = zero4();
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -656,26 +866,63 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   }
 }
 
-// Fast variant, one workgroup per (chunk, head).  The head is the fastest grid
-// index: workgroups that run together read whole token rows (all heads) of q, k,
-// v and g, and write adjacent records.
+// Fast variant: persistent workgroups walk the items (chunk, head), head fastest, so
+// that the workgroups in flight read whole token rows (all heads) of q, k, v and g and
+// write adjacent records.  The next item's loads are issued as soon as the current
+// item's inputs sit in registers.
+//
+// The loads of the next item are issued unconditionally (the last item re-reads its
+// own inputs) and unpacked after the current item's record stores, so that on every
+// path the same number of stores follows them: waiting for the loads then does not
+// wait for the stores (one in-order counter covers both).
 template <int DK, int DV, typename InT>
-__global__ __launch_bounds__(256, 2) void chunk_prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(kPrepThreads, 1) void chunk_prep_kernel(PrepArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int chunk = (int)(blockIdx.x / (unsigned)a.H);
-  if (chunk >= a.info[0]) return;  // uniform for the workgroup
-  prep_item<DK, DV, InT, false>(a, chunk, (int)(blockIdx.x % (unsigned)a.H), smem);
+  // items chunk * H + head (fewer than 2^31), kept in scalar registers
+  const int n_items = (int)sload_u32(a.info) * a.H;
+  int it = blockIdx.x;
+  if (it >= n_items) return;  // uniform for the workgroup
+  RawIn<DK, DV, InT> raw;
+  ItemIn<DK, DV> in;
+  load_raw(raw, a, ld_entry(a.table + it / a.H), it % a.H);
+  unpack_raw(in, raw);
+  for (;;) {
+    const int nx = __builtin_amdgcn_readfirstlane(it + (int)gridDim.x);
+    const int ld = nx < n_items ? nx : it;
+    const RawAt at = raw_at<DK, DV>(a, ld_entry(a.table + ld / a.H), ld % a.H);
+    load_part<0>(raw, a, at);
+    prep_item<DK, DV, false>(a, it / a.H, it % a.H, in, smem, [&](int phase) {
+      if (phase == 1) load_part<1>(raw, a, at);
+      if (phase == 2) load_part<2>(raw, a, at);
+    });
+    unpack_raw(in, raw);
+    __syncthreads();  // LDS is rewritten by the next item
+    if (nx >= n_items) break;
+    it = nx;
+  }
 }
 
-// Exact variant over the chunks the fast variant deferred.
+// Exact variant over the items the fast variant deferred: workgroup b scans the mask
+// words b, b + grid, ... and takes every item whose bit is set.
 template <int DK, int DV, typename InT>
-__global__ __launch_bounds__(256) void chunk_prep_exact_kernel(PrepArgs a) {
+__global__ __launch_bounds__(kPrepThreads, 1) void chunk_prep_exact_kernel(PrepArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int n = *a.defer_count;
-  for (int i = blockIdx.x; i < n; i += gridDim.x) {
-    const int item = a.defer_list[i];
-    prep_item<DK, DV, InT, true>(a, item / a.H, item % a.H, smem);
-    __syncthreads();  // LDS is rewritten by the next item
+  const int n_items = (int)sload_u32(a.info) * a.H;
+  const int n_words = (n_items + 31) >> 5;
+  for (int wd = blockIdx.x; wd < n_words; wd += gridDim.x) {
+    uint32_t bits = sload_u32(a.defer_mask + wd);
+    while (bits) {
+      const int b = __builtin_ctz(bits);
+      bits &= bits - 1;
+      const int item = wd * 32 + b;
+      const int chunk = item / a.H, h = item % a.H;
+      RawIn<DK, DV, InT> raw;
+      load_raw(raw, a, ld_entry(a.table + chunk), h);
+      ItemIn<DK, DV> in;
+      unpack_raw(in, raw);
+      prep_item<DK, DV, true>(a, chunk, h, in, smem, [](int) {});
+      __syncthreads();  // LDS is rewritten by the next item
+    }
   }
 }
 

@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void state_scan_kernel(ScanArgs a) {
       f32x4 o = oacc[nt];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) o = mfma16(dfr[s2][nt], cur.af[s2], o);
-      if (i_loc < len && tok < a.T_total) {
+      if (i_loc < len && tok >= 0 && tok < a.T_total) {
         float v4[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v4[r] = ldexpf(o[r], -es) * oscale;
