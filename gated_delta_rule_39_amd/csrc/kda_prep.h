@@ -589,20 +589,43 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   }
 
   if (!EXACT) {
-    // diagonal tile in one fp32 product around the tile's middle row m = 16w + 7:
+    // diagonal tile in one product around the tile's middle row m = 16w + 7:
     // rows exp(G_i - G_m) = exp(G_i - Gprev) exp(Gprev - G_m),
-    // columns exp(G_m - G_j) = exp(Gnext - G_j) exp(G_m - Gnext)
+    // columns exp(G_m - G_j) = exp(Gnext - G_j) exp(G_m - Gnext).
+    // Both half-span factors are >= 1; when every one of this wave's channels keeps
+    // them <= 2^11 the operands fit fp16 (|.| <= 2^11) and the tile takes two fp16
+    // MFMA steps, otherwise fp32 MFMA (factors up to the guard's 2^115).
+    float er[KH][8], ec[KH][8];
+    bool wide = false;
 #pragma unroll
     for (int sl = 0; sl < KH; ++sl) {
-      const int s = sb + sl;
-      float er[8], ec[8];
-      lane_step(et, 11 + w, s, er);
-      lane_step(et, 15 + w, s, ec);
+      lane_step(et, 11 + w, sb + sl, er[sl]);
+      lane_step(et, 15 + w, sb + sl, ec[sl]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float xkr = XB[8 * sl + e] * er[e], xqr = QB[8 * sl + e] * er[e], ykc = YC[8 * sl + e] * ec[e];
-        dL = __builtin_amdgcn_mfma_f32_16x16x4f32(xkr, ykc, dL, 0, 0, 0);
-        dA = __builtin_amdgcn_mfma_f32_16x16x4f32(ykc, xqr, dA, 0, 0, 0);
+      for (int e = 0; e < 8; ++e) wide |= (er[sl][e] > 2048.f) | (ec[sl][e] > 2048.f);
+    }
+    if (__any(wide)) {
+#pragma unroll
+      for (int sl = 0; sl < KH; ++sl)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xkr = XB[8 * sl + e] * er[sl][e], xqr = QB[8 * sl + e] * er[sl][e];
+          const float ykc = YC[8 * sl + e] * ec[sl][e];
+          dL = __builtin_amdgcn_mfma_f32_16x16x4f32(xkr, ykc, dL, 0, 0, 0);
+          dA = __builtin_amdgcn_mfma_f32_16x16x4f32(ykc, xqr, dA, 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+      for (int sl = 0; sl < KH; ++sl) {
+        f16x8 xk8, xq8, yc8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xk8[e] = (_Float16)(XB[8 * sl + e] * er[sl][e]);
+          xq8[e] = (_Float16)(QB[8 * sl + e] * er[sl][e]);
+          yc8[e] = (_Float16)(YC[8 * sl + e] * ec[sl][e]);
+        }
+        dL = mfma16(xk8, yc8, dL);
+        dA = mfma16(yc8, xq8, dA);
       }
     }
     // keep L strictly below the diagonal and Aqk on and below it
@@ -785,35 +808,62 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     for (int i = 0; i < 16; ++i) Tm[(16 * w + i) * LP + 16 * w + c] = x[i];
   }
   __syncthreads();  // #6
-  // levels: Tinv_ab = -Tinv_aa * sum_{c=b}^{a-1} A_ac Tinv_cb, for a - b = 1, 2, 3.
-  // Z_ab goes to the free upper block (b, a) of the L buffer.  The blocks of a level are
-  // shared out over the two 256-thread halves of the workgroup.
+  // Off-diagonal blocks by doubling, on fp32 MFMA (16x16 blocks, D_a = Tinv_aa):
+  //   inverse of a 32x32 half: [[D0, 0], [-D1 A10 D0, D1]]
+  //   inverse of the whole:    [[T1, 0], [-T2 A21 T1, T2]]   (T1, T2 the half inverses,
+  //                            A21 the lower-left 32x32 quarter of A)
+  // with Y = A21 T1 formed first.  Y goes to the free upper blocks of the L buffer.
+  {
+    float* Y00 = Lm + 0 * LP + 16;   // Y blocks (row block, column block) of A21 T1
+    float* Y01 = Lm + 0 * LP + 32;
+    float* Y10 = Lm + 0 * LP + 48;
+    float* Y11 = Lm + 16 * LP + 32;
+    auto blk = [&](float* base, int rb, int cb2) { return base + 16 * rb * LP + 16 * cb2; };
+    // c + Lf Rf with Lf read by rows from LDS and Rf either from LDS or a C-layout tile
+    auto mm_lds = [&](const float* Lf, const float* Rf, f32x4 c) {
+      const float4 lr = *reinterpret_cast<const float4*>(Lf + t * LP + 4 * gq);
+      const float lv[4] = {lr.x, lr.y, lr.z, lr.w};
 #pragma unroll
-  for (int lev = 1; lev <= 3; ++lev) {
-    const int nblk = 4 - lev;
-    const int r = (tid >> 4) & 15, col = tid & 15, m0 = tid >> 8;
-    for (int m = m0; m < nblk; m += 2) {
-      const int b = m, aa = m + lev;
-      float z = 0.f;
-      for (int c = b; c < aa; ++c) {
-        const float* arow = Lm + (16 * aa + r) * LP + 16 * c;
-        const float* tcol = Tm + (16 * c) * LP + 16 * b + col;
+      for (int p = 0; p < 4; ++p) c = __builtin_amdgcn_mfma_f32_16x16x4f32(lv[p], Rf[(4 * gq + p) * LP + t], c, 0, 0, 0);
+      return c;
+    };
+    auto mm_reg = [&](const float* Lf, const f32x4& Rc, f32x4 c) {
+      const float4 lr = *reinterpret_cast<const float4*>(Lf + t * LP + 4 * gq);
+      const float lv[4] = {lr.x, lr.y, lr.z, lr.w};
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) z = fmaf(arow[kk], tcol[kk * LP], z);
-      }
-      Lm[(16 * b + r) * LP + 16 * aa + col] = z;
+      for (int p = 0; p < 4; ++p) c = __builtin_amdgcn_mfma_f32_16x16x4f32(lv[p], Rc[p], c, 0, 0, 0);
+      return c;
+    };
+    auto put = [&](float* dst, const f32x4& c, float sgn) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(4 * gq + r) * LP + t] = sgn * c[r];
+    };
+    f32x4 y = zero4();
+    if (wv == 0) {         // T10 = -D1 A10 D0
+      const f32x4 pq = mm_lds(blk(Lm, 1, 0), blk(Tm, 0, 0), zero4());
+      put(blk(Tm, 1, 0), mm_reg(blk(Tm, 1, 1), pq, zero4()), -1.f);
+    } else if (wv == 1) {  // T32 = -D3 A32 D2
+      const f32x4 pq = mm_lds(blk(Lm, 3, 2), blk(Tm, 2, 2), zero4());
+      put(blk(Tm, 3, 2), mm_reg(blk(Tm, 3, 3), pq, zero4()), -1.f);
+    } else if (wv == 2) {  // Y01 = A21 D1
+      put(Y01, mm_lds(blk(Lm, 2, 1), blk(Tm, 1, 1), zero4()), 1.f);
+    } else if (wv == 3) {  // Y11 = A31 D1
+      put(Y11, mm_lds(blk(Lm, 3, 1), blk(Tm, 1, 1), zero4()), 1.f);
+    } else if (wv == 4) {  // Y00 = A20 D0 + A21 T10 (first term)
+      y = mm_lds(blk(Lm, 2, 0), blk(Tm, 0, 0), zero4());
+    } else if (wv == 5) {  // Y10 = A30 D0 + A31 T10 (first term)
+      y = mm_lds(blk(Lm, 3, 0), blk(Tm, 0, 0), zero4());
     }
-    __syncthreads();
-    for (int m = m0; m < nblk; m += 2) {
-      const int b = m, aa = m + lev;
-      const float* trow = Tm + (16 * aa + r) * LP + 16 * aa;
-      const float* zcol = Lm + (16 * b) * LP + 16 * aa + col;
-      float y = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk) y = fmaf(trow[kk], zcol[kk * LP], y);
-      Tm[(16 * aa + r) * LP + 16 * b + col] = -y;
-    }
-    __syncthreads();
+    __syncthreads();  // #7: T10, T32, Y01, Y11 visible
+    if (wv == 4) put(Y00, mm_lds(blk(Lm, 2, 1), blk(Tm, 1, 0), y), 1.f);
+    if (wv == 5) put(Y10, mm_lds(blk(Lm, 3, 1), blk(Tm, 1, 0), y), 1.f);
+    __syncthreads();  // #8: Y complete
+    // [T20 T21; T30 T31] = -[[D2, 0], [T32, D3]] Y
+    if (wv == 0) put(blk(Tm, 2, 0), mm_lds(blk(Tm, 2, 2), Y00, zero4()), -1.f);
+    if (wv == 1) put(blk(Tm, 2, 1), mm_lds(blk(Tm, 2, 2), Y01, zero4()), -1.f);
+    if (wv == 2) put(blk(Tm, 3, 0), mm_lds(blk(Tm, 3, 3), Y10, mm_lds(blk(Tm, 3, 2), Y00, zero4())), -1.f);
+    if (wv == 3) put(blk(Tm, 3, 1), mm_lds(blk(Tm, 3, 3), Y11, mm_lds(blk(Tm, 3, 2), Y01, zero4())), -1.f);
+    __syncthreads();  // #9: Tinv complete
   }
 
   // ---------------- (b) W = Tinv Bw (as W^T tiles) and U = Tinv Bu ----------------

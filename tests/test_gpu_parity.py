@@ -43,7 +43,9 @@ def test_head_sizes(dk, dv):
     _check(x, "dk=%d dv=%d" % (dk, dv))
 
 
-@pytest.mark.parametrize("gate", ["slow", "deep", "zero"])
+# slow: every diagonal tile on fp16; mid (about 17 bits of decay per half tile): the
+# fp32 diagonal tiles; deep (about 230 bits): the exact variant.
+@pytest.mark.parametrize("gate", ["slow", "mid", "deep", "zero"])
 def test_gate_regimes(gate):
     x = make_inputs(1, 300, 4, 128, 128, seed=7, dtype="bf16", gate=gate)
     _check(x, "gate=%s" % gate)

@@ -105,7 +105,7 @@ def make_inputs(B=1, T=64, H=2, dk=64, dv=64, *, seed=0, dtype="bf16", h0_std=0.
 
     q, k: N(0,1) times a per-token LogNormal(0, 0.5) scale; v ~ N(0,1);
     g = -exp(N(-2, 1)); beta = sigmoid(N(0,1)); h0 ~ N(0, h0_std) or None.
-    ``gate`` may be "base", "slow" (-1e-4), "deep" (-20) or "zero".
+    ``gate`` may be "base", "slow" (-1e-4), "mid" (-1.5), "deep" (-20) or "zero".
     """
     rng = np.random.default_rng(seed)
     q = _base_qk(rng, (B, T, H, dk))
@@ -115,6 +115,8 @@ def make_inputs(B=1, T=64, H=2, dk=64, dv=64, *, seed=0, dtype="bf16", h0_std=0.
         g = _base_gate(rng, (B, T, H, dk))
     elif gate == "slow":
         g = (-1e-4 * (1 + 0.01 * rng.standard_normal((B, T, H, dk)))).astype(np.float32)
+    elif gate == "mid":
+        g = (-1.5 * (1 + 0.01 * rng.standard_normal((B, T, H, dk)))).astype(np.float32)
     elif gate == "deep":
         g = (-20.0 * (1 + 0.01 * rng.standard_normal((B, T, H, dk)))).astype(np.float32)
     elif gate == "zero":
