@@ -57,7 +57,7 @@ static hipError_t launch_scan_nv(const ForwardPlan& p, hipStream_t stream) {
   const size_t smem = ScanSmem<DK, DV, NV>::BYTES;
   auto kern = state_scan_kernel<DK, DV, NV, OutT>;
   const int64_t blocks = p.N * (int64_t)p.H * (DV / NV);
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), smem, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kScanThreads), smem, stream, a);
   return hipGetLastError();
 }
 
@@ -65,8 +65,8 @@ template <int DK, int DV, typename OutT>
 static hipError_t launch_scan(const ForwardPlan& p, hipStream_t stream) {
   switch (p.slice) {
     case 16: return launch_scan_nv<DK, DV, 16, OutT>(p, stream);
-    case 64: return launch_scan_nv<DK, DV, 64, OutT>(p, stream);
-    default: return launch_scan_nv<DK, DV, 32, OutT>(p, stream);
+    case 32: return launch_scan_nv<DK, DV, 32, OutT>(p, stream);
+    default: return launch_scan_nv<DK, DV, 64, OutT>(p, stream);
   }
 }
 

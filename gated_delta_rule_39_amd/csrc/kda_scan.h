@@ -16,6 +16,16 @@
 // Boundaries come from the chunk table (built from cu_seqlens on the device);
 // the walk never drops history.
 //
+// Work split (8 waves): waves 0..3 each own a 16-token block of the chunk: they
+// hold that block's rows of W, Qhat*exp(G), Aqk and U, form its rows of Delta and
+// of the output.  Waves 4..7 each own DK/4 key channels of the state: they hold
+// the fp32 state rows and the matching rows of (Khat*exp(G_last-G))^T and
+// exp(G_last), and form S_next.  Each chunk factor is read from memory once per
+// workgroup.  Per chunk there are two barriers: A (Delta complete in LDS) and B
+// (S_next complete in LDS); the fp16 state copy is double buffered because the
+// token waves still read the chunk's S0 (for the output) while the key waves
+// write the next one.
+//
 // fp16 range: the state is linear in (v, h0).  For beta in [0, 1], g <= 0 and
 // unit keys, every column s of the state obeys ||s_t||^2 <= ||s_{t-1}||^2 + v_t^2,
 // hence ||s_t|| <= B = sqrt(max_col ||h0_col||^2 + L vmax^2) over a sequence of
@@ -27,6 +37,12 @@
 #include "kda_device.h"
 
 namespace kda {
+
+constexpr int kScanThreads = 512;  // 4 token-block waves + 4 key-block waves
+#ifndef KDA_SCAN_DEPTH
+#define KDA_SCAN_DEPTH 3
+#endif
+constexpr int kScanDepth = KDA_SCAN_DEPTH;  // chunks of factors held in registers (prefetch distance + 1)
 
 struct ScanArgs {
   const float* h0;
@@ -48,74 +64,103 @@ template <int DK, int DV, int NV>
 struct ScanSmem {
   static constexpr int KSK = DK / 32;
   static constexpr int NT = NV / 16;
-  static constexpr size_t SB = 0;                              // S fragments [KSK][NT][64] f16x8
-  static constexpr size_t DB = SB + (size_t)KSK * NT * 64 * 16;  // Delta fragments [2][NT][64] f16x8
-  static constexpr size_t CN = DB + (size_t)2 * NT * 64 * 16;    // column norms [4][NV]
-  static constexpr size_t RED = CN + 4 * NV * 4;                 // [8]
+  static constexpr size_t SBUF = (size_t)KSK * NT * 64 * 16;      // fp16 S0 fragments [KSK][NT][64] f16x8
+  static constexpr size_t SB = 0;                                  // two S0 buffers (chunk parity)
+  static constexpr size_t DB = SB + 2 * SBUF;                      // Delta fragments [2][NT][64] f16x8
+  static constexpr size_t CN = DB + (size_t)2 * NT * 64 * 16;      // column norm partials [4][NV]
+  static constexpr size_t RED = CN + 4 * NV * 4;                   // [8]
   static constexpr size_t BYTES = RED + 8 * 4;
 };
 
-template <int DK, int DV, int NV>
-struct ChunkRegs {
+// Chunk factors of one token-block wave: rows 16 i .. 16 i + 15 of W, Qhat*exp(G),
+// Aqk (A fragments) and the wave's slice of U (C-layout tiles).
+template <int DK, int NV>
+struct TokRegs {
   static constexpr int KSK = DK / 32;
-  static constexpr int TPW = DK / 64;  // 16-row state tiles owned by each wave
   static constexpr int NT = NV / 16;
   f16x8 wf[KSK];
   f16x8 qf[KSK];
   f16x8 af[2];
-  f16x8 kt[TPW][2];
   f16x4 uf[NT];
-  float4 lam[TPW];
   int ue;
 };
 
-template <int DK, int DV, int NV>
-__device__ inline void load_chunk(ChunkRegs<DK, DV, NV>& c, const uint8_t* rec, int w, int l, int slice) {
+// Chunk factors of one key-block wave: its row tiles of (Khat*exp(G_last-G))^T
+// (A fragments over the chunk's tokens) and exp(G_last).
+template <int DK>
+struct KeyRegs {
+  static constexpr int TPK = DK / 64;  // 16-row tiles per key wave
+  f16x8 kt[TPK][2];
+  float4 lam[TPK];
+};
+
+// The loads of a chunk's factors are issued in groups spread over the previous chunk's
+// step, so that the eight waves never queue all of them on the vector-memory path at
+// once.  Token waves: 0 = W, 1 = Qhat*exp(G), 2 = Aqk, U and ue.  Key waves: 0 = K~^T,
+// 1 = exp(G_last).
+template <int PART, int DK, int DV, int NV>
+__device__ __forceinline__ void load_tok(TokRegs<DK, NV>& c, const uint8_t* rec, int i, int l, int slice) {
   using R = Rec<DK, DV>;
-  using CR = ChunkRegs<DK, DV, NV>;
-  const int t = l & 15, gq = l >> 4;
+  using TR = TokRegs<DK, NV>;
+  if (PART == 0) {
 #pragma unroll
-  for (int s = 0; s < CR::KSK; ++s) {
-    c.wf[s] = *reinterpret_cast<const f16x8*>(rec + R::W + ((size_t)(w * CR::KSK + s) * 64 + l) * 16);
-    c.qf[s] = *reinterpret_cast<const f16x8*>(rec + R::Q + ((size_t)(w * CR::KSK + s) * 64 + l) * 16);
-  }
+    for (int s = 0; s < TR::KSK; ++s)
+      c.wf[s] = *reinterpret_cast<const f16x8*>(rec + R::W + ((size_t)(i * TR::KSK + s) * 64 + l) * 16);
+  } else if (PART == 1) {
 #pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2)
-    c.af[s2] = *reinterpret_cast<const f16x8*>(rec + R::A + ((size_t)(w * 2 + s2) * 64 + l) * 16);
-#pragma unroll
-  for (int m = 0; m < CR::TPW; ++m) {
-    const int ct = CR::TPW * w + m;
+    for (int s = 0; s < TR::KSK; ++s)
+      c.qf[s] = *reinterpret_cast<const f16x8*>(rec + R::Q + ((size_t)(i * TR::KSK + s) * 64 + l) * 16);
+  } else {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
-      c.kt[m][s2] = *reinterpret_cast<const f16x8*>(rec + R::KT + ((size_t)(ct * 2 + s2) * 64 + l) * 16);
-    c.lam[m] = *reinterpret_cast<const float4*>(rec + R::LAM + (size_t)(16 * ct + 4 * gq) * 4);
-  }
+      c.af[s2] = *reinterpret_cast<const f16x8*>(rec + R::A + ((size_t)(i * 2 + s2) * 64 + l) * 16);
 #pragma unroll
-  for (int nt = 0; nt < CR::NT; ++nt)
-    c.uf[nt] = *reinterpret_cast<const f16x4*>(
-        rec + R::U + ((size_t)(w * R::NTV + slice * CR::NT + nt) * 64 + l) * 8);
-  c.ue = reinterpret_cast<const int32_t*>(rec + R::HDR)[1];
-  (void)t;
+    for (int nt = 0; nt < TR::NT; ++nt)
+      c.uf[nt] = *reinterpret_cast<const f16x4*>(rec + R::U + ((size_t)(i * R::NTV + slice * TR::NT + nt) * 64 + l) * 8);
+    c.ue = reinterpret_cast<const int32_t*>(rec + R::HDR)[1];
+  }
+}
+
+template <int PART, int DK, int DV>
+__device__ __forceinline__ void load_key(KeyRegs<DK>& c, const uint8_t* rec, int m, int l) {
+  using R = Rec<DK, DV>;
+  using KR = KeyRegs<DK>;
+  const int gq = l >> 4;
+#pragma unroll
+  for (int p = 0; p < KR::TPK; ++p) {
+    const int ct = KR::TPK * m + p;
+    if (PART == 0) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        c.kt[p][s2] = *reinterpret_cast<const f16x8*>(rec + R::KT + ((size_t)(ct * 2 + s2) * 64 + l) * 16);
+    } else {
+      c.lam[p] = *reinterpret_cast<const float4*>(rec + R::LAM + (size_t)(16 * ct + 4 * gq) * 4);
+    }
+  }
 }
 
 template <int DK, int DV, int NV, typename OutT>
-__global__ __launch_bounds__(256) void state_scan_kernel(ScanArgs a) {
+__global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
   using R = Rec<DK, DV>;
   using SM = ScanSmem<DK, DV, NV>;
-  using CR = ChunkRegs<DK, DV, NV>;
+  using TR = TokRegs<DK, NV>;
+  using KR = KeyRegs<DK>;
   constexpr int KSK = DK / 32;
-  constexpr int TPW = DK / 64;
+  constexpr int TPK = DK / 64;
   constexpr int NT = NV / 16;
   constexpr int NS = DV / NV;
 
   extern __shared__ __align__(16) uint8_t smem[];
-  f16x8* sb = reinterpret_cast<f16x8*>(smem + SM::SB);
+  uint8_t* sbb = smem + SM::SB;
   uint8_t* db = smem + SM::DB;
   float* cn = reinterpret_cast<float*>(smem + SM::CN);
   float* red = reinterpret_cast<float*>(smem + SM::RED);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, t = l & 15, gq = l >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int l = tid & 63, t = l & 15, gq = l >> 4;
+  const bool tok_wave = wv < 4;
+  const int i = wv & 3;  // token block (tok_wave) or key block (otherwise)
   // Workgroups are dispatched round-robin over the 8 XCDs (block id mod 8).  The NS
   // slices of one (sequence, head) share every chunk factor except U, so they are
   // mapped to block ids with equal residue mod 8: one XCD's L2 serves all of them.
@@ -139,41 +184,46 @@ __global__ __launch_bounds__(256) void state_scan_kernel(ScanArgs a) {
   const int64_t L = seq_len(a.cu, a.T, n);
   const int64_t s0 = seq_start(a.cu, a.T, n);
   const int col0 = slice * NV;
-
-  // initial state (fp32, C layout: lane holds rows 16*tile + 4gq + r of column col0 + 16nt + t)
-  float S[TPW][NT][4];
   const size_t sbase = ((size_t)n * a.H + h) * DK * DV;
+
+  // fp32 state rows of a key wave (C layout: lane holds rows 16 ct + 4 gq + r of
+  // column col0 + 16 nt + t, ct = TPK * i + p)
+  float S[TPK][NT][4];
 #pragma unroll
-  for (int m = 0; m < TPW; ++m)
+  for (int p = 0; p < TPK; ++p)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = 16 * (TPW * w + m) + 4 * gq + r;
-        S[m][nt][r] = a.h0 ? a.h0[sbase + (size_t)row * DV + col0 + 16 * nt + t] : 0.f;
+        const int row = 16 * (TPK * i + p) + 4 * gq + r;
+        S[p][nt][r] = (!tok_wave && a.h0) ? a.h0[sbase + (size_t)row * DV + col0 + 16 * nt + t] : 0.f;
       }
 
   // power-of-two scale of the fp16 copies from the bound B (see the file comment)
   float vm = 0.f;
-  for (int64_t c = c0 + tid; c < c1; c += 256)
+  for (int64_t c = c0 + tid; c < c1; c += kScanThreads)
     vm = fmaxf(vm, reinterpret_cast<const float*>(a.rec + ((size_t)c * a.H + h) * R::BYTES + R::HDR)[0]);
   vm = wave_max(vm);
+  if (l == 0) red[wv] = vm;
+  if (!tok_wave) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float ss = 0.f;
+    for (int nt = 0; nt < NT; ++nt) {
+      float ss = 0.f;
 #pragma unroll
-    for (int m = 0; m < TPW; ++m)
+      for (int p = 0; p < TPK; ++p)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ss = fmaf(S[m][nt][r], S[m][nt][r], ss);
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
-    if (gq == 0) cn[w * NV + 16 * nt + t] = ss;
+        for (int r = 0; r < 4; ++r) ss = fmaf(S[p][nt][r], S[p][nt][r], ss);
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      if (gq == 0) cn[i * NV + 16 * nt + t] = ss;
+    }
   }
-  if (l == 0) red[w] = vm;
   __syncthreads();
   float cmax = 0.f;
   for (int j = 0; j < NV; ++j) cmax = fmaxf(cmax, cn[j] + cn[NV + j] + cn[2 * NV + j] + cn[3 * NV + j]);
-  const float vmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float vmax = red[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) vmax = fmaxf(vmax, red[j]);
   int es = 0;
   {
     const double b2 = (double)cmax + (double)L * (double)vmax * (double)vmax;
@@ -181,131 +231,172 @@ __global__ __launch_bounds__(256) void state_scan_kernel(ScanArgs a) {
     es = es < -250 ? -250 : (es > 250 ? 250 : es);
   }
 
-  auto write_state = [&]() {
+  // fp16 S0 fragments of k-step s, column tile nt: slot half (ct & 1) of [(ct / 2) * NT + nt]
+  auto write_state = [&](int buf) {
+    uint8_t* sb = sbb + (size_t)buf * SM::SBUF;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      if (TPW == 2) {
-        f16x8 f;
+    for (int p = 0; p < TPK; ++p) {
+      const int ct = TPK * i + p;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          f[r] = (_Float16)ldexpf(S[0][nt][r], es);
-          f[4 + r] = (_Float16)ldexpf(S[TPW - 1][nt][r], es);
-        }
-        sb[(w * NT + nt) * 64 + l] = f;
-      } else {
+      for (int nt = 0; nt < NT; ++nt) {
         f16x4 f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) f[r] = (_Float16)ldexpf(S[0][nt][r], es);
-        *reinterpret_cast<f16x4*>(reinterpret_cast<uint8_t*>(sb) +
-                                  (((size_t)(w >> 1) * NT + nt) * 64 + l) * 16 + (w & 1) * 8) = f;
+        for (int r = 0; r < 4; ++r) f[r] = (_Float16)ldexpf(S[p][nt][r], es);
+        *reinterpret_cast<f16x4*>(sb + (((size_t)(ct >> 1) * NT + nt) * 64 + l) * 16 + (ct & 1) * 8) = f;
       }
     }
   };
-  write_state();
-  __syncthreads();
+  if (!tok_wave) write_state(0);
+  __syncthreads();  // S0 of the first chunk visible
 
   OutT* out = reinterpret_cast<OutT*>(a.out);
   const float oscale = a.scale;
-
-  // One chunk step on the factors in `cur`.
-  auto step = [&](const CR& cur, int64_t c) {
-    // S0 fragments (B operand of W S0 and, read as A of S0^T, of the output)
-    f16x8 sf[KSK][NT];
-#pragma unroll
-    for (int s = 0; s < KSK; ++s)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sf[s][nt] = sb[(s * NT + nt) * 64 + l];
-
-    // Delta rows 16w..16w+15 (C layout: lane column = value column, rows = tokens 4gq + r)
-    f32x4 oacc[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 d = zero4();
-#pragma unroll
-      for (int s = 0; s < KSK; ++s) d = mfma16(cur.wf[s], sf[s][nt], d);
-      f16x4 df;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) df[r] = (_Float16)(ldexpf((float)cur.uf[nt][r], es - cur.ue) - d[r]);
-      *reinterpret_cast<f16x4*>(db + (((size_t)(w >> 1) * NT + nt) * 64 + l) * 16 + (w & 1) * 8) = df;
-      // o^T, inter-chunk part: S0^T (Qhat exp(G))^T
-      f32x4 o = zero4();
-#pragma unroll
-      for (int s = 0; s < KSK; ++s) o = mfma16(sf[s][nt], cur.qf[s], o);
-      oacc[nt] = o;
-    }
-    __syncthreads();
-
-    f16x8 dfr[2][NT];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        dfr[s2][nt] = *reinterpret_cast<const f16x8*>(db + (((size_t)s2 * NT + nt) * 64 + l) * 16);
-
-    // state update on the wave's key-channel rows
-#pragma unroll
-    for (int m = 0; m < TPW; ++m) {
-      const float lam[4] = {cur.lam[m].x, cur.lam[m].y, cur.lam[m].z, cur.lam[m].w};
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        f32x4 u = zero4();
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) u = mfma16(cur.kt[m][s2], dfr[s2][nt], u);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S[m][nt][r] = fmaf(lam[r], S[m][nt][r], ldexpf(u[r], -es));
-      }
-    }
-    write_state();
-
-    // o^T, intra-chunk part: Delta^T Aqk^T; then store 4 consecutive value columns per lane
-    const int64_t idx = c - c0;
-    const int64_t rem = L - idx * kChunk;
-    const int len = rem < kChunk ? (int)rem : kChunk;
-    const int i_loc = 16 * w + t;
-    const int64_t tok = s0 + idx * kChunk + i_loc;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 o = oacc[nt];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) o = mfma16(dfr[s2][nt], cur.af[s2], o);
-      if (i_loc < len && tok >= 0 && tok < a.T_total) {
-        float v4[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v4[r] = ldexpf(o[r], -es) * oscale;
-        store4(out + ((size_t)tok * a.H + h) * DV + col0 + 16 * nt + 4 * gq, v4);
-      }
-    }
-    __syncthreads();
-  };
-
-  // Ping-pong prefetch: the factors of chunk c+1 are requested (unconditionally; the
-  // last chunk is re-read at the end) before chunk c is processed.
   auto rec_of = [&](int64_t c) {
-    const int64_t cc = c < c1 ? c : c1 - 1;
+    const int64_t cc = c < c1 ? c : c1 - 1;  // past the end: the last chunk again (loaded, never used)
     return a.rec + ((size_t)cc * a.H + h) * R::BYTES;
   };
-  if (c0 < c1) {
-    CR bufA, bufB;
-    load_chunk<DK, DV, NV>(bufA, rec_of(c0), w, l, slice);
-    for (int64_t c = c0; c < c1; c += 2) {
-      load_chunk<DK, DV, NV>(bufB, rec_of(c + 1), w, l, slice);
-      step(bufA, c);
-      if (c + 1 >= c1) break;
-      load_chunk<DK, DV, NV>(bufA, rec_of(c + 2), w, l, slice);
-      step(bufB, c + 1);
-    }
-  }
 
-  if (a.ht) {
+  if (tok_wave) {
+    // ---- token block i: Delta rows, then the output rows ----
+    auto step = [&](const TR& cur, TR& nxt, const uint8_t* nrec, int64_t c) {
+      load_tok<0, DK, DV, NV>(nxt, nrec, i, l, slice);
+      const f16x8* sb = reinterpret_cast<const f16x8*>(sbb + (size_t)((c - c0) & 1) * SM::SBUF);
+      // all S0 fragments at once, so that the MFMA chains below never wait on LDS one by one
+      f16x8 sf[KSK][NT];
 #pragma unroll
-    for (int m = 0; m < TPW; ++m)
+      for (int s = 0; s < KSK; ++s)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+        for (int nt = 0; nt < NT; ++nt) sf[s][nt] = sb[(s * NT + nt) * 64 + l];
+      // Delta = U 2^(es - ue) - W S0 (rows 16 i.., C layout: lane column = value column)
+      f32x4 d[NT];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * (TPW * w + m) + 4 * gq + r;
-          a.ht[sbase + (size_t)row * DV + col0 + 16 * nt + t] = S[m][nt][r];
+      for (int nt = 0; nt < NT; ++nt) d[nt] = zero4();
+#pragma unroll
+      for (int s = 0; s < KSK; ++s)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) d[nt] = mfma16(cur.wf[s], sf[s][nt], d[nt]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        f16x4 df;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) df[r] = (_Float16)(ldexpf((float)cur.uf[nt][r], es - cur.ue) - d[nt][r]);
+        *reinterpret_cast<f16x4*>(db + (((size_t)(i >> 1) * NT + nt) * 64 + l) * 16 + (i & 1) * 8) = df;
+      }
+      load_tok<1, DK, DV, NV>(nxt, nrec, i, l, slice);
+      // o^T, inter-chunk part: S0^T (Qhat exp(G))^T
+      f32x4 o[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[nt] = zero4();
+#pragma unroll
+      for (int s = 0; s < KSK; ++s)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) o[nt] = mfma16(sf[s][nt], cur.qf[s], o[nt]);
+      __syncthreads();  // A: Delta complete
+      load_tok<2, DK, DV, NV>(nxt, nrec, i, l, slice);
+      // o^T, intra-chunk part: Delta^T Aqk^T; then 4 consecutive value columns per lane
+      f16x8 dfr[2][NT];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          dfr[s2][nt] = *reinterpret_cast<const f16x8*>(db + (((size_t)s2 * NT + nt) * 64 + l) * 16);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) o[nt] = mfma16(dfr[s2][nt], cur.af[s2], o[nt]);
+      const int64_t idx = c - c0;
+      const int64_t rem = L - idx * kChunk;
+      const int len = rem < kChunk ? (int)rem : kChunk;
+      const int i_loc = 16 * i + t;
+      const int64_t tok = s0 + idx * kChunk + i_loc;
+      if (i_loc < len && tok >= 0 && tok < a.T_total) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          float v4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v4[r] = ldexpf(o[nt][r], -es) * oscale;
+          store4(out + ((size_t)tok * a.H + h) * DV + col0 + 16 * nt + 4 * gq, v4);
         }
+      }
+      __syncthreads();  // B: next S0 complete
+    };
+    // Ring of kScanDepth register buffers: the factors of chunk c + kScanDepth - 1 are
+    // requested while chunk c is processed (the HBM latency spans several steps).
+    if (c0 < c1) {
+      TR buf[kScanDepth];
+#pragma unroll
+      for (int j = 0; j < kScanDepth - 1; ++j) {
+        load_tok<0, DK, DV, NV>(buf[j], rec_of(c0 + j), i, l, slice);
+        load_tok<1, DK, DV, NV>(buf[j], rec_of(c0 + j), i, l, slice);
+        load_tok<2, DK, DV, NV>(buf[j], rec_of(c0 + j), i, l, slice);
+      }
+      // whole groups of kScanDepth steps (no conditional step: the compiler's memory-counter
+      // waits then stay exact across iterations), then the remaining steps
+      int64_t c = c0;
+      for (; c + kScanDepth <= c1; c += kScanDepth) {
+#pragma unroll
+        for (int j = 0; j < kScanDepth; ++j)
+          step(buf[j], buf[(j + kScanDepth - 1) % kScanDepth], rec_of(c + j + kScanDepth - 1), c + j);
+      }
+#pragma unroll
+      for (int j = 0; j < kScanDepth - 1; ++j)
+        if (c + j < c1) step(buf[j], buf[(j + kScanDepth - 1) % kScanDepth], rec_of(c + j + kScanDepth - 1), c + j);
+    }
+  } else {
+    // ---- key block i: S_next = Diag(exp(G_last)) S0 + K~^T Delta ----
+    auto step = [&](const KR& cur, KR& nxt, const uint8_t* nrec, int64_t c) {
+      load_key<0, DK, DV>(nxt, nrec, i, l);
+      __syncthreads();  // A: Delta complete
+      f16x8 dfr[2][NT];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          dfr[s2][nt] = *reinterpret_cast<const f16x8*>(db + (((size_t)s2 * NT + nt) * 64 + l) * 16);
+#pragma unroll
+      for (int p = 0; p < TPK; ++p) {
+        const float lam[4] = {cur.lam[p].x, cur.lam[p].y, cur.lam[p].z, cur.lam[p].w};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          f32x4 u = zero4();
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) u = mfma16(cur.kt[p][s2], dfr[s2][nt], u);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S[p][nt][r] = fmaf(lam[r], S[p][nt][r], ldexpf(u[r], -es));
+        }
+      }
+      load_key<1, DK, DV>(nxt, nrec, i, l);
+      write_state((int)((c - c0 + 1) & 1));
+      __syncthreads();  // B: next S0 complete
+    };
+    if (c0 < c1) {
+      KR buf[kScanDepth];
+#pragma unroll
+      for (int j = 0; j < kScanDepth - 1; ++j) {
+        load_key<0, DK, DV>(buf[j], rec_of(c0 + j), i, l);
+        load_key<1, DK, DV>(buf[j], rec_of(c0 + j), i, l);
+      }
+      int64_t c = c0;
+      for (; c + kScanDepth <= c1; c += kScanDepth) {
+#pragma unroll
+        for (int j = 0; j < kScanDepth; ++j)
+          step(buf[j], buf[(j + kScanDepth - 1) % kScanDepth], rec_of(c + j + kScanDepth - 1), c + j);
+      }
+#pragma unroll
+      for (int j = 0; j < kScanDepth - 1; ++j)
+        if (c + j < c1) step(buf[j], buf[(j + kScanDepth - 1) % kScanDepth], rec_of(c + j + kScanDepth - 1), c + j);
+    }
+    if (a.ht) {
+#pragma unroll
+      for (int p = 0; p < TPK; ++p)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 16 * (TPK * i + p) + 4 * gq + r;
+            a.ht[sbase + (size_t)row * DV + col0 + 16 * nt + t] = S[p][nt][r];
+          }
+    }
   }
 }
 
