@@ -86,12 +86,15 @@ struct TokRegs {
 };
 
 // Chunk factors of one key-block wave: its row tiles of (Khat*exp(G_last-G))^T
-// (A fragments over the chunk's tokens) and exp(G_last).
+// (A fragments over the chunk's tokens) and exp(G_last), one value per lane: lane
+// (t, gq) holds channel 16 ct + 4 gq + (t & 3), and row broadcasts inside each row of
+// 16 lanes hand every lane its four C-layout rows 16 ct + 4 gq + r (a float4 per lane
+// would load each value sixteen times).
 template <int DK>
 struct KeyRegs {
   static constexpr int TPK = DK / 64;  // 16-row tiles per key wave
   f16x8 kt[TPK][2];
-  float4 lam[TPK];
+  float lam[TPK];
 };
 
 // The loads of a chunk's factors are issued in groups spread over the previous chunk's
@@ -134,7 +137,7 @@ __device__ __forceinline__ void load_key(KeyRegs<DK>& c, const uint8_t* rec, int
       for (int s2 = 0; s2 < 2; ++s2)
         c.kt[p][s2] = *reinterpret_cast<const f16x8*>(rec + R::KT + ((size_t)(ct * 2 + s2) * 64 + l) * 16);
     } else {
-      c.lam[p] = *reinterpret_cast<const float4*>(rec + R::LAM + (size_t)(16 * ct + 4 * gq) * 4);
+      c.lam[p] = *reinterpret_cast<const float*>(rec + R::LAM + (size_t)(16 * ct + 4 * gq + (l & 3)) * 4);
     }
   }
 }
@@ -355,7 +358,8 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
           dfr[s2][nt] = *reinterpret_cast<const f16x8*>(db + (((size_t)s2 * NT + nt) * 64 + l) * 16);
 #pragma unroll
       for (int p = 0; p < TPK; ++p) {
-        const float lam[4] = {cur.lam[p].x, cur.lam[p].y, cur.lam[p].z, cur.lam[p].w};
+        const float lam[4] = {row_bcast<0>(cur.lam[p]), row_bcast<1>(cur.lam[p]), row_bcast<2>(cur.lam[p]),
+                              row_bcast<3>(cur.lam[p])};  // rows 16 ct + 4 gq + r
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           f32x4 u = zero4();
