@@ -918,8 +918,8 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
 
 // Fast variant: persistent workgroups walk the items (chunk, head), head fastest, so
 // that the workgroups in flight read whole token rows (all heads) of q, k, v and g and
-// write adjacent records.  The next item's loads are issued as soon as the current
-// item's inputs sit in registers.
+// write adjacent records; chunks go from the last to the first.  The next item's loads
+// are issued as soon as the current item's inputs sit in registers.
 //
 // The loads of the next item are issued unconditionally (the last item re-reads its
 // own inputs) and unpacked after the current item's record stores, so that on every
@@ -934,14 +934,18 @@ __global__ __launch_bounds__(kPrepThreads, 1) void chunk_prep_kernel(PrepArgs a)
   if (it >= n_items) return;  // uniform for the workgroup
   RawIn<DK, DV, InT> raw;
   ItemIn<DK, DV> in;
-  load_raw(raw, a, ld_entry(a.table + it / a.H), it % a.H);
+  // chunks from the last to the first: the records the scan reads first are written last
+  // and are still in the caches (L2, MALL) when it starts
+  const int n_chunks = n_items / a.H;
+  auto chunk_of = [&](int x) { return n_chunks - 1 - x / a.H; };
+  load_raw(raw, a, ld_entry(a.table + chunk_of(it)), it % a.H);
   unpack_raw(in, raw);
   for (;;) {
     const int nx = __builtin_amdgcn_readfirstlane(it + (int)gridDim.x);
     const int ld = nx < n_items ? nx : it;
-    const RawAt at = raw_at<DK, DV>(a, ld_entry(a.table + ld / a.H), ld % a.H);
+    const RawAt at = raw_at<DK, DV>(a, ld_entry(a.table + chunk_of(ld)), ld % a.H);
     load_part<0>(raw, a, at);
-    prep_item<DK, DV, false>(a, it / a.H, it % a.H, in, smem, [&](int phase) {
+    prep_item<DK, DV, false>(a, chunk_of(it), it % a.H, in, smem, [&](int phase) {
       if (phase == 1) load_part<1>(raw, a, at);
       if (phase == 2) load_part<2>(raw, a, at);
     });
