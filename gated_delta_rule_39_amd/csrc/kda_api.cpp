@@ -75,6 +75,21 @@ int slice_width(const kda_problem_t* p, int64_t N) {
   return 16;
 }
 
+// Workgroups of the persistent chunk kernel: one per compute unit, or fewer when
+// KDA_CHUNK_WGS=n (n >= 1) asks for it (tuning, and tests of long per-workgroup walks).
+int chunk_workgroups() {
+  int dev = 0, cus = 0;
+  hipGetDevice(&dev);
+  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int n = cus > 0 ? cus : 256;
+  const char* env = std::getenv("KDA_CHUNK_WGS");
+  if (env) {
+    const int v = std::atoi(env);
+    if (v >= 1 && v < n) n = v;
+  }
+  return n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -186,6 +201,7 @@ static kda_status_t forward(const kda_problem_t* prob, const void* q, const void
   p.rec = ws + c.rec;
   p.defer_mask = reinterpret_cast<uint32_t*>(ws + c.defer);
   p.slice = slice_width(prob, N);
+  p.chunk_wgs = chunk_workgroups();
   for (int i = 0; i < 5; ++i) p.marks[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
   hipError_t e = kda::launch_forward(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;

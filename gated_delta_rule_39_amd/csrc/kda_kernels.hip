@@ -32,11 +32,8 @@ static hipError_t launch_prep(const ForwardPlan& p, hipStream_t stream) {
   auto exact = chunk_prep_exact_kernel<DK, DV, InT>;
   hipFuncSetAttribute(reinterpret_cast<const void*>(fast), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   hipFuncSetAttribute(reinterpret_cast<const void*>(exact), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  // persistent workgroups, one per compute unit (the LDS footprint admits one)
-  int dev = 0, cus = 0;
-  hipGetDevice(&dev);
-  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  int64_t grid = cus > 0 ? cus : 256;
+  // persistent workgroups, at most one per compute unit (the LDS footprint admits one)
+  int64_t grid = p.chunk_wgs > 0 ? p.chunk_wgs : 256;
   const int64_t items = p.n_chunk_ub * (int64_t)p.H;
   if (grid > items) grid = items;
   hipLaunchKernelGGL(fast, dim3((unsigned)grid), dim3(kPrepThreads), smem, stream, a);

@@ -30,6 +30,7 @@ struct ForwardPlan {
   uint8_t* rec;
   uint32_t* defer_mask;  // bit (chunk * H + head) set: the item goes to the exact chunk kernel
   int32_t slice;  // value columns per scan workgroup (16, 32 or 64)
+  int32_t chunk_wgs;  // workgroups of the persistent chunk kernel (>= 1)
   hipEvent_t marks[5];  // optional timing marks around the kernels (may be null)
 };
 

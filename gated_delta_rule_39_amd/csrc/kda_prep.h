@@ -94,7 +94,8 @@ struct PrepSmem {
   static constexpr size_t NRM = GP + 2 * 16 * 64 * 16;  // norm partials: [exp | sum][tensor 2][half 2][token 64]
   static constexpr size_t BETA = NRM + 2 * 2 * 2 * 64 * 4;
   static constexpr size_t RED = BETA + 64 * 4;    // [8] max |v| per wave, then the guard flag
-  static constexpr size_t BYTES = RED + 16 * 4;
+  static constexpr size_t META = RED + 16 * 4;    // [64] per-item (first token lo, hi, valid tokens, -)
+  static constexpr size_t BYTES = META + 64 * 16;
 };
 
 struct PrepArgs {
@@ -182,22 +183,27 @@ struct RawAt {
   bool valid;
 };
 
+// `start`: first token of the chunk in the flattened order, `len`: its valid tokens.
 template <int DK, int DV>
-__device__ __forceinline__ RawAt raw_at(const PrepArgs& a, const ChunkEntry& ce, int h) {
+__device__ __forceinline__ RawAt raw_at_tok(const PrepArgs& a, int64_t start, int len, int h) {
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int w = wv & 3, hf = wv >> 2, l = tid & 63, t = l & 15, gq = l >> 4;
   const int i_loc = 16 * w + t;
-  const int64_t s0 = a.cu ? (int64_t)(int32_t)sload_u32(a.cu + ce.seq) : (int64_t)ce.seq * a.T;
-  const int64_t start = s0 + (int64_t)ce.idx * kChunk;
   const int64_t tok = start + i_loc;
   RawAt at;
-  at.valid = (i_loc < ce.len) && (tok >= 0) && (tok < a.T_total);
+  at.valid = (i_loc < len) && (tok >= 0) && (tok < a.T_total);
   const int64_t tk = at.valid ? tok : 0;
   at.rowk = ((size_t)tk * a.H + h) * DK + hf * (DK / 2) + 4 * gq;
   at.rowv = ((size_t)tk * a.H + h) * DV + hf * (DV / 2) + 4 * gq;
   at.bidx = (size_t)tk * a.H + h;
   return at;
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ RawAt raw_at(const PrepArgs& a, const ChunkEntry& ce, int h) {
+  const int64_t s0 = a.cu ? (int64_t)(int32_t)sload_u32(a.cu + ce.seq) : (int64_t)ce.seq * a.T;
+  return raw_at_tok<DK, DV>(a, s0 + (int64_t)ce.idx * kChunk, ce.len, h);
 }
 
 // Issues one group of an item's loads: 0 = q, k, beta; 1 = g; 2 = v.  The groups are
@@ -273,6 +279,15 @@ __device__ __forceinline__ void unpack_raw(ItemIn<DK, DV>& in, const RawIn<DK, D
 //   15..18  exp(Gmid(w) - Gnext(w))        (>= 1, used under the guard)
 constexpr float kGuardLog2 = 115.0f;  // 80 nats: half-span limit of the fp32 diagonal path
 constexpr int kNoExp = -1000;         // exponent recorded for an all-zero half row
+
+// Step J.. of the substitution for a unit lower-triangular 16x16 block (see its caller):
+// x[r] += am[J] * (row J's x[r]), am = minus this lane's row of the strictly lower part.
+template <int J>
+__device__ __forceinline__ void subst_rows(float (&x)[4], const float (&am)[16]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x[r] = fmaf(am[J], row_bcast<J>(x[r]), x[r]);
+  if constexpr (J + 1 < 15) subst_rows<J + 1>(x, am);
+}
 
 // One (chunk, head) from its fp32 inputs.  EXACT = false: guarded fp32 diagonal tiles,
 // the chunk is deferred when the guard fails.  EXACT = true: per-group references on
@@ -793,19 +808,23 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   __syncthreads();  // #5: L complete; table consumed
 
   // ---------------- (b) Tinv = (I + A)^-1, blocked ----------------
-  if (hf == 0 && l < 16) {  // diagonal block w, column c = l, forward substitution
-    const int c = l;
-    float x[16];
+  if (hf == 0) {
+    // diagonal block w by substitution, one whole wave: lane (row i = t, quarter gq) holds
+    // Tinv[i][4 gq + r]; row j is final after the updates from rows 0..j-1 and is then
+    // broadcast along each row of 16 lanes to the rows below it (A is zero on and above
+    // the diagonal, so the other rows keep their values)
+    const float* arow = Lm + (16 * w + t) * LP + 16 * w;
+    float am[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float acc = (i == c) ? 1.f : 0.f;
-      const float* arow = Lm + (16 * w + i) * LP + 16 * w;
-#pragma unroll
-      for (int j = 0; j < i; ++j) acc = fmaf(-arow[j], x[j], acc);
-      x[i] = acc;
+    for (int q = 0; q < 4; ++q) {
+      const float4 a4 = *reinterpret_cast<const float4*>(arow + 4 * q);
+      am[4 * q + 0] = -a4.x; am[4 * q + 1] = -a4.y; am[4 * q + 2] = -a4.z; am[4 * q + 3] = -a4.w;
     }
+    float x[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) Tm[(16 * w + i) * LP + 16 * w + c] = x[i];
+    for (int r = 0; r < 4; ++r) x[r] = (t == 4 * gq + r) ? 1.f : 0.f;
+    subst_rows<0>(x, am);
+    *reinterpret_cast<float4*>(Tm + (16 * w + t) * LP + 16 * w + 4 * gq) = make_float4(x[0], x[1], x[2], x[3]);
   }
   __syncthreads();  // #6
   // Off-diagonal blocks by doubling, on fp32 MFMA (16x16 blocks, D_a = Tinv_aa):
@@ -932,26 +951,57 @@ __global__ __launch_bounds__(kPrepThreads, 1) void chunk_prep_kernel(PrepArgs a)
   const int n_items = (int)sload_u32(a.info) * a.H;
   int it = blockIdx.x;
   if (it >= n_items) return;  // uniform for the workgroup
-  RawIn<DK, DV, InT> raw;
-  ItemIn<DK, DV> in;
   // chunks from the last to the first: the records the scan reads first are written last
   // and are still in the caches (L2, MALL) when it starts
   const int n_chunks = n_items / a.H;
   auto chunk_of = [&](int x) { return n_chunks - 1 - x / a.H; };
-  load_raw(raw, a, ld_entry(a.table + chunk_of(it)), it % a.H);
+  // Where the chunks of this workgroup's first 64 items start and how many tokens they
+  // hold, staged in LDS (entry j: item blockIdx.x + j * gridDim.x) with one batch of
+  // vector loads: the next item's input loads then never wait behind dependent scalar
+  // metadata loads.  Later items (more than 64 per workgroup) read the chunk table.
+  int4* meta = reinterpret_cast<int4*>(smem + PrepSmem<DK, DV>::META);
+  if (threadIdx.x < 64) {
+    const int64_t item = (int64_t)blockIdx.x + (int64_t)threadIdx.x * gridDim.x;
+    int4 m = make_int4(0, 0, 0, 0);
+    if (item < n_items) {
+      const ChunkEntry e = a.table[chunk_of((int)item)];
+      const int64_t st = seq_start(a.cu, a.T, e.seq) + (int64_t)e.idx * kChunk;
+      m = make_int4((int32_t)(uint32_t)st, (int32_t)(st >> 32), e.len, 0);
+    }
+    meta[threadIdx.x] = m;
+  }
+  __syncthreads();
+  auto at_of = [&](int j, int item) {
+    if (j < 64) {
+      const int4 m = meta[j];  // same address in every lane
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(m.x);
+      const int32_t hi = __builtin_amdgcn_readfirstlane(m.y);
+      const int len = __builtin_amdgcn_readfirstlane(m.z);
+      return raw_at_tok<DK, DV>(a, (int64_t)(((uint64_t)(uint32_t)hi << 32) | lo), len, item % a.H);
+    }
+    return raw_at<DK, DV>(a, ld_entry(a.table + chunk_of(item)), item % a.H);
+  };
+  RawIn<DK, DV, InT> raw;
+  ItemIn<DK, DV> in;
+  {
+    const RawAt at = at_of(0, it);
+    load_part<0>(raw, a, at);
+    load_part<1>(raw, a, at);
+    load_part<2>(raw, a, at);
+  }
   unpack_raw(in, raw);
-  for (;;) {
+  for (int j = 0;; ++j) {
     const int nx = __builtin_amdgcn_readfirstlane(it + (int)gridDim.x);
-    const int ld = nx < n_items ? nx : it;
-    const RawAt at = raw_at<DK, DV>(a, ld_entry(a.table + chunk_of(ld)), ld % a.H);
+    const bool more = nx < n_items;
+    const RawAt at = at_of(more ? j + 1 : j, more ? nx : it);
     load_part<0>(raw, a, at);
     prep_item<DK, DV, false>(a, chunk_of(it), it % a.H, in, smem, [&](int phase) {
       if (phase == 1) load_part<1>(raw, a, at);
       if (phase == 2) load_part<2>(raw, a, at);
     });
     unpack_raw(in, raw);
+    if (!more) break;
     __syncthreads();  // LDS is rewritten by the next item
-    if (nx >= n_items) break;
     it = nx;
   }
 }

@@ -121,6 +121,11 @@ kda_status_t kda_fwd_validate(const kda_problem_t* prob, const void* q, const vo
  * values) get no accuracy guarantee but never make the kernels read or write
  * out of bounds.  cu_seqlens is read on the device; its validity is the
  * caller's precondition (see kda_fwd_validate).
+ *
+ * Tuning (read at every call; results are the same up to rounding):
+ *   KDA_SCAN_SLICE=16|32|64  value columns per state-scan workgroup (default 16)
+ *   KDA_CHUNK_WGS=n          at most n workgroups for the persistent chunk
+ *                            kernel (default: one per compute unit)
  */
 kda_status_t kda_fwd(const kda_problem_t* prob, const void* q, const void* k, const void* v,
                      const float* g, const void* beta, const float* h0,

@@ -104,3 +104,25 @@ def test_in_place_state_update():
     out, ht = kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], st, None, x.scale, ht=st)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(st.cpu().numpy(), ref_h)
+
+
+# The persistent chunk kernel reads the first 64 items of each workgroup from a staged
+# table and later ones from the chunk table: a small grid makes every workgroup walk
+# hundreds of items, fixed-length and packed.
+@pytest.mark.parametrize("packed", [False, True])
+def test_long_walks_of_the_chunk_kernel(packed, monkeypatch):
+    monkeypatch.setenv("KDA_CHUNK_WGS", "3")
+    if packed:
+        lens = [700, 1, 64, 1333, 0, 999, 65, 1000]
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        x = make_inputs(1, int(cu[-1]), 6, 64, 64, seed=21, dtype="bf16", cu_seqlens=cu)
+    else:
+        x = make_inputs(2, 2100, 6, 64, 64, seed=22, dtype="bf16")
+    _check(x, "chunk kernel on 3 workgroups, packed=%s" % packed)
+
+
+@pytest.mark.parametrize("slice_", ["16", "32", "64"])
+def test_scan_slice_widths(slice_, monkeypatch):
+    monkeypatch.setenv("KDA_SCAN_SLICE", slice_)
+    x = make_inputs(1, 333, 3, 128, 128, seed=5, dtype="bf16")
+    _check(x, "scan slice %s" % slice_)
