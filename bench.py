@@ -187,8 +187,8 @@ def main():
     K, W = args.steps, args.warmup
     marks = []
     for _ in range(K):
-        row = (ctypes.c_void_p * 5)()
-        for j in range(5):
+        row = (ctypes.c_void_p * 4)()
+        for j in range(4):
             e = ctypes.c_void_p()
             if hip.hipEventCreate(ctypes.byref(e)) != 0:
                 raise RuntimeError("hipEventCreate failed")
@@ -221,13 +221,12 @@ def main():
 
     k_map = np.mean([elapsed(m[0], m[1]) for m in marks])
     k_prep = np.mean([elapsed(m[1], m[2]) for m in marks])
-    k_exact = np.mean([elapsed(m[2], m[3]) for m in marks])
-    k_scan = np.mean([elapsed(m[3], m[4]) for m in marks])
+    k_scan = np.mean([elapsed(m[2], m[3]) for m in marks])
     for m in marks:
-        for j in range(5):
+        for j in range(4):
             hip.hipEventDestroy(m[j])
     log("timed %d steps: %.4f ms/step (wall %.4f ms/step); kernels: chunk map %.4f ms, chunk %.4f ms, "
-        "exact chunk %.4f ms, scan %.4f ms" % (K, ms_per_step, 1e3 * t_wall / K, k_map, k_prep, k_exact, k_scan))
+        "scan %.4f ms" % (K, ms_per_step, 1e3 * t_wall / K, k_map, k_prep, k_scan))
 
     tokens = B * T
     value = tokens / (ms_per_step * 1e-3)
@@ -306,7 +305,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": dom_bytes},
         "kernels_ms": {"chunk_map": round(float(k_map), 5), "chunk_prep": round(float(k_prep), 5),
-                       "chunk_prep_exact": round(float(k_exact), 5), "state_scan": round(float(k_scan), 5)},
+                       "state_scan": round(float(k_scan), 5)},
         "mfma": {"flops_per_step": total_flops,
                  "frac_of_peak": round(total_flops / (ms_per_step * 1e-3) / (MFMA_F16_PEAK_TFLOPS * 1e12), 5),
                  "peak_tflops": MFMA_F16_PEAK_TFLOPS},

@@ -94,7 +94,7 @@ int chunk_workgroups() {
 
 extern "C" {
 
-int kda_version(void) { return 100; }
+int kda_version(void) { return 101; }
 
 const char* kda_status_string(kda_status_t s) {
   switch (s) {
@@ -199,10 +199,10 @@ static kda_status_t forward(const kda_problem_t* prob, const void* q, const void
   p.seq_off = reinterpret_cast<int32_t*>(ws + c.seq_off);
   p.seq_order = reinterpret_cast<int32_t*>(ws + c.seq_order);
   p.rec = ws + c.rec;
-  p.defer_mask = reinterpret_cast<uint32_t*>(ws + c.defer);
+  p.defer = reinterpret_cast<int32_t*>(ws + c.defer);
   p.slice = slice_width(prob, N);
   p.chunk_wgs = chunk_workgroups();
-  for (int i = 0; i < 5; ++i) p.marks[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
+  for (int i = 0; i < 4; ++i) p.marks[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
   hipError_t e = kda::launch_forward(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -9,8 +9,6 @@
 //
 // One workgroup of 1024 threads builds:
 //   info[0]           total number of chunks
-//   defer_mask        cleared: one bit per (chunk, head) item, set by the chunk kernel
-//                     for the items it hands to its exact variant
 //   table[c]          (sequence, valid length, index inside the sequence) of chunk c
 //   seq_off[n]        first chunk of sequence n (exclusive prefix of chunk counts), seq_off[N] = total
 //   seq_order[i]      sequences ordered by chunk count, longest first (buckets of
@@ -29,16 +27,13 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* _
                                                                 int32_t* __restrict__ info,
                                                                 ChunkEntry* __restrict__ table,
                                                                 int32_t* __restrict__ seq_off,
-                                                                int32_t* __restrict__ seq_order,
-                                                                uint32_t* __restrict__ defer_mask,
-                                                                int64_t n_mask_words) {
+                                                                int32_t* __restrict__ seq_order) {
   __shared__ int32_t scan[kMapThreads];
   __shared__ int32_t hist[34];
   __shared__ int32_t carry_s;
   const int tid = threadIdx.x;
   if (tid == 0) carry_s = 0;
   if (tid < 34) hist[tid] = 0;
-  for (int64_t i = tid; i < n_mask_words; i += kMapThreads) defer_mask[i] = 0u;
   __syncthreads();
 
   // 1. chunk counts, exclusive prefix -> seq_off; bucket histogram
@@ -71,7 +66,6 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* _
   if (tid == 0) {
     info[0] = total;
     info[1] = (carry_s > n_chunk_ub) ? 1 : 0;
-    info[2] = 0;
     seq_off[N] = carry_s;
   }
   __syncthreads();

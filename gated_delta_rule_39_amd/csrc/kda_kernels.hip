@@ -26,22 +26,15 @@ static hipError_t launch_prep(const ForwardPlan& p, hipStream_t stream) {
   a.info = p.info;
   a.table = reinterpret_cast<const ChunkEntry*>(p.table);
   a.rec = p.rec;
-  a.defer_mask = p.defer_mask;
+  a.defer = p.defer;
   const size_t smem = PrepSmem<DK, DV>::BYTES;
-  auto fast = chunk_prep_kernel<DK, DV, InT>;
-  auto exact = chunk_prep_exact_kernel<DK, DV, InT>;
-  hipFuncSetAttribute(reinterpret_cast<const void*>(fast), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  hipFuncSetAttribute(reinterpret_cast<const void*>(exact), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  auto kern = chunk_prep_kernel<DK, DV, InT>;
+  hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   // persistent workgroups, at most one per compute unit (the LDS footprint admits one)
   int64_t grid = p.chunk_wgs > 0 ? p.chunk_wgs : 256;
   const int64_t items = p.n_chunk_ub * (int64_t)p.H;
   if (grid > items) grid = items;
-  hipLaunchKernelGGL(fast, dim3((unsigned)grid), dim3(kPrepThreads), smem, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  mark(p, 2, stream);
-  // the exact variant walks the deferred items (usually none: its workgroups exit at once)
-  hipLaunchKernelGGL(exact, dim3((unsigned)grid), dim3(kPrepThreads), smem, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kPrepThreads), smem, stream, a);
   return hipGetLastError();
 }
 
@@ -73,12 +66,10 @@ static hipError_t launch_dkdv(const ForwardPlan& p, hipStream_t stream) {
   if (p.T_total > 0) {
     e = (p.dtype == 0) ? launch_prep<DK, DV, uint16_t>(p, stream) : launch_prep<DK, DV, float>(p, stream);
     if (e != hipSuccess) return e;
-  } else {
-    mark(p, 2, stream);
   }
-  mark(p, 3, stream);
+  mark(p, 2, stream);
   e = (p.dtype == 0) ? launch_scan<DK, DV, uint16_t>(p, stream) : launch_scan<DK, DV, float>(p, stream);
-  mark(p, 4, stream);
+  mark(p, 3, stream);
   return e;
 }
 
@@ -86,8 +77,7 @@ hipError_t launch_forward(const ForwardPlan& p, hipStream_t stream) {
   if (p.N <= 0) return hipSuccess;
   mark(p, 0, stream);
   hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kMapThreads), 0, stream, p.cu, p.T, p.N, p.n_chunk_ub,
-                     p.info, reinterpret_cast<ChunkEntry*>(p.table), p.seq_off, p.seq_order, p.defer_mask,
-                     (p.n_chunk_ub * (int64_t)p.H + 31) / 32);
+                     p.info, reinterpret_cast<ChunkEntry*>(p.table), p.seq_off, p.seq_order);
   mark(p, 1, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -28,10 +28,10 @@ struct ForwardPlan {
   int32_t* seq_off;
   int32_t* seq_order;
   uint8_t* rec;
-  uint32_t* defer_mask;  // bit (chunk * H + head) set: the item goes to the exact chunk kernel
+  int32_t* defer;  // per (chunk, head): the item needs the exact diagonal tiles (chunk kernel scratch)
   int32_t slice;  // value columns per scan workgroup (16, 32 or 64)
   int32_t chunk_wgs;  // workgroups of the persistent chunk kernel (>= 1)
-  hipEvent_t marks[5];  // optional timing marks around the kernels (may be null)
+  hipEvent_t marks[4];  // optional timing marks around the kernels (may be null)
 };
 
 // Bytes of one per-(chunk, head) record.

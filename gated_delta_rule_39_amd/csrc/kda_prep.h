@@ -45,8 +45,8 @@
 //      factors in [exp(-D), exp(D)] with D the larger half-span of the tile's
 //      decay; when D <= 80 nats on every channel of all four diagonal tiles
 //      (checked per chunk and head) each tile is one fp32 MFMA product.
-//      Otherwise the chunk is handed to the exact variant of this kernel
-//      (a second launch over the deferred items), which uses per-4-token
+//      Otherwise the item is flagged and, once the workgroup has walked all
+//      its items, redone by the exact variant, which uses per-4-token
 //      column-group references plus exp(g) products inside each group, on
 //      fp16 MFMA, exact at any depth.
 //  (b) Tinv by blocked forward substitution in fp32 (16x16 diagonal blocks by
@@ -111,7 +111,7 @@ struct PrepArgs {
   const int32_t* info;
   const ChunkEntry* table;
   uint8_t* rec;     // records [n_chunk_ub][H]
-  uint32_t* defer_mask;  // bit (chunk * H + head): item handed to the exact variant (cleared by the chunk map)
+  int32_t* defer;   // [chunk * H + head]: 1 if the item needs the exact diagonal tiles (written for every item)
 };
 
 // Four consecutive input elements as loaded (bf16 pairs or fp32).
@@ -501,13 +501,10 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   }
   __syncthreads();  // #3: table and guard visible
   if (!EXACT) {
-    // A diagonal tile spans more decay than the fp32 path covers: the item is handed to
-    // the exact variant, which rewrites its record.  This variant still runs to the end
-    // (its record is overwritten), so every item issues the same memory operations.
-    if (*guard && tid == 0) {
-      const int item = chunk * a.H + h;
-      atomicOr(a.defer_mask + (item >> 5), 1u << (item & 31));  // no return value: no wait
-    }
+    // A diagonal tile spans more decay than the fp32 path covers: the item is flagged
+    // and redone by the exact variant, which rewrites its record.  This variant still
+    // runs to the end, so every item issues the same memory operations.
+    if (tid == 0) a.defer[(size_t)chunk * a.H + h] = *guard;
   }
 
   // identity fragments: B[k][n] = 1 iff the channel of slot k is 16*hh + n of the step
@@ -935,19 +932,24 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   }
 }
 
-// Fast variant: persistent workgroups walk the items (chunk, head), head fastest, so
-// that the workgroups in flight read whole token rows (all heads) of q, k, v and g and
-// write adjacent records; chunks go from the last to the first.  The next item's loads
-// are issued as soon as the current item's inputs sit in registers.
+// Persistent workgroups walk the items x = chunk position * H + head slot, workgroup
+// b taking x = b, b + grid, ...: the workgroups in flight read whole token rows (all
+// heads) of q, k, v and g and write adjacent records.  Chunks go from the last to the
+// first; the head of slot s at chunk position p is (s + p) mod H, so that a workgroup
+// meets every head as it walks (items flagged for the exact pass, often whole heads,
+// then spread evenly over the workgroups).  The next item's loads are issued as soon
+// as the current item's inputs sit in registers.
 //
 // The loads of the next item are issued unconditionally (the last item re-reads its
 // own inputs) and unpacked after the current item's record stores, so that on every
 // path the same number of stores follows them: waiting for the loads then does not
 // wait for the stores (one in-order counter covers both).
+//
+// After its walk, each workgroup redoes its own flagged items with the exact variant.
 template <int DK, int DV, typename InT>
 __global__ __launch_bounds__(kPrepThreads, 1) void chunk_prep_kernel(PrepArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  // items chunk * H + head (fewer than 2^31), kept in scalar registers
+  // items (fewer than 2^31), kept in scalar registers
   const int n_items = (int)sload_u32(a.info) * a.H;
   int it = blockIdx.x;
   if (it >= n_items) return;  // uniform for the workgroup
@@ -955,6 +957,7 @@ __global__ __launch_bounds__(kPrepThreads, 1) void chunk_prep_kernel(PrepArgs a)
   // and are still in the caches (L2, MALL) when it starts
   const int n_chunks = n_items / a.H;
   auto chunk_of = [&](int x) { return n_chunks - 1 - x / a.H; };
+  auto head_of = [&](int x) { return (x % a.H + x / a.H) % a.H; };
   // Where the chunks of this workgroup's first 64 items start and how many tokens they
   // hold, staged in LDS (entry j: item blockIdx.x + j * gridDim.x) with one batch of
   // vector loads: the next item's input loads then never wait behind dependent scalar
@@ -977,54 +980,56 @@ __global__ __launch_bounds__(kPrepThreads, 1) void chunk_prep_kernel(PrepArgs a)
       const uint32_t lo = __builtin_amdgcn_readfirstlane(m.x);
       const int32_t hi = __builtin_amdgcn_readfirstlane(m.y);
       const int len = __builtin_amdgcn_readfirstlane(m.z);
-      return raw_at_tok<DK, DV>(a, (int64_t)(((uint64_t)(uint32_t)hi << 32) | lo), len, item % a.H);
+      return raw_at_tok<DK, DV>(a, (int64_t)(((uint64_t)(uint32_t)hi << 32) | lo), len, head_of(item));
     }
-    return raw_at<DK, DV>(a, ld_entry(a.table + chunk_of(item)), item % a.H);
+    return raw_at<DK, DV>(a, ld_entry(a.table + chunk_of(item)), head_of(item));
   };
-  RawIn<DK, DV, InT> raw;
-  ItemIn<DK, DV> in;
   {
-    const RawAt at = at_of(0, it);
-    load_part<0>(raw, a, at);
-    load_part<1>(raw, a, at);
-    load_part<2>(raw, a, at);
-  }
-  unpack_raw(in, raw);
-  for (int j = 0;; ++j) {
-    const int nx = __builtin_amdgcn_readfirstlane(it + (int)gridDim.x);
-    const bool more = nx < n_items;
-    const RawAt at = at_of(more ? j + 1 : j, more ? nx : it);
-    load_part<0>(raw, a, at);
-    prep_item<DK, DV, false>(a, chunk_of(it), it % a.H, in, smem, [&](int phase) {
-      if (phase == 1) load_part<1>(raw, a, at);
-      if (phase == 2) load_part<2>(raw, a, at);
-    });
+    RawIn<DK, DV, InT> raw;
+    ItemIn<DK, DV> in;
+    {
+      const RawAt at = at_of(0, it);
+      load_part<0>(raw, a, at);
+      load_part<1>(raw, a, at);
+      load_part<2>(raw, a, at);
+    }
     unpack_raw(in, raw);
-    if (!more) break;
-    __syncthreads();  // LDS is rewritten by the next item
-    it = nx;
+    for (int j = 0;; ++j) {
+      const int nx = __builtin_amdgcn_readfirstlane(it + (int)gridDim.x);
+      const bool more = nx < n_items;
+      const RawAt at = at_of(more ? j + 1 : j, more ? nx : it);
+      load_part<0>(raw, a, at);
+      prep_item<DK, DV, false>(a, chunk_of(it), head_of(it), in, smem, [&](int phase) {
+        if (phase == 1) load_part<1>(raw, a, at);
+        if (phase == 2) load_part<2>(raw, a, at);
+      });
+      unpack_raw(in, raw);
+      if (!more) break;
+      __syncthreads();  // LDS is rewritten by the next item
+      it = nx;
+    }
   }
-}
+  __syncthreads();  // LDS is rewritten below; this workgroup's flags are visible to it
 
-// Exact variant over the items the fast variant deferred: workgroup b scans the mask
-// words b, b + grid, ... and takes every item whose bit is set.
-template <int DK, int DV, typename InT>
-__global__ __launch_bounds__(kPrepThreads, 1) void chunk_prep_exact_kernel(PrepArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  const int n_items = (int)sload_u32(a.info) * a.H;
-  const int n_words = (n_items + 31) >> 5;
-  for (int wd = blockIdx.x; wd < n_words; wd += gridDim.x) {
-    uint32_t bits = sload_u32(a.defer_mask + wd);
+  // exact pass over this workgroup's flagged items, 64 items per batch of flag loads
+  const int n_own = (n_items - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int lane = threadIdx.x & 63;
+  for (int kb = 0; kb < n_own; kb += 64) {
+    int f = 0;
+    if (kb + lane < n_own) {
+      const int x = (int)blockIdx.x + (kb + lane) * (int)gridDim.x;
+      f = a.defer[(size_t)chunk_of(x) * a.H + head_of(x)];
+    }
+    uint64_t bits = __ballot(f != 0);  // the same in every wave
     while (bits) {
-      const int b = __builtin_ctz(bits);
+      const int b = __builtin_ctzll(bits);
       bits &= bits - 1;
-      const int item = wd * 32 + b;
-      const int chunk = item / a.H, h = item % a.H;
+      const int x = __builtin_amdgcn_readfirstlane((int)blockIdx.x + (kb + b) * (int)gridDim.x);
       RawIn<DK, DV, InT> raw;
-      load_raw(raw, a, ld_entry(a.table + chunk), h);
+      load_raw(raw, a, ld_entry(a.table + chunk_of(x)), head_of(x));
       ItemIn<DK, DV> in;
       unpack_raw(in, raw);
-      prep_item<DK, DV, true>(a, chunk, h, in, smem, [](int) {});
+      prep_item<DK, DV, true>(a, chunk_of(x), head_of(x), in, smem, [](int) {});
       __syncthreads();  // LDS is rewritten by the next item
     }
   }

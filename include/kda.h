@@ -135,12 +135,11 @@ kda_status_t kda_fwd(const kda_problem_t* prob, const void* q, const void* k, co
 /*
  * kda_fwd with timing marks for profiling: identical work, plus hipEventRecord
  * of events[0] before the chunk map, events[1] after it, events[2] after the
- * chunk kernel, events[3] after the exact chunk kernel (the pass over chunks
- * whose in-chunk decay exceeds the fast kernel's range; usually empty) and
- * events[4] after the state scan, all on `stream`.  `events` is a host array
- * of 5 hipEvent_t handles created by the caller (NULL entries are skipped);
- * the elapsed time between consecutive marks is the duration of each kernel.
- * Errors as for kda_fwd.
+ * chunk kernel (including its pass over chunks whose in-chunk decay exceeds the
+ * fast path's range) and events[3] after the state scan, all on `stream`.
+ * `events` is a host array of 4 hipEvent_t handles created by the caller (NULL
+ * entries are skipped); the elapsed time between consecutive marks is the
+ * duration of each kernel.  Errors as for kda_fwd.
  */
 kda_status_t kda_fwd_timed(const kda_problem_t* prob, const void* q, const void* k, const void* v,
                            const float* g, const void* beta, const float* h0,
