@@ -7,7 +7,9 @@
 // sequence start, so a chunk never straddles two sequences; the last chunk of
 // a sequence may be partial.
 //
-// One workgroup of 1024 threads builds:
+// Packed sequences only (fixed-length rows need no table: the kernels derive a
+// chunk's row, index and length from its number).  One workgroup of 1024 threads
+// builds:
 //   info[0]           total number of chunks
 //   table[c]          (sequence, valid length, index inside the sequence) of chunk c
 //   seq_off[n]        first chunk of sequence n (exclusive prefix of chunk counts), seq_off[N] = total

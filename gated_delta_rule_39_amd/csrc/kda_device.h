@@ -42,9 +42,10 @@ __device__ inline float row_shr(float x) {
 }
 
 // Lane N of each row of 16 lanes, broadcast to the whole row (DPP row_newbcast).
+// Every lane is written, so no old value is needed.
 template <int N>
 __device__ inline float row_bcast(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + N, 0xF, 0xF, false));
 }
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }

@@ -24,6 +24,7 @@ static hipError_t launch_prep(const ForwardPlan& p, hipStream_t stream) {
   a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.beta = p.beta; a.cu = p.cu;
   a.T = p.T; a.T_total = p.T_total; a.H = p.H;
   a.info = p.info;
+  a.nc = p.cu ? 0 : (p.T + kChunk - 1) / kChunk;
   a.table = reinterpret_cast<const ChunkEntry*>(p.table);
   a.rec = p.rec;
   a.defer = p.defer;
@@ -44,6 +45,7 @@ static hipError_t launch_scan_nv(const ForwardPlan& p, hipStream_t stream) {
   a.h0 = p.h0; a.ht = p.ht; a.out = p.out; a.cu = p.cu;
   a.T = p.T; a.T_total = p.T_total; a.N = p.N; a.H = p.H; a.n_chunk_ub = p.n_chunk_ub;
   a.seq_off = p.seq_off; a.seq_order = p.seq_order; a.rec = p.rec; a.scale = p.scale;
+  a.nc = p.cu ? 0 : (p.T + kChunk - 1) / kChunk;
   const size_t smem = ScanSmem<DK, DV, NV>::BYTES;
   auto kern = state_scan_kernel<DK, DV, NV, OutT>;
   const int64_t blocks = p.N * (int64_t)p.H * (DV / NV);
@@ -76,11 +78,15 @@ static hipError_t launch_dkdv(const ForwardPlan& p, hipStream_t stream) {
 hipError_t launch_forward(const ForwardPlan& p, hipStream_t stream) {
   if (p.N <= 0) return hipSuccess;
   mark(p, 0, stream);
-  hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kMapThreads), 0, stream, p.cu, p.T, p.N, p.n_chunk_ub,
-                     p.info, reinterpret_cast<ChunkEntry*>(p.table), p.seq_off, p.seq_order);
+  // packed sequences: chunk table, sequence offsets and order from cu_seqlens on the device;
+  // fixed-length rows need none of it (the kernels derive every chunk from its index)
+  if (p.cu) {
+    hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kMapThreads), 0, stream, p.cu, p.T, p.N, p.n_chunk_ub,
+                       p.info, reinterpret_cast<ChunkEntry*>(p.table), p.seq_off, p.seq_order);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   mark(p, 1, stream);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   if (p.dk == 64 && p.dv == 64) return launch_dkdv<64, 64>(p, stream);
   if (p.dk == 64 && p.dv == 128) return launch_dkdv<64, 128>(p, stream);
   if (p.dk == 128 && p.dv == 64) return launch_dkdv<128, 64>(p, stream);

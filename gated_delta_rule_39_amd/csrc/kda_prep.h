@@ -108,8 +108,9 @@ struct PrepArgs {
   int64_t T;        // tokens per row (fixed) / total tokens (packed)
   int64_t T_total;  // total tokens in the flattened [B*T] order
   int32_t H;
-  const int32_t* info;
-  const ChunkEntry* table;
+  const int32_t* info;       // packed mode: info[0] = number of chunks
+  const ChunkEntry* table;   // packed mode: the chunk table
+  int64_t nc;                // fixed-length mode (cu == NULL): chunks per row; no table is built
   uint8_t* rec;     // records [n_chunk_ub][H]
   int32_t* defer;   // [chunk * H + head]: 1 if the item needs the exact diagonal tiles (written for every item)
 };
@@ -162,6 +163,17 @@ __device__ __forceinline__ uint64_t sload_u64(const void* p) {
   uint64_t r;
   asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
   return r;
+}
+// Chunk c of a fixed-length batch: chunk c mod nc of row c / nc.
+__device__ __forceinline__ ChunkEntry entry_fixed(const PrepArgs& a, int64_t c) {
+  ChunkEntry e;
+  const int64_t row = c / a.nc, idx = c - row * a.nc;
+  const int64_t rem = a.T - idx * kChunk;
+  e.seq = (int32_t)row;
+  e.len = (int32_t)(rem < kChunk ? rem : kChunk);
+  e.idx = (int32_t)idx;
+  e.pad = 0;
+  return e;
 }
 __device__ __forceinline__ ChunkEntry ld_entry(const ChunkEntry* p) {
   const uint64_t sl = sload_u64(p);
@@ -284,8 +296,11 @@ constexpr int kNoExp = -1000;         // exponent recorded for an all-zero half 
 // x[r] += am[J] * (row J's x[r]), am = minus this lane's row of the strictly lower part.
 template <int J>
 __device__ __forceinline__ void subst_rows(float (&x)[4], const float (&am)[16]) {
+  float b[4];  // all four broadcasts first: no VALU-to-DPP wait states between them and the FMAs
 #pragma unroll
-  for (int r = 0; r < 4; ++r) x[r] = fmaf(am[J], row_bcast<J>(x[r]), x[r]);
+  for (int r = 0; r < 4; ++r) b[r] = row_bcast<J>(x[r]);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x[r] = fmaf(am[J], b[r], x[r]);
   if constexpr (J + 1 < 15) subst_rows<J + 1>(x, am);
 }
 
@@ -950,9 +965,10 @@ template <int DK, int DV, typename InT>
 __global__ __launch_bounds__(kPrepThreads, 1) void chunk_prep_kernel(PrepArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   // items (fewer than 2^31), kept in scalar registers
-  const int n_items = (int)sload_u32(a.info) * a.H;
+  const int n_items = (a.cu ? (int)sload_u32(a.info) : (int)(a.nc * (a.T_total / (a.T > 0 ? a.T : 1)))) * a.H;
   int it = blockIdx.x;
   if (it >= n_items) return;  // uniform for the workgroup
+  auto entry = [&](int c) { return a.cu ? ld_entry(a.table + c) : entry_fixed(a, c); };
   // chunks from the last to the first: the records the scan reads first are written last
   // and are still in the caches (L2, MALL) when it starts
   const int n_chunks = n_items / a.H;
@@ -967,7 +983,7 @@ __global__ __launch_bounds__(kPrepThreads, 1) void chunk_prep_kernel(PrepArgs a)
     const int64_t item = (int64_t)blockIdx.x + (int64_t)threadIdx.x * gridDim.x;
     int4 m = make_int4(0, 0, 0, 0);
     if (item < n_items) {
-      const ChunkEntry e = a.table[chunk_of((int)item)];
+      const ChunkEntry e = a.cu ? a.table[chunk_of((int)item)] : entry_fixed(a, chunk_of((int)item));
       const int64_t st = seq_start(a.cu, a.T, e.seq) + (int64_t)e.idx * kChunk;
       m = make_int4((int32_t)(uint32_t)st, (int32_t)(st >> 32), e.len, 0);
     }
@@ -982,7 +998,7 @@ __global__ __launch_bounds__(kPrepThreads, 1) void chunk_prep_kernel(PrepArgs a)
       const int len = __builtin_amdgcn_readfirstlane(m.z);
       return raw_at_tok<DK, DV>(a, (int64_t)(((uint64_t)(uint32_t)hi << 32) | lo), len, head_of(item));
     }
-    return raw_at<DK, DV>(a, ld_entry(a.table + chunk_of(item)), head_of(item));
+    return raw_at<DK, DV>(a, entry(chunk_of(item)), head_of(item));
   };
   {
     RawIn<DK, DV, InT> raw;
@@ -1026,7 +1042,7 @@ __global__ __launch_bounds__(kPrepThreads, 1) void chunk_prep_kernel(PrepArgs a)
       bits &= bits - 1;
       const int x = __builtin_amdgcn_readfirstlane((int)blockIdx.x + (kb + b) * (int)gridDim.x);
       RawIn<DK, DV, InT> raw;
-      load_raw(raw, a, ld_entry(a.table + chunk_of(x)), head_of(x));
+      load_raw(raw, a, entry(chunk_of(x)), head_of(x));
       ItemIn<DK, DV> in;
       unpack_raw(in, raw);
       prep_item<DK, DV, true>(a, chunk_of(x), head_of(x), in, smem, [](int) {});

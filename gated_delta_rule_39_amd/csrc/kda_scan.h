@@ -54,8 +54,9 @@ struct ScanArgs {
   int64_t N;
   int32_t H;
   int64_t n_chunk_ub;
-  const int32_t* seq_off;
-  const int32_t* seq_order;
+  const int32_t* seq_off;    // packed mode: first chunk of each sequence
+  const int32_t* seq_order;  // packed mode: sequences, longest first
+  int64_t nc;                // fixed-length mode (cu == NULL): chunks per row
   const uint8_t* rec;
   float scale;
 };
@@ -180,8 +181,9 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
   }
   const int slice = (int)slice_l;
   const int h = (int)(chain % a.H);
-  const int64_t n = a.seq_order[chain / a.H];
-  int64_t c0 = a.seq_off[n], c1 = a.seq_off[n + 1];
+  const int64_t n = a.cu ? (int64_t)a.seq_order[chain / a.H] : chain / a.H;
+  int64_t c0 = a.cu ? (int64_t)a.seq_off[n] : n * a.nc;
+  int64_t c1 = a.cu ? (int64_t)a.seq_off[n + 1] : (n + 1) * a.nc;
   if (c1 > a.n_chunk_ub) c1 = a.n_chunk_ub;  // only on invalid cu_seqlens
   if (c0 > c1) c0 = c1;
   const int64_t L = seq_len(a.cu, a.T, n);
