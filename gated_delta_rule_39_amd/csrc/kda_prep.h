@@ -218,24 +218,25 @@ __device__ __forceinline__ RawAt raw_at(const PrepArgs& a, const ChunkEntry& ce,
   return raw_at_tok<DK, DV>(a, s0 + (int64_t)ce.idx * kChunk, ce.len, h);
 }
 
-// Issues one group of an item's loads: 0 = q, k, beta; 1 = g; 2 = v.  The groups are
-// issued at different points of the previous item so that the loads of all compute
-// units do not reach HBM in one burst.
+// Issues one group of an item's loads: 0 = q; 1 = k, beta; 2 = g; 3 = v.  The groups
+// are issued at different points of the previous item: the vector-memory path takes
+// each wave's load instructions one after the other, and a single burst from all eight
+// waves would hold the last of them for over a thousand cycles.
 template <int PART, int DK, int DV, typename InT>
 __device__ __forceinline__ void load_part(RawIn<DK, DV, InT>& r, const PrepArgs& a, const RawAt& at) {
   using RI = RawIn<DK, DV, InT>;
   using V4 = typename RI::V4;
   if (PART == 0) {
     const InT* q = reinterpret_cast<const InT*>(a.q);
-    const InT* k = reinterpret_cast<const InT*>(a.k);
 #pragma unroll
-    for (int j = 0; j < 2 * RI::KH; ++j) {
-      r.q[j] = *reinterpret_cast<const V4*>(q + at.rowk + 16 * j);
-      r.k[j] = *reinterpret_cast<const V4*>(k + at.rowk + 16 * j);
-    }
-    r.beta = reinterpret_cast<const InT*>(a.beta)[at.bidx];
+    for (int j = 0; j < 2 * RI::KH; ++j) r.q[j] = *reinterpret_cast<const V4*>(q + at.rowk + 16 * j);
     r.valid = at.valid;
   } else if (PART == 1) {
+    const InT* k = reinterpret_cast<const InT*>(a.k);
+#pragma unroll
+    for (int j = 0; j < 2 * RI::KH; ++j) r.k[j] = *reinterpret_cast<const V4*>(k + at.rowk + 16 * j);
+    r.beta = reinterpret_cast<const InT*>(a.beta)[at.bidx];
+  } else if (PART == 2) {
 #pragma unroll
     for (int j = 0; j < 2 * RI::KH; ++j) r.g[j] = *reinterpret_cast<const float4*>(a.g + at.rowk + 16 * j);
   } else {
@@ -251,6 +252,7 @@ __device__ __forceinline__ void load_raw(RawIn<DK, DV, InT>& r, const PrepArgs& 
   load_part<0>(r, a, at);
   load_part<1>(r, a, at);
   load_part<2>(r, a, at);
+  load_part<3>(r, a, at);
 }
 
 template <int DK, int DV, typename InT>
@@ -307,7 +309,7 @@ __device__ __forceinline__ void subst_rows(float (&x)[4], const float (&am)[16])
 // One (chunk, head) from its fp32 inputs.  EXACT = false: guarded fp32 diagonal tiles,
 // the chunk is deferred when the guard fails.  EXACT = true: per-group references on
 // every diagonal tile.  Every wave of the workgroup calls it (it holds barriers).
-// `mid(1)` and `mid(2)` run right after barriers #2 and #4 (the persistent kernel
+// `mid(1)`, `mid(2)` and `mid(3)` run right after barriers #1, #2 and #4 (the persistent kernel
 // issues the next item's remaining loads there).
 template <int DK, int DV, bool EXACT, typename Mid>
 __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, const int h, ItemIn<DK, DV>& in,
@@ -438,6 +440,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   vm = wave_max(vm);
   if (l == 0) red[wv] = vm;
   __syncthreads();  // #1: block totals, norm partials, max |v|
+  mid(1);
   finish_norm(xq, 0, exq, ssq);
   finish_norm(xk, 1, exk, ssk);
 #pragma unroll
@@ -470,7 +473,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
           make_float4(G[4 * j], G[4 * j + 1], G[4 * j + 2], G[4 * j + 3]);
   }
   __syncthreads();  // #2: group-end gates visible, block totals and norm partials consumed
-  mid(1);
+  mid(2);
 
   // decay-factor table and the guard of the fp32 diagonal path
   if (tid < DK) {
@@ -577,7 +580,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     }
   }
   __syncthreads();  // #4: column operands visible
-  mid(2);
+  mid(3);
 
   // ---------------- (b) Gram matrices L (row block w) and Aqk^T (column block w) ----------------
   // Partial sums over this half's channels.  offL[b]: L tile (w, b) and offA[b]: Aqk^T
@@ -1008,6 +1011,7 @@ __global__ __launch_bounds__(kPrepThreads, 1) void chunk_prep_kernel(PrepArgs a)
       load_part<0>(raw, a, at);
       load_part<1>(raw, a, at);
       load_part<2>(raw, a, at);
+      load_part<3>(raw, a, at);
     }
     unpack_raw(in, raw);
     for (int j = 0;; ++j) {
@@ -1018,6 +1022,7 @@ __global__ __launch_bounds__(kPrepThreads, 1) void chunk_prep_kernel(PrepArgs a)
       prep_item<DK, DV, false>(a, chunk_of(it), head_of(it), in, smem, [&](int phase) {
         if (phase == 1) load_part<1>(raw, a, at);
         if (phase == 2) load_part<2>(raw, a, at);
+        if (phase == 3) load_part<3>(raw, a, at);
       });
       unpack_raw(in, raw);
       if (!more) break;
