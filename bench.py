@@ -12,6 +12,11 @@ speed.  The oracle run on the whole batch is also the CPU baseline.
 
 Per-kernel durations come from HIP events that kda_fwd_timed records between
 the library's kernels on the stream they run on.
+
+Beside the headline workload the line also carries the two 8,192-token varlen
+batches (uniform and skewed lengths), timed the same way and checked against the
+oracle, the geomean of the three, and the headline workload with cold caches
+(--no-extra skips these, for profiling runs).
 """
 import argparse
 import ctypes
@@ -118,6 +123,73 @@ def kernel_source_hash(kernel):
     return h.hexdigest()
 
 
+def extra_measurements(args, lib, kda, make_config, upload, dev, torch, argv1, out1, ht1, x1):
+    """The other two 8,192-token workloads (uniform and skewed varlen batches), each timed
+    like the headline one and checked against the oracle, their geomean with the headline
+    workload, and the headline workload with cold caches (a 512 MiB buffer written before
+    every call, outside the timed call)."""
+    from oracle import oracle_fwd
+    rel = lambda a, b: float(np.linalg.norm(a.astype(np.float64) - b) / np.linalg.norm(b))
+    res = {"ok": True}
+    per = {}
+    K, W = args.steps, args.warmup
+    for idx in (2, 3):
+        y = make_config(idx)
+        B, T, H, dk, dv = y.shape
+        io = torch.bfloat16 if y.dtype == "bf16" else torch.float32
+        d = upload(y)
+        N = y.num_seqs
+        o = torch.empty((B, T, H, dv), dtype=io, device=dev)
+        h = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+        prob = kda.make_problem(B, T, H, dk, dv, kda.KDA_BF16 if io == torch.bfloat16 else kda.KDA_F32,
+                                N if d["cu"] is not None else 0)
+        wsb = int(lib.kda_fwd_workspace_size(ctypes.byref(prob)))
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        P = lambda t_: None if t_ is None else ctypes.c_void_p(t_.data_ptr())
+        argv = [ctypes.byref(prob), P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["h0"]),
+                P(d["cu"]), ctypes.c_float(y.scale), P(o), P(h), P(ws), ctypes.c_size_t(wsb),
+                ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)]
+        for _ in range(W):
+            if lib.kda_fwd(*argv):
+                raise RuntimeError("kda_fwd failed")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(K):
+            lib.kda_fwd(*argv)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / K
+        ro, rh = oracle_fwd(y.q, y.k, y.v, y.g, y.beta, y.h0, y.cu_seqlens, y.scale)
+        eo, eh = rel(o.float().cpu().numpy(), ro), rel(h.cpu().numpy(), rh)
+        good = eo <= TOL and eh <= TOL
+        res["ok"] = res["ok"] and good
+        per[y.name] = {"tokens_per_s": round(B * T / (ms * 1e-3), 1) if good else None,
+                       "ms_per_step": round(ms, 5), "sequences": int(N),
+                       "out_rel_rmse": eo, "state_rel_rmse": eh}
+        log("workload %s: %.4f ms/step, parity out %.2e state %.2e" % (y.name, ms, eo, eh))
+        del d, o, h, ws
+    res["workloads"] = per
+
+    # headline workload with cold caches
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    times = []
+    for _ in range(10):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        lib.kda_fwd(*argv1)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del flush
+    B1, T1 = x1.shape[0], x1.shape[1]
+    cold_ms = float(np.median(times))
+    res["cold"] = {"ms_per_call": round(cold_ms, 5), "tokens_per_s": round(B1 * T1 / (cold_ms * 1e-3), 1),
+                   "calls": len(times), "note": "512 MiB written before every call, outside its timing"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +200,8 @@ def main():
     ap.add_argument("--no-verify", action="store_true", help="skip parity (then no speed is reported)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="run only a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the varlen workloads and the cold-cache timing (profiling runs)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -259,6 +333,10 @@ def main():
         del ro, rh
         # replay: new contents in the same buffers, same call; check 4 heads against the oracle
         y = make_config(args.workload, seed=1000 + args.workload)
+        # the same sequence boundaries (a varlen draw with another seed has other lengths)
+        y.cu_seqlens = x.cu_seqlens
+        if x.h0 is not None and (y.h0 is None or y.h0.shape != x.h0.shape):
+            y.h0 = np.ascontiguousarray(-x.h0[::-1])
         dy = upload(y)
         for key in ("q", "k", "v", "g", "beta", "h0"):
             if d[key] is not None:
@@ -276,6 +354,11 @@ def main():
         log("parity: " + json.dumps(parity))
         if args.no_cpu_baseline:
             cpu_baseline = None
+
+    extra = {}
+    if not args.no_extra and not args.no_verify:
+        extra = extra_measurements(args, lib, kda, make_config, upload, dev, torch, argv, out, ht, x)
+        ok = ok and extra.pop("ok")
 
     nch = n_chunks_of(x)
     wk = algorithmic_work(x, nch)
@@ -314,6 +397,11 @@ def main():
         "parity": parity,
         "cpu_baseline": cpu_baseline,
     }
+    res.update(extra)
+    if res.get("workloads") and res["value"] is not None:
+        vals = [res["value"]] + [w["tokens_per_s"] for w in res["workloads"].values()]
+        if all(v_ is not None for v_ in vals):
+            res["geomean_fixed_varlen_tokens_per_s"] = round(float(np.exp(np.mean(np.log(vals)))), 1)
     print(json.dumps(res), flush=True)
     if not ok:
         log("PARITY FAILED: no speed reported")

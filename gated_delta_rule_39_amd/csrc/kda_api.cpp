@@ -65,23 +65,33 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
   return a0 < b0 + bn && b0 < a0 + an;
 }
 
+int compute_units() {
+  int dev = 0, cus = 0;
+  hipGetDevice(&dev);
+  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  return cus > 0 ? cus : 256;
+}
+
+// Value columns per state-scan workgroup.  A workgroup's step costs about the same for
+// 16, 32 or 64 columns (it is bound by loading the chunk's factors), so the widest slice
+// that still gives every compute unit a workgroup wins: fewer workgroups walk the chains
+// in fewer rounds.  KDA_SCAN_SLICE=16|32|64 overrides.
 int slice_width(const kda_problem_t* p, int64_t N) {
   const char* env = std::getenv("KDA_SCAN_SLICE");
   if (env) {
     int v = std::atoi(env);
     if ((v == 16 || v == 32 || v == 64) && v <= p->dv) return v;
   }
-  (void)N;
+  const int64_t cus = compute_units();
+  for (int v = 64; v > 16; v >>= 1)
+    if (v <= p->dv && N * (int64_t)p->heads * (p->dv / v) >= cus) return v;
   return 16;
 }
 
 // Workgroups of the persistent chunk kernel: one per compute unit, or fewer when
 // KDA_CHUNK_WGS=n (n >= 1) asks for it (tuning, and tests of long per-workgroup walks).
 int chunk_workgroups() {
-  int dev = 0, cus = 0;
-  hipGetDevice(&dev);
-  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  int n = cus > 0 ? cus : 256;
+  int n = compute_units();
   const char* env = std::getenv("KDA_CHUNK_WGS");
   if (env) {
     const int v = std::atoi(env);

@@ -123,7 +123,8 @@ kda_status_t kda_fwd_validate(const kda_problem_t* prob, const void* q, const vo
  * caller's precondition (see kda_fwd_validate).
  *
  * Tuning (read at every call; results are the same up to rounding):
- *   KDA_SCAN_SLICE=16|32|64  value columns per state-scan workgroup (default 16)
+ *   KDA_SCAN_SLICE=16|32|64  value columns per state-scan workgroup (default: the widest
+ *                            that still gives every compute unit a workgroup)
  *   KDA_CHUNK_WGS=n          at most n workgroups for the persistent chunk
  *                            kernel (default: one per compute unit)
  */
