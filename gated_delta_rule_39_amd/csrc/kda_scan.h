@@ -42,7 +42,10 @@ constexpr int kScanThreads = 512;  // 4 token-block waves + 4 key-block waves
 #ifndef KDA_SCAN_DEPTH
 #define KDA_SCAN_DEPTH 3
 #endif
-constexpr int kScanDepth = KDA_SCAN_DEPTH;  // chunks of factors held in registers (prefetch distance + 1)
+// chunks of factors held in registers (prefetch distance + 1): three for 16-column slices;
+// wider slices hold more state and output fragments, so their ring is two deep (no spills)
+template <int NV>
+constexpr int scan_depth() { return NV <= 16 ? KDA_SCAN_DEPTH : 2; }
 
 struct ScanArgs {
   const float* h0;
@@ -153,6 +156,7 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
   constexpr int TPK = DK / 64;
   constexpr int NT = NV / 16;
   constexpr int NS = DV / NV;
+  constexpr int kScanDepth = scan_depth<NV>();
 
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* sbb = smem + SM::SB;
