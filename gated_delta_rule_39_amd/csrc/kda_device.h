@@ -50,12 +50,12 @@ __device__ inline float row_bcast(float x) {
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// Round-to-nearest-even fp32 -> bf16 (NaN stays NaN).
-__device__ inline uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Two fp32 -> bf16 conversions in one instruction (v_cvt_pk_bf16_f32: round to nearest
+// even under the default rounding mode; NaN stays NaN), low half = a.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Load four consecutive elements (bf16 or fp32) as fp32.
@@ -76,8 +76,8 @@ __device__ inline float load1(const float* p) { return *p; }
 // Store four consecutive elements from fp32 (bf16 rounds to nearest even).
 __device__ inline void store4(uint16_t* p, const float* x) {
   uint2 r;
-  r.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
-  r.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+  r.x = pack_bf16x2(x[0], x[1]);
+  r.y = pack_bf16x2(x[2], x[3]);
   *reinterpret_cast<uint2*>(p) = r;
 }
 __device__ inline void store4(float* p, const float* x) {
