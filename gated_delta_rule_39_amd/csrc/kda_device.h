@@ -84,9 +84,37 @@ __device__ inline void store4(float* p, const float* x) {
   *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
 }
 
+// Reductions across the four rows of 16 lanes (lanes t, t + 16, t + 32, t + 48), the result
+// in every lane, through the gfx950 row swaps (v_permlane16_swap: odd rows of the first
+// operand with even rows of the second; v_permlane32_swap: upper half of the first with lower
+// half of the second).  With both operands equal, the two results hold a lane's own row and
+// its partner row, so their sum (max) is the pairwise sum (max); VALU latency, where a
+// shuffle through ds_bpermute waits on the LDS.  Sums add in the same pairs as a butterfly.
+__device__ inline float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ inline float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Row rotation by N lanes inside each row of 16 (DPP row_ror), every lane written.
+template <int N>
+__device__ inline float row_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x120 + N, 0xF, 0xF, false));
+}
+
 __device__ inline float wave_max(float x) {
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
+  x = fmaxf(x, row_ror<8>(x));
+  x = fmaxf(x, row_ror<4>(x));
+  x = fmaxf(x, row_ror<2>(x));
+  x = fmaxf(x, row_ror<1>(x));
+  return rows4_max(x);
 }
 
 // Per 64-token chunk and head, the chunk factors handed from the chunk kernel

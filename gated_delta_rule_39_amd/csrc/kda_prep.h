@@ -387,8 +387,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     float m = 0.f;
 #pragma unroll
     for (int e = 0; e < NE; ++e) m = fmaxf(m, fabsf(x[e]));
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    m = rows4_max(m);
     ex = (m > 0.f) ? ilogbf(m) : kNoExp;
     float ss = 0.f;
 #pragma unroll
@@ -396,8 +395,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
       x[e] = ldexpf(x[e], -ex);
       ss = fmaf(x[e], x[e], ss);
     }
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
+    ss = rows4_sum(ss);
     if (gq == 0) {
       nrm_ex[(which * 2 + hf) * 64 + i_loc] = ex;
       nrm_ss[(which * 2 + hf) * 64 + i_loc] = ss;
@@ -733,8 +731,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
       bandA[1] = mfma16(kk, q2, bandA[1]);
       bandA[2] = mfma16(kk, q3, bandA[2]);
     }
-    adiag += __shfl_xor(adiag, 16, 64);
-    adiag += __shfl_xor(adiag, 32, 64);
+    adiag = rows4_sum(adiag);
     // L tile (w,w): lane (col j = t, rows 4gq + r); keep (i = j + d) inside j's group
     // Aqk^T tile (w,w): lane (col i = t, rows j = 4gq + r); keep (j = i - d) inside i's group
 #pragma unroll

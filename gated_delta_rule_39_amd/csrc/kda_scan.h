@@ -222,8 +222,7 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
       for (int p = 0; p < TPK; ++p)
 #pragma unroll
         for (int r = 0; r < 4; ++r) ss = fmaf(S[p][nt][r], S[p][nt][r], ss);
-      ss += __shfl_xor(ss, 16, 64);
-      ss += __shfl_xor(ss, 32, 64);
+      ss = rows4_sum(ss);
       if (gq == 0) cn[i * NV + 16 * nt + t] = ss;
     }
   }
