@@ -48,6 +48,10 @@ __device__ inline float row_bcast(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + N, 0xF, 0xF, false));
 }
 
+// floor(log2(x)) of a finite x > 0, denormals included (v_frexp_exp_i32_f32; the library
+// ilogbf goes through double precision).
+__device__ inline int ilogb_pos(float x) { return __builtin_amdgcn_frexp_expf(x) - 1; }
+
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
 // Two fp32 -> bf16 conversions in one instruction (v_cvt_pk_bf16_f32: round to nearest

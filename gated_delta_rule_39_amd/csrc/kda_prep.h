@@ -388,7 +388,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
 #pragma unroll
     for (int e = 0; e < NE; ++e) m = fmaxf(m, fabsf(x[e]));
     m = rows4_max(m);
-    ex = (m > 0.f) ? ilogbf(m) : kNoExp;
+    ex = (m > 0.f) ? ilogb_pos(m) : kNoExp;
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
@@ -408,7 +408,9 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     const float ss_p = nrm_ss[(which * 2 + (hf ^ 1)) * 64 + i_loc];
     const int exm = ex > ex_p ? ex : ex_p;
     const float tot = ldexpf(ss, 2 * (ex - exm)) + ldexpf(ss_p, 2 * (ex_p - exm));
-    const float f = (tot > 0.f) ? ldexpf(1.0f / sqrtf(tot), ex - exm) : 0.f;
+    // tot >= 1 (the larger half's entries were scaled to [1, 2)): the hardware reciprocal
+    // square root (about 1 ulp) is far inside the fp16 operand rounding that follows
+    const float f = (tot > 0.f) ? ldexpf(__builtin_amdgcn_rsqf(tot), ex - exm) : 0.f;
 #pragma unroll
     for (int e = 0; e < NE; ++e) x[e] *= f;
   };
@@ -457,7 +459,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   float vmax = red[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) vmax = fmaxf(vmax, red[i]);
-  const int ue = (vmax > 0.f) ? 12 - (ilogbf(vmax) + 1) : 0;
+  const int ue = (vmax > 0.f) ? 12 - (ilogb_pos(vmax) + 1) : 0;
   // beta v 2^ue rows in fp16 (|.| < 2^12)
   f16x8 vr[VH];
 #pragma unroll
