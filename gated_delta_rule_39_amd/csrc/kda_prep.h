@@ -379,11 +379,11 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   float* G = in.g;
   float* xv = in.v;
   const float bt = in.beta;
-  if (gq == 0 && hf == 0) sbeta[i_loc] = bt;
-  if (tid == 0) *guard = 0;
 
-  // half-row L2 norm partials (4 lanes share a token: lanes t, t+16, t+32, t+48)
-  auto half_norm = [&](float* x, int which, int& ex) {
+  // half-row L2 norm partials (4 lanes share a token: lanes t, t+16, t+32, t+48); every
+  // conditional store of this phase comes after all of its arithmetic, so the q, k, gate
+  // and v chains form one block that the compiler can interleave
+  auto half_norm = [&](float* x, int& ex) {
     float m = 0.f;
 #pragma unroll
     for (int e = 0; e < NE; ++e) m = fmaxf(m, fabsf(x[e]));
@@ -395,12 +395,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
       x[e] = ldexpf(x[e], -ex);
       ss = fmaf(x[e], x[e], ss);
     }
-    ss = rows4_sum(ss);
-    if (gq == 0) {
-      nrm_ex[(which * 2 + hf) * 64 + i_loc] = ex;
-      nrm_ss[(which * 2 + hf) * 64 + i_loc] = ss;
-    }
-    return ss;
+    return rows4_sum(ss);
   };
   // both halves at the larger exponent, then x * 2^(ex - exm) / ||row||
   auto finish_norm = [&](float* x, int which, int ex, float ss) {
@@ -415,8 +410,8 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     for (int e = 0; e < NE; ++e) x[e] *= f;
   };
   int exq, exk;
-  const float ssq = half_norm(xq, 0, exq);
-  const float ssk = half_norm(xk, 1, exk);
+  const float ssq = half_norm(xq, exq);
+  const float ssk = half_norm(xk, exk);
 
   // cumulative log2-gate inside the 16-token block (rows of 16 lanes), then block offsets
 #pragma unroll
@@ -428,17 +423,26 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     x += row_shr<8>(x);
     G[e] = x;
   }
+  float vm = 0.f;
+#pragma unroll
+  for (int e = 0; e < NEV; ++e) vm = fmaxf(vm, fabsf(xv[e]));
+  vm = wave_max(vm);
+
+  if (gq == 0) {
+    nrm_ex[(0 * 2 + hf) * 64 + i_loc] = exq;
+    nrm_ss[(0 * 2 + hf) * 64 + i_loc] = ssq;
+    nrm_ex[(1 * 2 + hf) * 64 + i_loc] = exk;
+    nrm_ss[(1 * 2 + hf) * 64 + i_loc] = ssk;
+    if (hf == 0) sbeta[i_loc] = bt;
+  }
   if (t == 15) {
 #pragma unroll
     for (int j = 0; j < 2 * KH; ++j)
       *reinterpret_cast<float4*>(btot + w * DK + cb + 16 * j + 4 * gq) =
           make_float4(G[4 * j], G[4 * j + 1], G[4 * j + 2], G[4 * j + 3]);
   }
-  float vm = 0.f;
-#pragma unroll
-  for (int e = 0; e < NEV; ++e) vm = fmaxf(vm, fabsf(xv[e]));
-  vm = wave_max(vm);
   if (l == 0) red[wv] = vm;
+  if (tid == 0) *guard = 0;
   __syncthreads();  // #1: block totals, norm partials, max |v|
   mid(1);
   finish_norm(xq, 0, exq, ssq);
