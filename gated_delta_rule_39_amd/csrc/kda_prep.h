@@ -450,13 +450,14 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
 #pragma unroll
   for (int j = 0; j < 2 * KH; ++j) {
     // totals of the earlier 16-token blocks, added in block order
+    // (every row is read and the later ones masked, so this stays one block without branches)
     float4 off = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int b = 0; b < 3; ++b) {
-      if (b < w) {
-        const float4 bt4 = *reinterpret_cast<const float4*>(btot + b * DK + cb + 16 * j + 4 * gq);
-        off.x += bt4.x; off.y += bt4.y; off.z += bt4.z; off.w += bt4.w;
-      }
+      const float4 bt4 = *reinterpret_cast<const float4*>(btot + b * DK + cb + 16 * j + 4 * gq);
+      const bool use = b < w;
+      off.x += use ? bt4.x : 0.f; off.y += use ? bt4.y : 0.f;
+      off.z += use ? bt4.z : 0.f; off.w += use ? bt4.w : 0.f;
     }
     G[4 * j + 0] += off.x; G[4 * j + 1] += off.y; G[4 * j + 2] += off.z; G[4 * j + 3] += off.w;
   }
