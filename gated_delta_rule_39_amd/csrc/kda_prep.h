@@ -77,7 +77,7 @@ struct PrepSmem {
   static constexpr int LP = 68;  // pitch (floats) of 64x64 fp32 matrices
   static constexpr int ET_ROWS = 19;
   static constexpr size_t BTOT = 4 * DK * 4;
-  static constexpr size_t YBF = 3 * KSK * 64 * 16;
+  static constexpr size_t YBF = 4 * KSK * 64 * 16;
   static constexpr size_t BWX = (size_t)NTK * 2 * 64 * 16;
   static constexpr size_t BUX = (size_t)NTV * 2 * 64 * 16;
   static_assert(YBF <= BWX, "column operands must not reach the Bu fragments");
@@ -326,7 +326,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   constexpr int LP = SM::LP;
 
   float* btot = reinterpret_cast<float*>(smem + SM::X);            // [4][DK]
-  f16x8* ybf = reinterpret_cast<f16x8*>(smem + SM::X);             // [3][KSK][64]
+  f16x8* ybf = reinterpret_cast<f16x8*>(smem + SM::X);             // [4][KSK][64]
   uint8_t* bwx = smem + SM::X;                                     // [NTK][2][64] f16x8
   uint8_t* bux = smem + SM::X + SM::BWX;                           // [NTV][2][64] f16x8
   float* Lm = reinterpret_cast<float*>(smem + SM::Y);              // [64][LP]
@@ -507,12 +507,9 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   {
     float gp[NE], gn[NE];
     lane_row(gend, 4 * w + 3, gn);
-    if (w > 0) {
-      lane_row(gend, 4 * w - 1, gp);
-    } else {
+    lane_row(gend, w > 0 ? 4 * w - 1 : 0, gp);  // read always, zero for block 0: no branch
 #pragma unroll
-      for (int e = 0; e < NE; ++e) gp[e] = 0.f;
-    }
+    for (int e = 0; e < NE; ++e) gp[e] = (w > 0) ? gp[e] : 0.f;
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
       const float fb = exp2_hw(G[e] - gp[e]);
@@ -565,7 +562,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
         *reinterpret_cast<f16x4*>(rec + R::KT + ((size_t)(ct * 2 + (w >> 1)) * 64 + l) * 16 + (w & 1) * 8) = h4;
       }
       // column-side operands of the off-diagonal Gram tiles (reference = end of block w)
-      if (w < 3) ybf[(w * KSK + s) * 64 + l] = y;
+      ybf[(w * KSK + s) * 64 + l] = y;  // block 3's slot is never read (no branch around the store)
     }
     // Bu fragments (beta v 2^ue, rows = value channels, tokens in pi order)
 #pragma unroll
