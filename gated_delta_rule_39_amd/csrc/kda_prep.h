@@ -764,41 +764,37 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     return x;
   };
   // The two halves' partial tiles meet in LDS: half 0 completes L, half 1 completes Aqk.
+  // (tiles above block w are written too, into slots nobody reads: no branches here)
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    if (b <= w) {
-      float* dst = (hf == 1 ? gpl : gpa) + ((w * 4 + b) * 64 + l) * 4;
-      *reinterpret_cast<f32x4*>(dst) = (hf == 1) ? tileL(b) : tileA(b);
-    }
+    float* dst = (hf == 1 ? gpl : gpa) + ((w * 4 + b) * 64 + l) * 4;
+    *reinterpret_cast<f32x4*>(dst) = (hf == 1) ? tileL(b) : tileA(b);
   }
   __syncthreads();  // #5a: partial tiles visible; every wave is past the column operands
 
   if (hf == 0) {
-    // A = diag(beta) L into LDS (blocks (w, b <= w))
+    // A = diag(beta) L into LDS (blocks (w, b <= w)).  The blocks above the diagonal get
+    // values nobody reads before the doubling steps overwrite them (their scratch), so
+    // every block is written without a branch.
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      if (b <= w) {
-        const f32x4 p = *reinterpret_cast<const f32x4*>(gpl + ((w * 4 + b) * 64 + l) * 4);
-        const f32x4 own = tileL(b);
+      const f32x4 p = *reinterpret_cast<const f32x4*>(gpl + ((w * 4 + b) * 64 + l) * 4);
+      const f32x4 own = tileL(b);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * w + 4 * gq + r;
-          Lm[i * LP + 16 * b + t] = sbeta[i] * (own[r] + p[r]);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * w + 4 * gq + r;
+        Lm[i * LP + 16 * b + t] = sbeta[i] * (own[r] + p[r]);
       }
     }
   } else {
     // Aqk A-fragments for row block w: slots (rows of Aqk^T tile (2 s2, w), rows of tile (2 s2 + 1, w))
     f32x4 full[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      full[b] = zero4();
-      if (b <= w) {
-        const f32x4 p = *reinterpret_cast<const f32x4*>(gpa + ((w * 4 + b) * 64 + l) * 4);
-        const f32x4 own = tileA(b);
+    for (int b = 0; b < 4; ++b) {  // zero above the diagonal (selected, not branched)
+      const f32x4 p = *reinterpret_cast<const f32x4*>(gpa + ((w * 4 + b) * 64 + l) * 4);
+      const f32x4 own = tileA(b);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) full[b][r] = own[r] + p[r];
-      }
+      for (int r = 0; r < 4; ++r) full[b][r] = (b <= w) ? own[r] + p[r] : 0.f;
     }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -903,7 +899,6 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
 
   // ---------------- (b) W = Tinv Bw (as W^T tiles) and U = Tinv Bu ----------------
   {
-    const int nks = (w >= 2) ? 2 : 1;  // Tinv rows of block w vanish beyond column 16w+15
     // Tinv row 16w + t at the tokens of the pi-ordered slots of step s
     f16x8 tf[2];
 #pragma unroll
@@ -922,13 +917,11 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
       const int sk = sb + skl;
       f32x4 c0 = zero4(), c1 = zero4();
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (s < nks) {
-          const f16x8 a0 = *reinterpret_cast<const f16x8*>(bwx + ((size_t)((2 * sk) * 2 + s) * 64 + l) * 16);
-          const f16x8 a1 = *reinterpret_cast<const f16x8*>(bwx + ((size_t)((2 * sk + 1) * 2 + s) * 64 + l) * 16);
-          c0 = mfma16(a0, tf[s], c0);
-          c1 = mfma16(a1, tf[s], c1);
-        }
+      for (int s = 0; s < 2; ++s) {  // tf[1] is zero for blocks 0 and 1: no branch needed
+        const f16x8 a0 = *reinterpret_cast<const f16x8*>(bwx + ((size_t)((2 * sk) * 2 + s) * 64 + l) * 16);
+        const f16x8 a1 = *reinterpret_cast<const f16x8*>(bwx + ((size_t)((2 * sk + 1) * 2 + s) * 64 + l) * 16);
+        c0 = mfma16(a0, tf[s], c0);
+        c1 = mfma16(a1, tf[s], c1);
       }
       f16x8 wf = {(_Float16)c0[0], (_Float16)c0[1], (_Float16)c0[2], (_Float16)c0[3],
                   (_Float16)c1[0], (_Float16)c1[1], (_Float16)c1[2], (_Float16)c1[3]};
@@ -940,10 +933,8 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
       f32x4 c = zero4();
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        if (s < nks) {
-          const f16x8 bfr = *reinterpret_cast<const f16x8*>(bux + ((size_t)(nt * 2 + s) * 64 + l) * 16);
-          c = mfma16(tf[s], bfr, c);
-        }
+        const f16x8 bfr = *reinterpret_cast<const f16x8*>(bux + ((size_t)(nt * 2 + s) * 64 + l) * 16);
+        c = mfma16(tf[s], bfr, c);
       }
       f16x4 uf = {(_Float16)c[0], (_Float16)c[1], (_Float16)c[2], (_Float16)c[3]};
       *reinterpret_cast<f16x4*>(rec + R::U + ((size_t)(w * NTV + nt) * 64 + l) * 8) = uf;
