@@ -15,8 +15,9 @@ the library's kernels on the stream they run on.
 
 Beside the headline workload the line also carries the two 8,192-token varlen
 batches (uniform and skewed lengths), timed the same way and checked against the
-oracle, the geomean of the three, and the headline workload with cold caches
-(--no-extra skips these, for profiling runs).
+oracle, the geomean of the three, the headline workload with cold caches, and a
+decode step (kda_decode) over 256 sequences with its HBM roofline (--no-extra skips
+these, for profiling runs).
 """
 import argparse
 import ctypes
@@ -187,7 +188,51 @@ def extra_measurements(args, lib, kda, make_config, upload, dev, torch, argv1, o
     cold_ms = float(np.median(times))
     res["cold"] = {"ms_per_call": round(cold_ms, 5), "tokens_per_s": round(B1 * T1 / (cold_ms * 1e-3), 1),
                    "calls": len(times), "note": "512 MiB written before every call, outside its timing"}
+    res["decode"] = decode_measurement(args, lib, kda, upload, dev, torch)
+    res["ok"] = res["ok"] and res["decode"]["ok"]
     return res
+
+
+def decode_measurement(args, lib, kda, upload, dev, torch, B=256):
+    """One decode step (kda_decode, one token per sequence) of B sequences at H=32, d=128:
+    timed like the forward, checked against the oracle, with its HBM roofline (the fp32
+    state is read once and written once per call)."""
+    from oracle import oracle_fwd
+    from workloads import make_inputs
+    rel = lambda a, b: float(np.linalg.norm(a.astype(np.float64) - b) / np.linalg.norm(b))
+    y = make_inputs(B, 1, 32, 128, 128, seed=5, dtype="bf16", name="decode-%dx1" % B)
+    Bd, T, H, dk, dv = y.shape
+    d = upload(y)
+    o = torch.empty((Bd, T, H, dv), dtype=torch.bfloat16, device=dev)
+    h = torch.empty((Bd, H, dk, dv), dtype=torch.float32, device=dev)
+    prob = kda.make_problem(Bd, T, H, dk, dv, kda.KDA_BF16, 0)
+    P = lambda t_: None if t_ is None else ctypes.c_void_p(t_.data_ptr())
+    argv = [ctypes.byref(prob), P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["h0"]), None,
+            ctypes.c_float(y.scale), P(o), P(h), ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)]
+    for _ in range(args.warmup):
+        rc = lib.kda_decode(*argv)
+        if rc:
+            raise kda.KDAError(rc)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        lib.kda_decode(*argv)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    ro, rh = oracle_fwd(y.q, y.k, y.v, y.g, y.beta, y.h0, None, y.scale)
+    eo, eh = rel(o.float().cpu().numpy(), ro), rel(h.cpu().numpy(), rh)
+    good = eo <= TOL and eh <= TOL
+    nbytes = Bd * H * (2 * dk * dv * 4 + 2 * dk * 2 + dk * 4 + dv * 2 + 2 + dv * 2)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log("decode %s: %.4f ms/call, %.0f GB/s, parity out %.2e state %.2e" % (y.name, ms, gbs, eo, eh))
+    return {"ok": good, "workload": "decode step: %d sequences x 1 token, H=32, dk=dv=128, bf16 io, fp32 state "
+                                    "in and out" % Bd,
+            "ms_per_step": round(ms, 5), "tokens_per_s": round(Bd * T / (ms * 1e-3), 1) if good else None,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_call": int(nbytes)},
+            "out_rel_rmse": eo, "state_rel_rmse": eh}
 
 
 def main():

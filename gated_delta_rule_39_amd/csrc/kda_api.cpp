@@ -104,7 +104,7 @@ int chunk_workgroups() {
 
 extern "C" {
 
-int kda_version(void) { return 101; }
+int kda_version(void) { return 102; }
 
 const char* kda_status_string(kda_status_t s) {
   switch (s) {
@@ -136,10 +136,13 @@ size_t kda_fwd_workspace_size(const kda_problem_t* prob) {
   return best;
 }
 
-kda_status_t kda_fwd_validate(const kda_problem_t* prob, const void* q, const void* k, const void* v,
-                              const float* g, const void* beta, const float* h0,
-                              const int32_t* cu_seqlens, float scale, const void* out, const float* ht,
-                              const void* workspace, size_t workspace_bytes) {
+}  // extern "C"
+
+// The checks of kda_fwd_validate; `use_workspace` = false for kda_decode, which takes none.
+static kda_status_t validate(const kda_problem_t* prob, const void* q, const void* k, const void* v,
+                             const float* g, const void* beta, const float* h0, const int32_t* cu_seqlens,
+                             float scale, const void* out, const float* ht, const void* workspace,
+                             size_t workspace_bytes, bool use_workspace) {
   if (!prob) return KDA_ERR_NULL;
   if (!dims_supported(prob)) return KDA_ERR_UNSUPPORTED;
   const bool packed = cu_seqlens != nullptr;
@@ -148,11 +151,16 @@ kda_status_t kda_fwd_validate(const kda_problem_t* prob, const void* q, const vo
   if (!std::isfinite(scale)) return KDA_ERR_BAD_ARG;
   const int64_t toks = prob->batch * prob->seqlen;
   if (toks > 0 && (!q || !k || !v || !g || !beta || !out)) return KDA_ERR_NULL;
-  if (!workspace) return KDA_ERR_NULL;
+  if (!use_workspace) {
+    workspace = nullptr;
+    workspace_bytes = 0;
+  } else if (!workspace) {
+    return KDA_ERR_NULL;
+  }
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(beta) ||
       misaligned(h0) || misaligned(out) || misaligned(ht) || misaligned(workspace))
     return KDA_ERR_ALIGN;
-  if (workspace_bytes < carve(prob, N, ub).total) return KDA_ERR_WORKSPACE;
+  if (use_workspace && workspace_bytes < carve(prob, N, ub).total) return KDA_ERR_WORKSPACE;
   const size_t es = prob->dtype == KDA_BF16 ? 2 : 4;
   const size_t nqk = (size_t)toks * prob->heads * prob->dk;
   const size_t nv = (size_t)toks * prob->heads * prob->dv;
@@ -176,6 +184,15 @@ kda_status_t kda_fwd_validate(const kda_problem_t* prob, const void* q, const vo
       if (host[i + 1] < host[i]) return KDA_ERR_BAD_ARG;
   }
   return KDA_OK;
+}
+
+extern "C" {
+
+kda_status_t kda_fwd_validate(const kda_problem_t* prob, const void* q, const void* k, const void* v,
+                              const float* g, const void* beta, const float* h0,
+                              const int32_t* cu_seqlens, float scale, const void* out, const float* ht,
+                              const void* workspace, size_t workspace_bytes) {
+  return validate(prob, q, k, v, g, beta, h0, cu_seqlens, scale, out, ht, workspace, workspace_bytes, true);
 }
 
 static kda_status_t forward(const kda_problem_t* prob, const void* q, const void* k, const void* v,
@@ -222,6 +239,30 @@ kda_status_t kda_fwd(const kda_problem_t* prob, const void* q, const void* k, co
                      float* ht, void* workspace, size_t workspace_bytes, void* stream) {
   return forward(prob, q, k, v, g, beta, h0, cu_seqlens, scale, out, ht, workspace, workspace_bytes, stream,
                  nullptr);
+}
+
+kda_status_t kda_decode(const kda_problem_t* prob, const void* q, const void* k, const void* v,
+                        const float* g, const void* beta, const float* h0, const int32_t* cu_seqlens,
+                        float scale, void* out, float* ht, void* stream) {
+  kda_status_t st = validate(prob, q, k, v, g, beta, h0, cu_seqlens, scale, out, ht, nullptr, 0, false);
+  if (st != KDA_OK) return st;
+  int64_t N = 0, ub = 0;
+  sizes_ok(prob, cu_seqlens != nullptr, &N, &ub);
+  kda::ForwardPlan p{};
+  p.B = prob->batch;
+  p.T = prob->seqlen;
+  p.N = N;
+  p.T_total = prob->batch * prob->seqlen;
+  p.H = prob->heads;
+  p.dk = prob->dk;
+  p.dv = prob->dv;
+  p.dtype = prob->dtype;
+  p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.cu = cu_seqlens;
+  p.scale = scale;
+  p.out = out;
+  p.ht = ht;
+  hipError_t e = kda::launch_recurrent(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 kda_status_t kda_fwd_timed(const kda_problem_t* prob, const void* q, const void* k, const void* v,

@@ -3,6 +3,7 @@
 #include "kda_chunkmap.h"
 #include "kda_prep.h"
 #include "kda_scan.h"
+#include "kda_recurrent.h"
 
 namespace kda {
 
@@ -91,6 +92,33 @@ hipError_t launch_forward(const ForwardPlan& p, hipStream_t stream) {
   if (p.dk == 64 && p.dv == 128) return launch_dkdv<64, 128>(p, stream);
   if (p.dk == 128 && p.dv == 64) return launch_dkdv<128, 64>(p, stream);
   return launch_dkdv<128, 128>(p, stream);
+}
+
+template <int DK, int DV, typename InT>
+static hipError_t launch_recurrent_dkdv(const ForwardPlan& p, hipStream_t stream) {
+  RecurrentArgs a;
+  a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.beta = p.beta; a.h0 = p.h0; a.cu = p.cu;
+  a.ht = p.ht; a.out = p.out; a.T = p.T; a.N = p.N; a.H = p.H; a.scale = p.scale;
+  a.waves = p.N * (int64_t)p.H * (DV / kRecCols);
+  const int64_t per_block = kRecThreads / 64;
+  const int64_t blocks = (a.waves + per_block - 1) / per_block;
+  auto kern = recurrent_kernel<DK, DV, InT>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kRecThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t launch_recurrent_dt(const ForwardPlan& p, hipStream_t stream) {
+  return p.dtype == 0 ? launch_recurrent_dkdv<DK, DV, uint16_t>(p, stream)
+                      : launch_recurrent_dkdv<DK, DV, float>(p, stream);
+}
+
+hipError_t launch_recurrent(const ForwardPlan& p, hipStream_t stream) {
+  if (p.N <= 0) return hipSuccess;
+  if (p.dk == 64 && p.dv == 64) return launch_recurrent_dt<64, 64>(p, stream);
+  if (p.dk == 64 && p.dv == 128) return launch_recurrent_dt<64, 128>(p, stream);
+  if (p.dk == 128 && p.dv == 64) return launch_recurrent_dt<128, 64>(p, stream);
+  return launch_recurrent_dt<128, 128>(p, stream);
 }
 
 }  // namespace kda

@@ -40,4 +40,8 @@ size_t record_bytes(int dk, int dv);
 // Enqueue chunk map, chunk kernel and state scan on `stream`.
 hipError_t launch_forward(const ForwardPlan& p, hipStream_t stream);
 
+// Enqueue the token-by-token recurrent kernel on `stream` (uses the sizes, tensors and
+// scale of `p`; no workspace).
+hipError_t launch_recurrent(const ForwardPlan& p, hipStream_t stream);
+
 }  // namespace kda

@@ -38,6 +38,8 @@ _lib.kda_fwd_validate.restype = ctypes.c_int
 _lib.kda_fwd.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
                          ctypes.c_size_t, _P]
 _lib.kda_fwd.restype = ctypes.c_int
+_lib.kda_decode.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]
+_lib.kda_decode.restype = ctypes.c_int
 _lib.kda_status_string.argtypes = [ctypes.c_int]
 _lib.kda_status_string.restype = ctypes.c_char_p
 _lib.kda_version.argtypes = []
@@ -84,11 +86,8 @@ def _dtype_code(dt):
     raise TypeError("q, k, v and beta must be bfloat16 or float32, got %s" % dt)
 
 
-def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, *, out=None, ht=None, workspace=None,
-        output_final_state=True, stream=None):
-    """KDA forward.  Shapes: q, k, g [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H];
-    h0 [N, H, dk, dv] fp32 or None; cu_seqlens int32 [N + 1] (B must be 1) or None.
-    Returns (out [B, T, H, dv] in q's dtype, ht [N, H, dk, dv] fp32 or None)."""
+def _check(q, k, v, g, beta, h0, cu_seqlens, extra):
+    """Shape, dtype and layout checks shared by fwd and decode; returns (B, T, H, dk, dv, N, code)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     code = _dtype_code(q.dtype)
@@ -97,7 +96,7 @@ def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, *, out=None, ht=
             raise TypeError("%s must have q's dtype" % name)
     if g.dtype != torch.float32:
         raise TypeError("g must be float32")
-    tensors = [q, k, v, g, beta] + [x for x in (h0, cu_seqlens, out, ht, workspace) if x is not None]
+    tensors = [q, k, v, g, beta] + [x for x in (h0, cu_seqlens) + tuple(extra) if x is not None]
     for t_ in tensors:
         if not t_.is_cuda or not t_.is_contiguous():
             raise ValueError("all tensors must be contiguous device tensors")
@@ -111,6 +110,15 @@ def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, *, out=None, ht=
         N = B
     if h0 is not None and (h0.dtype != torch.float32 or tuple(h0.shape) != (N, H, dk, dv)):
         raise ValueError("h0 must be float32 [N, H, dk, dv]")
+    return B, T, H, dk, dv, N, code
+
+
+def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, *, out=None, ht=None, workspace=None,
+        output_final_state=True, stream=None):
+    """KDA forward.  Shapes: q, k, g [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H];
+    h0 [N, H, dk, dv] fp32 or None; cu_seqlens int32 [N + 1] (B must be 1) or None.
+    Returns (out [B, T, H, dv] in q's dtype, ht [N, H, dk, dv] fp32 or None)."""
+    B, T, H, dk, dv, N, code = _check(q, k, v, g, beta, h0, cu_seqlens, (out, ht, workspace))
     if scale is None:
         scale = dk ** -0.5
     prob = make_problem(B, T, H, dk, dv, code, N if cu_seqlens is not None else 0)
@@ -126,6 +134,28 @@ def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, *, out=None, ht=
     rc = _lib.kda_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
                       _ptr(cu_seqlens), float(scale), _ptr(out), _ptr(ht), _ptr(workspace),
                       workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KDAError(rc)
+    return out, ht
+
+
+def decode(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, *, out=None, ht=None,
+           output_final_state=True, stream=None):
+    """The same forward, token by token (kda_decode): for decode steps (T = 1) and short
+    continuations.  Arguments and results as for fwd; no workspace.  Pass ht=h0 to update
+    the state in place."""
+    B, T, H, dk, dv, N, code = _check(q, k, v, g, beta, h0, cu_seqlens, (out, ht))
+    if scale is None:
+        scale = dk ** -0.5
+    prob = make_problem(B, T, H, dk, dv, code, N if cu_seqlens is not None else 0)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    if ht is None and output_final_state:
+        ht = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = _lib.kda_decode(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                         _ptr(cu_seqlens), float(scale), _ptr(out), _ptr(ht), ctypes.c_void_p(stream))
     if rc != 0:
         raise KDAError(rc)
     return out, ht

@@ -148,6 +148,29 @@ kda_status_t kda_fwd_timed(const kda_problem_t* prob, const void* q, const void*
                            void* workspace, size_t workspace_bytes, void* stream,
                            void* const* events);
 
+/*
+ * The same forward evaluated token by token, for decode steps (one new token
+ * per sequence, seqlen == 1) and other short continuations of many sequences.
+ * It is the step that "Autoresearch on Kimi Delta Attention", section "KDA in
+ * one minute", describes (per-channel forgetting, read the prediction, write
+ * the correction), applied once per token:
+ *
+ *     a = Diag(exp(g_t)) S,  delta = v_t - a^T khat_t,  S = a + beta_t khat_t delta^T,
+ *     o_t = scale * S^T qhat_t
+ *
+ * Arguments, shapes, dtypes, modes (fixed-length rows or cu_seqlens), the
+ * initial/final state convention (h0 NULL = zeros, ht NULL = not written,
+ * ht == h0 for an in-place update, empty sequences return ht = h0), alignment,
+ * aliasing rules and errors are those of kda_fwd; there is no workspace.  The
+ * state is read from HBM once and written once per call and carried in fp32
+ * registers in between; every step is fp32.  Each token costs O(dk * dv) per
+ * (sequence, head) with no parallelism along the sequence, so long prompts
+ * belong to kda_fwd; results agree with kda_fwd up to rounding.
+ */
+kda_status_t kda_decode(const kda_problem_t* prob, const void* q, const void* k, const void* v,
+                        const float* g, const void* beta, const float* h0,
+                        const int32_t* cu_seqlens, float scale, void* out, float* ht, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* kda_status_string(kda_status_t status);
 

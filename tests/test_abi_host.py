@@ -101,3 +101,35 @@ def test_alignment_workspace_and_aliasing():
     p2 = dict(p)
     p2["ht"] = p2["ws"] + 4096  # state written into the workspace
     assert _validate(prob, p2, wsb) == ALIAS
+
+
+def _decode(prob, p, scale=0.125, cu=False):
+    P = lambda n: None if p.get(n) is None else ctypes.c_void_p(p[n])
+    return kda.library().kda_decode(ctypes.byref(prob), P("q"), P("k"), P("v"), P("g"), P("beta"), P("h0"),
+                                    P("cu") if cu else None, ctypes.c_float(scale), P("out"), P("ht"), None)
+
+
+def test_decode_rejects_what_the_forward_rejects():
+    """kda_decode applies kda_fwd's checks (without a workspace).  Only calls that fail are
+    made here: they return before any HIP call."""
+    prob, p, _ = _args(B=8, T=1)
+    for n in ["q", "k", "v", "g", "beta", "out"]:
+        p2 = dict(p)
+        p2[n] = None
+        assert _decode(prob, p2) == NULL, n
+    assert kda.library().kda_decode(None, *([None] * 7), ctypes.c_float(1.0), None, None, None) == NULL
+    prob2, p2, _ = _args(B=8, T=1, dk=96)
+    assert _decode(prob2, p2) == UNSUP
+    assert _decode(prob, p, scale=math.inf) == BAD
+    prob2, p2, _ = _args(B=2, T=1, packed_n=3)  # packed mode needs B == 1
+    assert _decode(prob2, p2, cu=True) == BAD
+    for n in ["q", "h0", "out", "ht"]:
+        p2 = dict(p)
+        p2[n] += 4
+        assert _decode(prob, p2) == ALIGN, n
+    p2 = dict(p)
+    p2["out"] = p2["v"]  # out overlaps v
+    assert _decode(prob, p2) == ALIAS
+    p2 = dict(p)
+    p2["ht"] = p2["h0"] + 512  # partial overlap with h0
+    assert _decode(prob, p2) == ALIAS
