@@ -193,7 +193,7 @@ def extra_measurements(args, lib, kda, make_config, upload, dev, torch, argv1, o
     return res
 
 
-def decode_measurement(args, lib, kda, upload, dev, torch, B=256):
+def decode_measurement(args, lib, kda, upload, dev, torch, B=256, verify=True):
     """One decode step (kda_decode, one token per sequence) of B sequences at H=32, d=128:
     timed like the forward, checked against the oracle, with its HBM roofline (the fp32
     state is read once and written once per call)."""
@@ -221,12 +221,15 @@ def decode_measurement(args, lib, kda, upload, dev, torch, B=256):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    ro, rh = oracle_fwd(y.q, y.k, y.v, y.g, y.beta, y.h0, None, y.scale)
-    eo, eh = rel(o.float().cpu().numpy(), ro), rel(h.cpu().numpy(), rh)
-    good = eo <= TOL and eh <= TOL
+    eo = eh = None
+    good = False
+    if verify:
+        ro, rh = oracle_fwd(y.q, y.k, y.v, y.g, y.beta, y.h0, None, y.scale)
+        eo, eh = rel(o.float().cpu().numpy(), ro), rel(h.cpu().numpy(), rh)
+        good = eo <= TOL and eh <= TOL
     nbytes = Bd * H * (2 * dk * dv * 4 + 2 * dk * 2 + dk * 4 + dv * 2 + 2 + dv * 2)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    log("decode %s: %.4f ms/call, %.0f GB/s, parity out %.2e state %.2e" % (y.name, ms, gbs, eo, eh))
+    log("decode %s: %.4f ms/call, %.0f GB/s, parity out %s state %s" % (y.name, ms, gbs, eo, eh))
     return {"ok": good, "workload": "decode step: %d sequences x 1 token, H=32, dk=dv=128, bf16 io, fp32 state "
                                     "in and out" % Bd,
             "ms_per_step": round(ms, 5), "tokens_per_s": round(Bd * T / (ms * 1e-3), 1) if good else None,
@@ -247,6 +250,8 @@ def main():
     ap.add_argument("--no-verify", action="store_true", help="skip parity (then no speed is reported)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="run only a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time only the decode step (kda_decode, 256 sequences x 1 token); prints its own line")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the varlen workloads and the cold-cache timing (profiling runs)")
     args = ap.parse_args()
@@ -274,6 +279,25 @@ def main():
 
     import gated_delta_rule_39_amd.kda as kda
     from workloads import make_config
+
+    if args.decode:
+        def upload_bf16(y):
+            t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+            return dict(q=t(y.q, torch.bfloat16), k=t(y.k, torch.bfloat16), v=t(y.v, torch.bfloat16),
+                        g=t(y.g, torch.float32), beta=t(y.beta, torch.bfloat16),
+                        h0=None if y.h0 is None else t(y.h0, torch.float32), cu=None)
+        r = decode_measurement(args, kda.library(), kda, upload_bf16, dev, torch, verify=not args.no_verify)
+        ok = r.pop("ok")
+        line = {"metric": "KDA decode step tokens/s (one token per sequence)",
+                "value": r["tokens_per_s"] if ok else None, "unit": "tokens/s", "n_gpus": 1,
+                "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
+                "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+                "data": "synthetic", "config": {"workload": r["workload"]}, "roofline": r["roofline"],
+                "parity": {"out_rel_rmse": r["out_rel_rmse"], "state_rel_rmse": r["state_rel_rmse"]}}
+        print(json.dumps(line), flush=True)
+        if not ok and not args.no_verify:
+            sys.exit(1)
+        return
 
     t0 = time.time()
     x = make_config(args.workload)
