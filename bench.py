@@ -111,7 +111,18 @@ def traffic_from_profiles(kernel):
 
 
 KERNEL_SOURCES = {"chunk_prep_kernel": ["kda_device.h", "kda_prep.h"],
-                  "state_scan_kernel": ["kda_device.h", "kda_scan.h"]}
+                  "state_scan_kernel": ["kda_device.h", "kda_scan.h"],
+                  "fused_fwd_kernel": ["kda_device.h", "kda_prep.h", "kda_scan.h", "kda_kernels.hip"]}
+
+
+def takes_fused_path(x, torch):
+    """The library's choice (csrc/kda_api.cpp): fixed-length rows whose (row, head, 64-column
+    slice) chains fit in a quarter of the compute units run as one fused kernel."""
+    if x.cu_seqlens is not None or os.environ.get("KDA_FUSED", "1")[:1] == "0":
+        return False
+    B, T, H, dk, dv = x.shape
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return T > 0 and B * H * (dv // 64) * 4 <= cus
 
 
 def kernel_source_hash(kernel):
@@ -370,8 +381,13 @@ def main():
     for m in marks:
         for j in range(4):
             hip.hipEventDestroy(m[j])
-    log("timed %d steps: %.4f ms/step (wall %.4f ms/step); kernels: chunk map %.4f ms, chunk %.4f ms, "
-        "scan %.4f ms" % (K, ms_per_step, 1e3 * t_wall / K, k_map, k_prep, k_scan))
+    fused = takes_fused_path(x, torch)
+    if fused:
+        log("timed %d steps: %.4f ms/step (wall %.4f ms/step); kernels: fused forward %.4f ms"
+            % (K, ms_per_step, 1e3 * t_wall / K, k_prep))
+    else:
+        log("timed %d steps: %.4f ms/step (wall %.4f ms/step); kernels: chunk map %.4f ms, chunk %.4f ms, "
+            "scan %.4f ms" % (K, ms_per_step, 1e3 * t_wall / K, k_map, k_prep, k_scan))
 
     tokens = B * T
     value = tokens / (ms_per_step * 1e-3)
@@ -433,11 +449,15 @@ def main():
 
     nch = n_chunks_of(x)
     wk = algorithmic_work(x, nch)
-    dominant = "chunk" if k_prep >= k_scan else "scan"
-    dom_bytes = wk["prep_bytes"] if dominant == "chunk" else wk["scan_bytes"]
-    dom_ms = k_prep if dominant == "chunk" else k_scan
+    if fused:
+        # one kernel does the chunk walk and the scan: its bytes are both kernels' bytes
+        dom_bytes, dom_ms, kname = wk["prep_bytes"] + wk["scan_bytes"], k_prep, "fused_fwd_kernel"
+    else:
+        dominant = "chunk" if k_prep >= k_scan else "scan"
+        dom_bytes = wk["prep_bytes"] if dominant == "chunk" else wk["scan_bytes"]
+        dom_ms = k_prep if dominant == "chunk" else k_scan
+        kname = "chunk_prep_kernel" if dominant == "chunk" else "state_scan_kernel"
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    kname = "chunk_prep_kernel" if dominant == "chunk" else "state_scan_kernel"
     traffic = traffic_from_profiles(kname)
     total_flops = wk["prep_flops"] + wk["scan_flops"]
     res = {
@@ -458,8 +478,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": dom_bytes},
-        "kernels_ms": {"chunk_map": round(float(k_map), 5), "chunk_prep": round(float(k_prep), 5),
-                       "state_scan": round(float(k_scan), 5)},
+        "kernels_ms": ({"chunk_map": round(float(k_map), 5), "fused_fwd": round(float(k_prep), 5)} if fused else
+                       {"chunk_map": round(float(k_map), 5), "chunk_prep": round(float(k_prep), 5),
+                        "state_scan": round(float(k_scan), 5)}),
         "mfma": {"flops_per_step": total_flops,
                  "frac_of_peak": round(total_flops / (ms_per_step * 1e-3) / (MFMA_F16_PEAK_TFLOPS * 1e12), 5),
                  "peak_tflops": MFMA_F16_PEAK_TFLOPS},

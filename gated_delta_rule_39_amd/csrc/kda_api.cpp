@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -18,7 +20,7 @@ constexpr int64_t kChunkTokens = 64;
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct Carve {
-  size_t info, table, seq_off, seq_order, defer, rec, total;
+  size_t info, table, seq_off, seq_order, defer, flags, rec, total;
 };
 
 bool sizes_ok(const kda_problem_t* p, bool packed, int64_t* N, int64_t* n_chunk_ub) {
@@ -52,7 +54,8 @@ Carve carve(const kda_problem_t* p, int64_t N, int64_t n_chunk_ub) {
   c.seq_off = c.table + align256((size_t)n_chunk_ub * 16);
   c.seq_order = c.seq_off + align256((size_t)(N + 1) * 4);
   c.defer = c.seq_order + align256((size_t)N * 4);
-  c.rec = c.defer + align256((size_t)n_chunk_ub * (size_t)p->heads * 4);
+  c.flags = c.defer + align256((size_t)n_chunk_ub * (size_t)p->heads * 4);
+  c.rec = c.flags + align256((size_t)n_chunk_ub * (size_t)p->heads * 8);
   c.total = c.rec + (size_t)n_chunk_ub * (size_t)p->heads * kda::record_bytes(p->dk, p->dv);
   return c;
 }
@@ -98,6 +101,30 @@ int chunk_workgroups() {
     if (v >= 1 && v < n) n = v;
   }
   return n;
+}
+
+// Fused forward (one kernel: chunk walk and scan side by side) for fixed-length rows when
+// the chains are few: the scan then runs on 64-column slices in a quarter of the compute
+// units or less and the chunk walk on the rest.  KDA_FUSED=0 turns it off.  Returns the
+// number of chunk-walk workgroups, 0 for the two-kernel path.
+int fused_producers(const kda_problem_t* p, int64_t N, bool packed) {
+  const char* env = std::getenv("KDA_FUSED");
+  if (env && env[0] == '0') return 0;
+  if (packed || p->seqlen <= 0) return 0;
+  const int64_t cus = compute_units();
+  const int64_t chains = N * (int64_t)p->heads * (p->dv / 64);
+  if (chains * 4 > cus) return 0;
+  const int64_t walk = cus - chains;
+  const int64_t cap = chunk_workgroups();  // KDA_CHUNK_WGS caps the chunk walk here too
+  return (int)(walk < cap ? walk : cap);
+}
+
+// Flag value of a fused call: a process-wide counter from a time-derived start, so that
+// flags left by earlier calls (or uninitialised workspace) do not match.
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> counter{
+      (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9E3779B97F4A7C15ull | 1ull};
+  return counter.fetch_add(2, std::memory_order_relaxed);
 }
 
 }  // namespace
@@ -227,6 +254,9 @@ static kda_status_t forward(const kda_problem_t* prob, const void* q, const void
   p.seq_order = reinterpret_cast<int32_t*>(ws + c.seq_order);
   p.rec = ws + c.rec;
   p.defer = reinterpret_cast<int32_t*>(ws + c.defer);
+  p.flags = reinterpret_cast<uint64_t*>(ws + c.flags);
+  p.fuse_producers = fused_producers(prob, N, packed);
+  p.epoch = p.fuse_producers > 0 ? next_epoch() : 0;
   p.slice = slice_width(prob, N);
   p.chunk_wgs = chunk_workgroups();
   for (int i = 0; i < 4; ++i) p.marks[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;

@@ -146,6 +146,43 @@ struct Rec {
   static constexpr size_t BYTES = (HDR + 16 + 255) / 256 * 256;
 };
 
+// Raw buffer resources (record stores and loads of the fused kernel): dword 3 with a 32-bit
+// data format, byte offsets, no swizzle; accesses past num_records are dropped.
+constexpr int kBufferFlags = 0x00020000;
+typedef uint32_t uint4_v __attribute__((ext_vector_type(4)));
+typedef uint32_t uint2_v __attribute__((ext_vector_type(2)));
+
+// Record loads.  COHERENT (the scan role of the fused kernel): device-scope (sc1) buffer
+// loads, which see records that another compute die wrote through; otherwise plain loads.
+template <typename V, bool COHERENT>
+__device__ __forceinline__ V rec_load(const uint8_t* rec, int bytes, size_t off) {
+  if constexpr (COHERENT) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(rec), 0, bytes, kBufferFlags);
+    if constexpr (sizeof(V) == 16) {
+      return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 16));
+    } else if constexpr (sizeof(V) == 8) {
+      return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, 16));
+    } else {
+      return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, 16));
+    }
+  } else {
+    return *reinterpret_cast<const V*>(rec + off);
+  }
+}
+
+// Hand-off between the two roles of the fused forward kernel: the chunk workgroups
+// publish each (chunk, head) record by writing `epoch` into its flag once the record's
+// stores have completed, the scan workgroups wait for the flag before loading the record.
+// Records and flags move only through device-scope (sc1) stores and loads, which are
+// coherent across the compute dies without L2 write-backs or invalidations.  A new epoch
+// per call means the flags never need clearing.
+struct FuseArgs {
+  uint64_t* flags;     // [chunk * H + head]
+  uint64_t epoch;
+  int32_t producers;   // workgroups 0 .. producers-1 run the chunk walk, the rest the scan
+  int32_t spin_limit;  // polls (about 130 cycles each) before a wait gives up
+};
+
 // One entry of the chunk table.
 struct ChunkEntry {
   int32_t seq;   // sequence index

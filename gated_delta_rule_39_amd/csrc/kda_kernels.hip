@@ -63,9 +63,72 @@ static hipError_t launch_scan(const ForwardPlan& p, hipStream_t stream) {
   }
 }
 
+// Fused forward: workgroups 0 .. producers-1 walk the chunks (in the order the scan
+// consumes them) and publish each record; the others each walk one (row, head, 64-column
+// slice) chain, waiting for each record before loading it.  The chunk workgroups never
+// wait on anything, and they have the lower block ids, so they are dispatched first.
+template <int DK, int DV, typename InT>
+__global__ __launch_bounds__(kPrepThreads, 1) void fused_fwd_kernel(PrepArgs pa, ScanArgs sa, FuseArgs fz) {
+  static_assert(kPrepThreads == kScanThreads, "one block size for both roles");
+  extern __shared__ __align__(16) uint8_t smem[];
+  if ((int)blockIdx.x < fz.producers)
+    chunk_walk<DK, DV, InT, true>(pa, fz, (int)blockIdx.x, fz.producers, smem);
+  else
+    scan_chain<DK, DV, 64, InT, true>(sa, fz, (int64_t)blockIdx.x - fz.producers,
+                                      (int64_t)gridDim.x - fz.producers, smem);
+}
+
+static PrepArgs prep_args(const ForwardPlan& p) {
+  PrepArgs a;
+  a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.beta = p.beta; a.cu = p.cu;
+  a.T = p.T; a.T_total = p.T_total; a.H = p.H;
+  a.info = p.info;
+  a.nc = p.cu ? 0 : (p.T + kChunk - 1) / kChunk;
+  a.table = reinterpret_cast<const ChunkEntry*>(p.table);
+  a.rec = p.rec;
+  a.defer = p.defer;
+  return a;
+}
+
+static ScanArgs scan_args(const ForwardPlan& p) {
+  ScanArgs a;
+  a.h0 = p.h0; a.ht = p.ht; a.out = p.out; a.cu = p.cu;
+  a.T = p.T; a.T_total = p.T_total; a.N = p.N; a.H = p.H; a.n_chunk_ub = p.n_chunk_ub;
+  a.seq_off = p.seq_off; a.seq_order = p.seq_order; a.rec = p.rec; a.scale = p.scale;
+  a.nc = p.cu ? 0 : (p.T + kChunk - 1) / kChunk;
+  return a;
+}
+
+template <int DK, int DV, typename InT>
+static hipError_t launch_fused(const ForwardPlan& p, hipStream_t stream) {
+  FuseArgs fz;
+  fz.flags = p.flags;
+  fz.epoch = p.epoch;
+  fz.producers = p.fuse_producers;
+  // a wait never needs longer than the whole chunk walk (about 10 us per item and
+  // workgroup, a poll about 60 ns): allow several times that
+  const int64_t per_wg = p.n_chunk_ub * (int64_t)p.H / p.fuse_producers + 2;
+  const int64_t spins = per_wg * 1000;
+  fz.spin_limit = (int32_t)(spins < (1 << 16) ? (1 << 16) : (spins > (1 << 30) ? (1 << 30) : spins));
+  const size_t s1 = PrepSmem<DK, DV>::BYTES, s2 = ScanSmem<DK, DV, 64>::BYTES;
+  const size_t smem = s1 > s2 ? s1 : s2;
+  auto kern = fused_fwd_kernel<DK, DV, InT>;
+  hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  const int64_t chains = p.N * (int64_t)p.H * (DV / 64);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(p.fuse_producers + chains)), dim3(kPrepThreads), smem, stream,
+                     prep_args(p), scan_args(p), fz);
+  return hipGetLastError();
+}
+
 template <int DK, int DV>
 static hipError_t launch_dkdv(const ForwardPlan& p, hipStream_t stream) {
   hipError_t e = hipSuccess;
+  if (p.fuse_producers > 0) {
+    e = (p.dtype == 0) ? launch_fused<DK, DV, uint16_t>(p, stream) : launch_fused<DK, DV, float>(p, stream);
+    mark(p, 2, stream);
+    mark(p, 3, stream);
+    return e;
+  }
   if (p.T_total > 0) {
     e = (p.dtype == 0) ? launch_prep<DK, DV, uint16_t>(p, stream) : launch_prep<DK, DV, float>(p, stream);
     if (e != hipSuccess) return e;

@@ -29,6 +29,9 @@ struct ForwardPlan {
   int32_t* seq_order;
   uint8_t* rec;
   int32_t* defer;  // per (chunk, head): the item needs the exact diagonal tiles (chunk kernel scratch)
+  uint64_t* flags;        // per (chunk, head): record-ready flags of the fused kernel
+  uint64_t epoch;         // this call's flag value (fused kernel)
+  int32_t fuse_producers;  // > 0: one fused kernel, this many workgroups run the chunk walk
   int32_t slice;  // value columns per scan workgroup (16, 32 or 64)
   int32_t chunk_wgs;  // workgroups of the persistent chunk kernel (>= 1)
   hipEvent_t marks[4];  // optional timing marks around the kernels (may be null)

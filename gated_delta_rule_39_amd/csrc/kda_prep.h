@@ -306,12 +306,31 @@ __device__ __forceinline__ void subst_rows(float (&x)[4], const float (&am)[16])
   if constexpr (J + 1 < 15) subst_rows<J + 1>(x, am);
 }
 
+// Record stores.  WT (the fused kernel): device-scope stores (sc1), which write through
+// the L2 of the compute die, so that once they complete the record is visible to the scan
+// workgroups on every die; otherwise plain stores, kept in L2 for the scan kernel.
+template <bool WT, int BYTES, typename V>
+__device__ __forceinline__ void rec_store(uint8_t* rec, size_t off, const V& v) {
+  if constexpr (WT) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(rec, 0, BYTES, kBufferFlags);
+    if constexpr (sizeof(V) == 16) {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4_v, v), rs, (int)off, 0, 16);
+    } else if constexpr (sizeof(V) == 8) {
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2_v, v), rs, (int)off, 0, 16);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, (int)off, 0, 16);
+    }
+  } else {
+    *reinterpret_cast<V*>(rec + off) = v;
+  }
+}
+
 // One (chunk, head) from its fp32 inputs.  EXACT = false: guarded fp32 diagonal tiles,
 // the chunk is deferred when the guard fails.  EXACT = true: per-group references on
 // every diagonal tile.  Every wave of the workgroup calls it (it holds barriers).
 // `mid(1)`, `mid(2)` and `mid(3)` run right after barriers #1, #2 and #4 (the persistent kernel
 // issues the next item's remaining loads there).
-template <int DK, int DV, bool EXACT, typename Mid>
+template <int DK, int DV, bool EXACT, bool WT, typename Mid>
 __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, const int h, ItemIn<DK, DV>& in,
                                           uint8_t* smem, Mid&& mid) {
   using R = Rec<DK, DV>;
@@ -552,14 +571,14 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
         bwr[sl][e] = (_Float16)(bt * XB[8 * sl + e] * eS[e]); // beta khat exp(G)
         y[e] = (_Float16)YC[8 * sl + e];
       }
-      *reinterpret_cast<f16x8*>(rec + R::Q + ((size_t)(w * KSK + s) * 64 + l) * 16) = qf;
+      rec_store<WT, R::BYTES>(rec, R::Q + ((size_t)(w * KSK + s) * 64 + l) * 16, qf);
       // K~^T fragments: (K~ I) holds, per lane, key channel 16 ct + t at tokens 16 w + 4 gq + r
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const f32x4 c = mfma16(kf, ident[hh], zero4());
         const int ct = 2 * s + hh;
         f16x4 h4 = {(_Float16)c[0], (_Float16)c[1], (_Float16)c[2], (_Float16)c[3]};
-        *reinterpret_cast<f16x4*>(rec + R::KT + ((size_t)(ct * 2 + (w >> 1)) * 64 + l) * 16 + (w & 1) * 8) = h4;
+        rec_store<WT, R::BYTES>(rec, R::KT + ((size_t)(ct * 2 + (w >> 1)) * 64 + l) * 16 + (w & 1) * 8, h4);
       }
       // column-side operands of the off-diagonal Gram tiles (reference = end of block w)
       ybf[(w * KSK + s) * 64 + l] = y;  // block 3's slot is never read (no branch around the store)
@@ -575,10 +594,10 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
         *reinterpret_cast<f16x4*>(bux + ((size_t)((2 * sv + hh) * 2 + (w >> 1)) * 64 + l) * 16 + (w & 1) * 8) = h4;
       }
     }
-    if (tid < DK) reinterpret_cast<float*>(rec + R::LAM)[tid] = exp2_hw(gend[15 * DK + tid]);
+    if (tid < DK) rec_store<WT, R::BYTES>(rec, R::LAM + (size_t)tid * 4, exp2_hw(gend[15 * DK + tid]));
     if (tid == 0) {
-      reinterpret_cast<float*>(rec + R::HDR)[0] = vmax;
-      reinterpret_cast<int32_t*>(rec + R::HDR)[1] = ue;
+      rec_store<WT, R::BYTES>(rec, R::HDR, vmax);
+      rec_store<WT, R::BYTES>(rec, R::HDR + 4, ue);
     }
   }
   __syncthreads();  // #4: column operands visible
@@ -804,7 +823,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
         f[r] = (_Float16)full[2 * s2][r];
         f[4 + r] = (_Float16)full[2 * s2 + 1][r];
       }
-      *reinterpret_cast<f16x8*>(rec + R::A + ((size_t)(w * 2 + s2) * 64 + l) * 16) = f;
+      rec_store<WT, R::BYTES>(rec, R::A + ((size_t)(w * 2 + s2) * 64 + l) * 16, f);
     }
   }
   // Bw^T fragments through identity products (rows = key channels, tokens in pi order)
@@ -925,7 +944,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
       }
       f16x8 wf = {(_Float16)c0[0], (_Float16)c0[1], (_Float16)c0[2], (_Float16)c0[3],
                   (_Float16)c1[0], (_Float16)c1[1], (_Float16)c1[2], (_Float16)c1[3]};
-      *reinterpret_cast<f16x8*>(rec + R::W + ((size_t)(w * KSK + sk) * 64 + l) * 16) = wf;
+      rec_store<WT, R::BYTES>(rec, R::W + ((size_t)(w * KSK + sk) * 64 + l) * 16, wf);
     }
 #pragma unroll
     for (int ntl = 0; ntl < NTV / 2; ++ntl) {
@@ -937,7 +956,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
         c = mfma16(tf[s], bfr, c);
       }
       f16x4 uf = {(_Float16)c[0], (_Float16)c[1], (_Float16)c[2], (_Float16)c[3]};
-      *reinterpret_cast<f16x4*>(rec + R::U + ((size_t)(w * NTV + nt) * 64 + l) * 8) = uf;
+      rec_store<WT, R::BYTES>(rec, R::U + ((size_t)(w * NTV + nt) * 64 + l) * 8, uf);
     }
   }
 }
@@ -956,18 +975,36 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
 // wait for the stores (one in-order counter covers both).
 //
 // After its walk, each workgroup redoes its own flagged items with the exact variant.
-template <int DK, int DV, typename InT>
-__global__ __launch_bounds__(kPrepThreads, 1) void chunk_prep_kernel(PrepArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];
+//
+// FUSED (the chunk role of the fused forward kernel, fixed-length rows only): the walk
+// goes in the order the scan consumes, every row's first chunk first, and each record is
+// published (device-scope release, then its flag) as soon as it is final: right after
+// its item, or after the exact pass for a flagged item.
+template <int DK, int DV, typename InT, bool FUSED>
+__device__ __forceinline__ void chunk_walk(const PrepArgs& a, const FuseArgs& fz, const int wg, const int n_wg,
+                                           uint8_t* smem) {
   // items (fewer than 2^31), kept in scalar registers
-  const int n_items = (a.cu ? (int)sload_u32(a.info) : (int)(a.nc * (a.T_total / (a.T > 0 ? a.T : 1)))) * a.H;
-  int it = blockIdx.x;
+  const int n_rows = (int)(a.T_total / (a.T > 0 ? a.T : 1));
+  const int n_items = (a.cu ? (int)sload_u32(a.info) : (int)(a.nc * n_rows)) * a.H;
+  int it = wg;
   if (it >= n_items) return;  // uniform for the workgroup
   auto entry = [&](int c) { return a.cu ? ld_entry(a.table + c) : entry_fixed(a, c); };
   // chunks from the last to the first: the records the scan reads first are written last
-  // and are still in the caches (L2, MALL) when it starts
+  // and are still in the caches (L2, MALL) when it starts.  Fused: position p holds chunk
+  // p / rows of row p % rows.
   const int n_chunks = n_items / a.H;
-  auto chunk_of = [&](int x) { return n_chunks - 1 - x / a.H; };
+  auto chunk_of = [&](int x) {
+    const int pos = x / a.H;
+    return FUSED ? (pos % n_rows) * (int)a.nc + pos / n_rows : n_chunks - 1 - pos;
+  };
+  // every wave's record stores (written through at device scope) complete, then the flag
+  // (a device-scope store)
+  auto publish = [&](int chunk, int h, bool ready) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0 && ready)
+      __hip_atomic_store(fz.flags + (size_t)chunk * a.H + h, fz.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   auto head_of = [&](int x) { return (x % a.H + x / a.H) % a.H; };
   // Where the chunks of this workgroup's first 64 items start and how many tokens they
   // hold, staged in LDS (entry j: item blockIdx.x + j * gridDim.x) with one batch of
@@ -975,7 +1012,7 @@ __global__ __launch_bounds__(kPrepThreads, 1) void chunk_prep_kernel(PrepArgs a)
   // metadata loads.  Later items (more than 64 per workgroup) read the chunk table.
   int4* meta = reinterpret_cast<int4*>(smem + PrepSmem<DK, DV>::META);
   if (threadIdx.x < 64) {
-    const int64_t item = (int64_t)blockIdx.x + (int64_t)threadIdx.x * gridDim.x;
+    const int64_t item = (int64_t)wg + (int64_t)threadIdx.x * n_wg;
     int4 m = make_int4(0, 0, 0, 0);
     if (item < n_items) {
       const ChunkEntry e = a.cu ? a.table[chunk_of((int)item)] : entry_fixed(a, chunk_of((int)item));
@@ -1007,45 +1044,63 @@ __global__ __launch_bounds__(kPrepThreads, 1) void chunk_prep_kernel(PrepArgs a)
     }
     unpack_raw(in, raw);
     for (int j = 0;; ++j) {
-      const int nx = __builtin_amdgcn_readfirstlane(it + (int)gridDim.x);
+      const int nx = __builtin_amdgcn_readfirstlane(it + n_wg);
       const bool more = nx < n_items;
       const RawAt at = at_of(more ? j + 1 : j, more ? nx : it);
       load_part<0>(raw, a, at);
-      prep_item<DK, DV, false>(a, chunk_of(it), head_of(it), in, smem, [&](int phase) {
+      prep_item<DK, DV, false, FUSED>(a, chunk_of(it), head_of(it), in, smem, [&](int phase) {
         if (phase == 1) load_part<1>(raw, a, at);
         if (phase == 2) load_part<2>(raw, a, at);
         if (phase == 3) load_part<3>(raw, a, at);
       });
-      unpack_raw(in, raw);
-      if (!more) break;
-      __syncthreads();  // LDS is rewritten by the next item
+      if (FUSED) {
+        // the guard flag of this item, before the next item resets it
+        const bool deferred = *reinterpret_cast<volatile int*>(smem + PrepSmem<DK, DV>::RED + 32) != 0;
+        unpack_raw(in, raw);
+        publish(chunk_of(it), head_of(it), !deferred);  // its barrier also guards the LDS reuse
+        if (!more) break;
+      } else {
+        unpack_raw(in, raw);
+        if (!more) break;
+        __syncthreads();  // LDS is rewritten by the next item
+      }
       it = nx;
     }
   }
   __syncthreads();  // LDS is rewritten below; this workgroup's flags are visible to it
 
   // exact pass over this workgroup's flagged items, 64 items per batch of flag loads
-  const int n_own = (n_items - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int n_own = (n_items - wg + n_wg - 1) / n_wg;
   const int lane = threadIdx.x & 63;
   for (int kb = 0; kb < n_own; kb += 64) {
     int f = 0;
     if (kb + lane < n_own) {
-      const int x = (int)blockIdx.x + (kb + lane) * (int)gridDim.x;
+      const int x = wg + (kb + lane) * n_wg;
       f = a.defer[(size_t)chunk_of(x) * a.H + head_of(x)];
     }
     uint64_t bits = __ballot(f != 0);  // the same in every wave
     while (bits) {
       const int b = __builtin_ctzll(bits);
       bits &= bits - 1;
-      const int x = __builtin_amdgcn_readfirstlane((int)blockIdx.x + (kb + b) * (int)gridDim.x);
+      const int x = __builtin_amdgcn_readfirstlane(wg + (kb + b) * n_wg);
       RawIn<DK, DV, InT> raw;
       load_raw(raw, a, entry(chunk_of(x)), head_of(x));
       ItemIn<DK, DV> in;
       unpack_raw(in, raw);
-      prep_item<DK, DV, true>(a, chunk_of(x), head_of(x), in, smem, [](int) {});
-      __syncthreads();  // LDS is rewritten by the next item
+      prep_item<DK, DV, true, FUSED>(a, chunk_of(x), head_of(x), in, smem, [](int) {});
+      if (FUSED) {
+        publish(chunk_of(x), head_of(x), true);
+      } else {
+        __syncthreads();  // LDS is rewritten by the next item
+      }
     }
   }
+}
+
+template <int DK, int DV, typename InT>
+__global__ __launch_bounds__(kPrepThreads, 1) void chunk_prep_kernel(PrepArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  chunk_walk<DK, DV, InT, false>(a, FuseArgs{}, (int)blockIdx.x, (int)gridDim.x, smem);
 }
 
 }  // namespace kda

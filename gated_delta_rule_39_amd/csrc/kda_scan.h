@@ -87,6 +87,7 @@ struct TokRegs {
   f16x8 af[2];
   f16x4 uf[NT];
   int ue;
+  float vmax;  // max |v| of the chunk (read only by the fused kernel)
 };
 
 // Chunk factors of one key-block wave: its row tiles of (Khat*exp(G_last-G))^T
@@ -99,55 +100,71 @@ struct KeyRegs {
   static constexpr int TPK = DK / 64;  // 16-row tiles per key wave
   f16x8 kt[TPK][2];
   float lam[TPK];
+  float vmax;  // max |v| of the chunk (read only by the fused kernel)
 };
 
 // The loads of a chunk's factors are issued in groups spread over the previous chunk's
 // step, so that the eight waves never queue all of them on the vector-memory path at
 // once.  Token waves: 0 = W, 1 = Qhat*exp(G), 2 = Aqk, U and ue.  Key waves: 0 = K~^T,
 // 1 = exp(G_last).
-template <int PART, int DK, int DV, int NV>
+template <int PART, int DK, int DV, int NV, bool FUSED = false>
 __device__ __forceinline__ void load_tok(TokRegs<DK, NV>& c, const uint8_t* rec, int i, int l, int slice) {
   using R = Rec<DK, DV>;
   using TR = TokRegs<DK, NV>;
   if (PART == 0) {
 #pragma unroll
     for (int s = 0; s < TR::KSK; ++s)
-      c.wf[s] = *reinterpret_cast<const f16x8*>(rec + R::W + ((size_t)(i * TR::KSK + s) * 64 + l) * 16);
+      c.wf[s] = rec_load<f16x8, FUSED>(rec, R::BYTES, R::W + ((size_t)(i * TR::KSK + s) * 64 + l) * 16);
   } else if (PART == 1) {
 #pragma unroll
     for (int s = 0; s < TR::KSK; ++s)
-      c.qf[s] = *reinterpret_cast<const f16x8*>(rec + R::Q + ((size_t)(i * TR::KSK + s) * 64 + l) * 16);
+      c.qf[s] = rec_load<f16x8, FUSED>(rec, R::BYTES, R::Q + ((size_t)(i * TR::KSK + s) * 64 + l) * 16);
   } else {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
-      c.af[s2] = *reinterpret_cast<const f16x8*>(rec + R::A + ((size_t)(i * 2 + s2) * 64 + l) * 16);
+      c.af[s2] = rec_load<f16x8, FUSED>(rec, R::BYTES, R::A + ((size_t)(i * 2 + s2) * 64 + l) * 16);
 #pragma unroll
     for (int nt = 0; nt < TR::NT; ++nt)
-      c.uf[nt] = *reinterpret_cast<const f16x4*>(rec + R::U + ((size_t)(i * R::NTV + slice * TR::NT + nt) * 64 + l) * 8);
-    c.ue = reinterpret_cast<const int32_t*>(rec + R::HDR)[1];
+      c.uf[nt] = rec_load<f16x4, FUSED>(rec, R::BYTES, R::U + ((size_t)(i * R::NTV + slice * TR::NT + nt) * 64 + l) * 8);
+    c.ue = rec_load<int32_t, FUSED>(rec, R::BYTES, R::HDR + 4);
+    if (FUSED) c.vmax = rec_load<float, true>(rec, R::BYTES, R::HDR);
   }
 }
 
-template <int PART, int DK, int DV>
+template <int PART, int DK, int DV, bool FUSED = false>
 __device__ __forceinline__ void load_key(KeyRegs<DK>& c, const uint8_t* rec, int m, int l) {
   using R = Rec<DK, DV>;
   using KR = KeyRegs<DK>;
   const int gq = l >> 4;
+  if (FUSED && PART == 0) c.vmax = rec_load<float, true>(rec, R::BYTES, R::HDR);
 #pragma unroll
   for (int p = 0; p < KR::TPK; ++p) {
     const int ct = KR::TPK * m + p;
     if (PART == 0) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
-        c.kt[p][s2] = *reinterpret_cast<const f16x8*>(rec + R::KT + ((size_t)(ct * 2 + s2) * 64 + l) * 16);
+        c.kt[p][s2] = rec_load<f16x8, FUSED>(rec, R::BYTES, R::KT + ((size_t)(ct * 2 + s2) * 64 + l) * 16);
     } else {
-      c.lam[p] = *reinterpret_cast<const float*>(rec + R::LAM + (size_t)(16 * ct + 4 * gq + (l & 3)) * 4);
+      c.lam[p] = rec_load<float, FUSED>(rec, R::BYTES, R::LAM + (size_t)(16 * ct + 4 * gq + (l & 3)) * 4);
     }
   }
 }
 
-template <int DK, int DV, int NV, typename OutT>
-__global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
+// Exponent es of the fp16 state and Delta copies for a bound B^2 = b2 on the state's
+// column norms (2^es B <= 2^14).
+__device__ inline int copy_exponent(double b2) {
+  int es = 0;
+  if (b2 > 0.0 && b2 < 1e300) es = 14 - (ilogb(sqrt(b2)) + 1);
+  return es < -250 ? -250 : (es > 250 ? 250 : es);
+}
+
+// One scan workgroup: chain `bid` of `nblk`.  FUSED: the chunk records are produced while
+// the chain walks them (the fused forward kernel): each chunk's ready flag is awaited
+// before its factors are loaded, and the copy exponent follows the running bound over the
+// chunks walked so far instead of the whole sequence's.
+template <int DK, int DV, int NV, typename OutT, bool FUSED>
+__device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz, const int64_t bid,
+                                           const int64_t nblk, uint8_t* smem) {
   using R = Rec<DK, DV>;
   using SM = ScanSmem<DK, DV, NV>;
   using TR = TokRegs<DK, NV>;
@@ -157,8 +174,8 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
   constexpr int NT = NV / 16;
   constexpr int NS = DV / NV;
   constexpr int kScanDepth = scan_depth<NV>();
+  static_assert(!FUSED || kScanDepth == 2, "the fused walk reads the next chunk's header from the ring");
 
-  extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* sbb = smem + SM::SB;
   uint8_t* db = smem + SM::DB;
   float* cn = reinterpret_cast<float*>(smem + SM::CN);
@@ -172,8 +189,6 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
   // Workgroups are dispatched round-robin over the 8 XCDs (block id mod 8).  The NS
   // slices of one (sequence, head) share every chunk factor except U, so they are
   // mapped to block ids with equal residue mod 8: one XCD's L2 serves all of them.
-  const int64_t nblk = (int64_t)gridDim.x;
-  const int64_t bid = blockIdx.x;
   int64_t chain, slice_l;
   if (nblk % (8 * NS) == 0) {
     const int64_t xcd = bid & 7, k = bid >> 3;
@@ -210,8 +225,10 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
 
   // power-of-two scale of the fp16 copies from the bound B (see the file comment)
   float vm = 0.f;
-  for (int64_t c = c0 + tid; c < c1; c += kScanThreads)
-    vm = fmaxf(vm, reinterpret_cast<const float*>(a.rec + ((size_t)c * a.H + h) * R::BYTES + R::HDR)[0]);
+  if (!FUSED) {
+    for (int64_t c = c0 + tid; c < c1; c += kScanThreads)
+      vm = fmaxf(vm, reinterpret_cast<const float*>(a.rec + ((size_t)c * a.H + h) * R::BYTES + R::HDR)[0]);
+  }
   vm = wave_max(vm);
   if (l == 0) red[wv] = vm;
   if (!tok_wave) {
@@ -232,12 +249,36 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
   float vmax = red[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) vmax = fmaxf(vmax, red[j]);
-  int es = 0;
-  {
-    const double b2 = (double)cmax + (double)L * (double)vmax * (double)vmax;
-    if (b2 > 0.0 && b2 < 1e300) es = 14 - (ilogb(sqrt(b2)) + 1);
-    es = es < -250 ? -250 : (es > 250 ? 250 : es);
-  }
+  int es = copy_exponent((double)cmax + (double)L * (double)vmax * (double)vmax);
+  // fused: running maximum of max|v| over the chunks walked so far, and the bound at the
+  // end of chunk c (the state's column norms after t tokens are at most cmax + t vmax^2)
+  float vrun = 0.f;
+  auto es_at = [&](int64_t c, float vmax_c) {
+    vrun = fmaxf(vrun, vmax_c);
+    const int64_t toks = (c - c0 + 1) * kChunk < L ? (c - c0 + 1) * kChunk : L;
+    return copy_exponent((double)cmax + (double)toks * (double)vrun * (double)vrun);
+  };
+  // fused: wait until chunk c's record is complete (bounded: a flag that never comes
+  // ends the wait, the walk then reads whatever the record holds).  The flag is read one
+  // step ahead (`pre`), so a record that is already published costs no round trip.
+  uint64_t pre = 0;
+  auto prepoll = [&](int64_t c) {
+    if (FUSED && c < c1) pre = __hip_atomic_load(fz.flags + (size_t)c * a.H + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto await_chunk = [&](int64_t c) {
+    if (FUSED && c < c1) {
+      const uint64_t* fl = fz.flags + (size_t)c * a.H + h;
+      int spins = 0;
+      if (pre != fz.epoch) {
+        while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != fz.epoch && spins < fz.spin_limit) {
+          __builtin_amdgcn_s_sleep(2);
+          ++spins;
+        }
+      }
+      pre = 0;
+      asm volatile("" ::: "memory");  // the record's loads stay after the wait
+    }
+  };
 
   // fp16 S0 fragments of k-step s, column tile nt: slot half (ct & 1) of [(ct / 2) * NT + nt]
   auto write_state = [&](int buf) {
@@ -254,8 +295,10 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
       }
     }
   };
-  if (!tok_wave) write_state(0);
-  __syncthreads();  // S0 of the first chunk visible
+  if (!FUSED) {
+    if (!tok_wave) write_state(0);
+    __syncthreads();  // S0 of the first chunk visible
+  }
 
   OutT* out = reinterpret_cast<OutT*>(a.out);
   const float oscale = a.scale;
@@ -267,7 +310,12 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
   if (tok_wave) {
     // ---- token block i: Delta rows, then the output rows ----
     auto step = [&](const TR& cur, TR& nxt, const uint8_t* nrec, int64_t c) {
-      load_tok<0, DK, DV, NV>(nxt, nrec, i, l, slice);
+      if (FUSED) {
+        es = es_at(c, cur.vmax);
+        await_chunk(c + kScanDepth - 1);
+        prepoll(c + kScanDepth);
+      }
+      load_tok<0, DK, DV, NV, FUSED>(nxt, nrec, i, l, slice);
       const f16x8* sb = reinterpret_cast<const f16x8*>(sbb + (size_t)((c - c0) & 1) * SM::SBUF);
       // all S0 fragments at once, so that the MFMA chains below never wait on LDS one by one
       f16x8 sf[KSK][NT];
@@ -290,7 +338,7 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
         for (int r = 0; r < 4; ++r) df[r] = (_Float16)(ldexpf((float)cur.uf[nt][r], es - cur.ue) - d[nt][r]);
         *reinterpret_cast<f16x4*>(db + (((size_t)(i >> 1) * NT + nt) * 64 + l) * 16 + (i & 1) * 8) = df;
       }
-      load_tok<1, DK, DV, NV>(nxt, nrec, i, l, slice);
+      load_tok<1, DK, DV, NV, FUSED>(nxt, nrec, i, l, slice);
       // o^T, inter-chunk part: S0^T (Qhat exp(G))^T
       f32x4 o[NT];
 #pragma unroll
@@ -300,7 +348,7 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) o[nt] = mfma16(sf[s][nt], cur.qf[s], o[nt]);
       __syncthreads();  // A: Delta complete
-      load_tok<2, DK, DV, NV>(nxt, nrec, i, l, slice);
+      load_tok<2, DK, DV, NV, FUSED>(nxt, nrec, i, l, slice);
       // o^T, intra-chunk part: Delta^T Aqk^T; then 4 consecutive value columns per lane
       f16x8 dfr[2][NT];
 #pragma unroll
@@ -330,14 +378,17 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
     };
     // Ring of kScanDepth register buffers: the factors of chunk c + kScanDepth - 1 are
     // requested while chunk c is processed (the HBM latency spans several steps).
+    if (FUSED && c0 >= c1) __syncthreads();  // the first-state barrier of the key waves
     if (c0 < c1) {
       TR buf[kScanDepth];
 #pragma unroll
       for (int j = 0; j < kScanDepth - 1; ++j) {
-        load_tok<0, DK, DV, NV>(buf[j], rec_of(c0 + j), i, l, slice);
-        load_tok<1, DK, DV, NV>(buf[j], rec_of(c0 + j), i, l, slice);
-        load_tok<2, DK, DV, NV>(buf[j], rec_of(c0 + j), i, l, slice);
+        await_chunk(c0 + j);
+        load_tok<0, DK, DV, NV, FUSED>(buf[j], rec_of(c0 + j), i, l, slice);
+        load_tok<1, DK, DV, NV, FUSED>(buf[j], rec_of(c0 + j), i, l, slice);
+        load_tok<2, DK, DV, NV, FUSED>(buf[j], rec_of(c0 + j), i, l, slice);
       }
+      if (FUSED) __syncthreads();  // S0 of the first chunk visible
       // whole groups of kScanDepth steps (no conditional step: the compiler's memory-counter
       // waits then stay exact across iterations), then the remaining steps
       int64_t c = c0;
@@ -353,7 +404,11 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
   } else {
     // ---- key block i: S_next = Diag(exp(G_last)) S0 + K~^T Delta ----
     auto step = [&](const KR& cur, KR& nxt, const uint8_t* nrec, int64_t c) {
-      load_key<0, DK, DV>(nxt, nrec, i, l);
+      if (FUSED) {
+        await_chunk(c + kScanDepth - 1);
+        prepoll(c + kScanDepth);
+      }
+      load_key<0, DK, DV, FUSED>(nxt, nrec, i, l);
       __syncthreads();  // A: Delta complete
       f16x8 dfr[2][NT];
 #pragma unroll
@@ -374,16 +429,28 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
           for (int r = 0; r < 4; ++r) S[p][nt][r] = fmaf(lam[r], S[p][nt][r], ldexpf(u[r], -es));
         }
       }
-      load_key<1, DK, DV>(nxt, nrec, i, l);
+      load_key<1, DK, DV, FUSED>(nxt, nrec, i, l);
+      // the next chunk's copy exponent (the same value its token waves derive)
+      if (FUSED && c + 1 < c1) es = es_at(c + 1, nxt.vmax);
       write_state((int)((c - c0 + 1) & 1));
       __syncthreads();  // B: next S0 complete
     };
+    if (FUSED && c0 >= c1) {
+      write_state(0);
+      __syncthreads();  // the first-state barrier
+    }
     if (c0 < c1) {
       KR buf[kScanDepth];
 #pragma unroll
       for (int j = 0; j < kScanDepth - 1; ++j) {
-        load_key<0, DK, DV>(buf[j], rec_of(c0 + j), i, l);
-        load_key<1, DK, DV>(buf[j], rec_of(c0 + j), i, l);
+        await_chunk(c0 + j);
+        load_key<0, DK, DV, FUSED>(buf[j], rec_of(c0 + j), i, l);
+        load_key<1, DK, DV, FUSED>(buf[j], rec_of(c0 + j), i, l);
+      }
+      if (FUSED) {
+        es = es_at(c0, buf[0].vmax);
+        write_state(0);
+        __syncthreads();  // S0 of the first chunk visible
       }
       int64_t c = c0;
       for (; c + kScanDepth <= c1; c += kScanDepth) {
@@ -407,6 +474,12 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
           }
     }
   }
+}
+
+template <int DK, int DV, int NV, typename OutT>
+__global__ __launch_bounds__(kScanThreads) void state_scan_kernel(ScanArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  scan_chain<DK, DV, NV, OutT, false>(a, FuseArgs{}, blockIdx.x, gridDim.x, smem);
 }
 
 }  // namespace kda

@@ -111,6 +111,8 @@ def test_in_place_state_update():
 # hundreds of items, fixed-length and packed.
 @pytest.mark.parametrize("packed", [False, True])
 def test_long_walks_of_the_chunk_kernel(packed, monkeypatch):
+    """Three chunk workgroups (KDA_CHUNK_WGS=3): long persistent walks; fixed-length rows
+    take the fused kernel, whose scan workgroups then wait on most records."""
     monkeypatch.setenv("KDA_CHUNK_WGS", "3")
     if packed:
         lens = [700, 1, 64, 1333, 0, 999, 65, 1000]
@@ -124,5 +126,27 @@ def test_long_walks_of_the_chunk_kernel(packed, monkeypatch):
 @pytest.mark.parametrize("slice_", ["16", "32", "64"])
 def test_scan_slice_widths(slice_, monkeypatch):
     monkeypatch.setenv("KDA_SCAN_SLICE", slice_)
+    monkeypatch.setenv("KDA_FUSED", "0")  # the slice width belongs to the two-kernel path
     x = make_inputs(1, 333, 3, 128, 128, seed=5, dtype="bf16")
     _check(x, "scan slice %s" % slice_)
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv", [(1, 1000, 4, 128, 128), (2, 777, 3, 64, 128), (3, 130, 5, 128, 64),
+                                         (1, 64, 32, 128, 128)])
+def test_fused_and_two_kernel_paths(B, T, H, dk, dv, monkeypatch):
+    """Fixed-length rows with few (row, head) chains take the fused kernel (chunk walk and
+    scan side by side); KDA_FUSED=0 takes the two kernels.  Both against the oracle, and
+    against each other."""
+    x = make_inputs(B, T, H, dk, dv, seed=B * 1000 + T + H, dtype="bf16")
+    d = to_device(x)
+    o1, h1 = run_gpu(x, d)
+    monkeypatch.setenv("KDA_FUSED", "0")
+    o2, h2 = run_gpu(x, d)
+    ro, rh = run_oracle(x)
+    print("B=%d T=%d H=%d dk=%d dv=%d: fused out %.3e state %.3e; two-kernel out %.3e state %.3e; "
+          "between them out %.3e state %.3e" % (B, T, H, dk, dv, rel_rmse(o1, ro), rel_rmse(h1, rh),
+                                                rel_rmse(o2, ro), rel_rmse(h2, rh), rel_rmse(o1, o2),
+                                                rel_rmse(h1, h2)), flush=True)
+    for o, h in ((o1, h1), (o2, h2)):
+        assert rel_rmse(o, ro) <= TOL and rel_rmse(h, rh) <= TOL
+    assert rel_rmse(o1, o2) <= 1e-3 and rel_rmse(h1, h2) <= 1e-3

@@ -13,7 +13,7 @@ from workloads import make_config
 pytestmark = pytest.mark.gpu
 
 
-def _check_workload(idx, packed=False):
+def _check_workload(idx, packed=False, two_kernel_too=False, monkeypatch=None):
     t0 = time.time()
     x = make_config(idx, packed=packed)
     print("workload %d (%s): generated in %.1fs" % (idx, x.name, time.time() - t0), flush=True)
@@ -21,6 +21,14 @@ def _check_workload(idx, packed=False):
     t1 = time.time()
     ro, rh = run_oracle(x)
     print("  oracle %.1fs" % (time.time() - t1), flush=True)
+    if two_kernel_too:
+        # the same inputs through the two-kernel path (the default path here is the fused kernel)
+        monkeypatch.setenv("KDA_FUSED", "0")
+        o2, h2 = run_gpu(x)
+        monkeypatch.delenv("KDA_FUSED")
+        e2o, e2h = rel_rmse(o2, ro), rel_rmse(h2, rh)
+        print("  two-kernel path: rel-RMSE out %.3e state %.3e" % (e2o, e2h), flush=True)
+        assert e2o <= TOL and e2h <= TOL
     eo, eh = rel_rmse(o, ro), rel_rmse(h, rh)
     print("  rel-RMSE out %.3e state %.3e; max|err| out %.3e" % (eo, eh, np.max(np.abs(o - ro))), flush=True)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(h))
@@ -34,8 +42,8 @@ def _check_workload(idx, packed=False):
     assert worst[0] <= TOL and worst[1] <= TOL
 
 
-def test_fixed_8192():
-    _check_workload(1)
+def test_fixed_8192(monkeypatch):
+    _check_workload(1, two_kernel_too=True, monkeypatch=monkeypatch)
 
 
 def test_varlen_uniform_8192():
