@@ -80,8 +80,9 @@ typedef struct {
  * Bytes of device workspace kda_fwd needs for `prob` (0 on an invalid
  * problem).  The workspace holds the chunk table and, per 64-token chunk and
  * head, the chunk's factors (the WY factors W and U, the decayed queries and
- * keys, the masked intra-chunk attention and the chunk decay).  Its contents
- * are scratch: nothing in it needs initialising and nothing survives the call.
+ * keys, the masked intra-chunk attention and the chunk decay) and a ready
+ * flag.  Its contents are scratch: nothing in it needs initialising and
+ * nothing survives the call (flags are compared with a per-call value).
  */
 size_t kda_fwd_workspace_size(const kda_problem_t* prob);
 
@@ -122,11 +123,19 @@ kda_status_t kda_fwd_validate(const kda_problem_t* prob, const void* q, const vo
  * out of bounds.  cu_seqlens is read on the device; its validity is the
  * caller's precondition (see kda_fwd_validate).
  *
+ * Kernels.  Fixed-length batches with few (row, head) chains -- rows x heads x
+ * dv/64 at most a quarter of the compute units -- run as one persistent
+ * kernel in which most workgroups compute the chunk factors and the others
+ * walk the chains as the factors appear; other batches run the chunk kernel
+ * and then the state scan (packed batches after a small chunk-map kernel).
+ *
  * Tuning (read at every call; results are the same up to rounding):
- *   KDA_SCAN_SLICE=16|32|64  value columns per state-scan workgroup (default: the widest
- *                            that still gives every compute unit a workgroup)
- *   KDA_CHUNK_WGS=n          at most n workgroups for the persistent chunk
- *                            kernel (default: one per compute unit)
+ *   KDA_FUSED=0              never use the single fused kernel
+ *   KDA_SCAN_SLICE=16|32|64  value columns per state-scan workgroup of the two-kernel
+ *                            path (default: the widest that still gives every compute
+ *                            unit a workgroup)
+ *   KDA_CHUNK_WGS=n          at most n workgroups compute chunk factors (default: one
+ *                            per compute unit, minus the chain workgroups when fused)
  */
 kda_status_t kda_fwd(const kda_problem_t* prob, const void* q, const void* k, const void* v,
                      const float* g, const void* beta, const float* h0,
@@ -137,7 +146,8 @@ kda_status_t kda_fwd(const kda_problem_t* prob, const void* q, const void* k, co
  * kda_fwd with timing marks for profiling: identical work, plus hipEventRecord
  * of events[0] before the chunk map, events[1] after it, events[2] after the
  * chunk kernel (including its pass over chunks whose in-chunk decay exceeds the
- * fast path's range) and events[3] after the state scan, all on `stream`.
+ * fast path's range) and events[3] after the state scan, all on `stream`
+ * (fused kernel: events[2] and events[3] both after it).
  * `events` is a host array of 4 hipEvent_t handles created by the caller (NULL
  * entries are skipped); the elapsed time between consecutive marks is the
  * duration of each kernel.  Errors as for kda_fwd.
