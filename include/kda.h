@@ -29,7 +29,9 @@
  *     thrown.  A failed call enqueues no work.
  *   - kda_fwd enqueues its kernels on `stream` and returns without waiting
  *     for them.  It keeps no pointer after that work completes, holds no
- *     global state and may be called from several host threads at once.
+ *     global state beyond a process-wide call counter (atomic) and may be
+ *     called from several host threads at once; two calls that run at the
+ *     same time need separate workspaces.
  *   - Results are deterministic: the same inputs on the same GPU and build
  *     give bitwise-equal out and ht.
  */
