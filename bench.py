@@ -383,6 +383,7 @@ def main():
         hip.hipEventElapsedTime(ctypes.byref(f), a, b)
         return f.value
 
+    per_call = np.array([elapsed(m[0], m[3]) for m in marks])
     k_map = np.mean([elapsed(m[0], m[1]) for m in marks])
     k_prep = np.mean([elapsed(m[1], m[2]) for m in marks])
     k_scan = np.mean([elapsed(m[2], m[3]) for m in marks])
@@ -494,6 +495,10 @@ def main():
                  "peak_tflops": MFMA_F16_PEAK_TFLOPS},
         "hbm_frac_whole_step": round((wk["prep_bytes"] + wk["scan_bytes"]) / (ms_per_step * 1e-3) / 1e9
                                      / HBM_PEAK_GBS, 4),
+        "call_ms_percentiles": {"p10": round(float(np.percentile(per_call, 10)), 5),
+                                "p50": round(float(np.percentile(per_call, 50)), 5),
+                                "p90": round(float(np.percentile(per_call, 90)), 5),
+                                "note": "per call, from the events of the second pass (first to last mark)"},
         "parity": parity,
         "cpu_baseline": cpu_baseline,
     }

@@ -150,3 +150,37 @@ def test_fused_and_two_kernel_paths(B, T, H, dk, dv, monkeypatch):
     for o, h in ((o1, h1), (o2, h2)):
         assert rel_rmse(o, ro) <= TOL and rel_rmse(h, rh) <= TOL
     assert rel_rmse(o1, o2) <= 1e-3 and rel_rmse(h1, h2) <= 1e-3
+
+
+def test_fused_back_to_back_calls_read_fresh_records():
+    """The fused kernel hands records over through memory with per-call flags: twenty calls
+    on one workspace, alternating two sets of input contents, must each reproduce that set's
+    result bitwise (a record or flag left over from the previous call would change it)."""
+    import torch
+    import gated_delta_rule_39_amd.kda as kda
+    xa = make_inputs(1, 1500, 8, 128, 128, seed=41, dtype="bf16")
+    xb = make_inputs(1, 1500, 8, 128, 128, seed=42, dtype="bf16")
+    da, db = to_device(xa), to_device(xb)
+    ws = torch.empty(kda.workspace_size(1, 1500, 8, 128, 128), dtype=torch.uint8, device="cuda")
+    run = lambda d, x: kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], None, x.scale, workspace=ws)
+    ref = {}
+    for i in range(20):
+        x, d = (xa, da) if i % 2 == 0 else (xb, db)
+        o, h = run(d, x)
+        torch.cuda.synchronize()
+        o, h = o.float().cpu().numpy(), h.cpu().numpy()
+        if x.seed not in ref:
+            ref[x.seed] = (o, h)
+            ro, rh = run_oracle(x)
+            assert rel_rmse(o, ro) <= TOL and rel_rmse(h, rh) <= TOL
+        else:
+            np.testing.assert_array_equal(o, ref[x.seed][0])
+            np.testing.assert_array_equal(h, ref[x.seed][1])
+
+
+def test_fused_deferred_items_on_long_walks(monkeypatch):
+    """Deep gates (every item takes the exact pass, published after the walk) with only three
+    chunk workgroups: the chain workgroups wait on records published late."""
+    monkeypatch.setenv("KDA_CHUNK_WGS", "3")
+    x = make_inputs(1, 700, 4, 128, 128, seed=43, dtype="bf16", gate="deep")
+    _check(x, "fused, deep gates, 3 chunk workgroups")

@@ -56,3 +56,8 @@ def test_varlen_skewed_8192():
 
 def test_stress_4x8192():
     _check_workload(4)
+
+
+def test_stress_4x8192_packed():
+    """The stress batch as four packed sequences (cu_seqlens = [0, 8192, 16384, 24576, 32768])."""
+    _check_workload(4, packed=True)
