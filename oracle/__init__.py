@@ -6,3 +6,4 @@ its Python binding) never imports, links or calls it, and this package never
 imports the product path.
 """
 from .kda_oracle import build_oracle, oracle_fwd, oracle_threads  # noqa: F401
+from .kda_oracle_bwd import forward_states, oracle_bwd  # noqa: F401,E402
