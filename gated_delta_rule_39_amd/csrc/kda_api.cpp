@@ -131,7 +131,7 @@ uint64_t next_epoch() {
 
 extern "C" {
 
-int kda_version(void) { return 102; }
+int kda_version(void) { return 103; }
 
 const char* kda_status_string(kda_status_t s) {
   switch (s) {
@@ -292,6 +292,100 @@ kda_status_t kda_decode(const kda_problem_t* prob, const void* q, const void* k,
   p.out = out;
   p.ht = ht;
   hipError_t e = kda::launch_recurrent(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+// Backward workspace: chunk map (packed), checkpoints of every 64-token segment's state,
+// the persistent workgroups' replay scratch, dL/dqhat and dL/dkhat.
+struct BwdCarve {
+  size_t info, table, seq_off, seq_order, ckpt, scratch, dqh, dkh, total;
+  int32_t grid;
+};
+
+static BwdCarve bwd_carve(const kda_problem_t* p, int64_t N, int64_t n_chunk_ub) {
+  BwdCarve c;
+  const int64_t cus = compute_units();
+  const int64_t chains = N * (int64_t)p->heads;
+  c.grid = (int32_t)(chains < cus ? chains : cus);
+  const size_t state = (size_t)p->dk * p->dv * 4;
+  const size_t toks = (size_t)(p->batch * p->seqlen);
+  c.info = 0;
+  c.table = c.info + 256;
+  c.seq_off = c.table + align256((size_t)n_chunk_ub * 16);
+  c.seq_order = c.seq_off + align256((size_t)(N + 1) * 4);
+  c.ckpt = c.seq_order + align256((size_t)N * 4);
+  c.scratch = c.ckpt + align256((size_t)n_chunk_ub * p->heads * state);
+  c.dqh = c.scratch + align256((size_t)c.grid * 64 * state);
+  c.dkh = c.dqh + align256(toks * p->heads * p->dk * 4);
+  c.total = c.dkh + align256(toks * p->heads * p->dk * 4);
+  return c;
+}
+
+size_t kda_bwd_workspace_size(const kda_problem_t* prob) {
+  if (!prob || !dims_supported(prob)) return 0;
+  size_t best = 0;
+  int64_t N = 0, ub = 0;
+  if (sizes_ok(prob, false, &N, &ub)) best = bwd_carve(prob, N, ub).total;
+  if (sizes_ok(prob, true, &N, &ub)) {
+    const size_t t = bwd_carve(prob, N, ub).total;
+    if (t > best) best = t;
+  }
+  return best;
+}
+
+kda_status_t kda_bwd(const kda_problem_t* prob, const void* q, const void* k, const void* v, const float* g,
+                     const void* beta, const float* h0, const int32_t* cu_seqlens, float scale,
+                     const void* dout, const float* dht, void* dq, void* dk, void* dv, float* dg, void* dbeta,
+                     float* dh0, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!prob) return KDA_ERR_NULL;
+  if (!dims_supported(prob)) return KDA_ERR_UNSUPPORTED;
+  const bool packed = cu_seqlens != nullptr;
+  int64_t N = 0, ub = 0;
+  if (!sizes_ok(prob, packed, &N, &ub)) return KDA_ERR_BAD_ARG;
+  if (!std::isfinite(scale)) return KDA_ERR_BAD_ARG;
+  const int64_t toks = prob->batch * prob->seqlen;
+  if (toks > 0 && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
+    return KDA_ERR_NULL;
+  if (!workspace) return KDA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, g, beta, h0, dout, dht, dq, dk, dv, dg, dbeta, dh0, workspace};
+  for (const void* ptr : ptrs)
+    if (misaligned(ptr)) return KDA_ERR_ALIGN;
+  const BwdCarve c = bwd_carve(prob, N, ub);
+  if (workspace_bytes < c.total) return KDA_ERR_WORKSPACE;
+  const size_t es = prob->dtype == KDA_BF16 ? 2 : 4;
+  const size_t nqk = (size_t)toks * prob->heads * prob->dk;
+  const size_t nv = (size_t)toks * prob->heads * prob->dv;
+  const size_t nst = (size_t)N * prob->heads * prob->dk * prob->dv * 4;
+  struct Buf { const void* p; size_t n; };
+  const Buf ins[] = {{q, nqk * es}, {k, nqk * es}, {v, nv * es}, {g, nqk * 4},
+                     {beta, (size_t)toks * prob->heads * es}, {h0, h0 ? nst : 0},
+                     {cu_seqlens, packed ? (size_t)(N + 1) * 4 : 0}, {dout, nv * es},
+                     {dht, dht ? nst : 0}, {workspace, workspace_bytes}};
+  const Buf outs[] = {{dq, nqk * es}, {dk, nqk * es}, {dv, nv * es}, {dg, nqk * 4},
+                      {dbeta, (size_t)toks * prob->heads * es}, {dh0, dh0 ? nst : 0}};
+  for (const Buf& o : outs) {
+    for (const Buf& in : ins)
+      if (overlap(o.p, o.n, in.p, in.n)) return KDA_ERR_ALIAS;
+    for (const Buf& o2 : outs)
+      if (&o2 != &o && overlap(o.p, o.n, o2.p, o2.n)) return KDA_ERR_ALIAS;
+  }
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  kda::BackwardPlan p{};
+  p.B = prob->batch; p.T = prob->seqlen; p.N = N; p.T_total = toks; p.n_chunk_ub = ub;
+  p.H = prob->heads; p.dk = prob->dk; p.dv = prob->dv; p.dtype = prob->dtype;
+  p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.cu = cu_seqlens; p.scale = scale;
+  p.dout = dout; p.dht = dht;
+  p.dq = dq; p.dk_ = dk; p.dv_ = dv; p.dg = dg; p.dbeta = dbeta; p.dh0 = dh0;
+  p.info = reinterpret_cast<int32_t*>(ws + c.info);
+  p.table = ws + c.table;
+  p.seq_off = reinterpret_cast<int32_t*>(ws + c.seq_off);
+  p.seq_order = reinterpret_cast<int32_t*>(ws + c.seq_order);
+  p.ckpt = reinterpret_cast<float*>(ws + c.ckpt);
+  p.scratch = reinterpret_cast<float*>(ws + c.scratch);
+  p.dqh = reinterpret_cast<float*>(ws + c.dqh);
+  p.dkh = reinterpret_cast<float*>(ws + c.dkh);
+  p.grid = c.grid;
+  hipError_t e = kda::launch_backward(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

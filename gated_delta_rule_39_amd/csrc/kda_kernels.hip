@@ -4,6 +4,7 @@
 #include "kda_prep.h"
 #include "kda_scan.h"
 #include "kda_recurrent.h"
+#include "kda_recurrent_bwd.h"
 
 namespace kda {
 
@@ -182,6 +183,45 @@ hipError_t launch_recurrent(const ForwardPlan& p, hipStream_t stream) {
   if (p.dk == 64 && p.dv == 128) return launch_recurrent_dt<64, 128>(p, stream);
   if (p.dk == 128 && p.dv == 64) return launch_recurrent_dt<128, 64>(p, stream);
   return launch_recurrent_dt<128, 128>(p, stream);
+}
+
+template <int DK, int DV, typename InT>
+static hipError_t launch_backward_t(const BackwardPlan& p, hipStream_t stream) {
+  BwdArgs a;
+  a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.beta = p.beta; a.h0 = p.h0; a.cu = p.cu;
+  a.seq_off = p.cu ? p.seq_off : nullptr;
+  a.dout = p.dout; a.dht = p.dht;
+  a.dqh = p.dqh; a.dkh = p.dkh; a.dv = p.dv_; a.dg = p.dg; a.dbeta = p.dbeta; a.dh0 = p.dh0;
+  a.ckpt = p.ckpt; a.scratch = p.scratch;
+  a.T = p.T; a.N = p.N; a.nc = p.cu ? 0 : (p.T + kBwdSeg - 1) / kBwdSeg; a.H = p.H; a.scale = p.scale;
+  auto kern = recurrent_bwd_kernel<DK, DV, InT>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.grid), dim3(64 * (DV / kRecCols)), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.T_total == 0) return e;
+  const int64_t rows = p.T_total * (int64_t)p.H;
+  auto fin = norm_bwd_kernel<DK, InT>;
+  hipLaunchKernelGGL(fin, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p.q, p.k, p.dqh, p.dkh, p.dq, p.dk_,
+                     rows);
+  return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t launch_backward_dt(const BackwardPlan& p, hipStream_t stream) {
+  return p.dtype == 0 ? launch_backward_t<DK, DV, uint16_t>(p, stream) : launch_backward_t<DK, DV, float>(p, stream);
+}
+
+hipError_t launch_backward(const BackwardPlan& p, hipStream_t stream) {
+  if (p.N <= 0) return hipSuccess;
+  if (p.cu) {
+    hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kMapThreads), 0, stream, p.cu, p.T, p.N, p.n_chunk_ub,
+                       p.info, reinterpret_cast<ChunkEntry*>(p.table), p.seq_off, p.seq_order);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.dk == 64 && p.dv == 64) return launch_backward_dt<64, 64>(p, stream);
+  if (p.dk == 64 && p.dv == 128) return launch_backward_dt<64, 128>(p, stream);
+  if (p.dk == 128 && p.dv == 64) return launch_backward_dt<128, 64>(p, stream);
+  return launch_backward_dt<128, 128>(p, stream);
 }
 
 }  // namespace kda

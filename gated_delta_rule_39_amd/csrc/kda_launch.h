@@ -43,6 +43,23 @@ size_t record_bytes(int dk, int dv);
 // Enqueue chunk map, chunk kernel and state scan on `stream`.
 hipError_t launch_forward(const ForwardPlan& p, hipStream_t stream);
 
+// Backward of the forward described by a ForwardPlan-like set of sizes.
+struct BackwardPlan {
+  int64_t B, T, N, T_total, n_chunk_ub;
+  int32_t H, dk, dv, dtype;
+  const void* q; const void* k; const void* v; const float* g; const void* beta; const float* h0;
+  const int32_t* cu;
+  float scale;
+  const void* dout; const float* dht;
+  void* dq; void* dk_; void* dv_; float* dg; void* dbeta; float* dh0;
+  // workspace
+  int32_t* info; void* table; int32_t* seq_off; int32_t* seq_order;
+  float* ckpt; float* scratch; float* dqh; float* dkh;
+  int32_t grid;  // persistent workgroups of the backward kernel (scratch is sized for them)
+};
+
+hipError_t launch_backward(const BackwardPlan& p, hipStream_t stream);
+
 // Enqueue the token-by-token recurrent kernel on `stream` (uses the sizes, tensors and
 // scale of `p`; no workspace).
 hipError_t launch_recurrent(const ForwardPlan& p, hipStream_t stream);

@@ -40,6 +40,10 @@ _lib.kda_fwd.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, ct
 _lib.kda_fwd.restype = ctypes.c_int
 _lib.kda_decode.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]
 _lib.kda_decode.restype = ctypes.c_int
+_lib.kda_bwd_workspace_size.argtypes = [ctypes.POINTER(Problem)]
+_lib.kda_bwd_workspace_size.restype = ctypes.c_size_t
+_lib.kda_bwd.argtypes = [ctypes.POINTER(Problem)] + [_P] * 7 + [ctypes.c_float] + [_P] * 9 + [ctypes.c_size_t, _P]
+_lib.kda_bwd.restype = ctypes.c_int
 _lib.kda_status_string.argtypes = [ctypes.c_int]
 _lib.kda_status_string.restype = ctypes.c_char_p
 _lib.kda_version.argtypes = []
@@ -159,3 +163,32 @@ def decode(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, *, out=None, 
     if rc != 0:
         raise KDAError(rc)
     return out, ht
+
+
+def bwd(q, k, v, g, beta, do, h0=None, cu_seqlens=None, scale=None, dht=None, *, workspace=None, stream=None):
+    """Gradients of the forward (kda_bwd) for dL/dout = do and dL/dht = dht (None: 0).
+    Returns (dq, dk, dv, dg, dbeta, dh0): dq, dk, dv, dbeta in q's dtype, dg and dh0 fp32
+    (dh0 is the gradient with respect to the initial state, also when h0 is None)."""
+    B, T, H, dk, dv, N, code = _check(q, k, v, g, beta, h0, cu_seqlens, (do, dht, workspace))
+    if do.shape != v.shape or do.dtype != q.dtype:
+        raise ValueError("do must have v's shape and q's dtype")
+    if dht is not None and (dht.dtype != torch.float32 or tuple(dht.shape) != (N, H, dk, dv)):
+        raise ValueError("dht must be float32 [N, H, dk, dv]")
+    if scale is None:
+        scale = dk ** -0.5
+    prob = make_problem(B, T, H, dk, dv, code, N if cu_seqlens is not None else 0)
+    dq, dkk, dvv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg, dbeta = torch.empty_like(g), torch.empty_like(beta)
+    dh0 = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    wsb = int(_lib.kda_bwd_workspace_size(ctypes.byref(prob)))
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = _lib.kda_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                      _ptr(cu_seqlens), float(scale), _ptr(do), _ptr(dht), _ptr(dq), _ptr(dkk), _ptr(dvv),
+                      _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(workspace),
+                      workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KDAError(rc)
+    return dq, dkk, dvv, dg, dbeta, dh0

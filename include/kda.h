@@ -183,6 +183,35 @@ kda_status_t kda_decode(const kda_problem_t* prob, const void* q, const void* k,
                         const float* g, const void* beta, const float* h0,
                         const int32_t* cu_seqlens, float scale, void* out, float* ht, void* stream);
 
+/*
+ * Backward pass: the gradients of a kda_fwd call.  "Autoresearch on Kimi Delta
+ * Attention" (stage "Frozen outside the loop": full gradients against an
+ * independent reference; phase "Move the path into CUDA": the reverse
+ * recurrence over value tiles) fixes what it must return.
+ *
+ *   q, k, v, g, beta, h0, cu_seqlens, scale   the forward's inputs, as for kda_fwd
+ *   dout        [B, T, H, dv]  dtype   dL/dout
+ *   dht         [N, H, dk, dv] fp32    dL/dht, or NULL for zero
+ *   dq, dk      [B, T, H, dk]  dtype   dL/dq, dL/dk (through the L2 normalisation;
+ *                                      zero for a zero q or k vector)
+ *   dv          [B, T, H, dv]  dtype   dL/dv
+ *   dg          [B, T, H, dk]  fp32    dL/dg
+ *   dbeta       [B, T, H]      dtype   dL/dbeta
+ *   dh0         [N, H, dk, dv] fp32    dL/dh0 (also when h0 is NULL, i.e. zero), or NULL
+ *   workspace   >= kda_bwd_workspace_size(prob) bytes of device scratch
+ *
+ * The walk is token by token per (sequence, head) with the state split over 32-column
+ * slices (fp32 throughout); the forward is replayed from checkpoints every 64 tokens.
+ * Conventions (stream, no allocation, errors, alignment) as for kda_fwd; outputs must
+ * not overlap any input, the workspace or each other.  Results are deterministic.
+ */
+size_t kda_bwd_workspace_size(const kda_problem_t* prob);
+kda_status_t kda_bwd(const kda_problem_t* prob, const void* q, const void* k, const void* v,
+                     const float* g, const void* beta, const float* h0, const int32_t* cu_seqlens,
+                     float scale, const void* dout, const float* dht, void* dq, void* dk, void* dv,
+                     float* dg, void* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* kda_status_string(kda_status_t status);
 

@@ -1,0 +1,91 @@
+"""GPU parity of the backward pass (kda_bwd) against the fp64 backward oracle
+(oracle/kda_oracle_bwd.py, pinned to finite differences), through the C ABI.
+
+Gate: relative RMSE against the oracle <= 5e-3 for the gradients written in the
+inputs' dtype (dq, dk, dv, dbeta: bf16 rounding of the result itself) and <= 1e-4
+for the fp32 ones (dg, dh0; the walk is fp32 throughout).
+"""
+import numpy as np
+import pytest
+
+from kda_gpu_util import TOL, rel_rmse, to_device
+from oracle import oracle_bwd
+from workloads import make_inputs
+from workloads.kda_inputs import round_bf16
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-4
+
+
+def _dout(x, seed, with_dht=True):
+    rng = np.random.default_rng(seed)
+    do = rng.standard_normal(x.v.shape).astype(np.float32)
+    if x.dtype == "bf16":
+        do = round_bf16(do)
+    N = x.num_seqs
+    dht = (0.5 * rng.standard_normal((N,) + x.v.shape[2:3] + (x.q.shape[-1], x.v.shape[-1]))).astype(np.float32) \
+        if with_dht else None
+    return do, dht
+
+
+def _check(x, do, dht, label):
+    import torch
+    import gated_delta_rule_39_amd.kda as kda
+    d = to_device(x)
+    io = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+    t = lambda a, dt: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda().to(dt)
+    outs = kda.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], t(do, io), d["h0"], d["cu_seqlens"], x.scale,
+                   t(dht, torch.float32))
+    torch.cuda.synchronize()
+    got = [o.float().cpu().numpy().astype(np.float64) for o in outs]
+    ref = oracle_bwd(x.q, x.k, x.v, x.g, x.beta, do, x.h0, x.cu_seqlens, x.scale, dht)
+    names = ["dq", "dk", "dv", "dg", "dbeta", "dh0"]
+    errs = {n: rel_rmse(a, b) for n, a, b in zip(names, got, ref)}
+    print("%s: %s" % (label, " ".join("%s %.2e" % kv for kv in errs.items())), flush=True)
+    for n, a in zip(names, got):
+        assert np.all(np.isfinite(a)), n
+    io_tol = F32_TOL if x.dtype != "bf16" else TOL
+    for n in ["dq", "dk", "dv", "dbeta"]:
+        assert errs[n] <= io_tol, (label, n, errs[n])
+    for n in ["dg", "dh0"]:
+        assert errs[n] <= F32_TOL, (label, n, errs[n])
+    return got, ref
+
+
+def test_bwd_fixed_rows():
+    x = make_inputs(2, 150, 3, 128, 128, seed=301, dtype="bf16")
+    _check(x, *_dout(x, 302), "bwd fixed B=2 T=150 H=3")
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_head_sizes_and_dtypes(dk, dv, dtype):
+    x = make_inputs(1, 70, 2, dk, dv, seed=dk + dv + (dtype == "f32"), dtype=dtype)
+    _check(x, *_dout(x, 303), "bwd dk=%d dv=%d %s" % (dk, dv, dtype))
+
+
+def test_bwd_packed_with_empty_sequences_and_no_dht():
+    lens = [0, 1, 64, 65, 130, 0, 7]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    x = make_inputs(1, int(cu[-1]), 2, 128, 128, seed=304, dtype="bf16", cu_seqlens=cu)
+    do, _ = _dout(x, 305, with_dht=False)
+    got, ref = _check(x, do, None, "bwd packed, dht None")
+    for n, L in enumerate(lens):
+        if L == 0:
+            np.testing.assert_array_equal(got[5][n], 0.0)  # ht = h0 and dht = 0: dh0 = 0
+
+
+def test_bwd_null_h0_and_gate_regimes():
+    for gate in ["slow", "deep", "zero"]:
+        x = make_inputs(1, 100, 2, 128, 128, seed=306, dtype="f32", gate=gate, h0_std=None)
+        _check(x, *_dout(x, 307), "bwd gate=%s h0 None" % gate)
+
+
+def test_bwd_zero_vectors_and_large_entries():
+    x = make_inputs(1, 90, 2, 128, 128, seed=308, dtype="bf16")
+    x.q[0, 5] = 0.0
+    x.k[0, 9] = 0.0
+    x.q[0, 20, 0, :3] = float(round_bf16(np.array([1e30], np.float32))[0])
+    x.k[0, 33, 1, 7] = float(round_bf16(np.array([-3e35], np.float32))[0])
+    _check(x, *_dout(x, 309), "bwd zero vectors and large entries")
