@@ -202,7 +202,56 @@ def extra_measurements(args, lib, kda, make_config, upload, dev, torch, argv1, o
                    "calls": len(times), "note": "512 MiB written before every call, outside its timing"}
     res["decode"] = decode_measurement(args, lib, kda, upload, dev, torch)
     res["ok"] = res["ok"] and res["decode"]["ok"]
+    res["backward"] = backward_measurement(kda, dev, torch)
+    res["ok"] = res["ok"] and res["backward"]["ok"]
     return res
+
+
+def backward_measurement(kda, dev, torch, calls=3):
+    """kda_bwd on the headline workload (B=1, T=8192, H=32, d=128, bf16), timed over a few
+    calls (it walks every token in sequence), with its parity checked on a small problem
+    against the fp64 backward oracle (the oracle keeps every state, too large at full size)."""
+    from oracle import oracle_bwd
+    from workloads import make_config, make_inputs
+    rel = lambda a, b: float(np.linalg.norm(a.astype(np.float64) - b) / np.linalg.norm(b))
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+    # parity on a small problem
+    y = make_inputs(1, 200, 4, 128, 128, seed=11, dtype="bf16")
+    do = np.random.default_rng(12).standard_normal(y.v.shape).astype(np.float32)
+    do_d = t(do, torch.bfloat16)
+    do = do_d.float().cpu().numpy()
+    got = kda.bwd(t(y.q, torch.bfloat16), t(y.k, torch.bfloat16), t(y.v, torch.bfloat16), t(y.g, torch.float32),
+                  t(y.beta, torch.bfloat16), do_d, t(y.h0, torch.float32), None, y.scale)
+    torch.cuda.synchronize()
+    ref = oracle_bwd(y.q, y.k, y.v, y.g, y.beta, do, y.h0, None, y.scale, None)
+    errs = {n: rel(a.float().cpu().numpy(), r) for n, a, r in zip(["dq", "dk", "dv", "dg", "dbeta", "dh0"], got, ref)}
+    good = all(e <= TOL for e in errs.values())
+    # timing on the headline workload
+    x = make_config(1)
+    B, T, H, dk, dv = x.shape
+    args_ = [t(x.q, torch.bfloat16), t(x.k, torch.bfloat16), t(x.v, torch.bfloat16), t(x.g, torch.float32),
+             t(x.beta, torch.bfloat16), t(np.random.default_rng(13).standard_normal(x.v.shape), torch.bfloat16),
+             t(x.h0, torch.float32), None, x.scale]
+    kda.bwd(*args_)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        kda.bwd(*args_)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    # bytes every call must move: inputs (q, k, v bf16, g fp32, beta, dout) and gradients once, h0 and dh0
+    # reads q, k, v, dout (bf16), g (fp32), beta; writes dq, dk, dv (bf16), dg (fp32), dbeta
+    nbytes = B * T * H * (16 * dk + 6 * dv + 4) + 2 * H * dk * dv * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log("backward %s: %.3f ms/call, parity (B=1 T=200 H=4) %s" % (x.name, ms, errs))
+    return {"ok": good, "workload": "backward of %s (B=1 T=8192 H=32 d=128 bf16)" % x.name,
+            "ms_per_call": round(ms, 3), "tokens_per_s": round(B * T / (ms * 1e-3), 1) if good else None,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 5), "bytes_per_call": int(nbytes),
+                         "note": "token by token: bound by the per-token latency of each (sequence, head) walk"},
+            "parity_small": errs}
 
 
 def decode_measurement(args, lib, kda, upload, dev, torch, B=256, verify=True):
@@ -262,6 +311,8 @@ def main():
     ap.add_argument("--no-verify", action="store_true", help="skip parity (then no speed is reported)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="run only a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time only the backward pass (kda_bwd) of the headline workload; prints its own line")
     ap.add_argument("--decode", action="store_true",
                     help="time only the decode step (kda_decode, 256 sequences x 1 token); prints its own line")
     ap.add_argument("--no-extra", action="store_true",
@@ -291,6 +342,20 @@ def main():
 
     import gated_delta_rule_39_amd.kda as kda
     from workloads import make_config
+
+    if args.backward:
+        r = backward_measurement(kda, dev, torch, calls=max(1, min(args.steps, 5)))
+        ok = r.pop("ok")
+        line = {"metric": "KDA backward tokens/s (dq, dk, dv, dg, dbeta, dh0)",
+                "value": r["tokens_per_s"] if ok else None, "unit": "tokens/s", "n_gpus": 1,
+                "steps": max(1, min(args.steps, 5)), "warmup": 1, "ms_per_step": r["ms_per_call"],
+                "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+                "data": "synthetic", "config": {"workload": r["workload"]}, "roofline": r["roofline"],
+                "parity_small": r["parity_small"]}
+        print(json.dumps(line), flush=True)
+        if not ok:
+            sys.exit(1)
+        return
 
     if args.decode:
         def upload_bf16(y):

@@ -133,3 +133,36 @@ def test_decode_rejects_what_the_forward_rejects():
     p2 = dict(p)
     p2["ht"] = p2["h0"] + 512  # partial overlap with h0
     assert _decode(prob, p2) == ALIAS
+
+
+def test_backward_rejects_bad_arguments():
+    """kda_bwd's host checks; only calls that fail are made (they return before any HIP call)."""
+    lib = kda.library()
+    prob, p, _ = _args(B=2, T=100)
+    names = ["q", "k", "v", "g", "beta", "h0", "cu", "dout", "dht", "dq", "dk", "dv", "dg", "dbeta", "dh0", "ws"]
+    base = {n: (i + 1) * GB for i, n in enumerate(names)}
+    wsb = lib.kda_bwd_workspace_size(ctypes.byref(prob))
+    assert wsb > 0
+
+    def call(pp, wsb=wsb, cu=False, scale=0.125, pr=prob):
+        P = lambda n: None if pp.get(n) is None else ctypes.c_void_p(pp[n])
+        return lib.kda_bwd(ctypes.byref(pr), P("q"), P("k"), P("v"), P("g"), P("beta"), P("h0"),
+                           P("cu") if cu else None, ctypes.c_float(scale), P("dout"), P("dht"), P("dq"), P("dk"),
+                           P("dv"), P("dg"), P("dbeta"), P("dh0"), P("ws"), ctypes.c_size_t(wsb), None)
+    for n in ["q", "dout", "dq", "dg", "dbeta", "ws"]:
+        p2 = dict(base)
+        p2[n] = None
+        assert call(p2) == NULL, n
+    assert call(base, scale=math.nan) == BAD
+    assert call(base, wsb=wsb - 1) == WS
+    p2 = dict(base)
+    p2["dv"] += 8
+    assert call(p2) == ALIGN
+    p2 = dict(base)
+    p2["dq"] = p2["q"]  # a gradient written over an input
+    assert call(p2) == ALIAS
+    p2 = dict(base)
+    p2["dk"] = p2["dq"] + 64  # two gradients overlapping
+    assert call(p2) == ALIAS
+    prob2, _, _ = _args(B=2, T=100, dk=96)
+    assert call(base, pr=prob2) == UNSUP
