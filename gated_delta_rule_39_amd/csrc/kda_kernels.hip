@@ -195,7 +195,7 @@ static hipError_t launch_backward_t(const BackwardPlan& p, hipStream_t stream) {
   a.ckpt = p.ckpt; a.scratch = p.scratch;
   a.T = p.T; a.N = p.N; a.nc = p.cu ? 0 : (p.T + kBwdSeg - 1) / kBwdSeg; a.H = p.H; a.scale = p.scale;
   auto kern = recurrent_bwd_kernel<DK, DV, InT>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)p.grid), dim3(64 * (DV / kRecCols)), 0, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.grid), dim3(64 * (DV / kBwdCols)), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.T_total == 0) return e;
   const int64_t rows = p.T_total * (int64_t)p.H;

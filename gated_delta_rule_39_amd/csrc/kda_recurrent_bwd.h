@@ -15,12 +15,13 @@
 // and dL/dh0 = G at the sequence start; dq, dk follow from dqhat, dkhat through
 // the L2 normalisation (finish kernel).
 //
-// Work split: one workgroup per (sequence, head), one wave per 32-column slice of
+// Work split: one workgroup per (sequence, head), one wave per 16-column slice of
 // the state (the columns evolve independently, so the slices only meet in the
 // per-row sums dqhat, dkhat, dg and the scalar dbeta, which they add through LDS in
-// a fixed order: results are deterministic).  Lane (rg = l / 8, cg = l % 8) holds
-// key channels rg*NR .. rg*NR + NR - 1 of the slice's columns 4 cg .. 4 cg + 3, as
-// in the forward recurrent kernel.  The walk:
+// a fixed order: results are deterministic).  Slices are 16 columns wide, one wave
+// each: lane (rg = l / 4, cg = l % 4) holds key channels rg*NR .. rg*NR + NR - 1 of the
+// slice's columns 4 cg .. 4 cg + 3 (the narrow slice leaves room in registers for the
+// next token's inputs and state, requested one token ahead in every walk).  The walk:
 //   1. forward over the sequence, storing the slice's state at every 64-token
 //      boundary (checkpoints, fp32, in the workspace);
 //   2. backwards over the 64-token segments: from the segment's checkpoint the
@@ -71,29 +72,28 @@ __device__ inline float wave_sum(float x) {
   return rows4_sum(x);
 }
 
-// Sum over the eight lanes of a row group (l ^ 1, l ^ 2, l ^ 4 with the same l / 8): quad
-// swaps by DPP, then the other quad of the group: row_ror:12 hands lane i the value of lane
-// (i - 12) mod 16 = i + 4 inside the row of 16, the partner quad for the lanes with
-// l % 8 < 4, which are the ones that use the result.
-__device__ inline float cols8_sum(float x) {
+// Sum over the four lanes of a column quad (l ^ 1, l ^ 2: the lanes with the same l / 4),
+// every lane gets the sum.
+__device__ inline float quad_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));  // quad [1,0,3,2]
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));  // quad [2,3,0,1]
-  return x + row_ror<12>(x);
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
 }
 
+constexpr int kBwdCols = 16;  // value columns per wave (8 waves for dv = 128)
+
 template <int DK, int DV, typename InT>
-__global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdArgs a) {
-  constexpr int NS = DV / kRecCols;     // slices = waves
-  constexpr int CG = kRecCols / 4;      // 8
+__global__ __launch_bounds__(512) void recurrent_bwd_kernel(BwdArgs a) {
+  constexpr int NS = DV / kBwdCols;     // slices = waves
+  constexpr int CG = kBwdCols / 4;      // 4 lanes per row group
   constexpr int NR = DK * CG / 64;      // key channels per lane
-  constexpr int SLICE = DK * kRecCols;  // floats of one slice's state
+  constexpr int SLICE = DK * kBwdCols;  // floats of one slice's state
   // LDS: per slice and token parity, the row sums [dqhat | dkhat | dg] and dbeta
   __shared__ float part[2][NS][3 * DK + 4];
   const int l = threadIdx.x & 63;
   const int s = threadIdx.x >> 6;  // slice
   const int cg = l % CG, rg = l / CG;
   const int r0 = rg * NR;
-  const int col = s * kRecCols + 4 * cg;
+  const int col = s * kBwdCols + 4 * cg;
   float* scratch = a.scratch + (size_t)blockIdx.x * kBwdSeg * DK * DV + (size_t)s * SLICE;
   const InT* dout = reinterpret_cast<const InT*>(a.dout);
   InT* dvo = reinterpret_cast<InT*>(a.dv);
@@ -133,11 +133,11 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < NR; ++i) load4(base + ((size_t)i * 64 + l) * 4, S[i]);
     };
-    // one forward step of the slice (as in the recurrent kernel, without the output)
-    auto fwd_step = [&](float (&S)[NR][4], int64_t tok) {
-      TokIn<NR> in;
-      load_token<DK, DV, NR, InT>(in, ra, tok, h, r0, col);
-      normalise<kRecCols>(in.k);
+    auto load = [&](TokIn<NR>& in, int64_t tok) { load_token<DK, DV, NR, InT>(in, ra, tok, h, r0, col); };
+    // one forward step of the slice from already loaded inputs (as in the recurrent kernel,
+    // without the output)
+    auto fwd_step = [&](float (&S)[NR][4], TokIn<NR>& in) {
+      normalise<kBwdCols>(in.k);
       float p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
@@ -150,12 +150,25 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdArgs a) {
       }
       float d[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) d[j] = in.v[j] - rowgroups_sum<kRecCols>(p[j]);
+      for (int j = 0; j < 4; ++j) d[j] = in.v[j] - rowgroups_sum<kBwdCols>(p[j]);
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
         const float bk = in.beta * in.k[i];
 #pragma unroll
         for (int j = 0; j < 4; ++j) S[i][j] = fmaf(bk, d[j], S[i][j]);
+      }
+    };
+    // forward over [ta, tb) from S; `at` stores the state before token t (or nothing)
+    auto forward = [&](float (&S)[NR][4], int64_t ta, int64_t tb, auto&& at) {
+      if (ta >= tb) return;
+      TokIn<NR> cur;
+      load(cur, ta);
+      for (int64_t tok = ta; tok < tb; ++tok) {
+        TokIn<NR> nxt;  // the next token's inputs are requested before this token's arithmetic
+        load(nxt, tok + 1 < tb ? tok + 1 : tok);
+        at(tok, S);
+        fwd_step(S, cur);
+        cur = nxt;
       }
     };
 
@@ -167,10 +180,9 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdArgs a) {
         if (a.h0) load4(a.h0 + sbase + (size_t)(r0 + i) * DV + col, S[i]);
         else S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
       }
-      for (int64_t tok = t0; tok < t1; ++tok) {
-        if ((tok - t0) % kBwdSeg == 0) put(ck((tok - t0) / kBwdSeg), S);
-        fwd_step(S, tok);
-      }
+      forward(S, t0, t1, [&](int64_t tok, const float (&St)[NR][4]) {
+        if ((tok - t0) % kBwdSeg == 0) put(ck((tok - t0) / kBwdSeg), St);
+      });
     }
 
     // 2. backwards over the segments
@@ -186,20 +198,31 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdArgs a) {
       {
         float S[NR][4];
         get(ck(seg), S);
-        for (int64_t tok = ts; tok < te; ++tok) {
-          put(scratch + (size_t)(tok - ts) * DK * DV, S);
-          fwd_step(S, tok);
-        }
+        forward(S, ts, te, [&](int64_t tok, const float (&St)[NR][4]) {
+          put(scratch + (size_t)(tok - ts) * DK * DV, St);
+        });
       }
+      // reverse walk; the next (earlier) token's inputs and state are requested one token ahead
+      TokIn<NR> cur;
+      float dov[4], An[NR][4];
+      load(cur, te - 1);
+      load4(dout + ((size_t)(te - 1) * a.H + h) * DV + col, dov);
+      get(scratch + (size_t)(te - 1 - ts) * DK * DV, An);
       for (int64_t tok = te - 1; tok >= ts; --tok) {
+        const int64_t pt = tok > ts ? tok - 1 : tok;
         float A[NR][4];  // S_{t-1}, then a
-        get(scratch + (size_t)(tok - ts) * DK * DV, A);
-        TokIn<NR> in;
-        load_token<DK, DV, NR, InT>(in, ra, tok, h, r0, col);
-        float dov[4];
-        load4(dout + ((size_t)tok * a.H + h) * DV + col, dov);
-        normalise<kRecCols>(in.q);
-        normalise<kRecCols>(in.k);
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) A[i][j] = An[i][j];
+        TokIn<NR> nxt;
+        float don[4];
+        load(nxt, pt);
+        load4(dout + ((size_t)pt * a.H + h) * DV + col, don);
+        get(scratch + (size_t)(pt - ts) * DK * DV, An);
+        TokIn<NR>& in = cur;
+        normalise<kBwdCols>(in.q);
+        normalise<kBwdCols>(in.k);
         float e[NR];
         float p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -215,10 +238,10 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdArgs a) {
         float ddo = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          d[j] = in.v[j] - rowgroups_sum<kRecCols>(p[j]);
+          d[j] = in.v[j] - rowgroups_sum<kBwdCols>(p[j]);
           ddo = fmaf(d[j], dov[j], ddo);
         }
-        ddo = cols8_sum(ddo);  // delta . do over the slice's columns (lanes with cg < 4)
+        ddo = quad_sum(ddo);  // delta . do over the slice's columns
         // G += scale qhat do^T, then u = G^T khat
         float u[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -231,12 +254,12 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdArgs a) {
           }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) u[j] = rowgroups_sum<kRecCols>(u[j]);
+        for (int j = 0; j < 4; ++j) u[j] = rowgroups_sum<kBwdCols>(u[j]);
         float db = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) db = fmaf(u[j], d[j], db);
-        db = cols8_sum(db);
-        // per-row partials over this lane's four columns, then over the row group's lanes
+        db = quad_sum(db);
+        // per-row partials over this lane's four columns, then over the quad
         float pq[NR], pk[NR], pg[NR];
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
@@ -250,17 +273,16 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdArgs a) {
             ag = fmaf(A[i][j], da, ag);
             G[i][j] = e[i] * da;  // dL/dS_{t-1}
           }
-          pq[i] = cols8_sum(aq);
-          pk[i] = cols8_sum(gd - au);
-          pg[i] = cols8_sum(ag);
+          pq[i] = quad_sum(aq);
+          pk[i] = quad_sum(gd - au);
+          pg[i] = quad_sum(ag);
         }
         // this slice's row sums to LDS (lanes cg == 0 hold the row group's totals)
         float* pp = part[par][s];
         if (cg == 0) {
 #pragma unroll
           for (int i = 0; i < NR; ++i) {
-            // dqhat = scale (a do + beta khat (delta . do)): the second term is the same in
-            // every slice except for delta . do, which is summed per slice here
+            // dqhat = scale (a do + beta khat (delta . do)): per slice, summed over slices below
             pp[r0 + i] = a.scale * (pq[i] + in.beta * in.k[i] * ddo);
             pp[DK + r0 + i] = in.beta * pk[i];
             pp[2 * DK + r0 + i] = pg[i];
@@ -275,7 +297,7 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdArgs a) {
           store4(dvo + ((size_t)tok * a.H + h) * DV + col, dvv);
         }
         __syncthreads();
-        // the slices' sums in a fixed order: wave s finishes rows 32 s' ... of the three rows sets
+        // the slices' sums in a fixed order
         {
           const size_t th = (size_t)tok * a.H + h;
           for (int idx = threadIdx.x; idx < 3 * DK + 1; idx += 64 * NS) {
@@ -285,13 +307,13 @@ __global__ __launch_bounds__(256) void recurrent_bwd_kernel(BwdArgs a) {
             if (idx < DK) a.dqh[th * DK + idx] = acc;
             else if (idx < 2 * DK) a.dkh[th * DK + idx - DK] = acc;
             else if (idx < 3 * DK) a.dg[th * DK + idx - 2 * DK] = acc;
-            else {
-              float one = acc;
-              store1(dbo + th, one);
-            }
+            else store1(dbo + th, acc);
           }
         }
         par ^= 1;  // the other buffer is written next: one barrier per token suffices
+        cur = nxt;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dov[j] = don[j];
       }
     }
     if (a.dh0) {
