@@ -295,29 +295,33 @@ kda_status_t kda_decode(const kda_problem_t* prob, const void* q, const void* k,
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-// Backward workspace: chunk map (packed), checkpoints of every 64-token segment's state,
-// the persistent workgroups' replay scratch, dL/dqhat and dL/dkhat.
+// Backward workspace: chunk map (packed), unit q and k, exp(g), checkpoints of the state at
+// every 8-token segment start, every token's delta, and each 32-column part's partial row
+// sums (dqhat, dkhat, dg, dbeta).
 struct BwdCarve {
-  size_t info, table, seq_off, seq_order, ckpt, scratch, dqh, dkh, total;
-  int32_t grid;
+  size_t info, table, seq_off, seq_order, qh, kh, eg, ckpt, delta, dqh_p, dkh_p, dg_p, dbeta_p, total;
 };
 
 static BwdCarve bwd_carve(const kda_problem_t* p, int64_t N, int64_t n_chunk_ub) {
   BwdCarve c;
-  const int64_t cus = compute_units();
-  const int64_t chains = N * (int64_t)p->heads;
-  c.grid = (int32_t)(chains < cus ? chains : cus);
+  const size_t parts = (size_t)p->dv / 32;
   const size_t state = (size_t)p->dk * p->dv * 4;
-  const size_t toks = (size_t)(p->batch * p->seqlen);
+  const size_t rows = (size_t)(p->batch * p->seqlen) * p->heads;
   c.info = 0;
   c.table = c.info + 256;
   c.seq_off = c.table + align256((size_t)n_chunk_ub * 16);
   c.seq_order = c.seq_off + align256((size_t)(N + 1) * 4);
-  c.ckpt = c.seq_order + align256((size_t)N * 4);
-  c.scratch = c.ckpt + align256((size_t)n_chunk_ub * p->heads * state);
-  c.dqh = c.scratch + align256((size_t)c.grid * 64 * state);
-  c.dkh = c.dqh + align256(toks * p->heads * p->dk * 4);
-  c.total = c.dkh + align256(toks * p->heads * p->dk * 4);
+  c.qh = c.seq_order + align256((size_t)N * 4);
+  c.kh = c.qh + align256(rows * p->dk * 4);
+  c.eg = c.kh + align256(rows * p->dk * 4);
+  c.ckpt = c.eg + align256(rows * p->dk * 4);
+  // every sequence of L tokens owns 8 slots per 64-token chunk, ceil(L / 8) <= 8 ceil(L / 64)
+  c.delta = c.ckpt + align256((size_t)n_chunk_ub * 8 * p->heads * state);
+  c.dqh_p = c.delta + align256(rows * p->dv * 4);
+  c.dkh_p = c.dqh_p + align256(parts * rows * p->dk * 4);
+  c.dg_p = c.dkh_p + align256(parts * rows * p->dk * 4);
+  c.dbeta_p = c.dg_p + align256(parts * rows * p->dk * 4);
+  c.total = c.dbeta_p + align256(parts * rows * 4);
   return c;
 }
 
@@ -380,11 +384,15 @@ kda_status_t kda_bwd(const kda_problem_t* prob, const void* q, const void* k, co
   p.table = ws + c.table;
   p.seq_off = reinterpret_cast<int32_t*>(ws + c.seq_off);
   p.seq_order = reinterpret_cast<int32_t*>(ws + c.seq_order);
+  p.qh = reinterpret_cast<float*>(ws + c.qh);
+  p.kh = reinterpret_cast<float*>(ws + c.kh);
+  p.eg = reinterpret_cast<float*>(ws + c.eg);
   p.ckpt = reinterpret_cast<float*>(ws + c.ckpt);
-  p.scratch = reinterpret_cast<float*>(ws + c.scratch);
-  p.dqh = reinterpret_cast<float*>(ws + c.dqh);
-  p.dkh = reinterpret_cast<float*>(ws + c.dkh);
-  p.grid = c.grid;
+  p.delta = reinterpret_cast<float*>(ws + c.delta);
+  p.dqh_p = reinterpret_cast<float*>(ws + c.dqh_p);
+  p.dkh_p = reinterpret_cast<float*>(ws + c.dkh_p);
+  p.dg_p = reinterpret_cast<float*>(ws + c.dg_p);
+  p.dbeta_p = reinterpret_cast<float*>(ws + c.dbeta_p);
   hipError_t e = kda::launch_backward(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

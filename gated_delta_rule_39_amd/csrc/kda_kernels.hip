@@ -187,21 +187,32 @@ hipError_t launch_recurrent(const ForwardPlan& p, hipStream_t stream) {
 
 template <int DK, int DV, typename InT>
 static hipError_t launch_backward_t(const BackwardPlan& p, hipStream_t stream) {
-  BwdArgs a;
-  a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.beta = p.beta; a.h0 = p.h0; a.cu = p.cu;
-  a.seq_off = p.cu ? p.seq_off : nullptr;
-  a.dout = p.dout; a.dht = p.dht;
-  a.dqh = p.dqh; a.dkh = p.dkh; a.dv = p.dv_; a.dg = p.dg; a.dbeta = p.dbeta; a.dh0 = p.dh0;
-  a.ckpt = p.ckpt; a.scratch = p.scratch;
-  a.T = p.T; a.N = p.N; a.nc = p.cu ? 0 : (p.T + kBwdSeg - 1) / kBwdSeg; a.H = p.H; a.scale = p.scale;
-  auto kern = recurrent_bwd_kernel<DK, DV, InT>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)p.grid), dim3(64 * (DV / kBwdCols)), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.T_total == 0) return e;
   const int64_t rows = p.T_total * (int64_t)p.H;
-  auto fin = norm_bwd_kernel<DK, InT>;
-  hipLaunchKernelGGL(fin, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p.q, p.k, p.dqh, p.dkh, p.dq, p.dk_,
-                     rows);
+  if (rows > 0) {
+    auto pre = bwd_prep_kernel<DK, InT>;
+    hipLaunchKernelGGL(pre, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p.q, p.k, p.g, p.qh, p.kh,
+                       p.eg, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  BwdArgs a;
+  a.qh = p.qh; a.kh = p.kh; a.eg = p.eg; a.v = p.v; a.beta = p.beta; a.h0 = p.h0; a.cu = p.cu;
+  a.seq_off = p.cu ? p.seq_off : nullptr;
+  a.seq_order = p.cu ? p.seq_order : nullptr;
+  a.dout = p.dout; a.dht = p.dht;
+  a.dqh_p = p.dqh_p; a.dkh_p = p.dkh_p; a.dg_p = p.dg_p; a.dbeta_p = p.dbeta_p;
+  a.dv = p.dv_; a.dh0 = p.dh0; a.ckpt = p.ckpt; a.delta = p.delta;
+  a.T = p.T; a.T_total = p.T_total; a.N = p.N; a.nc = p.cu ? 0 : (p.T + kChunk - 1) / kChunk;
+  a.n_chunk_ub = p.n_chunk_ub;
+  a.H = p.H; a.scale = p.scale;
+  constexpr int parts = DV / kBwdPartCols;
+  auto kern = recurrent_bwd_kernel<DK, DV, InT>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(p.N * p.H * parts)), dim3(kBwdThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || rows == 0) return e;
+  auto fin = bwd_finish_kernel<DK, InT>;
+  hipLaunchKernelGGL(fin, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p.q, p.k, p.dqh_p, p.dkh_p,
+                     p.dg_p, p.dbeta_p, parts, rows, p.dq, p.dk_, p.dg, p.dbeta);
   return hipGetLastError();
 }
 

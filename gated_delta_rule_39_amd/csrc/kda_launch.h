@@ -54,8 +54,10 @@ struct BackwardPlan {
   void* dq; void* dk_; void* dv_; float* dg; void* dbeta; float* dh0;
   // workspace
   int32_t* info; void* table; int32_t* seq_off; int32_t* seq_order;
-  float* ckpt; float* scratch; float* dqh; float* dkh;
-  int32_t grid;  // persistent workgroups of the backward kernel (scratch is sized for them)
+  float* qh; float* kh; float* eg;                        // unit q, k and exp(g) (pre-pass)
+  float* ckpt;                                            // state checkpoints every 8 tokens
+  float* delta;                                           // v - a^T khat of every token
+  float* dqh_p; float* dkh_p; float* dg_p; float* dbeta_p;  // per-part row sums
 };
 
 hipError_t launch_backward(const BackwardPlan& p, hipStream_t stream);

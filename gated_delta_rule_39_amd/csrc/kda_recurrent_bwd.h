@@ -15,48 +15,60 @@
 // and dL/dh0 = G at the sequence start; dq, dk follow from dqhat, dkhat through
 // the L2 normalisation (finish kernel).
 //
-// Work split: one workgroup per (sequence, head), one wave per 16-column slice of
-// the state (the columns evolve independently, so the slices only meet in the
-// per-row sums dqhat, dkhat, dg and the scalar dbeta, which they add through LDS in
-// a fixed order: results are deterministic).  Slices are 16 columns wide, one wave
-// each: lane (rg = l / 4, cg = l % 4) holds key channels rg*NR .. rg*NR + NR - 1 of the
-// slice's columns 4 cg .. 4 cg + 3 (the narrow slice leaves room in registers for the
-// next token's inputs and state, requested one token ahead in every walk).  The walk:
-//   1. forward over the sequence, storing the slice's state at every 64-token
-//      boundary (checkpoints, fp32, in the workspace);
-//   2. backwards over the 64-token segments: from the segment's checkpoint the
-//      forward is replayed into a per-workgroup scratch (the state before each of
-//      the segment's tokens), then the segment's tokens are walked in reverse.
-// Workgroups are persistent (one per compute unit at most), so the scratch is
-// bounded by the grid, not by the number of sequences.
+// Work split.  The value columns of the state evolve independently (a step mixes
+// key channels only), so each (sequence, head) is cut into parts of 32 value
+// columns, one workgroup per part, and each of its eight waves owns 4 columns: lane
+// l holds key channels l*NR .. l*NR + NR - 1 (NR = dk / 64) of those 4 columns, so
+// a lane carries 8 state elements (dk = 128) and a step is short.  Sums over key
+// channels (per column) are wave sums; the per-row sums dqhat, dkhat, dg and the
+// scalar dbeta add the eight waves' columns through LDS in a fixed order, and the
+// parts' partial sums are added (again in a fixed order) by the finish kernel:
+// results are deterministic.
+//
+// The walk, per part:
+//   1. forward over the sequence, storing the part's state at the start of every
+//      8-token segment (checkpoints, fp32, in the workspace);
+//   2. backwards over the segments: the segment's forward is replayed from its
+//      checkpoint into registers (the state before each of its tokens), then its
+//      tokens are walked in reverse.
+// Each segment's inputs (unit q and k from the norm pre-pass, g, beta and the part's
+// columns of v and dout) are staged in LDS, the next segment's loads in flight while
+// the current one is walked, so a step waits on LDS, never on HBM.
 #pragma once
 
 #include "kda_recurrent.h"
 
 namespace kda {
 
-constexpr int kBwdSeg = 64;  // tokens per checkpoint segment
+constexpr int kBwdWaves = 8;                              // waves per workgroup
+constexpr int kBwdWaveCols = 4;                           // value columns per wave
+constexpr int kBwdPartCols = kBwdWaves * kBwdWaveCols;    // value columns per workgroup
+constexpr int kBwdSeg = 8;                                // tokens per checkpoint segment
+constexpr int kBwdThreads = 64 * kBwdWaves;
 
 struct BwdArgs {
-  const void* q;
-  const void* k;
+  const float* qh;        // [tokens, H, DK] fp32 unit q (pre-pass)
+  const float* kh;        // [tokens, H, DK] fp32 unit k
+  const float* eg;        // [tokens, H, DK] fp32 exp(g) (pre-pass)
   const void* v;
-  const float* g;
   const void* beta;
   const float* h0;
-  const int32_t* cu;      // packed offsets (device) or NULL
-  const int32_t* seq_off; // packed: first 64-token segment of each sequence (chunk map), or NULL
+  const int32_t* cu;        // packed offsets (device) or NULL
+  const int32_t* seq_off;   // packed: first 64-token chunk of each sequence (chunk map), or NULL
+  const int32_t* seq_order; // packed: sequences longest first (chunk map), or NULL
   const void* dout;
   const float* dht;
-  float* dqh;             // [tokens, H, DK] fp32: dL/dqhat (workspace)
-  float* dkh;             // [tokens, H, DK] fp32: dL/dkhat (workspace)
+  float* dqh_p;           // [parts, tokens * H, DK] fp32 partial dL/dqhat of each part
+  float* dkh_p;           // [parts, tokens * H, DK] fp32 partial dL/dkhat
+  float* dg_p;            // [parts, tokens * H, DK] fp32 partial dL/dg
+  float* dbeta_p;         // [parts, tokens * H] fp32 partial dL/dbeta
   void* dv;               // [tokens, H, DV] io dtype
-  float* dg;              // [tokens, H, DK]
-  void* dbeta;            // [tokens, H] io dtype
   float* dh0;             // [N, H, DK, DV] or NULL
-  float* ckpt;            // [segments, H, DK * DV] fp32
-  float* scratch;         // [grid, kBwdSeg, DK * DV] fp32
-  int64_t T, N, nc;       // tokens per row (fixed) / total (packed); sequences; fixed: segments per row
+  float* ckpt;            // [slots, H, parts, waves, 64 lanes, NR, 4] fp32
+  float* delta;           // [tokens, H, DV] fp32: v - a^T khat of every token (walk 1)
+  int64_t T, T_total, N;  // tokens per row (fixed) / total (packed); all tokens; sequences
+  int64_t nc;             // fixed: 64-token chunks per row
+  int64_t n_chunk_ub;     // 64-token chunks the workspace holds (8 checkpoint slots each)
   int32_t H;
   float scale;
 };
@@ -64,287 +76,434 @@ struct BwdArgs {
 __device__ inline void store1(uint16_t* p, float x) { *p = (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu); }
 __device__ inline void store1(float* p, float x) { *p = x; }
 
+// Row rotation written as a DPP move with a zero old value and bound_ctrl (the rotation
+// reads a lane in every case, so the result is row_ror's): the compiler folds it into the
+// add that consumes it (v_add_f32_dpp).
+template <int N>
+__device__ inline float row_ror_z(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xF, 0xF, true));
+}
+
 __device__ inline float wave_sum(float x) {
-  x += row_ror<8>(x);
-  x += row_ror<4>(x);
-  x += row_ror<2>(x);
-  x += row_ror<1>(x);
+  x += row_ror_z<8>(x);
+  x += row_ror_z<4>(x);
+  x += row_ror_z<2>(x);
+  x += row_ror_z<1>(x);
   return rows4_sum(x);
 }
 
-// Sum over the four lanes of a column quad (l ^ 1, l ^ 2: the lanes with the same l / 4),
-// every lane gets the sum.
-__device__ inline float quad_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));  // quad [1,0,3,2]
-  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
-}
+// One segment's inputs in LDS, fp32.  The arrays are contiguous in this order, so the
+// float4 slot s of the staging loads lands at float 4 s (qhat, khat, exp(g), v or delta,
+// dout), and beta follows.  Walk 1 stages v, walk 2 the deltas walk 1 stored.
+template <int DK>
+struct BwdStage {
+  float qh[kBwdSeg][DK];
+  float kh[kBwdSeg][DK];
+  float e[kBwdSeg][DK];
+  float v[kBwdSeg][kBwdPartCols];  // v (walk 1) or delta (walk 2)
+  float dout[kBwdSeg][kBwdPartCols];
+  float beta[kBwdSeg];
+};
 
-constexpr int kBwdCols = 16;  // value columns per wave (8 waves for dv = 128)
+// A segment's staging loads held by one thread between issue and commit.
+template <int DK>
+struct StageRegs {
+  static constexpr int A4 = 3 * kBwdSeg * DK / 4;                 // float4 slots of qhat, khat, g
+  static constexpr int V4 = 2 * kBwdSeg * kBwdPartCols / 4;       // 4-element slots of v, dout
+  static constexpr int NSLOT = A4 + V4 + kBwdSeg;                 // + one slot per beta
+  static constexpr int ROUNDS = (NSLOT + kBwdThreads - 1) / kBwdThreads;
+  float x[ROUNDS][4];
+};
 
-template <int DK, int DV, typename InT>
-__global__ __launch_bounds__(512) void recurrent_bwd_kernel(BwdArgs a) {
-  constexpr int NS = DV / kBwdCols;     // slices = waves
-  constexpr int CG = kBwdCols / 4;      // 4 lanes per row group
-  constexpr int NR = DK * CG / 64;      // key channels per lane
-  constexpr int SLICE = DK * kBwdCols;  // floats of one slice's state
-  // LDS: per slice and token parity, the row sums [dqhat | dkhat | dg] and dbeta
-  __shared__ float part[2][NS][3 * DK + 4];
-  const int l = threadIdx.x & 63;
-  const int s = threadIdx.x >> 6;  // slice
-  const int cg = l % CG, rg = l / CG;
-  const int r0 = rg * NR;
-  const int col = s * kBwdCols + 4 * cg;
-  float* scratch = a.scratch + (size_t)blockIdx.x * kBwdSeg * DK * DV + (size_t)s * SLICE;
-  const InT* dout = reinterpret_cast<const InT*>(a.dout);
-  InT* dvo = reinterpret_cast<InT*>(a.dv);
-  InT* dbo = reinterpret_cast<InT*>(a.dbeta);
-  int par = 0;
-  RecurrentArgs ra;  // the token loads of the forward recurrent kernel read these fields
-  ra.q = a.q; ra.k = a.k; ra.v = a.v; ra.g = a.g; ra.beta = a.beta; ra.H = a.H;
-
-  for (int64_t nh = blockIdx.x; nh < a.N * a.H; nh += gridDim.x) {
-    const int h = (int)(nh % a.H);
-    const int64_t n = nh / a.H;
-    int64_t t0 = n * a.T, t1 = t0 + a.T, seg0 = n * a.nc;
-    if (a.cu) {
-      t0 = a.cu[n];
-      t1 = a.cu[n + 1];
-      t0 = t0 < 0 ? 0 : (t0 > a.T ? a.T : t0);
-      t1 = t1 < t0 ? t0 : (t1 > a.T ? a.T : t1);
-      seg0 = a.seq_off[n];
-    }
-    int64_t nseg = (t1 - t0 + kBwdSeg - 1) / kBwdSeg;
-    if (a.cu) {
-      // the checkpoints the chunk map set aside for this sequence (fewer only when
-      // cu_seqlens breaks its precondition: the walk then stops there)
-      const int64_t room = (int64_t)a.seq_off[n + 1] - seg0;
-      nseg = nseg < room ? nseg : (room > 0 ? room : 0);
-      t1 = t0 + nseg * kBwdSeg < t1 ? t0 + nseg * kBwdSeg : t1;
-    }
-    const size_t sbase = ((size_t)n * a.H + h) * DK * DV;
-    auto ck = [&](int64_t seg) { return a.ckpt + (((size_t)(seg0 + seg) * a.H + h) * NS + s) * SLICE; };
-    // slice state element (row r0 + i, columns col..col+3) in a lane-major block: float4 index i * 64 + l
-    auto put = [&](float* base, const float (&S)[NR][4]) {
+// Request the inputs of tokens [ts, te) (te - ts <= kBwdSeg; missing tokens read as 0)
+// of head h, value columns c0 .. c0 + 31 (WALK2: the stored deltas in place of v).
+template <int DK, int DV, typename InT, bool WALK2>
+__device__ inline void stage_issue(StageRegs<DK>& r, const BwdArgs& a, int64_t ts, int64_t te, int h, int c0) {
+  using SR = StageRegs<DK>;
 #pragma unroll
-      for (int i = 0; i < NR; ++i)
-        *reinterpret_cast<float4*>(base + ((size_t)i * 64 + l) * 4) = make_float4(S[i][0], S[i][1], S[i][2], S[i][3]);
-    };
-    auto get = [&](const float* base, float (&S)[NR][4]) {
-#pragma unroll
-      for (int i = 0; i < NR; ++i) load4(base + ((size_t)i * 64 + l) * 4, S[i]);
-    };
-    auto load = [&](TokIn<NR>& in, int64_t tok) { load_token<DK, DV, NR, InT>(in, ra, tok, h, r0, col); };
-    // one forward step of the slice from already loaded inputs (as in the recurrent kernel,
-    // without the output)
-    auto fwd_step = [&](float (&S)[NR][4], TokIn<NR>& in) {
-      normalise<kBwdCols>(in.k);
-      float p[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        const float e = exp2_hw(in.g[i] * kLog2e);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          S[i][j] *= e;
-          p[j] = fmaf(in.k[i], S[i][j], p[j]);
-        }
+  for (int rd = 0; rd < SR::ROUNDS; ++rd) {
+    const int s = (int)threadIdx.x + rd * kBwdThreads;
+    r.x[rd][0] = r.x[rd][1] = r.x[rd][2] = r.x[rd][3] = 0.f;
+    if (s < SR::A4) {
+      constexpr int PER = kBwdSeg * DK / 4;
+      const int which = s / PER, rem = s % PER;
+      const int64_t t = ts + rem / (DK / 4);
+      const float* src = which == 0 ? a.qh : (which == 1 ? a.kh : a.eg);
+      if (t < te) load4(src + ((size_t)t * a.H + h) * DK + 4 * (rem % (DK / 4)), r.x[rd]);
+    } else if (s < SR::A4 + SR::V4) {
+      constexpr int PER = kBwdSeg * kBwdPartCols / 4;
+      const int s2 = s - SR::A4;
+      const int which = s2 / PER, rem = s2 % PER;
+      const int64_t t = ts + rem / (kBwdPartCols / 4);
+      const size_t off = ((size_t)t * a.H + h) * DV + c0 + 4 * (rem % (kBwdPartCols / 4));
+      if (t < te) {
+        if (which != 0) load4(reinterpret_cast<const InT*>(a.dout) + off, r.x[rd]);
+        else if (WALK2) load4(a.delta + off, r.x[rd]);
+        else load4(reinterpret_cast<const InT*>(a.v) + off, r.x[rd]);
       }
-      float d[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) d[j] = in.v[j] - rowgroups_sum<kBwdCols>(p[j]);
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        const float bk = in.beta * in.k[i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) S[i][j] = fmaf(bk, d[j], S[i][j]);
-      }
-    };
-    // forward over [ta, tb) from S; `at` stores the state before token t (or nothing)
-    auto forward = [&](float (&S)[NR][4], int64_t ta, int64_t tb, auto&& at) {
-      if (ta >= tb) return;
-      TokIn<NR> cur;
-      load(cur, ta);
-      for (int64_t tok = ta; tok < tb; ++tok) {
-        TokIn<NR> nxt;  // the next token's inputs are requested before this token's arithmetic
-        load(nxt, tok + 1 < tb ? tok + 1 : tok);
-        at(tok, S);
-        fwd_step(S, cur);
-        cur = nxt;
-      }
-    };
-
-    // 1. forward with checkpoints
-    {
-      float S[NR][4];
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        if (a.h0) load4(a.h0 + sbase + (size_t)(r0 + i) * DV + col, S[i]);
-        else S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
-      }
-      forward(S, t0, t1, [&](int64_t tok, const float (&St)[NR][4]) {
-        if ((tok - t0) % kBwdSeg == 0) put(ck((tok - t0) / kBwdSeg), St);
-      });
+    } else if (s < SR::NSLOT) {
+      const int64_t t = ts + (s - SR::A4 - SR::V4);
+      if (t < te) r.x[rd][0] = load1(reinterpret_cast<const InT*>(a.beta) + (size_t)t * a.H + h);
     }
-
-    // 2. backwards over the segments
-    float G[NR][4];
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      if (a.dht) load4(a.dht + sbase + (size_t)(r0 + i) * DV + col, G[i]);
-      else G[i][0] = G[i][1] = G[i][2] = G[i][3] = 0.f;
-    }
-    for (int64_t seg = nseg - 1; seg >= 0; --seg) {
-      const int64_t ts = t0 + seg * kBwdSeg;
-      const int64_t te = ts + kBwdSeg < t1 ? ts + kBwdSeg : t1;
-      {
-        float S[NR][4];
-        get(ck(seg), S);
-        forward(S, ts, te, [&](int64_t tok, const float (&St)[NR][4]) {
-          put(scratch + (size_t)(tok - ts) * DK * DV, St);
-        });
-      }
-      // reverse walk; the next (earlier) token's inputs and state are requested one token ahead
-      TokIn<NR> cur;
-      float dov[4], An[NR][4];
-      load(cur, te - 1);
-      load4(dout + ((size_t)(te - 1) * a.H + h) * DV + col, dov);
-      get(scratch + (size_t)(te - 1 - ts) * DK * DV, An);
-      for (int64_t tok = te - 1; tok >= ts; --tok) {
-        const int64_t pt = tok > ts ? tok - 1 : tok;
-        float A[NR][4];  // S_{t-1}, then a
-#pragma unroll
-        for (int i = 0; i < NR; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) A[i][j] = An[i][j];
-        TokIn<NR> nxt;
-        float don[4];
-        load(nxt, pt);
-        load4(dout + ((size_t)pt * a.H + h) * DV + col, don);
-        get(scratch + (size_t)(pt - ts) * DK * DV, An);
-        TokIn<NR>& in = cur;
-        normalise<kBwdCols>(in.q);
-        normalise<kBwdCols>(in.k);
-        float e[NR];
-        float p[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < NR; ++i) {
-          e[i] = exp2_hw(in.g[i] * kLog2e);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            A[i][j] *= e[i];
-            p[j] = fmaf(in.k[i], A[i][j], p[j]);
-          }
-        }
-        float d[4];
-        float ddo = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          d[j] = in.v[j] - rowgroups_sum<kBwdCols>(p[j]);
-          ddo = fmaf(d[j], dov[j], ddo);
-        }
-        ddo = quad_sum(ddo);  // delta . do over the slice's columns
-        // G += scale qhat do^T, then u = G^T khat
-        float u[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < NR; ++i) {
-          const float sq = a.scale * in.q[i];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            G[i][j] = fmaf(sq, dov[j], G[i][j]);
-            u[j] = fmaf(in.k[i], G[i][j], u[j]);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) u[j] = rowgroups_sum<kBwdCols>(u[j]);
-        float db = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) db = fmaf(u[j], d[j], db);
-        db = quad_sum(db);
-        // per-row partials over this lane's four columns, then over the quad
-        float pq[NR], pk[NR], pg[NR];
-#pragma unroll
-        for (int i = 0; i < NR; ++i) {
-          float aq = 0.f, gd = 0.f, au = 0.f, ag = 0.f;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            aq = fmaf(A[i][j], dov[j], aq);
-            gd = fmaf(G[i][j], d[j], gd);
-            au = fmaf(A[i][j], u[j], au);
-            const float da = G[i][j] - in.beta * in.k[i] * u[j];
-            ag = fmaf(A[i][j], da, ag);
-            G[i][j] = e[i] * da;  // dL/dS_{t-1}
-          }
-          pq[i] = quad_sum(aq);
-          pk[i] = quad_sum(gd - au);
-          pg[i] = quad_sum(ag);
-        }
-        // this slice's row sums to LDS (lanes cg == 0 hold the row group's totals)
-        float* pp = part[par][s];
-        if (cg == 0) {
-#pragma unroll
-          for (int i = 0; i < NR; ++i) {
-            // dqhat = scale (a do + beta khat (delta . do)): per slice, summed over slices below
-            pp[r0 + i] = a.scale * (pq[i] + in.beta * in.k[i] * ddo);
-            pp[DK + r0 + i] = in.beta * pk[i];
-            pp[2 * DK + r0 + i] = pg[i];
-          }
-        }
-        if (l == 0) pp[3 * DK] = db;
-        // dv for this slice's columns (complete: no other slice touches them)
-        if (rg == 0) {
-          float dvv[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) dvv[j] = in.beta * u[j];
-          store4(dvo + ((size_t)tok * a.H + h) * DV + col, dvv);
-        }
-        __syncthreads();
-        // the slices' sums in a fixed order
-        {
-          const size_t th = (size_t)tok * a.H + h;
-          for (int idx = threadIdx.x; idx < 3 * DK + 1; idx += 64 * NS) {
-            float acc = 0.f;
-#pragma unroll
-            for (int ss = 0; ss < NS; ++ss) acc += part[par][ss][idx];
-            if (idx < DK) a.dqh[th * DK + idx] = acc;
-            else if (idx < 2 * DK) a.dkh[th * DK + idx - DK] = acc;
-            else if (idx < 3 * DK) a.dg[th * DK + idx - 2 * DK] = acc;
-            else store1(dbo + th, acc);
-          }
-        }
-        par ^= 1;  // the other buffer is written next: one barrier per token suffices
-        cur = nxt;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dov[j] = don[j];
-      }
-    }
-    if (a.dh0) {
-#pragma unroll
-      for (int i = 0; i < NR; ++i) store4(a.dh0 + sbase + (size_t)(r0 + i) * DV + col, G[i]);
-    }
-    __syncthreads();  // the next (sequence, head) rewrites LDS and scratch
   }
 }
 
-// dq, dk from dqhat, dkhat through the L2 normalisation: dx = (dxhat - xhat (xhat . dxhat)) / |x|
-// (0 for a zero vector), one wave per (token, head), the norm taken after the same exact
-// power-of-two rescale as in the forward kernels.
+template <int DK>
+__device__ inline void stage_commit(const StageRegs<DK>& r, BwdStage<DK>* st) {
+  using SR = StageRegs<DK>;
+  float* f = reinterpret_cast<float*>(st);
+#pragma unroll
+  for (int rd = 0; rd < SR::ROUNDS; ++rd) {
+    const int s = (int)threadIdx.x + rd * kBwdThreads;
+    if (s < SR::A4 + SR::V4) {
+      *reinterpret_cast<float4*>(f + 4 * s) = make_float4(r.x[rd][0], r.x[rd][1], r.x[rd][2], r.x[rd][3]);
+    } else if (s < SR::NSLOT) {
+      f[4 * (SR::A4 + SR::V4) + (s - SR::A4 - SR::V4)] = r.x[rd][0];
+    }
+  }
+}
+
+template <int N>
+__device__ inline void lds_read(const float* p, float (&o)[N]) {
+  if constexpr (N == 2) {
+    const float2 x = *reinterpret_cast<const float2*>(p);
+    o[0] = x.x; o[1] = x.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) o[i] = p[i];
+  }
+}
+
+template <int DK, int DV, typename InT>
+__global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
+  constexpr int NR = DK / 64;                  // key channels per lane
+  constexpr int PARTS = DV / kBwdPartCols;     // workgroups per (sequence, head)
+  constexpr int CK = 64 * NR * 4;              // floats of one wave's share of a checkpoint
+  static_assert(DV % kBwdPartCols == 0 && DK % 64 == 0, "unsupported head dimensions");
+  __shared__ __align__(16) BwdStage<DK> stage[2];
+  // per token parity and wave: the wave's row sums [dqhat | dkhat | dg] and dbeta
+  __shared__ float part[2][kBwdWaves][3 * DK + 1];
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r0 = l * NR;            // first key channel of the lane
+  const int wc = w * kBwdWaveCols;  // first column of the wave inside the part
+  const int pidx = (int)(blockIdx.x % PARTS);
+  const int64_t nh = blockIdx.x / PARTS;
+  const int h = (int)(nh % a.H);
+  const int64_t n = a.cu ? (int64_t)a.seq_order[nh / a.H] : nh / a.H;
+  const int c0 = pidx * kBwdPartCols;  // first column of the part
+  const int col = c0 + wc;             // first column of the wave
+
+  int64_t t0 = n * a.T, t1 = t0 + a.T, slot0 = n * a.nc * (kChunk / kBwdSeg);
+  if (a.cu) {
+    t0 = a.cu[n];
+    t1 = a.cu[n + 1];
+    t0 = t0 < 0 ? 0 : (t0 > a.T ? a.T : t0);
+    t1 = t1 < t0 ? t0 : (t1 > a.T ? a.T : t1);
+    slot0 = (int64_t)a.seq_off[n] * (kChunk / kBwdSeg);
+  }
+  int64_t nseg = (t1 - t0 + kBwdSeg - 1) / kBwdSeg;
+  if (a.cu) {
+    // the checkpoints the chunk map set aside for this sequence (fewer only when
+    // cu_seqlens breaks its precondition: the walk then stops there)
+    const int64_t end = (int64_t)a.seq_off[n + 1] < a.n_chunk_ub ? (int64_t)a.seq_off[n + 1] : a.n_chunk_ub;
+    const int64_t room = (end - a.seq_off[n]) * (kChunk / kBwdSeg);
+    nseg = nseg < room ? nseg : (room > 0 ? room : 0);
+    t1 = t0 + nseg * kBwdSeg < t1 ? t0 + nseg * kBwdSeg : t1;
+  }
+  const size_t sbase = ((size_t)n * a.H + h) * DK * DV;
+  auto ck = [&](int64_t seg) {
+    return a.ckpt + ((((size_t)(slot0 + seg) * a.H + h) * PARTS + pidx) * kBwdWaves + w) * CK;
+  };
+  auto put = [&](float* base, const float (&S)[NR][4]) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      *reinterpret_cast<float4*>(base + ((size_t)i * 64 + l) * 4) = make_float4(S[i][0], S[i][1], S[i][2], S[i][3]);
+  };
+  auto get = [&](const float* base, float (&S)[NR][4]) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) load4(base + ((size_t)i * 64 + l) * 4, S[i]);
+  };
+  auto seg_end = [&](int64_t ts) { return ts + kBwdSeg < t1 ? ts + kBwdSeg : t1; };
+
+  // walk 1: one forward step of the lane's state from the staged token u; the token's
+  // delta (v - a^T khat for the wave's columns) is stored for walk 2
+  auto fwd_step = [&](float (&S)[NR][4], const BwdStage<DK>& st, int u, int64_t tok) {
+    float ek[NR], kk[NR];
+    lds_read<NR>(&st.e[u][r0], ek);
+    lds_read<NR>(&st.kh[u][r0], kk);
+    const float4 vv = *reinterpret_cast<const float4*>(&st.v[u][wc]);
+    const float b = st.beta[u];
+    float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        S[i][j] *= ek[i];
+        p[j] = fmaf(kk[i], S[i][j], p[j]);
+      }
+    const float d[4] = {vv.x - wave_sum(p[0]), vv.y - wave_sum(p[1]), vv.z - wave_sum(p[2]),
+                        vv.w - wave_sum(p[3])};
+    if (l == 0) store4(a.delta + ((size_t)tok * a.H + h) * DV + col, d);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const float bk = b * kk[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[i][j] = fmaf(bk, d[j], S[i][j]);
+    }
+  };
+  // walk 2: the same step from the stored delta (elementwise: no sums over key channels,
+  // and bitwise the state walk 1 had)
+  auto replay_step = [&](float (&S)[NR][4], const BwdStage<DK>& st, int u) {
+    float ek[NR], kk[NR];
+    lds_read<NR>(&st.e[u][r0], ek);
+    lds_read<NR>(&st.kh[u][r0], kk);
+    const float4 dd = *reinterpret_cast<const float4*>(&st.v[u][wc]);
+    const float d[4] = {dd.x, dd.y, dd.z, dd.w};
+    const float b = st.beta[u];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const float bk = b * kk[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[i][j] = fmaf(bk, d[j], S[i][j] * ek[i]);
+    }
+  };
+
+  StageRegs<DK> rg;
+
+  // 1. forward with a checkpoint at every segment start
+  {
+    float S[NR][4];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      if (a.h0) load4(a.h0 + sbase + (size_t)(r0 + i) * DV + col, S[i]);
+      else S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
+    }
+    if (nseg > 0) {
+      stage_issue<DK, DV, InT, false>(rg, a, t0, seg_end(t0), h, c0);
+      stage_commit<DK>(rg, &stage[0]);
+    }
+    __syncthreads();
+    for (int64_t k = 0; k < nseg; ++k) {
+      const int64_t ts = t0 + k * kBwdSeg;
+      const int len = (int)(seg_end(ts) - ts);
+      if (k + 1 < nseg) stage_issue<DK, DV, InT, false>(rg, a, ts + kBwdSeg, seg_end(ts + kBwdSeg), h, c0);
+      put(ck(k), S);
+      const BwdStage<DK>& st = stage[k & 1];
+#pragma unroll
+      for (int u = 0; u < kBwdSeg; ++u)
+        if (u < len) fwd_step(S, st, u, ts + u);
+      if (k + 1 < nseg) stage_commit<DK>(rg, &stage[(k + 1) & 1]);
+      __syncthreads();  // also orders walk 1's delta and checkpoint stores before walk 2 reads them
+    }
+  }
+
+  // 2. backwards over the segments
+  float G[NR][4];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    if (a.dht) load4(a.dht + sbase + (size_t)(r0 + i) * DV + col, G[i]);
+    else G[i][0] = G[i][1] = G[i][2] = G[i][3] = 0.f;
+  }
+  InT* dvo = reinterpret_cast<InT*>(a.dv);
+  const size_t pbase = (size_t)pidx * (size_t)a.T_total * a.H;
+  int par = 0;
+  float ckn[NR][4];
+  if (nseg > 0) {
+    const int64_t ts = t0 + (nseg - 1) * kBwdSeg;
+    stage_issue<DK, DV, InT, true>(rg, a, ts, seg_end(ts), h, c0);
+    stage_commit<DK>(rg, &stage[(nseg - 1) & 1]);
+    get(ck(nseg - 1), ckn);
+  }
+  __syncthreads();
+  for (int64_t k = nseg - 1; k >= 0; --k) {
+    const int64_t ts = t0 + k * kBwdSeg;
+    const int len = (int)(seg_end(ts) - ts);
+    if (k > 0) stage_issue<DK, DV, InT, true>(rg, a, ts - kBwdSeg, ts, h, c0);
+    // St[u]: the state before token ts + u
+    float St[kBwdSeg][NR][4];
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) St[0][i][j] = ckn[i][j];
+    if (k > 0) get(ck(k - 1), ckn);  // the previous segment's checkpoint, one segment ahead
+    const BwdStage<DK>& st = stage[k & 1];
+#pragma unroll
+    for (int u = 0; u + 1 < kBwdSeg; ++u) {
+      if (u + 1 < len) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) St[u + 1][i][j] = St[u][i][j];
+        replay_step(St[u + 1], st, u);
+      }
+    }
+#pragma unroll
+    for (int u = kBwdSeg - 1; u >= 0; --u) {
+      if (u >= len) continue;
+      float (&A)[NR][4] = St[u];  // S_{t-1}, then a
+      const int64_t tok = ts + u;
+      float ek[NR], kk[NR], qq[NR];
+      lds_read<NR>(&st.e[u][r0], ek);
+      lds_read<NR>(&st.kh[u][r0], kk);
+      lds_read<NR>(&st.qh[u][r0], qq);
+      const float4 dd = *reinterpret_cast<const float4*>(&st.v[u][wc]);
+      const float d[4] = {dd.x, dd.y, dd.z, dd.w};
+      const float4 d4 = *reinterpret_cast<const float4*>(&st.dout[u][wc]);
+      const float dov[4] = {d4.x, d4.y, d4.z, d4.w};
+      const float b = st.beta[u];
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) A[i][j] *= ek[i];
+      // G += scale qhat do^T, then u = G^T khat (column sums over the key channels)
+      float uu[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const float sq = a.scale * qq[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          G[i][j] = fmaf(sq, dov[j], G[i][j]);
+          uu[j] = fmaf(kk[i], G[i][j], uu[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) uu[j] = wave_sum(uu[j]);
+      float ddo = 0.f, db = 0.f;  // delta . do and u . delta over the wave's columns
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ddo = fmaf(d[j], dov[j], ddo);
+        db = fmaf(uu[j], d[j], db);
+      }
+      float* pp = part[par][w];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        float aq = 0.f, gd = 0.f, au = 0.f, ag = 0.f;
+        const float bk = b * kk[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          aq = fmaf(A[i][j], dov[j], aq);
+          gd = fmaf(G[i][j], d[j], gd);
+          au = fmaf(A[i][j], uu[j], au);
+          const float da = G[i][j] - bk * uu[j];
+          ag = fmaf(A[i][j], da, ag);
+          G[i][j] = ek[i] * da;  // dL/dS_{t-1}
+        }
+        // dqhat = scale (a do + beta khat (delta . do)), dkhat = beta (G delta - a u), dg
+        pp[r0 + i] = a.scale * (aq + bk * ddo);
+        pp[DK + r0 + i] = b * (gd - au);
+        pp[2 * DK + r0 + i] = ag;
+      }
+      const size_t th = (size_t)tok * a.H + h;
+      if (l == 0) {
+        pp[3 * DK] = db;
+        // dv for the wave's columns (complete: no other wave or part touches them)
+        const float dvv[4] = {b * uu[0], b * uu[1], b * uu[2], b * uu[3]};
+        store4(dvo + th * DV + col, dvv);
+      }
+      __syncthreads();
+      // the waves' sums in a fixed order: this part's share of the row sums
+      for (int idx = tid; idx < 3 * DK + 1; idx += kBwdThreads) {
+        float acc = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kBwdWaves; ++ww) acc += part[par][ww][idx];
+        if (idx < DK) a.dqh_p[(pbase + th) * DK + idx] = acc;
+        else if (idx < 2 * DK) a.dkh_p[(pbase + th) * DK + idx - DK] = acc;
+        else if (idx < 3 * DK) a.dg_p[(pbase + th) * DK + idx - 2 * DK] = acc;
+        else a.dbeta_p[pbase + th] = acc;
+      }
+      par ^= 1;  // the other buffer is written next: one barrier per token suffices
+    }
+    if (k > 0) stage_commit<DK>(rg, &stage[(k - 1) & 1]);
+    __syncthreads();
+  }
+  if (a.dh0) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) store4(a.dh0 + sbase + (size_t)(r0 + i) * DV + col, G[i]);
+  }
+}
+
+// Pre-pass for the walks: unit q and k, x / |x| after the exact power-of-two rescale by
+// the largest entry (as in the forward kernels; a zero vector stays zero), and exp(g), one
+// wave per (token, head).
 template <int DK, typename InT>
-__global__ __launch_bounds__(256) void norm_bwd_kernel(const void* qv, const void* kv, const float* dqh,
-                                                       const float* dkh, void* dqv, void* dkv, int64_t rows) {
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const void* qv, const void* kv, const float* g, float* qh,
+                                                       float* kh, float* eg, int64_t rows) {
   constexpr int PL = DK / 64;  // channels per lane
   const int l = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;  // whole waves, no barrier
 #pragma unroll
+  for (int c = 0; c < PL; ++c) eg[row * DK + l * PL + c] = exp2_hw(g[row * DK + l * PL + c] * kLog2e);
+#pragma unroll
   for (int which = 0; which < 2; ++which) {
     const InT* x = reinterpret_cast<const InT*>(which ? kv : qv) + row * DK + l * PL;
-    const float* dxh = (which ? dkh : dqh) + row * DK + l * PL;
+    float* o = (which ? kh : qh) + row * DK + l * PL;
+    float xv[PL];
+#pragma unroll
+    for (int c = 0; c < PL; ++c) xv[c] = load1(x + c);
+    float m = 0.f;
+#pragma unroll
+    for (int c = 0; c < PL; ++c) m = fmaxf(m, fabsf(xv[c]));
+    m = wave_max(m);
+    const int ex = m > 0.f ? ilogb_pos(m) : 0;
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < PL; ++c) {
+      xv[c] = ldexpf(xv[c], -ex);
+      ss = fmaf(xv[c], xv[c], ss);
+    }
+    ss = wave_sum(ss);
+    const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
+#pragma unroll
+    for (int c = 0; c < PL; ++c) o[c] = xv[c] * inv;
+  }
+}
+
+// Finish: the parts' partial sums added in a fixed order (dg and dbeta written), then dq,
+// dk from dqhat, dkhat through the L2 normalisation: dx = (dxhat - xhat (xhat . dxhat)) / |x|
+// (0 for a zero vector), one wave per (token, head), the norm taken after the same exact
+// power-of-two rescale as in the forward kernels.
+template <int DK, typename InT>
+__global__ __launch_bounds__(256) void bwd_finish_kernel(const void* qv, const void* kv, const float* dqh_p,
+                                                         const float* dkh_p, const float* dg_p,
+                                                         const float* dbeta_p, int parts, int64_t rows,
+                                                         void* dqv, void* dkv, float* dg, void* dbeta) {
+  constexpr int PL = DK / 64;  // channels per lane
+  const int l = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // whole waves, no barrier
+  const size_t stride = (size_t)rows * DK;  // one part's share
+  {
+    float acc[PL];
+#pragma unroll
+    for (int c = 0; c < PL; ++c) acc[c] = 0.f;
+    for (int p = 0; p < parts; ++p)
+#pragma unroll
+      for (int c = 0; c < PL; ++c) acc[c] += dg_p[p * stride + row * DK + l * PL + c];
+#pragma unroll
+    for (int c = 0; c < PL; ++c) dg[row * DK + l * PL + c] = acc[c];
+    if (l == 0) {
+      float db = 0.f;
+      for (int p = 0; p < parts; ++p) db += dbeta_p[(size_t)p * rows + row];
+      store1(reinterpret_cast<InT*>(dbeta) + row, db);
+    }
+  }
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const InT* x = reinterpret_cast<const InT*>(which ? kv : qv) + row * DK + l * PL;
+    const float* dxp = (which ? dkh_p : dqh_p) + row * DK + l * PL;
     InT* dx = reinterpret_cast<InT*>(which ? dkv : dqv) + row * DK + l * PL;
     float xv[PL], dh[PL];
 #pragma unroll
     for (int c = 0; c < PL; ++c) {
       xv[c] = load1(x + c);
-      dh[c] = dxh[c];
+      dh[c] = 0.f;
     }
+    for (int p = 0; p < parts; ++p)
+#pragma unroll
+      for (int c = 0; c < PL; ++c) dh[c] += dxp[p * stride + c];
     float m = 0.f;
 #pragma unroll
     for (int c = 0; c < PL; ++c) m = fmaxf(m, fabsf(xv[c]));

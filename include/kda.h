@@ -200,8 +200,12 @@ kda_status_t kda_decode(const kda_problem_t* prob, const void* q, const void* k,
  *   dh0         [N, H, dk, dv] fp32    dL/dh0 (also when h0 is NULL, i.e. zero), or NULL
  *   workspace   >= kda_bwd_workspace_size(prob) bytes of device scratch
  *
- * The walk is token by token per (sequence, head) with the state split over 32-column
- * slices (fp32 throughout); the forward is replayed from checkpoints every 64 tokens.
+ * The walk is token by token per (sequence, head), fp32 throughout, with the state's
+ * value columns split over workgroups of 32 columns (4 per wave); a first walk stores the
+ * state every 8 tokens and each token's delta, and the reverse walk replays each 8-token
+ * segment from them.  The workspace holds those checkpoints (dk * dv * 4 bytes per 8
+ * tokens and head), unit q and k, exp(g), the deltas and each part's partial row sums:
+ * about 4.3 GB for 8,192 tokens of 32 heads at dk = dv = 128.
  * Conventions (stream, no allocation, errors, alignment) as for kda_fwd; outputs must
  * not overlap any input, the workspace or each other.  Results are deterministic.
  */
