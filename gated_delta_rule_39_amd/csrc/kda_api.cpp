@@ -295,11 +295,11 @@ kda_status_t kda_decode(const kda_problem_t* prob, const void* q, const void* k,
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-// Backward workspace: chunk map (packed), unit q and k, exp(g), checkpoints of the state at
-// every 8-token segment start, every token's delta, and each 32-column part's partial row
-// sums (dqhat, dkhat, dg, dbeta).
+// Backward workspace: chunk map (packed), the pre-pass records (unit q and k, exp(g), beta),
+// checkpoints of the state at every 8-token segment start, every token's delta, and each
+// 32-column part's partial row sums (dqhat, dkhat, dg, dbeta).
 struct BwdCarve {
-  size_t info, table, seq_off, seq_order, qh, kh, eg, ckpt, delta, dqh_p, dkh_p, dg_p, dbeta_p, total;
+  size_t info, table, seq_off, seq_order, rec, ckpt, delta, dqh_p, dkh_p, dg_p, dbeta_p, total;
 };
 
 static BwdCarve bwd_carve(const kda_problem_t* p, int64_t N, int64_t n_chunk_ub) {
@@ -311,10 +311,8 @@ static BwdCarve bwd_carve(const kda_problem_t* p, int64_t N, int64_t n_chunk_ub)
   c.table = c.info + 256;
   c.seq_off = c.table + align256((size_t)n_chunk_ub * 16);
   c.seq_order = c.seq_off + align256((size_t)(N + 1) * 4);
-  c.qh = c.seq_order + align256((size_t)N * 4);
-  c.kh = c.qh + align256(rows * p->dk * 4);
-  c.eg = c.kh + align256(rows * p->dk * 4);
-  c.ckpt = c.eg + align256(rows * p->dk * 4);
+  c.rec = c.seq_order + align256((size_t)N * 4);
+  c.ckpt = c.rec + align256(rows * (3 * (size_t)p->dk + 4) * 4);
   // every sequence of L tokens owns 8 slots per 64-token chunk, ceil(L / 8) <= 8 ceil(L / 64)
   c.delta = c.ckpt + align256((size_t)n_chunk_ub * 8 * p->heads * state);
   c.dqh_p = c.delta + align256(rows * p->dv * 4);
@@ -384,9 +382,7 @@ kda_status_t kda_bwd(const kda_problem_t* prob, const void* q, const void* k, co
   p.table = ws + c.table;
   p.seq_off = reinterpret_cast<int32_t*>(ws + c.seq_off);
   p.seq_order = reinterpret_cast<int32_t*>(ws + c.seq_order);
-  p.qh = reinterpret_cast<float*>(ws + c.qh);
-  p.kh = reinterpret_cast<float*>(ws + c.kh);
-  p.eg = reinterpret_cast<float*>(ws + c.eg);
+  p.rec = reinterpret_cast<float*>(ws + c.rec);
   p.ckpt = reinterpret_cast<float*>(ws + c.ckpt);
   p.delta = reinterpret_cast<float*>(ws + c.delta);
   p.dqh_p = reinterpret_cast<float*>(ws + c.dqh_p);

@@ -190,13 +190,13 @@ static hipError_t launch_backward_t(const BackwardPlan& p, hipStream_t stream) {
   const int64_t rows = p.T_total * (int64_t)p.H;
   if (rows > 0) {
     auto pre = bwd_prep_kernel<DK, InT>;
-    hipLaunchKernelGGL(pre, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p.q, p.k, p.g, p.qh, p.kh,
-                       p.eg, rows);
+    hipLaunchKernelGGL(pre, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p.q, p.k, p.g, p.beta,
+                       p.rec, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   BwdArgs a;
-  a.qh = p.qh; a.kh = p.kh; a.eg = p.eg; a.v = p.v; a.beta = p.beta; a.h0 = p.h0; a.cu = p.cu;
+  a.rec = p.rec; a.v = p.v; a.h0 = p.h0; a.cu = p.cu;
   a.seq_off = p.cu ? p.seq_off : nullptr;
   a.seq_order = p.cu ? p.seq_order : nullptr;
   a.dout = p.dout; a.dht = p.dht;

@@ -54,7 +54,7 @@ struct BackwardPlan {
   void* dq; void* dk_; void* dv_; float* dg; void* dbeta; float* dh0;
   // workspace
   int32_t* info; void* table; int32_t* seq_off; int32_t* seq_order;
-  float* qh; float* kh; float* eg;                        // unit q, k and exp(g) (pre-pass)
+  float* rec;                                             // per (token, head): qhat, khat, exp(g), beta
   float* ckpt;                                            // state checkpoints every 8 tokens
   float* delta;                                           // v - a^T khat of every token
   float* dqh_p; float* dkh_p; float* dg_p; float* dbeta_p;  // per-part row sums

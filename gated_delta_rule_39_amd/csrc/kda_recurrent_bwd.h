@@ -31,9 +31,10 @@
 //   2. backwards over the segments: the segment's forward is replayed from its
 //      checkpoint into registers (the state before each of its tokens), then its
 //      tokens are walked in reverse.
-// Each segment's inputs (unit q and k from the norm pre-pass, g, beta and the part's
-// columns of v and dout) are staged in LDS, the next segment's loads in flight while
-// the current one is walked, so a step waits on LDS, never on HBM.
+// A pre-pass packs, per (token, head), [qhat | khat | exp(g) | beta] into one fp32 record.
+// Each 8-token segment's records and the part's columns of v (walk 1) or of the stored
+// deltas and dout (walk 2) are staged in LDS, the next segment's loads in flight while the
+// current one is walked, so a step waits on LDS, never on HBM.
 #pragma once
 
 #include "kda_recurrent.h"
@@ -46,12 +47,16 @@ constexpr int kBwdPartCols = kBwdWaves * kBwdWaveCols;    // value columns per w
 constexpr int kBwdSeg = 8;                                // tokens per checkpoint segment
 constexpr int kBwdThreads = 64 * kBwdWaves;
 
+// The pre-pass record of one (token, head): qhat [DK], khat [DK], exp(g) [DK], beta, 3 zeros.
+template <int DK>
+struct BwdRec {
+  static constexpr int FLOATS = 3 * DK + 4;
+  static constexpr int U4 = FLOATS / 4;  // 16-byte units
+};
+
 struct BwdArgs {
-  const float* qh;        // [tokens, H, DK] fp32 unit q (pre-pass)
-  const float* kh;        // [tokens, H, DK] fp32 unit k
-  const float* eg;        // [tokens, H, DK] fp32 exp(g) (pre-pass)
+  const float* rec;       // [tokens, H, 3 DK + 4] fp32 records (pre-pass)
   const void* v;
-  const void* beta;
   const float* h0;
   const int32_t* cu;        // packed offsets (device) or NULL
   const int32_t* seq_off;   // packed: first 64-token chunk of each sequence (chunk map), or NULL
@@ -92,76 +97,81 @@ __device__ inline float wave_sum(float x) {
   return rows4_sum(x);
 }
 
-// One segment's inputs in LDS, fp32.  The arrays are contiguous in this order, so the
-// float4 slot s of the staging loads lands at float 4 s (qhat, khat, exp(g), v or delta,
-// dout), and beta follows.  Walk 1 stages v, walk 2 the deltas walk 1 stored.
-template <int DK>
-struct BwdStage {
-  float qh[kBwdSeg][DK];
-  float kh[kBwdSeg][DK];
-  float e[kBwdSeg][DK];
-  float v[kBwdSeg][kBwdPartCols];  // v (walk 1) or delta (walk 2)
-  float dout[kBwdSeg][kBwdPartCols];
-  float beta[kBwdSeg];
+// One segment's staged inputs in LDS, as 16-byte units copied unchanged from HBM:
+//   [kBwdSeg records][kBwdSeg rows of V1][kBwdSeg rows of V2]
+// V1 = the part's 32 columns of v (walk 1, io dtype) or of the deltas (walk 2, fp32),
+// V2 = the part's 32 columns of dout (walk 2 only, io dtype).  Slot s of the staging loads
+// is unit s.
+template <int DK, typename InT, bool WALK2>
+struct BwdStageMap {
+  static constexpr int AR = BwdRec<DK>::U4;                                 // units per record
+  static constexpr int V1 = kBwdPartCols * (WALK2 ? 4 : (int)sizeof(InT)) / 16;  // units per V1 row
+  static constexpr int V2 = WALK2 ? kBwdPartCols * (int)sizeof(InT) / 16 : 0;     // units per V2 row
+  static constexpr int UNITS = kBwdSeg * (AR + V1 + V2);
+  static constexpr int ROUNDS = (UNITS + kBwdThreads - 1) / kBwdThreads;
 };
-
-// A segment's staging loads held by one thread between issue and commit.
 template <int DK>
-struct StageRegs {
-  static constexpr int A4 = 3 * kBwdSeg * DK / 4;                 // float4 slots of qhat, khat, g
-  static constexpr int V4 = 2 * kBwdSeg * kBwdPartCols / 4;       // 4-element slots of v, dout
-  static constexpr int NSLOT = A4 + V4 + kBwdSeg;                 // + one slot per beta
-  static constexpr int ROUNDS = (NSLOT + kBwdThreads - 1) / kBwdThreads;
-  float x[ROUNDS][4];
-};
+constexpr int kBwdStageBytes = 16 * kBwdSeg * (BwdRec<DK>::U4 + 8 + 8);  // the largest map
 
-// Request the inputs of tokens [ts, te) (te - ts <= kBwdSeg; missing tokens read as 0)
-// of head h, value columns c0 .. c0 + 31 (WALK2: the stored deltas in place of v).
-template <int DK, int DV, typename InT, bool WALK2>
-__device__ inline void stage_issue(StageRegs<DK>& r, const BwdArgs& a, int64_t ts, int64_t te, int h, int c0) {
-  using SR = StageRegs<DK>;
+// Request the inputs of tokens [ts, te) (0 < te - ts <= kBwdSeg) of head h, value columns
+// c0 .. c0 + 31.  Every slot is one 16-byte load whose address is selected, not branched
+// on, so the loads stay in flight until the commit (slots past te read token te - 1 and
+// are never used).
+template <int DK, int DV, typename InT, bool WALK2, int R>
+__device__ inline void stage_issue(uint4_v (&r)[R], const BwdArgs& a, int64_t ts, int64_t te, int h, int c0) {
+  using M = BwdStageMap<DK, InT, WALK2>;
+  static_assert(R == M::ROUNDS, "staging registers");
+  const uint8_t* rec = reinterpret_cast<const uint8_t*>(a.rec);
+  const uint8_t* v1 = WALK2 ? reinterpret_cast<const uint8_t*>(a.delta) : reinterpret_cast<const uint8_t*>(a.v);
+  const uint8_t* v2 = reinterpret_cast<const uint8_t*>(a.dout);
+  constexpr size_t E1 = WALK2 ? 4 : sizeof(InT);
+  auto tok = [&](int u) { return ts + u < te ? ts + u : te - 1; };
 #pragma unroll
-  for (int rd = 0; rd < SR::ROUNDS; ++rd) {
+  for (int rd = 0; rd < M::ROUNDS; ++rd) {
     const int s = (int)threadIdx.x + rd * kBwdThreads;
-    r.x[rd][0] = r.x[rd][1] = r.x[rd][2] = r.x[rd][3] = 0.f;
-    if (s < SR::A4) {
-      constexpr int PER = kBwdSeg * DK / 4;
-      const int which = s / PER, rem = s % PER;
-      const int64_t t = ts + rem / (DK / 4);
-      const float* src = which == 0 ? a.qh : (which == 1 ? a.kh : a.eg);
-      if (t < te) load4(src + ((size_t)t * a.H + h) * DK + 4 * (rem % (DK / 4)), r.x[rd]);
-    } else if (s < SR::A4 + SR::V4) {
-      constexpr int PER = kBwdSeg * kBwdPartCols / 4;
-      const int s2 = s - SR::A4;
-      const int which = s2 / PER, rem = s2 % PER;
-      const int64_t t = ts + rem / (kBwdPartCols / 4);
-      const size_t off = ((size_t)t * a.H + h) * DV + c0 + 4 * (rem % (kBwdPartCols / 4));
-      if (t < te) {
-        if (which != 0) load4(reinterpret_cast<const InT*>(a.dout) + off, r.x[rd]);
-        else if (WALK2) load4(a.delta + off, r.x[rd]);
-        else load4(reinterpret_cast<const InT*>(a.v) + off, r.x[rd]);
-      }
-    } else if (s < SR::NSLOT) {
-      const int64_t t = ts + (s - SR::A4 - SR::V4);
-      if (t < te) r.x[rd][0] = load1(reinterpret_cast<const InT*>(a.beta) + (size_t)t * a.H + h);
+    const int s1 = s - kBwdSeg * M::AR;
+    const int s2 = s1 - kBwdSeg * M::V1;
+    const uint8_t* src;
+    if (s1 < 0) {
+      src = rec + (((size_t)tok(s / M::AR) * a.H + h) * M::AR + s % M::AR) * 16;
+    } else if (s2 < 0) {
+      src = v1 + (((size_t)tok(s1 / M::V1) * a.H + h) * DV + c0) * E1 + (size_t)(s1 % M::V1) * 16;
+    } else {
+      const int s2c = M::V2 > 0 ? s2 : 0;
+      const int v2u = M::V2 > 0 ? M::V2 : 1;
+      src = v2 + (((size_t)tok(s2c / v2u) * a.H + h) * DV + c0) * sizeof(InT) + (size_t)(s2c % v2u) * 16;
     }
+    if (s < M::UNITS) r[rd] = *reinterpret_cast<const uint4_v*>(src);
   }
 }
 
-template <int DK>
-__device__ inline void stage_commit(const StageRegs<DK>& r, BwdStage<DK>* st) {
-  using SR = StageRegs<DK>;
-  float* f = reinterpret_cast<float*>(st);
+template <int DK, typename InT, bool WALK2, int R>
+__device__ inline void stage_commit(const uint4_v (&r)[R], uint8_t* st) {
+  using M = BwdStageMap<DK, InT, WALK2>;
+  static_assert(R == M::ROUNDS, "staging registers");
 #pragma unroll
-  for (int rd = 0; rd < SR::ROUNDS; ++rd) {
+  for (int rd = 0; rd < M::ROUNDS; ++rd) {
     const int s = (int)threadIdx.x + rd * kBwdThreads;
-    if (s < SR::A4 + SR::V4) {
-      *reinterpret_cast<float4*>(f + 4 * s) = make_float4(r.x[rd][0], r.x[rd][1], r.x[rd][2], r.x[rd][3]);
-    } else if (s < SR::NSLOT) {
-      f[4 * (SR::A4 + SR::V4) + (s - SR::A4 - SR::V4)] = r.x[rd][0];
-    }
+    if (s < M::UNITS) *reinterpret_cast<uint4_v*>(st + (size_t)s * 16) = r[rd];
   }
 }
+
+// Four consecutive staged elements of a V row as fp32.
+__device__ inline void lds4(const uint8_t* p, bool bf16, float* o) {
+  if (bf16) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    o[0] = __uint_as_float(x.x << 16); o[1] = __uint_as_float(x.x & 0xffff0000u);
+    o[2] = __uint_as_float(x.y << 16); o[3] = __uint_as_float(x.y & 0xffff0000u);
+  } else {
+    const float4 x = *reinterpret_cast<const float4*>(p);
+    o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+  }
+}
+
+// s_waitcnt vmcnt(0) as an instruction the compiler's wait tracking sees (gfx9 encoding:
+// vmcnt 0, expcnt and lgkmcnt at their maxima): no vector-memory load is pending after it
+// on any path, so a walk's loop never waits on loads issued before it.
+__device__ inline void wait_vm_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int N>
 __device__ inline void lds_read(const float* p, float (&o)[N]) {
@@ -174,13 +184,47 @@ __device__ inline void lds_read(const float* p, float (&o)[N]) {
   }
 }
 
+// Sums over the wave of four independent values, the four reductions interleaved step by
+// step so that each one's DPP and row-swap latencies overlap the others.
+__device__ inline void wave_sum4(float (&x)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] += row_ror_z<8>(x[j]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] += row_ror_z<4>(x[j]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] += row_ror_z<2>(x[j]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] += row_ror_z<1>(x[j]);
+  uint32_t y[4][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[j]), __float_as_uint(x[j]), false, false);
+    y[j][0] = t[0];
+    y[j][1] = t[1];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = __uint_as_float(y[j][0]) + __uint_as_float(y[j][1]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[j]), __float_as_uint(x[j]), false, false);
+    y[j][0] = t[0];
+    y[j][1] = t[1];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = __uint_as_float(y[j][0]) + __uint_as_float(y[j][1]);
+}
+
 template <int DK, int DV, typename InT>
 __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
   constexpr int NR = DK / 64;                  // key channels per lane
   constexpr int PARTS = DV / kBwdPartCols;     // workgroups per (sequence, head)
   constexpr int CK = 64 * NR * 4;              // floats of one wave's share of a checkpoint
+  constexpr bool BF = sizeof(InT) == 2;
+  using M1 = BwdStageMap<DK, InT, false>;
+  using M2 = BwdStageMap<DK, InT, true>;
+  constexpr int RF = BwdRec<DK>::FLOATS;
   static_assert(DV % kBwdPartCols == 0 && DK % 64 == 0, "unsupported head dimensions");
-  __shared__ __align__(16) BwdStage<DK> stage[2];
+  __shared__ __align__(16) uint8_t stage[2][kBwdStageBytes<DK>];
   // per token parity and wave: the wave's row sums [dqhat | dkhat | dg] and dbeta
   __shared__ float part[2][kBwdWaves][3 * DK + 1];
   const int tid = threadIdx.x;
@@ -226,15 +270,26 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
     for (int i = 0; i < NR; ++i) load4(base + ((size_t)i * 64 + l) * 4, S[i]);
   };
   auto seg_end = [&](int64_t ts) { return ts + kBwdSeg < t1 ? ts + kBwdSeg : t1; };
+  // staged token u: its record, and the wave's four columns of V1 / V2
+  auto srec = [&](const uint8_t* st, int u) { return reinterpret_cast<const float*>(st) + u * RF; };
+  auto sv1 = [&](const uint8_t* st, int u, bool walk2, float* o) {
+    const int v1u = walk2 ? M2::V1 : M1::V1;
+    const size_t e1 = walk2 ? 4 : sizeof(InT);
+    lds4(st + 16 * (kBwdSeg * M1::AR + u * v1u) + wc * e1, BF && !walk2, o);
+  };
+  auto sv2 = [&](const uint8_t* st, int u, float* o) {
+    lds4(st + 16 * (kBwdSeg * (M2::AR + M2::V1) + u * M2::V2) + wc * sizeof(InT), BF, o);
+  };
 
   // walk 1: one forward step of the lane's state from the staged token u; the token's
   // delta (v - a^T khat for the wave's columns) is stored for walk 2
-  auto fwd_step = [&](float (&S)[NR][4], const BwdStage<DK>& st, int u, int64_t tok) {
-    float ek[NR], kk[NR];
-    lds_read<NR>(&st.e[u][r0], ek);
-    lds_read<NR>(&st.kh[u][r0], kk);
-    const float4 vv = *reinterpret_cast<const float4*>(&st.v[u][wc]);
-    const float b = st.beta[u];
+  auto fwd_step = [&](float (&S)[NR][4], const uint8_t* st, int u, int64_t tok) {
+    const float* rc = srec(st, u);
+    float ek[NR], kk[NR], vv[4];
+    lds_read<NR>(rc + 2 * DK + r0, ek);
+    lds_read<NR>(rc + DK + r0, kk);
+    sv1(st, u, false, vv);
+    const float b = rc[3 * DK];
     float p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NR; ++i)
@@ -243,8 +298,8 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
         S[i][j] *= ek[i];
         p[j] = fmaf(kk[i], S[i][j], p[j]);
       }
-    const float d[4] = {vv.x - wave_sum(p[0]), vv.y - wave_sum(p[1]), vv.z - wave_sum(p[2]),
-                        vv.w - wave_sum(p[3])};
+    wave_sum4(p);
+    const float d[4] = {vv[0] - p[0], vv[1] - p[1], vv[2] - p[2], vv[3] - p[3]};
     if (l == 0) store4(a.delta + ((size_t)tok * a.H + h) * DV + col, d);
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -255,13 +310,13 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
   };
   // walk 2: the same step from the stored delta (elementwise: no sums over key channels,
   // and bitwise the state walk 1 had)
-  auto replay_step = [&](float (&S)[NR][4], const BwdStage<DK>& st, int u) {
-    float ek[NR], kk[NR];
-    lds_read<NR>(&st.e[u][r0], ek);
-    lds_read<NR>(&st.kh[u][r0], kk);
-    const float4 dd = *reinterpret_cast<const float4*>(&st.v[u][wc]);
-    const float d[4] = {dd.x, dd.y, dd.z, dd.w};
-    const float b = st.beta[u];
+  auto replay_step = [&](float (&S)[NR][4], const uint8_t* st, int u) {
+    const float* rc = srec(st, u);
+    float ek[NR], kk[NR], d[4];
+    lds_read<NR>(rc + 2 * DK + r0, ek);
+    lds_read<NR>(rc + DK + r0, kk);
+    sv1(st, u, true, d);
+    const float b = rc[3 * DK];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const float bk = b * kk[i];
@@ -270,10 +325,9 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
     }
   };
 
-  StageRegs<DK> rg;
-
   // 1. forward with a checkpoint at every segment start
   {
+    uint4_v rg[M1::ROUNDS];
     float S[NR][4];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -282,24 +336,26 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
     }
     if (nseg > 0) {
       stage_issue<DK, DV, InT, false>(rg, a, t0, seg_end(t0), h, c0);
-      stage_commit<DK>(rg, &stage[0]);
+      stage_commit<DK, InT, false>(rg, stage[0]);
     }
+    wait_vm_loads();
     __syncthreads();
     for (int64_t k = 0; k < nseg; ++k) {
       const int64_t ts = t0 + k * kBwdSeg;
       const int len = (int)(seg_end(ts) - ts);
       if (k + 1 < nseg) stage_issue<DK, DV, InT, false>(rg, a, ts + kBwdSeg, seg_end(ts + kBwdSeg), h, c0);
       put(ck(k), S);
-      const BwdStage<DK>& st = stage[k & 1];
+      const uint8_t* st = stage[k & 1];
 #pragma unroll
       for (int u = 0; u < kBwdSeg; ++u)
         if (u < len) fwd_step(S, st, u, ts + u);
-      if (k + 1 < nseg) stage_commit<DK>(rg, &stage[(k + 1) & 1]);
+      if (k + 1 < nseg) stage_commit<DK, InT, false>(rg, stage[(k + 1) & 1]);
       __syncthreads();  // also orders walk 1's delta and checkpoint stores before walk 2 reads them
     }
   }
 
   // 2. backwards over the segments
+  uint4_v rg[M2::ROUNDS];
   float G[NR][4];
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
@@ -313,9 +369,10 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
   if (nseg > 0) {
     const int64_t ts = t0 + (nseg - 1) * kBwdSeg;
     stage_issue<DK, DV, InT, true>(rg, a, ts, seg_end(ts), h, c0);
-    stage_commit<DK>(rg, &stage[(nseg - 1) & 1]);
+    stage_commit<DK, InT, true>(rg, stage[(nseg - 1) & 1]);
     get(ck(nseg - 1), ckn);
   }
+  wait_vm_loads();
   __syncthreads();
   for (int64_t k = nseg - 1; k >= 0; --k) {
     const int64_t ts = t0 + k * kBwdSeg;
@@ -328,7 +385,7 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) St[0][i][j] = ckn[i][j];
     if (k > 0) get(ck(k - 1), ckn);  // the previous segment's checkpoint, one segment ahead
-    const BwdStage<DK>& st = stage[k & 1];
+    const uint8_t* st = stage[k & 1];
 #pragma unroll
     for (int u = 0; u + 1 < kBwdSeg; ++u) {
       if (u + 1 < len) {
@@ -344,15 +401,14 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
       if (u >= len) continue;
       float (&A)[NR][4] = St[u];  // S_{t-1}, then a
       const int64_t tok = ts + u;
-      float ek[NR], kk[NR], qq[NR];
-      lds_read<NR>(&st.e[u][r0], ek);
-      lds_read<NR>(&st.kh[u][r0], kk);
-      lds_read<NR>(&st.qh[u][r0], qq);
-      const float4 dd = *reinterpret_cast<const float4*>(&st.v[u][wc]);
-      const float d[4] = {dd.x, dd.y, dd.z, dd.w};
-      const float4 d4 = *reinterpret_cast<const float4*>(&st.dout[u][wc]);
-      const float dov[4] = {d4.x, d4.y, d4.z, d4.w};
-      const float b = st.beta[u];
+      const float* rc = srec(st, u);
+      float ek[NR], kk[NR], qq[NR], d[4], dov[4];
+      lds_read<NR>(rc + 2 * DK + r0, ek);
+      lds_read<NR>(rc + DK + r0, kk);
+      lds_read<NR>(rc + r0, qq);
+      sv1(st, u, true, d);
+      sv2(st, u, dov);
+      const float b = rc[3 * DK];
 #pragma unroll
       for (int i = 0; i < NR; ++i)
 #pragma unroll
@@ -368,8 +424,7 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
           uu[j] = fmaf(kk[i], G[i][j], uu[j]);
         }
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) uu[j] = wave_sum(uu[j]);
+      wave_sum4(uu);
       float ddo = 0.f, db = 0.f;  // delta . do and u . delta over the wave's columns
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -415,7 +470,7 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
       }
       par ^= 1;  // the other buffer is written next: one barrier per token suffices
     }
-    if (k > 0) stage_commit<DK>(rg, &stage[(k - 1) & 1]);
+    if (k > 0) stage_commit<DK, InT, true>(rg, stage[(k - 1) & 1]);
     __syncthreads();
   }
   if (a.dh0) {
@@ -424,22 +479,23 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
   }
 }
 
-// Pre-pass for the walks: unit q and k, x / |x| after the exact power-of-two rescale by
-// the largest entry (as in the forward kernels; a zero vector stays zero), and exp(g), one
-// wave per (token, head).
+// Pre-pass for the walks, one wave per (token, head): the record [qhat | khat | exp(g) |
+// beta, 0, 0, 0], with x / |x| taken after the exact power-of-two rescale by the largest
+// entry (as in the forward kernels; a zero vector stays zero).
 template <int DK, typename InT>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const void* qv, const void* kv, const float* g, float* qh,
-                                                       float* kh, float* eg, int64_t rows) {
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const void* qv, const void* kv, const float* g,
+                                                       const void* beta, float* rec, int64_t rows) {
   constexpr int PL = DK / 64;  // channels per lane
   const int l = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;  // whole waves, no barrier
+  float* o = rec + row * BwdRec<DK>::FLOATS;
 #pragma unroll
-  for (int c = 0; c < PL; ++c) eg[row * DK + l * PL + c] = exp2_hw(g[row * DK + l * PL + c] * kLog2e);
+  for (int c = 0; c < PL; ++c) o[2 * DK + l * PL + c] = exp2_hw(g[row * DK + l * PL + c] * kLog2e);
+  if (l < 4) o[3 * DK + l] = l == 0 ? load1(reinterpret_cast<const InT*>(beta) + row) : 0.f;
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
     const InT* x = reinterpret_cast<const InT*>(which ? kv : qv) + row * DK + l * PL;
-    float* o = (which ? kh : qh) + row * DK + l * PL;
     float xv[PL];
 #pragma unroll
     for (int c = 0; c < PL; ++c) xv[c] = load1(x + c);
@@ -457,7 +513,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* qv, const voi
     ss = wave_sum(ss);
     const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
 #pragma unroll
-    for (int c = 0; c < PL; ++c) o[c] = xv[c] * inv;
+    for (int c = 0; c < PL; ++c) o[which * DK + l * PL + c] = xv[c] * inv;
   }
 }
 
