@@ -297,14 +297,14 @@ kda_status_t kda_decode(const kda_problem_t* prob, const void* q, const void* k,
 
 // Backward workspace: chunk map (packed), the pre-pass records (unit q and k, exp(g), beta),
 // checkpoints of the state at every 8-token segment start, every token's delta, and each
-// 32-column part's partial row sums (dqhat, dkhat, dg, dbeta).
+// column part's partial row sums (dqhat, dkhat, dg, dbeta).
 struct BwdCarve {
   size_t info, table, seq_off, seq_order, rec, ckpt, delta, dqh_p, dkh_p, dg_p, dbeta_p, total;
 };
 
 static BwdCarve bwd_carve(const kda_problem_t* p, int64_t N, int64_t n_chunk_ub) {
   BwdCarve c;
-  const size_t parts = (size_t)p->dv / 32;
+  const size_t parts = (size_t)kda::backward_parts(p->dv);
   const size_t state = (size_t)p->dk * p->dv * 4;
   const size_t rows = (size_t)(p->batch * p->seqlen) * p->heads;
   c.info = 0;

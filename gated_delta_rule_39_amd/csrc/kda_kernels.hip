@@ -221,6 +221,8 @@ static hipError_t launch_backward_dt(const BackwardPlan& p, hipStream_t stream) 
   return p.dtype == 0 ? launch_backward_t<DK, DV, uint16_t>(p, stream) : launch_backward_t<DK, DV, float>(p, stream);
 }
 
+int backward_parts(int dv) { return dv / kBwdPartCols; }
+
 hipError_t launch_backward(const BackwardPlan& p, hipStream_t stream) {
   if (p.N <= 0) return hipSuccess;
   if (p.cu) {

@@ -62,6 +62,10 @@ struct BackwardPlan {
 
 hipError_t launch_backward(const BackwardPlan& p, hipStream_t stream);
 
+// Workgroups of the backward kernel per (sequence, head): the value columns are cut into
+// this many parts, each with its own partial row sums in the workspace.
+int backward_parts(int dv);
+
 // Enqueue the token-by-token recurrent kernel on `stream` (uses the sizes, tensors and
 // scale of `p`; no workspace).
 hipError_t launch_recurrent(const ForwardPlan& p, hipStream_t stream);

@@ -16,10 +16,10 @@
 // the L2 normalisation (finish kernel).
 //
 // Work split.  The value columns of the state evolve independently (a step mixes
-// key channels only), so each (sequence, head) is cut into parts of 32 value
-// columns, one workgroup per part, and each of its eight waves owns 4 columns: lane
-// l holds key channels l*NR .. l*NR + NR - 1 (NR = dk / 64) of those 4 columns, so
-// a lane carries 8 state elements (dk = 128) and a step is short.  Sums over key
+// key channels only), so each (sequence, head) is cut into parts of 16 value
+// columns, one workgroup per part, and each of its eight waves owns 2 columns: lane
+// l holds key channels l*NR .. l*NR + NR - 1 (NR = dk / 64) of those 2 columns, so
+// a lane carries 4 state elements (dk = 128) and a step is short.  Sums over key
 // channels (per column) are wave sums; the per-row sums dqhat, dkhat, dg and the
 // scalar dbeta add the eight waves' columns through LDS in a fixed order, and the
 // parts' partial sums are added (again in a fixed order) by the finish kernel:
@@ -42,7 +42,7 @@
 namespace kda {
 
 constexpr int kBwdWaves = 8;                              // waves per workgroup
-constexpr int kBwdWaveCols = 4;                           // value columns per wave
+constexpr int kBwdWaveCols = 2;                           // value columns per wave (2 or 4)
 constexpr int kBwdPartCols = kBwdWaves * kBwdWaveCols;    // value columns per workgroup
 constexpr int kBwdSeg = 8;                                // tokens per checkpoint segment
 constexpr int kBwdThreads = 64 * kBwdWaves;
@@ -99,8 +99,8 @@ __device__ inline float wave_sum(float x) {
 
 // One segment's staged inputs in LDS, as 16-byte units copied unchanged from HBM:
 //   [kBwdSeg records][kBwdSeg rows of V1][kBwdSeg rows of V2]
-// V1 = the part's 32 columns of v (walk 1, io dtype) or of the deltas (walk 2, fp32),
-// V2 = the part's 32 columns of dout (walk 2 only, io dtype).  Slot s of the staging loads
+// V1 = the part's columns of v (walk 1, io dtype) or of the deltas (walk 2, fp32),
+// V2 = the part's columns of dout (walk 2 only, io dtype).  Slot s of the staging loads
 // is unit s.
 template <int DK, typename InT, bool WALK2>
 struct BwdStageMap {
@@ -113,10 +113,10 @@ struct BwdStageMap {
 template <int DK>
 constexpr int kBwdStageBytes = 16 * kBwdSeg * (BwdRec<DK>::U4 + 8 + 8);  // the largest map
 
-// Request the inputs of tokens [ts, te) (0 < te - ts <= kBwdSeg) of head h, value columns
-// c0 .. c0 + 31.  Every slot is one 16-byte load whose address is selected, not branched
-// on, so the loads stay in flight until the commit (slots past te read token te - 1 and
-// are never used).
+// Request the inputs of tokens [ts, te) (0 < te - ts <= kBwdSeg) of head h, the part's value
+// columns from c0.  Every slot is one unconditional 16-byte load whose address is chosen
+// first, so no value merge waits on a load and the loads stay in flight until the commit
+// (slots past te read token te - 1 and are never used).
 template <int DK, int DV, typename InT, bool WALK2, int R>
 __device__ inline void stage_issue(uint4_v (&r)[R], const BwdArgs& a, int64_t ts, int64_t te, int h, int c0) {
   using M = BwdStageMap<DK, InT, WALK2>;
@@ -141,7 +141,9 @@ __device__ inline void stage_issue(uint4_v (&r)[R], const BwdArgs& a, int64_t ts
       const int v2u = M::V2 > 0 ? M::V2 : 1;
       src = v2 + (((size_t)tok(s2c / v2u) * a.H + h) * DV + c0) * sizeof(InT) + (size_t)(s2c % v2u) * 16;
     }
-    if (s < M::UNITS) r[rd] = *reinterpret_cast<const uint4_v*>(src);
+    // slots past UNITS fall in the last region with an in-bounds address (clamped token,
+    // unit index modulo the row): loaded unconditionally, never committed
+    r[rd] = *reinterpret_cast<const uint4_v*>(src);
   }
 }
 
@@ -156,16 +158,52 @@ __device__ inline void stage_commit(const uint4_v (&r)[R], uint8_t* st) {
   }
 }
 
-// Four consecutive staged elements of a V row as fp32.
-__device__ inline void lds4(const uint8_t* p, bool bf16, float* o) {
-  if (bf16) {
-    const uint2 x = *reinterpret_cast<const uint2*>(p);
-    o[0] = __uint_as_float(x.x << 16); o[1] = __uint_as_float(x.x & 0xffff0000u);
-    o[2] = __uint_as_float(x.y << 16); o[3] = __uint_as_float(x.y & 0xffff0000u);
+// WC (2 or 4) consecutive staged elements of a V row as fp32.
+template <int WC>
+__device__ inline void lds_cols(const uint8_t* p, bool bf16, float* o) {
+  if constexpr (WC == 4) {
+    if (bf16) {
+      const uint2 x = *reinterpret_cast<const uint2*>(p);
+      o[0] = __uint_as_float(x.x << 16); o[1] = __uint_as_float(x.x & 0xffff0000u);
+      o[2] = __uint_as_float(x.y << 16); o[3] = __uint_as_float(x.y & 0xffff0000u);
+    } else {
+      const float4 x = *reinterpret_cast<const float4*>(p);
+      o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+    }
   } else {
-    const float4 x = *reinterpret_cast<const float4*>(p);
-    o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+    if (bf16) {
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(p);
+      o[0] = __uint_as_float(x << 16); o[1] = __uint_as_float(x & 0xffff0000u);
+    } else {
+      const float2 x = *reinterpret_cast<const float2*>(p);
+      o[0] = x.x; o[1] = x.y;
+    }
   }
+}
+
+// WC consecutive global elements (fp32 or bf16) as fp32, and back (bf16 rounds to nearest
+// even).
+template <int WC, typename T>
+__device__ inline void gload_cols(const T* p, float* o) {
+  if constexpr (WC == 4) {
+    load4(p, o);
+  } else if constexpr (sizeof(T) == 4) {
+    const float2 x = *reinterpret_cast<const float2*>(p);
+    o[0] = x.x; o[1] = x.y;
+  } else {
+    const uint32_t x = *reinterpret_cast<const uint32_t*>(p);
+    o[0] = __uint_as_float(x << 16); o[1] = __uint_as_float(x & 0xffff0000u);
+  }
+}
+template <int WC>
+__device__ inline void gstore_cols(float* p, const float* x) {
+  if constexpr (WC == 4) store4(p, x);
+  else *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+}
+template <int WC>
+__device__ inline void gstore_cols(uint16_t* p, const float* x) {
+  if constexpr (WC == 4) store4(p, x);
+  else *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(x[0], x[1]);
 }
 
 // s_waitcnt vmcnt(0) as an instruction the compiler's wait tracking sees (gfx9 encoding:
@@ -184,41 +222,43 @@ __device__ inline void lds_read(const float* p, float (&o)[N]) {
   }
 }
 
-// Sums over the wave of four independent values, the four reductions interleaved step by
-// step so that each one's DPP and row-swap latencies overlap the others.
-__device__ inline void wave_sum4(float (&x)[4]) {
+// Sums over the wave of N independent values, the reductions interleaved step by step so
+// that each one's DPP and row-swap latencies overlap the others.
+template <int N>
+__device__ inline void wave_sums(float (&x)[N]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) x[j] += row_ror_z<8>(x[j]);
+  for (int j = 0; j < N; ++j) x[j] += row_ror_z<8>(x[j]);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) x[j] += row_ror_z<4>(x[j]);
+  for (int j = 0; j < N; ++j) x[j] += row_ror_z<4>(x[j]);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) x[j] += row_ror_z<2>(x[j]);
+  for (int j = 0; j < N; ++j) x[j] += row_ror_z<2>(x[j]);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) x[j] += row_ror_z<1>(x[j]);
-  uint32_t y[4][2];
+  for (int j = 0; j < N; ++j) x[j] += row_ror_z<1>(x[j]);
+  uint32_t y[N][2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < N; ++j) {
     const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[j]), __float_as_uint(x[j]), false, false);
     y[j][0] = t[0];
     y[j][1] = t[1];
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) x[j] = __uint_as_float(y[j][0]) + __uint_as_float(y[j][1]);
+  for (int j = 0; j < N; ++j) x[j] = __uint_as_float(y[j][0]) + __uint_as_float(y[j][1]);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < N; ++j) {
     const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[j]), __float_as_uint(x[j]), false, false);
     y[j][0] = t[0];
     y[j][1] = t[1];
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) x[j] = __uint_as_float(y[j][0]) + __uint_as_float(y[j][1]);
+  for (int j = 0; j < N; ++j) x[j] = __uint_as_float(y[j][0]) + __uint_as_float(y[j][1]);
 }
 
 template <int DK, int DV, typename InT>
 __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
   constexpr int NR = DK / 64;                  // key channels per lane
   constexpr int PARTS = DV / kBwdPartCols;     // workgroups per (sequence, head)
-  constexpr int CK = 64 * NR * 4;              // floats of one wave's share of a checkpoint
+  constexpr int WC = kBwdWaveCols;             // value columns per wave
+  constexpr int CK = 64 * NR * WC;             // floats of one wave's share of a checkpoint
   constexpr bool BF = sizeof(InT) == 2;
   using M1 = BwdStageMap<DK, InT, false>;
   using M2 = BwdStageMap<DK, InT, true>;
@@ -260,14 +300,13 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
   auto ck = [&](int64_t seg) {
     return a.ckpt + ((((size_t)(slot0 + seg) * a.H + h) * PARTS + pidx) * kBwdWaves + w) * CK;
   };
-  auto put = [&](float* base, const float (&S)[NR][4]) {
+  auto put = [&](float* base, const float (&S)[NR][WC]) {
 #pragma unroll
-    for (int i = 0; i < NR; ++i)
-      *reinterpret_cast<float4*>(base + ((size_t)i * 64 + l) * 4) = make_float4(S[i][0], S[i][1], S[i][2], S[i][3]);
+    for (int i = 0; i < NR; ++i) gstore_cols<WC>(base + ((size_t)i * 64 + l) * WC, S[i]);
   };
-  auto get = [&](const float* base, float (&S)[NR][4]) {
+  auto get = [&](const float* base, float (&S)[NR][WC]) {
 #pragma unroll
-    for (int i = 0; i < NR; ++i) load4(base + ((size_t)i * 64 + l) * 4, S[i]);
+    for (int i = 0; i < NR; ++i) gload_cols<WC>(base + ((size_t)i * 64 + l) * WC, S[i]);
   };
   auto seg_end = [&](int64_t ts) { return ts + kBwdSeg < t1 ? ts + kBwdSeg : t1; };
   // staged token u: its record, and the wave's four columns of V1 / V2
@@ -275,44 +314,48 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
   auto sv1 = [&](const uint8_t* st, int u, bool walk2, float* o) {
     const int v1u = walk2 ? M2::V1 : M1::V1;
     const size_t e1 = walk2 ? 4 : sizeof(InT);
-    lds4(st + 16 * (kBwdSeg * M1::AR + u * v1u) + wc * e1, BF && !walk2, o);
+    lds_cols<WC>(st + 16 * (kBwdSeg * M1::AR + u * v1u) + wc * e1, BF && !walk2, o);
   };
   auto sv2 = [&](const uint8_t* st, int u, float* o) {
-    lds4(st + 16 * (kBwdSeg * (M2::AR + M2::V1) + u * M2::V2) + wc * sizeof(InT), BF, o);
+    lds_cols<WC>(st + 16 * (kBwdSeg * (M2::AR + M2::V1) + u * M2::V2) + wc * sizeof(InT), BF, o);
   };
 
   // walk 1: one forward step of the lane's state from the staged token u; the token's
   // delta (v - a^T khat for the wave's columns) is stored for walk 2
-  auto fwd_step = [&](float (&S)[NR][4], const uint8_t* st, int u, int64_t tok) {
+  auto fwd_step = [&](float (&S)[NR][WC], const uint8_t* st, int u, int64_t tok) {
     const float* rc = srec(st, u);
-    float ek[NR], kk[NR], vv[4];
+    float ek[NR], kk[NR], vv[WC];
     lds_read<NR>(rc + 2 * DK + r0, ek);
     lds_read<NR>(rc + DK + r0, kk);
     sv1(st, u, false, vv);
     const float b = rc[3 * DK];
-    float p[4] = {0.f, 0.f, 0.f, 0.f};
+    float p[WC];
+#pragma unroll
+    for (int j = 0; j < WC; ++j) p[j] = 0.f;
 #pragma unroll
     for (int i = 0; i < NR; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < WC; ++j) {
         S[i][j] *= ek[i];
         p[j] = fmaf(kk[i], S[i][j], p[j]);
       }
-    wave_sum4(p);
-    const float d[4] = {vv[0] - p[0], vv[1] - p[1], vv[2] - p[2], vv[3] - p[3]};
-    if (l == 0) store4(a.delta + ((size_t)tok * a.H + h) * DV + col, d);
+    wave_sums<WC>(p);
+    float d[WC];
+#pragma unroll
+    for (int j = 0; j < WC; ++j) d[j] = vv[j] - p[j];
+    if (l == 0) gstore_cols<WC>(a.delta + ((size_t)tok * a.H + h) * DV + col, d);
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const float bk = b * kk[i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) S[i][j] = fmaf(bk, d[j], S[i][j]);
+      for (int j = 0; j < WC; ++j) S[i][j] = fmaf(bk, d[j], S[i][j]);
     }
   };
   // walk 2: the same step from the stored delta (elementwise: no sums over key channels,
   // and bitwise the state walk 1 had)
-  auto replay_step = [&](float (&S)[NR][4], const uint8_t* st, int u) {
+  auto replay_step = [&](float (&S)[NR][WC], const uint8_t* st, int u) {
     const float* rc = srec(st, u);
-    float ek[NR], kk[NR], d[4];
+    float ek[NR], kk[NR], d[WC];
     lds_read<NR>(rc + 2 * DK + r0, ek);
     lds_read<NR>(rc + DK + r0, kk);
     sv1(st, u, true, d);
@@ -321,18 +364,20 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
     for (int i = 0; i < NR; ++i) {
       const float bk = b * kk[i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) S[i][j] = fmaf(bk, d[j], S[i][j] * ek[i]);
+      for (int j = 0; j < WC; ++j) S[i][j] = fmaf(bk, d[j], S[i][j] * ek[i]);
     }
   };
 
   // 1. forward with a checkpoint at every segment start
   {
     uint4_v rg[M1::ROUNDS];
-    float S[NR][4];
+    float S[NR][WC];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-      if (a.h0) load4(a.h0 + sbase + (size_t)(r0 + i) * DV + col, S[i]);
-      else S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
+      if (a.h0) gload_cols<WC>(a.h0 + sbase + (size_t)(r0 + i) * DV + col, S[i]);
+      else
+#pragma unroll
+        for (int j = 0; j < WC; ++j) S[i][j] = 0.f;
     }
     if (nseg > 0) {
       stage_issue<DK, DV, InT, false>(rg, a, t0, seg_end(t0), h, c0);
@@ -356,16 +401,18 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
 
   // 2. backwards over the segments
   uint4_v rg[M2::ROUNDS];
-  float G[NR][4];
+  float G[NR][WC];
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
-    if (a.dht) load4(a.dht + sbase + (size_t)(r0 + i) * DV + col, G[i]);
-    else G[i][0] = G[i][1] = G[i][2] = G[i][3] = 0.f;
+    if (a.dht) gload_cols<WC>(a.dht + sbase + (size_t)(r0 + i) * DV + col, G[i]);
+    else
+#pragma unroll
+      for (int j = 0; j < WC; ++j) G[i][j] = 0.f;
   }
   InT* dvo = reinterpret_cast<InT*>(a.dv);
   const size_t pbase = (size_t)pidx * (size_t)a.T_total * a.H;
   int par = 0;
-  float ckn[NR][4];
+  float ckn[NR][WC];
   if (nseg > 0) {
     const int64_t ts = t0 + (nseg - 1) * kBwdSeg;
     stage_issue<DK, DV, InT, true>(rg, a, ts, seg_end(ts), h, c0);
@@ -379,11 +426,11 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
     const int len = (int)(seg_end(ts) - ts);
     if (k > 0) stage_issue<DK, DV, InT, true>(rg, a, ts - kBwdSeg, ts, h, c0);
     // St[u]: the state before token ts + u
-    float St[kBwdSeg][NR][4];
+    float St[kBwdSeg][NR][WC];
 #pragma unroll
     for (int i = 0; i < NR; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) St[0][i][j] = ckn[i][j];
+      for (int j = 0; j < WC; ++j) St[0][i][j] = ckn[i][j];
     if (k > 0) get(ck(k - 1), ckn);  // the previous segment's checkpoint, one segment ahead
     const uint8_t* st = stage[k & 1];
 #pragma unroll
@@ -392,17 +439,17 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < NR; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) St[u + 1][i][j] = St[u][i][j];
+          for (int j = 0; j < WC; ++j) St[u + 1][i][j] = St[u][i][j];
         replay_step(St[u + 1], st, u);
       }
     }
 #pragma unroll
     for (int u = kBwdSeg - 1; u >= 0; --u) {
       if (u >= len) continue;
-      float (&A)[NR][4] = St[u];  // S_{t-1}, then a
+      float (&A)[NR][WC] = St[u];  // S_{t-1}, then a
       const int64_t tok = ts + u;
       const float* rc = srec(st, u);
-      float ek[NR], kk[NR], qq[NR], d[4], dov[4];
+      float ek[NR], kk[NR], qq[NR], d[WC], dov[WC];
       lds_read<NR>(rc + 2 * DK + r0, ek);
       lds_read<NR>(rc + DK + r0, kk);
       lds_read<NR>(rc + r0, qq);
@@ -412,22 +459,24 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < NR; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) A[i][j] *= ek[i];
+        for (int j = 0; j < WC; ++j) A[i][j] *= ek[i];
       // G += scale qhat do^T, then u = G^T khat (column sums over the key channels)
-      float uu[4] = {0.f, 0.f, 0.f, 0.f};
+      float uu[WC];
+#pragma unroll
+      for (int j = 0; j < WC; ++j) uu[j] = 0.f;
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
         const float sq = a.scale * qq[i];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < WC; ++j) {
           G[i][j] = fmaf(sq, dov[j], G[i][j]);
           uu[j] = fmaf(kk[i], G[i][j], uu[j]);
         }
       }
-      wave_sum4(uu);
+      wave_sums<WC>(uu);
       float ddo = 0.f, db = 0.f;  // delta . do and u . delta over the wave's columns
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < WC; ++j) {
         ddo = fmaf(d[j], dov[j], ddo);
         db = fmaf(uu[j], d[j], db);
       }
@@ -437,7 +486,7 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
         float aq = 0.f, gd = 0.f, au = 0.f, ag = 0.f;
         const float bk = b * kk[i];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < WC; ++j) {
           aq = fmaf(A[i][j], dov[j], aq);
           gd = fmaf(G[i][j], d[j], gd);
           au = fmaf(A[i][j], uu[j], au);
@@ -454,8 +503,10 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
       if (l == 0) {
         pp[3 * DK] = db;
         // dv for the wave's columns (complete: no other wave or part touches them)
-        const float dvv[4] = {b * uu[0], b * uu[1], b * uu[2], b * uu[3]};
-        store4(dvo + th * DV + col, dvv);
+        float dvv[WC];
+#pragma unroll
+        for (int j = 0; j < WC; ++j) dvv[j] = b * uu[j];
+        gstore_cols<WC>(dvo + th * DV + col, dvv);
       }
       __syncthreads();
       // the waves' sums in a fixed order: this part's share of the row sums
@@ -475,7 +526,7 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
   }
   if (a.dh0) {
 #pragma unroll
-    for (int i = 0; i < NR; ++i) store4(a.dh0 + sbase + (size_t)(r0 + i) * DV + col, G[i]);
+    for (int i = 0; i < NR; ++i) gstore_cols<WC>(a.dh0 + sbase + (size_t)(r0 + i) * DV + col, G[i]);
   }
 }
 
