@@ -35,6 +35,11 @@ import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published (no sparsity)
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published (counts packed fp32 FMA)
+# fp32 operations per state element per (token, head) that the token-by-token backward must
+# do: one forward recompute (decay 1, prediction 2, correction 2) and the reverse step
+# (decay 1, G update 2, u 2, a.do 2, G.delta 2, a.u 2, da 2, a.da 2, G decay 1)
+BWD_FLOPS_PER_ELEM = 21
 TOL = 5e-3
 
 
@@ -113,7 +118,7 @@ def traffic_from_profiles(kernel):
 
 KERNEL_SOURCES = {"chunk_prep_kernel": ["kda_device.h", "kda_prep.h"],
                   "state_scan_kernel": ["kda_device.h", "kda_scan.h"],
-                  "fused_fwd_kernel": ["kda_device.h", "kda_prep.h", "kda_scan.h", "kda_kernels.hip"]}
+                  "fused_fwd_kernel": ["kda_device.h", "kda_prep.h", "kda_scan.h", "kda_fused.h"]}
 
 
 def takes_fused_path(x, torch):
@@ -244,13 +249,17 @@ def backward_measurement(kda, dev, torch, calls=3):
     # bytes every call must move: inputs (q, k, v bf16, g fp32, beta, dout) and gradients once, h0 and dh0
     # reads q, k, v, dout (bf16), g (fp32), beta; writes dq, dk, dv (bf16), dg (fp32), dbeta
     nbytes = B * T * H * (16 * dk + 6 * dv + 4) + 2 * H * dk * dv * 4
-    gbs = nbytes / (ms * 1e-3) / 1e9
+    flops = BWD_FLOPS_PER_ELEM * B * T * H * dk * dv
+    tflops = flops / (ms * 1e-3) / 1e12
     log("backward %s: %.3f ms/call, parity (B=1 T=200 H=4) %s" % (x.name, ms, errs))
     return {"ok": good, "workload": "backward of %s (B=1 T=8192 H=32 d=128 bf16)" % x.name,
             "ms_per_call": round(ms, 3), "tokens_per_s": round(B * T / (ms * 1e-3), 1) if good else None,
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 5), "bytes_per_call": int(nbytes),
-                         "note": "token by token: bound by the per-token latency of each (sequence, head) walk"},
+            "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
+                         "flops_per_call": int(flops), "bytes_per_call": int(nbytes),
+                         "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+                         "note": "token by token (fp32 vector work on the state, %d flops per element and "
+                                 "token); the walks issue one VALU stream per wave" % BWD_FLOPS_PER_ELEM},
             "parity_small": errs}
 
 

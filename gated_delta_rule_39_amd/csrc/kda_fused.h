@@ -1,0 +1,27 @@
+// The fused forward kernel (fixed-length batches whose state-scan chains leave most of
+// the compute units free): both roles of the two-kernel path in one launch, handing each
+// chunk's record over through device-scope flags (kda_prep.h: chunk_walk; kda_scan.h:
+// scan_chain).
+#pragma once
+
+#include "kda_prep.h"
+#include "kda_scan.h"
+
+namespace kda {
+
+// Fused forward: workgroups 0 .. producers-1 walk the chunks (in the order the scan
+// consumes them) and publish each record; the others each walk one (row, head, 64-column
+// slice) chain, waiting for each record before loading it.  The chunk workgroups never
+// wait on anything, and they have the lower block ids, so they are dispatched first.
+template <int DK, int DV, typename InT>
+__global__ __launch_bounds__(kPrepThreads, 1) void fused_fwd_kernel(PrepArgs pa, ScanArgs sa, FuseArgs fz) {
+  static_assert(kPrepThreads == kScanThreads, "one block size for both roles");
+  extern __shared__ __align__(16) uint8_t smem[];
+  if ((int)blockIdx.x < fz.producers)
+    chunk_walk<DK, DV, InT, true>(pa, fz, (int)blockIdx.x, fz.producers, smem);
+  else
+    scan_chain<DK, DV, 64, InT, true>(sa, fz, (int64_t)blockIdx.x - fz.producers,
+                                      (int64_t)gridDim.x - fz.producers, smem);
+}
+
+}  // namespace kda

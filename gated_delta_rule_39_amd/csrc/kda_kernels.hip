@@ -3,6 +3,7 @@
 #include "kda_chunkmap.h"
 #include "kda_prep.h"
 #include "kda_scan.h"
+#include "kda_fused.h"
 #include "kda_recurrent.h"
 #include "kda_recurrent_bwd.h"
 
@@ -62,21 +63,6 @@ static hipError_t launch_scan(const ForwardPlan& p, hipStream_t stream) {
     case 32: return launch_scan_nv<DK, DV, 32, OutT>(p, stream);
     default: return launch_scan_nv<DK, DV, 64, OutT>(p, stream);
   }
-}
-
-// Fused forward: workgroups 0 .. producers-1 walk the chunks (in the order the scan
-// consumes them) and publish each record; the others each walk one (row, head, 64-column
-// slice) chain, waiting for each record before loading it.  The chunk workgroups never
-// wait on anything, and they have the lower block ids, so they are dispatched first.
-template <int DK, int DV, typename InT>
-__global__ __launch_bounds__(kPrepThreads, 1) void fused_fwd_kernel(PrepArgs pa, ScanArgs sa, FuseArgs fz) {
-  static_assert(kPrepThreads == kScanThreads, "one block size for both roles");
-  extern __shared__ __align__(16) uint8_t smem[];
-  if ((int)blockIdx.x < fz.producers)
-    chunk_walk<DK, DV, InT, true>(pa, fz, (int)blockIdx.x, fz.producers, smem);
-  else
-    scan_chain<DK, DV, 64, InT, true>(sa, fz, (int64_t)blockIdx.x - fz.producers,
-                                      (int64_t)gridDim.x - fz.producers, smem);
 }
 
 static PrepArgs prep_args(const ForwardPlan& p) {
