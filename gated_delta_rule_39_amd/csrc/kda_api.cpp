@@ -297,9 +297,9 @@ kda_status_t kda_decode(const kda_problem_t* prob, const void* q, const void* k,
 
 // Backward workspace: chunk map (packed), the pre-pass records (unit q and k, exp(g), beta),
 // checkpoints of the state at every 8-token segment start, every token's delta, and each
-// column part's partial row sums (dqhat, dkhat, dg, dbeta).
+// column part's row sums (dqhat, dkhat, dg, dbeta).
 struct BwdCarve {
-  size_t info, table, seq_off, seq_order, rec, ckpt, delta, dqh_p, dkh_p, dg_p, dbeta_p, total;
+  size_t info, table, seq_off, seq_order, rec, ckpt, delta, psum, total;
 };
 
 static BwdCarve bwd_carve(const kda_problem_t* p, int64_t N, int64_t n_chunk_ub) {
@@ -315,11 +315,8 @@ static BwdCarve bwd_carve(const kda_problem_t* p, int64_t N, int64_t n_chunk_ub)
   c.ckpt = c.rec + align256(rows * (3 * (size_t)p->dk + 4) * 4);
   // every sequence of L tokens owns 8 slots per 64-token chunk, ceil(L / 8) <= 8 ceil(L / 64)
   c.delta = c.ckpt + align256((size_t)n_chunk_ub * 8 * p->heads * state);
-  c.dqh_p = c.delta + align256(rows * p->dv * 4);
-  c.dkh_p = c.dqh_p + align256(parts * rows * p->dk * 4);
-  c.dg_p = c.dkh_p + align256(parts * rows * p->dk * 4);
-  c.dbeta_p = c.dg_p + align256(parts * rows * p->dk * 4);
-  c.total = c.dbeta_p + align256(parts * rows * 4);
+  c.psum = c.delta + align256(rows * p->dv * 4);
+  c.total = c.psum + align256(parts * rows * (3 * (size_t)p->dk + 4) * 4);
   return c;
 }
 
@@ -385,10 +382,7 @@ kda_status_t kda_bwd(const kda_problem_t* prob, const void* q, const void* k, co
   p.rec = reinterpret_cast<float*>(ws + c.rec);
   p.ckpt = reinterpret_cast<float*>(ws + c.ckpt);
   p.delta = reinterpret_cast<float*>(ws + c.delta);
-  p.dqh_p = reinterpret_cast<float*>(ws + c.dqh_p);
-  p.dkh_p = reinterpret_cast<float*>(ws + c.dkh_p);
-  p.dg_p = reinterpret_cast<float*>(ws + c.dg_p);
-  p.dbeta_p = reinterpret_cast<float*>(ws + c.dbeta_p);
+  p.psum = reinterpret_cast<float*>(ws + c.psum);
   hipError_t e = kda::launch_backward(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -186,7 +186,7 @@ static hipError_t launch_backward_t(const BackwardPlan& p, hipStream_t stream) {
   a.seq_off = p.cu ? p.seq_off : nullptr;
   a.seq_order = p.cu ? p.seq_order : nullptr;
   a.dout = p.dout; a.dht = p.dht;
-  a.dqh_p = p.dqh_p; a.dkh_p = p.dkh_p; a.dg_p = p.dg_p; a.dbeta_p = p.dbeta_p;
+  a.psum = p.psum;
   a.dv = p.dv_; a.dh0 = p.dh0; a.ckpt = p.ckpt; a.delta = p.delta;
   a.T = p.T; a.T_total = p.T_total; a.N = p.N; a.nc = p.cu ? 0 : (p.T + kChunk - 1) / kChunk;
   a.n_chunk_ub = p.n_chunk_ub;
@@ -197,8 +197,8 @@ static hipError_t launch_backward_t(const BackwardPlan& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || rows == 0) return e;
   auto fin = bwd_finish_kernel<DK, InT>;
-  hipLaunchKernelGGL(fin, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p.q, p.k, p.dqh_p, p.dkh_p,
-                     p.dg_p, p.dbeta_p, parts, rows, p.dq, p.dk_, p.dg, p.dbeta);
+  hipLaunchKernelGGL(fin, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p.q, p.k, p.psum, parts, rows,
+                     p.dq, p.dk_, p.dg, p.dbeta);
   return hipGetLastError();
 }
 

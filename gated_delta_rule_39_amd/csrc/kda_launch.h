@@ -57,7 +57,7 @@ struct BackwardPlan {
   float* rec;                                             // per (token, head): qhat, khat, exp(g), beta
   float* ckpt;                                            // state checkpoints every 8 tokens
   float* delta;                                           // v - a^T khat of every token
-  float* dqh_p; float* dkh_p; float* dg_p; float* dbeta_p;  // per-part row sums
+  float* psum;                                            // per-part row sums
 };
 
 hipError_t launch_backward(const BackwardPlan& p, hipStream_t stream);

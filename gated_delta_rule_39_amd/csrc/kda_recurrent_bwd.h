@@ -63,10 +63,8 @@ struct BwdArgs {
   const int32_t* seq_order; // packed: sequences longest first (chunk map), or NULL
   const void* dout;
   const float* dht;
-  float* dqh_p;           // [parts, tokens * H, DK] fp32 partial dL/dqhat of each part
-  float* dkh_p;           // [parts, tokens * H, DK] fp32 partial dL/dkhat
-  float* dg_p;            // [parts, tokens * H, DK] fp32 partial dL/dg
-  float* dbeta_p;         // [parts, tokens * H] fp32 partial dL/dbeta
+  float* psum;            // [parts, tokens * H, 3 DK + 4] fp32: each part's row sums
+                          // [dL/dqhat | dL/dkhat | dL/dg | dL/dbeta, 0, 0, 0]
   void* dv;               // [tokens, H, DV] io dtype
   float* dh0;             // [N, H, DK, DV] or NULL
   float* ckpt;            // [slots, H, parts, waves, 64 lanes, NR, 4] fp32
@@ -509,15 +507,13 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
         gstore_cols<WC>(dvo + th * DV + col, dvv);
       }
       __syncthreads();
-      // the waves' sums in a fixed order: this part's share of the row sums
+      // the waves' sums in a fixed order: this part's share of the row sums, one
+      // contiguous row per (token, head)
       for (int idx = tid; idx < 3 * DK + 1; idx += kBwdThreads) {
         float acc = 0.f;
 #pragma unroll
         for (int ww = 0; ww < kBwdWaves; ++ww) acc += part[par][ww][idx];
-        if (idx < DK) a.dqh_p[(pbase + th) * DK + idx] = acc;
-        else if (idx < 2 * DK) a.dkh_p[(pbase + th) * DK + idx - DK] = acc;
-        else if (idx < 3 * DK) a.dg_p[(pbase + th) * DK + idx - 2 * DK] = acc;
-        else a.dbeta_p[pbase + th] = acc;
+        a.psum[(pbase + th) * (3 * DK + 4) + idx] = acc;
       }
       par ^= 1;  // the other buffer is written next: one barrier per token suffices
     }
@@ -568,49 +564,45 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* qv, const voi
   }
 }
 
-// Finish: the parts' partial sums added in a fixed order (dg and dbeta written), then dq,
-// dk from dqhat, dkhat through the L2 normalisation: dx = (dxhat - xhat (xhat . dxhat)) / |x|
+// Finish: the parts' row sums added in a fixed order (dg and dbeta written), then dq, dk
+// from dqhat, dkhat through the L2 normalisation: dx = (dxhat - xhat (xhat . dxhat)) / |x|
 // (0 for a zero vector), one wave per (token, head), the norm taken after the same exact
 // power-of-two rescale as in the forward kernels.
 template <int DK, typename InT>
-__global__ __launch_bounds__(256) void bwd_finish_kernel(const void* qv, const void* kv, const float* dqh_p,
-                                                         const float* dkh_p, const float* dg_p,
-                                                         const float* dbeta_p, int parts, int64_t rows,
-                                                         void* dqv, void* dkv, float* dg, void* dbeta) {
+__global__ __launch_bounds__(256) void bwd_finish_kernel(const void* qv, const void* kv, const float* psum,
+                                                         int parts, int64_t rows, void* dqv, void* dkv,
+                                                         float* dg, void* dbeta) {
   constexpr int PL = DK / 64;  // channels per lane
+  constexpr int PR = 3 * DK + 4;
   const int l = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;  // whole waves, no barrier
-  const size_t stride = (size_t)rows * DK;  // one part's share
-  {
-    float acc[PL];
+  float sq[PL], sk[PL], sg[PL], sb = 0.f;
 #pragma unroll
-    for (int c = 0; c < PL; ++c) acc[c] = 0.f;
-    for (int p = 0; p < parts; ++p)
+  for (int c = 0; c < PL; ++c) sq[c] = sk[c] = sg[c] = 0.f;
+  for (int p = 0; p < parts; ++p) {
+    const float* r = psum + ((size_t)p * rows + row) * PR + l * PL;
 #pragma unroll
-      for (int c = 0; c < PL; ++c) acc[c] += dg_p[p * stride + row * DK + l * PL + c];
-#pragma unroll
-    for (int c = 0; c < PL; ++c) dg[row * DK + l * PL + c] = acc[c];
-    if (l == 0) {
-      float db = 0.f;
-      for (int p = 0; p < parts; ++p) db += dbeta_p[(size_t)p * rows + row];
-      store1(reinterpret_cast<InT*>(dbeta) + row, db);
+    for (int c = 0; c < PL; ++c) {
+      sq[c] += r[c];
+      sk[c] += r[DK + c];
+      sg[c] += r[2 * DK + c];
     }
+    if (l == 0) sb += psum[((size_t)p * rows + row) * PR + 3 * DK];
   }
+#pragma unroll
+  for (int c = 0; c < PL; ++c) dg[row * DK + l * PL + c] = sg[c];
+  if (l == 0) store1(reinterpret_cast<InT*>(dbeta) + row, sb);
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
     const InT* x = reinterpret_cast<const InT*>(which ? kv : qv) + row * DK + l * PL;
-    const float* dxp = (which ? dkh_p : dqh_p) + row * DK + l * PL;
     InT* dx = reinterpret_cast<InT*>(which ? dkv : dqv) + row * DK + l * PL;
     float xv[PL], dh[PL];
 #pragma unroll
     for (int c = 0; c < PL; ++c) {
       xv[c] = load1(x + c);
-      dh[c] = 0.f;
+      dh[c] = which ? sk[c] : sq[c];
     }
-    for (int p = 0; p < parts; ++p)
-#pragma unroll
-      for (int c = 0; c < PL; ++c) dh[c] += dxp[p * stride + c];
     float m = 0.f;
 #pragma unroll
     for (int c = 0; c < PL; ++c) m = fmaxf(m, fabsf(xv[c]));
