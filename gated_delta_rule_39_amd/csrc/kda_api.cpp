@@ -131,7 +131,7 @@ uint64_t next_epoch() {
 
 extern "C" {
 
-int kda_version(void) { return 103; }
+int kda_version(void) { return 104; }
 
 const char* kda_status_string(kda_status_t s) {
   switch (s) {
