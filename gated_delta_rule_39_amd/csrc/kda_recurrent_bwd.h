@@ -27,10 +27,12 @@
 //
 // The walk, per part:
 //   1. forward over the sequence, storing the part's state at the start of every
-//      8-token segment (checkpoints, fp32, in the workspace);
+//      8-token segment (checkpoints, fp32, in the workspace) and every token's delta for
+//      the part's columns;
 //   2. backwards over the segments: the segment's forward is replayed from its
-//      checkpoint into registers (the state before each of its tokens), then its
-//      tokens are walked in reverse.
+//      checkpoint into registers with the stored deltas (elementwise, no sums: the state
+//      before each of its tokens, bitwise walk 1's), then its tokens are walked in
+//      reverse.
 // A pre-pass packs, per (token, head), [qhat | khat | exp(g) | beta] into one fp32 record.
 // Each 8-token segment's records and the part's columns of v (walk 1) or of the stored
 // deltas and dout (walk 2) are staged in LDS, the next segment's loads in flight while the
