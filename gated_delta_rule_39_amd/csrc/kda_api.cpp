@@ -302,9 +302,15 @@ struct BwdCarve {
   size_t info, table, seq_off, seq_order, rec, ckpt, delta, psum, total;
 };
 
+// Value columns per wave of the backward walk: 4 once 32-column parts give every compute
+// unit a workgroup (less work per column), else 2 (16-column parts, twice the workgroups).
+static int bwd_wcols(const kda_problem_t* p, int64_t N) {
+  return N * (int64_t)p->heads * (p->dv / 32) >= compute_units() ? 4 : 2;
+}
+
 static BwdCarve bwd_carve(const kda_problem_t* p, int64_t N, int64_t n_chunk_ub) {
   BwdCarve c;
-  const size_t parts = (size_t)kda::backward_parts(p->dv);
+  const size_t parts = (size_t)kda::backward_parts(p->dv, bwd_wcols(p, N));
   const size_t state = (size_t)p->dk * p->dv * 4;
   const size_t rows = (size_t)(p->batch * p->seqlen) * p->heads;
   c.info = 0;
@@ -383,6 +389,7 @@ kda_status_t kda_bwd(const kda_problem_t* prob, const void* q, const void* k, co
   p.ckpt = reinterpret_cast<float*>(ws + c.ckpt);
   p.delta = reinterpret_cast<float*>(ws + c.delta);
   p.psum = reinterpret_cast<float*>(ws + c.psum);
+  p.wcols = bwd_wcols(prob, N);
   hipError_t e = kda::launch_backward(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -191,8 +191,8 @@ static hipError_t launch_backward_t(const BackwardPlan& p, hipStream_t stream) {
   a.T = p.T; a.T_total = p.T_total; a.N = p.N; a.nc = p.cu ? 0 : (p.T + kChunk - 1) / kChunk;
   a.n_chunk_ub = p.n_chunk_ub;
   a.H = p.H; a.scale = p.scale;
-  constexpr int parts = DV / kBwdPartCols;
-  auto kern = recurrent_bwd_kernel<DK, DV, InT>;
+  const int parts = backward_parts(DV, p.wcols);
+  auto kern = p.wcols == 4 ? recurrent_bwd_kernel<DK, DV, InT, 4> : recurrent_bwd_kernel<DK, DV, InT, 2>;
   hipLaunchKernelGGL(kern, dim3((unsigned)(p.N * p.H * parts)), dim3(kBwdThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || rows == 0) return e;
@@ -207,7 +207,7 @@ static hipError_t launch_backward_dt(const BackwardPlan& p, hipStream_t stream) 
   return p.dtype == 0 ? launch_backward_t<DK, DV, uint16_t>(p, stream) : launch_backward_t<DK, DV, float>(p, stream);
 }
 
-int backward_parts(int dv) { return dv / kBwdPartCols; }
+int backward_parts(int dv, int wcols) { return dv / (kBwdWaves * wcols); }
 
 hipError_t launch_backward(const BackwardPlan& p, hipStream_t stream) {
   if (p.N <= 0) return hipSuccess;

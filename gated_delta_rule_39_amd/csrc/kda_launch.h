@@ -58,13 +58,15 @@ struct BackwardPlan {
   float* ckpt;                                            // state checkpoints every 8 tokens
   float* delta;                                           // v - a^T khat of every token
   float* psum;                                            // per-part row sums
+  int32_t wcols;                                          // value columns per wave (2 or 4)
 };
 
 hipError_t launch_backward(const BackwardPlan& p, hipStream_t stream);
 
-// Workgroups of the backward kernel per (sequence, head): the value columns are cut into
-// this many parts, each with its own partial row sums in the workspace.
-int backward_parts(int dv);
+// Workgroups of the backward kernel per (sequence, head) at `wcols` (2 or 4) value columns
+// per wave: the value columns are cut into this many parts, each with its own row sums in
+// the workspace.
+int backward_parts(int dv, int wcols);
 
 // Enqueue the token-by-token recurrent kernel on `stream` (uses the sizes, tensors and
 // scale of `p`; no workspace).

@@ -16,10 +16,12 @@
 // the L2 normalisation (finish kernel).
 //
 // Work split.  The value columns of the state evolve independently (a step mixes
-// key channels only), so each (sequence, head) is cut into parts of 16 value
-// columns, one workgroup per part, and each of its eight waves owns 2 columns: lane
-// l holds key channels l*NR .. l*NR + NR - 1 (NR = dk / 64) of those 2 columns, so
-// a lane carries 4 state elements (dk = 128) and a step is short.  Sums over key
+// key channels only), so each (sequence, head) is cut into parts of 16 (or 32) value
+// columns, one workgroup per part, and each of its eight waves owns WC = 2 (or 4)
+// columns: lane l holds key channels l*NR .. l*NR + NR - 1 (NR = dk / 64) of those
+// columns, so a lane carries 4 (or 8) state elements (dk = 128) and a step is short.
+// Narrow parts give a few (sequence, head) pairs enough workgroups to fill the chip;
+// wide ones do less work per column once there are workgroups enough.  Sums over key
 // channels (per column) are wave sums; the per-row sums dqhat, dkhat, dg and the
 // scalar dbeta add the eight waves' columns through LDS in a fixed order, and the
 // parts' partial sums are added (again in a fixed order) by the finish kernel:
@@ -44,8 +46,8 @@
 namespace kda {
 
 constexpr int kBwdWaves = 8;                              // waves per workgroup
-constexpr int kBwdWaveCols = 2;                           // value columns per wave (2 or 4)
-constexpr int kBwdPartCols = kBwdWaves * kBwdWaveCols;    // value columns per workgroup
+// value columns per wave: 2 or 4 (a template parameter of the kernel, chosen per call), so a
+// workgroup (a part) owns kBwdWaves * 2 or * 4 value columns
 constexpr int kBwdSeg = 8;                                // tokens per checkpoint segment
 constexpr int kBwdThreads = 64 * kBwdWaves;
 
@@ -102,11 +104,11 @@ __device__ inline float wave_sum(float x) {
 // V1 = the part's columns of v (walk 1, io dtype) or of the deltas (walk 2, fp32),
 // V2 = the part's columns of dout (walk 2 only, io dtype).  Slot s of the staging loads
 // is unit s.
-template <int DK, typename InT, bool WALK2>
+template <int DK, typename InT, bool WALK2, int PC>
 struct BwdStageMap {
-  static constexpr int AR = BwdRec<DK>::U4;                                 // units per record
-  static constexpr int V1 = kBwdPartCols * (WALK2 ? 4 : (int)sizeof(InT)) / 16;  // units per V1 row
-  static constexpr int V2 = WALK2 ? kBwdPartCols * (int)sizeof(InT) / 16 : 0;     // units per V2 row
+  static constexpr int AR = BwdRec<DK>::U4;                               // units per record
+  static constexpr int V1 = PC * (WALK2 ? 4 : (int)sizeof(InT)) / 16;    // units per V1 row
+  static constexpr int V2 = WALK2 ? PC * (int)sizeof(InT) / 16 : 0;      // units per V2 row
   static constexpr int UNITS = kBwdSeg * (AR + V1 + V2);
   static constexpr int ROUNDS = (UNITS + kBwdThreads - 1) / kBwdThreads;
 };
@@ -117,9 +119,9 @@ constexpr int kBwdStageBytes = 16 * kBwdSeg * (BwdRec<DK>::U4 + 8 + 8);  // the 
 // columns from c0.  Every slot is one unconditional 16-byte load whose address is chosen
 // first, so no value merge waits on a load and the loads stay in flight until the commit
 // (slots past te read token te - 1 and are never used).
-template <int DK, int DV, typename InT, bool WALK2, int R>
+template <int DK, int DV, typename InT, bool WALK2, int PC, int R>
 __device__ inline void stage_issue(uint4_v (&r)[R], const BwdArgs& a, int64_t ts, int64_t te, int h, int c0) {
-  using M = BwdStageMap<DK, InT, WALK2>;
+  using M = BwdStageMap<DK, InT, WALK2, PC>;
   static_assert(R == M::ROUNDS, "staging registers");
   const uint8_t* rec = reinterpret_cast<const uint8_t*>(a.rec);
   const uint8_t* v1 = WALK2 ? reinterpret_cast<const uint8_t*>(a.delta) : reinterpret_cast<const uint8_t*>(a.v);
@@ -147,9 +149,9 @@ __device__ inline void stage_issue(uint4_v (&r)[R], const BwdArgs& a, int64_t ts
   }
 }
 
-template <int DK, typename InT, bool WALK2, int R>
+template <int DK, typename InT, bool WALK2, int PC, int R>
 __device__ inline void stage_commit(const uint4_v (&r)[R], uint8_t* st) {
-  using M = BwdStageMap<DK, InT, WALK2>;
+  using M = BwdStageMap<DK, InT, WALK2, PC>;
   static_assert(R == M::ROUNDS, "staging registers");
 #pragma unroll
   for (int rd = 0; rd < M::ROUNDS; ++rd) {
@@ -253,17 +255,18 @@ __device__ inline void wave_sums(float (&x)[N]) {
   for (int j = 0; j < N; ++j) x[j] = __uint_as_float(y[j][0]) + __uint_as_float(y[j][1]);
 }
 
-template <int DK, int DV, typename InT>
+template <int DK, int DV, typename InT, int WC>
 __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
+  static_assert(WC == 2 || WC == 4, "2 or 4 value columns per wave");
   constexpr int NR = DK / 64;                  // key channels per lane
-  constexpr int PARTS = DV / kBwdPartCols;     // workgroups per (sequence, head)
-  constexpr int WC = kBwdWaveCols;             // value columns per wave
+  constexpr int PC = kBwdWaves * WC;           // value columns per workgroup (part)
+  constexpr int PARTS = DV / PC;               // workgroups per (sequence, head)
   constexpr int CK = 64 * NR * WC;             // floats of one wave's share of a checkpoint
   constexpr bool BF = sizeof(InT) == 2;
-  using M1 = BwdStageMap<DK, InT, false>;
-  using M2 = BwdStageMap<DK, InT, true>;
+  using M1 = BwdStageMap<DK, InT, false, PC>;
+  using M2 = BwdStageMap<DK, InT, true, PC>;
   constexpr int RF = BwdRec<DK>::FLOATS;
-  static_assert(DV % kBwdPartCols == 0 && DK % 64 == 0, "unsupported head dimensions");
+  static_assert(DV % PC == 0 && DK % 64 == 0, "unsupported head dimensions");
   __shared__ __align__(16) uint8_t stage[2][kBwdStageBytes<DK>];
   // per token parity and wave: the wave's row sums [dqhat | dkhat | dg] and dbeta
   __shared__ float part[2][kBwdWaves][3 * DK + 1];
@@ -271,12 +274,12 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
   const int l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r0 = l * NR;            // first key channel of the lane
-  const int wc = w * kBwdWaveCols;  // first column of the wave inside the part
+  const int wc = w * WC;            // first column of the wave inside the part
   const int pidx = (int)(blockIdx.x % PARTS);
   const int64_t nh = blockIdx.x / PARTS;
   const int h = (int)(nh % a.H);
   const int64_t n = a.cu ? (int64_t)a.seq_order[nh / a.H] : nh / a.H;
-  const int c0 = pidx * kBwdPartCols;  // first column of the part
+  const int c0 = pidx * PC;            // first column of the part
   const int col = c0 + wc;             // first column of the wave
 
   int64_t t0 = n * a.T, t1 = t0 + a.T, slot0 = n * a.nc * (kChunk / kBwdSeg);
@@ -380,21 +383,21 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
         for (int j = 0; j < WC; ++j) S[i][j] = 0.f;
     }
     if (nseg > 0) {
-      stage_issue<DK, DV, InT, false>(rg, a, t0, seg_end(t0), h, c0);
-      stage_commit<DK, InT, false>(rg, stage[0]);
+      stage_issue<DK, DV, InT, false, PC>(rg, a, t0, seg_end(t0), h, c0);
+      stage_commit<DK, InT, false, PC>(rg, stage[0]);
     }
     wait_vm_loads();
     __syncthreads();
     for (int64_t k = 0; k < nseg; ++k) {
       const int64_t ts = t0 + k * kBwdSeg;
       const int len = (int)(seg_end(ts) - ts);
-      if (k + 1 < nseg) stage_issue<DK, DV, InT, false>(rg, a, ts + kBwdSeg, seg_end(ts + kBwdSeg), h, c0);
+      if (k + 1 < nseg) stage_issue<DK, DV, InT, false, PC>(rg, a, ts + kBwdSeg, seg_end(ts + kBwdSeg), h, c0);
       put(ck(k), S);
       const uint8_t* st = stage[k & 1];
 #pragma unroll
       for (int u = 0; u < kBwdSeg; ++u)
         if (u < len) fwd_step(S, st, u, ts + u);
-      if (k + 1 < nseg) stage_commit<DK, InT, false>(rg, stage[(k + 1) & 1]);
+      if (k + 1 < nseg) stage_commit<DK, InT, false, PC>(rg, stage[(k + 1) & 1]);
       __syncthreads();  // also orders walk 1's delta and checkpoint stores before walk 2 reads them
     }
   }
@@ -415,8 +418,8 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
   float ckn[NR][WC];
   if (nseg > 0) {
     const int64_t ts = t0 + (nseg - 1) * kBwdSeg;
-    stage_issue<DK, DV, InT, true>(rg, a, ts, seg_end(ts), h, c0);
-    stage_commit<DK, InT, true>(rg, stage[(nseg - 1) & 1]);
+    stage_issue<DK, DV, InT, true, PC>(rg, a, ts, seg_end(ts), h, c0);
+    stage_commit<DK, InT, true, PC>(rg, stage[(nseg - 1) & 1]);
     get(ck(nseg - 1), ckn);
   }
   wait_vm_loads();
@@ -424,7 +427,7 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
   for (int64_t k = nseg - 1; k >= 0; --k) {
     const int64_t ts = t0 + k * kBwdSeg;
     const int len = (int)(seg_end(ts) - ts);
-    if (k > 0) stage_issue<DK, DV, InT, true>(rg, a, ts - kBwdSeg, ts, h, c0);
+    if (k > 0) stage_issue<DK, DV, InT, true, PC>(rg, a, ts - kBwdSeg, ts, h, c0);
     // St[u]: the state before token ts + u
     float St[kBwdSeg][NR][WC];
 #pragma unroll
@@ -519,7 +522,7 @@ __global__ __launch_bounds__(kBwdThreads) void recurrent_bwd_kernel(BwdArgs a) {
       }
       par ^= 1;  // the other buffer is written next: one barrier per token suffices
     }
-    if (k > 0) stage_commit<DK, InT, true>(rg, stage[(k - 1) & 1]);
+    if (k > 0) stage_commit<DK, InT, true, PC>(rg, stage[(k - 1) & 1]);
     __syncthreads();
   }
   if (a.dh0) {

@@ -201,12 +201,12 @@ kda_status_t kda_decode(const kda_problem_t* prob, const void* q, const void* k,
  *   workspace   >= kda_bwd_workspace_size(prob) bytes of device scratch
  *
  * The walk is token by token per (sequence, head), fp32 throughout, with the state's
- * value columns split over workgroups of 16 columns (2 per wave); a first walk stores the
- * state every 8 tokens and each token's delta, and the reverse walk replays each 8-token
- * segment from them.  The workspace holds those checkpoints (dk * dv * 4 bytes per 8
- * tokens and head), per (token, head) records of unit q and k, exp(g) and beta, the
- * deltas and each part's partial row sums: about 5.9 GB for 8,192 tokens of 32 heads at
- * dk = dv = 128.
+ * value columns split over workgroups of 16 columns (2 per wave), or 32 (4 per wave) once
+ * N * H * dv / 32 reaches the number of compute units; a first walk stores the state every
+ * 8 tokens and each token's delta, and the reverse walk replays each 8-token segment from
+ * them.  The workspace holds those checkpoints (dk * dv * 4 bytes per 8 tokens and head),
+ * per (token, head) records of unit q and k, exp(g) and beta, the deltas and each part's
+ * row sums: about 5.9 GB for 8,192 tokens of 32 heads at dk = dv = 128.
  * Conventions (stream, no allocation, errors, alignment) as for kda_fwd; outputs must
  * not overlap any input, the workspace or each other.  Results are deterministic.
  */

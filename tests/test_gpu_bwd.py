@@ -124,3 +124,19 @@ def test_bwd_deterministic():
     torch.cuda.synchronize()
     for a, b in zip(first, second):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_wide_parts(dtype):
+    # enough (sequence, head) pairs for 32-column parts (4 columns per wave) on every
+    # compute unit: B * H * dv / 32 = 512
+    x = make_inputs(64, 24, 2, 128, 128, seed=318, dtype=dtype)
+    _check(x, *_dout(x, 319), "bwd B=64 T=24 H=2 (wide parts) %s" % dtype)
+
+
+def test_bwd_wide_parts_packed():
+    rng = np.random.default_rng(320)
+    lens = rng.integers(0, 40, size=80)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    x = make_inputs(1, int(cu[-1]), 4, 128, 64, seed=321, dtype="bf16", cu_seqlens=cu)
+    _check(x, *_dout(x, 322), "bwd packed 80 sequences H=4 dv=64 (wide parts)")
