@@ -246,6 +246,24 @@ def backward_measurement(kda, dev, torch, calls=3):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / calls
+    # the two packed 8,192-token batches (their longest sequence walks its tokens in sequence)
+    varlen = {}
+    for i in (2, 3):
+        y2 = make_config(i)
+        cu = torch.from_numpy(np.ascontiguousarray(y2.cu_seqlens)).to(dev)
+        a2 = [t(y2.q, torch.bfloat16), t(y2.k, torch.bfloat16), t(y2.v, torch.bfloat16), t(y2.g, torch.float32),
+              t(y2.beta, torch.bfloat16), t(np.random.default_rng(14).standard_normal(y2.v.shape), torch.bfloat16),
+              t(y2.h0, torch.float32), cu, y2.scale]
+        kda.bwd(*a2)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(calls):
+            kda.bwd(*a2)
+        e1.record()
+        torch.cuda.synchronize()
+        ms2 = e0.elapsed_time(e1) / calls
+        varlen[y2.name] = {"ms_per_call": round(ms2, 3), "tokens_per_s": round(y2.shape[1] / (ms2 * 1e-3), 1),
+                           "sequences": int(y2.num_seqs), "longest": int(np.max(np.diff(y2.cu_seqlens)))}
     # bytes every call must move: inputs (q, k, v bf16, g fp32, beta, dout) and gradients once, h0 and dh0
     # reads q, k, v, dout (bf16), g (fp32), beta; writes dq, dk, dv (bf16), dg (fp32), dbeta
     nbytes = B * T * H * (16 * dk + 6 * dv + 4) + 2 * H * dk * dv * 4
@@ -260,7 +278,7 @@ def backward_measurement(kda, dev, torch, calls=3):
                          "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
                          "note": "token by token (fp32 vector work on the state, %d flops per element and "
                                  "token); the walks issue one VALU stream per wave" % BWD_FLOPS_PER_ELEM},
-            "parity_small": errs}
+            "parity_small": errs, "varlen": varlen}
 
 
 def decode_measurement(args, lib, kda, upload, dev, torch, B=256, verify=True):
@@ -360,7 +378,7 @@ def main():
                 "steps": max(1, min(args.steps, 5)), "warmup": 1, "ms_per_step": r["ms_per_call"],
                 "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
                 "data": "synthetic", "config": {"workload": r["workload"]}, "roofline": r["roofline"],
-                "parity_small": r["parity_small"]}
+                "parity_small": r["parity_small"], "varlen": r["varlen"]}
         print(json.dumps(line), flush=True)
         if not ok:
             sys.exit(1)
