@@ -140,3 +140,33 @@ def test_bwd_wide_parts_packed():
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     x = make_inputs(1, int(cu[-1]), 4, 128, 64, seed=321, dtype="bf16", cu_seqlens=cu)
     _check(x, *_dout(x, 322), "bwd packed 80 sequences H=4 dv=64 (wide parts)")
+
+
+def test_bwd_full_size_sampled_heads():
+    # the fixed 8,192-token batch of 32 heads, in the launch configuration bench.py times;
+    # two heads checked against the oracle (each head's backward is independent of the others)
+    import torch
+    import gated_delta_rule_39_amd.kda as kda
+    from workloads import make_config
+    x = make_config(1)
+    B, T, H, dk, dv = x.shape
+    do = round_bf16(np.random.default_rng(323).standard_normal(x.v.shape).astype(np.float32))
+    d = to_device(x)
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(dt)
+    outs = kda.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], t(do, torch.bfloat16), d["h0"], None, x.scale)
+    torch.cuda.synchronize()
+    got = [o.float().cpu().numpy().astype(np.float64) for o in outs]
+    for h in (3, 30):
+        sl = lambda a: np.ascontiguousarray(a[:, :, h:h + 1])
+        ref = oracle_bwd(sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta), sl(do), x.h0[:, h:h + 1], None,
+                         x.scale, None)
+        names = ["dq", "dk", "dv", "dg", "dbeta", "dh0"]
+        errs = {}
+        for n, a, r in zip(names, got, ref):
+            a_h = a[:, h:h + 1] if n == "dh0" else a[:, :, h:h + 1]
+            errs[n] = rel_rmse(a_h, r)
+        print("bwd full size, head %d: %s" % (h, " ".join("%s %.2e" % kv for kv in errs.items())), flush=True)
+        for n in ["dq", "dk", "dv", "dbeta"]:
+            assert errs[n] <= TOL, (h, n, errs[n])
+        for n in ["dg", "dh0"]:
+            assert errs[n] <= F32_TOL, (h, n, errs[n])
