@@ -55,7 +55,7 @@ Carve carve(const kda_problem_t* p, int64_t N, int64_t n_chunk_ub) {
   c.seq_order = c.seq_off + align256((size_t)(N + 1) * 4);
   c.defer = c.seq_order + align256((size_t)N * 4);
   c.flags = c.defer + align256((size_t)n_chunk_ub * (size_t)p->heads * 4);
-  c.rec = c.flags + align256((size_t)n_chunk_ub * (size_t)p->heads * 8);
+  c.rec = c.flags + align256((size_t)n_chunk_ub * (size_t)p->heads * 8 * 2);  // a flag per 64-column slice
   c.total = c.rec + (size_t)n_chunk_ub * (size_t)p->heads * kda::record_bytes(p->dk, p->dv);
   return c;
 }

@@ -171,13 +171,15 @@ __device__ __forceinline__ V rec_load(const uint8_t* rec, int bytes, size_t off)
 }
 
 // Hand-off between the two roles of the fused forward kernel: the chunk workgroups
-// publish each (chunk, head) record by writing `epoch` into its flag once the record's
-// stores have completed, the scan workgroups wait for the flag before loading the record.
-// Records and flags move only through device-scope (sc1) stores and loads, which are
-// coherent across the compute dies without L2 write-backs or invalidations.  A new epoch
-// per call means the flags never need clearing.
+// publish each (chunk, head) record by writing `epoch` into its flags (one per 64-column
+// scan slice) once the record's stores have completed, the scan workgroups wait for their
+// flag before loading the record.  Records and flags move only through device-scope (sc1)
+// stores and loads, which are coherent across the compute dies without L2 write-backs or
+// invalidations.  A new epoch per call keeps flags left by other calls (or uninitialised
+// workspace) from matching; each scan workgroup clears its flags when its chain is done, so
+// a replay of the same launch with the same epoch (a captured graph) also waits.
 struct FuseArgs {
-  uint64_t* flags;     // [chunk * H + head]
+  uint64_t* flags;     // [chunk * H + head][DV / 64]
   uint64_t epoch;
   int32_t producers;   // workgroups 0 .. producers-1 run the chunk walk, the rest the scan
   int32_t spin_limit;  // polls (about 130 cycles each) before a wait gives up

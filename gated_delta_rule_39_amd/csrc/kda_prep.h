@@ -997,13 +997,15 @@ __device__ __forceinline__ void chunk_walk(const PrepArgs& a, const FuseArgs& fz
     const int pos = x / a.H;
     return FUSED ? (pos % n_rows) * (int)a.nc + pos / n_rows : n_chunks - 1 - pos;
   };
-  // every wave's record stores (written through at device scope) complete, then the flag
-  // (a device-scope store)
+  // every wave's record stores (written through at device scope) complete, then the flags
+  // (device-scope stores), one per 64-column scan slice that reads the record
+  constexpr int NSF = DV / 64;
   auto publish = [&](int chunk, int h, bool ready) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (threadIdx.x == 0 && ready)
-      __hip_atomic_store(fz.flags + (size_t)chunk * a.H + h, fz.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int)threadIdx.x < NSF && ready)
+      __hip_atomic_store(fz.flags + ((size_t)chunk * a.H + h) * NSF + threadIdx.x, fz.epoch, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   };
   auto head_of = [&](int x) { return (x % a.H + x / a.H) % a.H; };
   // Where the chunks of this workgroup's first 64 items start and how many tokens they

@@ -262,12 +262,15 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
   // ends the wait, the walk then reads whatever the record holds).  The flag is read one
   // step ahead (`pre`), so a record that is already published costs no round trip.
   uint64_t pre = 0;
+  // the flag of chunk c for this slice (the chunk walk writes one per slice)
+  constexpr int NSF = DV / NV;
+  auto flag_of = [&](int64_t c) { return fz.flags + ((size_t)c * a.H + h) * NSF + slice; };
   auto prepoll = [&](int64_t c) {
-    if (FUSED && c < c1) pre = __hip_atomic_load(fz.flags + (size_t)c * a.H + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (FUSED && c < c1) pre = __hip_atomic_load(flag_of(c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   auto await_chunk = [&](int64_t c) {
     if (FUSED && c < c1) {
-      const uint64_t* fl = fz.flags + (size_t)c * a.H + h;
+      const uint64_t* fl = flag_of(c);
       int spins = 0;
       if (pre != fz.epoch) {
         while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != fz.epoch && spins < fz.spin_limit) {
@@ -473,6 +476,13 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
             a.ht[sbase + (size_t)row * DV + col0 + 16 * nt + t] = S[p][nt][r];
           }
     }
+  }
+  if (FUSED) {
+    // every wave is past its last wait: clear this slice's flags, so that a replay of the same
+    // launch (a captured graph keeps the call's epoch) waits for its own records
+    __syncthreads();
+    for (int64_t c = c0 + tid; c < c1; c += kScanThreads)
+      __hip_atomic_store(flag_of(c), (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

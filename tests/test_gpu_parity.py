@@ -184,3 +184,38 @@ def test_fused_deferred_items_on_long_walks(monkeypatch):
     monkeypatch.setenv("KDA_CHUNK_WGS", "3")
     x = make_inputs(1, 700, 4, 128, 128, seed=43, dtype="bf16", gate="deep")
     _check(x, "fused, deep gates, 3 chunk workgroups")
+
+
+def test_fused_forward_in_a_captured_graph():
+    # kda_fwd captured once and replayed with new inputs copied into the captured buffers:
+    # every replay must match an eager call on the same inputs (the fused kernel's flags
+    # carry the captured call's epoch, so each replay relies on the flags being cleared)
+    import torch
+    import gated_delta_rule_39_amd.kda as kda
+    xs = [make_inputs(1, 1000, 8, 128, 128, seed=500 + i, dtype="bf16") for i in range(3)]
+    bufs = to_device(xs[0])
+    ws = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")
+    out = torch.empty((1, 1000, 8, 128), dtype=torch.bfloat16, device="cuda")
+    ht = torch.empty((1, 8, 128, 128), dtype=torch.float32, device="cuda")
+    call = lambda: kda.fwd(bufs["q"], bufs["k"], bufs["v"], bufs["g"], bufs["beta"], bufs["h0"], None,
+                           xs[0].scale, out=out, ht=ht, workspace=ws)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for rep in range(6):
+        x = xs[rep % 3]
+        d = to_device(x)
+        for name in ("q", "k", "v", "g", "beta", "h0"):
+            bufs[name].copy_(d[name])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got_o, got_h = out.clone(), ht.clone()
+        ref_o, ref_h = kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], None, x.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(got_o, ref_o) and torch.equal(got_h, ref_h), rep
