@@ -31,7 +31,10 @@
  *     for them.  It keeps no pointer after that work completes, holds no
  *     global state beyond a process-wide call counter (atomic) and may be
  *     called from several host threads at once; two calls that run at the
- *     same time need separate workspaces.
+ *     same time need separate workspaces.  The enqueued work is safe to capture
+ *     in a HIP graph and replay (no memset nodes; the fused kernel's hand-off
+ *     flags are cleared by the kernel itself, so a replay with the captured
+ *     call's flag value still waits for its own records).
  *   - Results are deterministic: the same inputs on the same GPU and build
  *     give bitwise-equal out and ht.
  */
