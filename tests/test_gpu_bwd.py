@@ -170,3 +170,40 @@ def test_bwd_full_size_sampled_heads():
             assert errs[n] <= TOL, (h, n, errs[n])
         for n in ["dg", "dh0"]:
             assert errs[n] <= F32_TOL, (h, n, errs[n])
+
+
+def test_bwd_in_a_captured_graph():
+    # kda_bwd captured once, replayed with new inputs copied into the captured buffers;
+    # every replay bitwise equal to an eager call on the same inputs
+    import torch
+    import gated_delta_rule_39_amd.kda as kda
+    xs = [make_inputs(1, 300, 4, 128, 128, seed=330 + i, dtype="bf16") for i in range(2)]
+    dos = [round_bf16(np.random.default_rng(340 + i).standard_normal(xs[0].v.shape).astype(np.float32))
+           for i in range(2)]
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(dt)
+    bufs = to_device(xs[0])
+    bufs["do"] = t(dos[0], torch.bfloat16)
+    call = lambda: kda.bwd(bufs["q"], bufs["k"], bufs["v"], bufs["g"], bufs["beta"], bufs["do"], bufs["h0"],
+                           None, xs[0].scale)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = call()
+    for rep in range(4):
+        x, do = xs[rep % 2], dos[rep % 2]
+        d = to_device(x)
+        for name in ("q", "k", "v", "g", "beta", "h0"):
+            bufs[name].copy_(d[name])
+        bufs["do"].copy_(t(do, torch.bfloat16))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [o.clone() for o in outs]
+        ref = kda.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], t(do, torch.bfloat16), d["h0"], None, x.scale)
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), rep
