@@ -68,12 +68,38 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
   return a0 < b0 + bn && b0 < a0 + an;
 }
 
+// Compute units of the current device, queried once per device (a HIP attribute query
+// on every call cost host time on the launch path).
 int compute_units() {
-  int dev = 0, cus = 0;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];  // 0 = not yet queried
+  int dev = 0;
   hipGetDevice(&dev);
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
   hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  return cus > 0 ? cus : 256;
+  if (cus <= 0) cus = 256;
+  if (dev >= 0 && dev < kMaxDevices) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
+
+// Polls before a wait of the fused kernel gives up: KDA_SPIN_LIMIT=n (n >= 1) overrides the
+// default (several times the whole chunk walk), which the tests use to force the failure
+// path; 0 = default.
+int spin_limit_override() {
+  const char* env = std::getenv("KDA_SPIN_LIMIT");
+  if (!env) return 0;
+  const long v = std::atol(env);
+  return v >= 1 ? (int)(v < (1L << 30) ? v : (1L << 30)) : 0;
+}
+
+// Byte offset of the control words inside the workspace's info block (256 bytes: the chunk
+// map's counters come first): [0] flag value of the most recent launch, [1] flag value of a
+// launch whose wait gave up, [2] launch counter of captured fused calls.
+constexpr size_t kCtlOffset = 64;
 
 // Value columns per state-scan workgroup.  A workgroup's step costs about the same for
 // 16, 32 or 64 columns (it is bound by loading the chunk's factors), so the widest slice
@@ -143,6 +169,7 @@ const char* kda_status_string(kda_status_t s) {
     case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace smaller than kda_fwd_workspace_size()";
     case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: out or ht overlaps an input";
     case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP launch failed";
+    case KDA_ERR_TIMEOUT: return "KDA_ERR_TIMEOUT: a wait of the fused kernel gave up; its outputs hold NaN";
   }
   return "unknown kda_status_t";
 }
@@ -255,8 +282,16 @@ static kda_status_t forward(const kda_problem_t* prob, const void* q, const void
   p.rec = ws + c.rec;
   p.defer = reinterpret_cast<int32_t*>(ws + c.defer);
   p.flags = reinterpret_cast<uint64_t*>(ws + c.flags);
+  p.ctl = reinterpret_cast<uint64_t*>(ws + c.info + kCtlOffset);
   p.fuse_producers = fused_producers(prob, N, packed);
   p.epoch = p.fuse_producers > 0 ? next_epoch() : 0;
+  p.spin_limit = spin_limit_override();
+  p.captured = false;
+  if (p.fuse_producers > 0) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs) != hipSuccess) return KDA_ERR_HIP;
+    p.captured = cs == hipStreamCaptureStatusActive;
+  }
   p.slice = slice_width(prob, N);
   p.chunk_wgs = chunk_workgroups();
   for (int i = 0; i < 4; ++i) p.marks[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
@@ -269,6 +304,19 @@ kda_status_t kda_fwd(const kda_problem_t* prob, const void* q, const void* k, co
                      float* ht, void* workspace, size_t workspace_bytes, void* stream) {
   return forward(prob, q, k, v, g, beta, h0, cu_seqlens, scale, out, ht, workspace, workspace_bytes, stream,
                  nullptr);
+}
+
+kda_status_t kda_fwd_status(const void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return KDA_ERR_NULL;
+  if (misaligned(workspace)) return KDA_ERR_ALIGN;
+  if (workspace_bytes < 256) return KDA_ERR_WORKSPACE;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERR_HIP;
+  uint64_t ctl[2] = {0, 0};
+  if (hipMemcpy(ctl, static_cast<const uint8_t*>(workspace) + kCtlOffset, sizeof(ctl), hipMemcpyDeviceToHost) !=
+      hipSuccess)
+    return KDA_ERR_HIP;
+  // flag values are odd; the two-kernel path records 0 (it has no waits)
+  return ((ctl[0] & 1u) && ctl[1] == ctl[0]) ? KDA_ERR_TIMEOUT : KDA_OK;
 }
 
 kda_status_t kda_decode(const kda_problem_t* prob, const void* q, const void* k, const void* v,

@@ -32,7 +32,7 @@ __device__ inline f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
 
 __device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// 2^x on the hardware exp unit (x <= 0 everywhere it is used: results in [0, 1]).
+// 2^x on the hardware exp unit (x <= 126 everywhere it is used: finite results).
 __device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Shift a value D lanes up inside each row of 16 lanes; lanes with no source get 0.
@@ -143,7 +143,10 @@ struct Rec {
   static constexpr size_t LAM = U + 64 * DV * 2;
   // HDR: { float vmax (max |v| over the chunk), int ue (U scale exponent), pad, pad }
   static constexpr size_t HDR = LAM + DK * 4;
-  static constexpr size_t BYTES = (HDR + 16 + 255) / 256 * 256;
+  // EC: per key channel c, the exponent ec <= 0 by which row c of Khat*exp(G_last-G) is
+  // scaled (by 2^-ec) before its fp16 rounding, int8 [DK]
+  static constexpr size_t EC = HDR + 16;
+  static constexpr size_t BYTES = (EC + DK + 255) / 256 * 256;
 };
 
 // Raw buffer resources (record stores and loads of the fused kernel): dword 3 with a 32-bit
@@ -162,8 +165,11 @@ __device__ __forceinline__ V rec_load(const uint8_t* rec, int bytes, size_t off)
       return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 16));
     } else if constexpr (sizeof(V) == 8) {
       return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, 16));
-    } else {
+    } else if constexpr (sizeof(V) == 4) {
       return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, 16));
+    } else {
+      static_assert(sizeof(V) == 1, "record loads are 1, 4, 8 or 16 bytes");
+      return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b8(rs, (int)off, 0, 16));
     }
   } else {
     return *reinterpret_cast<const V*>(rec + off);
@@ -171,19 +177,48 @@ __device__ __forceinline__ V rec_load(const uint8_t* rec, int bytes, size_t off)
 }
 
 // Hand-off between the two roles of the fused forward kernel: the chunk workgroups
-// publish each (chunk, head) record by writing `epoch` into its flags (one per 64-column
-// scan slice) once the record's stores have completed, the scan workgroups wait for their
-// flag before loading the record.  Records and flags move only through device-scope (sc1)
-// stores and loads, which are coherent across the compute dies without L2 write-backs or
-// invalidations.  A new epoch per call keeps flags left by other calls (or uninitialised
-// workspace) from matching; each scan workgroup clears its flags when its chain is done, so
-// a replay of the same launch with the same epoch (a captured graph) also waits.
+// publish each (chunk, head) record by writing the launch's flag value into its flags (one
+// per 64-column scan slice) once the record's stores have completed, the scan workgroups
+// wait for their flag before loading the record.  Records and flags move only through
+// device-scope (sc1) stores and loads, which are coherent across the compute dies without
+// L2 write-backs or invalidations.
+//
+// Every launch has its own flag value, so flags left by earlier launches (or an
+// uninitialised workspace) never match and nothing needs clearing.  An eager call takes a
+// fresh value from a process-wide host counter.  A call captured into a graph would replay
+// the captured value, so there the value is derived on the device: a one-thread kernel
+// captured just before the fused kernel advances a counter in the workspace, and every
+// workgroup mixes the counter with the captured salt.
+//
+// Waits are bounded.  A wait that gives up marks the launch as failed: the workgroup
+// stores the launch's flag value into the workspace's error word (kda_fwd_status reports
+// it), writes NaN into the outputs it would have produced from that chunk on and into its
+// part of the final state, and stops waiting.  No index or address is ever derived from a
+// record's contents, so reading a record that is not complete is harmless.
 struct FuseArgs {
-  uint64_t* flags;     // [chunk * H + head][DV / 64]
-  uint64_t epoch;
-  int32_t producers;   // workgroups 0 .. producers-1 run the chunk walk, the rest the scan
-  int32_t spin_limit;  // polls (about 130 cycles each) before a wait gives up
+  uint64_t* flags;            // [chunk * H + head][DV / 64]
+  uint64_t epoch;             // eager call: the flag value; captured call: the salt
+  const uint64_t* dev_epoch;  // captured call: the counter advanced before each launch; else null
+  uint64_t* ctl;              // [0] flag value of the most recent launch, [1] value of a failed one
+  int32_t producers;          // workgroups 0 .. producers-1 run the chunk walk, the rest the scan
+  int32_t spin_limit;         // polls (about 130 cycles each) before a wait gives up
 };
+
+// The flag value of this launch (the same in every workgroup: the counter is written by
+// the kernel before it on the stream).  Always odd, so zeroed memory never matches.
+__device__ inline uint64_t launch_epoch(const FuseArgs& fz) {
+  if (!fz.dev_epoch) return fz.epoch;
+  const uint64_t d = __hip_atomic_load(fz.dev_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (d * 0x9E3779B97F4A7C15ull + fz.epoch) | 1ull;
+}
+
+// Advances the per-workspace launch counter of captured fused calls (one thread).
+__global__ void epoch_advance_kernel(uint64_t* dev_epoch) {
+  if (threadIdx.x == 0) {
+    const uint64_t d = __hip_atomic_load(dev_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(dev_epoch, d + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
 
 // One entry of the chunk table.
 struct ChunkEntry {

@@ -17,11 +17,13 @@ template <int DK, int DV, typename InT>
 __global__ __launch_bounds__(kPrepThreads, 1) void fused_fwd_kernel(PrepArgs pa, ScanArgs sa, FuseArgs fz) {
   static_assert(kPrepThreads == kScanThreads, "one block size for both roles");
   extern __shared__ __align__(16) uint8_t smem[];
-  if ((int)blockIdx.x < fz.producers)
-    chunk_walk<DK, DV, InT, true>(pa, fz, (int)blockIdx.x, fz.producers, smem);
+  FuseArgs f = fz;
+  f.epoch = launch_epoch(fz);
+  if ((int)blockIdx.x < f.producers)
+    chunk_walk<DK, DV, InT, true>(pa, f, (int)blockIdx.x, f.producers, smem);
   else
-    scan_chain<DK, DV, 64, InT, true>(sa, fz, (int64_t)blockIdx.x - fz.producers,
-                                      (int64_t)gridDim.x - fz.producers, smem);
+    scan_chain<DK, DV, 64, InT, true>(sa, f, (int64_t)blockIdx.x - f.producers,
+                                      (int64_t)gridDim.x - f.producers, smem);
 }
 
 }  // namespace kda

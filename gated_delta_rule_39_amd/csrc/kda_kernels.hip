@@ -1,5 +1,8 @@
 // Kernel instantiations and launch sequence of the KDA forward (gfx950).
 #include "kda_launch.h"
+
+#include <atomic>
+
 #include "kda_chunkmap.h"
 #include "kda_prep.h"
 #include "kda_scan.h"
@@ -17,8 +20,23 @@ size_t record_bytes(int dk, int dv) {
   return 0;
 }
 
+// Raises a kernel's dynamic LDS limit once per device (the attribute persists; setting it
+// on every call cost host time on the launch path).
+template <typename K>
+static hipError_t allow_smem(K kern, size_t smem) {
+  static std::atomic<uint64_t> done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+
 static void mark(const ForwardPlan& p, int i, hipStream_t stream) {
-  if (p.marks[i]) hipEventRecord(p.marks[i], stream);
+  if (p.marks[i]) (void)hipEventRecord(p.marks[i], stream);
 }
 
 template <int DK, int DV, typename InT>
@@ -33,7 +51,8 @@ static hipError_t launch_prep(const ForwardPlan& p, hipStream_t stream) {
   a.defer = p.defer;
   const size_t smem = PrepSmem<DK, DV>::BYTES;
   auto kern = chunk_prep_kernel<DK, DV, InT>;
-  hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  hipError_t ea = allow_smem(kern, smem);
+  if (ea != hipSuccess) return ea;
   // persistent workgroups, at most one per compute unit (the LDS footprint admits one)
   int64_t grid = p.chunk_wgs > 0 ? p.chunk_wgs : 256;
   const int64_t items = p.n_chunk_ub * (int64_t)p.H;
@@ -49,6 +68,7 @@ static hipError_t launch_scan_nv(const ForwardPlan& p, hipStream_t stream) {
   a.T = p.T; a.T_total = p.T_total; a.N = p.N; a.H = p.H; a.n_chunk_ub = p.n_chunk_ub;
   a.seq_off = p.seq_off; a.seq_order = p.seq_order; a.rec = p.rec; a.scale = p.scale;
   a.nc = p.cu ? 0 : (p.T + kChunk - 1) / kChunk;
+  a.ctl = p.ctl;
   const size_t smem = ScanSmem<DK, DV, NV>::BYTES;
   auto kern = state_scan_kernel<DK, DV, NV, OutT>;
   const int64_t blocks = p.N * (int64_t)p.H * (DV / NV);
@@ -83,6 +103,7 @@ static ScanArgs scan_args(const ForwardPlan& p) {
   a.T = p.T; a.T_total = p.T_total; a.N = p.N; a.H = p.H; a.n_chunk_ub = p.n_chunk_ub;
   a.seq_off = p.seq_off; a.seq_order = p.seq_order; a.rec = p.rec; a.scale = p.scale;
   a.nc = p.cu ? 0 : (p.T + kChunk - 1) / kChunk;
+  a.ctl = p.ctl;
   return a;
 }
 
@@ -91,16 +112,31 @@ static hipError_t launch_fused(const ForwardPlan& p, hipStream_t stream) {
   FuseArgs fz;
   fz.flags = p.flags;
   fz.epoch = p.epoch;
+  fz.ctl = p.ctl;
+  fz.dev_epoch = nullptr;
   fz.producers = p.fuse_producers;
-  // a wait never needs longer than the whole chunk walk (about 10 us per item and
-  // workgroup, a poll about 60 ns): allow several times that
-  const int64_t per_wg = p.n_chunk_ub * (int64_t)p.H / p.fuse_producers + 2;
-  const int64_t spins = per_wg * 1000;
-  fz.spin_limit = (int32_t)(spins < (1 << 16) ? (1 << 16) : (spins > (1 << 30) ? (1 << 30) : spins));
+  if (p.spin_limit > 0) {
+    fz.spin_limit = p.spin_limit;
+  } else {
+    // a wait never needs longer than the whole chunk walk (about 10 us per item and
+    // workgroup, a poll about 60 ns): allow several times that
+    const int64_t per_wg = p.n_chunk_ub * (int64_t)p.H / p.fuse_producers + 2;
+    const int64_t spins = per_wg * 1000;
+    fz.spin_limit = (int32_t)(spins < (1 << 16) ? (1 << 16) : (spins > (1 << 30) ? (1 << 30) : spins));
+  }
+  if (p.captured) {
+    // a replay of a captured launch keeps its arguments: the flag value is derived on the
+    // device from a counter that this one-thread kernel advances before every replay
+    hipLaunchKernelGGL(epoch_advance_kernel, dim3(1), dim3(64), 0, stream, p.ctl + 2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    fz.dev_epoch = p.ctl + 2;
+  }
   const size_t s1 = PrepSmem<DK, DV>::BYTES, s2 = ScanSmem<DK, DV, 64>::BYTES;
   const size_t smem = s1 > s2 ? s1 : s2;
   auto kern = fused_fwd_kernel<DK, DV, InT>;
-  hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  hipError_t ea = allow_smem(kern, smem);
+  if (ea != hipSuccess) return ea;
   const int64_t chains = p.N * (int64_t)p.H * (DV / 64);
   hipLaunchKernelGGL(kern, dim3((unsigned)(p.fuse_producers + chains)), dim3(kPrepThreads), smem, stream,
                      prep_args(p), scan_args(p), fz);

@@ -30,7 +30,10 @@ struct ForwardPlan {
   uint8_t* rec;
   int32_t* defer;  // per (chunk, head): the item needs the exact diagonal tiles (chunk kernel scratch)
   uint64_t* flags;        // per (chunk, head): record-ready flags of the fused kernel
-  uint64_t epoch;         // this call's flag value (fused kernel)
+  uint64_t epoch;         // this call's flag value (eager fused call) or salt (captured call)
+  uint64_t* ctl;          // workspace control words: [0] last launch, [1] failed launch, [2] launch counter
+  bool captured;          // the stream is capturing a graph: flag values come from the device counter
+  int32_t spin_limit;     // polls before a fused-kernel wait gives up
   int32_t fuse_producers;  // > 0: one fused kernel, this many workgroups run the chunk walk
   int32_t slice;  // value columns per scan workgroup (16, 32 or 64)
   int32_t chunk_wgs;  // workgroups of the persistent chunk kernel (>= 1)

@@ -89,8 +89,8 @@ struct PrepSmem {
   static constexpr size_t X = 0;                  // btot -> column operands | Bu fragments -> Bw^T | Bu
   static constexpr size_t Y = X + X_BYTES;        // L (strict lower) + inverse temporaries (upper)
   static constexpr size_t Z = Y + MAT;            // decay-factor table -> Tinv
-  static constexpr size_t GE = Z + Z_BYTES;       // G (log2 units) at the 16 group ends
-  static constexpr size_t GP = GE + 16 * DK * 4;  // Gram partial tiles: [L | Aqk^T][block w][tile b][lane] x 4 fp32
+  static constexpr size_t GE = Z + Z_BYTES;       // G (log2 units) at the 16 group ends, then at token j*
+  static constexpr size_t GP = GE + 17 * DK * 4;  // Gram partial tiles: [L | Aqk^T][block w][tile b][lane] x 4 fp32
   static constexpr size_t NRM = GP + 2 * 16 * 64 * 16;  // norm partials: [exp | sum][tensor 2][half 2][token 64]
   static constexpr size_t BETA = NRM + 2 * 2 * 2 * 64 * 4;
   static constexpr size_t RED = BETA + 64 * 4;    // [8] max |v| per wave, then the guard flag
@@ -317,8 +317,11 @@ __device__ __forceinline__ void rec_store(uint8_t* rec, size_t off, const V& v) 
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4_v, v), rs, (int)off, 0, 16);
     } else if constexpr (sizeof(V) == 8) {
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2_v, v), rs, (int)off, 0, 16);
-    } else {
+    } else if constexpr (sizeof(V) == 4) {
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, (int)off, 0, 16);
+    } else {
+      static_assert(sizeof(V) == 1, "record stores are 1, 4, 8 or 16 bytes");
+      __builtin_amdgcn_raw_buffer_store_b8(__builtin_bit_cast(uint8_t, v), rs, (int)off, 0, 16);
     }
   } else {
     *reinterpret_cast<V*>(rec + off) = v;
@@ -496,6 +499,19 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
       *reinterpret_cast<float4*>(gend + (4 * w + (t >> 2)) * DK + cb + 16 * j + 4 * gq) =
           make_float4(G[4 * j], G[4 * j + 1], G[4 * j + 2], G[4 * j + 3]);
   }
+  // j*: the last token with beta > 0 (-1: none).  Tokens after it write nothing (their
+  // Delta rows are exactly zero), so the rows of the state-update operand
+  // Khat*exp(G_last - G) are scaled by the largest factor that still multiplies a nonzero
+  // Delta row, exp(G_last - G_j*) per channel: with deep decays and beta = 0 at the end of
+  // a chunk, the entries that carry the new state would otherwise fall below fp16's range.
+  const uint64_t bmask = __ballot(sbeta[l] > 0.f);
+  const int jstar = bmask ? 63 - __builtin_clzll(bmask) : -1;  // wave-uniform
+  if (i_loc == jstar) {
+#pragma unroll
+    for (int j = 0; j < 2 * KH; ++j)
+      *reinterpret_cast<float4*>(gend + 16 * DK + cb + 16 * j + 4 * gq) =
+          make_float4(G[4 * j], G[4 * j + 1], G[4 * j + 2], G[4 * j + 3]);
+  }
   __syncthreads();  // #2: group-end gates visible, block totals and norm partials consumed
   mid(2);
 
@@ -504,12 +520,15 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     const int c = tid;
     auto ge = [&](int p) { return p < 0 ? 0.f : gend[p * DK + c]; };
     const float glast = ge(15);
+    // row exponent of Khat*exp(G_last - G): 2^-ec times every entry up to token j* stays
+    // below 2 (|khat| <= 1, exp(G_last - G_j) <= exp(G_last - G_j*) for j <= j*)
+    const int ec = jstar >= 0 ? max(-126, (int)floorf(glast - gend[16 * DK + c])) : 0;
     int bad = 0;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
       const float gp = ge(4 * ww - 1), gn = ge(4 * ww + 3), gm = ge(4 * ww + 1);
       et[ww * DK + c] = exp2_hw(gp);
-      et[(4 + ww) * DK + c] = exp2_hw(glast - gn);
+      et[(4 + ww) * DK + c] = exp2_hw(glast - gn - (float)ec);
       const float d1 = gp - gm, d2 = gm - gn;
       if (!(d1 <= kGuardLog2 && d2 <= kGuardLog2)) bad = 1;
       et[(11 + ww) * DK + c] = exp2_hw(fminf(d1, kGuardLog2));
@@ -519,6 +538,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     et[9 * DK + c] = exp2_hw(ge(11) - ge(3));
     et[10 * DK + c] = exp2_hw(ge(11) - ge(7));
     if (bad) atomicOr(guard, 1);
+    rec_store<WT, R::BYTES>(rec, R::EC + (size_t)c, (int8_t)ec);
   }
   // operand bases: rows khat_i exp(G_i - Gprev(w)) and qhat_i exp(G_i - Gprev(w)),
   // columns khat_j exp(Gnext(w) - G_j); all factors <= 1
@@ -567,7 +587,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         qf[e] = (_Float16)(QB[8 * sl + e] * eS[e]);          // qhat exp(G)
-        kf[e] = (_Float16)(YC[8 * sl + e] * eE[e]);          // khat exp(G_last - G)
+        kf[e] = (_Float16)(i_loc <= jstar ? YC[8 * sl + e] * eE[e] : 0.f);  // khat exp(G_last - G) 2^-ec
         bwr[sl][e] = (_Float16)(bt * XB[8 * sl + e] * eS[e]); // beta khat exp(G)
         y[e] = (_Float16)YC[8 * sl + e];
       }

@@ -62,6 +62,7 @@ struct ScanArgs {
   int64_t nc;                // fixed-length mode (cu == NULL): chunks per row
   const uint8_t* rec;
   float scale;
+  uint64_t* ctl;  // workspace control words ([0]: flag value of the most recent launch; 0 here)
 };
 
 template <int DK, int DV, int NV>
@@ -73,7 +74,8 @@ struct ScanSmem {
   static constexpr size_t DB = SB + 2 * SBUF;                      // Delta fragments [2][NT][64] f16x8
   static constexpr size_t CN = DB + (size_t)2 * NT * 64 * 16;      // column norm partials [4][NV]
   static constexpr size_t RED = CN + 4 * NV * 4;                   // [8]
-  static constexpr size_t BYTES = RED + 8 * 4;
+  static constexpr size_t FAIL = RED + 8 * 4;                      // fused: a wait of this workgroup gave up
+  static constexpr size_t BYTES = FAIL + 16;
 };
 
 // Chunk factors of one token-block wave: rows 16 i .. 16 i + 15 of W, Qhat*exp(G),
@@ -100,6 +102,7 @@ struct KeyRegs {
   static constexpr int TPK = DK / 64;  // 16-row tiles per key wave
   f16x8 kt[TPK][2];
   float lam[TPK];
+  int ec[TPK];  // row exponents of K~^T (the rows were scaled by 2^-ec)
   float vmax;  // max |v| of the chunk (read only by the fused kernel)
 };
 
@@ -146,6 +149,7 @@ __device__ __forceinline__ void load_key(KeyRegs<DK>& c, const uint8_t* rec, int
         c.kt[p][s2] = rec_load<f16x8, FUSED>(rec, R::BYTES, R::KT + ((size_t)(ct * 2 + s2) * 64 + l) * 16);
     } else {
       c.lam[p] = rec_load<float, FUSED>(rec, R::BYTES, R::LAM + (size_t)(16 * ct + 4 * gq + (l & 3)) * 4);
+      c.ec[p] = rec_load<int8_t, FUSED>(rec, R::BYTES, R::EC + (size_t)(16 * ct + 4 * gq + (l & 3)));
     }
   }
 }
@@ -180,6 +184,7 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
   uint8_t* db = smem + SM::DB;
   float* cn = reinterpret_cast<float*>(smem + SM::CN);
   float* red = reinterpret_cast<float*>(smem + SM::RED);
+  volatile int* wfail = reinterpret_cast<volatile int*>(smem + SM::FAIL);
 
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -231,6 +236,13 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
   }
   vm = wave_max(vm);
   if (l == 0) red[wv] = vm;
+  if (tid == 0) {
+    *wfail = 0;
+    // the most recent launch on this workspace (kda_fwd_status): this launch's flag value,
+    // or 0 for the two-kernel path (which has no waits)
+    if (FUSED) __hip_atomic_store(fz.ctl, fz.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else if (a.ctl && bid == 0) __hip_atomic_store(a.ctl, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (!tok_wave) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -258,10 +270,13 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
     const int64_t toks = (c - c0 + 1) * kChunk < L ? (c - c0 + 1) * kChunk : L;
     return copy_exponent((double)cmax + (double)toks * (double)vrun * (double)vrun);
   };
-  // fused: wait until chunk c's record is complete (bounded: a flag that never comes
-  // ends the wait, the walk then reads whatever the record holds).  The flag is read one
-  // step ahead (`pre`), so a record that is already published costs no round trip.
+  // fused: wait until chunk c's record is complete.  The wait is bounded: a flag that
+  // never comes ends it, marks the launch as failed in the workspace's error word and in
+  // this workgroup's LDS flag (its outputs from then on and its part of the final state
+  // become NaN), and no later chunk is waited for.  The flag is read one step ahead (`pre`),
+  // so a record that is already published costs no round trip.
   uint64_t pre = 0;
+  bool failed = false;  // wave-uniform: a wait of this wave gave up
   // the flag of chunk c for this slice (the chunk walk writes one per slice)
   constexpr int NSF = DV / NV;
   auto flag_of = [&](int64_t c) { return fz.flags + ((size_t)c * a.H + h) * NSF + slice; };
@@ -271,11 +286,22 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
   auto await_chunk = [&](int64_t c) {
     if (FUSED && c < c1) {
       const uint64_t* fl = flag_of(c);
-      int spins = 0;
-      if (pre != fz.epoch) {
-        while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != fz.epoch && spins < fz.spin_limit) {
+      if (pre != fz.epoch && !failed) {
+        int spins = 0;
+        bool seen = false;
+        while (true) {
+          seen = __hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == fz.epoch;
+          seen = __builtin_amdgcn_readfirstlane((int)seen) != 0;
+          if (seen || spins >= fz.spin_limit) break;
           __builtin_amdgcn_s_sleep(2);
           ++spins;
+        }
+        if (!seen) {
+          failed = true;
+          if (l == 0) {
+            *wfail = 1;
+            __hip_atomic_store(fz.ctl + 1, fz.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
       }
       pre = 0;
@@ -368,12 +394,14 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
       const int len = rem < kChunk ? (int)rem : kChunk;
       const int i_loc = 16 * i + t;
       const int64_t tok = s0 + idx * kChunk + i_loc;
+      // (fused) a wait of this workgroup gave up: NaN from here on
+      const bool poison = FUSED && (failed || *wfail != 0);
       if (i_loc < len && tok >= 0 && tok < a.T_total) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           float v4[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v4[r] = ldexpf(o[nt][r], -es) * oscale;
+          for (int r = 0; r < 4; ++r) v4[r] = poison ? __builtin_nanf("") : ldexpf(o[nt][r], -es) * oscale;
           store4(out + ((size_t)tok * a.H + h) * DV + col0 + 16 * nt + 4 * gq, v4);
         }
       }
@@ -423,13 +451,16 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
       for (int p = 0; p < TPK; ++p) {
         const float lam[4] = {row_bcast<0>(cur.lam[p]), row_bcast<1>(cur.lam[p]), row_bcast<2>(cur.lam[p]),
                               row_bcast<3>(cur.lam[p])};  // rows 16 ct + 4 gq + r
+        const float ecf = __int_as_float(cur.ec[p]);
+        const int ue4[4] = {__float_as_int(row_bcast<0>(ecf)) - es, __float_as_int(row_bcast<1>(ecf)) - es,
+                            __float_as_int(row_bcast<2>(ecf)) - es, __float_as_int(row_bcast<3>(ecf)) - es};
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           f32x4 u = zero4();
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) u = mfma16(cur.kt[p][s2], dfr[s2][nt], u);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) S[p][nt][r] = fmaf(lam[r], S[p][nt][r], ldexpf(u[r], -es));
+          for (int r = 0; r < 4; ++r) S[p][nt][r] = fmaf(lam[r], S[p][nt][r], ldexpf(u[r], ue4[r]));
         }
       }
       load_key<1, DK, DV, FUSED>(nxt, nrec, i, l);
@@ -466,6 +497,8 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
         if (c + j < c1) step(buf[j], buf[(j + kScanDepth - 1) % kScanDepth], rec_of(c + j + kScanDepth - 1), c + j);
     }
     if (a.ht) {
+      // (fused) every token wave's failure is in the LDS flag before the last barrier B
+      const bool poison = FUSED && (failed || *wfail != 0);
 #pragma unroll
       for (int p = 0; p < TPK; ++p)
 #pragma unroll
@@ -473,16 +506,9 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int row = 16 * (TPK * i + p) + 4 * gq + r;
-            a.ht[sbase + (size_t)row * DV + col0 + 16 * nt + t] = S[p][nt][r];
+            a.ht[sbase + (size_t)row * DV + col0 + 16 * nt + t] = poison ? __builtin_nanf("") : S[p][nt][r];
           }
     }
-  }
-  if (FUSED) {
-    // every wave is past its last wait: clear this slice's flags, so that a replay of the same
-    // launch (a captured graph keeps the call's epoch) waits for its own records
-    __syncthreads();
-    for (int64_t c = c0 + tid; c < c1; c += kScanThreads)
-      __hip_atomic_store(flag_of(c), (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -20,7 +20,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 KDA_BF16, KDA_F32 = 0, 1
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_BAD_ARG",
-          4: "KDA_ERR_ALIGN", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_ALIAS", 7: "KDA_ERR_HIP"}
+          4: "KDA_ERR_ALIGN", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_ALIAS", 7: "KDA_ERR_HIP",
+          8: "KDA_ERR_TIMEOUT"}
 
 
 class Problem(ctypes.Structure):
@@ -38,6 +39,8 @@ _lib.kda_fwd_validate.restype = ctypes.c_int
 _lib.kda_fwd.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
                          ctypes.c_size_t, _P]
 _lib.kda_fwd.restype = ctypes.c_int
+_lib.kda_fwd_status.argtypes = [_P, ctypes.c_size_t, _P]
+_lib.kda_fwd_status.restype = ctypes.c_int
 _lib.kda_decode.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]
 _lib.kda_decode.restype = ctypes.c_int
 _lib.kda_bwd_workspace_size.argtypes = [ctypes.POINTER(Problem)]
@@ -141,6 +144,16 @@ def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, *, out=None, ht=
     if rc != 0:
         raise KDAError(rc)
     return out, ht
+
+
+def fwd_status(workspace, stream=None):
+    """Outcome of the most recent fwd call on `workspace` (kda_fwd_status): returns the status
+    code (0 = KDA_OK, 8 = KDA_ERR_TIMEOUT: a wait of the fused kernel gave up and its outputs
+    hold NaN).  Synchronises the stream."""
+    if stream is None:
+        stream = torch.cuda.current_stream(workspace.device).cuda_stream
+    return int(_lib.kda_fwd_status(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   ctypes.c_void_p(stream)))
 
 
 def decode(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, *, out=None, ht=None,

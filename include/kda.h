@@ -29,12 +29,13 @@
  *     thrown.  A failed call enqueues no work.
  *   - kda_fwd enqueues its kernels on `stream` and returns without waiting
  *     for them.  It keeps no pointer after that work completes, holds no
- *     global state beyond a process-wide call counter (atomic) and may be
+ *     global state beyond a process-wide call counter (atomic) and per-device
+ *     caches of the compute-unit count and kernel attributes, and may be
  *     called from several host threads at once; two calls that run at the
  *     same time need separate workspaces.  The enqueued work is safe to capture
- *     in a HIP graph and replay (no memset nodes; the fused kernel's hand-off
- *     flags are cleared by the kernel itself, so a replay with the captured
- *     call's flag value still waits for its own records).
+ *     in a HIP graph and replay (no memset nodes; a captured fused call also
+ *     captures a one-thread kernel that advances a launch counter in the
+ *     workspace, so every replay has its own hand-off flag value).
  *   - Results are deterministic: the same inputs on the same GPU and build
  *     give bitwise-equal out and ht.
  */
@@ -59,7 +60,8 @@ typedef enum {
   KDA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
   KDA_ERR_WORKSPACE = 5,   /* workspace smaller than kda_fwd_workspace_size() */
   KDA_ERR_ALIAS = 6,       /* out or ht overlaps an input (ht == h0 exactly is allowed) */
-  KDA_ERR_HIP = 7          /* a HIP launch reported an error */
+  KDA_ERR_HIP = 7,         /* a HIP launch reported an error */
+  KDA_ERR_TIMEOUT = 8      /* (kda_fwd_status) a wait of the fused kernel gave up */
 } kda_status_t;
 
 /*
@@ -86,8 +88,12 @@ typedef struct {
  * problem).  The workspace holds the chunk table and, per 64-token chunk and
  * head, the chunk's factors (the WY factors W and U, the decayed queries and
  * keys, the masked intra-chunk attention and the chunk decay) and a ready
- * flag.  Its contents are scratch: nothing in it needs initialising and
- * nothing survives the call (flags are compared with a per-call value).
+ * flag.  Its contents are scratch: nothing in it needs initialising (flags are
+ * compared with a per-launch value).  The only state that outlives a call is
+ * the outcome word that kda_fwd_status reads.  The chunkwise form whose
+ * per-chunk factors these are is the one "Autoresearch on Kimi Delta
+ * Attention", section "KDA in one minute", points to (matrix products inside
+ * a chunk, the state carried between chunks).
  */
 size_t kda_fwd_workspace_size(const kda_problem_t* prob);
 
@@ -96,7 +102,11 @@ size_t kda_fwd_workspace_size(const kda_problem_t* prob);
  * sizes, dtype, NULL pointers, alignment, workspace size and overlaps.  With
  * the environment variable KDA_VALIDATE_CU_SEQLENS=1 it also copies
  * cu_seqlens to the host (a synchronising copy) and checks cu[0] == 0,
- * non-decreasing offsets and cu[N] == seqlen.  Arguments as for kda_fwd.
+ * non-decreasing offsets and cu[N] == seqlen (KDA_ERR_BAD_ARG otherwise;
+ * kda_fwd then enqueues nothing).  Arguments as for kda_fwd.  This is the
+ * legal-input side of the contract: "Kernel Design Agents (KDA) optimize Kimi
+ * Delta Attention (KDA)", section "04 - Hardening" (a strict specification of
+ * the legal inputs, on each of which the kernels must be correct).
  */
 kda_status_t kda_fwd_validate(const kda_problem_t* prob, const void* q, const void* k,
                               const void* v, const float* g, const void* beta, const float* h0,
@@ -104,7 +114,10 @@ kda_status_t kda_fwd_validate(const kda_problem_t* prob, const void* q, const vo
                               const float* ht, const void* workspace, size_t workspace_bytes);
 
 /*
- * KDA forward pass.
+ * KDA forward pass: the operation at the top of this header, over the batches
+ * that "Kernel Design Agents (KDA) optimize Kimi Delta Attention (KDA)",
+ * section "01 - Results", benchmarks (fixed-length and packed varlen, initial
+ * and final state).
  *
  *   q, k        [B, T, H, dk]  dtype        queries and keys (any finite magnitude;
  *                                           normalised inside the kernels)
@@ -141,11 +154,31 @@ kda_status_t kda_fwd_validate(const kda_problem_t* prob, const void* q, const vo
  *                            unit a workgroup)
  *   KDA_CHUNK_WGS=n          at most n workgroups compute chunk factors (default: one
  *                            per compute unit, minus the chain workgroups when fused)
+ *   KDA_SPIN_LIMIT=n         polls before a wait of the fused kernel gives up (default:
+ *                            several times the whole chunk walk); a small n forces the
+ *                            failure path that kda_fwd_status reports
  */
 kda_status_t kda_fwd(const kda_problem_t* prob, const void* q, const void* k, const void* v,
                      const float* g, const void* beta, const float* h0,
                      const int32_t* cu_seqlens, float scale, void* out, float* ht,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Outcome of the most recent kda_fwd call on `workspace`.  Waits inside the
+ * fused kernel are bounded; one that gives up (its spin limit ran out before
+ * the awaited chunk factors were published) writes NaN into the outputs and
+ * final-state entries it would have produced and records the launch's flag
+ * value in the workspace.  This call synchronises `stream`, copies that word
+ * to the host and returns KDA_ERR_TIMEOUT if the most recent launch on the
+ * workspace failed this way, KDA_OK otherwise (also for calls that took the
+ * two-kernel path, which has no waits).  A failed launch captured in a graph
+ * is reported again by each replay that fails.  KDA_ERR_NULL / KDA_ERR_ALIGN /
+ * KDA_ERR_WORKSPACE for a bad workspace argument (at least 256 bytes).
+ * "Kernel Design Agents (KDA) optimize Kimi Delta Attention (KDA)", section
+ * "04 - Hardening", asks for correctness on every legal input: a result the
+ * kernel could not finish must not pass silently.
+ */
+kda_status_t kda_fwd_status(const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kda_fwd with timing marks for profiling: identical work, plus hipEventRecord

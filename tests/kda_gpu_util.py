@@ -1,15 +1,84 @@
 """Helpers for GPU tests: move seeded inputs to the device, call the C ABI
-through the binding, and compare with the fp64 oracle."""
+through the binding, and compare with the fp64 oracle.
+
+Acceptance ("Kernel Design Agents (KDA) optimize Kimi Delta Attention (KDA)",
+section "04 - Hardening": strict element-wise tolerances), applied to the
+output and to the final state separately:
+  * relative RMSE <= 5e-3 over the whole tensor, and again over every
+    (sequence, head) on its own, so that one wrong head or one wrong short
+    sequence cannot hide inside a global norm;
+  * every element: |x - ref| <= RTOL_ELEM |ref| + ATOL * rms(ref over its
+    (sequence, head)).  RTOL_ELEM = 2^-8 is twice the bf16 output rounding
+    (2^-9 relative); ATOL covers the fp16 operand rounding of the chunked
+    products (unit roundoff 2^-11, contractions over 128 key channels and 64
+    tokens with fp32 accumulation), whose largest element-wise effect measured
+    on the five workloads is 0.016 (outputs, heavy-tailed skewed batch) and
+    0.0065 (final states) of the (sequence, head) RMS: the bounds leave about
+    three times that.
+"""
 import numpy as np
 
 TOL = 5e-3  # relative RMSE gate on outputs and on the final state
+RTOL_ELEM = 2.0 ** -8
+ATOL_OUT = 0.05
+ATOL_STATE = 0.02
 
 
 def rel_rmse(x, ref):
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     nr = np.linalg.norm(ref)
-    return float(np.linalg.norm(x - ref) / nr) if nr > 0 else float(np.max(np.abs(x)))
+    return float(np.linalg.norm(x - ref) / nr) if nr > 0 else float(np.max(np.abs(x), initial=0.0))
+
+
+def _elem_excess(x, ref, atol):
+    """max over elements of (|x - ref| - RTOL_ELEM |ref|) / rms(ref); <= atol passes.
+    A reference that is exactly zero everywhere needs |x| <= 1e-6."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if x.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    if rms == 0.0:
+        return float(np.max(np.abs(x))) * (atol / 1e-6)
+    return float(np.max((np.abs(x - ref) - RTOL_ELEM * np.abs(ref)) / rms))
+
+
+def gate(x, o, h, ro, rh, label="", tol=TOL, check_state=True):
+    """Applies every acceptance bound above; prints one line and returns the measured values."""
+    assert np.all(np.isfinite(o)), label
+    B, T, H, dk, dv = x.shape
+    res = {"out": rel_rmse(o, ro), "state": rel_rmse(h, rh) if check_state else 0.0,
+           "out_head": 0.0, "state_head": 0.0, "out_elem": 0.0, "state_elem": 0.0,
+           "out_maxabs": float(np.max(np.abs(o - ro), initial=0.0)),
+           "state_maxabs": float(np.max(np.abs(h - rh), initial=0.0)) if check_state else 0.0}
+    of = o.reshape(-1, H, dv)
+    rf = ro.reshape(-1, H, dv)
+    worst = None
+    for n, (a, b) in enumerate(x.seq_bounds()):
+        for hh in range(H):
+            if b > a:
+                e = rel_rmse(of[a:b, hh], rf[a:b, hh])
+                if e > res["out_head"]:
+                    res["out_head"], worst = e, ("out", n, hh)
+                res["out_elem"] = max(res["out_elem"], _elem_excess(of[a:b, hh], rf[a:b, hh], ATOL_OUT))
+            if check_state:
+                e = rel_rmse(h[n, hh], rh[n, hh])
+                if e > res["state_head"]:
+                    res["state_head"] = e
+                    if e > res["out_head"]:
+                        worst = ("state", n, hh)
+                res["state_elem"] = max(res["state_elem"], _elem_excess(h[n, hh], rh[n, hh], ATOL_STATE))
+    print("%s: rel-RMSE out %.3e state %.3e; worst (sequence, head) out %.3e state %.3e %s; element excess "
+          "out %.4f (<= %.2f) state %.4f (<= %.2f); max|err| out %.3e state %.3e"
+          % (label, res["out"], res["state"], res["out_head"], res["state_head"], worst, res["out_elem"],
+             ATOL_OUT, res["state_elem"], ATOL_STATE, res["out_maxabs"], res["state_maxabs"]), flush=True)
+    if check_state:
+        assert np.all(np.isfinite(h)), label
+    assert res["out"] <= tol and res["state"] <= tol, (label, res)
+    assert res["out_head"] <= tol and res["state_head"] <= tol, (label, worst, res)
+    assert res["out_elem"] <= ATOL_OUT and res["state_elem"] <= ATOL_STATE, (label, res)
+    return res
 
 
 def to_device(x):
