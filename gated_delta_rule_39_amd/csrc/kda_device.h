@@ -139,14 +139,12 @@ struct Rec {
   static constexpr size_t A = KT + 64 * DK * 2;
   // U: C-layout tiles of U * 2^ue [64 x DV], [row block 4][NTV][lane] x f16x4
   static constexpr size_t U = A + 64 * 64 * 2;
-  // LAM: exp(G_last) per key channel, fp32 [DK]
+  // LAM: per key channel c, { float exp(G_last), int ec } [DK]: ec <= 0 is the exponent by
+  // which row c of Khat*exp(G_last-G) was scaled (by 2^-ec) before its fp16 rounding
   static constexpr size_t LAM = U + 64 * DV * 2;
   // HDR: { float vmax (max |v| over the chunk), int ue (U scale exponent), pad, pad }
-  static constexpr size_t HDR = LAM + DK * 4;
-  // EC: per key channel c, the exponent ec <= 0 by which row c of Khat*exp(G_last-G) is
-  // scaled (by 2^-ec) before its fp16 rounding, int8 [DK]
-  static constexpr size_t EC = HDR + 16;
-  static constexpr size_t BYTES = (EC + DK + 255) / 256 * 256;
+  static constexpr size_t HDR = LAM + DK * 8;
+  static constexpr size_t BYTES = (HDR + 16 + 255) / 256 * 256;
 };
 
 // Raw buffer resources (record stores and loads of the fused kernel): dword 3 with a 32-bit
@@ -165,11 +163,9 @@ __device__ __forceinline__ V rec_load(const uint8_t* rec, int bytes, size_t off)
       return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 16));
     } else if constexpr (sizeof(V) == 8) {
       return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, 16));
-    } else if constexpr (sizeof(V) == 4) {
-      return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, 16));
     } else {
-      static_assert(sizeof(V) == 1, "record loads are 1, 4, 8 or 16 bytes");
-      return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b8(rs, (int)off, 0, 16));
+      static_assert(sizeof(V) == 4, "record loads are 4, 8 or 16 bytes");
+      return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, 16));
     }
   } else {
     return *reinterpret_cast<const V*>(rec + off);
@@ -190,11 +186,11 @@ __device__ __forceinline__ V rec_load(const uint8_t* rec, int bytes, size_t off)
 // captured just before the fused kernel advances a counter in the workspace, and every
 // workgroup mixes the counter with the captured salt.
 //
-// Waits are bounded.  A wait that gives up marks the launch as failed: the workgroup
-// stores the launch's flag value into the workspace's error word (kda_fwd_status reports
-// it), writes NaN into the outputs it would have produced from that chunk on and into its
-// part of the final state, and stops waiting.  No index or address is ever derived from a
-// record's contents, so reading a record that is not complete is harmless.
+// Waits are bounded.  A wave whose wait gives up stores the launch's flag value into the
+// workspace's error word (kda_fwd_status reports it) and stops waiting; its chain's final
+// state is written as NaN, and a key wave's state rows become NaN at once, so the outputs
+// after that point (which read the state) are NaN too.  No index or address is ever
+// derived from a record's contents, so reading a record that is not complete is harmless.
 struct FuseArgs {
   uint64_t* flags;            // [chunk * H + head][DV / 64]
   uint64_t epoch;             // eager call: the flag value; captured call: the salt

@@ -317,11 +317,9 @@ __device__ __forceinline__ void rec_store(uint8_t* rec, size_t off, const V& v) 
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4_v, v), rs, (int)off, 0, 16);
     } else if constexpr (sizeof(V) == 8) {
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2_v, v), rs, (int)off, 0, 16);
-    } else if constexpr (sizeof(V) == 4) {
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, (int)off, 0, 16);
     } else {
-      static_assert(sizeof(V) == 1, "record stores are 1, 4, 8 or 16 bytes");
-      __builtin_amdgcn_raw_buffer_store_b8(__builtin_bit_cast(uint8_t, v), rs, (int)off, 0, 16);
+      static_assert(sizeof(V) == 4, "record stores are 4, 8 or 16 bytes");
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, (int)off, 0, 16);
     }
   } else {
     *reinterpret_cast<V*>(rec + off) = v;
@@ -538,7 +536,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     et[9 * DK + c] = exp2_hw(ge(11) - ge(3));
     et[10 * DK + c] = exp2_hw(ge(11) - ge(7));
     if (bad) atomicOr(guard, 1);
-    rec_store<WT, R::BYTES>(rec, R::EC + (size_t)c, (int8_t)ec);
+    rec_store<WT, R::BYTES>(rec, R::LAM + (size_t)c * 8, uint2_v{__float_as_uint(exp2_hw(glast)), (uint32_t)ec});
   }
   // operand bases: rows khat_i exp(G_i - Gprev(w)) and qhat_i exp(G_i - Gprev(w)),
   // columns khat_j exp(Gnext(w) - G_j); all factors <= 1
@@ -614,7 +612,6 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
         *reinterpret_cast<f16x4*>(bux + ((size_t)((2 * sv + hh) * 2 + (w >> 1)) * 64 + l) * 16 + (w & 1) * 8) = h4;
       }
     }
-    if (tid < DK) rec_store<WT, R::BYTES>(rec, R::LAM + (size_t)tid * 4, exp2_hw(gend[15 * DK + tid]));
     if (tid == 0) {
       rec_store<WT, R::BYTES>(rec, R::HDR, vmax);
       rec_store<WT, R::BYTES>(rec, R::HDR + 4, ue);

@@ -74,7 +74,7 @@ struct ScanSmem {
   static constexpr size_t DB = SB + 2 * SBUF;                      // Delta fragments [2][NT][64] f16x8
   static constexpr size_t CN = DB + (size_t)2 * NT * 64 * 16;      // column norm partials [4][NV]
   static constexpr size_t RED = CN + 4 * NV * 4;                   // [8]
-  static constexpr size_t FAIL = RED + 8 * 4;                      // fused: a wait of this workgroup gave up
+  static constexpr size_t FAIL = RED + 8 * 4;                      // fused: a token wave's wait gave up
   static constexpr size_t BYTES = FAIL + 16;
 };
 
@@ -148,8 +148,9 @@ __device__ __forceinline__ void load_key(KeyRegs<DK>& c, const uint8_t* rec, int
       for (int s2 = 0; s2 < 2; ++s2)
         c.kt[p][s2] = rec_load<f16x8, FUSED>(rec, R::BYTES, R::KT + ((size_t)(ct * 2 + s2) * 64 + l) * 16);
     } else {
-      c.lam[p] = rec_load<float, FUSED>(rec, R::BYTES, R::LAM + (size_t)(16 * ct + 4 * gq + (l & 3)) * 4);
-      c.ec[p] = rec_load<int8_t, FUSED>(rec, R::BYTES, R::EC + (size_t)(16 * ct + 4 * gq + (l & 3)));
+      const uint2_v le = rec_load<uint2_v, FUSED>(rec, R::BYTES, R::LAM + (size_t)(16 * ct + 4 * gq + (l & 3)) * 8);
+      c.lam[p] = __uint_as_float(le[0]);
+      c.ec[p] = (int)le[1];
     }
   }
 }
@@ -184,7 +185,7 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
   uint8_t* db = smem + SM::DB;
   float* cn = reinterpret_cast<float*>(smem + SM::CN);
   float* red = reinterpret_cast<float*>(smem + SM::RED);
-  volatile int* wfail = reinterpret_cast<volatile int*>(smem + SM::FAIL);
+  volatile int* tok_failed = reinterpret_cast<volatile int*>(smem + SM::FAIL);
 
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -237,7 +238,7 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
   vm = wave_max(vm);
   if (l == 0) red[wv] = vm;
   if (tid == 0) {
-    *wfail = 0;
+    *tok_failed = 0;
     // the most recent launch on this workspace (kda_fwd_status): this launch's flag value,
     // or 0 for the two-kernel path (which has no waits)
     if (FUSED) __hip_atomic_store(fz.ctl, fz.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -271,10 +272,11 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
     return copy_exponent((double)cmax + (double)toks * (double)vrun * (double)vrun);
   };
   // fused: wait until chunk c's record is complete.  The wait is bounded: a flag that
-  // never comes ends it, marks the launch as failed in the workspace's error word and in
-  // this workgroup's LDS flag (its outputs from then on and its part of the final state
-  // become NaN), and no later chunk is waited for.  The flag is read one step ahead (`pre`),
-  // so a record that is already published costs no round trip.
+  // never comes ends it, marks the launch as failed in the workspace's error word, and this
+  // wave waits for no later chunk.  A key wave's state rows become NaN at that point (so do
+  // all later outputs, which read the state); a token wave's failure is noted in LDS and
+  // turns the final state NaN at the end.  The flag is read one step ahead (`pre`), so a
+  // record that is already published costs no round trip.
   uint64_t pre = 0;
   bool failed = false;  // wave-uniform: a wait of this wave gave up
   // the flag of chunk c for this slice (the chunk walk writes one per slice)
@@ -288,20 +290,23 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
       const uint64_t* fl = flag_of(c);
       if (pre != fz.epoch && !failed) {
         int spins = 0;
-        bool seen = false;
-        while (true) {
-          seen = __hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == fz.epoch;
-          seen = __builtin_amdgcn_readfirstlane((int)seen) != 0;
-          if (seen || spins >= fz.spin_limit) break;
+        while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != fz.epoch && spins < fz.spin_limit) {
           __builtin_amdgcn_s_sleep(2);
           ++spins;
         }
-        if (!seen) {
+        if (__any(spins >= fz.spin_limit)) {
           failed = true;
           if (l == 0) {
-            *wfail = 1;
             __hip_atomic_store(fz.ctl + 1, fz.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (tok_wave) *tok_failed = 1;
           }
+          // a key wave's state rows become NaN here and stay NaN (they only enter products)
+#pragma unroll
+          for (int p = 0; p < TPK; ++p)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) S[p][nt][r] = __builtin_nanf("");
         }
       }
       pre = 0;
@@ -394,14 +399,12 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
       const int len = rem < kChunk ? (int)rem : kChunk;
       const int i_loc = 16 * i + t;
       const int64_t tok = s0 + idx * kChunk + i_loc;
-      // (fused) a wait of this workgroup gave up: NaN from here on
-      const bool poison = FUSED && (failed || *wfail != 0);
       if (i_loc < len && tok >= 0 && tok < a.T_total) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           float v4[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v4[r] = poison ? __builtin_nanf("") : ldexpf(o[nt][r], -es) * oscale;
+          for (int r = 0; r < 4; ++r) v4[r] = ldexpf(o[nt][r], -es) * oscale;
           store4(out + ((size_t)tok * a.H + h) * DV + col0 + 16 * nt + 4 * gq, v4);
         }
       }
@@ -463,6 +466,7 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
           for (int r = 0; r < 4; ++r) S[p][nt][r] = fmaf(lam[r], S[p][nt][r], ldexpf(u[r], ue4[r]));
         }
       }
+
       load_key<1, DK, DV, FUSED>(nxt, nrec, i, l);
       // the next chunk's copy exponent (the same value its token waves derive)
       if (FUSED && c + 1 < c1) es = es_at(c + 1, nxt.vmax);
@@ -497,8 +501,9 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
         if (c + j < c1) step(buf[j], buf[(j + kScanDepth - 1) % kScanDepth], rec_of(c + j + kScanDepth - 1), c + j);
     }
     if (a.ht) {
-      // (fused) every token wave's failure is in the LDS flag before the last barrier B
-      const bool poison = FUSED && (failed || *wfail != 0);
+      // (fused) a token wave's wait gave up: the final state is not valid (every wave is past
+      // the last barrier B, so the note is visible)
+      const bool poison = FUSED && *tok_failed != 0;
 #pragma unroll
       for (int p = 0; p < TPK; ++p)
 #pragma unroll
