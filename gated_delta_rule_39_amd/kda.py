@@ -39,6 +39,8 @@ _lib.kda_fwd_validate.restype = ctypes.c_int
 _lib.kda_fwd.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
                          ctypes.c_size_t, _P]
 _lib.kda_fwd.restype = ctypes.c_int
+_lib.kda_fwd_noalloc.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]
+_lib.kda_fwd_noalloc.restype = ctypes.c_int
 _lib.kda_fwd_status.argtypes = [_P, ctypes.c_size_t, _P]
 _lib.kda_fwd_status.restype = ctypes.c_int
 _lib.kda_decode.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]
@@ -141,6 +143,23 @@ def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, *, out=None, ht=
     rc = _lib.kda_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
                       _ptr(cu_seqlens), float(scale), _ptr(out), _ptr(ht), _ptr(workspace),
                       workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KDAError(rc)
+    return out, ht
+
+
+def fwd_noalloc(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, *, out, ht=None, stream=None):
+    """kda_fwd_noalloc: the forward with the library's static device workspace (no allocation in
+    the call; problems larger than KDA_NOALLOC_SCRATCH_BYTES raise KDA_ERR_WORKSPACE).  The caller
+    passes `out` (and `ht`, or None for no final state)."""
+    B, T, H, dk, dv, N, code = _check(q, k, v, g, beta, h0, cu_seqlens, (out, ht))
+    if scale is None:
+        scale = dk ** -0.5
+    prob = make_problem(B, T, H, dk, dv, code, N if cu_seqlens is not None else 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = _lib.kda_fwd_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                              _ptr(cu_seqlens), float(scale), _ptr(out), _ptr(ht), ctypes.c_void_p(stream))
     if rc != 0:
         raise KDAError(rc)
     return out, ht

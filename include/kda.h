@@ -197,6 +197,26 @@ kda_status_t kda_fwd_timed(const kda_problem_t* prob, const void* q, const void*
                            void* const* events);
 
 /*
+ * kda_fwd without a workspace argument, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The workspace is a static device array of
+ * KDA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until
+ * the process ends; the call itself allocates nothing.  Problems whose
+ * kda_fwd_workspace_size exceeds that size are rejected with KDA_ERR_WORKSPACE
+ * before anything is enqueued (64 MiB: 8,192 tokens of up to 6 heads at
+ * dk = dv = 128, i.e. up to 894 pairs of a 64-token chunk and a head).  All calls on
+ * one GPU share its array: two calls that overlap in time on the same GPU (other
+ * streams, other host threads) race and give wrong results; calls ordered on
+ * one stream do not.  Arguments, results and the other errors as for kda_fwd.
+ * A wait of the fused kernel that gives up still writes NaN into the affected
+ * outputs; kda_fwd_status does not see this array.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+kda_status_t kda_fwd_noalloc(const kda_problem_t* prob, const void* q, const void* k, const void* v,
+                             const float* g, const void* beta, const float* h0,
+                             const int32_t* cu_seqlens, float scale, void* out, float* ht, void* stream);
+
+/*
  * The same forward evaluated token by token, for decode steps (one new token
  * per sequence, seqlen == 1) and other short continuations of many sequences.
  * It is the step that "Autoresearch on Kimi Delta Attention", section "KDA in
