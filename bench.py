@@ -16,9 +16,18 @@ steps (the headline timing has no events between the kernels).
 
 Beside the headline workload the line also carries the two 8,192-token varlen
 batches (uniform and skewed lengths), timed the same way and checked against the
-oracle, the geomean of the three, the headline workload with cold caches, and a
-decode step (kda_decode) over 256 sequences with its HBM roofline (--no-extra skips
-these, for profiling runs).
+oracle, the geomean of the three, the headline workload with cold caches, a
+decode step (kda_decode) over 256 sequences with its HBM roofline, the backward
+pass, and the serial bound of the state pass (the chain-latency bound: the
+longest chain's chunks times the step latency of a lone chain); --no-extra skips
+these, for profiling runs.
+
+The roofline of the fused kernel counts the method minimum as its algorithmic
+bytes (every input read once, the output written once, h0 and ht once); the
+bytes the design itself moves (its per-chunk records written and read back) are
+reported beside them as design_bytes.  traffic, mfma_util_pct and valu_busy_pct
+come from the committed rocprofv3 counter summary (profiles/traffic.json) while
+it matches the kernel sources.
 """
 import argparse
 import ctypes
@@ -36,6 +45,9 @@ import numpy as np  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published (no sparsity)
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published (counts packed fp32 FMA)
+# fp32 vector peak without packed instructions, which every HIP object here is built
+# without: 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz
+FP32_VECTOR_NONPACKED_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 # fp32 operations per state element per (token, head) that the token-by-token backward must
 # do: one forward recompute (decay 1, prediction 2, correction 2) and the reverse step
 # (decay 1, G update 2, u 2, a.do 2, G.delta 2, a.u 2, da 2, a.da 2, G decay 1)
@@ -52,8 +64,10 @@ def log(*a):
 # ---------------------------------------------------------------------------
 
 def record_bytes(dk, dv):
-    raw = 64 * dk * 2 * 3 + 64 * 64 * 2 + 64 * dv * 2 + dk * 4 + 16
-    return raw
+    """Bytes of the per-(chunk, head) record the chunk walk hands to the scan: W, Qhat*exp(G),
+    (Khat*exp(G_last-G))^T (fp16, 64 x dk each), the masked attention (fp16 64 x 64), U (fp16
+    64 x dv), {exp(G_last), row exponent} per key channel and a 16-byte header."""
+    return 64 * dk * 2 * 3 + 64 * 64 * 2 + 64 * dv * 2 + dk * 8 + 16
 
 
 def algorithmic_work(x, n_chunks):
@@ -74,6 +88,17 @@ def algorithmic_work(x, n_chunks):
     prep_flops = ch * 2 * (tri_strict * dk + tri_incl * dk + tri_incl * dk + tri_incl * dv)
     scan_flops = ch * 2 * (C * dk * dv * 3 + tri_incl * dv)
     return dict(prep_bytes=prep_bytes, scan_bytes=scan_bytes, prep_flops=prep_flops, scan_flops=scan_flops)
+
+
+def method_min_bytes(x):
+    """The fused minimum: every input read once, the output written once, the initial state read
+    and the final state written once (1,538 bytes per token and head at dk = dv = 128 with bf16
+    q, k, v, beta and out, fp32 g)."""
+    B, T, H, dk, dv = x.shape
+    es = 2 if x.dtype == "bf16" else 4
+    per_tok_head = (2 * dk + dv) * es + dk * 4 + es + dv * es
+    state = x.num_seqs * H * dk * dv * 4 * ((x.h0 is not None) + 1)
+    return B * T * H * per_tok_head + state
 
 
 def n_chunks_of(x):
@@ -100,9 +125,9 @@ def hip_runtime():
     return hip
 
 
-def traffic_from_profiles(kernel):
-    """HBM bytes per launch from the committed counter summary, if it was taken on the
-    current kernel sources (else None)."""
+def counters_from_profiles(kernel):
+    """The committed counter summary of `kernel` (HBM bytes per launch, MFMA and VALU busy), if
+    it was taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -113,7 +138,12 @@ def traffic_from_profiles(kernel):
     k = rec.get("kernels", {}).get(kernel)
     if k is None or k.get("source_sha256") != kernel_source_hash(kernel):
         return None
-    return k.get("hbm_bytes_per_launch")
+    return k
+
+
+def traffic_from_profiles(kernel):
+    k = counters_from_profiles(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
 
 
 KERNEL_SOURCES = {"chunk_prep_kernel": ["kda_device.h", "kda_prep.h"],
@@ -212,6 +242,65 @@ def extra_measurements(args, lib, kda, make_config, upload, dev, torch, argv1, o
     return res
 
 
+def chain_latency(kda, dev, torch, x, kernel_ms, reps=20):
+    """The serial bound of the state pass: the longest chain's chunks times the latency of one
+    chunk step of a lone chain (one head of the same sequence length, 64-column slices, the
+    two-kernel path, so that nothing else shares the GPU): the step the fused kernel's scan
+    workgroups repeat, without the chunk walk running beside it."""
+    import ctypes as ct
+    B, T, H, dk, dv = x.shape
+    y_q = torch.zeros((1, T, 1, dk), dtype=torch.bfloat16, device=dev).normal_()
+    y_k = torch.zeros_like(y_q).normal_()
+    y_v = torch.zeros((1, T, 1, dv), dtype=torch.bfloat16, device=dev).normal_()
+    y_g = -torch.rand((1, T, 1, dk), dtype=torch.float32, device=dev) * 0.2
+    y_b = torch.full((1, T, 1), 0.5, dtype=torch.bfloat16, device=dev)
+    saved = {k_: os.environ.get(k_) for k_ in ("KDA_FUSED", "KDA_SCAN_SLICE")}
+    os.environ["KDA_FUSED"], os.environ["KDA_SCAN_SLICE"] = "0", "64"
+    try:
+        hip = hip_runtime()
+        lib = kda.library()
+        prob = kda.make_problem(1, T, 1, dk, dv, kda.KDA_BF16, 0)
+        wsb = int(lib.kda_fwd_workspace_size(ct.byref(prob)))
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        out = torch.empty_like(y_v)
+        P = lambda t_: ct.c_void_p(t_.data_ptr())
+        argv = [ct.byref(prob), P(y_q), P(y_k), P(y_v), P(y_g), P(y_b), None, None, ct.c_float(dk ** -0.5),
+                P(out), None, P(ws), ct.c_size_t(wsb), ct.c_void_p(torch.cuda.current_stream(dev).cuda_stream)]
+        for _ in range(5):
+            lib.kda_fwd(*argv)
+        rows = []
+        for _ in range(reps):
+            row = (ct.c_void_p * 4)()
+            for j in range(4):
+                e = ct.c_void_p()
+                hip.hipEventCreate(ct.byref(e))
+                row[j] = e
+            lib.kda_fwd_timed(*argv, ct.cast(row, ct.c_void_p))
+            rows.append(row)
+        torch.cuda.synchronize()
+
+        def el(a, b):
+            f = ct.c_float()
+            hip.hipEventElapsedTime(ct.byref(f), a, b)
+            return f.value
+        scan_ms = float(np.median([el(r[2], r[3]) for r in rows]))
+        for r in rows:
+            for j in range(4):
+                hip.hipEventDestroy(r[j])
+    finally:
+        for k_, v_ in saved.items():
+            if v_ is None:
+                os.environ.pop(k_, None)
+            else:
+                os.environ[k_] = v_
+    steps = (T + 63) // 64
+    step_us = 1e3 * scan_ms / steps
+    return {"steps": steps, "step_us": round(step_us, 4), "bound_us": round(step_us * steps, 2),
+            "kernel_us": round(1e3 * float(kernel_ms), 2), "frac": round(step_us * steps / (1e3 * float(kernel_ms)), 4),
+            "note": "step latency of one 64-column chain measured alone (state scan of a 1-head problem, "
+                    "the whole scan kernel divided by its chunks)"}
+
+
 def backward_measurement(kda, dev, torch, calls=3):
     """kda_bwd on the headline workload (B=1, T=8192, H=32, d=128, bf16), timed over a few
     calls (it walks every token in sequence), with its parity checked on a small problem
@@ -272,8 +361,11 @@ def backward_measurement(kda, dev, torch, calls=3):
     log("backward %s: %.3f ms/call, parity (B=1 T=200 H=4) %s" % (x.name, ms, errs))
     return {"ok": good, "workload": "backward of %s (B=1 T=8192 H=32 d=128 bf16)" % x.name,
             "ms_per_call": round(ms, 3), "tokens_per_s": round(B * T / (ms * 1e-3), 1) if good else None,
-            "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
+            "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": round(FP32_VECTOR_NONPACKED_TFLOPS, 2),
+                         "unit": "TFLOP/s", "frac": round(tflops / FP32_VECTOR_NONPACKED_TFLOPS, 4),
+                         "peak_note": "fp32 vector without packed instructions (the build disables them): "
+                                      "256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz; the published "
+                                      "157.3 TFLOP/s counts packed fp32 FMA",
                          "flops_per_call": int(flops), "bytes_per_call": int(nbytes),
                          "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
                          "note": "token by token (fp32 vector work on the state, %d flops per element and "
@@ -550,17 +642,24 @@ def main():
 
     nch = n_chunks_of(x)
     wk = algorithmic_work(x, nch)
+    mm_bytes = method_min_bytes(x)
     if fused:
-        # one kernel does the chunk walk and the scan: its bytes are both kernels' bytes
-        dom_bytes, dom_ms, kname = wk["prep_bytes"] + wk["scan_bytes"], k_prep, "fused_fwd_kernel"
+        # one kernel does the whole forward: its algorithmic bytes are the method minimum
+        # (inputs and output once, h0 and ht once); the record round trip is the design's own
+        dom_bytes, dom_ms, kname = mm_bytes, k_prep, "fused_fwd_kernel"
+        design_bytes = wk["prep_bytes"] + wk["scan_bytes"]
     else:
+        # the split path: the dominant kernel's own reads and writes (its record traffic included)
         dominant = "chunk" if k_prep >= k_scan else "scan"
         dom_bytes = wk["prep_bytes"] if dominant == "chunk" else wk["scan_bytes"]
         dom_ms = k_prep if dominant == "chunk" else k_scan
         kname = "chunk_prep_kernel" if dominant == "chunk" else "state_scan_kernel"
+        design_bytes = dom_bytes
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles(kname)
+    counters = counters_from_profiles(kname) or {}
+    traffic = counters.get("hbm_bytes_per_launch")
     total_flops = wk["prep_flops"] + wk["scan_flops"]
+    chain = chain_latency(kda, dev, torch, x, dom_ms) if fused and not args.no_extra else None
     res = {
         "metric": "KDA fwd tokens/s @ H=32,d=128, 8192-token fixed+varlen; % bf16 MFMA peak",
         "value": round(value, 1) if ok and not args.no_verify else None,
@@ -575,10 +674,24 @@ def main():
         "dtype": "f16xf32",
         "data": "synthetic",
         "config": {"workload": x.name, "global_batch": B, "seq_len": T, "heads": H, "dk": dk, "dv": dv,
-                   "io_dtype": x.dtype, "parallelism": "single-gpu"},
+                   "io_dtype": x.dtype, "parallelism": "single-gpu",
+                   "value_is": "tokens/s of this workload alone; the geomean over the three 8,192-token "
+                               "workloads (fixed, varlen uniform, varlen skewed) is "
+                               "geomean_fixed_varlen_tokens_per_s"},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes": dom_bytes},
+                     "traffic": traffic, "algorithmic_bytes": int(dom_bytes),
+                     "algorithmic_basis": ("method minimum: q, k, v, g, beta read once, out written once, "
+                                           "h0 read and ht written once (1,538 B per token and head at "
+                                           "d = 128, bf16)") if fused else
+                                          "the kernel's own reads and writes, its chunk records included",
+                     "kernel_ms": round(float(dom_ms), 5),
+                     "design_bytes": int(design_bytes),
+                     "design_frac": round(design_bytes / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "mfma_util_pct": counters.get("MfmaUtil"), "valu_busy_pct": counters.get("VALUBusy"),
+                     "counters_note": "traffic, mfma_util_pct and valu_busy_pct from profiles/traffic.json "
+                                      "(rocprofv3 counters of the same kernel sources), null when stale"},
+        "chain_latency": chain,
         "kernels_ms": ({"chunk_map": round(float(k_map), 5), "fused_fwd": round(float(k_prep), 5)} if fused else
                        {"chunk_map": round(float(k_map), 5), "chunk_prep": round(float(k_prep), 5),
                         "state_scan": round(float(k_scan), 5)}),

@@ -350,6 +350,10 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   uint8_t* bwx = smem + SM::X;                                     // [NTK][2][64] f16x8
   uint8_t* bux = smem + SM::X + SM::BWX;                           // [NTV][2][64] f16x8
   float* Lm = reinterpret_cast<float*>(smem + SM::Y);              // [64][LP]
+  // K~^T halves on their way to one 16-byte record store per lane, in the L buffer (free
+  // between barriers #3 and #5a): [hf][token block pair][pair half][j][lane] x f16x4
+  f16x4* ktx = reinterpret_cast<f16x4*>(smem + SM::Y);
+  static_assert(2 * 2 * 2 * (2 * (DK / 64)) * 64 * 8 <= SM::MAT, "K~^T exchange must fit the L buffer");
   float* et = reinterpret_cast<float*>(smem + SM::Z);              // [19][DK]
   float* Tm = reinterpret_cast<float*>(smem + SM::Z);              // [64][LP]
   float* gend = reinterpret_cast<float*>(smem + SM::GE);           // [16][DK]
@@ -590,13 +594,16 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
         y[e] = (_Float16)YC[8 * sl + e];
       }
       rec_store<WT, R::BYTES>(rec, R::Q + ((size_t)(w * KSK + s) * 64 + l) * 16, qf);
-      // K~^T fragments: (K~ I) holds, per lane, key channel 16 ct + t at tokens 16 w + 4 gq + r
+      // K~^T fragments: (K~ I) holds, per lane, key channel 16 ct + t at tokens 16 w + 4 gq + r,
+      // ct = 2 s + hh.  The 16-byte record fragment of (ct, token pair w / 2) joins the halves of
+      // token blocks 2 (w / 2) and 2 (w / 2) + 1: both go to LDS here, and after barrier #4 each
+      // wave of the pair stores half of the pair's fragments whole (one 16-byte store per lane).
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const f32x4 c = mfma16(kf, ident[hh], zero4());
-        const int ct = 2 * s + hh;
+        const int j = 2 * sl + hh;
         f16x4 h4 = {(_Float16)c[0], (_Float16)c[1], (_Float16)c[2], (_Float16)c[3]};
-        rec_store<WT, R::BYTES>(rec, R::KT + ((size_t)(ct * 2 + (w >> 1)) * 64 + l) * 16 + (w & 1) * 8, h4);
+        ktx[((((hf * 2 + (w >> 1)) * 2 + (w & 1)) * (2 * KH) + j) * 64) + l] = h4;
       }
       // column-side operands of the off-diagonal Gram tiles (reference = end of block w)
       ybf[(w * KSK + s) * 64 + l] = y;  // block 3's slot is never read (no branch around the store)
@@ -619,6 +626,17 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   }
   __syncthreads();  // #4: column operands visible
   mid(3);
+
+  // whole K~^T fragments: this wave of the pair stores j = (w & 1) KH .. (w & 1) KH + KH - 1
+#pragma unroll
+  for (int jj = 0; jj < KH; ++jj) {
+    const int j = (w & 1) * KH + jj;             // wave-uniform
+    const int ct = 2 * (sb + (j >> 1)) + (j & 1);
+    const f16x4 lo = ktx[((((hf * 2 + (w >> 1)) * 2 + 0) * (2 * KH) + j) * 64) + l];
+    const f16x4 hi = ktx[((((hf * 2 + (w >> 1)) * 2 + 1) * (2 * KH) + j) * 64) + l];
+    const f16x8 frag = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    rec_store<WT, R::BYTES>(rec, R::KT + ((size_t)(ct * 2 + (w >> 1)) * 64 + l) * 16, frag);
+  }
 
   // ---------------- (b) Gram matrices L (row block w) and Aqk^T (column block w) ----------------
   // Partial sums over this half's channels.  offL[b]: L tile (w, b) and offA[b]: Aqk^T
