@@ -11,11 +11,13 @@ import re
 import torch  # loaded first so the library binds to the HIP runtime torch uses
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkda.so")
+# KDA_LIBRARY=path loads another build of this same library (the CPU sanitizer test loads a
+# build whose host code carries AddressSanitizer and UndefinedBehaviorSanitizer)
+LIB_PATH = os.environ.get("KDA_LIBRARY") or os.path.join(_PKG, "libkda.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "kda.h")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libkda.so is not built: run __graft_entry__.build() (hipcc, gfx950) first")
+    raise ImportError("%s is not built: run __graft_entry__.build() (hipcc, gfx950) first" % LIB_PATH)
 _lib = ctypes.CDLL(LIB_PATH)
 
 KDA_BF16, KDA_F32 = 0, 1

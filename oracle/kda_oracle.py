@@ -22,24 +22,29 @@ _LIB = os.path.join(_HERE, "libkda_oracle.so")
 _lib = None
 
 
-def build_oracle(force=False):
-    """Compile kda_oracle.c with gcc (fp64, OpenMP) into libkda_oracle.so."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
+def build_oracle(force=False, out=None, extra_flags=()):
+    """Compile kda_oracle.c with gcc (fp64, OpenMP) into libkda_oracle.so (or into `out`, with
+    `extra_flags` added: the CPU sanitizer test builds an instrumented copy this way)."""
+    target = out or _LIB
+    if force or out or not os.path.exists(target) or os.path.getmtime(target) < os.path.getmtime(_SRC):
+        tmp = target + ".tmp%d" % os.getpid()
         # -ffp-contract=off keeps each multiply and add separately rounded, as written.
-        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC",
-               "-o", tmp, _SRC, "-lm"]
+        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC"] + list(extra_flags)
+        cmd += ["-o", tmp, _SRC, "-lm"]
         subprocess.check_call(cmd)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, target)
+    return target
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build_oracle()
-        lib = ctypes.CDLL(_LIB)
+        path = os.environ.get("KDA_ORACLE_LIBRARY")  # another build of kda_oracle.c (sanitizer test)
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build_oracle()
+        lib = ctypes.CDLL(path)
         p = ctypes.c_void_p
         lib.kda_oracle_fwd.argtypes = [ctypes.c_int64, p, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_int64, p, p, p, p, p, p, ctypes.c_double, p, p,
