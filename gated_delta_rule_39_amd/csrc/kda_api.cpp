@@ -348,7 +348,14 @@ kda_status_t kda_decode(const kda_problem_t* prob, const void* q, const void* k,
 // column part's row sums (dqhat, dkhat, dg, dbeta).
 struct BwdCarve {
   size_t info, table, seq_off, seq_order, rec, ckpt, delta, psum, total;
+  size_t cb_fac, cb_st, cb_total;  // chunkwise form
 };
+
+// The token walk instead of the chunkwise form: KDA_BWD_WALK=1.
+static bool bwd_walk() {
+  const char* env = std::getenv("KDA_BWD_WALK");
+  return env && env[0] == '1';
+}
 
 // Value columns per wave of the backward walk: 4 once 32-column parts give every compute
 // unit a workgroup (less work per column), else 2 (16-column parts, twice the workgroups).
@@ -371,6 +378,11 @@ static BwdCarve bwd_carve(const kda_problem_t* p, int64_t N, int64_t n_chunk_ub)
   c.delta = c.ckpt + align256((size_t)n_chunk_ub * 8 * p->heads * state);
   c.psum = c.delta + align256(rows * p->dv * 4);
   c.total = c.psum + align256(parts * rows * (3 * (size_t)p->dk + 4) * 4);
+  const size_t items = (size_t)n_chunk_ub * p->heads;
+  c.cb_fac = c.rec;
+  c.cb_st = c.cb_fac + align256(items * kda::chunk_bwd_factor_floats(p->dk, p->dv) * 4);
+  c.cb_total = c.cb_st + align256(items * kda::chunk_bwd_state_floats(p->dk, p->dv) * 4);
+  if (c.cb_total > c.total) c.total = c.cb_total;
   return c;
 }
 
@@ -438,6 +450,9 @@ kda_status_t kda_bwd(const kda_problem_t* prob, const void* q, const void* k, co
   p.delta = reinterpret_cast<float*>(ws + c.delta);
   p.psum = reinterpret_cast<float*>(ws + c.psum);
   p.wcols = bwd_wcols(prob, N);
+  p.chunked = bwd_walk() ? 0 : 1;
+  p.cb_fac = reinterpret_cast<float*>(ws + c.cb_fac);
+  p.cb_st = reinterpret_cast<float*>(ws + c.cb_st);
   hipError_t e = kda::launch_backward(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -2,6 +2,9 @@
 #include "kda_launch.h"
 
 #include <atomic>
+#include <mutex>
+#include <utility>
+#include <vector>
 
 #include "kda_chunkmap.h"
 #include "kda_prep.h"
@@ -9,6 +12,7 @@
 #include "kda_fused.h"
 #include "kda_recurrent.h"
 #include "kda_recurrent_bwd.h"
+#include "kda_chunk_bwd.h"
 
 namespace kda {
 
@@ -20,19 +24,29 @@ size_t record_bytes(int dk, int dv) {
   return 0;
 }
 
-// Raises a kernel's dynamic LDS limit once per device (the attribute persists; setting it
-// on every call cost host time on the launch path).
+// Raises a kernel's dynamic LDS limit once per (kernel, device) (the attribute persists;
+// setting it on every call cost host time on the launch path).
 template <typename K>
 static hipError_t allow_smem(K kern, size_t smem) {
-  static std::atomic<uint64_t> done{0};
+  static std::mutex mu;
+  static std::vector<std::pair<const void*, uint64_t>> done;  // kernel, bit set of devices
+  const void* key = reinterpret_cast<const void*>(kern);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
-  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
-  return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& d : done)
+    if (d.first == key && (d.second & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(key, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  for (auto& d : done)
+    if (d.first == key) {
+      d.second |= bit;
+      return hipSuccess;
+    }
+  done.emplace_back(key, bit);
+  return hipSuccess;
 }
 
 static void mark(const ForwardPlan& p, int i, hipStream_t stream) {
@@ -238,9 +252,76 @@ static hipError_t launch_backward_t(const BackwardPlan& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int DK, int DV, typename InT>
+static hipError_t launch_chunk_backward_t(const BackwardPlan& p, hipStream_t stream) {
+  using WS = CbWs<DK, DV>;
+  CbArgs a;
+  a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.beta = p.beta; a.h0 = p.h0;
+  a.cu = p.cu;
+  a.info = p.info;
+  a.table = reinterpret_cast<const ChunkEntry*>(p.table);
+  a.seq_off = p.seq_off;
+  a.dout = p.dout; a.dht = p.dht;
+  a.dq = p.dq; a.dk = p.dk_; a.dv = p.dv_; a.dg = p.dg; a.dbeta = p.dbeta; a.dh0 = p.dh0;
+  const int64_t items = p.n_chunk_ub * (int64_t)p.H;
+  float* f = p.cb_fac;
+  a.W = f; f += (size_t)items * WS::W;
+  a.U = f; f += (size_t)items * WS::U;
+  a.KdT = f; f += (size_t)items * WS::KDT;
+  a.QgT = f; f += (size_t)items * WS::QGT;
+  a.PT = f; f += (size_t)items * WS::PT;
+  a.L = f; f += (size_t)items * WS::L;
+  a.TT = f; f += (size_t)items * WS::TT;
+  a.eGn = f;
+  a.st = p.cb_st;
+  a.T = p.T; a.N = p.N; a.nc = p.cu ? 0 : (p.T + kChunk - 1) / kChunk;
+  a.n_chunk_ub = p.n_chunk_ub;
+  a.H = p.H; a.scale = p.scale;
+  hipError_t e = hipSuccess;
+  if (items > 0) {
+    auto fac = cb_factor_kernel<DK, DV, InT>;
+    const size_t smem = CbFacSmem<DK>::BYTES;
+    if ((e = allow_smem(fac, smem)) != hipSuccess) return e;
+    hipLaunchKernelGGL(fac, dim3((unsigned)items), dim3(256), smem, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int64_t chains = p.N * (int64_t)p.H * (DV / 16);
+  hipLaunchKernelGGL((cb_state_fwd_kernel<DK, DV>), dim3((unsigned)chains), dim3(256), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((cb_state_rev_kernel<DK, DV, InT>), dim3((unsigned)chains), dim3(256), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (items > 0) {
+    hipLaunchKernelGGL((cb_grad_a_kernel<DK, DV, InT>), dim3((unsigned)items), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    auto gb = cb_grad_b_kernel<DK, DV, InT>;
+    const size_t smem = CbGradSmem<DK>::BYTES;
+    if ((e = allow_smem(gb, smem)) != hipSuccess) return e;
+    hipLaunchKernelGGL(gb, dim3((unsigned)items), dim3(256), smem, stream, a);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
 template <int DK, int DV>
 static hipError_t launch_backward_dt(const BackwardPlan& p, hipStream_t stream) {
+  if (p.chunked)
+    return p.dtype == 0 ? launch_chunk_backward_t<DK, DV, uint16_t>(p, stream)
+                        : launch_chunk_backward_t<DK, DV, float>(p, stream);
   return p.dtype == 0 ? launch_backward_t<DK, DV, uint16_t>(p, stream) : launch_backward_t<DK, DV, float>(p, stream);
+}
+
+size_t chunk_bwd_factor_floats(int dk, int dv) {
+  if (dk == 64 && dv == 64) return CbWs<64, 64>::FACTOR_FLOATS;
+  if (dk == 64 && dv == 128) return CbWs<64, 128>::FACTOR_FLOATS;
+  if (dk == 128 && dv == 64) return CbWs<128, 64>::FACTOR_FLOATS;
+  return CbWs<128, 128>::FACTOR_FLOATS;
+}
+
+size_t chunk_bwd_state_floats(int dk, int dv) {
+  if (dk == 64 && dv == 64) return CbWs<64, 64>::SB;
+  if (dk == 64 && dv == 128) return CbWs<64, 128>::SB;
+  if (dk == 128 && dv == 64) return CbWs<128, 64>::SB;
+  return CbWs<128, 128>::SB;
 }
 
 int backward_parts(int dv, int wcols) { return dv / (kBwdWaves * wcols); }

@@ -62,7 +62,15 @@ struct BackwardPlan {
   float* delta;                                           // v - a^T khat of every token
   float* psum;                                            // per-part row sums
   int32_t wcols;                                          // value columns per wave (2 or 4)
+  // chunkwise form (used when chunked != 0): per-(chunk, head) factors and state blocks
+  int32_t chunked;
+  float* cb_fac;                                          // items * chunk_bwd_factor_floats
+  float* cb_st;                                           // items * chunk_bwd_state_floats
 };
+
+// fp32 words per (chunk, head) item of the chunkwise backward: its factors and its state block.
+size_t chunk_bwd_factor_floats(int dk, int dv);
+size_t chunk_bwd_state_floats(int dk, int dv);
 
 hipError_t launch_backward(const BackwardPlan& p, hipStream_t stream);
 
