@@ -59,6 +59,35 @@ __device__ inline f32x4 mfma_f32(float a, float b, const f32x4& c) {
 
 __device__ inline float cb_exp(float x) { return exp2_hw(x * kLog2e); }
 
+// Buffer loads: a resource over one chunk's array (uniform, in scalar registers) and 32-bit
+// byte offsets per lane.  Per-lane 64-bit addresses of loads inside the chunk loops would be
+// strength-reduced into pointers that stay live across the loop; these offsets do not
+// change with the chunk.  Loads past `bytes` return 0.
+__device__ inline __amdgpu_buffer_rsrc_t cb_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferFlags);
+}
+__device__ inline float cb_ld1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ inline float4 cb_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const uint4_v v = __builtin_bit_cast(uint4_v, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+// one element of the io dtype as fp32
+__device__ inline float cb_ld_io(__amdgpu_buffer_rsrc_t r, uint32_t idx, const uint16_t*) {
+  return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, (int)(idx * 2), 0, 0));
+}
+__device__ inline float cb_ld_io(__amdgpu_buffer_rsrc_t r, uint32_t idx, const float*) {
+  return cb_ld1(r, idx * 4);
+}
+// four consecutive elements of the io dtype as fp32
+__device__ inline float4 cb_ld4_io(__amdgpu_buffer_rsrc_t r, uint32_t idx, const uint16_t*) {
+  const uint2_v v = __builtin_bit_cast(uint2_v, __builtin_amdgcn_raw_buffer_load_b64(r, (int)(idx * 2), 0, 0));
+  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+                     __uint_as_float(v.y & 0xffff0000u));
+}
+__device__ inline float4 cb_ld4_io(__amdgpu_buffer_rsrc_t r, uint32_t idx, const float*) { return cb_ld4(r, idx * 4); }
+
 // Tile list of the lower 4 x 4 block triangle: diagonal blocks first, then by distance.
 __device__ __host__ constexpr int cb_tile_i(int p) {
   return p < 4 ? p : p < 7 ? p - 3 : p < 9 ? p - 5 : 3;
@@ -151,14 +180,15 @@ __device__ inline void cb_chunks(const CbArgs& a, int64_t n, int64_t& c0, int64_
 // LDS rows of the chunk: unit q and unit k (rows past the chunk's end are zero), the
 // in-chunk cumulative gate G (constant past the end), beta (zero past the end), and per
 // token the norm data of q and k: |x| 2^-ex and ex, after the same exact power-of-two
-// rescale as the forward kernels.  256 threads; row stride KS = DK + 4 floats.
-template <int DK, typename InT>
+// rescale as the forward kernels.  NT threads (256 or 512); row stride KS = DK + 4 floats.
+template <int DK, typename InT, int NT = 256>
 __device__ void cb_load_rows(const CbArgs& a, const CbItem& it, int h, float* kh, float* qh, float* G,
                              float* bs, float* nrm) {
   constexpr int KS = DK + 4;
-  constexpr int CH = DK / 4;  // channels per thread
+  constexpr int TP = NT / 64;   // threads per token
+  constexpr int CH = DK / TP;  // channels per thread
   const int tid = threadIdx.x;
-  const int t = tid >> 2, p = tid & 3;
+  const int t = tid / TP, p = tid % TP;
   const bool valid = t < it.len;
   const int64_t row = (it.tok0 + t) * a.H + h;
 #pragma unroll
@@ -175,8 +205,8 @@ __device__ void cb_load_rows(const CbArgs& a, const CbItem& it, int h, float* kh
     float m = 0.f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) m = fmaxf(m, fabsf(x[c]));
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
+#pragma unroll
+    for (int o = 1; o < TP; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
     const int ex = m > 0.f ? ilogb_pos(m) : 0;
     float ss = 0.f;
 #pragma unroll
@@ -184,8 +214,8 @@ __device__ void cb_load_rows(const CbArgs& a, const CbItem& it, int h, float* kh
       x[c] = ldexpf(x[c], -ex);
       ss = fmaf(x[c], x[c], ss);
     }
-    ss += __shfl_xor(ss, 1);
-    ss += __shfl_xor(ss, 2);
+#pragma unroll
+    for (int o = 1; o < TP; o <<= 1) ss += __shfl_xor(ss, o);
     const float nv = sqrtf(ss);
     float* dst = (which ? kh : qh) + t * KS + p * CH;
 #pragma unroll
@@ -203,14 +233,39 @@ __device__ void cb_load_rows(const CbArgs& a, const CbItem& it, int h, float* kh
     }
   }
   if (tid < 64) bs[tid] = tid < it.len ? load1(reinterpret_cast<const InT*>(a.beta) + (it.tok0 + tid) * a.H + h) : 0.f;
-  if (tid < DK) {
-    const float* gsrc = a.g + (it.tok0 * a.H + h) * DK + tid;
-    const int64_t step = (int64_t)a.H * DK;
+  // g: coalesced 16-byte loads of the chunk's rows into LDS (rows past the end are 0), then
+  // the cumulative sum down each channel in PT parts of 64 / PT tokens, each part adding
+  // the totals of the parts before it
+  {
+    constexpr int C4 = DK / 4;
+    const auto gr = cb_rsrc(a.g + (it.tok0 * a.H + h) * DK, (uint32_t)(((it.len - 1) * a.H * DK + DK) * 4));
+#pragma unroll
+    for (int j = 0; j < 64 * C4 / NT; ++j) {
+      const int e4 = tid + NT * j;
+      const int t = e4 / C4, c4 = e4 - t * C4;
+      const float4 v4 = cb_ld4(gr, (uint32_t)((t * a.H * DK + 4 * c4) * 4));
+      *reinterpret_cast<float4*>(G + t * KS + 4 * c4) = v4;
+    }
+  }
+  __syncthreads();
+  {
+    constexpr int PT = NT / DK, TL = 64 / PT;
+    const int c = tid % DK, part = tid / DK;
     float acc = 0.f;
-#pragma unroll 16
-    for (int u = 0; u < 64; ++u) {
-      acc += u < it.len ? gsrc[u * step] : 0.f;
-      G[u * KS + tid] = acc;
+#pragma unroll
+    for (int u = 0; u < TL; ++u) {
+      acc += G[(part * TL + u) * KS + c];
+      G[(part * TL + u) * KS + c] = acc;
+    }
+    __syncthreads();
+    float carry = 0.f;
+#pragma unroll
+    for (int p = 0; p < PT - 1; ++p)
+      if (p < part) carry += G[(p * TL + TL - 1) * KS + c];
+    __syncthreads();
+    if (part > 0) {
+#pragma unroll
+      for (int u = 0; u < TL; ++u) G[(part * TL + u) * KS + c] += carry;
     }
   }
 }
@@ -299,13 +354,14 @@ __device__ void cb_gram_block(const float* kh, const float* qh, const float* G, 
   }
 }
 
+// DK / 16 waves (two per SIMD at DK = 128).
 template <int DK, int DV, typename InT>
-__global__ __launch_bounds__(256) void cb_factor_kernel(CbArgs a) {
+__global__ __launch_bounds__(DK * 4) void cb_factor_kernel(CbArgs a) {
   extern __shared__ __align__(16) float sm[];
   using S = CbFacSmem<DK>;
   using WS = CbWs<DK, DV>;
   constexpr int KS = S::KS;
-  constexpr int KR = DK / 64, VR = DV / 64;  // 16-wide tiles per wave
+  constexpr int NW = DK / 16, NT = DK * 4, NTK = DK / 16, NTV = DV / 16;
   const int64_t item = blockIdx.x;
   const int64_t c = item / a.H;
   const int h = (int)(item - c * a.H);
@@ -319,19 +375,19 @@ __global__ __launch_bounds__(256) void cb_factor_kernel(CbArgs a) {
   float* Ts = sm + S::TI;
   float* bs = sm + S::BETA;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, gq = l >> 4;
-  for (int i = tid; i < 3 * 64 * 64 / 4; i += 256)
+  for (int i = tid; i < 3 * 64 * 64 / 4; i += NT)
     reinterpret_cast<float4*>(Ls)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  cb_load_rows<DK, InT>(a, it, h, kh, qh, G, bs, nullptr);
+  cb_load_rows<DK, InT, NT>(a, it, h, kh, qh, G, bs, nullptr);
   __syncthreads();
 
-  // 1. gated Grams, 10 blocks over the four waves
-  for (int p = w; p < 10; p += 4) cb_gram_block<DK>(kh, qh, G, cb_tile_i(p), cb_tile_j(p), Ls, Ps);
+  // 1. gated Grams, 10 blocks over the waves
+  for (int p = w; p < 10; p += NW) cb_gram_block<DK>(kh, qh, G, cb_tile_i(p), cb_tile_j(p), Ls, Ps);
   __syncthreads();
 
   // 2. T = (I + diag(beta) L)^-1: diagonal blocks by substitution (wave w: block w, lane
   // column lr), then the off-diagonal blocks by distance from the diagonal:
   // T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, with A = diag(beta) L
-  {
+  if (w < 4) {
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -369,20 +425,25 @@ __global__ __launch_bounds__(256) void cb_factor_kernel(CbArgs a) {
     __syncthreads();
   }
 
-  // 3. W = T X (X = diag(beta) khat e^G) and U = T Y (Y = diag(beta) V); wave w owns KR
-  // key tiles and VR value tiles
+  // 3. W = T X (X = diag(beta) khat e^G) and U = T Y (Y = diag(beta) V), 16-column tiles
+  // over the waves (the key tiles of W, then the value tiles of U)
   float* Wo = a.W + item * WS::W;
   float* Uo = a.U + item * WS::U;
-#pragma unroll
-  for (int r = 0; r < KR; ++r) {
-    const int cc = 16 * (w * KR + r) + lr;
+  for (int tile = w; tile < NTK + NTV; tile += NW) {
+    const bool isw = tile < NTK;
+    const int cc = 16 * (isw ? tile : tile - NTK) + lr;
     float X[4][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = 16 * kt + 4 * gq + e;
-        X[kt][e] = bs[j] * kh[j * KS + cc] * cb_exp(G[j * KS + cc]);
+        if (isw) {
+          X[kt][e] = bs[j] * kh[j * KS + cc] * cb_exp(G[j * KS + cc]);
+        } else {
+          X[kt][e] = j < it.len ? bs[j] * load1(reinterpret_cast<const InT*>(a.v) + ((it.tok0 + j) * a.H + h) * DV + cc)
+                                : 0.f;
+        }
       }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -396,41 +457,20 @@ __global__ __launch_bounds__(256) void cb_factor_kernel(CbArgs a) {
         acc = mfma_f32(tv.w, X[kt][3], acc);
       }
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) Wo[(16 * mt + 4 * gq + ii) * DK + cc] = acc[ii];
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < VR; ++r) {
-    const int cv = 16 * (w * VR + r) + lr;
-    float Y[4][4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = 16 * kt + 4 * gq + e;
-        Y[kt][e] = j < it.len ? bs[j] * load1(reinterpret_cast<const InT*>(a.v) + ((it.tok0 + j) * a.H + h) * DV + cv)
-                              : 0.f;
+      for (int ii = 0; ii < 4; ++ii) {
+        if (isw) {
+          Wo[(16 * mt + 4 * gq + ii) * DK + cc] = acc[ii];
+        } else {
+          Uo[(16 * mt + 4 * gq + ii) * DV + cc] = acc[ii];
+        }
       }
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kt = 0; kt <= mt; ++kt) {
-        const float4 tv = *reinterpret_cast<const float4*>(Ts + (16 * mt + lr) * 64 + 16 * kt + 4 * gq);
-        acc = mfma_f32(tv.x, Y[kt][0], acc);
-        acc = mfma_f32(tv.y, Y[kt][1], acc);
-        acc = mfma_f32(tv.z, Y[kt][2], acc);
-        acc = mfma_f32(tv.w, Y[kt][3], acc);
-      }
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) Uo[(16 * mt + 4 * gq + ii) * DV + cv] = acc[ii];
     }
   }
 
   // 4. Kd^T, Qg^T, e^G_n, P^T, L, T^T
   float* kdt = a.KdT + item * WS::KDT;
   float* qgt = a.QgT + item * WS::QGT;
-  for (int idx = tid; idx < DK * 16; idx += 256) {
+  for (int idx = tid; idx < DK * 16; idx += NT) {
     const int cc = idx >> 4, t4 = (idx & 15) * 4;
     const float gn = G[63 * KS + cc];
     float kd[4], qg[4];
@@ -447,7 +487,7 @@ __global__ __launch_bounds__(256) void cb_factor_kernel(CbArgs a) {
   float* pt = a.PT + item * WS::PT;
   float* tt = a.TT + item * WS::TT;
   float* lo = a.L + item * WS::L;
-  for (int idx = tid; idx < 64 * 16; idx += 256) {
+  for (int idx = tid; idx < 64 * 16; idx += NT) {
     const int j = idx >> 4, i4 = (idx & 15) * 4;
     *reinterpret_cast<float4*>(pt + j * 64 + i4) =
         make_float4(Ps[i4 * 64 + j], Ps[(i4 + 1) * 64 + j], Ps[(i4 + 2) * 64 + j], Ps[(i4 + 3) * 64 + j]);
@@ -458,107 +498,256 @@ __global__ __launch_bounds__(256) void cb_factor_kernel(CbArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// cb_state_fwd_kernel: S0 of every chunk.  Workgroup = (sequence, head, 16 value columns);
-// wave w owns key rows [w DK/4, (w+1) DK/4).
+// State scans.  Workgroup = (sequence, head, 16 value columns) with DK / 16 waves: wave w
+// owns key rows [16 w, 16 w + 16) of the slice's state, one C tile.  A step adds the
+// waves' partial sums over key rows through LDS (two buffers, one barrier per step); the
+// next chunk's factors are loaded while the current chunk is processed.  When the count of
+// (sequence, head) pairs is a multiple of 8, the slices of a pair run on one compute die
+// (workgroups are dealt to the 8 dies in turn), where they share its L2.
+
+// LDS of a scan workgroup: the waves' partial tiles [2 buffers][NW waves][4 token tiles][64]
+// and the summed tiles [2 buffers][4 token tiles][64], f32x4.  A step writes its partials,
+// waves 0..3 each add up one token tile (in wave order) after a barrier, and after a second
+// barrier every wave reads the four sums.
+template <int DK>
+struct CbScanSmem {
+  static constexpr int NW = DK / 16;
+  static constexpr int PART = 0;
+  static constexpr int SUM = 2 * NW * 4 * 64;  // in f32x4
+  static constexpr size_t BYTES = (SUM + 2 * 4 * 64) * 16;
+};
+
+// Sum of the NW waves' partial tiles in wave order, every read issued before the adds.
+template <int NW>
+__device__ inline f32x4 cb_red_sum(const f32x4* part, int buf, int mt, int l) {
+  f32x4 p[NW];
+#pragma unroll
+  for (int v = 0; v < NW; ++v) p[v] = part[((buf * NW + v) * 4 + mt) * 64 + l];
+  f32x4 sum = p[0];
+#pragma unroll
+  for (int v = 1; v < NW; ++v) sum += p[v];
+  return sum;
+}
+
+__device__ inline void cb_scan_slot(int64_t wg, int64_t pairs, int ns, int64_t& nh, int& s) {
+  if ((pairs & 7) == 0) {
+    const int64_t j = wg >> 3;
+    nh = (wg & 7) + 8 * (j / ns);
+    s = (int)(j % ns);
+  } else {
+    nh = wg / ns;
+    s = (int)(wg % ns);
+  }
+}
+
+// One chunk's operands of the forward scan for wave w (key rows 16 w ..).
+struct CbFwdOps {
+  float4 w[4];    // W[16 mt + lr][16 w + 4 gq + e]          A of W S
+  float u[4];     // U[16 w + 4 gq + i][col] (waves 0..3)     C tile of U
+  float4 kd[4];   // Kd^T[16 w + lr][16 mt + 4 gq + e]        A of Kd^T D
+  float4 eg;      // e^G_n[16 w + 4 gq + i]
+};
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void cb_state_fwd_kernel(CbArgs a) {
+__device__ inline void cb_fwd_load(const CbArgs& a, int64_t item, int w, int l, int col, CbFwdOps& o) {
   using WS = CbWs<DK, DV>;
-  constexpr int NS = DV / 16;
-  constexpr int RT = DK / 64;
-  __shared__ f32x4 red[2][4][4][64];
+  const unsigned lr = l & 15, gq = l >> 4;
+  const auto Wr = cb_rsrc(a.W + item * WS::W, WS::W * 4);
+  const auto Ur = cb_rsrc(a.U + item * WS::U, WS::U * 4);
+  const auto Kr = cb_rsrc(a.KdT + item * WS::KDT, WS::KDT * 4);
+  const auto Er = cb_rsrc(a.eGn + item * WS::EGN, WS::EGN * 4);
+#pragma unroll
+  for (unsigned mt = 0; mt < 4; ++mt) {
+    o.w[mt] = cb_ld4(Wr, 4 * ((16 * mt + lr) * DK + 16 * w + 4 * gq));
+    o.kd[mt] = cb_ld4(Kr, 4 * ((16 * w + lr) * 64 + 16 * mt + 4 * gq));
+  }
+  // waves 4.. read past the end of U (zeros): no branch around the loads
+#pragma unroll
+  for (unsigned ii = 0; ii < 4; ++ii) o.u[ii] = cb_ld1(Ur, 4 * ((16 * w + 4 * gq + ii) * DV + col));
+  o.eg = cb_ld4(Er, 4 * (16 * w + 4 * gq));
+}
+
+// cb_state_fwd_kernel: S0 of every chunk.
+template <int DK, int DV>
+__global__ __launch_bounds__(DK * 4) void cb_state_fwd_kernel(CbArgs a) {
+  using WS = CbWs<DK, DV>;
+  using SM = CbScanSmem<DK>;
+  constexpr int NW = DK / 16, NS = DV / 16;
+  extern __shared__ __align__(16) f32x4 red[];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, gq = l >> 4;
-  const int64_t wg = blockIdx.x;
-  const int s = (int)(wg % NS);
-  const int64_t nh = wg / NS;
+  int64_t nh;
+  int s;
+  cb_scan_slot(blockIdx.x, a.N * a.H, NS, nh, s);
   const int h = (int)(nh % a.H);
   const int64_t n = nh / a.H;
   int64_t c0, cnt;
   cb_chunks(a, n, c0, cnt);
   const int col = 16 * s + lr;
-  f32x4 S[RT];
+  const int row0 = 16 * w + 4 * gq;
+  f32x4 S;
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const int row0 = 16 * (w * RT + r) + 4 * gq;
+  for (int ii = 0; ii < 4; ++ii) S[ii] = a.h0 ? a.h0[((n * a.H + h) * DK + row0 + ii) * DV + col] : 0.f;
+  // S0 of chunk i + 1 is stored at the end of step i, after the step's waits for its loads,
+  // so no wait covers a store
+  auto store_s0 = [&](int64_t i) {
+    float* st = a.st + ((c0 + i) * a.H + h) * WS::SB;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-      S[r][ii] = a.h0 ? a.h0[((n * a.H + h) * DK + row0 + ii) * DV + col] : 0.f;
-  }
-  for (int64_t i = 0; i < cnt; ++i) {
-    const int64_t item = (c0 + i) * a.H + h;
-    float* st = a.st + item * WS::SB;
-    const float* Wi = a.W + item * WS::W;
-    const float* Ui = a.U + item * WS::U;
-    const float* Ki = a.KdT + item * WS::KDT;
-    const float* Ei = a.eGn + item * WS::EGN;
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const int row0 = 16 * (w * RT + r) + 4 * gq;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) st[WS::S0 + (row0 + ii) * DV + col] = S[r][ii];
-    }
-    // partial D over this wave's key rows
-    f32x4 Dp[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      Dp[mt] = zero4();
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const float4 wv = *reinterpret_cast<const float4*>(Wi + (16 * mt + lr) * DK + 16 * (w * RT + r) + 4 * gq);
-        Dp[mt] = mfma_f32(wv.x, S[r][0], Dp[mt]);
-        Dp[mt] = mfma_f32(wv.y, S[r][1], Dp[mt]);
-        Dp[mt] = mfma_f32(wv.z, S[r][2], Dp[mt]);
-        Dp[mt] = mfma_f32(wv.w, S[r][3], Dp[mt]);
-      }
-    }
+    for (int ii = 0; ii < 4; ++ii) st[WS::S0 + (unsigned)((row0 + ii) * DV + col)] = S[ii];
+  };
+  auto step = [&](const CbFwdOps& o, int64_t i) {
     const int buf = (int)(i & 1);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) red[buf][w][mt][l] = Dp[mt];
-    float uv[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) uv[mt][ii] = Ui[(16 * mt + 4 * gq + ii) * DV + col];
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 dp = zero4();
+      dp = mfma_f32(o.w[mt].x, S[0], dp);
+      dp = mfma_f32(o.w[mt].y, S[1], dp);
+      dp = mfma_f32(o.w[mt].z, S[2], dp);
+      dp = mfma_f32(o.w[mt].w, S[3], dp);
+      red[SM::PART + ((buf * NW + w) * 4 + mt) * 64 + l] = dp;
+    }
     __syncthreads();
-    f32x4 D[4];
+    if (w < 4) {  // D = U - W S, token tile w
+      const f32x4 sum = cb_red_sum<NW>(red + SM::PART, buf, w, l);
+      f32x4 D;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) D[ii] = o.u[ii] - sum[ii];
+      red[SM::SUM + (buf * 4 + w) * 64 + l] = D;
+    }
+    __syncthreads();
+    f32x4 Dt[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) Dt[mt] = red[SM::SUM + (buf * 4 + mt) * 64 + l];
+    f32x4 acc[2] = {f32x4{S[0] * o.eg.x, S[1] * o.eg.y, S[2] * o.eg.z, S[3] * o.eg.w}, zero4()};
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const f32x4 sum = ((red[buf][0][mt][l] + red[buf][1][mt][l]) + red[buf][2][mt][l]) + red[buf][3][mt][l];
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) D[mt][ii] = uv[mt][ii] - sum[ii];
+      acc[mt & 1] = mfma_f32(o.kd[mt].x, Dt[mt][0], acc[mt & 1]);
+      acc[mt & 1] = mfma_f32(o.kd[mt].y, Dt[mt][1], acc[mt & 1]);
+      acc[mt & 1] = mfma_f32(o.kd[mt].z, Dt[mt][2], acc[mt & 1]);
+      acc[mt & 1] = mfma_f32(o.kd[mt].w, Dt[mt][3], acc[mt & 1]);
     }
-    // S <- diag(e^G_n) S + Kd^T D on this wave's rows
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const int rb = 16 * (w * RT + r);
-      const float4 eg = *reinterpret_cast<const float4*>(Ei + rb + 4 * gq);
-      f32x4 acc = {S[r][0] * eg.x, S[r][1] * eg.y, S[r][2] * eg.z, S[r][3] * eg.w};
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const float4 kd = *reinterpret_cast<const float4*>(Ki + (rb + lr) * 64 + 16 * mt + 4 * gq);
-        acc = mfma_f32(kd.x, D[mt][0], acc);
-        acc = mfma_f32(kd.y, D[mt][1], acc);
-        acc = mfma_f32(kd.z, D[mt][2], acc);
-        acc = mfma_f32(kd.w, D[mt][3], acc);
-      }
-      S[r] = acc;
-    }
+    S = acc[0] + acc[1];
+    if (i + 1 < cnt) store_s0(i + 1);
+  };
+  // the next chunk's loads are issued unconditionally (past the last chunk they reload the
+  // last one), so the wait counts stay exact across the loop
+  CbFwdOps A, B;
+  auto load = [&](int64_t i, CbFwdOps& o) {
+    cb_fwd_load<DK, DV>(a, (c0 + (i < cnt ? i : cnt - 1)) * a.H + h, w, l, col, o);
+  };
+  if (cnt > 0) {
+    load(0, A);
+    store_s0(0);
+  }
+  for (int64_t i = 0; i < cnt; i += 2) {
+    load(i + 1, B);
+    step(A, i);
+    if (i + 1 >= cnt) break;
+    load(i + 2, A);
+    step(B, i + 1);
   }
 }
 
-// ---------------------------------------------------------------------------------------
-// cb_state_rev_kernel: Hn and dD of every chunk, walking backwards; dh0.
+// One chunk's operands of the reverse scan for wave w (key rows 16 w ..).  The terms that
+// do not involve Hn (scale Qg^T dO on the wave's rows; scale P^T dO, split over the waves:
+// token tile w % 4 of the contraction, output token tiles w / 4 + q NW / 4) are formed
+// from their loads after the previous chunk's step, so only their results stay live.
+template <int DK>
+struct CbRevOps {
+  static constexpr int MP = 16 / (DK / 16);
+  float kd[4][4];   // Kd[16 mt + lr][16 w + 4 gq + e]           A of Kd Hn
+  float wt[4][4];   // W[16 kt + 4 gq + e][16 w + lr]             A of W^T dD
+  float4 eg;        // e^G_n[16 w + 4 gq + i]
+  f32x4 qacc;       // scale Qg^T dO on the wave's rows
+  f32x4 pp[MP];     // scale P^T dO, the wave's share
+};
+template <int DK>
+struct CbRevRaw {
+  static constexpr int MP = CbRevOps<DK>::MP;
+  float4 qg[4];     // Qg^T[16 w + lr][16 kt + 4 gq + e]
+  float4 pt[MP];    // P^T[16 mt + lr][16 (w % 4) + 4 gq + e]
+  float dob[4][4];  // scale dO[16 kt + 4 gq + e][col]
+};
 
 template <int DK, int DV, typename InT>
-__global__ __launch_bounds__(256) void cb_state_rev_kernel(CbArgs a) {
+__device__ inline void cb_rev_load(const CbArgs& a, int64_t item, int h, int64_t t0, int64_t len, int w, int l,
+                                   int col, CbRevOps<DK>& o, CbRevRaw<DK>& r) {
   using WS = CbWs<DK, DV>;
-  constexpr int NS = DV / 16;
-  constexpr int RT = DK / 64;
-  __shared__ f32x4 red[2][4][4][64];
+  constexpr int NW = DK / 16;
+  const unsigned lr = l & 15, gq = l >> 4;
+  const auto Wr = cb_rsrc(a.W + item * WS::W, WS::W * 4);
+  const auto Kr = cb_rsrc(a.KdT + item * WS::KDT, WS::KDT * 4);
+  const auto Qr = cb_rsrc(a.QgT + item * WS::QGT, WS::QGT * 4);
+  const auto Pr = cb_rsrc(a.PT + item * WS::PT, WS::PT * 4);
+  const auto Er = cb_rsrc(a.eGn + item * WS::EGN, WS::EGN * 4);
+  // the chunk's rows of dout for the slice's 16 columns; tokens past the chunk's end fall
+  // outside the resource and read 0
+  const unsigned tstride = (unsigned)a.H * DV;
+  const auto Dr = cb_rsrc(reinterpret_cast<const InT*>(a.dout) + (t0 * a.H + h) * DV + (col & ~15),
+                          (uint32_t)(((len - 1) * tstride + 16) * sizeof(InT)));
+#pragma unroll
+  for (unsigned m = 0; m < 4; ++m) {
+    r.qg[m] = cb_ld4(Qr, 4 * ((16 * w + lr) * 64 + 16 * m + 4 * gq));
+#pragma unroll
+    for (unsigned e = 0; e < 4; ++e) {
+      o.kd[m][e] = cb_ld1(Kr, 4 * ((16 * w + 4 * gq + e) * 64 + 16 * m + lr));
+      o.wt[m][e] = cb_ld1(Wr, 4 * ((16 * m + 4 * gq + e) * DK + 16 * w + lr));
+      const unsigned t = 16 * m + 4 * gq + e;
+      r.dob[m][e] = a.scale * cb_ld_io(Dr, t * tstride + lr, (const InT*)nullptr);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < CbRevOps<DK>::MP; ++q) {
+    const unsigned mt = (unsigned)(w >> 2) + q * (NW / 4);
+    r.pt[q] = cb_ld4(Pr, 4 * ((16 * mt + lr) * 64 + 16 * (w & 3) + 4 * gq));
+  }
+  o.eg = cb_ld4(Er, 4 * (16 * w + 4 * gq));
+}
+
+template <int DK>
+__device__ inline void cb_rev_finish(int w, CbRevOps<DK>& o, const CbRevRaw<DK>& r) {
+  f32x4 q0 = zero4(), q1 = zero4();
+#pragma unroll
+  for (int kt = 0; kt < 4; kt += 2) {
+    q0 = mfma_f32(r.qg[kt].x, r.dob[kt][0], q0);
+    q1 = mfma_f32(r.qg[kt + 1].x, r.dob[kt + 1][0], q1);
+    q0 = mfma_f32(r.qg[kt].y, r.dob[kt][1], q0);
+    q1 = mfma_f32(r.qg[kt + 1].y, r.dob[kt + 1][1], q1);
+    q0 = mfma_f32(r.qg[kt].z, r.dob[kt][2], q0);
+    q1 = mfma_f32(r.qg[kt + 1].z, r.dob[kt + 1][2], q1);
+    q0 = mfma_f32(r.qg[kt].w, r.dob[kt][3], q0);
+    q1 = mfma_f32(r.qg[kt + 1].w, r.dob[kt + 1][3], q1);
+  }
+  o.qacc = q0 + q1;
+  float db[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    db[e] = r.dob[0][e];
+#pragma unroll
+    for (int kt = 1; kt < 4; ++kt)
+      if ((w & 3) == kt) db[e] = r.dob[kt][e];
+  }
+#pragma unroll
+  for (int q = 0; q < CbRevOps<DK>::MP; ++q) {
+    f32x4 pp = zero4();
+    pp = mfma_f32(r.pt[q].x, db[0], pp);
+    pp = mfma_f32(r.pt[q].y, db[1], pp);
+    pp = mfma_f32(r.pt[q].z, db[2], pp);
+    pp = mfma_f32(r.pt[q].w, db[3], pp);
+    o.pp[q] = pp;
+  }
+}
+
+// cb_state_rev_kernel: Hn and dD of every chunk, walking backwards; dh0.
+template <int DK, int DV, typename InT>
+__global__ __launch_bounds__(DK * 4) void cb_state_rev_kernel(CbArgs a) {
+  using WS = CbWs<DK, DV>;
+  using SM = CbScanSmem<DK>;
+  constexpr int NW = DK / 16, NS = DV / 16, MP = CbRevOps<DK>::MP;
+  extern __shared__ __align__(16) f32x4 red[];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, gq = l >> 4;
-  const int64_t wg = blockIdx.x;
-  const int s = (int)(wg % NS);
-  const int64_t nh = wg / NS;
+  int64_t nh;
+  int s;
+  cb_scan_slot(blockIdx.x, a.N * a.H, NS, nh, s);
   const int h = (int)(nh % a.H);
   const int64_t n = nh / a.H;
   int64_t c0, cnt;
@@ -566,107 +755,81 @@ __global__ __launch_bounds__(256) void cb_state_rev_kernel(CbArgs a) {
   const int64_t seq0 = a.cu ? (int64_t)a.cu[n] : n * a.T;
   const int64_t seqlen = a.cu ? (int64_t)(a.cu[n + 1] - a.cu[n]) : a.T;
   const int col = 16 * s + lr;
-  f32x4 Hs[RT];
+  const int row0 = 16 * w + 4 * gq;
+  f32x4 Hs;
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const int row0 = 16 * (w * RT + r) + 4 * gq;
+  for (int ii = 0; ii < 4; ++ii) Hs[ii] = a.dht ? a.dht[((n * a.H + h) * DK + row0 + ii) * DV + col] : 0.f;
+  // Hn of chunk i - 1 is stored at the end of step i (see the forward scan)
+  auto store_hn = [&](int64_t i) {
+    float* st = a.st + ((c0 + i) * a.H + h) * WS::SB;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-      Hs[r][ii] = a.dht ? a.dht[((n * a.H + h) * DK + row0 + ii) * DV + col] : 0.f;
-  }
-  const InT* dO = reinterpret_cast<const InT*>(a.dout);
-  for (int64_t i = cnt - 1; i >= 0; --i) {
-    const int64_t item = (c0 + i) * a.H + h;
-    const int64_t t0 = seq0 + i * kChunk;
-    const int64_t len = seqlen - i * kChunk < kChunk ? seqlen - i * kChunk : kChunk;
-    float* st = a.st + item * WS::SB;
-    const float* Wi = a.W + item * WS::W;
-    const float* Ki = a.KdT + item * WS::KDT;
-    const float* Qi = a.QgT + item * WS::QGT;
-    const float* Pi = a.PT + item * WS::PT;
-    const float* Ei = a.eGn + item * WS::EGN;
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const int row0 = 16 * (w * RT + r) + 4 * gq;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) st[WS::HN + (row0 + ii) * DV + col] = Hs[r][ii];
-    }
-    // scale dO as the B operand over the chunk's tokens
-    float dob[4][4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * kt + 4 * gq + e;
-        dob[kt][e] = t < len ? a.scale * load1(dO + ((t0 + t) * a.H + h) * DV + col) : 0.f;
-      }
-    // partial dD: Kd Hn over this wave's key rows, scale P^T dO over token tile w
-    f32x4 Dp[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      Dp[mt] = zero4();
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const int rb = 16 * (w * RT + r) + 4 * gq;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Dp[mt] = mfma_f32(Ki[(rb + e) * 64 + 16 * mt + lr], Hs[r][e], Dp[mt]);
-      }
-      const float4 pv = *reinterpret_cast<const float4*>(Pi + (16 * mt + lr) * 64 + 16 * w + 4 * gq);
-      float d0 = dob[0][0], d1 = dob[0][1], d2 = dob[0][2], d3 = dob[0][3];
-#pragma unroll
-      for (int kt = 1; kt < 4; ++kt)
-        if (kt == w) { d0 = dob[kt][0]; d1 = dob[kt][1]; d2 = dob[kt][2]; d3 = dob[kt][3]; }
-      Dp[mt] = mfma_f32(pv.x, d0, Dp[mt]);
-      Dp[mt] = mfma_f32(pv.y, d1, Dp[mt]);
-      Dp[mt] = mfma_f32(pv.z, d2, Dp[mt]);
-      Dp[mt] = mfma_f32(pv.w, d3, Dp[mt]);
-    }
+    for (int ii = 0; ii < 4; ++ii) st[WS::HN + (unsigned)((row0 + ii) * DV + col)] = Hs[ii];
+  };
+  auto step = [&](const CbRevOps<DK>& o, int64_t i) {
+    float* st = a.st + ((c0 + i) * a.H + h) * WS::SB;
     const int buf = (int)(i & 1);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) red[buf][w][mt][l] = Dp[mt];
-    __syncthreads();
-    f32x4 dD[4];
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 dp = zero4();
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      dD[mt] = ((red[buf][0][mt][l] + red[buf][1][mt][l]) + red[buf][2][mt][l]) + red[buf][3][mt][l];
+      for (int e = 0; e < 4; ++e) dp = mfma_f32(o.kd[mt][e], Hs[e], dp);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      if (mt == w) {
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) st[WS::DD + (16 * mt + 4 * gq + ii) * DV + col] = dD[mt][ii];
-      }
-    // Hn <- diag(e^G_n) Hn + scale Qg^T dO - W^T dD on this wave's rows
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const int rb = 16 * (w * RT + r);
-      const float4 eg = *reinterpret_cast<const float4*>(Ei + rb + 4 * gq);
-      f32x4 acc = {Hs[r][0] * eg.x, Hs[r][1] * eg.y, Hs[r][2] * eg.z, Hs[r][3] * eg.w};
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const float4 qg = *reinterpret_cast<const float4*>(Qi + (rb + lr) * 64 + 16 * kt + 4 * gq);
-        acc = mfma_f32(qg.x, dob[kt][0], acc);
-        acc = mfma_f32(qg.y, dob[kt][1], acc);
-        acc = mfma_f32(qg.z, dob[kt][2], acc);
-        acc = mfma_f32(qg.w, dob[kt][3], acc);
-      }
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc = mfma_f32(-Wi[(16 * kt + 4 * gq + e) * DK + rb + lr], dD[kt][e], acc);
-      Hs[r] = acc;
+      for (int q = 0; q < MP; ++q)
+        if ((w >> 2) + q * (NW / 4) == mt) dp += o.pp[q];
+      red[SM::PART + ((buf * NW + w) * 4 + mt) * 64 + l] = dp;
     }
+    __syncthreads();
+    if (w < 4) {  // dD, token tile w
+      const f32x4 dD = cb_red_sum<NW>(red + SM::PART, buf, w, l);
+      red[SM::SUM + (buf * 4 + w) * 64 + l] = dD;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) st[WS::DD + (unsigned)((16 * w + 4 * gq + ii) * DV + col)] = dD[ii];
+    }
+    __syncthreads();
+    f32x4 acc0 = {Hs[0] * o.eg.x, Hs[1] * o.eg.y, Hs[2] * o.eg.z, Hs[3] * o.eg.w};
+    f32x4 acc1 = o.qacc;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const f32x4 dD = red[SM::SUM + (buf * 4 + kt) * 64 + l];
+      if (kt & 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc1 = mfma_f32(-o.wt[kt][e], dD[e], acc1);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc0 = mfma_f32(-o.wt[kt][e], dD[e], acc0);
+      }
+    }
+    Hs = acc0 + acc1;
+    if (i > 0) store_hn(i - 1);
+  };
+  CbRevOps<DK> A, B;
+  CbRevRaw<DK> R;
+  // as in the forward scan, loads past the first chunk reload it
+  auto load = [&](int64_t i, CbRevOps<DK>& o) {
+    if (i < 0) i = 0;
+    const int64_t rem = seqlen - i * kChunk;
+    cb_rev_load<DK, DV, InT>(a, (c0 + i) * a.H + h, h, seq0 + i * kChunk, rem < kChunk ? rem : kChunk, w, l, col,
+                             o, R);
+  };
+  if (cnt > 0) {
+    load(cnt - 1, A);
+    store_hn(cnt - 1);
+    cb_rev_finish<DK>(w, A, R);
+  }
+  for (int64_t i = cnt - 1; i >= 0; i -= 2) {
+    load(i - 1, B);
+    step(A, i);
+    if (i < 1) break;
+    cb_rev_finish<DK>(w, B, R);
+    load(i - 2, A);
+    step(B, i - 1);
+    cb_rev_finish<DK>(w, A, R);
   }
   if (a.dh0) {
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const int row0 = 16 * (w * RT + r) + 4 * gq;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) a.dh0[((n * a.H + h) * DK + row0 + ii) * DV + col] = Hs[r][ii];
-    }
+    for (int ii = 0; ii < 4; ++ii) a.dh0[((n * a.H + h) * DK + row0 + ii) * DV + col] = Hs[ii];
   }
 }
-
 
 __device__ inline float f4_at(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
 
@@ -708,8 +871,27 @@ __global__ __launch_bounds__(256) void cb_grad_a_kernel(CbArgs a) {
   const InT* dO = reinterpret_cast<const InT*>(a.dout);
   const InT* V = reinterpret_cast<const InT*>(a.v);
 
-  // 1. D^T for this wave's value tiles
+  // the item's state block and the chunk's rows of dout: buffer resources, 32-bit offsets
+  const auto Sr = cb_rsrc(st, WS::SB * 4);
+  const auto Wr = cb_rsrc(Wi, WS::W * 4);
+  const uint32_t tsd = (uint32_t)a.H * DV;  // token stride of dout, v (elements)
+  const auto Or = cb_rsrc(dO + (it.tok0 * a.H + h) * DV, (uint32_t)(((it.len - 1) * tsd + DV) * sizeof(InT)));
+
+  // 1. D^T for this wave's value tiles; the next key tile's operands load during the current one
   {
+    struct Ops {
+      float4 wv[4];    // W[16 nt + lr][16 kt + 4 gq + e]            B = W^T
+      float s0[VR][4]; // S0[16 kt + 4 gq + e][16 (w VR + r) + lr]   A = -S0^T
+    };
+    auto load = [&](int kt, Ops& o) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) o.wv[nt] = cb_ld4(Wr, 4 * ((16 * nt + lr) * DK + 16 * kt + 4 * gq));
+#pragma unroll
+      for (int r = 0; r < VR; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o.s0[r][e] = cb_ld1(Sr, 4 * (WS::S0 + (16 * kt + 4 * gq + e) * DV + 16 * (w * VR + r) + lr));
+    };
     f32x4 Dt[VR][4];
 #pragma unroll
     for (int r = 0; r < VR; ++r)
@@ -718,20 +900,22 @@ __global__ __launch_bounds__(256) void cb_grad_a_kernel(CbArgs a) {
         const float4 u = *reinterpret_cast<const float4*>(Ui + (16 * nt + lr) * DV + 16 * (w * VR + r) + 4 * gq);
         Dt[r][nt] = f32x4{u.x, u.y, u.z, u.w};
       }
-#pragma unroll 2
-    for (int kt = 0; kt < NTK; ++kt) {
-      float4 wv[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        wv[nt] = *reinterpret_cast<const float4*>(Wi + (16 * nt + lr) * DK + 16 * kt + 4 * gq);
+    auto work = [&](const Ops& o) {
 #pragma unroll
       for (int r = 0; r < VR; ++r)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float av = -S0[(16 * kt + 4 * gq + e) * DV + 16 * (w * VR + r) + lr];
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) Dt[r][nt] = mfma_f32(av, f4_at(wv[nt], e), Dt[r][nt]);
-        }
+          for (int nt = 0; nt < 4; ++nt) Dt[r][nt] = mfma_f32(-o.s0[r][e], f4_at(o.wv[nt], e), Dt[r][nt]);
+    };
+    Ops A, B;
+    load(0, A);
+#pragma unroll 1
+    for (int kt = 0; kt < NTK; kt += 2) {
+      load(kt + 1, B);
+      work(A);
+      load(kt + 2 < NTK ? kt + 2 : kt + 1, A);
+      work(B);
     }
 #pragma unroll
     for (int r = 0; r < VR; ++r)
@@ -740,7 +924,8 @@ __global__ __launch_bounds__(256) void cb_grad_a_kernel(CbArgs a) {
   }
   __syncthreads();
 
-  // 2. products over the value channels
+  // 2. products over the value channels, the next value tile's operands loading during the
+  // current one
   f32x4 gQ[KR][4], gW[4][KR], gK[KR][4], gP[3];
   float gn[KR];
 #pragma unroll
@@ -758,41 +943,37 @@ __global__ __launch_bounds__(256) void cb_grad_a_kernel(CbArgs a) {
     pJ[qq] = p < 10 ? cb_tile_j(p) : 0;
   }
   const int np = w < 2 ? 3 : 2;
-#pragma unroll 1
-  for (int kt = 0; kt < NTV; ++kt) {
-    float4 s0v[KR], hnv[KR], ddv[4];
-    float dov[4][4];
-    f32x4 dtv[4];
+  struct Ops2 {
+    float4 s0v[KR], hnv[KR];  // S0, Hn rows 16 (w KR + r) + lr, value channels 16 kt + 4 gq ..
+    float4 ddv[4], dov[4];    // dD, dout rows 16 mt + lr (dout zero past the chunk's end)
+  };
+  auto load2 = [&](int kt, Ops2& o) {
 #pragma unroll
     for (int r = 0; r < KR; ++r) {
-      s0v[r] = *reinterpret_cast<const float4*>(S0 + (16 * (w * KR + r) + lr) * DV + 16 * kt + 4 * gq);
-      hnv[r] = *reinterpret_cast<const float4*>(Hn + (16 * (w * KR + r) + lr) * DV + 16 * kt + 4 * gq);
+      const uint32_t off = (16 * (w * KR + r) + lr) * DV + 16 * kt + 4 * gq;
+      o.s0v[r] = cb_ld4(Sr, 4 * (WS::S0 + off));
+      o.hnv[r] = cb_ld4(Sr, 4 * (WS::HN + off));
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const int t = 16 * mt + lr;
-      if (t < it.len) {
-        load4(dO + ((it.tok0 + t) * a.H + h) * DV + 16 * kt + 4 * gq, dov[mt]);
-      } else {
-        dov[mt][0] = dov[mt][1] = dov[mt][2] = dov[mt][3] = 0.f;
-      }
-      ddv[mt] = *reinterpret_cast<const float4*>(dD + (16 * mt + lr) * DV + 16 * kt + 4 * gq);
-      dtv[mt] = DT[(kt * 4 + mt) * 64 + l];
+      o.ddv[mt] = cb_ld4(Sr, 4 * (WS::DD + (16 * mt + lr) * DV + 16 * kt + 4 * gq));
+      o.dov[mt] = cb_ld4_io(Or, (16 * mt + lr) * tsd + 16 * kt + 4 * gq, (const InT*)nullptr);
     }
-    // the wave's dP tiles: A rows of dO (token tile I), B fragments of D^T (token tile J)
-    float pa[3][4];
+  };
+  auto work2 = [&](const Ops2& o, int kt) {
+    f32x4 dtv[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) dtv[mt] = DT[(kt * 4 + mt) * 64 + l];
+    // the wave's dP tiles: A rows of dout (token tile I), B fragments of D^T (token tile J)
+    float4 pa[3];
     f32x4 pb[3];
 #pragma unroll
     for (int qq = 0; qq < 3; ++qq) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pa[qq][e] = dov[0][e];
+      pa[qq] = o.dov[0];
       pb[qq] = dtv[0];
 #pragma unroll
       for (int mt = 1; mt < 4; ++mt) {
-        if (pI[qq] == mt) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pa[qq][e] = dov[mt][e];
-        }
+        if (pI[qq] == mt) pa[qq] = o.dov[mt];
         if (pJ[qq] == mt) pb[qq] = dtv[mt];
       }
     }
@@ -800,18 +981,29 @@ __global__ __launch_bounds__(256) void cb_grad_a_kernel(CbArgs a) {
     for (int e = 0; e < 4; ++e) {
 #pragma unroll
       for (int r = 0; r < KR; ++r) {
-        const float sv = f4_at(s0v[r], e), hv = f4_at(hnv[r], e);
+        const float sv = f4_at(o.s0v[r], e), hv = f4_at(o.hnv[r], e);
         gn[r] = fmaf(sv, hv, gn[r]);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-          gQ[r][nt] = mfma_f32(sv, dov[nt][e], gQ[r][nt]);
-          gW[nt][r] = mfma_f32(f4_at(ddv[nt], e), sv, gW[nt][r]);
+          gQ[r][nt] = mfma_f32(sv, f4_at(o.dov[nt], e), gQ[r][nt]);
+          gW[nt][r] = mfma_f32(f4_at(o.ddv[nt], e), sv, gW[nt][r]);
           gK[r][nt] = mfma_f32(hv, dtv[nt][e], gK[r][nt]);
         }
       }
 #pragma unroll
       for (int qq = 0; qq < 3; ++qq)
-        if (qq < np) gP[qq] = mfma_f32(pa[qq][e], pb[qq][e], gP[qq]);
+        if (qq < np) gP[qq] = mfma_f32(f4_at(pa[qq], e), pb[qq][e], gP[qq]);
+    }
+  };
+  {
+    Ops2 A, B;
+    load2(0, A);
+#pragma unroll 1
+    for (int kt = 0; kt < NTV; kt += 2) {
+      load2(kt + 1, B);
+      work2(A, kt);
+      load2(kt + 2 < NTV ? kt + 2 : kt + 1, A);
+      work2(B, kt + 1);
     }
   }
 #pragma unroll
@@ -952,22 +1144,23 @@ struct CbGradSmem {
   static constexpr size_t G = QH + 64 * KS;
   static constexpr size_t DL = G + 64 * KS;       // [64][MS] diag(beta) dA; later dG [64][KS]
   static constexpr size_t DP = DL + 64 * MS;      // [64][MS]
+  static constexpr int NW = DK / 16;             // waves
   static constexpr size_t NRM = DP + 64 * MS;     // [2][2][64]: per q, k: |x| 2^-ex, ex
   static constexpr size_t BETA = NRM + 256;       // [64]
-  static constexpr size_t DOT = BETA + 64;        // [2][4][64]
-  static constexpr size_t DBP = DOT + 512;        // [4][64]
-  static constexpr size_t DPD = DBP + 256;        // [64] diagonal of dP
+  static constexpr size_t DOT = BETA + 64;        // [2][NW][64]
+  static constexpr size_t DBP = DOT + 2 * NW * 64;  // [NW][64]
+  static constexpr size_t DPD = DBP + NW * 64;    // [64] diagonal of dP
   static constexpr size_t BYTES = (DPD + 64) * 4;
   static_assert(64 * KS <= 2 * 64 * MS, "dG must fit the dL and dP rows");
 };
 
 template <int DK, int DV, typename InT>
-__global__ __launch_bounds__(256) void cb_grad_b_kernel(CbArgs a) {
+__global__ __launch_bounds__(DK * 4) void cb_grad_b_kernel(CbArgs a) {
   extern __shared__ __align__(16) float sm[];
   using S = CbGradSmem<DK>;
   using WS = CbWs<DK, DV>;
-  constexpr int KS = S::KS, MS = S::MS;
-  constexpr int KR = DK / 64;
+  constexpr int KS = S::KS, MS = S::MS, NW = S::NW, NT = DK * 4;
+  constexpr int KR = 1;
   const int64_t item = blockIdx.x;
   const int64_t c = item / a.H;
   const int h = (int)(item - c * a.H);
@@ -985,9 +1178,9 @@ __global__ __launch_bounds__(256) void cb_grad_b_kernel(CbArgs a) {
   float* dpd = sm + S::DPD;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, gq = l >> 4;
   const float* st = a.st + item * WS::SB;
-  cb_load_rows<DK, InT>(a, it, h, kh, qh, G, bs, nrm);
+  cb_load_rows<DK, InT, NT>(a, it, h, kh, qh, G, bs, nrm);
   __syncthreads();
-  for (int idx = tid; idx < 64 * 16; idx += 256) {
+  for (int idx = tid; idx < 64 * 16; idx += NT) {
     const int i = idx >> 4, j4 = (idx & 15) * 4;
     const float4 av = *reinterpret_cast<const float4*>(st + WS::GA + i * 64 + j4);
     const float4 pv = *reinterpret_cast<const float4*>(st + WS::GP + i * 64 + j4);
@@ -1228,7 +1421,7 @@ __global__ __launch_bounds__(256) void cb_grad_b_kernel(CbArgs a) {
     const float sb = rows4_sum(dbx[nt]);
     if (gq == 0) {
       dots[w * 64 + t] = sq;
-      dots[256 + w * 64 + t] = sk;
+      dots[NW * 64 + w * 64 + t] = sk;
       dbp[w * 64 + t] = sb;
     }
   }
@@ -1242,8 +1435,10 @@ __global__ __launch_bounds__(256) void cb_grad_b_kernel(CbArgs a) {
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
       const float* xh = which ? kh : qh;
-      const float* dsum = dots + which * 256;
-      const float dot = ((dsum[t] + dsum[64 + t]) + dsum[128 + t]) + dsum[192 + t];
+      const float* dsum = dots + which * NW * 64;
+      float dot = dsum[t];
+#pragma unroll
+      for (int v = 1; v < NW; ++v) dot += dsum[v * 64 + t];
       const float nv = nrm[which * 128 + t];
       const int ex = (int)nrm[which * 128 + 64 + t];
 #pragma unroll
@@ -1274,10 +1469,12 @@ __global__ __launch_bounds__(256) void cb_grad_b_kernel(CbArgs a) {
       gds[t * KS + tid] = acc;
     }
   }
-  if (tid >= 192 && tid - 192 < it.len) {
-    const int t = tid - 192;
-    const float v = st[WS::GB + t] + (((dbp[t] + dbp[64 + t]) + dbp[128 + t]) + dbp[192 + t]);
-    store1(reinterpret_cast<InT*>(a.dbeta) + (it.tok0 + t) * a.H + h, v);
+  if (tid >= NT - 64 && tid - (NT - 64) < it.len) {
+    const int t = tid - (NT - 64);
+    float v = dbp[t];
+#pragma unroll
+    for (int u = 1; u < NW; ++u) v += dbp[u * 64 + t];
+    store1(reinterpret_cast<InT*>(a.dbeta) + (it.tok0 + t) * a.H + h, st[WS::GB + t] + v);
   }
   __syncthreads();
   // 6. dg = that sum + the Kd prefix + e^G_n rowsum(Hn o S0)

@@ -282,13 +282,17 @@ static hipError_t launch_chunk_backward_t(const BackwardPlan& p, hipStream_t str
     auto fac = cb_factor_kernel<DK, DV, InT>;
     const size_t smem = CbFacSmem<DK>::BYTES;
     if ((e = allow_smem(fac, smem)) != hipSuccess) return e;
-    hipLaunchKernelGGL(fac, dim3((unsigned)items), dim3(256), smem, stream, a);
+    hipLaunchKernelGGL(fac, dim3((unsigned)items), dim3(DK * 4), smem, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int64_t chains = p.N * (int64_t)p.H * (DV / 16);
-  hipLaunchKernelGGL((cb_state_fwd_kernel<DK, DV>), dim3((unsigned)chains), dim3(256), 0, stream, a);
+  const size_t ssm = CbScanSmem<DK>::BYTES;
+  auto sf = cb_state_fwd_kernel<DK, DV>;
+  auto sr = cb_state_rev_kernel<DK, DV, InT>;
+  if ((e = allow_smem(sf, ssm)) != hipSuccess || (e = allow_smem(sr, ssm)) != hipSuccess) return e;
+  hipLaunchKernelGGL(sf, dim3((unsigned)chains), dim3(DK * 4), ssm, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((cb_state_rev_kernel<DK, DV, InT>), dim3((unsigned)chains), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(sr, dim3((unsigned)chains), dim3(DK * 4), ssm, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (items > 0) {
     hipLaunchKernelGGL((cb_grad_a_kernel<DK, DV, InT>), dim3((unsigned)items), dim3(256), 0, stream, a);
@@ -296,7 +300,7 @@ static hipError_t launch_chunk_backward_t(const BackwardPlan& p, hipStream_t str
     auto gb = cb_grad_b_kernel<DK, DV, InT>;
     const size_t smem = CbGradSmem<DK>::BYTES;
     if ((e = allow_smem(gb, smem)) != hipSuccess) return e;
-    hipLaunchKernelGGL(gb, dim3((unsigned)items), dim3(256), smem, stream, a);
+    hipLaunchKernelGGL(gb, dim3((unsigned)items), dim3(DK * 4), smem, stream, a);
     e = hipGetLastError();
   }
   return e;
