@@ -20,20 +20,19 @@
 // normalisation.
 //
 // Every product runs on v_mfma_f32_16x16x4f32 (fp32 operands and sums): the fp32
-// gradients (dg, dh0) keep the precision of a scalar fp32 walk.  Five kernels:
+// gradients (dg, dh0) keep the precision of a scalar fp32 walk.  Four kernels:
 //   cb_factor_kernel     per (chunk, head): unit q and k, G, the gated Grams L and P, T, W,
 //                        U, Kd^T, Qg^T, e^G_n
-//   cb_state_fwd_kernel  per (sequence, head, 16 value columns): the state at every chunk
-//                        start (S0), walking the chunks forwards
-//   cb_state_rev_kernel  per (sequence, head, 16 value columns): Hn of every chunk and dD,
-//                        walking the chunks backwards; dh0
+//   cb_state_scan_kernel per (sequence, head, 16 value columns): the state at every chunk
+//                        start (S0), walking the chunks forwards, and beside it Hn of every
+//                        chunk and dD, walking them backwards; dh0
 //   cb_grad_a_kernel     per (chunk, head): the products over value channels (dQg, dW, dKd,
 //                        dP, D recomputed), dX, dY, dv, dA
 //   cb_grad_b_kernel     per (chunk, head): the gated-product backward, dG and dg, dq, dk,
 //                        dbeta
 // The value columns of the state evolve independently in both scans, so a scan workgroup
-// owns 16 columns and its four waves split the key rows; a step adds the waves' partial
-// sums through LDS in a fixed order.  Results are deterministic.
+// owns 16 columns and its waves split the key rows; a step adds the waves' partial sums
+// through LDS in a fixed order.  Results are deterministic.
 //
 // Gated products: M_ij = sum_c a_ic b_jc e^(G_ic - G_jc) over 16 x 16 token blocks is a
 // matrix product of a e^(G - G_r) and b e^(G_r - G) for a reference row r.  Off-diagonal
@@ -58,6 +57,8 @@ __device__ inline f32x4 mfma_f32(float a, float b, const f32x4& c) {
 }
 
 __device__ inline float cb_exp(float x) { return exp2_hw(x * kLog2e); }
+
+__device__ inline float f4_at(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
 
 // Buffer loads: a resource over one chunk's array (uniform, in scalar registers) and 32-bit
 // byte offsets per lane.  Per-lane 64-bit addresses of loads inside the chunk loops would be
@@ -95,6 +96,10 @@ __device__ __host__ constexpr int cb_tile_i(int p) {
 __device__ __host__ constexpr int cb_tile_j(int p) {
   return p < 4 ? p : p < 7 ? p - 4 : p < 9 ? p - 7 : 0;
 }
+// Position in that list of block (I, J), I >= J.
+__device__ __host__ constexpr int cb_blk(int I, int J) {
+  return I == J ? I : I - J == 1 ? 4 + J : I - J == 2 ? 7 + J : 9;
+}
 
 // Per-(chunk, head) workspace.  Item it = chunk * H + head.
 template <int DK, int DV>
@@ -103,16 +108,19 @@ struct CbWs {
   static constexpr size_t U = 64 * DV;        // U [64][DV]
   static constexpr size_t KDT = DK * 64;      // Kd^T [DK][64]
   static constexpr size_t QGT = DK * 64;      // Qg^T [DK][64]
-  static constexpr size_t PT = 64 * 64;       // P^T [64][64]
-  static constexpr size_t L = 64 * 64;        // L [64][64]
-  static constexpr size_t TT = 64 * 64;       // T^T [64][64]
+  // the lower triangular 64 x 64 factors keep their 10 lower 16 x 16 blocks, in the order
+  // of cb_tile_i / cb_tile_j, each row-major
+  static constexpr size_t PT = 10 * 256;      // P^T: block p holds (block (I, J) of P)^T
+  static constexpr size_t L = 10 * 256;       // L: block p holds block (I, J) of L
+  static constexpr size_t TT = 10 * 256;      // T^T: as P^T
   static constexpr size_t EGN = DK;           // e^G_n [DK]
-  // State block: S0 [DK][DV], Hn [DK][DV], dD [64][DV]; cb_grad_a_kernel then reuses it for
-  // its results (dQg^T, dKd^T, dX^T as C fragments [DK/16][4][64 lanes][4], dA and dP
-  // [64][64], a partial dbeta [64] and a partial dG_n [DK]).
+  // State block: S0 [DK][DV], Hn [DK][DV], dD [64][DV], D [64][DV]; cb_grad_a_kernel then
+  // reuses it for its results (dQg^T, dKd^T, dX^T as C fragments [DK/16][4][64 lanes][4],
+  // dA and dP [64][64], a partial dbeta [64] and a partial dG_n [DK]).
   static constexpr size_t S0 = 0;
   static constexpr size_t HN = DK * DV;
   static constexpr size_t DD = 2 * DK * DV;
+  static constexpr size_t DM = DD + 64 * DV;
   static constexpr size_t GQ = 0;
   static constexpr size_t GKD = DK * 64;
   static constexpr size_t GX = 2 * DK * 64;
@@ -121,7 +129,7 @@ struct CbWs {
   static constexpr size_t GB = GP + 64 * 64;
   static constexpr size_t GN = GB + 64;
   static constexpr size_t GEND = GN + DK;
-  static constexpr size_t SB0 = DD + 64 * DV > GEND ? DD + 64 * DV : GEND;
+  static constexpr size_t SB0 = DM + 64 * DV > GEND ? DM + 64 * DV : GEND;
   static constexpr size_t SB = (SB0 + 63) / 64 * 64;
   static constexpr size_t FACTOR_FLOATS = W + U + KDT + QGT + PT + L + TT + EGN;
 };
@@ -217,16 +225,11 @@ __device__ void cb_load_rows(const CbArgs& a, const CbItem& it, int h, float* kh
 #pragma unroll
     for (int o = 1; o < TP; o <<= 1) ss += __shfl_xor(ss, o);
     const float nv = sqrtf(ss);
+    const float inv = ss > 0.f ? 1.f / nv : 0.f;
     float* dst = (which ? kh : qh) + t * KS + p * CH;
 #pragma unroll
-    for (int c = 0; c < CH; c += 4) {
-      float4 o;
-      o.x = ss > 0.f ? x[c] / nv : 0.f;
-      o.y = ss > 0.f ? x[c + 1] / nv : 0.f;
-      o.z = ss > 0.f ? x[c + 2] / nv : 0.f;
-      o.w = ss > 0.f ? x[c + 3] / nv : 0.f;
-      *reinterpret_cast<float4*>(dst + c) = o;
-    }
+    for (int c = 0; c < CH; c += 4)
+      *reinterpret_cast<float4*>(dst + c) = make_float4(x[c] * inv, x[c + 1] * inv, x[c + 2] * inv, x[c + 3] * inv);
     if (nrm && p == 0) {
       nrm[which * 128 + t] = nv;
       nrm[which * 128 + 64 + t] = (float)ex;
@@ -374,7 +377,8 @@ __global__ __launch_bounds__(DK * 4) void cb_factor_kernel(CbArgs a) {
   float* Ps = sm + S::P;
   float* Ts = sm + S::TI;
   float* bs = sm + S::BETA;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, gq = l >> 4;
+  const int tid = threadIdx.x, l = tid & 63, lr = l & 15, gq = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   for (int i = tid; i < 3 * 64 * 64 / 4; i += NT)
     reinterpret_cast<float4*>(Ls)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   cb_load_rows<DK, InT, NT>(a, it, h, kh, qh, G, bs, nullptr);
@@ -487,34 +491,42 @@ __global__ __launch_bounds__(DK * 4) void cb_factor_kernel(CbArgs a) {
   float* pt = a.PT + item * WS::PT;
   float* tt = a.TT + item * WS::TT;
   float* lo = a.L + item * WS::L;
-  for (int idx = tid; idx < 64 * 16; idx += NT) {
-    const int j = idx >> 4, i4 = (idx & 15) * 4;
-    *reinterpret_cast<float4*>(pt + j * 64 + i4) =
-        make_float4(Ps[i4 * 64 + j], Ps[(i4 + 1) * 64 + j], Ps[(i4 + 2) * 64 + j], Ps[(i4 + 3) * 64 + j]);
-    *reinterpret_cast<float4*>(tt + j * 64 + i4) =
-        make_float4(Ts[i4 * 64 + j], Ts[(i4 + 1) * 64 + j], Ts[(i4 + 2) * 64 + j], Ts[(i4 + 3) * 64 + j]);
-    reinterpret_cast<float4*>(lo)[idx] = reinterpret_cast<const float4*>(Ls)[idx];
+  for (int idx = tid; idx < 10 * 64; idx += NT) {
+    const int p = idx >> 6, r = (idx >> 2) & 15, c4 = (idx & 3) * 4;
+    const int I = cb_tile_i(p), J = cb_tile_j(p);
+    const int i0 = 16 * I, j0 = 16 * J;
+    const size_t o = (size_t)p * 256 + r * 16 + c4;
+    *reinterpret_cast<float4*>(lo + o) = *reinterpret_cast<const float4*>(Ls + (i0 + r) * 64 + j0 + c4);
+    *reinterpret_cast<float4*>(pt + o) = make_float4(Ps[(i0 + c4) * 64 + j0 + r], Ps[(i0 + c4 + 1) * 64 + j0 + r],
+                                                     Ps[(i0 + c4 + 2) * 64 + j0 + r], Ps[(i0 + c4 + 3) * 64 + j0 + r]);
+    *reinterpret_cast<float4*>(tt + o) = make_float4(Ts[(i0 + c4) * 64 + j0 + r], Ts[(i0 + c4 + 1) * 64 + j0 + r],
+                                                     Ts[(i0 + c4 + 2) * 64 + j0 + r], Ts[(i0 + c4 + 3) * 64 + j0 + r]);
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// State scans.  Workgroup = (sequence, head, 16 value columns) with DK / 16 waves: wave w
-// owns key rows [16 w, 16 w + 16) of the slice's state, one C tile.  A step adds the
-// waves' partial sums over key rows through LDS (two buffers, one barrier per step); the
-// next chunk's factors are loaded while the current chunk is processed.  When the count of
-// (sequence, head) pairs is a multiple of 8, the slices of a pair run on one compute die
-// (workgroups are dealt to the 8 dies in turn), where they share its L2.
+// cb_state_scan_kernel: the two scans over a sequence's chunks in one loop.  The forward
+// scan (S0 of every chunk, walking up) and the reverse scan (Hn and dD of every chunk,
+// walking down; dh0) do not depend on each other, so a workgroup walks both: step j is
+// forward step j and reverse step cnt - 1 - j, and the two chains share its barriers, each
+// one's matrix-core work filling the other's waits.
+//
+// Workgroup = (sequence, head, 16 value columns) with DK / 16 waves: wave w owns key rows
+// [16 w, 16 w + 16) of both slices' states, one C tile each.  A step adds the waves' partial
+// sums over key rows through LDS: the waves write their partials, then (after a barrier)
+// four waves each add up one token tile of the forward D and four one of the reverse dD (in
+// wave order), and after a second barrier every wave reads the sums.  The next chunks'
+// factors are loaded while the current ones are processed.  When the count of (sequence,
+// head) pairs is a multiple of 8, the slices of a pair run on one compute die (workgroups
+// are dealt to the 8 dies in turn), where they share its L2.
 
-// LDS of a scan workgroup: the waves' partial tiles [2 buffers][NW waves][4 token tiles][64]
-// and the summed tiles [2 buffers][4 token tiles][64], f32x4.  A step writes its partials,
-// waves 0..3 each add up one token tile (in wave order) after a barrier, and after a second
-// barrier every wave reads the four sums.
 template <int DK>
 struct CbScanSmem {
   static constexpr int NW = DK / 16;
-  static constexpr int PART = 0;
-  static constexpr int SUM = 2 * NW * 4 * 64;  // in f32x4
-  static constexpr size_t BYTES = (SUM + 2 * 4 * 64) * 16;
+  static constexpr int PART = 0;                  // [2 buffers][NW][4 token tiles][64] f32x4
+  static constexpr int SUM = 2 * NW * 4 * 64;     // [2 buffers][4 token tiles][64] f32x4
+  static constexpr int ONE = SUM + 2 * 4 * 64;    // one scan's share, f32x4
+  static constexpr size_t BYTES = (size_t)2 * ONE * 16;  // forward, then reverse
 };
 
 // Sum of the NW waves' partial tiles in wave order, every read issued before the adds.
@@ -540,41 +552,33 @@ __device__ inline void cb_scan_slot(int64_t wg, int64_t pairs, int ns, int64_t& 
   }
 }
 
-// One chunk's operands of the forward scan for wave w (key rows 16 w ..).
-struct CbFwdOps {
-  float4 w[4];    // W[16 mt + lr][16 w + 4 gq + e]          A of W S
-  float u[4];     // U[16 w + 4 gq + i][col] (waves 0..3)     C tile of U
-  float4 kd[4];   // Kd^T[16 w + lr][16 mt + 4 gq + e]        A of Kd^T D
-  float4 eg;      // e^G_n[16 w + 4 gq + i]
+// Buffer resources over one chunk's factors.
+template <int DK, int DV>
+struct CbChunkRes {
+  __amdgpu_buffer_rsrc_t W, U, K, Q, P, E;
+  __device__ CbChunkRes(const CbArgs& a, int64_t item) {
+    using WS = CbWs<DK, DV>;
+    W = cb_rsrc(a.W + item * WS::W, WS::W * 4);
+    U = cb_rsrc(a.U + item * WS::U, WS::U * 4);
+    K = cb_rsrc(a.KdT + item * WS::KDT, WS::KDT * 4);
+    Q = cb_rsrc(a.QgT + item * WS::QGT, WS::QGT * 4);
+    P = cb_rsrc(a.PT + item * WS::PT, WS::PT * 4);
+    E = cb_rsrc(a.eGn + item * WS::EGN, WS::EGN * 4);
+  }
 };
 
-template <int DK, int DV>
-__device__ inline void cb_fwd_load(const CbArgs& a, int64_t item, int w, int l, int col, CbFwdOps& o) {
-  using WS = CbWs<DK, DV>;
-  const unsigned lr = l & 15, gq = l >> 4;
-  const auto Wr = cb_rsrc(a.W + item * WS::W, WS::W * 4);
-  const auto Ur = cb_rsrc(a.U + item * WS::U, WS::U * 4);
-  const auto Kr = cb_rsrc(a.KdT + item * WS::KDT, WS::KDT * 4);
-  const auto Er = cb_rsrc(a.eGn + item * WS::EGN, WS::EGN * 4);
-#pragma unroll
-  for (unsigned mt = 0; mt < 4; ++mt) {
-    o.w[mt] = cb_ld4(Wr, 4 * ((16 * mt + lr) * DK + 16 * w + 4 * gq));
-    o.kd[mt] = cb_ld4(Kr, 4 * ((16 * w + lr) * 64 + 16 * mt + 4 * gq));
-  }
-  // waves 4.. read past the end of U (zeros): no branch around the loads
-#pragma unroll
-  for (unsigned ii = 0; ii < 4; ++ii) o.u[ii] = cb_ld1(Ur, 4 * ((16 * w + 4 * gq + ii) * DV + col));
-  o.eg = cb_ld4(Er, 4 * (16 * w + 4 * gq));
-}
-
-// cb_state_fwd_kernel: S0 of every chunk.
-template <int DK, int DV>
-__global__ __launch_bounds__(DK * 4) void cb_state_fwd_kernel(CbArgs a) {
+template <int DK, int DV, typename InT>
+__global__ __launch_bounds__(DK * 4) void cb_state_scan_kernel(CbArgs a) {
   using WS = CbWs<DK, DV>;
   using SM = CbScanSmem<DK>;
+  using Res = CbChunkRes<DK, DV>;
   constexpr int NW = DK / 16, NS = DV / 16;
+  constexpr int MP = 16 / NW;  // output token tiles of the wave's share of P^T dO
   extern __shared__ __align__(16) f32x4 red[];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, gq = l >> 4;
+  f32x4* redF = red;
+  f32x4* redR = red + SM::ONE;
+  const int tid = threadIdx.x, l = tid & 63, lr = l & 15, gq = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   int64_t nh;
   int s;
   cb_scan_slot(blockIdx.x, a.N * a.H, NS, nh, s);
@@ -582,248 +586,210 @@ __global__ __launch_bounds__(DK * 4) void cb_state_fwd_kernel(CbArgs a) {
   const int64_t n = nh / a.H;
   int64_t c0, cnt;
   cb_chunks(a, n, c0, cnt);
+  if (cnt == 0) {  // no chunks: dh0 = dht
+    if (a.dh0) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int64_t o = ((n * a.H + h) * DK + 16 * w + 4 * gq + ii) * DV + 16 * s + lr;
+        a.dh0[o] = a.dht ? a.dht[o] : 0.f;
+      }
+    }
+    return;
+  }
+  const int64_t seq0 = a.cu ? (int64_t)a.cu[n] : n * a.T;
+  const int64_t seqlen = a.cu ? (int64_t)(a.cu[n + 1] - a.cu[n]) : a.T;
   const int col = 16 * s + lr;
   const int row0 = 16 * w + 4 * gq;
-  f32x4 S;
+  const int tw = w & 3;
+  // which token tiles this wave sums: with 8 waves, waves 0..3 the forward ones and 4..7 the
+  // reverse ones; with 4 waves, each both
+  const bool sum_f = NW == 4 || w < 4, sum_r = NW == 4 || w >= 4;
+  const unsigned tstride = (unsigned)a.H * DV;
+  const unsigned ulr = lr, ugq = gq;
+
+  // Operands, one buffer each, refilled for the next chunk as soon as the current values
+  // are consumed (so each load has most of a step to arrive):
+  float4 fw[4];    // forward: W[16 mt + lr][16 w + 4 gq + e]          A of W S
+  float fu[4];     //          U[16 tw + 4 gq + i][col]                 C tile of U
+  float4 fk[4];    //          Kd^T[16 w + lr][16 mt + 4 gq + e]       A of Kd^T D
+  float4 fe;       //          e^G_n[16 w + 4 gq + i]
+  float rk[4][4];  // reverse: Kd[16 mt + lr][16 w + 4 gq + e]          A of Kd Hn
+  float rw[4][4];  //          W[16 kt + 4 gq + e][16 w + lr]            A of W^T dD
+  float4 re;       //          e^G_n[16 w + 4 gq + i]
+  float4 qg[4];    //          Qg^T[16 w + lr][16 kt + 4 gq + e]        A of Qg^T dO
+  float4 pt[MP];   //          P^T[16 mt + lr][16 tw + 4 gq + e]        A of P^T dO
+  float dob[4][4]; //          scale dO[16 kt + 4 gq + e][col]          B over the chunk's tokens
+  f32x4 qacc, pp[MP];  // scale Qg^T dO on the wave's rows; the wave's share of scale P^T dO
+
+  auto itemf = [&](int64_t i) { return (c0 + (i < cnt ? i : cnt - 1)) * a.H + h; };  // clamped
+  auto itemr = [&](int64_t i) { return (c0 + (i > 0 ? i : 0)) * a.H + h; };
+  auto load_fw = [&](const Res& r) {
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii) S[ii] = a.h0 ? a.h0[((n * a.H + h) * DK + row0 + ii) * DV + col] : 0.f;
-  // S0 of chunk i + 1 is stored at the end of step i, after the step's waits for its loads,
-  // so no wait covers a store
+    for (unsigned mt = 0; mt < 4; ++mt) fw[mt] = cb_ld4(r.W, 4 * ((16 * mt + ulr) * DK + 16 * w + 4 * ugq));
+  };
+  auto load_fu = [&](const Res& r) {
+#pragma unroll
+    for (unsigned ii = 0; ii < 4; ++ii) fu[ii] = cb_ld1(r.U, 4 * ((16 * tw + 4 * ugq + ii) * DV + col));
+  };
+  auto load_fk = [&](const Res& r) {
+#pragma unroll
+    for (unsigned mt = 0; mt < 4; ++mt) fk[mt] = cb_ld4(r.K, 4 * ((16 * w + ulr) * 64 + 16 * mt + 4 * ugq));
+    fe = cb_ld4(r.E, 4 * (16 * w + 4 * ugq));
+  };
+  auto load_rk = [&](const Res& r) {
+#pragma unroll
+    for (unsigned m = 0; m < 4; ++m)
+#pragma unroll
+      for (unsigned e = 0; e < 4; ++e) rk[m][e] = cb_ld1(r.K, 4 * ((16 * w + 4 * ugq + e) * 64 + 16 * m + ulr));
+  };
+  auto load_rw = [&](const Res& r) {
+#pragma unroll
+    for (unsigned m = 0; m < 4; ++m)
+#pragma unroll
+      for (unsigned e = 0; e < 4; ++e) rw[m][e] = cb_ld1(r.W, 4 * ((16 * m + 4 * ugq + e) * DK + 16 * w + ulr));
+    re = cb_ld4(r.E, 4 * (16 * w + 4 * ugq));
+  };
+  auto load_raw = [&](const Res& r, int64_t i) {
+    if (i < 0) i = 0;
+    const int64_t rem = seqlen - i * kChunk;
+    const int64_t len = rem < kChunk ? rem : kChunk;
+    // the chunk's rows of dout for the slice's 16 columns; tokens past the chunk's end fall
+    // outside the resource and read 0
+    const auto Dr = cb_rsrc(reinterpret_cast<const InT*>(a.dout) + ((seq0 + i * kChunk) * a.H + h) * DV + 16 * s,
+                            (uint32_t)(((len - 1) * tstride + 16) * sizeof(InT)));
+#pragma unroll
+    for (unsigned m = 0; m < 4; ++m) {
+      qg[m] = cb_ld4(r.Q, 4 * ((16 * w + ulr) * 64 + 16 * m + 4 * ugq));
+#pragma unroll
+      for (unsigned e = 0; e < 4; ++e)
+        dob[m][e] = a.scale * cb_ld_io(Dr, (16 * m + 4 * ugq + e) * tstride + ulr, (const InT*)nullptr);
+    }
+#pragma unroll
+    for (int q = 0; q < MP; ++q) {  // P^T[j][i] = 0 for token tile of i < that of j
+      const int mt = (w >> 2) + q * (NW / 4);
+      pt[q] = tw >= mt ? cb_ld4(r.P, 4 * (cb_blk(tw, mt) * 256 + ulr * 16 + 4 * ugq)) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto finish_raw = [&]() {  // qacc and pp of the chunk whose raw operands are loaded
+    f32x4 q0 = zero4(), q1 = zero4();
+#pragma unroll
+    for (int kt = 0; kt < 4; kt += 2)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        q0 = mfma_f32(f4_at(qg[kt], e), dob[kt][e], q0);
+        q1 = mfma_f32(f4_at(qg[kt + 1], e), dob[kt + 1][e], q1);
+      }
+    qacc = q0 + q1;
+    float db[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      db[e] = dob[0][e];
+#pragma unroll
+      for (int kt = 1; kt < 4; ++kt)
+        if (tw == kt) db[e] = dob[kt][e];
+    }
+#pragma unroll
+    for (int q = 0; q < MP; ++q) {
+      f32x4 p = zero4();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p = mfma_f32(f4_at(pt[q], e), db[e], p);
+      pp[q] = p;
+    }
+  };
+
+  f32x4 S, Hs;
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    S[ii] = a.h0 ? a.h0[((n * a.H + h) * DK + row0 + ii) * DV + col] : 0.f;
+    Hs[ii] = a.dht ? a.dht[((n * a.H + h) * DK + row0 + ii) * DV + col] : 0.f;
+  }
   auto store_s0 = [&](int64_t i) {
     float* st = a.st + ((c0 + i) * a.H + h) * WS::SB;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) st[WS::S0 + (unsigned)((row0 + ii) * DV + col)] = S[ii];
   };
-  auto step = [&](const CbFwdOps& o, int64_t i) {
-    const int buf = (int)(i & 1);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4 dp = zero4();
-      dp = mfma_f32(o.w[mt].x, S[0], dp);
-      dp = mfma_f32(o.w[mt].y, S[1], dp);
-      dp = mfma_f32(o.w[mt].z, S[2], dp);
-      dp = mfma_f32(o.w[mt].w, S[3], dp);
-      red[SM::PART + ((buf * NW + w) * 4 + mt) * 64 + l] = dp;
-    }
-    __syncthreads();
-    if (w < 4) {  // D = U - W S, token tile w
-      const f32x4 sum = cb_red_sum<NW>(red + SM::PART, buf, w, l);
-      f32x4 D;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) D[ii] = o.u[ii] - sum[ii];
-      red[SM::SUM + (buf * 4 + w) * 64 + l] = D;
-    }
-    __syncthreads();
-    f32x4 Dt[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) Dt[mt] = red[SM::SUM + (buf * 4 + mt) * 64 + l];
-    f32x4 acc[2] = {f32x4{S[0] * o.eg.x, S[1] * o.eg.y, S[2] * o.eg.z, S[3] * o.eg.w}, zero4()};
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      acc[mt & 1] = mfma_f32(o.kd[mt].x, Dt[mt][0], acc[mt & 1]);
-      acc[mt & 1] = mfma_f32(o.kd[mt].y, Dt[mt][1], acc[mt & 1]);
-      acc[mt & 1] = mfma_f32(o.kd[mt].z, Dt[mt][2], acc[mt & 1]);
-      acc[mt & 1] = mfma_f32(o.kd[mt].w, Dt[mt][3], acc[mt & 1]);
-    }
-    S = acc[0] + acc[1];
-    if (i + 1 < cnt) store_s0(i + 1);
-  };
-  // the next chunk's loads are issued unconditionally (past the last chunk they reload the
-  // last one), so the wait counts stay exact across the loop
-  CbFwdOps A, B;
-  auto load = [&](int64_t i, CbFwdOps& o) {
-    cb_fwd_load<DK, DV>(a, (c0 + (i < cnt ? i : cnt - 1)) * a.H + h, w, l, col, o);
-  };
-  if (cnt > 0) {
-    load(0, A);
-    store_s0(0);
-  }
-  for (int64_t i = 0; i < cnt; i += 2) {
-    load(i + 1, B);
-    step(A, i);
-    if (i + 1 >= cnt) break;
-    load(i + 2, A);
-    step(B, i + 1);
-  }
-}
-
-// One chunk's operands of the reverse scan for wave w (key rows 16 w ..).  The terms that
-// do not involve Hn (scale Qg^T dO on the wave's rows; scale P^T dO, split over the waves:
-// token tile w % 4 of the contraction, output token tiles w / 4 + q NW / 4) are formed
-// from their loads after the previous chunk's step, so only their results stay live.
-template <int DK>
-struct CbRevOps {
-  static constexpr int MP = 16 / (DK / 16);
-  float kd[4][4];   // Kd[16 mt + lr][16 w + 4 gq + e]           A of Kd Hn
-  float wt[4][4];   // W[16 kt + 4 gq + e][16 w + lr]             A of W^T dD
-  float4 eg;        // e^G_n[16 w + 4 gq + i]
-  f32x4 qacc;       // scale Qg^T dO on the wave's rows
-  f32x4 pp[MP];     // scale P^T dO, the wave's share
-};
-template <int DK>
-struct CbRevRaw {
-  static constexpr int MP = CbRevOps<DK>::MP;
-  float4 qg[4];     // Qg^T[16 w + lr][16 kt + 4 gq + e]
-  float4 pt[MP];    // P^T[16 mt + lr][16 (w % 4) + 4 gq + e]
-  float dob[4][4];  // scale dO[16 kt + 4 gq + e][col]
-};
-
-template <int DK, int DV, typename InT>
-__device__ inline void cb_rev_load(const CbArgs& a, int64_t item, int h, int64_t t0, int64_t len, int w, int l,
-                                   int col, CbRevOps<DK>& o, CbRevRaw<DK>& r) {
-  using WS = CbWs<DK, DV>;
-  constexpr int NW = DK / 16;
-  const unsigned lr = l & 15, gq = l >> 4;
-  const auto Wr = cb_rsrc(a.W + item * WS::W, WS::W * 4);
-  const auto Kr = cb_rsrc(a.KdT + item * WS::KDT, WS::KDT * 4);
-  const auto Qr = cb_rsrc(a.QgT + item * WS::QGT, WS::QGT * 4);
-  const auto Pr = cb_rsrc(a.PT + item * WS::PT, WS::PT * 4);
-  const auto Er = cb_rsrc(a.eGn + item * WS::EGN, WS::EGN * 4);
-  // the chunk's rows of dout for the slice's 16 columns; tokens past the chunk's end fall
-  // outside the resource and read 0
-  const unsigned tstride = (unsigned)a.H * DV;
-  const auto Dr = cb_rsrc(reinterpret_cast<const InT*>(a.dout) + (t0 * a.H + h) * DV + (col & ~15),
-                          (uint32_t)(((len - 1) * tstride + 16) * sizeof(InT)));
-#pragma unroll
-  for (unsigned m = 0; m < 4; ++m) {
-    r.qg[m] = cb_ld4(Qr, 4 * ((16 * w + lr) * 64 + 16 * m + 4 * gq));
-#pragma unroll
-    for (unsigned e = 0; e < 4; ++e) {
-      o.kd[m][e] = cb_ld1(Kr, 4 * ((16 * w + 4 * gq + e) * 64 + 16 * m + lr));
-      o.wt[m][e] = cb_ld1(Wr, 4 * ((16 * m + 4 * gq + e) * DK + 16 * w + lr));
-      const unsigned t = 16 * m + 4 * gq + e;
-      r.dob[m][e] = a.scale * cb_ld_io(Dr, t * tstride + lr, (const InT*)nullptr);
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < CbRevOps<DK>::MP; ++q) {
-    const unsigned mt = (unsigned)(w >> 2) + q * (NW / 4);
-    r.pt[q] = cb_ld4(Pr, 4 * ((16 * mt + lr) * 64 + 16 * (w & 3) + 4 * gq));
-  }
-  o.eg = cb_ld4(Er, 4 * (16 * w + 4 * gq));
-}
-
-template <int DK>
-__device__ inline void cb_rev_finish(int w, CbRevOps<DK>& o, const CbRevRaw<DK>& r) {
-  f32x4 q0 = zero4(), q1 = zero4();
-#pragma unroll
-  for (int kt = 0; kt < 4; kt += 2) {
-    q0 = mfma_f32(r.qg[kt].x, r.dob[kt][0], q0);
-    q1 = mfma_f32(r.qg[kt + 1].x, r.dob[kt + 1][0], q1);
-    q0 = mfma_f32(r.qg[kt].y, r.dob[kt][1], q0);
-    q1 = mfma_f32(r.qg[kt + 1].y, r.dob[kt + 1][1], q1);
-    q0 = mfma_f32(r.qg[kt].z, r.dob[kt][2], q0);
-    q1 = mfma_f32(r.qg[kt + 1].z, r.dob[kt + 1][2], q1);
-    q0 = mfma_f32(r.qg[kt].w, r.dob[kt][3], q0);
-    q1 = mfma_f32(r.qg[kt + 1].w, r.dob[kt + 1][3], q1);
-  }
-  o.qacc = q0 + q1;
-  float db[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    db[e] = r.dob[0][e];
-#pragma unroll
-    for (int kt = 1; kt < 4; ++kt)
-      if ((w & 3) == kt) db[e] = r.dob[kt][e];
-  }
-#pragma unroll
-  for (int q = 0; q < CbRevOps<DK>::MP; ++q) {
-    f32x4 pp = zero4();
-    pp = mfma_f32(r.pt[q].x, db[0], pp);
-    pp = mfma_f32(r.pt[q].y, db[1], pp);
-    pp = mfma_f32(r.pt[q].z, db[2], pp);
-    pp = mfma_f32(r.pt[q].w, db[3], pp);
-    o.pp[q] = pp;
-  }
-}
-
-// cb_state_rev_kernel: Hn and dD of every chunk, walking backwards; dh0.
-template <int DK, int DV, typename InT>
-__global__ __launch_bounds__(DK * 4) void cb_state_rev_kernel(CbArgs a) {
-  using WS = CbWs<DK, DV>;
-  using SM = CbScanSmem<DK>;
-  constexpr int NW = DK / 16, NS = DV / 16, MP = CbRevOps<DK>::MP;
-  extern __shared__ __align__(16) f32x4 red[];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, gq = l >> 4;
-  int64_t nh;
-  int s;
-  cb_scan_slot(blockIdx.x, a.N * a.H, NS, nh, s);
-  const int h = (int)(nh % a.H);
-  const int64_t n = nh / a.H;
-  int64_t c0, cnt;
-  cb_chunks(a, n, c0, cnt);
-  const int64_t seq0 = a.cu ? (int64_t)a.cu[n] : n * a.T;
-  const int64_t seqlen = a.cu ? (int64_t)(a.cu[n + 1] - a.cu[n]) : a.T;
-  const int col = 16 * s + lr;
-  const int row0 = 16 * w + 4 * gq;
-  f32x4 Hs;
-#pragma unroll
-  for (int ii = 0; ii < 4; ++ii) Hs[ii] = a.dht ? a.dht[((n * a.H + h) * DK + row0 + ii) * DV + col] : 0.f;
-  // Hn of chunk i - 1 is stored at the end of step i (see the forward scan)
   auto store_hn = [&](int64_t i) {
     float* st = a.st + ((c0 + i) * a.H + h) * WS::SB;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) st[WS::HN + (unsigned)((row0 + ii) * DV + col)] = Hs[ii];
   };
-  auto step = [&](const CbRevOps<DK>& o, int64_t i) {
-    float* st = a.st + ((c0 + i) * a.H + h) * WS::SB;
-    const int buf = (int)(i & 1);
+  {
+    const Res rf(a, itemf(0)), rr(a, itemr(cnt - 1));
+    load_fw(rf);
+    load_fu(rf);
+    load_fk(rf);
+    load_rk(rr);
+    load_rw(rr);
+    load_raw(rr, cnt - 1);
+    finish_raw();
+  }
+  store_s0(0);
+  store_hn(cnt - 1);
+  // step j: forward chunk j, reverse chunk cnt - 1 - j.  Loads past either end reload the
+  // end chunk, so every step issues the same loads and the wait counts stay exact.
+#pragma unroll 1
+  for (int64_t j = 0; j < cnt; ++j) {
+    const int64_t jr = cnt - 1 - j;
+    const int buf = (int)(j & 1);
+    const Res nf(a, itemf(j + 1)), nr(a, itemr(jr - 1));
+    load_raw(nr, jr - 1);  // raw operands of the next reverse chunk: formed after this step
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       f32x4 dp = zero4();
+      dp = mfma_f32(fw[mt].x, S[0], dp);
+      dp = mfma_f32(fw[mt].y, S[1], dp);
+      dp = mfma_f32(fw[mt].z, S[2], dp);
+      dp = mfma_f32(fw[mt].w, S[3], dp);
+      redF[SM::PART + ((buf * NW + w) * 4 + mt) * 64 + l] = dp;
+      f32x4 rp = zero4();
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dp = mfma_f32(o.kd[mt][e], Hs[e], dp);
+      for (int e = 0; e < 4; ++e) rp = mfma_f32(rk[mt][e], Hs[e], rp);
 #pragma unroll
       for (int q = 0; q < MP; ++q)
-        if ((w >> 2) + q * (NW / 4) == mt) dp += o.pp[q];
-      red[SM::PART + ((buf * NW + w) * 4 + mt) * 64 + l] = dp;
+        if ((w >> 2) + q * (NW / 4) == mt) rp += pp[q];
+      redR[SM::PART + ((buf * NW + w) * 4 + mt) * 64 + l] = rp;
     }
+    load_fw(nf);
+    load_rk(nr);
     __syncthreads();
-    if (w < 4) {  // dD, token tile w
-      const f32x4 dD = cb_red_sum<NW>(red + SM::PART, buf, w, l);
-      red[SM::SUM + (buf * 4 + w) * 64 + l] = dD;
+    if (sum_f) {  // D = U - W S0, token tile tw (kept for the gradient kernel)
+      const f32x4 sum = cb_red_sum<NW>(redF + SM::PART, buf, tw, l);
+      f32x4 D;
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) st[WS::DD + (unsigned)((16 * w + 4 * gq + ii) * DV + col)] = dD[ii];
+      for (int ii = 0; ii < 4; ++ii) D[ii] = fu[ii] - sum[ii];
+      redF[SM::SUM + (buf * 4 + tw) * 64 + l] = D;
+      float* st = a.st + ((c0 + j) * a.H + h) * WS::SB;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) st[WS::DM + (unsigned)((16 * tw + 4 * gq + ii) * DV + col)] = D[ii];
     }
+    if (sum_r) {  // dD, token tile tw
+      const f32x4 dD = cb_red_sum<NW>(redR + SM::PART, buf, tw, l);
+      redR[SM::SUM + (buf * 4 + tw) * 64 + l] = dD;
+      float* st = a.st + ((c0 + jr) * a.H + h) * WS::SB;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) st[WS::DD + (unsigned)((16 * tw + 4 * gq + ii) * DV + col)] = dD[ii];
+    }
+    load_fu(nf);
     __syncthreads();
-    f32x4 acc0 = {Hs[0] * o.eg.x, Hs[1] * o.eg.y, Hs[2] * o.eg.z, Hs[3] * o.eg.w};
-    f32x4 acc1 = o.qacc;
+    f32x4 fa[2] = {f32x4{S[0] * fe.x, S[1] * fe.y, S[2] * fe.z, S[3] * fe.w}, zero4()};
+    f32x4 ra[2] = {f32x4{Hs[0] * re.x, Hs[1] * re.y, Hs[2] * re.z, Hs[3] * re.w}, qacc};
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const f32x4 dD = red[SM::SUM + (buf * 4 + kt) * 64 + l];
-      if (kt & 1) {
+    for (int mt = 0; mt < 4; ++mt) {
+      const f32x4 Dt = redF[SM::SUM + (buf * 4 + mt) * 64 + l];
+      const f32x4 dDt = redR[SM::SUM + (buf * 4 + mt) * 64 + l];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc1 = mfma_f32(-o.wt[kt][e], dD[e], acc1);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc0 = mfma_f32(-o.wt[kt][e], dD[e], acc0);
+      for (int e = 0; e < 4; ++e) {
+        fa[mt & 1] = mfma_f32(f4_at(fk[mt], e), Dt[e], fa[mt & 1]);
+        ra[mt & 1] = mfma_f32(-rw[mt][e], dDt[e], ra[mt & 1]);
       }
     }
-    Hs = acc0 + acc1;
-    if (i > 0) store_hn(i - 1);
-  };
-  CbRevOps<DK> A, B;
-  CbRevRaw<DK> R;
-  // as in the forward scan, loads past the first chunk reload it
-  auto load = [&](int64_t i, CbRevOps<DK>& o) {
-    if (i < 0) i = 0;
-    const int64_t rem = seqlen - i * kChunk;
-    cb_rev_load<DK, DV, InT>(a, (c0 + i) * a.H + h, h, seq0 + i * kChunk, rem < kChunk ? rem : kChunk, w, l, col,
-                             o, R);
-  };
-  if (cnt > 0) {
-    load(cnt - 1, A);
-    store_hn(cnt - 1);
-    cb_rev_finish<DK>(w, A, R);
-  }
-  for (int64_t i = cnt - 1; i >= 0; i -= 2) {
-    load(i - 1, B);
-    step(A, i);
-    if (i < 1) break;
-    cb_rev_finish<DK>(w, B, R);
-    load(i - 2, A);
-    step(B, i - 1);
-    cb_rev_finish<DK>(w, A, R);
+    S = fa[0] + fa[1];
+    Hs = ra[0] + ra[1];
+    load_fk(nf);
+    load_rw(nr);
+    if (j + 1 < cnt) store_s0(j + 1);
+    if (jr > 0) store_hn(jr - 1);
+    finish_raw();
   }
   if (a.dh0) {
 #pragma unroll
@@ -831,37 +797,46 @@ __global__ __launch_bounds__(DK * 4) void cb_state_rev_kernel(CbArgs a) {
   }
 }
 
-__device__ inline float f4_at(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
-
 // ---------------------------------------------------------------------------------------
-// cb_grad_a_kernel: per (chunk, head).  Wave w owns key tiles [w KR, (w+1) KR) and value
-// tiles [w VR, (w+1) VR) of 16 channels.
-//   D^T = U^T - S0^T W^T for its value tiles (into LDS as B fragments over value channels)
+// cb_grad_a_kernel: per (chunk, head), DK / 16 waves.  Wave w owns key tile w and value
+// tiles [w VR, (w+1) VR) of 16 channels (with fewer value tiles than waves, waves 0.. own
+// one each and the rest none).
 //   over all value channels: dQg^T = scale S0 dO^T, dW = -dD S0^T, dKd^T = Hn D^T (its key
-//   tiles), dP = scale dO D^T (its share of the 10 lower tiles), rowsum(Hn o S0)
+//   tile), dP = scale dO D^T (its share of the 10 lower tiles), rowsum(Hn o S0)
 //   dX^T = dW^T T, dY^T = dD^T T, dv = beta dY, dA partial = -(dX W^T + dY U^T)
 // The results go to the item's state block, whose S0, Hn and dD this workgroup alone reads,
 // after a barrier that follows the last of those reads.
 
+template <int DK, int DV>
+struct CbGradASmem {
+  static constexpr int NW = DK / 16;
+  static constexpr int RED = NW * 10 * 64;  // dA partials, f32x4
+  static constexpr size_t DAS = (size_t)RED * 4;  // floats: dA [64][64]
+  static constexpr size_t DYV = DAS + 64 * 64;    // [NW][64]
+  static constexpr size_t BYTES = (DYV + NW * 64) * 4;
+};
+
 template <int DK, int DV, typename InT>
-__global__ __launch_bounds__(256) void cb_grad_a_kernel(CbArgs a) {
+__global__ __launch_bounds__(DK * 4) void cb_grad_a_kernel(CbArgs a) {
   using WS = CbWs<DK, DV>;
-  constexpr int NTK = DK / 16, NTV = DV / 16, KR = NTK / 4, VR = NTV / 4;
-  constexpr int RED = NTV * 4 * 64 * 4 > 4 * 10 * 64 * 4 ? NTV * 4 * 64 * 4 : 4 * 10 * 64 * 4;
-  __shared__ __align__(16) float sm[RED + 64 * 64 + 4 * 64];
-  f32x4* DT = reinterpret_cast<f32x4*>(sm);   // [NTV][4][64]
-  f32x4* red = reinterpret_cast<f32x4*>(sm);  // [4 waves][10 tiles][64], once DT is dead
-  float* dAs = sm + RED;                       // [64][64]
-  float* dyv = dAs + 64 * 64;                  // [4 waves][64]
+  using SM = CbGradASmem<DK, DV>;
+  constexpr int NW = DK / 16, NTK = DK / 16, NTV = DV / 16;
+  constexpr int VR = NTV >= NW ? NTV / NW : 1;  // value tiles per wave
+  constexpr int MAXP = (10 + NW - 1) / NW;      // lower tiles of dP per wave
+  extern __shared__ __align__(16) float sm[];
+  f32x4* red = reinterpret_cast<f32x4*>(sm);  // [NW][10][64]
+  float* dAs = sm + SM::DAS;                   // [64][64]
+  float* dyv = sm + SM::DYV;                   // [NW][64]
   const int64_t item = blockIdx.x;
   const int64_t c = item / a.H;
   const int h = (int)(item - c * a.H);
   CbItem it;
   if (!cb_item(a, c, it)) return;  // whole workgroup
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, gq = l >> 4;
+  const int tid = threadIdx.x, l = tid & 63, lr = l & 15, gq = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const bool vown = NTV >= NW || w < NTV;  // this wave owns value tiles
+  const int vt0 = w * VR;                  // its first value tile
   float* st = a.st + item * WS::SB;
-  const float* S0 = st + WS::S0;
-  const float* Hn = st + WS::HN;
   const float* dD = st + WS::DD;
   const float* Wi = a.W + item * WS::W;
   const float* Ui = a.U + item * WS::U;
@@ -870,105 +845,51 @@ __global__ __launch_bounds__(256) void cb_grad_a_kernel(CbArgs a) {
   const float* Ei = a.eGn + item * WS::EGN;
   const InT* dO = reinterpret_cast<const InT*>(a.dout);
   const InT* V = reinterpret_cast<const InT*>(a.v);
-
   // the item's state block and the chunk's rows of dout: buffer resources, 32-bit offsets
   const auto Sr = cb_rsrc(st, WS::SB * 4);
-  const auto Wr = cb_rsrc(Wi, WS::W * 4);
   const uint32_t tsd = (uint32_t)a.H * DV;  // token stride of dout, v (elements)
   const auto Or = cb_rsrc(dO + (it.tok0 * a.H + h) * DV, (uint32_t)(((it.len - 1) * tsd + DV) * sizeof(InT)));
 
-  // 1. D^T for this wave's value tiles; the next key tile's operands load during the current one
-  {
-    struct Ops {
-      float4 wv[4];    // W[16 nt + lr][16 kt + 4 gq + e]            B = W^T
-      float s0[VR][4]; // S0[16 kt + 4 gq + e][16 (w VR + r) + lr]   A = -S0^T
-    };
-    auto load = [&](int kt, Ops& o) {
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) o.wv[nt] = cb_ld4(Wr, 4 * ((16 * nt + lr) * DK + 16 * kt + 4 * gq));
-#pragma unroll
-      for (int r = 0; r < VR; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          o.s0[r][e] = cb_ld1(Sr, 4 * (WS::S0 + (16 * kt + 4 * gq + e) * DV + 16 * (w * VR + r) + lr));
-    };
-    f32x4 Dt[VR][4];
-#pragma unroll
-    for (int r = 0; r < VR; ++r)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const float4 u = *reinterpret_cast<const float4*>(Ui + (16 * nt + lr) * DV + 16 * (w * VR + r) + 4 * gq);
-        Dt[r][nt] = f32x4{u.x, u.y, u.z, u.w};
-      }
-    auto work = [&](const Ops& o) {
-#pragma unroll
-      for (int r = 0; r < VR; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) Dt[r][nt] = mfma_f32(-o.s0[r][e], f4_at(o.wv[nt], e), Dt[r][nt]);
-    };
-    Ops A, B;
-    load(0, A);
-#pragma unroll 1
-    for (int kt = 0; kt < NTK; kt += 2) {
-      load(kt + 1, B);
-      work(A);
-      load(kt + 2 < NTK ? kt + 2 : kt + 1, A);
-      work(B);
-    }
-#pragma unroll
-    for (int r = 0; r < VR; ++r)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) DT[((w * VR + r) * 4 + nt) * 64 + l] = Dt[r][nt];
-  }
-  __syncthreads();
-
-  // 2. products over the value channels, the next value tile's operands loading during the
+  // 1. products over the value channels, the next value tile's operands loading during the
   // current one
-  f32x4 gQ[KR][4], gW[4][KR], gK[KR][4], gP[3];
-  float gn[KR];
+  f32x4 gQ[4], gW[4], gK[4], gP[MAXP];
+  float gn = 0.f;
 #pragma unroll
-  for (int r = 0; r < KR; ++r) {
-    gn[r] = 0.f;
+  for (int nt = 0; nt < 4; ++nt) gQ[nt] = gW[nt] = gK[nt] = zero4();
+  int pI[MAXP], pJ[MAXP];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) gQ[r][nt] = gW[nt][r] = gK[r][nt] = zero4();
-  }
-  gP[0] = gP[1] = gP[2] = zero4();
-  int pI[3], pJ[3];
-#pragma unroll
-  for (int qq = 0; qq < 3; ++qq) {
-    const int p = w + 4 * qq;
+  for (int qq = 0; qq < MAXP; ++qq) {
+    const int p = w + NW * qq;
+    gP[qq] = zero4();
     pI[qq] = p < 10 ? cb_tile_i(p) : 0;
     pJ[qq] = p < 10 ? cb_tile_j(p) : 0;
   }
-  const int np = w < 2 ? 3 : 2;
   struct Ops2 {
-    float4 s0v[KR], hnv[KR];  // S0, Hn rows 16 (w KR + r) + lr, value channels 16 kt + 4 gq ..
-    float4 ddv[4], dov[4];    // dD, dout rows 16 mt + lr (dout zero past the chunk's end)
+    float4 s0v, hnv;        // S0, Hn row 16 w + lr, value channels 16 kt + 4 gq ..
+    float4 ddv[4], dov[4];  // dD, dout rows 16 mt + lr (dout zero past the chunk's end)
+    float4 dtv[4];          // D rows 16 mt + lr: B fragments of D^T over value channels
   };
   auto load2 = [&](int kt, Ops2& o) {
-#pragma unroll
-    for (int r = 0; r < KR; ++r) {
-      const uint32_t off = (16 * (w * KR + r) + lr) * DV + 16 * kt + 4 * gq;
-      o.s0v[r] = cb_ld4(Sr, 4 * (WS::S0 + off));
-      o.hnv[r] = cb_ld4(Sr, 4 * (WS::HN + off));
-    }
+    const uint32_t off = (16 * w + lr) * DV + 16 * kt + 4 * gq;
+    o.s0v = cb_ld4(Sr, 4 * (WS::S0 + off));
+    o.hnv = cb_ld4(Sr, 4 * (WS::HN + off));
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      o.ddv[mt] = cb_ld4(Sr, 4 * (WS::DD + (16 * mt + lr) * DV + 16 * kt + 4 * gq));
+      const uint32_t ro = (16 * mt + lr) * DV + 16 * kt + 4 * gq;
+      o.ddv[mt] = cb_ld4(Sr, 4 * (WS::DD + ro));
+      o.dtv[mt] = cb_ld4(Sr, 4 * (WS::DM + ro));
       o.dov[mt] = cb_ld4_io(Or, (16 * mt + lr) * tsd + 16 * kt + 4 * gq, (const InT*)nullptr);
     }
   };
   auto work2 = [&](const Ops2& o, int kt) {
     f32x4 dtv[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) dtv[mt] = DT[(kt * 4 + mt) * 64 + l];
+    for (int mt = 0; mt < 4; ++mt) dtv[mt] = f32x4{o.dtv[mt].x, o.dtv[mt].y, o.dtv[mt].z, o.dtv[mt].w};
     // the wave's dP tiles: A rows of dout (token tile I), B fragments of D^T (token tile J)
-    float4 pa[3];
-    f32x4 pb[3];
+    float4 pa[MAXP];
+    f32x4 pb[MAXP];
 #pragma unroll
-    for (int qq = 0; qq < 3; ++qq) {
+    for (int qq = 0; qq < MAXP; ++qq) {
       pa[qq] = o.dov[0];
       pb[qq] = dtv[0];
 #pragma unroll
@@ -979,20 +900,17 @@ __global__ __launch_bounds__(256) void cb_grad_a_kernel(CbArgs a) {
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
+      const float sv = f4_at(o.s0v, e), hv = f4_at(o.hnv, e);
+      gn = fmaf(sv, hv, gn);
 #pragma unroll
-      for (int r = 0; r < KR; ++r) {
-        const float sv = f4_at(o.s0v[r], e), hv = f4_at(o.hnv[r], e);
-        gn[r] = fmaf(sv, hv, gn[r]);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          gQ[r][nt] = mfma_f32(sv, f4_at(o.dov[nt], e), gQ[r][nt]);
-          gW[nt][r] = mfma_f32(f4_at(o.ddv[nt], e), sv, gW[nt][r]);
-          gK[r][nt] = mfma_f32(hv, dtv[nt][e], gK[r][nt]);
-        }
+      for (int nt = 0; nt < 4; ++nt) {
+        gQ[nt] = mfma_f32(sv, f4_at(o.dov[nt], e), gQ[nt]);
+        gW[nt] = mfma_f32(f4_at(o.ddv[nt], e), sv, gW[nt]);
+        gK[nt] = mfma_f32(hv, dtv[nt][e], gK[nt]);
       }
 #pragma unroll
-      for (int qq = 0; qq < 3; ++qq)
-        if (qq < np) gP[qq] = mfma_f32(f4_at(pa[qq], e), pb[qq][e], gP[qq]);
+      for (int qq = 0; qq < MAXP; ++qq)
+        if (w + NW * qq < 10) gP[qq] = mfma_f32(f4_at(pa[qq], e), pb[qq][e], gP[qq]);
     }
   };
   {
@@ -1006,61 +924,60 @@ __global__ __launch_bounds__(256) void cb_grad_a_kernel(CbArgs a) {
       work2(B, kt + 1);
     }
   }
+  gn = rows4_sum(gn);
 #pragma unroll
-  for (int r = 0; r < KR; ++r) {
-    gn[r] = rows4_sum(gn[r]);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      gQ[r][nt] *= a.scale;
-      gW[nt][r] = -gW[nt][r];
-    }
+  for (int nt = 0; nt < 4; ++nt) {
+    gQ[nt] *= a.scale;
+    gW[nt] = -gW[nt];
   }
 #pragma unroll
-  for (int qq = 0; qq < 3; ++qq) gP[qq] *= a.scale;
+  for (int qq = 0; qq < MAXP; ++qq) gP[qq] *= a.scale;
 
-  // 3. dX^T = dW^T T, dY^T = dD^T T (T lower: token tile I >= J)
-  f32x4 gX[KR][4], gY[VR][4];
+  // 2. dX^T = dW^T T, dY^T = dD^T T (T lower: token tile I >= J)
+  f32x4 gX[4], gY[VR][4];
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
-#pragma unroll
-    for (int r = 0; r < KR; ++r) gX[r][J] = zero4();
+    gX[J] = zero4();
 #pragma unroll
     for (int r = 0; r < VR; ++r) gY[r][J] = zero4();
 #pragma unroll
     for (int I = J; I < 4; ++I) {
-      const float4 tv = *reinterpret_cast<const float4*>(Ti + (16 * J + lr) * 64 + 16 * I + 4 * gq);
+      const float4 tv = *reinterpret_cast<const float4*>(Ti + cb_blk(I, J) * 256 + lr * 16 + 4 * gq);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float te = f4_at(tv, e);
+        gX[J] = mfma_f32(gW[I][e], te, gX[J]);
+        if (vown) {
 #pragma unroll
-        for (int r = 0; r < KR; ++r) gX[r][J] = mfma_f32(gW[I][r][e], te, gX[r][J]);
-#pragma unroll
-        for (int r = 0; r < VR; ++r)
-          gY[r][J] = mfma_f32(dD[(16 * I + 4 * gq + e) * DV + 16 * (w * VR + r) + lr], te, gY[r][J]);
+          for (int r = 0; r < VR; ++r)
+            gY[r][J] = mfma_f32(dD[(16 * I + 4 * gq + e) * DV + 16 * (vt0 + r) + lr], te, gY[r][J]);
+        }
       }
     }
   }
   // dv = beta dY; the dY o V part of dbeta
   {
     float dyp[4] = {0.f, 0.f, 0.f, 0.f};
+    if (vown) {
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
-      const int t = 16 * J + lr;
-      const bool valid = t < it.len;
-      const int64_t row = (it.tok0 + t) * a.H + h;
-      const float bt = valid ? load1(reinterpret_cast<const InT*>(a.beta) + row) : 0.f;
+      for (int J = 0; J < 4; ++J) {
+        const int t = 16 * J + lr;
+        const bool valid = t < it.len;
+        const int64_t row = (it.tok0 + t) * a.H + h;
+        const float bt = valid ? load1(reinterpret_cast<const InT*>(a.beta) + row) : 0.f;
 #pragma unroll
-      for (int r = 0; r < VR; ++r) {
-        const int cv = 16 * (w * VR + r) + 4 * gq;
-        float vv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (valid) load4(V + row * DV + cv, vv);
-        float o[4];
+        for (int r = 0; r < VR; ++r) {
+          const int cv = 16 * (vt0 + r) + 4 * gq;
+          float vv[4] = {0.f, 0.f, 0.f, 0.f};
+          if (valid) load4(V + row * DV + cv, vv);
+          float o[4];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          o[ii] = bt * gY[r][J][ii];
-          dyp[J] = fmaf(gY[r][J][ii], vv[ii], dyp[J]);
+          for (int ii = 0; ii < 4; ++ii) {
+            o[ii] = bt * gY[r][J][ii];
+            dyp[J] = fmaf(gY[r][J][ii], vv[ii], dyp[J]);
+          }
+          if (valid) store4(reinterpret_cast<InT*>(a.dv) + row * DV + cv, o);
         }
-        if (valid) store4(reinterpret_cast<InT*>(a.dv) + row * DV + cv, o);
       }
     }
 #pragma unroll
@@ -1069,37 +986,40 @@ __global__ __launch_bounds__(256) void cb_grad_a_kernel(CbArgs a) {
       if (gq == 0) dyv[w * 64 + 16 * J + lr] = sum;
     }
   }
-  __syncthreads();  // every wave is past its last read of DT
-
-  // 4. dA partial over this wave's key and value tiles, all 10 lower tiles
+  // 3. dA partial over this wave's key and value tiles, all 10 lower tiles
 #pragma unroll
   for (int p = 0; p < 10; ++p) {
     const int I = cb_tile_i(p), J = cb_tile_j(p);
     f32x4 acc = zero4();
+    {
+      const float4 wv = *reinterpret_cast<const float4*>(Wi + (16 * J + lr) * DK + 16 * w + 4 * gq);
 #pragma unroll
-    for (int r = 0; r < KR; ++r) {
-      const float4 wv = *reinterpret_cast<const float4*>(Wi + (16 * J + lr) * DK + 16 * (w * KR + r) + 4 * gq);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc = mfma_f32(gX[r][I][e], f4_at(wv, e), acc);
+      for (int e = 0; e < 4; ++e) acc = mfma_f32(gX[I][e], f4_at(wv, e), acc);
     }
+    if (vown) {
 #pragma unroll
-    for (int r = 0; r < VR; ++r) {
-      const float4 uv = *reinterpret_cast<const float4*>(Ui + (16 * J + lr) * DV + 16 * (w * VR + r) + 4 * gq);
+      for (int r = 0; r < VR; ++r) {
+        const float4 uv = *reinterpret_cast<const float4*>(Ui + (16 * J + lr) * DV + 16 * (vt0 + r) + 4 * gq);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc = mfma_f32(gY[r][I][e], f4_at(uv, e), acc);
+        for (int e = 0; e < 4; ++e) acc = mfma_f32(gY[r][I][e], f4_at(uv, e), acc);
+      }
     }
     red[(w * 10 + p) * 64 + l] = acc;
   }
   __syncthreads();  // all reads of S0, Hn and dD are complete: the state block is free
 
-  // 5. results: dA (strictly lower, summed over the waves in order), dP, the fragments
+  // 4. results: dA (strictly lower, summed over the waves in order), dP, the fragments
 #pragma unroll
-  for (int qq = 0; qq < 3; ++qq) {
-    const int p = w + 4 * qq;
+  for (int qq = 0; qq < MAXP; ++qq) {
+    const int p = w + NW * qq;
     if (p >= 10) continue;
     const int I = cb_tile_i(p), J = cb_tile_j(p);
-    const f32x4 sum = ((red[(0 * 10 + p) * 64 + l] + red[(1 * 10 + p) * 64 + l]) + red[(2 * 10 + p) * 64 + l]) +
-                      red[(3 * 10 + p) * 64 + l];
+    f32x4 part[NW];
+#pragma unroll
+    for (int v = 0; v < NW; ++v) part[v] = red[(v * 10 + p) * 64 + l];
+    f32x4 sum = part[0];
+#pragma unroll
+    for (int v = 1; v < NW; ++v) sum += part[v];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int i = 16 * I + 4 * gq + ii, j = 16 * J + lr;
@@ -1111,23 +1031,22 @@ __global__ __launch_bounds__(256) void cb_grad_a_kernel(CbArgs a) {
     }
   }
 #pragma unroll
-  for (int r = 0; r < KR; ++r) {
-    const int kc = w * KR + r;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const size_t f = ((size_t)(kc * 4 + nt) * 64 + l) * 4;
-      *reinterpret_cast<f32x4*>(st + WS::GQ + f) = gQ[r][nt];
-      *reinterpret_cast<f32x4*>(st + WS::GKD + f) = gK[r][nt];
-      *reinterpret_cast<f32x4*>(st + WS::GX + f) = gX[r][nt];
-    }
-    if (gq == 0) st[WS::GN + 16 * kc + lr] = Ei[16 * kc + lr] * gn[r];
+  for (int nt = 0; nt < 4; ++nt) {
+    const size_t f = ((size_t)(w * 4 + nt) * 64 + l) * 4;
+    *reinterpret_cast<f32x4*>(st + WS::GQ + f) = gQ[nt];
+    *reinterpret_cast<f32x4*>(st + WS::GKD + f) = gK[nt];
+    *reinterpret_cast<f32x4*>(st + WS::GX + f) = gX[nt];
   }
+  if (gq == 0) st[WS::GN + 16 * w + lr] = Ei[16 * w + lr] * gn;
   __syncthreads();
   if (tid < 64) {
     const int t = tid;
     float s = 0.f;
-    for (int j = 0; j < t; ++j) s = fmaf(dAs[t * 64 + j], Li[t * 64 + j], s);
-    st[WS::GB + t] = s + ((dyv[t] + dyv[64 + t]) + dyv[128 + t]) + dyv[192 + t];
+    for (int j = 0; j < t; ++j) s = fmaf(dAs[t * 64 + j], Li[cb_blk(t >> 4, j >> 4) * 256 + (t & 15) * 16 + (j & 15)], s);
+    float y = dyv[t];
+#pragma unroll
+    for (int v = 1; v < NW; ++v) y += dyv[v * 64 + t];
+    st[WS::GB + t] = s + y;
   }
 }
 
@@ -1176,7 +1095,8 @@ __global__ __launch_bounds__(DK * 4) void cb_grad_b_kernel(CbArgs a) {
   float* dots = sm + S::DOT;
   float* dbp = sm + S::DBP;
   float* dpd = sm + S::DPD;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, gq = l >> 4;
+  const int tid = threadIdx.x, l = tid & 63, lr = l & 15, gq = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const float* st = a.st + item * WS::SB;
   cb_load_rows<DK, InT, NT>(a, it, h, kh, qh, G, bs, nrm);
   __syncthreads();
@@ -1440,6 +1360,7 @@ __global__ __launch_bounds__(DK * 4) void cb_grad_b_kernel(CbArgs a) {
 #pragma unroll
       for (int v = 1; v < NW; ++v) dot += dsum[v * 64 + t];
       const float nv = nrm[which * 128 + t];
+      const float inv = nv > 0.f ? 1.f / nv : 0.f;
       const int ex = (int)nrm[which * 128 + 64 + t];
 #pragma unroll
       for (int r = 0; r < KR; ++r) {
@@ -1448,7 +1369,7 @@ __global__ __launch_bounds__(DK * 4) void cb_grad_b_kernel(CbArgs a) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const float dx = which ? dkh[r][nt][ii] : dqh[r][nt][ii];
-          o[ii] = nv > 0.f ? ldexpf((dx - xh[t * KS + cb + ii] * dot) / nv, -ex) : 0.f;
+          o[ii] = ldexpf((dx - xh[t * KS + cb + ii] * dot) * inv, -ex);
         }
         if (valid) store4(reinterpret_cast<InT*>(which ? a.dk : a.dq) + row * DK + cb, o);
       }

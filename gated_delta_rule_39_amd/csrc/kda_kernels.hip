@@ -287,15 +287,15 @@ static hipError_t launch_chunk_backward_t(const BackwardPlan& p, hipStream_t str
   }
   const int64_t chains = p.N * (int64_t)p.H * (DV / 16);
   const size_t ssm = CbScanSmem<DK>::BYTES;
-  auto sf = cb_state_fwd_kernel<DK, DV>;
-  auto sr = cb_state_rev_kernel<DK, DV, InT>;
-  if ((e = allow_smem(sf, ssm)) != hipSuccess || (e = allow_smem(sr, ssm)) != hipSuccess) return e;
-  hipLaunchKernelGGL(sf, dim3((unsigned)chains), dim3(DK * 4), ssm, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(sr, dim3((unsigned)chains), dim3(DK * 4), ssm, stream, a);
+  auto sc = cb_state_scan_kernel<DK, DV, InT>;
+  if ((e = allow_smem(sc, ssm)) != hipSuccess) return e;
+  hipLaunchKernelGGL(sc, dim3((unsigned)chains), dim3(DK * 4), ssm, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (items > 0) {
-    hipLaunchKernelGGL((cb_grad_a_kernel<DK, DV, InT>), dim3((unsigned)items), dim3(256), 0, stream, a);
+    auto ga = cb_grad_a_kernel<DK, DV, InT>;
+    const size_t gsm = CbGradASmem<DK, DV>::BYTES;
+    if ((e = allow_smem(ga, gsm)) != hipSuccess) return e;
+    hipLaunchKernelGGL(ga, dim3((unsigned)items), dim3(DK * 4), gsm, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     auto gb = cb_grad_b_kernel<DK, DV, InT>;
     const size_t smem = CbGradSmem<DK>::BYTES;
