@@ -807,12 +807,20 @@ __global__ __launch_bounds__(DK * 4) void cb_state_scan_kernel(CbArgs a) {
 // The results go to the item's state block, whose S0, Hn and dD this workgroup alone reads,
 // after a barrier that follows the last of those reads.
 
+// LDS of cb_grad_a_kernel: the chunk's rows of dD, D and dout (fp32, rows padded to DV + 4
+// floats so the 16 rows a fragment load touches fall in different banks), staged once for
+// all waves; later the waves' dA partials in the same space; dA; the dY o V row sums.
 template <int DK, int DV>
 struct CbGradASmem {
   static constexpr int NW = DK / 16;
-  static constexpr int RED = NW * 10 * 64;  // dA partials, f32x4
-  static constexpr size_t DAS = (size_t)RED * 4;  // floats: dA [64][64]
-  static constexpr size_t DYV = DAS + 64 * 64;    // [NW][64]
+  static constexpr int RS = DV + 4;                 // staged row stride, floats
+  static constexpr size_t DDS = 0;                  // dD [64][RS]
+  static constexpr size_t DMS = DDS + 64 * RS;      // D [64][RS]
+  static constexpr size_t DOS = DMS + 64 * RS;      // dout [64][RS]
+  static constexpr size_t STAGE = DOS + 64 * RS;
+  static constexpr size_t REDF = (size_t)NW * 10 * 64 * 4;  // dA partials [NW][10][64] f32x4, as floats
+  static constexpr size_t DAS = (STAGE > REDF ? STAGE : REDF);  // dA [64][64]
+  static constexpr size_t DYV = DAS + 64 * 64;      // [NW][64]
   static constexpr size_t BYTES = (DYV + NW * 64) * 4;
 };
 
@@ -820,11 +828,14 @@ template <int DK, int DV, typename InT>
 __global__ __launch_bounds__(DK * 4) void cb_grad_a_kernel(CbArgs a) {
   using WS = CbWs<DK, DV>;
   using SM = CbGradASmem<DK, DV>;
-  constexpr int NW = DK / 16, NTK = DK / 16, NTV = DV / 16;
+  constexpr int NW = DK / 16, NT = DK * 4, NTV = DV / 16, RS = SM::RS;
   constexpr int VR = NTV >= NW ? NTV / NW : 1;  // value tiles per wave
   constexpr int MAXP = (10 + NW - 1) / NW;      // lower tiles of dP per wave
   extern __shared__ __align__(16) float sm[];
-  f32x4* red = reinterpret_cast<f32x4*>(sm);  // [NW][10][64]
+  float* dDs = sm + SM::DDS;
+  float* Dms = sm + SM::DMS;
+  float* dOs = sm + SM::DOS;
+  f32x4* red = reinterpret_cast<f32x4*>(sm);  // [NW][10][64], once the staged rows are dead
   float* dAs = sm + SM::DAS;                   // [64][64]
   float* dyv = sm + SM::DYV;                   // [NW][64]
   const int64_t item = blockIdx.x;
@@ -837,21 +848,36 @@ __global__ __launch_bounds__(DK * 4) void cb_grad_a_kernel(CbArgs a) {
   const bool vown = NTV >= NW || w < NTV;  // this wave owns value tiles
   const int vt0 = w * VR;                  // its first value tile
   float* st = a.st + item * WS::SB;
-  const float* dD = st + WS::DD;
   const float* Wi = a.W + item * WS::W;
   const float* Ui = a.U + item * WS::U;
   const float* Ti = a.TT + item * WS::TT;
   const float* Li = a.L + item * WS::L;
   const float* Ei = a.eGn + item * WS::EGN;
-  const InT* dO = reinterpret_cast<const InT*>(a.dout);
   const InT* V = reinterpret_cast<const InT*>(a.v);
   // the item's state block and the chunk's rows of dout: buffer resources, 32-bit offsets
   const auto Sr = cb_rsrc(st, WS::SB * 4);
   const uint32_t tsd = (uint32_t)a.H * DV;  // token stride of dout, v (elements)
-  const auto Or = cb_rsrc(dO + (it.tok0 * a.H + h) * DV, (uint32_t)(((it.len - 1) * tsd + DV) * sizeof(InT)));
+  const auto Or = cb_rsrc(reinterpret_cast<const InT*>(a.dout) + (it.tok0 * a.H + h) * DV,
+                          (uint32_t)(((it.len - 1) * tsd + DV) * sizeof(InT)));
 
-  // 1. products over the value channels, the next value tile's operands loading during the
-  // current one
+  // 0. stage dD, D and dout (zero past the chunk's end) in LDS
+  {
+    constexpr int C4 = DV / 4;
+#pragma unroll
+    for (int j = 0; j < 64 * C4 / NT; ++j) {
+      const int e4 = tid + NT * j;
+      const int t = e4 / C4, c4 = 4 * (e4 - t * C4);
+      const float4 dd = cb_ld4(Sr, 4 * (WS::DD + t * DV + c4));
+      const float4 dm = cb_ld4(Sr, 4 * (WS::DM + t * DV + c4));
+      const float4 dz = cb_ld4_io(Or, t * tsd + c4, (const InT*)nullptr);
+      *reinterpret_cast<float4*>(dDs + t * RS + c4) = dd;
+      *reinterpret_cast<float4*>(Dms + t * RS + c4) = dm;
+      *reinterpret_cast<float4*>(dOs + t * RS + c4) = dz;
+    }
+  }
+
+  // 1. products over the value channels: S0 and Hn rows from HBM (two value tiles ahead),
+  // dD, D and dout rows from LDS
   f32x4 gQ[4], gW[4], gK[4], gP[MAXP];
   float gn = 0.f;
 #pragma unroll
@@ -864,37 +890,33 @@ __global__ __launch_bounds__(DK * 4) void cb_grad_a_kernel(CbArgs a) {
     pI[qq] = p < 10 ? cb_tile_i(p) : 0;
     pJ[qq] = p < 10 ? cb_tile_j(p) : 0;
   }
-  struct Ops2 {
-    float4 s0v, hnv;        // S0, Hn row 16 w + lr, value channels 16 kt + 4 gq ..
-    float4 ddv[4], dov[4];  // dD, dout rows 16 mt + lr (dout zero past the chunk's end)
-    float4 dtv[4];          // D rows 16 mt + lr: B fragments of D^T over value channels
+  struct SH {
+    float4 s0v, hnv;  // S0, Hn row 16 w + lr, value channels 16 kt + 4 gq ..
   };
-  auto load2 = [&](int kt, Ops2& o) {
-    const uint32_t off = (16 * w + lr) * DV + 16 * kt + 4 * gq;
+  auto loadsh = [&](int kt, SH& o) {
+    const int k = kt < NTV ? kt : NTV - 1;
+    const uint32_t off = (16 * w + lr) * DV + 16 * k + 4 * gq;
     o.s0v = cb_ld4(Sr, 4 * (WS::S0 + off));
     o.hnv = cb_ld4(Sr, 4 * (WS::HN + off));
+  };
+  auto work = [&](const SH& o, int kt) {
+    float4 ddv[4], dtv[4], dov[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const uint32_t ro = (16 * mt + lr) * DV + 16 * kt + 4 * gq;
-      o.ddv[mt] = cb_ld4(Sr, 4 * (WS::DD + ro));
-      o.dtv[mt] = cb_ld4(Sr, 4 * (WS::DM + ro));
-      o.dov[mt] = cb_ld4_io(Or, (16 * mt + lr) * tsd + 16 * kt + 4 * gq, (const InT*)nullptr);
+      const int ro = (16 * mt + lr) * RS + 16 * kt + 4 * gq;
+      ddv[mt] = *reinterpret_cast<const float4*>(dDs + ro);
+      dtv[mt] = *reinterpret_cast<const float4*>(Dms + ro);
+      dov[mt] = *reinterpret_cast<const float4*>(dOs + ro);
     }
-  };
-  auto work2 = [&](const Ops2& o, int kt) {
-    f32x4 dtv[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) dtv[mt] = f32x4{o.dtv[mt].x, o.dtv[mt].y, o.dtv[mt].z, o.dtv[mt].w};
     // the wave's dP tiles: A rows of dout (token tile I), B fragments of D^T (token tile J)
-    float4 pa[MAXP];
-    f32x4 pb[MAXP];
+    float4 pa[MAXP], pb[MAXP];
 #pragma unroll
     for (int qq = 0; qq < MAXP; ++qq) {
-      pa[qq] = o.dov[0];
+      pa[qq] = dov[0];
       pb[qq] = dtv[0];
 #pragma unroll
       for (int mt = 1; mt < 4; ++mt) {
-        if (pI[qq] == mt) pa[qq] = o.dov[mt];
+        if (pI[qq] == mt) pa[qq] = dov[mt];
         if (pJ[qq] == mt) pb[qq] = dtv[mt];
       }
     }
@@ -904,24 +926,30 @@ __global__ __launch_bounds__(DK * 4) void cb_grad_a_kernel(CbArgs a) {
       gn = fmaf(sv, hv, gn);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        gQ[nt] = mfma_f32(sv, f4_at(o.dov[nt], e), gQ[nt]);
-        gW[nt] = mfma_f32(f4_at(o.ddv[nt], e), sv, gW[nt]);
-        gK[nt] = mfma_f32(hv, dtv[nt][e], gK[nt]);
+        gQ[nt] = mfma_f32(sv, f4_at(dov[nt], e), gQ[nt]);
+        gW[nt] = mfma_f32(f4_at(ddv[nt], e), sv, gW[nt]);
+        gK[nt] = mfma_f32(hv, f4_at(dtv[nt], e), gK[nt]);
       }
 #pragma unroll
       for (int qq = 0; qq < MAXP; ++qq)
-        if (w + NW * qq < 10) gP[qq] = mfma_f32(f4_at(pa[qq], e), pb[qq][e], gP[qq]);
+        if (w + NW * qq < 10) gP[qq] = mfma_f32(f4_at(pa[qq], e), f4_at(pb[qq], e), gP[qq]);
     }
   };
   {
-    Ops2 A, B;
-    load2(0, A);
+    SH A, B, C;
+    loadsh(0, A);
+    loadsh(1, B);
+    __syncthreads();  // staged rows complete
 #pragma unroll 1
-    for (int kt = 0; kt < NTV; kt += 2) {
-      load2(kt + 1, B);
-      work2(A, kt);
-      load2(kt + 2 < NTV ? kt + 2 : kt + 1, A);
-      work2(B, kt + 1);
+    for (int kt = 0; kt < NTV; kt += 3) {
+      loadsh(kt + 2, C);
+      work(A, kt);
+      if (kt + 1 >= NTV) break;
+      loadsh(kt + 3, A);
+      work(B, kt + 1);
+      if (kt + 2 >= NTV) break;
+      loadsh(kt + 4, B);
+      work(C, kt + 2);
     }
   }
   gn = rows4_sum(gn);
@@ -934,6 +962,9 @@ __global__ __launch_bounds__(DK * 4) void cb_grad_a_kernel(CbArgs a) {
   for (int qq = 0; qq < MAXP; ++qq) gP[qq] *= a.scale;
 
   // 2. dX^T = dW^T T, dY^T = dD^T T (T lower: token tile I >= J)
+  float4 tv[10];
+#pragma unroll
+  for (int p = 0; p < 10; ++p) tv[p] = *reinterpret_cast<const float4*>(Ti + p * 256 + lr * 16 + 4 * gq);
   f32x4 gX[4], gY[VR][4];
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
@@ -942,41 +973,59 @@ __global__ __launch_bounds__(DK * 4) void cb_grad_a_kernel(CbArgs a) {
     for (int r = 0; r < VR; ++r) gY[r][J] = zero4();
 #pragma unroll
     for (int I = J; I < 4; ++I) {
-      const float4 tv = *reinterpret_cast<const float4*>(Ti + cb_blk(I, J) * 256 + lr * 16 + 4 * gq);
+      const float4 t4 = tv[cb_blk(I, J)];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float te = f4_at(tv, e);
+        const float te = f4_at(t4, e);
         gX[J] = mfma_f32(gW[I][e], te, gX[J]);
         if (vown) {
 #pragma unroll
           for (int r = 0; r < VR; ++r)
-            gY[r][J] = mfma_f32(dD[(16 * I + 4 * gq + e) * DV + 16 * (vt0 + r) + lr], te, gY[r][J]);
+            gY[r][J] = mfma_f32(dDs[(16 * I + 4 * gq + e) * RS + 16 * (vt0 + r) + lr], te, gY[r][J]);
         }
       }
     }
+  }
+  // operands of the dA products, loaded before the dv stores
+  float4 wv[4], uv[VR][4];
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    wv[J] = *reinterpret_cast<const float4*>(Wi + (16 * J + lr) * DK + 16 * w + 4 * gq);
+#pragma unroll
+    for (int r = 0; r < VR; ++r)
+      uv[r][J] = vown ? *reinterpret_cast<const float4*>(Ui + (16 * J + lr) * DV + 16 * (vt0 + r) + 4 * gq)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   // dv = beta dY; the dY o V part of dbeta
   {
     float dyp[4] = {0.f, 0.f, 0.f, 0.f};
     if (vown) {
+      float bt[4], vv[4][VR][4];
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
         const int t = 16 * J + lr;
         const bool valid = t < it.len;
         const int64_t row = (it.tok0 + t) * a.H + h;
-        const float bt = valid ? load1(reinterpret_cast<const InT*>(a.beta) + row) : 0.f;
+        bt[J] = valid ? load1(reinterpret_cast<const InT*>(a.beta) + row) : 0.f;
 #pragma unroll
         for (int r = 0; r < VR; ++r) {
-          const int cv = 16 * (vt0 + r) + 4 * gq;
-          float vv[4] = {0.f, 0.f, 0.f, 0.f};
-          if (valid) load4(V + row * DV + cv, vv);
+          vv[J][r][0] = vv[J][r][1] = vv[J][r][2] = vv[J][r][3] = 0.f;
+          if (valid) load4(V + row * DV + 16 * (vt0 + r) + 4 * gq, vv[J][r]);
+        }
+      }
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        const int t = 16 * J + lr;
+        const int64_t row = (it.tok0 + t) * a.H + h;
+#pragma unroll
+        for (int r = 0; r < VR; ++r) {
           float o[4];
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
-            o[ii] = bt * gY[r][J][ii];
-            dyp[J] = fmaf(gY[r][J][ii], vv[ii], dyp[J]);
+            o[ii] = bt[J] * gY[r][J][ii];
+            dyp[J] = fmaf(gY[r][J][ii], vv[J][r][ii], dyp[J]);
           }
-          if (valid) store4(reinterpret_cast<InT*>(a.dv) + row * DV + cv, o);
+          if (t < it.len) store4(reinterpret_cast<InT*>(a.dv) + row * DV + 16 * (vt0 + r) + 4 * gq, o);
         }
       }
     }
@@ -986,27 +1035,24 @@ __global__ __launch_bounds__(DK * 4) void cb_grad_a_kernel(CbArgs a) {
       if (gq == 0) dyv[w * 64 + 16 * J + lr] = sum;
     }
   }
+  __syncthreads();  // every wave is past its last read of the staged rows
+
   // 3. dA partial over this wave's key and value tiles, all 10 lower tiles
 #pragma unroll
   for (int p = 0; p < 10; ++p) {
     const int I = cb_tile_i(p), J = cb_tile_j(p);
     f32x4 acc = zero4();
-    {
-      const float4 wv = *reinterpret_cast<const float4*>(Wi + (16 * J + lr) * DK + 16 * w + 4 * gq);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc = mfma_f32(gX[I][e], f4_at(wv, e), acc);
-    }
+    for (int e = 0; e < 4; ++e) acc = mfma_f32(gX[I][e], f4_at(wv[J], e), acc);
     if (vown) {
 #pragma unroll
-      for (int r = 0; r < VR; ++r) {
-        const float4 uv = *reinterpret_cast<const float4*>(Ui + (16 * J + lr) * DV + 16 * (vt0 + r) + 4 * gq);
+      for (int r = 0; r < VR; ++r)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc = mfma_f32(gY[r][I][e], f4_at(uv, e), acc);
-      }
+        for (int e = 0; e < 4; ++e) acc = mfma_f32(gY[r][I][e], f4_at(uv[r][J], e), acc);
     }
     red[(w * 10 + p) * 64 + l] = acc;
   }
-  __syncthreads();  // all reads of S0, Hn and dD are complete: the state block is free
+  __syncthreads();  // all reads of S0, Hn, dD and D are complete: the state block is free
 
   // 4. results: dA (strictly lower, summed over the waves in order), dP, the fragments
 #pragma unroll
@@ -1039,10 +1085,24 @@ __global__ __launch_bounds__(DK * 4) void cb_grad_a_kernel(CbArgs a) {
   }
   if (gq == 0) st[WS::GN + 16 * w + lr] = Ei[16 * w + lr] * gn;
   __syncthreads();
+  // the dA o L part of dbeta: row t of L (its lower blocks) against row t of dA
   if (tid < 64) {
-    const int t = tid;
+    const int t = tid, I = t >> 4;
+    float4 lv[4][4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        lv[J][q] = J <= I ? *reinterpret_cast<const float4*>(Li + cb_blk(I, J) * 256 + (t & 15) * 16 + 4 * q)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
     float s = 0.f;
-    for (int j = 0; j < t; ++j) s = fmaf(dAs[t * 64 + j], Li[cb_blk(t >> 4, j >> 4) * 256 + (t & 15) * 16 + (j & 15)], s);
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 av = *reinterpret_cast<const float4*>(dAs + t * 64 + 16 * J + 4 * q);
+        s = fmaf(av.x, lv[J][q].x, fmaf(av.y, lv[J][q].y, fmaf(av.z, lv[J][q].z, fmaf(av.w, lv[J][q].w, s))));
+      }
     float y = dyv[t];
 #pragma unroll
     for (int v = 1; v < NW; ++v) y += dyv[v * 64 + t];
