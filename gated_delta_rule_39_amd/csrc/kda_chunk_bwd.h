@@ -195,21 +195,47 @@ __device__ void cb_load_rows(const CbArgs& a, const CbItem& it, int h, float* kh
   constexpr int KS = DK + 4;
   constexpr int TP = NT / 64;   // threads per token
   constexpr int CH = DK / TP;  // channels per thread
+  constexpr int C4 = DK / 4;
+  constexpr int GJ = 64 * C4 / NT;  // 16-byte pieces of g per thread
   const int tid = threadIdx.x;
   const int t = tid / TP, p = tid % TP;
-  const bool valid = t < it.len;
-  const int64_t row = (it.tok0 + t) * a.H + h;
+  // every load first (rows past the chunk's end fall outside the resources and read 0)
+  const uint32_t ts = (uint32_t)a.H * DK;  // token stride, elements
+  const uint32_t rows = (uint32_t)((it.len - 1) * ts + DK);
+  const int64_t base = (it.tok0 * a.H + h) * DK;
+  const auto qr = cb_rsrc(reinterpret_cast<const InT*>(a.q) + base, rows * sizeof(InT));
+  const auto kr = cb_rsrc(reinterpret_cast<const InT*>(a.k) + base, rows * sizeof(InT));
+  const auto gr = cb_rsrc(a.g + base, rows * 4);
+  float4 gv[GJ];
+#pragma unroll
+  for (int j = 0; j < GJ; ++j) {
+    const int e4 = tid + NT * j;
+    const int tt = e4 / C4, c4 = e4 - tt * C4;
+    gv[j] = cb_ld4(gr, (uint32_t)((tt * ts + 4 * c4) * 4));
+  }
+  float xs[2][CH];
+#pragma unroll
+  for (int c = 0; c < CH; c += 4) {
+    const float4 vq = cb_ld4_io(qr, t * ts + p * CH + c, (const InT*)nullptr);
+    const float4 vk = cb_ld4_io(kr, t * ts + p * CH + c, (const InT*)nullptr);
+    xs[0][c] = vq.x; xs[0][c + 1] = vq.y; xs[0][c + 2] = vq.z; xs[0][c + 3] = vq.w;
+    xs[1][c] = vk.x; xs[1][c + 1] = vk.y; xs[1][c + 2] = vk.z; xs[1][c + 3] = vk.w;
+  }
+  float bv = 0.f;
+  if (tid < 64) {
+    const auto br = cb_rsrc(reinterpret_cast<const InT*>(a.beta) + it.tok0 * a.H + h,
+                            (uint32_t)(((it.len - 1) * a.H + 1) * sizeof(InT)));
+    bv = cb_ld_io(br, tid * a.H, (const InT*)nullptr);
+  }
+#pragma unroll
+  for (int j = 0; j < GJ; ++j) {
+    const int e4 = tid + NT * j;
+    const int tt = e4 / C4, c4 = e4 - tt * C4;
+    *reinterpret_cast<float4*>(G + tt * KS + 4 * c4) = gv[j];
+  }
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
-    float x[CH];
-    if (valid) {
-      const InT* src = reinterpret_cast<const InT*>(which ? a.k : a.q) + row * DK + p * CH;
-#pragma unroll
-      for (int c = 0; c < CH; c += 4) load4(src + c, x + c);
-    } else {
-#pragma unroll
-      for (int c = 0; c < CH; ++c) x[c] = 0.f;
-    }
+    float* x = xs[which];
     float m = 0.f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) m = fmaxf(m, fabsf(x[c]));
@@ -235,21 +261,9 @@ __device__ void cb_load_rows(const CbArgs& a, const CbItem& it, int h, float* kh
       nrm[which * 128 + 64 + t] = (float)ex;
     }
   }
-  if (tid < 64) bs[tid] = tid < it.len ? load1(reinterpret_cast<const InT*>(a.beta) + (it.tok0 + tid) * a.H + h) : 0.f;
-  // g: coalesced 16-byte loads of the chunk's rows into LDS (rows past the end are 0), then
-  // the cumulative sum down each channel in PT parts of 64 / PT tokens, each part adding
-  // the totals of the parts before it
-  {
-    constexpr int C4 = DK / 4;
-    const auto gr = cb_rsrc(a.g + (it.tok0 * a.H + h) * DK, (uint32_t)(((it.len - 1) * a.H * DK + DK) * 4));
-#pragma unroll
-    for (int j = 0; j < 64 * C4 / NT; ++j) {
-      const int e4 = tid + NT * j;
-      const int t = e4 / C4, c4 = e4 - t * C4;
-      const float4 v4 = cb_ld4(gr, (uint32_t)((t * a.H * DK + 4 * c4) * 4));
-      *reinterpret_cast<float4*>(G + t * KS + 4 * c4) = v4;
-    }
-  }
+  if (tid < 64) bs[tid] = bv;
+  // the cumulative sum of g down each channel in PT parts of 64 / PT tokens, each part
+  // adding the totals of the parts before it
   __syncthreads();
   {
     constexpr int PT = NT / DK, TL = 64 / PT;
@@ -1158,12 +1172,22 @@ __global__ __launch_bounds__(DK * 4) void cb_grad_b_kernel(CbArgs a) {
   const int tid = threadIdx.x, l = tid & 63, lr = l & 15, gq = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const float* st = a.st + item * WS::SB;
+  constexpr int AJ = 64 * 16 / NT;  // 16-byte pieces of dA (and of dP) per thread
+  float4 avs[AJ], pvs[AJ];          // loaded before the rows, written to LDS after them
+#pragma unroll
+  for (int j = 0; j < AJ; ++j) {
+    const int idx = tid + NT * j, i = idx >> 4, j4 = (idx & 15) * 4;
+    avs[j] = *reinterpret_cast<const float4*>(st + WS::GA + i * 64 + j4);
+    pvs[j] = *reinterpret_cast<const float4*>(st + WS::GP + i * 64 + j4);
+  }
   cb_load_rows<DK, InT, NT>(a, it, h, kh, qh, G, bs, nrm);
   __syncthreads();
-  for (int idx = tid; idx < 64 * 16; idx += NT) {
+#pragma unroll
+  for (int jj = 0; jj < AJ; ++jj) {
+    const int idx = tid + NT * jj;
     const int i = idx >> 4, j4 = (idx & 15) * 4;
-    const float4 av = *reinterpret_cast<const float4*>(st + WS::GA + i * 64 + j4);
-    const float4 pv = *reinterpret_cast<const float4*>(st + WS::GP + i * 64 + j4);
+    const float4 av = avs[jj];
+    const float4 pv = pvs[jj];
     const float bi = bs[i];
     float4 lo, po;
     lo.x = j4 < i ? bi * av.x : 0.f;
