@@ -44,14 +44,7 @@ import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published (no sparsity)
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published (counts packed fp32 FMA)
-# fp32 vector peak without packed instructions, which every HIP object here is built
-# without: 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz
-FP32_VECTOR_NONPACKED_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
-# fp32 operations per state element per (token, head) that the token-by-token backward must
-# do: one forward recompute (decay 1, prediction 2, correction 2) and the reverse step
-# (decay 1, G update 2, u 2, a.do 2, G.delta 2, a.u 2, da 2, a.da 2, G decay 1)
-BWD_FLOPS_PER_ELEM = 21
+MFMA_F32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix (v_mfma_f32_*), published
 TOL = 5e-3
 
 
@@ -301,10 +294,29 @@ def chain_latency(kda, dev, torch, x, kernel_ms, reps=20):
                     "the whole scan kernel divided by its chunks)"}
 
 
+def bwd_chunk_flops(dk, dv):
+    """Matrix-core flops (2 m n k per product) of the chunkwise backward per 64-token chunk and
+    head, product by product; a lower-triangular 64 x 64 operand counts its 10 formed 16 x 16
+    blocks (10/16 of the square).  Factors: the gated Grams L and P (64 x 64 over dk), the
+    off-diagonal blocks of T = (I + diag(beta) L)^-1 (16 block products), W = T X and U = T Y.
+    Forward scan: W S0 and Kd^T D.  Reverse scan: Kd Hn, W^T dD, Qg^T dO and P^T dO.
+    Gradients: dQg = dO S0^T, dW = dD S0^T, dKd = D Hn^T, dP = dO D^T, dX = T^T dW,
+    dY = T^T dD, dA = dX W^T + dY U^T, and the four products of the gated backward (two per
+    Gram)."""
+    tri = 10.0 / 16.0
+    mm = lambda m, n, k: 2.0 * m * n * k
+    factors = 2 * tri * mm(64, 64, dk) + 16 * mm(16, 16, 16) + tri * (mm(64, dk, 64) + mm(64, dv, 64))
+    fwd = mm(64, dv, dk) + mm(dk, dv, 64)
+    rev = 3 * mm(64, dv, dk) + tri * mm(64, dv, 64)
+    grad_a = 3 * mm(64, dk, dv) + tri * (mm(64, 64, dv) + mm(64, dk, 64) + mm(64, dv, 64) + mm(64, 64, dk + dv))
+    grad_b = 4 * tri * mm(64, dk, 64)
+    return factors + fwd + rev + grad_a + grad_b
+
+
 def backward_measurement(kda, dev, torch, calls=3):
     """kda_bwd on the headline workload (B=1, T=8192, H=32, d=128, bf16), timed over a few
-    calls (it walks every token in sequence), with its parity checked on a small problem
-    against the fp64 backward oracle (the oracle keeps every state, too large at full size)."""
+    calls, with its parity checked on a small problem against the fp64 backward oracle (the
+    oracle keeps every state, too large at full size)."""
     from oracle import oracle_bwd
     from workloads import make_config, make_inputs
     rel = lambda a, b: float(np.linalg.norm(a.astype(np.float64) - b) / np.linalg.norm(b))
@@ -335,7 +347,7 @@ def backward_measurement(kda, dev, torch, calls=3):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / calls
-    # the two packed 8,192-token batches (their longest sequence walks its tokens in sequence)
+    # the two packed 8,192-token batches
     varlen = {}
     for i in (2, 3):
         y2 = make_config(i)
@@ -356,20 +368,22 @@ def backward_measurement(kda, dev, torch, calls=3):
     # bytes every call must move: inputs (q, k, v bf16, g fp32, beta, dout) and gradients once, h0 and dh0
     # reads q, k, v, dout (bf16), g (fp32), beta; writes dq, dk, dv (bf16), dg (fp32), dbeta
     nbytes = B * T * H * (16 * dk + 6 * dv + 4) + 2 * H * dk * dv * 4
-    flops = BWD_FLOPS_PER_ELEM * B * T * H * dk * dv
+    chunks = B * ((T + 63) // 64)
+    flops = bwd_chunk_flops(dk, dv) * chunks * H
     tflops = flops / (ms * 1e-3) / 1e12
+    ws = kda.bwd_workspace_size(B, T, H, dk, dv)
     log("backward %s: %.3f ms/call, parity (B=1 T=200 H=4) %s" % (x.name, ms, errs))
     return {"ok": good, "workload": "backward of %s (B=1 T=8192 H=32 d=128 bf16)" % x.name,
             "ms_per_call": round(ms, 3), "tokens_per_s": round(B * T / (ms * 1e-3), 1) if good else None,
-            "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": round(FP32_VECTOR_NONPACKED_TFLOPS, 2),
-                         "unit": "TFLOP/s", "frac": round(tflops / FP32_VECTOR_NONPACKED_TFLOPS, 4),
-                         "peak_note": "fp32 vector without packed instructions (the build disables them): "
-                                      "256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz; the published "
-                                      "157.3 TFLOP/s counts packed fp32 FMA",
+            "workspace_bytes": int(ws),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F32_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_F32_PEAK_TFLOPS, 4),
+                         "peak_note": "dense fp32 matrix cores (every product is v_mfma_f32_16x16x4f32)",
                          "flops_per_call": int(flops), "bytes_per_call": int(nbytes),
                          "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
-                         "note": "token by token (fp32 vector work on the state, %d flops per element and "
-                                 "token); the walks issue one VALU stream per wave" % BWD_FLOPS_PER_ELEM},
+                         "note": "chunkwise (64-token chunks): factors, one kernel walking both state "
+                                 "scans, two gradient kernels; flops are the products of the chunkwise "
+                                 "form (%.1f M per chunk and head)" % (bwd_chunk_flops(dk, dv) / 1e6)},
             "parity_small": errs, "varlen": varlen}
 
 

@@ -343,46 +343,22 @@ kda_status_t kda_decode(const kda_problem_t* prob, const void* q, const void* k,
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-// Backward workspace: chunk map (packed), the pre-pass records (unit q and k, exp(g), beta),
-// checkpoints of the state at every 8-token segment start, every token's delta, and each
-// column part's row sums (dqhat, dkhat, dg, dbeta).
+// Backward workspace: chunk map (packed), then per (chunk, head) the chunk's factors and its
+// state block (S0, Hn, dD, D; later the first gradient kernel's results).
 struct BwdCarve {
-  size_t info, table, seq_off, seq_order, rec, ckpt, delta, psum, total;
-  size_t cb_fac, cb_st, cb_total;  // chunkwise form
+  size_t info, table, seq_off, seq_order, fac, st, total;
 };
-
-// The token walk instead of the chunkwise form: KDA_BWD_WALK=1.
-static bool bwd_walk() {
-  const char* env = std::getenv("KDA_BWD_WALK");
-  return env && env[0] == '1';
-}
-
-// Value columns per wave of the backward walk: 4 once 32-column parts give every compute
-// unit a workgroup (less work per column), else 2 (16-column parts, twice the workgroups).
-static int bwd_wcols(const kda_problem_t* p, int64_t N) {
-  return N * (int64_t)p->heads * (p->dv / 32) >= compute_units() ? 4 : 2;
-}
 
 static BwdCarve bwd_carve(const kda_problem_t* p, int64_t N, int64_t n_chunk_ub) {
   BwdCarve c;
-  const size_t parts = (size_t)kda::backward_parts(p->dv, bwd_wcols(p, N));
-  const size_t state = (size_t)p->dk * p->dv * 4;
-  const size_t rows = (size_t)(p->batch * p->seqlen) * p->heads;
+  const size_t items = (size_t)n_chunk_ub * p->heads;
   c.info = 0;
   c.table = c.info + 256;
   c.seq_off = c.table + align256((size_t)n_chunk_ub * 16);
   c.seq_order = c.seq_off + align256((size_t)(N + 1) * 4);
-  c.rec = c.seq_order + align256((size_t)N * 4);
-  c.ckpt = c.rec + align256(rows * (3 * (size_t)p->dk + 4) * 4);
-  // every sequence of L tokens owns 8 slots per 64-token chunk, ceil(L / 8) <= 8 ceil(L / 64)
-  c.delta = c.ckpt + align256((size_t)n_chunk_ub * 8 * p->heads * state);
-  c.psum = c.delta + align256(rows * p->dv * 4);
-  c.total = c.psum + align256(parts * rows * (3 * (size_t)p->dk + 4) * 4);
-  const size_t items = (size_t)n_chunk_ub * p->heads;
-  c.cb_fac = c.rec;
-  c.cb_st = c.cb_fac + align256(items * kda::chunk_bwd_factor_floats(p->dk, p->dv) * 4);
-  c.cb_total = c.cb_st + align256(items * kda::chunk_bwd_state_floats(p->dk, p->dv) * 4);
-  if (c.cb_total > c.total) c.total = c.cb_total;
+  c.fac = c.seq_order + align256((size_t)N * 4);
+  c.st = c.fac + align256(items * kda::chunk_bwd_factor_floats(p->dk, p->dv) * 4);
+  c.total = c.st + align256(items * kda::chunk_bwd_state_floats(p->dk, p->dv) * 4);
   return c;
 }
 
@@ -445,14 +421,8 @@ kda_status_t kda_bwd(const kda_problem_t* prob, const void* q, const void* k, co
   p.table = ws + c.table;
   p.seq_off = reinterpret_cast<int32_t*>(ws + c.seq_off);
   p.seq_order = reinterpret_cast<int32_t*>(ws + c.seq_order);
-  p.rec = reinterpret_cast<float*>(ws + c.rec);
-  p.ckpt = reinterpret_cast<float*>(ws + c.ckpt);
-  p.delta = reinterpret_cast<float*>(ws + c.delta);
-  p.psum = reinterpret_cast<float*>(ws + c.psum);
-  p.wcols = bwd_wcols(prob, N);
-  p.chunked = bwd_walk() ? 0 : 1;
-  p.cb_fac = reinterpret_cast<float*>(ws + c.cb_fac);
-  p.cb_st = reinterpret_cast<float*>(ws + c.cb_st);
+  p.cb_fac = reinterpret_cast<float*>(ws + c.fac);
+  p.cb_st = reinterpret_cast<float*>(ws + c.st);
   hipError_t e = kda::launch_backward(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -37,9 +37,10 @@
 // Gated products: M_ij = sum_c a_ic b_jc e^(G_ic - G_jc) over 16 x 16 token blocks is a
 // matrix product of a e^(G - G_r) and b e^(G_r - G) for a reference row r.  Off-diagonal
 // blocks take r between the two blocks, so both factors are at most 1.  A diagonal block
-// takes its middle row, which keeps every factor within e^80 of 1 when the gate falls by at
-// most 80 nats over either half of the block (checked per block); past that the block is
-// summed element by element with one exponential per term.
+// takes its middle row, which keeps every factor within e^40 of 1 when the gate falls by at
+// most 40 nats over either half of the block (checked per block; products of such factors
+// and unit-norm rows stay far from fp32 denormals); past that the block is summed element
+// by element with one exponential per term.
 //
 // MFMA fragments (v_mfma_f32_16x16x4f32, lane l, r = l % 16, q = l / 16):
 //   A (16 x 4): lane holds A[r][q];  B (4 x 16): B[q][r];  C (16 x 16): C[4q + i][r], i = 0..3.
@@ -48,7 +49,7 @@
 // product over its rows and as the (transposed) A operand of one.
 #pragma once
 
-#include "kda_recurrent_bwd.h"
+#include "kda_device.h"
 
 namespace kda {
 
@@ -57,6 +58,10 @@ __device__ inline f32x4 mfma_f32(float a, float b, const f32x4& c) {
 }
 
 __device__ inline float cb_exp(float x) { return exp2_hw(x * kLog2e); }
+
+// Largest fall of the gate (nats) over either half of a diagonal 16 x 16 block for which the
+// block's gated product runs on the matrix cores.
+constexpr float kCbDiagSpan = 40.f;
 
 __device__ inline float f4_at(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
 
@@ -318,7 +323,7 @@ __device__ void cb_gram_block(const float* kh, const float* qh, const float* G, 
       const float gr = G[ref * KS + c];
       sp = fmaxf(sp, fmaxf(fabsf(G[16 * I * KS + c] - gr), fabsf(G[(16 * I + 15) * KS + c] - gr)));
     }
-    use_mfma = !__any(sp > 80.f);
+    use_mfma = !__any(sp > kCbDiagSpan);
   }
   if (use_mfma) {
     const int ia = 16 * I + lr, jb = 16 * J + lr;
@@ -1319,7 +1324,7 @@ __global__ __launch_bounds__(DK * 4) void cb_grad_b_kernel(CbArgs a) {
         const float gr = G[ref * KS + cc];
         sp = fmaxf(sp, fmaxf(fabsf(G[16 * B * KS + cc] - gr), fabsf(G[(16 * B + 15) * KS + cc] - gr)));
       }
-      if (!__any(sp > 80.f)) {
+      if (!__any(sp > kCbDiagSpan)) {
         f32x4 aL[KR], aP[KR], bL[KR], bP[KR];
 #pragma unroll
         for (int r = 0; r < KR; ++r) {

@@ -87,6 +87,8 @@ __device__ inline void store4(uint16_t* p, const float* x) {
 __device__ inline void store4(float* p, const float* x) {
   *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
 }
+__device__ inline void store1(uint16_t* p, float x) { *p = (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu); }
+__device__ inline void store1(float* p, float x) { *p = x; }
 
 // Reductions across the four rows of 16 lanes (lanes t, t + 16, t + 32, t + 48), the result
 // in every lane, through the gfx950 row swaps (v_permlane16_swap: odd rows of the first

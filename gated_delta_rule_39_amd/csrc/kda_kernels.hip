@@ -11,7 +11,6 @@
 #include "kda_scan.h"
 #include "kda_fused.h"
 #include "kda_recurrent.h"
-#include "kda_recurrent_bwd.h"
 #include "kda_chunk_bwd.h"
 
 namespace kda {
@@ -222,37 +221,6 @@ hipError_t launch_recurrent(const ForwardPlan& p, hipStream_t stream) {
 }
 
 template <int DK, int DV, typename InT>
-static hipError_t launch_backward_t(const BackwardPlan& p, hipStream_t stream) {
-  const int64_t rows = p.T_total * (int64_t)p.H;
-  if (rows > 0) {
-    auto pre = bwd_prep_kernel<DK, InT>;
-    hipLaunchKernelGGL(pre, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p.q, p.k, p.g, p.beta,
-                       p.rec, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  BwdArgs a;
-  a.rec = p.rec; a.v = p.v; a.h0 = p.h0; a.cu = p.cu;
-  a.seq_off = p.cu ? p.seq_off : nullptr;
-  a.seq_order = p.cu ? p.seq_order : nullptr;
-  a.dout = p.dout; a.dht = p.dht;
-  a.psum = p.psum;
-  a.dv = p.dv_; a.dh0 = p.dh0; a.ckpt = p.ckpt; a.delta = p.delta;
-  a.T = p.T; a.T_total = p.T_total; a.N = p.N; a.nc = p.cu ? 0 : (p.T + kChunk - 1) / kChunk;
-  a.n_chunk_ub = p.n_chunk_ub;
-  a.H = p.H; a.scale = p.scale;
-  const int parts = backward_parts(DV, p.wcols);
-  auto kern = p.wcols == 4 ? recurrent_bwd_kernel<DK, DV, InT, 4> : recurrent_bwd_kernel<DK, DV, InT, 2>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(p.N * p.H * parts)), dim3(kBwdThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || rows == 0) return e;
-  auto fin = bwd_finish_kernel<DK, InT>;
-  hipLaunchKernelGGL(fin, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p.q, p.k, p.psum, parts, rows,
-                     p.dq, p.dk_, p.dg, p.dbeta);
-  return hipGetLastError();
-}
-
-template <int DK, int DV, typename InT>
 static hipError_t launch_chunk_backward_t(const BackwardPlan& p, hipStream_t stream) {
   using WS = CbWs<DK, DV>;
   CbArgs a;
@@ -308,10 +276,8 @@ static hipError_t launch_chunk_backward_t(const BackwardPlan& p, hipStream_t str
 
 template <int DK, int DV>
 static hipError_t launch_backward_dt(const BackwardPlan& p, hipStream_t stream) {
-  if (p.chunked)
-    return p.dtype == 0 ? launch_chunk_backward_t<DK, DV, uint16_t>(p, stream)
-                        : launch_chunk_backward_t<DK, DV, float>(p, stream);
-  return p.dtype == 0 ? launch_backward_t<DK, DV, uint16_t>(p, stream) : launch_backward_t<DK, DV, float>(p, stream);
+  return p.dtype == 0 ? launch_chunk_backward_t<DK, DV, uint16_t>(p, stream)
+                      : launch_chunk_backward_t<DK, DV, float>(p, stream);
 }
 
 size_t chunk_bwd_factor_floats(int dk, int dv) {
@@ -327,8 +293,6 @@ size_t chunk_bwd_state_floats(int dk, int dv) {
   if (dk == 128 && dv == 64) return CbWs<128, 64>::SB;
   return CbWs<128, 128>::SB;
 }
-
-int backward_parts(int dv, int wcols) { return dv / (kBwdWaves * wcols); }
 
 hipError_t launch_backward(const BackwardPlan& p, hipStream_t stream) {
   if (p.N <= 0) return hipSuccess;

@@ -46,7 +46,7 @@ size_t record_bytes(int dk, int dv);
 // Enqueue chunk map, chunk kernel and state scan on `stream`.
 hipError_t launch_forward(const ForwardPlan& p, hipStream_t stream);
 
-// Backward of the forward described by a ForwardPlan-like set of sizes.
+// Backward of the forward described by a ForwardPlan-like set of sizes (chunkwise form).
 struct BackwardPlan {
   int64_t B, T, N, T_total, n_chunk_ub;
   int32_t H, dk, dv, dtype;
@@ -57,15 +57,8 @@ struct BackwardPlan {
   void* dq; void* dk_; void* dv_; float* dg; void* dbeta; float* dh0;
   // workspace
   int32_t* info; void* table; int32_t* seq_off; int32_t* seq_order;
-  float* rec;                                             // per (token, head): qhat, khat, exp(g), beta
-  float* ckpt;                                            // state checkpoints every 8 tokens
-  float* delta;                                           // v - a^T khat of every token
-  float* psum;                                            // per-part row sums
-  int32_t wcols;                                          // value columns per wave (2 or 4)
-  // chunkwise form (used when chunked != 0): per-(chunk, head) factors and state blocks
-  int32_t chunked;
-  float* cb_fac;                                          // items * chunk_bwd_factor_floats
-  float* cb_st;                                           // items * chunk_bwd_state_floats
+  float* cb_fac;                                          // per (chunk, head): chunk_bwd_factor_floats
+  float* cb_st;                                           // per (chunk, head): chunk_bwd_state_floats
 };
 
 // fp32 words per (chunk, head) item of the chunkwise backward: its factors and its state block.
@@ -73,11 +66,6 @@ size_t chunk_bwd_factor_floats(int dk, int dv);
 size_t chunk_bwd_state_floats(int dk, int dv);
 
 hipError_t launch_backward(const BackwardPlan& p, hipStream_t stream);
-
-// Workgroups of the backward kernel per (sequence, head) at `wcols` (2 or 4) value columns
-// per wave: the value columns are cut into this many parts, each with its own row sums in
-// the workspace.
-int backward_parts(int dv, int wcols);
 
 // Enqueue the token-by-token recurrent kernel on `stream` (uses the sizes, tensors and
 // scale of `p`; no workspace).

@@ -85,6 +85,10 @@ def workspace_size(B, T, H, dk, dv, dtype=KDA_BF16, num_seqs=0):
     return int(_lib.kda_fwd_workspace_size(ctypes.byref(make_problem(B, T, H, dk, dv, dtype, num_seqs))))
 
 
+def bwd_workspace_size(B, T, H, dk, dv, dtype=KDA_BF16, num_seqs=0):
+    return int(_lib.kda_bwd_workspace_size(ctypes.byref(make_problem(B, T, H, dk, dv, dtype, num_seqs))))
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 

@@ -242,8 +242,9 @@ kda_status_t kda_decode(const kda_problem_t* prob, const void* q, const void* k,
 /*
  * Backward pass: the gradients of a kda_fwd call.  "Autoresearch on Kimi Delta
  * Attention" (stage "Frozen outside the loop": full gradients against an
- * independent reference; phase "Move the path into CUDA": the reverse
- * recurrence over value tiles) fixes what it must return.
+ * independent reference; phase "Parallelize the recurrence": chunkwise transforms
+ * and a scan over chunks instead of the token-by-token reverse walk) fixes what it
+ * must return and the form it takes.
  *
  *   q, k, v, g, beta, h0, cu_seqlens, scale   the forward's inputs, as for kda_fwd
  *   dout        [B, T, H, dv]  dtype   dL/dout
@@ -256,15 +257,17 @@ kda_status_t kda_decode(const kda_problem_t* prob, const void* q, const void* k,
  *   dh0         [N, H, dk, dv] fp32    dL/dh0 (also when h0 is NULL, i.e. zero), or NULL
  *   workspace   >= kda_bwd_workspace_size(prob) bytes of device scratch
  *
- * The walk is token by token per (sequence, head), fp32 throughout, with the state's
- * value columns split over workgroups of 16 columns (2 per wave), or 32 (4 per wave) once
- * N * H * dv / 32 reaches the number of compute units; a first walk stores the state every
- * 8 tokens and each token's delta, and the reverse walk replays each 8-token segment from
- * them.  The workspace holds those checkpoints (dk * dv * 4 bytes per 8 tokens and head),
- * per (token, head) records of unit q and k, exp(g) and beta, the deltas and each part's
- * row sums: about 5.9 GB for 8,192 tokens of 32 heads at dk = dv = 128.
- * Conventions (stream, no allocation, errors, alignment) as for kda_fwd; outputs must
- * not overlap any input, the workspace or each other.  Results are deterministic.
+ * Chunkwise, per 64-token chunk and head, with every product on the fp32 matrix cores:
+ * a first kernel forms the chunk's factors (the gated Grams, the inverse of
+ * I + diag(beta) L, W, U); one kernel walks each (sequence, head, 16 value columns)
+ * forwards for the state at every chunk start and backwards for dL/dS at every chunk
+ * end; two kernels then form each chunk's gradients.  The workspace holds per (chunk,
+ * head) the factors (about 162 KB at dk = dv = 128) and a state block (S0, dL/dS and two
+ * 64 x dv matrices, 192 KB): 1.47 GB for 8,192 tokens of 32 heads.  With cu_seqlens the
+ * chunk count is bounded by T / 64 + N (the offsets stay on the device), so packed
+ * batches size for that bound.  Conventions (stream, no allocation, errors, alignment)
+ * as for kda_fwd; outputs must not overlap any input, the workspace or each other.
+ * Results are deterministic.
  */
 size_t kda_bwd_workspace_size(const kda_problem_t* prob);
 kda_status_t kda_bwd(const kda_problem_t* prob, const void* q, const void* k, const void* v,

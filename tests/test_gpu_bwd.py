@@ -3,7 +3,8 @@
 
 Gate: relative RMSE against the oracle <= 5e-3 for the gradients written in the
 inputs' dtype (dq, dk, dv, dbeta: bf16 rounding of the result itself) and <= 1e-4
-for the fp32 ones (dg, dh0; the walk is fp32 throughout).
+for the fp32 ones (dg, dh0; every product of the chunkwise form is fp32 on the matrix
+cores).
 """
 import numpy as np
 import pytest
@@ -127,19 +128,31 @@ def test_bwd_deterministic():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_bwd_wide_parts(dtype):
-    # enough (sequence, head) pairs for 32-column parts (4 columns per wave) on every
-    # compute unit: B * H * dv / 32 = 512
+def test_bwd_many_short_rows(dtype):
+    # 128 (sequence, head) pairs of one partial chunk each: 1,024 scan workgroups, a multiple
+    # of 8 pairs (the slices of a pair on one compute die)
     x = make_inputs(64, 24, 2, 128, 128, seed=318, dtype=dtype)
-    _check(x, *_dout(x, 319), "bwd B=64 T=24 H=2 (wide parts) %s" % dtype)
+    _check(x, *_dout(x, 319), "bwd B=64 T=24 H=2 %s" % dtype)
 
 
-def test_bwd_wide_parts_packed():
+def test_bwd_many_packed_sequences():
     rng = np.random.default_rng(320)
     lens = rng.integers(0, 40, size=80)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     x = make_inputs(1, int(cu[-1]), 4, 128, 64, seed=321, dtype="bf16", cu_seqlens=cu)
-    _check(x, *_dout(x, 322), "bwd packed 80 sequences H=4 dv=64 (wide parts)")
+    _check(x, *_dout(x, 322), "bwd packed 80 sequences H=4 dv=64")
+
+
+@pytest.mark.parametrize("gmean", [-4.75, -5.25])
+def test_bwd_diagonal_blocks_at_the_factor_limit(gmean):
+    # The diagonal 16 x 16 blocks of the gated products run on the matrix cores with factors
+    # e^(G - G_mid) when the gate falls by at most 40 nats over either half of the block, and
+    # term by term past that.  g = -4.75 per token falls 38 nats over 8 tokens (factors near
+    # e^38), g = -5.25 falls 42 (the term-by-term path); both in fp32 against the oracle.
+    x = make_inputs(1, 140, 2, 128, 128, seed=324, dtype="f32")
+    rng = np.random.default_rng(325)
+    x.g[...] = (gmean * (1 + 0.002 * rng.standard_normal(x.g.shape))).astype(np.float32)
+    _check(x, *_dout(x, 326), "bwd g=%.1f per token" % gmean)
 
 
 def test_bwd_full_size_sampled_heads():
