@@ -145,6 +145,7 @@ struct CbArgs {
   const int32_t* info;        // packed: info[0] = number of chunks
   const ChunkEntry* table;    // packed: chunk table
   const int32_t* seq_off;     // packed: first chunk of each sequence
+  const int32_t* seq_order;   // packed: sequences, longest first
   const void* dout; const float* dht;
   void* dq; void* dk; void* dv; float* dg; void* dbeta; float* dh0;
   float* W; float* U; float* KdT; float* QgT; float* PT; float* L; float* TT; float* eGn;
@@ -602,7 +603,9 @@ __global__ __launch_bounds__(DK * 4) void cb_state_scan_kernel(CbArgs a) {
   int s;
   cb_scan_slot(blockIdx.x, a.N * a.H, NS, nh, s);
   const int h = (int)(nh % a.H);
-  const int64_t n = nh / a.H;
+  // packed sequences in the chunk map's order, longest first, so the longest chains start
+  // first
+  const int64_t n = a.cu ? (int64_t)a.seq_order[nh / a.H] : nh / a.H;
   int64_t c0, cnt;
   cb_chunks(a, n, c0, cnt);
   if (cnt == 0) {  // no chunks: dh0 = dht

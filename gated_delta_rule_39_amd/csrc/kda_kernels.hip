@@ -229,6 +229,7 @@ static hipError_t launch_chunk_backward_t(const BackwardPlan& p, hipStream_t str
   a.info = p.info;
   a.table = reinterpret_cast<const ChunkEntry*>(p.table);
   a.seq_off = p.seq_off;
+  a.seq_order = p.seq_order;
   a.dout = p.dout; a.dht = p.dht;
   a.dq = p.dq; a.dk = p.dk_; a.dv = p.dv_; a.dg = p.dg; a.dbeta = p.dbeta; a.dh0 = p.dh0;
   const int64_t items = p.n_chunk_ub * (int64_t)p.H;
