@@ -20,7 +20,7 @@ constexpr int64_t kChunkTokens = 64;
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct Carve {
-  size_t info, table, seq_off, seq_order, defer, flags, rec, total;
+  size_t info, table, seq_off, seq_order, rank_desc, defer, flags, rec, total;
 };
 
 bool sizes_ok(const kda_problem_t* p, bool packed, int64_t* N, int64_t* n_chunk_ub) {
@@ -53,7 +53,8 @@ Carve carve(const kda_problem_t* p, int64_t N, int64_t n_chunk_ub) {
   c.table = c.info + 256;
   c.seq_off = c.table + align256((size_t)n_chunk_ub * 16);
   c.seq_order = c.seq_off + align256((size_t)(N + 1) * 4);
-  c.defer = c.seq_order + align256((size_t)N * 4);
+  c.rank_desc = c.seq_order + align256((size_t)N * 4);
+  c.defer = c.rank_desc + align256((size_t)N * 16);
   c.flags = c.defer + align256((size_t)n_chunk_ub * (size_t)p->heads * 4);
   c.rec = c.flags + align256((size_t)n_chunk_ub * (size_t)p->heads * 8 * 2);  // a flag per 64-column slice
   c.total = c.rec + (size_t)n_chunk_ub * (size_t)p->heads * kda::record_bytes(p->dk, p->dv);
@@ -115,6 +116,32 @@ int slice_width(const kda_problem_t* p, int64_t N) {
   for (int v = 64; v > 16; v >>= 1)
     if (v <= p->dv && N * (int64_t)p->heads * (p->dv / v) >= cus) return v;
   return 16;
+}
+
+// Packed batches: the persistent state scan on one workgroup per compute unit (KDA_TASK_SCAN=0
+// takes the one-workgroup-per-chain scan instead, KDA_TASK_SCAN=n >= 1 caps the workgroups at
+// n: tuning, and tests of long per-workgroup walks and of a single queue), with sequences of at least
+// KDA_LONG_CHUNKS chunks (rounded up to a power of two; default 4) taken one at a time from
+// a cold start, on narrower value slices when their chains alone would not fill the
+// compute units, and the shorter ones pipelined.
+int task_scan_workgroups(bool packed) {
+  if (!packed) return 0;
+  const int cus = compute_units();
+  const char* env = std::getenv("KDA_TASK_SCAN");
+  if (!env) return cus;
+  const int v = std::atoi(env);
+  if (v <= 0) return 0;
+  return v < cus ? v : cus;
+}
+
+int long_chunks() {
+  const char* env = std::getenv("KDA_LONG_CHUNKS");
+  if (!env) return 4;
+  const int v = std::atoi(env);
+  if (v <= 0) return 0;
+  int p = 1;
+  while (p < v && p < (1 << 30)) p <<= 1;  // rounded up to a power of two
+  return p;
 }
 
 // Workgroups of the persistent chunk kernel: one per compute unit, or fewer when
@@ -279,6 +306,7 @@ static kda_status_t forward(const kda_problem_t* prob, const void* q, const void
   p.table = ws + c.table;
   p.seq_off = reinterpret_cast<int32_t*>(ws + c.seq_off);
   p.seq_order = reinterpret_cast<int32_t*>(ws + c.seq_order);
+  p.rank_desc = ws + c.rank_desc;
   p.rec = ws + c.rec;
   p.defer = reinterpret_cast<int32_t*>(ws + c.defer);
   p.flags = reinterpret_cast<uint64_t*>(ws + c.flags);
@@ -294,6 +322,8 @@ static kda_status_t forward(const kda_problem_t* prob, const void* q, const void
   }
   p.slice = slice_width(prob, N);
   p.chunk_wgs = chunk_workgroups();
+  p.task_scan = task_scan_workgroups(packed);
+  p.long_chunks = long_chunks();
   for (int i = 0; i < 4; ++i) p.marks[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
   hipError_t e = kda::launch_forward(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;

@@ -13,8 +13,12 @@
 //   info[0]           total number of chunks
 //   table[c]          (sequence, valid length, index inside the sequence) of chunk c
 //   seq_off[n]        first chunk of sequence n (exclusive prefix of chunk counts), seq_off[N] = total
-//   seq_order[i]      sequences ordered by chunk count, longest first (buckets of
-//                     powers of two), so the state scan starts its longest chains first
+//   seq_order[i]      sequences ordered by chunk count, longest first (four buckets per
+//                     power of two), so the state scan starts its longest chains first
+//   rank_desc[i]      (optional) {sequence, first chunk, first token, length} of seq_order[i]
+//   info[2]           sequences of at least `long_chunks` chunks (a power of two, so they
+//                     are exactly the first ones of seq_order); 0 when long_chunks is 0
+//   info[8..15]       task counters of the persistent state scan, zeroed here
 #pragma once
 
 #include "kda_device.h"
@@ -22,6 +26,15 @@
 namespace kda {
 
 constexpr int kMapThreads = 1024;
+constexpr int kMapBuckets = 128;
+
+// Order bucket of a chunk count: 0 for none, else 1 + 4 floor(log2 c) + the next two bits
+// of c (monotone in c; a power of two starts its bucket).
+__device__ inline int order_bucket(int32_t c) {
+  if (c <= 0) return 0;
+  const int e = 31 - __clz(c);
+  return 1 + 4 * e + ((int)(((uint32_t)c << 2) >> e) & 3);
+}
 
 __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* __restrict__ cu,
                                                                 int64_t T, int64_t N,
@@ -29,13 +42,15 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* _
                                                                 int32_t* __restrict__ info,
                                                                 ChunkEntry* __restrict__ table,
                                                                 int32_t* __restrict__ seq_off,
-                                                                int32_t* __restrict__ seq_order) {
+                                                                int32_t* __restrict__ seq_order,
+                                                                int4* __restrict__ rank_desc,
+                                                                int32_t long_chunks) {
   __shared__ int32_t scan[kMapThreads];
-  __shared__ int32_t hist[34];
+  __shared__ int32_t hist[kMapBuckets];
   __shared__ int32_t carry_s;
   const int tid = threadIdx.x;
   if (tid == 0) carry_s = 0;
-  if (tid < 34) hist[tid] = 0;
+  if (tid < kMapBuckets) hist[tid] = 0;
   __syncthreads();
 
   // 1. chunk counts, exclusive prefix -> seq_off; bucket histogram
@@ -46,8 +61,7 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* _
       int64_t L = seq_len(cu, T, n);
       int64_t c = (L + kChunk - 1) / kChunk;
       cnt = (int32_t)(c < n_chunk_ub ? c : n_chunk_ub);
-      int b = cnt == 0 ? 0 : 32 - __clz(cnt);  // 1 + floor(log2(cnt))
-      atomicAdd(&hist[b], 1);
+      atomicAdd(&hist[order_bucket(cnt)], 1);
     }
     scan[tid] = cnt;
     __syncthreads();
@@ -70,6 +84,7 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* _
     info[1] = (carry_s > n_chunk_ub) ? 1 : 0;
     seq_off[N] = carry_s;
   }
+  if (tid < 8) info[8 + tid] = 0;
   __syncthreads();
 
   // 2. table: chunk c belongs to the last sequence n with seq_off[n] <= c
@@ -91,14 +106,24 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* _
     table[c] = e;
   }
 
-  // 3. longest-first order of sequences (bucket b = 1 + floor(log2(chunks)), descending)
-  if (tid == 0) {
-    int32_t run = 0;
-    for (int b = 33; b >= 0; --b) {
-      int32_t h = hist[b];
-      hist[b] = run;
-      run += h;
+  // 3. longest-first order of sequences (order buckets, descending): each bucket's first
+  //    position is the number of sequences in the buckets above it.  One wave scans the
+  //    buckets from the top, two per lane.
+  static_assert(kMapBuckets == 128, "two buckets per lane of one wave");
+  if (tid < 64) {
+    const int b1 = kMapBuckets - 1 - 2 * tid, b2 = b1 - 1;
+    const int32_t c1 = hist[b1], c2 = hist[b2];
+    int32_t incl = c1 + c2;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t v = __shfl_up(incl, o, 64);
+      if (tid >= o) incl += v;
     }
+    const int32_t above = incl - c1 - c2;
+    hist[b1] = above;
+    hist[b2] = above + c1;
+    // the long sequences are those of the buckets from long_chunks' on: the first position
+    // of the bucket below it (read by the wave that wrote it, before the placements below)
+    if (tid == 0) info[2] = long_chunks > 0 ? hist[order_bucket(long_chunks) - 1] : 0;
   }
   __syncthreads();
   for (int64_t base = 0; base < N; base += kMapThreads) {
@@ -107,9 +132,9 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* _
       int64_t L = seq_len(cu, T, n);
       int64_t c = (L + kChunk - 1) / kChunk;
       int32_t cnt = (int32_t)(c < n_chunk_ub ? c : n_chunk_ub);
-      int b = cnt == 0 ? 0 : 32 - __clz(cnt);
-      int32_t pos = atomicAdd(&hist[b], 1);
+      int32_t pos = atomicAdd(&hist[order_bucket(cnt)], 1);
       seq_order[pos] = (int32_t)n;
+      if (rank_desc) rank_desc[pos] = make_int4((int)n, seq_off[n], (int)seq_start(cu, T, n), (int)L);
     }
   }
 }

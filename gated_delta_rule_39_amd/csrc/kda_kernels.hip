@@ -9,6 +9,7 @@
 #include "kda_chunkmap.h"
 #include "kda_prep.h"
 #include "kda_scan.h"
+#include "kda_scan_tasks.h"
 #include "kda_fused.h"
 #include "kda_recurrent.h"
 #include "kda_chunk_bwd.h"
@@ -52,52 +53,6 @@ static void mark(const ForwardPlan& p, int i, hipStream_t stream) {
   if (p.marks[i]) (void)hipEventRecord(p.marks[i], stream);
 }
 
-template <int DK, int DV, typename InT>
-static hipError_t launch_prep(const ForwardPlan& p, hipStream_t stream) {
-  PrepArgs a;
-  a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.beta = p.beta; a.cu = p.cu;
-  a.T = p.T; a.T_total = p.T_total; a.H = p.H;
-  a.info = p.info;
-  a.nc = p.cu ? 0 : (p.T + kChunk - 1) / kChunk;
-  a.table = reinterpret_cast<const ChunkEntry*>(p.table);
-  a.rec = p.rec;
-  a.defer = p.defer;
-  const size_t smem = PrepSmem<DK, DV>::BYTES;
-  auto kern = chunk_prep_kernel<DK, DV, InT>;
-  hipError_t ea = allow_smem(kern, smem);
-  if (ea != hipSuccess) return ea;
-  // persistent workgroups, at most one per compute unit (the LDS footprint admits one)
-  int64_t grid = p.chunk_wgs > 0 ? p.chunk_wgs : 256;
-  const int64_t items = p.n_chunk_ub * (int64_t)p.H;
-  if (grid > items) grid = items;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kPrepThreads), smem, stream, a);
-  return hipGetLastError();
-}
-
-template <int DK, int DV, int NV, typename OutT>
-static hipError_t launch_scan_nv(const ForwardPlan& p, hipStream_t stream) {
-  ScanArgs a;
-  a.h0 = p.h0; a.ht = p.ht; a.out = p.out; a.cu = p.cu;
-  a.T = p.T; a.T_total = p.T_total; a.N = p.N; a.H = p.H; a.n_chunk_ub = p.n_chunk_ub;
-  a.seq_off = p.seq_off; a.seq_order = p.seq_order; a.rec = p.rec; a.scale = p.scale;
-  a.nc = p.cu ? 0 : (p.T + kChunk - 1) / kChunk;
-  a.ctl = p.ctl;
-  const size_t smem = ScanSmem<DK, DV, NV>::BYTES;
-  auto kern = state_scan_kernel<DK, DV, NV, OutT>;
-  const int64_t blocks = p.N * (int64_t)p.H * (DV / NV);
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kScanThreads), smem, stream, a);
-  return hipGetLastError();
-}
-
-template <int DK, int DV, typename OutT>
-static hipError_t launch_scan(const ForwardPlan& p, hipStream_t stream) {
-  switch (p.slice) {
-    case 16: return launch_scan_nv<DK, DV, 16, OutT>(p, stream);
-    case 32: return launch_scan_nv<DK, DV, 32, OutT>(p, stream);
-    default: return launch_scan_nv<DK, DV, 64, OutT>(p, stream);
-  }
-}
-
 static PrepArgs prep_args(const ForwardPlan& p) {
   PrepArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.beta = p.beta; a.cu = p.cu;
@@ -118,6 +73,55 @@ static ScanArgs scan_args(const ForwardPlan& p) {
   a.nc = p.cu ? 0 : (p.T + kChunk - 1) / kChunk;
   a.ctl = p.ctl;
   return a;
+}
+
+template <int DK, int DV, typename InT>
+static hipError_t launch_prep(const ForwardPlan& p, hipStream_t stream) {
+  const PrepArgs a = prep_args(p);
+  const size_t smem = PrepSmem<DK, DV>::BYTES;
+  auto kern = chunk_prep_kernel<DK, DV, InT>;
+  hipError_t ea = allow_smem(kern, smem);
+  if (ea != hipSuccess) return ea;
+  // persistent workgroups, at most one per compute unit (the LDS footprint admits one)
+  int64_t grid = p.chunk_wgs > 0 ? p.chunk_wgs : 256;
+  const int64_t items = p.n_chunk_ub * (int64_t)p.H;
+  if (grid > items) grid = items;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kPrepThreads), smem, stream, a);
+  return hipGetLastError();
+}
+
+template <int DK, int DV, int NV, typename OutT>
+static hipError_t launch_scan_nv(const ForwardPlan& p, hipStream_t stream) {
+  const ScanArgs a = scan_args(p);
+  const size_t smem = ScanSmem<DK, DV, NV>::BYTES;
+  auto kern = state_scan_kernel<DK, DV, NV, OutT>;
+  const int64_t blocks = p.N * (int64_t)p.H * (DV / NV);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kScanThreads), smem, stream, a);
+  return hipGetLastError();
+}
+
+template <int DK, int DV, typename OutT>
+static hipError_t launch_scan_tasks(const ForwardPlan& p, hipStream_t stream) {
+  constexpr int NVL = DV < 32 ? DV : 32, NVS = DV < 64 ? DV : 64;
+  ScanArgs a = scan_args(p);
+  TaskArgs ta;
+  ta.queue = p.info + 8;
+  ta.n_long = p.info + 2;
+  ta.rank_desc = reinterpret_cast<const int4*>(p.rank_desc);
+  const size_t smem = scan_tasks_smem<DK, DV, NVL, NVS>();
+  auto kern = state_scan_tasks_kernel<DK, DV, NVL, NVS, OutT>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.task_scan), dim3(kScanThreads), smem, stream, a, ta);
+  return hipGetLastError();
+}
+
+template <int DK, int DV, typename OutT>
+static hipError_t launch_scan(const ForwardPlan& p, hipStream_t stream) {
+  if (p.cu && p.task_scan > 0) return launch_scan_tasks<DK, DV, OutT>(p, stream);
+  switch (p.slice) {
+    case 16: return launch_scan_nv<DK, DV, 16, OutT>(p, stream);
+    case 32: return launch_scan_nv<DK, DV, 32, OutT>(p, stream);
+    default: return launch_scan_nv<DK, DV, 64, OutT>(p, stream);
+  }
 }
 
 template <int DK, int DV, typename InT>
@@ -182,7 +186,8 @@ hipError_t launch_forward(const ForwardPlan& p, hipStream_t stream) {
   // fixed-length rows need none of it (the kernels derive every chunk from its index)
   if (p.cu) {
     hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kMapThreads), 0, stream, p.cu, p.T, p.N, p.n_chunk_ub,
-                       p.info, reinterpret_cast<ChunkEntry*>(p.table), p.seq_off, p.seq_order);
+                       p.info, reinterpret_cast<ChunkEntry*>(p.table), p.seq_off, p.seq_order,
+                       reinterpret_cast<int4*>(p.rank_desc), p.long_chunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -299,7 +304,7 @@ hipError_t launch_backward(const BackwardPlan& p, hipStream_t stream) {
   if (p.N <= 0) return hipSuccess;
   if (p.cu) {
     hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kMapThreads), 0, stream, p.cu, p.T, p.N, p.n_chunk_ub,
-                       p.info, reinterpret_cast<ChunkEntry*>(p.table), p.seq_off, p.seq_order);
+                       p.info, reinterpret_cast<ChunkEntry*>(p.table), p.seq_off, p.seq_order, nullptr, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

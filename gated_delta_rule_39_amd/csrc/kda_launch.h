@@ -27,6 +27,7 @@ struct ForwardPlan {
   void* table;
   int32_t* seq_off;
   int32_t* seq_order;
+  void* rank_desc;  // packed: per rank of seq_order, {sequence, first chunk, first token, length}
   uint8_t* rec;
   int32_t* defer;  // per (chunk, head): the item needs the exact diagonal tiles (chunk kernel scratch)
   uint64_t* flags;        // per (chunk, head): record-ready flags of the fused kernel
@@ -36,6 +37,8 @@ struct ForwardPlan {
   int32_t spin_limit;     // polls before a fused-kernel wait gives up
   int32_t fuse_producers;  // > 0: one fused kernel, this many workgroups run the chunk walk
   int32_t slice;  // value columns per scan workgroup (16, 32 or 64)
+  int32_t task_scan;    // packed: > 0 runs the persistent state scan on this many workgroups
+  int32_t long_chunks;  // packed: sequences of at least this many chunks form the long class (power of two; 0: none)
   int32_t chunk_wgs;  // workgroups of the persistent chunk kernel (>= 1)
   hipEvent_t marks[4];  // optional timing marks around the kernels (may be null)
 };

@@ -163,13 +163,15 @@ __device__ inline int copy_exponent(double b2) {
   return es < -250 ? -250 : (es > 250 ? 250 : es);
 }
 
-// One scan workgroup: chain `bid` of `nblk`.  FUSED: the chunk records are produced while
+// One scan workgroup's walk of the chain (sequence n, head h, value slice `slice`), with a
+// ring of DEPTH chunks of factors in registers.  FUSED: the chunk records are produced while
 // the chain walks them (the fused forward kernel): each chunk's ready flag is awaited
 // before its factors are loaded, and the copy exponent follows the running bound over the
-// chunks walked so far instead of the whole sequence's.
-template <int DK, int DV, int NV, typename OutT, bool FUSED>
-__device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz, const int64_t bid,
-                                           const int64_t nblk, uint8_t* smem) {
+// chunks walked so far instead of the whole sequence's.  `mark` (one workgroup per launch)
+// records the launch in the workspace's control word.
+template <int DK, int DV, int NV, typename OutT, bool FUSED, int DEPTH = scan_depth<NV>()>
+__device__ __forceinline__ void scan_walk(const ScanArgs& a, const FuseArgs& fz, const int64_t n, const int h,
+                                          const int slice, const bool mark, uint8_t* smem) {
   using R = Rec<DK, DV>;
   using SM = ScanSmem<DK, DV, NV>;
   using TR = TokRegs<DK, NV>;
@@ -177,8 +179,7 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
   constexpr int KSK = DK / 32;
   constexpr int TPK = DK / 64;
   constexpr int NT = NV / 16;
-  constexpr int NS = DV / NV;
-  constexpr int kScanDepth = scan_depth<NV>();
+  constexpr int kScanDepth = DEPTH;
   static_assert(!FUSED || kScanDepth == 2, "the fused walk reads the next chunk's header from the ring");
 
   uint8_t* sbb = smem + SM::SB;
@@ -192,21 +193,6 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
   const int l = tid & 63, t = l & 15, gq = l >> 4;
   const bool tok_wave = wv < 4;
   const int i = wv & 3;  // token block (tok_wave) or key block (otherwise)
-  // Workgroups are dispatched round-robin over the 8 XCDs (block id mod 8).  The NS
-  // slices of one (sequence, head) share every chunk factor except U, so they are
-  // mapped to block ids with equal residue mod 8: one XCD's L2 serves all of them.
-  int64_t chain, slice_l;
-  if (nblk % (8 * NS) == 0) {
-    const int64_t xcd = bid & 7, k = bid >> 3;
-    slice_l = k % NS;
-    chain = (k / NS) * 8 + xcd;
-  } else {
-    slice_l = bid % NS;
-    chain = bid / NS;
-  }
-  const int slice = (int)slice_l;
-  const int h = (int)(chain % a.H);
-  const int64_t n = a.cu ? (int64_t)a.seq_order[chain / a.H] : chain / a.H;
   int64_t c0 = a.cu ? (int64_t)a.seq_off[n] : n * a.nc;
   int64_t c1 = a.cu ? (int64_t)a.seq_off[n + 1] : (n + 1) * a.nc;
   if (c1 > a.n_chunk_ub) c1 = a.n_chunk_ub;  // only on invalid cu_seqlens
@@ -242,7 +228,7 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
     // the most recent launch on this workspace (kda_fwd_status): this launch's flag value,
     // or 0 for the two-kernel path (which has no waits)
     if (FUSED) __hip_atomic_store(fz.ctl, fz.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else if (a.ctl && bid == 0) __hip_atomic_store(a.ctl, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else if (a.ctl && mark) __hip_atomic_store(a.ctl, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (!tok_wave) {
 #pragma unroll
@@ -257,8 +243,9 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
     }
   }
   __syncthreads();
-  float cmax = 0.f;
-  for (int j = 0; j < NV; ++j) cmax = fmaxf(cmax, cn[j] + cn[NV + j] + cn[2 * NV + j] + cn[3 * NV + j]);
+  // the largest column norm: one column per lane (the same sums as a loop over columns)
+  const int jc = l < NV ? l : 0;
+  const float cmax = wave_max(l < NV ? cn[jc] + cn[NV + jc] + cn[2 * NV + jc] + cn[3 * NV + jc] : 0.f);
   float vmax = red[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) vmax = fmaxf(vmax, red[j]);
@@ -515,6 +502,28 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz
           }
     }
   }
+}
+
+// One scan workgroup: chain `bid` of `nblk` (one per (sequence, head, slice)).
+template <int DK, int DV, int NV, typename OutT, bool FUSED>
+__device__ __forceinline__ void scan_chain(const ScanArgs& a, const FuseArgs& fz, const int64_t bid,
+                                           const int64_t nblk, uint8_t* smem) {
+  constexpr int NS = DV / NV;
+  // Workgroups are dispatched round-robin over the 8 XCDs (block id mod 8).  The NS
+  // slices of one (sequence, head) share every chunk factor except U, so they are
+  // mapped to block ids with equal residue mod 8: one XCD's L2 serves all of them.
+  int64_t chain, slice_l;
+  if (nblk % (8 * NS) == 0) {
+    const int64_t xcd = bid & 7, k = bid >> 3;
+    slice_l = k % NS;
+    chain = (k / NS) * 8 + xcd;
+  } else {
+    slice_l = bid % NS;
+    chain = bid / NS;
+  }
+  const int h = (int)(chain % a.H);
+  const int64_t n = a.cu ? (int64_t)a.seq_order[chain / a.H] : chain / a.H;
+  scan_walk<DK, DV, NV, OutT, FUSED>(a, fz, n, h, (int)slice_l, bid == 0, smem);
 }
 
 template <int DK, int DV, int NV, typename OutT>

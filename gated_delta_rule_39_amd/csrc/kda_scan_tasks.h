@@ -1,0 +1,502 @@
+// Persistent state scan for packed batches: the per-chunk step of state_scan_kernel
+// (kda_scan.h), walked by one resident workgroup per compute unit that takes (sequence,
+// head, value slice) tasks from a queue.
+//
+// Why: in a batch of many short sequences a one-shot workgroup per chain spends most of
+// its life waiting: for its initial state rows, for the maxima of its chunk headers, for
+// its first chunk's factors, and only then steps once or twice.
+//
+// Two classes of sequences ("Autoresearch on Kimi Delta Attention", section "The
+// optimization trace": the recurrence split across value tiles to expose more independent
+// work):
+//  * long (at least `long_chunks` chunks; the first ones of the longest-first order): one
+//    task at a time, walked by scan_walk from a cold start.  When their chains on
+//    NVS-column slices would leave compute units idle they walk on the narrower
+//    NVL-column slices with a deeper ring: a step of a narrow slice is shorter, so the
+//    longest chain, which bounds the launch, ends sooner.
+//  * short (fewer chunks): NVS-column slices, pipelined: the next task's initial state,
+//    header maxima and first chunk are requested while the current one walks, so those
+//    latencies run under its steps.  Task ids are taken two ahead (only short tasks are
+//    ever held that way, so no task waits behind a long one).
+//
+// Queues: one counter per XCD (block id mod 8 is the XCD a workgroup runs on); the
+// (sequence, head) pairs are dealt to the queues round-robin, and all slices of a pair sit
+// in one queue, so one XCD's L2 serves the chunk factors the slices share.  A queue hands
+// out its long tasks first, then its short ones.
+#pragma once
+
+#include "kda_scan.h"
+
+namespace kda {
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+constexpr int kQueueSlots = 8;
+typedef int32_t int4_v __attribute__((ext_vector_type(4)));  // task counters in the workspace info block (one per XCD)
+
+struct TaskArgs {
+  int32_t* queue;          // kQueueSlots counters, zeroed by the chunk map before the launch
+  const int32_t* n_long;   // sequences of at least long_chunks chunks (the first ones of seq_order)
+  const int4* rank_desc;   // per rank of seq_order: {sequence, first chunk, first token, length}
+};
+
+// Task u of queue x among the (sequence, head) pairs [p_lo, p_hi) with p = x (mod nq),
+// `slices` tasks per pair: its pair and slice, or false past the queue's end.
+// (32-bit: the host bounds (sequences x heads x 8) below 2^31.)  nq is 1 or 8, slices a
+// power of two.
+__device__ __forceinline__ bool queue_task(int u, int slices, int x, int nq, int p_lo, int p_hi, int& p,
+                                           int& slice) {
+  if (u < 0) return false;
+  const int first = p_lo + ((x - p_lo) & (nq - 1));
+  const int cnt = p_hi > first ? (p_hi - first + nq - 1) / nq : 0;
+  if (u >= cnt * slices) return false;
+  p = first + nq * (u / slices);
+  slice = u & (slices - 1);
+  return true;
+}
+
+// Queue request whose result is waited for only where it is read.  A fetch-add at an address
+// the compiler can prove uniform is rewritten into one wave-wide atomic whose result is
+// broadcast at once, which would hold the wave for the round trip right there; the
+// address is therefore offset by a register value the compiler cannot see through (0).
+__device__ __forceinline__ int queue_request(int32_t* ctr) {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return __hip_atomic_fetch_add(ctr + z, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct ScanTask {
+  bool ok;  // a task of the class being walked
+  int h, slice, rank;
+  int64_t n, c0, c1, L, s0;
+};
+
+// Shared by both classes: queue geometry and the id hand-off.
+struct QueueCtx {
+  int32_t* ctr;        // this workgroup's queue counter
+  int x, nq;           // queue index and number of queues
+  int long_pairs;      // pairs of the long class (p < long_pairs)
+  int pairs;           // all pairs
+  int long_tasks;      // long tasks of this queue (its ids below this are long tasks)
+  int long_slices;     // value slices per long pair (DV / NVL or DV / NVS)
+  int32_t* qs;         // LDS slots: [0] the published id, [1] a workgroup-wide id
+};
+
+// The queue position (class check, pair, slice) of id u; `NS_` slices per pair.
+__device__ __forceinline__ ScanTask task_ids(const ScanArgs& a, const QueueCtx& q, int u, bool is_long, int ns) {
+  ScanTask k;
+  int p = 0, sl = 0;
+  k.ok = is_long ? queue_task(u, ns, q.x, q.nq, 0, q.long_pairs, p, sl)
+                 : queue_task(u - q.long_tasks, ns, q.x, q.nq, q.long_pairs, q.pairs, p, sl);
+  const int hh = (int)a.H;
+  k.rank = p / hh;
+  k.h = p - k.rank * hh;
+  k.slice = sl;
+  k.n = k.c0 = k.c1 = k.L = k.s0 = 0;
+  return k;
+}
+
+// The sequence fields of task k from its rank descriptor d (wave-uniform values).
+__device__ __forceinline__ void task_fields(const ScanArgs& a, ScanTask& k, const int4_v d) {
+  if (!k.ok) return;
+  k.n = __builtin_amdgcn_readfirstlane(d[0]);
+  int64_t c0 = __builtin_amdgcn_readfirstlane(d[1]);
+  k.s0 = __builtin_amdgcn_readfirstlane(d[2]);
+  k.L = __builtin_amdgcn_readfirstlane(d[3]);
+  int64_t cnt = (k.L + kChunk - 1) / kChunk;
+  if (cnt > a.n_chunk_ub) cnt = a.n_chunk_ub;
+  int64_t c1 = c0 + cnt;
+  if (c1 > a.n_chunk_ub) c1 = a.n_chunk_ub;  // only on invalid cu_seqlens
+  if (c0 > c1) c0 = c1;
+  k.c0 = c0;
+  k.c1 = c1;
+}
+
+// Walk the short tasks from id `u_cur` on until the queue runs dry.  `pending` (lane 0 of
+// wave 0) holds the request for the id after u_cur.
+template <int DK, int DV, int NV, typename OutT>
+__device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueCtx& q, const int4* rank_desc,
+                                                 int u_cur, int pending, uint8_t* smem) {
+  using R = Rec<DK, DV>;
+  using SM = ScanSmem<DK, DV, NV>;
+  using TR = TokRegs<DK, NV>;
+  using KR = KeyRegs<DK>;
+  constexpr int KSK = DK / 32;
+  constexpr int TPK = DK / 64;
+  constexpr int NT = NV / 16;
+  constexpr int NS = DV / NV;
+  static_assert(scan_depth<NV>() == 2, "the task walk keeps a two-deep ring");
+
+  uint8_t* sbb = smem + SM::SB;
+  uint8_t* db = smem + SM::DB;
+  float* cn = reinterpret_cast<float*>(smem + SM::CN);
+  float* red = reinterpret_cast<float*>(smem + SM::RED);
+
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int l = tid & 63, t = l & 15, gq = l >> 4;
+  const bool tok_wave = wv < 4;
+  const int i = wv & 3;  // token block (tok_wave) or key block (otherwise)
+
+  ScanTask cur = task_ids(a, q, u_cur, false, NS);
+  if (!cur.ok) return;
+  task_fields(a, cur, reinterpret_cast<const int4_v*>(rank_desc)[cur.rank]);
+
+  auto hdr_of = [&](int64_t c, int h) __attribute__((always_inline)) {
+    return reinterpret_cast<const float*>(a.rec + ((size_t)c * a.H + h) * R::BYTES + R::HDR);
+  };
+  // record of virtual chunk v of the stream "this task's chunks, then the next task's"
+  auto vrec = [&](int64_t v, const ScanTask& k, const ScanTask& nx, bool nx_ok, int& sl) __attribute__((always_inline)) {
+    int64_t c;
+    int hh;
+    const int64_t nk = k.c1 - k.c0;
+    if (v < nk) {
+      c = k.c0 + v; hh = k.h; sl = k.slice;
+    } else if (nx_ok) {
+      const int64_t w = v - nk, nn = nx.c1 - nx.c0;
+      c = nx.c0 + (w < nn ? w : nn - 1); hh = nx.h; sl = nx.slice;
+    } else {
+      c = k.c1 - 1; hh = k.h; sl = k.slice;  // past the end: loaded, never used
+    }
+    if (c < 0) c = 0;
+    return a.rec + ((size_t)c * a.H + hh) * R::BYTES;
+  };
+
+  OutT* out = reinterpret_cast<OutT*>(a.out);
+  const float oscale = a.scale;
+
+  // The two roles run their own task loops (their ring registers are then never live at
+  // the same time) with the same sequence of barriers: 0 (norms, maxima and the published
+  // id visible), 1 (S0 of the first chunk visible), then A and B of every step.
+  //
+  // After barrier 0, in both roles: the copy exponent from the LDS partials, then the next
+  // task's queue position and its rank descriptor (a vector load, read after barrier 1, so
+  // its latency does not hold the LDS waits of the barrier).
+  auto after_barrier0 = [&](const ScanTask& k, ScanTask& nx, int4_v& nd, int& es_out) __attribute__((always_inline)) {
+    // the largest column norm: one column per lane (the same sums as a loop over columns)
+    const int j = l < NV ? l : 0;
+    const float cmax = wave_max(l < NV ? cn[j] + cn[NV + j] + cn[2 * NV + j] + cn[3 * NV + j] : 0.f);
+    float vmax = red[0];
+#pragma unroll
+    for (int jj = 1; jj < 8; ++jj) vmax = fmaxf(vmax, red[jj]);
+    es_out = copy_exponent((double)cmax + (double)k.L * (double)vmax * (double)vmax);
+    const int u_nxt = __builtin_amdgcn_readfirstlane(*q.qs);
+    if (tid == 0) pending = queue_request(q.ctr);
+    nx = task_ids(a, q, u_nxt, false, NS);
+    const int rk = nx.ok ? nx.rank : 0;
+    // a buffer load (vector memory: it is waited for only where the fields are read)
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int4*>(rank_desc + rk), 0, 16, kBufferFlags);
+    nd = __builtin_bit_cast(int4_v, __builtin_amdgcn_raw_buffer_load_b128(rs, 0, 0, 0));
+  };
+
+  bool have_pre = false;  // the current task's initial state / header maxima were prefetched
+  bool ring_ok = false;   // ring slot 0 holds the current task's first chunk
+
+  if (tok_wave) {
+    // ---- token block i: Delta rows, then the output rows ----
+    TR tb[2];
+    float hv = 0.f;  // header maxima max|v| of up to 256 chunks of a task (one per lane)
+    auto load_hdr = [&](const ScanTask& k) __attribute__((always_inline)) {
+      int64_t c = k.c0 + 64 * i + l;
+      if (c >= k.c1) c = k.c1 > k.c0 ? k.c1 - 1 : 0;  // loaded, masked at the boundary
+      hv = *hdr_of(c, k.h);
+    };
+    for (;;) {
+      if (tid == 0) *q.qs = pending;  // the id after the next (requested at the previous boundary)
+      if (!have_pre) load_hdr(cur);
+      float vm = (cur.c0 + 64 * i + l < cur.c1) ? hv : 0.f;
+      for (int64_t c = cur.c0 + 256 + tid; c < cur.c1; c += 256) vm = fmaxf(vm, *hdr_of(c, cur.h));
+      vm = wave_max(vm);
+      if (l == 0) red[wv] = vm;
+      __syncthreads();  // 0
+      int es;
+      ScanTask nxt;
+      int4_v nd;
+      after_barrier0(cur, nxt, nd, es);
+      const int64_t nk = cur.c1 - cur.c0;
+      if (!ring_ok && nk > 0) {
+        int sl;
+        const uint8_t* r0 = vrec(0, cur, nxt, false, sl);
+        load_tok<0, DK, DV, NV>(tb[0], r0, i, l, sl);
+        load_tok<1, DK, DV, NV>(tb[0], r0, i, l, sl);
+        load_tok<2, DK, DV, NV>(tb[0], r0, i, l, sl);
+      }
+      __syncthreads();  // 1
+      task_fields(a, nxt, nd);
+      const bool nx_pre = nxt.ok && nxt.c1 > nxt.c0;  // the ring may run on into the next task
+      if (nxt.ok) load_hdr(nxt);  // under this task's steps
+
+      const int col0 = cur.slice * NV;
+      auto step = [&](const TR& c_, TR& n_, const uint8_t* nrec, int nsl, int64_t k, auto same)
+                      __attribute__((always_inline)) {
+        constexpr bool SAME = decltype(same)::value != 0;
+        if (!SAME) load_tok<0, DK, DV, NV>(n_, nrec, i, l, nsl);
+        const f16x8* sb = reinterpret_cast<const f16x8*>(sbb + (size_t)(k & 1) * SM::SBUF);
+        f16x8 sf[KSK][NT];
+#pragma unroll
+        for (int s = 0; s < KSK; ++s)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) sf[s][nt] = sb[(s * NT + nt) * 64 + l];
+        f32x4 d[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) d[nt] = zero4();
+#pragma unroll
+        for (int s = 0; s < KSK; ++s)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) d[nt] = mfma16(c_.wf[s], sf[s][nt], d[nt]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          f16x4 df;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) df[r] = (_Float16)(ldexpf((float)c_.uf[nt][r], es - c_.ue) - d[nt][r]);
+          *reinterpret_cast<f16x4*>(db + (((size_t)(i >> 1) * NT + nt) * 64 + l) * 16 + (i & 1) * 8) = df;
+        }
+        if (SAME) load_tok<0, DK, DV, NV>(n_, nrec, i, l, nsl);
+        else load_tok<1, DK, DV, NV>(n_, nrec, i, l, nsl);
+        f32x4 o[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) o[nt] = zero4();
+#pragma unroll
+        for (int s = 0; s < KSK; ++s)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) o[nt] = mfma16(sf[s][nt], c_.qf[s], o[nt]);
+        if (SAME) load_tok<1, DK, DV, NV>(n_, nrec, i, l, nsl);
+        __syncthreads();  // A: Delta complete
+        if (!SAME) load_tok<2, DK, DV, NV>(n_, nrec, i, l, nsl);
+        f16x8 dfr[2][NT];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            dfr[s2][nt] = *reinterpret_cast<const f16x8*>(db + (((size_t)s2 * NT + nt) * 64 + l) * 16);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) o[nt] = mfma16(dfr[s2][nt], c_.af[s2], o[nt]);
+        if (SAME) load_tok<2, DK, DV, NV>(n_, nrec, i, l, nsl);
+        const int64_t rem = cur.L - k * kChunk;
+        const int len = rem < kChunk ? (int)rem : kChunk;
+        const int i_loc = 16 * i + t;
+        const int64_t tok = cur.s0 + k * kChunk + i_loc;
+        if (i_loc < len && tok >= 0 && tok < a.T_total) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            float v4[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v4[r] = ldexpf(o[nt][r], -es) * oscale;
+            store4(out + ((size_t)tok * a.H + cur.h) * DV + col0 + 16 * nt + 4 * gq, v4);
+          }
+        }
+        __syncthreads();  // B: next S0 complete
+      };
+      // ring slot of chunk k is k & 1, and the next task's first chunk lands in slot 0
+      {
+        int64_t k = 0;
+        int sl;
+        for (; k + 2 <= nk; k += 2) {
+          const uint8_t* n1 = vrec(k + 1, cur, nxt, nx_pre, sl);
+          step(tb[0], tb[1], n1, sl, k, IntC<0>{});
+          const uint8_t* n2 = vrec(k + 2, cur, nxt, nx_pre, sl);
+          step(tb[1], tb[0], n2, sl, k + 1, IntC<0>{});
+        }
+        if (k < nk) {
+          const uint8_t* n1 = vrec(k + 1, cur, nxt, nx_pre, sl);
+          step(tb[0], tb[0], n1, sl, k, IntC<1>{});
+        }
+      }
+      // the next task's first chunk sits in slot 0 when this task walked at least one step
+      // and the next one has a chunk
+      ring_ok = nk > 0 && nx_pre;
+      have_pre = nxt.ok;
+      if (!nxt.ok) return;
+      cur = nxt;
+    }
+  } else {
+    // ---- key block i: S_next = Diag(exp(G_last)) S0 + K~^T Delta ----
+    KR kb[2];
+    float S[TPK][NT][4];   // fp32 state rows (C layout, as in scan_walk)
+    float Sn[TPK][NT][4];  // the next task's initial rows, in flight
+    auto load_state = [&](const ScanTask& k) __attribute__((always_inline)) {
+      const size_t sbase = ((size_t)k.n * a.H + k.h) * DK * DV;
+      const int col0 = k.slice * NV;
+#pragma unroll
+      for (int p = 0; p < TPK; ++p)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 16 * (TPK * i + p) + 4 * gq + r;
+            Sn[p][nt][r] = a.h0 ? a.h0[sbase + (size_t)row * DV + col0 + 16 * nt + t] : 0.f;
+          }
+    };
+    for (;;) {
+      if (!have_pre) load_state(cur);
+#pragma unroll
+      for (int p = 0; p < TPK; ++p)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S[p][nt][r] = Sn[p][nt][r];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float ss = 0.f;
+#pragma unroll
+        for (int p = 0; p < TPK; ++p)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ss = fmaf(S[p][nt][r], S[p][nt][r], ss);
+        ss = rows4_sum(ss);
+        if (gq == 0) cn[i * NV + 16 * nt + t] = ss;
+      }
+      if (l == 0) red[wv] = 0.f;
+      __syncthreads();  // 0
+      int es;
+      ScanTask nxt;
+      int4_v nd;
+      after_barrier0(cur, nxt, nd, es);
+      const int64_t nk = cur.c1 - cur.c0;
+      if (!ring_ok && nk > 0) {
+        int sl;
+        const uint8_t* r0 = vrec(0, cur, nxt, false, sl);
+        load_key<0, DK, DV>(kb[0], r0, i, l);
+        load_key<1, DK, DV>(kb[0], r0, i, l);
+      }
+      auto write_state = [&](int buf) __attribute__((always_inline)) {
+        uint8_t* sb = sbb + (size_t)buf * SM::SBUF;
+#pragma unroll
+        for (int p = 0; p < TPK; ++p) {
+          const int ct = TPK * i + p;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            f16x4 f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) f[r] = (_Float16)ldexpf(S[p][nt][r], es);
+            *reinterpret_cast<f16x4*>(sb + (((size_t)(ct >> 1) * NT + nt) * 64 + l) * 16 + (ct & 1) * 8) = f;
+          }
+        }
+      };
+      write_state(0);
+      __syncthreads();  // 1
+      task_fields(a, nxt, nd);
+      const bool nx_pre = nxt.ok && nxt.c1 > nxt.c0;
+      if (nxt.ok) load_state(nxt);  // under this task's steps
+
+      auto step = [&](const KR& c_, KR& n_, const uint8_t* nrec, int64_t k, auto same) __attribute__((always_inline)) {
+        constexpr bool SAME = decltype(same)::value != 0;
+        if (!SAME) load_key<0, DK, DV>(n_, nrec, i, l);
+        __syncthreads();  // A: Delta complete
+        f16x8 dfr[2][NT];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            dfr[s2][nt] = *reinterpret_cast<const f16x8*>(db + (((size_t)s2 * NT + nt) * 64 + l) * 16);
+#pragma unroll
+        for (int p = 0; p < TPK; ++p) {
+          const float lam[4] = {row_bcast<0>(c_.lam[p]), row_bcast<1>(c_.lam[p]), row_bcast<2>(c_.lam[p]),
+                                row_bcast<3>(c_.lam[p])};
+          const float ecf = __int_as_float(c_.ec[p]);
+          const int ue4[4] = {__float_as_int(row_bcast<0>(ecf)) - es, __float_as_int(row_bcast<1>(ecf)) - es,
+                              __float_as_int(row_bcast<2>(ecf)) - es, __float_as_int(row_bcast<3>(ecf)) - es};
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            f32x4 u = zero4();
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) u = mfma16(c_.kt[p][s2], dfr[s2][nt], u);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[p][nt][r] = fmaf(lam[r], S[p][nt][r], ldexpf(u[r], ue4[r]));
+          }
+        }
+        if (SAME) load_key<0, DK, DV>(n_, nrec, i, l);
+        load_key<1, DK, DV>(n_, nrec, i, l);
+        write_state((int)((k + 1) & 1));
+        __syncthreads();  // B: next S0 complete
+      };
+      {
+        int64_t k = 0;
+        int sl;
+        for (; k + 2 <= nk; k += 2) {
+          step(kb[0], kb[1], vrec(k + 1, cur, nxt, nx_pre, sl), k, IntC<0>{});
+          step(kb[1], kb[0], vrec(k + 2, cur, nxt, nx_pre, sl), k + 1, IntC<0>{});
+        }
+        if (k < nk) step(kb[0], kb[0], vrec(k + 1, cur, nxt, nx_pre, sl), k, IntC<1>{});
+      }
+      if (a.ht) {
+        const size_t sbase = ((size_t)cur.n * a.H + cur.h) * DK * DV;
+        const int col0 = cur.slice * NV;
+#pragma unroll
+        for (int p = 0; p < TPK; ++p)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int row = 16 * (TPK * i + p) + 4 * gq + r;
+              a.ht[sbase + (size_t)row * DV + col0 + 16 * nt + t] = S[p][nt][r];
+            }
+      }
+      ring_ok = nk > 0 && nx_pre;
+      have_pre = nxt.ok;
+      if (!nxt.ok) return;
+      cur = nxt;
+    }
+  }
+}
+
+// One resident workgroup per compute unit (gridDim.x of them): long tasks one at a time,
+// then short tasks pipelined, each from this workgroup's queue.
+template <int DK, int DV, int NVL, int NVS, typename OutT>
+__global__ __launch_bounds__(kScanThreads) void state_scan_tasks_kernel(ScanArgs a, TaskArgs ta) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int DL = 2;  // ring depth of the narrow long walk (three deep spills)
+  constexpr size_t SL = ScanSmem<DK, DV, NVL>::BYTES, SS = ScanSmem<DK, DV, NVS>::BYTES;
+  constexpr size_t SMB = SL > SS ? SL : SS;
+  int32_t* qs = reinterpret_cast<int32_t*>(smem + ((SMB + 15) & ~(size_t)15));
+  QueueCtx q;
+  q.nq = gridDim.x >= kQueueSlots ? kQueueSlots : 1;
+  q.x = (int)(blockIdx.x % q.nq);
+  q.ctr = ta.queue + q.x;
+  q.pairs = (int)(a.N * a.H);
+  // narrow slices for the long class only when its chains on wide slices would leave
+  // compute units without a task
+  const int lp = *ta.n_long * (int)a.H;
+  const bool narrow = (int64_t)lp * (DV / NVS) < (int64_t)gridDim.x;
+  q.long_pairs = lp;
+  q.long_slices = narrow ? DV / NVL : DV / NVS;
+  const int lcnt = lp > q.x ? (lp - q.x + q.nq - 1) / q.nq : 0;
+  q.long_tasks = lcnt * q.long_slices;
+  q.qs = qs;
+  const int tid = threadIdx.x;
+
+  // long tasks: one id at a time
+  bool mark = blockIdx.x == 0;
+  int u;
+  for (;;) {
+    if (tid == 0) qs[1] = __hip_atomic_fetch_add(q.ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    u = __builtin_amdgcn_readfirstlane(qs[1]);
+    const ScanTask k = task_ids(a, q, u, true, q.long_slices);
+    if (!k.ok) break;
+    const int64_t n = a.seq_order[k.rank];
+    if (narrow) scan_walk<DK, DV, NVL, OutT, false, DL>(a, FuseArgs{}, n, k.h, k.slice, mark, smem);
+    else scan_walk<DK, DV, NVS, OutT, false>(a, FuseArgs{}, n, k.h, k.slice, mark, smem);
+    mark = false;
+  }
+  if (mark && tid == 0 && a.ctl)
+    __hip_atomic_store(a.ctl, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // no waits in this path
+  // short tasks: `u` is the first one (or past the queue's end); request the one after it
+  int pending = 0;
+  if (tid == 0) pending = queue_request(q.ctr);
+  scan_short_tasks<DK, DV, NVS, OutT>(a, q, ta.rank_desc, u, pending, smem);
+}
+
+template <int DK, int DV, int NVL, int NVS>
+constexpr size_t scan_tasks_smem() {
+  constexpr size_t SL = ScanSmem<DK, DV, NVL>::BYTES, SS = ScanSmem<DK, DV, NVS>::BYTES;
+  constexpr size_t SMB = SL > SS ? SL : SS;
+  return ((SMB + 15) & ~(size_t)15) + 16;
+}
+
+}  // namespace kda

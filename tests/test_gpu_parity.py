@@ -323,3 +323,36 @@ def test_validate_cu_seqlens_rejects_bad_offsets(bad, monkeypatch):
     o, h = run_gpu(x, d)  # the valid offsets pass the same check
     ro, rh = run_oracle(x)
     gate(x, o, h, ro, rh, "validated cu_seqlens")
+
+
+# Packed batches take the persistent state scan: sequences of at least KDA_LONG_CHUNKS
+# chunks walk one at a time (on 32-column slices when they are few), shorter ones are
+# pipelined (the next task's state, header maxima and first chunk fetched during the
+# current one).  Every split of a batch with one long sequence, short ones and empty ones,
+# the pipelined walk with one queue (3 workgroups) and with one workgroup per queue, and
+# the one-workgroup-per-chain scan.
+@pytest.mark.parametrize("env", [{}, {"KDA_LONG_CHUNKS": "1"}, {"KDA_LONG_CHUNKS": "0"},
+                                 {"KDA_LONG_CHUNKS": "1024"}, {"KDA_TASK_SCAN": "3"},
+                                 {"KDA_TASK_SCAN": "8"}, {"KDA_TASK_SCAN": "13", "KDA_LONG_CHUNKS": "2"},
+                                 {"KDA_TASK_SCAN": "0"}],
+                         ids=["default", "all-long", "no-long", "all-short", "3wg", "8wg", "13wg-long2", "off"])
+def test_persistent_scan_task_classes(env, monkeypatch):
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    rng = np.random.default_rng(77)
+    lens = [700, 0, 1, 64, 65, 129] + [int(v) for v in rng.integers(1, 100, size=40)] + [0, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    x = make_inputs(1, int(cu[-1]), 8, 128, 128, seed=79, dtype="bf16", cu_seqlens=cu)
+    o, h, ro, rh = _check(x, "persistent scan %s" % env)
+    for n, L in enumerate(lens):
+        if L == 0:
+            np.testing.assert_array_equal(h[n], x.h0[n])  # empty sequence: ht = h0
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64), (64, 128)])
+def test_persistent_scan_head_sizes(dk, dv):
+    """The long class on 32-column slices next to 64-column short tasks, every head size."""
+    lens = [900, 5, 70, 1, 33, 200, 0, 64]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    x = make_inputs(1, int(cu[-1]), 5, dk, dv, seed=dk * 3 + dv, dtype="bf16", cu_seqlens=cu)
+    _check(x, "persistent scan dk=%d dv=%d" % (dk, dv))
