@@ -102,14 +102,16 @@ static hipError_t launch_scan_nv(const ForwardPlan& p, hipStream_t stream) {
 
 template <int DK, int DV, typename OutT>
 static hipError_t launch_scan_tasks(const ForwardPlan& p, hipStream_t stream) {
-  constexpr int NVL = DV < 32 ? DV : 32, NVS = DV < 64 ? DV : 64;
+  constexpr int NVL = DV < 32 ? DV : 32, NVW = DV < 64 ? DV : 64;
   ScanArgs a = scan_args(p);
   TaskArgs ta;
   ta.queue = p.info + 8;
   ta.n_long = p.info + 2;
   ta.rank_desc = reinterpret_cast<const int4*>(p.rank_desc);
-  const size_t smem = scan_tasks_smem<DK, DV, NVL, NVS>();
-  auto kern = state_scan_tasks_kernel<DK, DV, NVL, NVS, OutT>;
+  const size_t smem = scan_tasks_smem<DK, DV, NVL, NVW>();
+  auto kern = state_scan_tasks_kernel<DK, DV, NVL, NVW, OutT>;
+  hipError_t ea = allow_smem(kern, smem);
+  if (ea != hipSuccess) return ea;
   hipLaunchKernelGGL(kern, dim3((unsigned)p.task_scan), dim3(kScanThreads), smem, stream, a, ta);
   return hipGetLastError();
 }

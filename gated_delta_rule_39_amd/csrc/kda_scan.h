@@ -108,8 +108,9 @@ struct KeyRegs {
 
 // The loads of a chunk's factors are issued in groups spread over the previous chunk's
 // step, so that the eight waves never queue all of them on the vector-memory path at
-// once.  Token waves: 0 = W, 1 = Qhat*exp(G), 2 = Aqk, U and ue.  Key waves: 0 = K~^T,
-// 1 = exp(G_last).
+// once.  Token waves: 0 = W, 1 = Qhat*exp(G), 2 = Aqk, U and ue (or 3 = U and ue, 4 = Aqk,
+// for a walk that reuses its slot and so requests each factor after its last use).  Key
+// waves: 0 = K~^T, 1 = exp(G_last).
 template <int PART, int DK, int DV, int NV, bool FUSED = false>
 __device__ __forceinline__ void load_tok(TokRegs<DK, NV>& c, const uint8_t* rec, int i, int l, int slice) {
   using R = Rec<DK, DV>;
@@ -123,14 +124,18 @@ __device__ __forceinline__ void load_tok(TokRegs<DK, NV>& c, const uint8_t* rec,
     for (int s = 0; s < TR::KSK; ++s)
       c.qf[s] = rec_load<f16x8, FUSED>(rec, R::BYTES, R::Q + ((size_t)(i * TR::KSK + s) * 64 + l) * 16);
   } else {
+    if (PART == 2 || PART == 4) {
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-      c.af[s2] = rec_load<f16x8, FUSED>(rec, R::BYTES, R::A + ((size_t)(i * 2 + s2) * 64 + l) * 16);
+      for (int s2 = 0; s2 < 2; ++s2)
+        c.af[s2] = rec_load<f16x8, FUSED>(rec, R::BYTES, R::A + ((size_t)(i * 2 + s2) * 64 + l) * 16);
+    }
+    if (PART == 2 || PART == 3) {
 #pragma unroll
-    for (int nt = 0; nt < TR::NT; ++nt)
-      c.uf[nt] = rec_load<f16x4, FUSED>(rec, R::BYTES, R::U + ((size_t)(i * R::NTV + slice * TR::NT + nt) * 64 + l) * 8);
-    c.ue = rec_load<int32_t, FUSED>(rec, R::BYTES, R::HDR + 4);
-    if (FUSED) c.vmax = rec_load<float, true>(rec, R::BYTES, R::HDR);
+      for (int nt = 0; nt < TR::NT; ++nt)
+        c.uf[nt] = rec_load<f16x4, FUSED>(rec, R::BYTES, R::U + ((size_t)(i * R::NTV + slice * TR::NT + nt) * 64 + l) * 8);
+      c.ue = rec_load<int32_t, FUSED>(rec, R::BYTES, R::HDR + 4);
+      if (FUSED) c.vmax = rec_load<float, true>(rec, R::BYTES, R::HDR);
+    }
   }
 }
 

@@ -4,20 +4,26 @@
 //
 // Why: in a batch of many short sequences a one-shot workgroup per chain spends most of
 // its life waiting: for its initial state rows, for the maxima of its chunk headers, for
-// its first chunk's factors, and only then steps once or twice.
+// its first chunk's factors, and only then steps once or twice; and each of the value
+// slices of a (sequence, head) pays that again.
 //
 // Two classes of sequences ("Autoresearch on Kimi Delta Attention", section "The
 // optimization trace": the recurrence split across value tiles to expose more independent
 // work):
 //  * long (at least `long_chunks` chunks; the first ones of the longest-first order): one
-//    task at a time, walked by scan_walk from a cold start.  When their chains on
-//    NVS-column slices would leave compute units idle they walk on the narrower
-//    NVL-column slices with a deeper ring: a step of a narrow slice is shorter, so the
-//    longest chain, which bounds the launch, ends sooner.
-//  * short (fewer chunks): NVS-column slices, pipelined: the next task's initial state,
-//    header maxima and first chunk are requested while the current one walks, so those
-//    latencies run under its steps.  Task ids are taken two ahead (only short tasks are
-//    ever held that way, so no task waits behind a long one).
+//    task at a time, walked by scan_walk from a cold start, on NVW-column slices; when
+//    those chains would leave compute units idle, on the narrower NVL-column slices: a
+//    step of a narrow slice is shorter, so the longest chain, which bounds the launch,
+//    ends sooner.
+//  * short (fewer chunks): one task per (sequence, head), all value columns, walked in
+//    64-column halves inside each step (so the registers stay those of a 64-column slice
+//    while the per-task costs and the chunk factors the halves share are paid once);
+//    pipelined: the next task's initial state, header maxima and first chunk are requested
+//    while the current one walks, so those latencies run under its steps.  The factors
+//    ring is one chunk deep (each step requests the next chunk into the slot it walks,
+//    each part after its last use): that leaves the registers for the next task's state.
+//    Task ids are taken two ahead (only short tasks are ever held that way, so no task
+//    waits behind a long one).
 //
 // Queues: one counter per XCD (block id mod 8 is the XCD a workgroup runs on); the
 // (sequence, head) pairs are dealt to the queues round-robin, and all slices of a pair sit
@@ -28,7 +34,6 @@
 #include "kda_scan.h"
 
 namespace kda {
-
 template <int V>
 struct IntC {
   static constexpr int value = V;
@@ -81,8 +86,8 @@ struct QueueCtx {
   int long_pairs;      // pairs of the long class (p < long_pairs)
   int pairs;           // all pairs
   int long_tasks;      // long tasks of this queue (its ids below this are long tasks)
-  int long_slices;     // value slices per long pair (DV / NVL or DV / NVS)
-  int32_t* qs;         // LDS slots: [0] the published id, [1] a workgroup-wide id
+  int long_slices;     // value slices per long pair (DV / NVL or DV / NVW)
+  int32_t* qs;         // LDS slots: [0] the published id, [1] a workgroup-wide id, [4..7] a descriptor
 };
 
 // The queue position (class check, pair, slice) of id u; `NS_` slices per pair.
@@ -115,20 +120,23 @@ __device__ __forceinline__ void task_fields(const ScanArgs& a, ScanTask& k, cons
   k.c1 = c1;
 }
 
-// Walk the short tasks from id `u_cur` on until the queue runs dry.  `pending` (lane 0 of
-// wave 0) holds the request for the id after u_cur.
-template <int DK, int DV, int NV, typename OutT>
+// Walk the short tasks (all DV columns of a (sequence, head), in 64-column halves) from id
+// `u_cur` on until the queue runs dry.  `pending` (lane 0 of wave 0) holds the request for
+// the id after u_cur.
+template <int DK, int DV, typename OutT>
 __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueCtx& q, const int4* rank_desc,
                                                  int u_cur, int pending, uint8_t* smem) {
+  constexpr int NV = DV;
   using R = Rec<DK, DV>;
   using SM = ScanSmem<DK, DV, NV>;
   using TR = TokRegs<DK, NV>;
   using KR = KeyRegs<DK>;
   constexpr int KSK = DK / 32;
   constexpr int TPK = DK / 64;
-  constexpr int NT = NV / 16;
-  constexpr int NS = DV / NV;
-  static_assert(scan_depth<NV>() == 2, "the task walk keeps a two-deep ring");
+  constexpr int NT = NV / 16;   // 16-column tiles of the task
+  constexpr int NH = NV / 64;   // 64-column halves
+  constexpr int NS = 1;         // one task per (sequence, head)
+  constexpr size_t STAGE = (SM::BYTES + 15) & ~(size_t)15;  // the key waves' state stage
 
   uint8_t* sbb = smem + SM::SB;
   uint8_t* db = smem + SM::DB;
@@ -172,33 +180,57 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
   // the same time) with the same sequence of barriers: 0 (norms, maxima and the published
   // id visible), 1 (S0 of the first chunk visible), then A and B of every step.
   //
+  // Ids and descriptors: lane 0 of wave 0 holds the id after the next one (`pending`, its
+  // request made at the previous boundary) and, once the request has returned (in the
+  // first step of a task), that task's rank descriptor; at a boundary it publishes both in
+  // LDS, so every wave decodes the next task from LDS alone (no vector-memory wait in the
+  // boundary, where the counter would hold it behind the previous task's stores).
+  int4_v pend_desc = {0, 0, 0, 0};
+  auto fetch_desc = [&](int u) __attribute__((always_inline)) {
+    const ScanTask k = task_ids(a, q, u, false, NS);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int4*>(rank_desc + (k.ok ? k.rank : 0)), 0, 16, kBufferFlags);
+    return __builtin_bit_cast(int4_v, __builtin_amdgcn_raw_buffer_load_b128(rs, 0, 0, 0));
+  };
+  if (tid == 0) pend_desc = fetch_desc(pending);
+  int4_v* qdesc = reinterpret_cast<int4_v*>(q.qs + 4);
+
   // After barrier 0, in both roles: the copy exponent from the LDS partials, then the next
-  // task's queue position and its rank descriptor (a vector load, read after barrier 1, so
-  // its latency does not hold the LDS waits of the barrier).
-  auto after_barrier0 = [&](const ScanTask& k, ScanTask& nx, int4_v& nd, int& es_out) __attribute__((always_inline)) {
-    // the largest column norm: one column per lane (the same sums as a loop over columns)
-    const int j = l < NV ? l : 0;
-    const float cmax = wave_max(l < NV ? cn[j] + cn[NV + j] + cn[2 * NV + j] + cn[3 * NV + j] : 0.f);
+  // task from the published id and descriptor.
+  auto after_barrier0 = [&](const ScanTask& k, ScanTask& nx, int& es_out) __attribute__((always_inline)) {
+    // the largest column norm: columns l and l + 64 per lane (the same sums as a loop over
+    // columns)
+    float cm = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      const int j = 64 * hh + l;
+      cm = fmaxf(cm, cn[j] + cn[NV + j] + cn[2 * NV + j] + cn[3 * NV + j]);
+    }
+    const float cmax = wave_max(cm);
     float vmax = red[0];
 #pragma unroll
     for (int jj = 1; jj < 8; ++jj) vmax = fmaxf(vmax, red[jj]);
     es_out = copy_exponent((double)cmax + (double)k.L * (double)vmax * (double)vmax);
     const int u_nxt = __builtin_amdgcn_readfirstlane(*q.qs);
+    const int4_v nd = *qdesc;
     if (tid == 0) pending = queue_request(q.ctr);
     nx = task_ids(a, q, u_nxt, false, NS);
-    const int rk = nx.ok ? nx.rank : 0;
-    // a buffer load (vector memory: it is waited for only where the fields are read)
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<int4*>(rank_desc + rk), 0, 16, kBufferFlags);
-    nd = __builtin_bit_cast(int4_v, __builtin_amdgcn_raw_buffer_load_b128(rs, 0, 0, 0));
+    task_fields(a, nx, nd);
+  };
+  // boundary start: publish the next task (lane 0 of wave 0)
+  auto publish = [&]() __attribute__((always_inline)) {
+    if (tid == 0) {
+      *q.qs = pending;
+      *qdesc = pend_desc;
+    }
   };
 
   bool have_pre = false;  // the current task's initial state / header maxima were prefetched
-  bool ring_ok = false;   // ring slot 0 holds the current task's first chunk
+  bool ring_ok = false;   // the ring slot holds the current task's first chunk
 
   if (tok_wave) {
     // ---- token block i: Delta rows, then the output rows ----
-    TR tb[2];
+    TR tb[1];
     float hv = 0.f;  // header maxima max|v| of up to 256 chunks of a task (one per lane)
     auto load_hdr = [&](const ScanTask& k) __attribute__((always_inline)) {
       int64_t c = k.c0 + 64 * i + l;
@@ -206,7 +238,7 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
       hv = *hdr_of(c, k.h);
     };
     for (;;) {
-      if (tid == 0) *q.qs = pending;  // the id after the next (requested at the previous boundary)
+      publish();
       if (!have_pre) load_hdr(cur);
       float vm = (cur.c0 + 64 * i + l < cur.c1) ? hv : 0.f;
       for (int64_t c = cur.c0 + 256 + tid; c < cur.c1; c += 256) vm = fmaxf(vm, *hdr_of(c, cur.h));
@@ -215,8 +247,7 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
       __syncthreads();  // 0
       int es;
       ScanTask nxt;
-      int4_v nd;
-      after_barrier0(cur, nxt, nd, es);
+      after_barrier0(cur, nxt, es);
       const int64_t nk = cur.c1 - cur.c0;
       if (!ring_ok && nk > 0) {
         int sl;
@@ -226,88 +257,107 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
         load_tok<2, DK, DV, NV>(tb[0], r0, i, l, sl);
       }
       __syncthreads();  // 1
-      task_fields(a, nxt, nd);
       const bool nx_pre = nxt.ok && nxt.c1 > nxt.c0;  // the ring may run on into the next task
       if (nxt.ok) load_hdr(nxt);  // under this task's steps
 
-      const int col0 = cur.slice * NV;
-      auto step = [&](const TR& c_, TR& n_, const uint8_t* nrec, int nsl, int64_t k, auto same)
+      // Delta for both halves before barrier A (the key waves wait for it); the output rows
+      // after it, half by half (S0 stays in its buffer until the step after)
+      auto step = [&](const TR& c_, TR& n_, const uint8_t* nrec, int nsl, int64_t k, auto same, auto first)
                       __attribute__((always_inline)) {
         constexpr bool SAME = decltype(same)::value != 0;
         if (!SAME) load_tok<0, DK, DV, NV>(n_, nrec, i, l, nsl);
         const f16x8* sb = reinterpret_cast<const f16x8*>(sbb + (size_t)(k & 1) * SM::SBUF);
-        f16x8 sf[KSK][NT];
 #pragma unroll
-        for (int s = 0; s < KSK; ++s)
+        for (int hh = 0; hh < NH; ++hh) {
+          f16x8 sf[KSK][4];
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) sf[s][nt] = sb[(s * NT + nt) * 64 + l];
-        f32x4 d[NT];
+          for (int s = 0; s < KSK; ++s)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) d[nt] = zero4();
+            for (int nt = 0; nt < 4; ++nt) sf[s][nt] = sb[(s * NT + 4 * hh + nt) * 64 + l];
+          f32x4 d[4];
 #pragma unroll
-        for (int s = 0; s < KSK; ++s)
+          for (int nt = 0; nt < 4; ++nt) d[nt] = zero4();
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) d[nt] = mfma16(c_.wf[s], sf[s][nt], d[nt]);
+          for (int s = 0; s < KSK; ++s)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          f16x4 df;
+            for (int nt = 0; nt < 4; ++nt) d[nt] = mfma16(c_.wf[s], sf[s][nt], d[nt]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) df[r] = (_Float16)(ldexpf((float)c_.uf[nt][r], es - c_.ue) - d[nt][r]);
-          *reinterpret_cast<f16x4*>(db + (((size_t)(i >> 1) * NT + nt) * 64 + l) * 16 + (i & 1) * 8) = df;
+          for (int nt = 0; nt < 4; ++nt) {
+            f16x4 df;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              df[r] = (_Float16)(ldexpf((float)c_.uf[4 * hh + nt][r], es - c_.ue) - d[nt][r]);
+            *reinterpret_cast<f16x4*>(db + (((size_t)(i >> 1) * NT + 4 * hh + nt) * 64 + l) * 16 + (i & 1) * 8) = df;
+          }
         }
-        if (SAME) load_tok<0, DK, DV, NV>(n_, nrec, i, l, nsl);
-        else load_tok<1, DK, DV, NV>(n_, nrec, i, l, nsl);
-        f32x4 o[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) o[nt] = zero4();
-#pragma unroll
-        for (int s = 0; s < KSK; ++s)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) o[nt] = mfma16(sf[s][nt], c_.qf[s], o[nt]);
-        if (SAME) load_tok<1, DK, DV, NV>(n_, nrec, i, l, nsl);
+        // the descriptor of the id held in reserve (its request has returned by now)
+        if (decltype(first)::value && tid == 0) pend_desc = fetch_desc(pending);
+        if (SAME) {
+          load_tok<0, DK, DV, NV>(n_, nrec, i, l, nsl);  // W, U and ue are spent
+          load_tok<3, DK, DV, NV>(n_, nrec, i, l, nsl);
+        } else {
+          load_tok<1, DK, DV, NV>(n_, nrec, i, l, nsl);
+        }
         __syncthreads();  // A: Delta complete
         if (!SAME) load_tok<2, DK, DV, NV>(n_, nrec, i, l, nsl);
-        f16x8 dfr[2][NT];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            dfr[s2][nt] = *reinterpret_cast<const f16x8*>(db + (((size_t)s2 * NT + nt) * 64 + l) * 16);
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) o[nt] = mfma16(dfr[s2][nt], c_.af[s2], o[nt]);
-        if (SAME) load_tok<2, DK, DV, NV>(n_, nrec, i, l, nsl);
         const int64_t rem = cur.L - k * kChunk;
         const int len = rem < kChunk ? (int)rem : kChunk;
         const int i_loc = 16 * i + t;
         const int64_t tok = cur.s0 + k * kChunk + i_loc;
-        if (i_loc < len && tok >= 0 && tok < a.T_total) {
+        const bool row_ok = i_loc < len && tok >= 0 && tok < a.T_total;
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            float v4[4];
+        for (int hh = 0; hh < NH; ++hh) {
+          // o^T = S0^T (Qhat exp(G))^T + Delta^T Aqk^T, columns of half hh
+          f16x8 sf[KSK][4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v4[r] = ldexpf(o[nt][r], -es) * oscale;
-            store4(out + ((size_t)tok * a.H + cur.h) * DV + col0 + 16 * nt + 4 * gq, v4);
+          for (int s = 0; s < KSK; ++s)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) sf[s][nt] = sb[(s * NT + 4 * hh + nt) * 64 + l];
+          f32x4 o[4];
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) o[nt] = zero4();
+#pragma unroll
+          for (int s = 0; s < KSK; ++s)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) o[nt] = mfma16(sf[s][nt], c_.qf[s], o[nt]);
+          f16x8 dfr[2][4];
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+              dfr[s2][nt] = *reinterpret_cast<const f16x8*>(db + (((size_t)s2 * NT + 4 * hh + nt) * 64 + l) * 16);
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) o[nt] = mfma16(dfr[s2][nt], c_.af[s2], o[nt]);
+          if (row_ok) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+              float v4[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) v4[r] = ldexpf(o[nt][r], -es) * oscale;
+              store4(out + ((size_t)tok * a.H + cur.h) * DV + 64 * hh + 16 * nt + 4 * gq, v4);
+            }
           }
+        }
+        if (SAME) {
+          load_tok<1, DK, DV, NV>(n_, nrec, i, l, nsl);
+          load_tok<4, DK, DV, NV>(n_, nrec, i, l, nsl);
         }
         __syncthreads();  // B: next S0 complete
       };
-      // ring slot of chunk k is k & 1, and the next task's first chunk lands in slot 0
-      {
-        int64_t k = 0;
+      // one slot: each step requests the next chunk (the next task's first after the last
+      // step) into the slot it walks, each part after its last use
+      // the first step on its own: a loop's memory-counter waits are set for its later
+      // iterations and would make this one wait for the prefetches issued just before it
+      auto walk_step = [&](int64_t k, auto first) __attribute__((always_inline)) {
         int sl;
-        for (; k + 2 <= nk; k += 2) {
-          const uint8_t* n1 = vrec(k + 1, cur, nxt, nx_pre, sl);
-          step(tb[0], tb[1], n1, sl, k, IntC<0>{});
-          const uint8_t* n2 = vrec(k + 2, cur, nxt, nx_pre, sl);
-          step(tb[1], tb[0], n2, sl, k + 1, IntC<0>{});
-        }
-        if (k < nk) {
-          const uint8_t* n1 = vrec(k + 1, cur, nxt, nx_pre, sl);
-          step(tb[0], tb[0], n1, sl, k, IntC<1>{});
-        }
-      }
+        const uint8_t* n1 = vrec(k + 1, cur, nxt, nx_pre, sl);
+        step(tb[0], tb[0], n1, sl, k, IntC<1>{}, first);
+      };
+      if (nk > 0) walk_step(0, IntC<1>{});
+      else if (tid == 0) pend_desc = fetch_desc(pending);
+      for (int64_t k = 1; k < nk; ++k) walk_step(k, IntC<0>{});
       // the next task's first chunk sits in slot 0 when this task walked at least one step
       // and the next one has a chunk
       ring_ok = nk > 0 && nx_pre;
@@ -317,30 +367,59 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
     }
   } else {
     // ---- key block i: S_next = Diag(exp(G_last)) S0 + K~^T Delta ----
-    KR kb[2];
+    KR kb[1];
     float S[TPK][NT][4];   // fp32 state rows (C layout, as in scan_walk)
-    float Sn[TPK][NT][4];  // the next task's initial rows, in flight
+    // The wave's RW state rows move between memory and S as 16-byte row pieces (piece
+    // f = 64 j + l: row f / (DV / 4), columns 4 (f % (DV / 4)) ..): 16 loads or stores per
+    // lane instead of 64 single words, which would fill the memory counter.  The C layout
+    // is taken from and given to this wave's own rows of a padded LDS stage (row pitch
+    // DV + 4 words: the 16 rows of a read or write fall in distinct banks); a wave's LDS
+    // operations complete in order, so no barrier is involved.
+    constexpr int RW = DK / 4;
+    constexpr int SP = DV + 4;
+    constexpr int PCS = RW * DV / 256;
+    float4 Sv[PCS];  // the next task's initial rows, in flight
+    constexpr int LPR = DV / 4;   // lanes per row of pieces
+    constexpr int RPJ = 64 / LPR;  // rows per piece index j
+    // piece j of lane l: memory offset 256 j + 4 l words from the wave's first row; stage
+    // offset RPJ SP j + (l / LPR) SP + 4 (l % LPR)
+    float* stage = reinterpret_cast<float*>(smem + STAGE) + (size_t)i * RW * SP;
+    float* stage_l = stage + (l / LPR) * SP + 4 * (l % LPR);
     auto load_state = [&](const ScanTask& k) __attribute__((always_inline)) {
-      const size_t sbase = ((size_t)k.n * a.H + k.h) * DK * DV;
-      const int col0 = k.slice * NV;
+      if (a.h0) {
+        const float* src = a.h0 + ((size_t)k.n * a.H + k.h) * DK * DV + (size_t)RW * i * DV + 4 * l;
+#pragma unroll
+        for (int j = 0; j < PCS; ++j) Sv[j] = *reinterpret_cast<const float4*>(src + 256 * j);
+      } else {
+#pragma unroll
+        for (int j = 0; j < PCS; ++j) Sv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    };
+    auto unpack_state = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < PCS; ++j) *reinterpret_cast<float4*>(stage_l + RPJ * SP * j) = Sv[j];
 #pragma unroll
       for (int p = 0; p < TPK; ++p)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = 16 * (TPK * i + p) + 4 * gq + r;
-            Sn[p][nt][r] = a.h0 ? a.h0[sbase + (size_t)row * DV + col0 + 16 * nt + t] : 0.f;
-          }
+          for (int r = 0; r < 4; ++r) S[p][nt][r] = stage[(16 * p + 4 * gq + r) * SP + 16 * nt + t];
+    };
+    auto store_state = [&](const ScanTask& k) __attribute__((always_inline)) {
+#pragma unroll
+      for (int p = 0; p < TPK; ++p)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) stage[(16 * p + 4 * gq + r) * SP + 16 * nt + t] = S[p][nt][r];
+      float* dst = a.ht + ((size_t)k.n * a.H + k.h) * DK * DV + (size_t)RW * i * DV + 4 * l;
+#pragma unroll
+      for (int j = 0; j < PCS; ++j)
+        *reinterpret_cast<float4*>(dst + 256 * j) = *reinterpret_cast<const float4*>(stage_l + RPJ * SP * j);
     };
     for (;;) {
       if (!have_pre) load_state(cur);
-#pragma unroll
-      for (int p = 0; p < TPK; ++p)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) S[p][nt][r] = Sn[p][nt][r];
+      unpack_state();
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         float ss = 0.f;
@@ -355,8 +434,7 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
       __syncthreads();  // 0
       int es;
       ScanTask nxt;
-      int4_v nd;
-      after_barrier0(cur, nxt, nd, es);
+      after_barrier0(cur, nxt, es);
       const int64_t nk = cur.c1 - cur.c0;
       if (!ring_ok && nk > 0) {
         int sl;
@@ -380,7 +458,6 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
       };
       write_state(0);
       __syncthreads();  // 1
-      task_fields(a, nxt, nd);
       const bool nx_pre = nxt.ok && nxt.c1 > nxt.c0;
       if (nxt.ok) load_state(nxt);  // under this task's steps
 
@@ -388,55 +465,49 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
         constexpr bool SAME = decltype(same)::value != 0;
         if (!SAME) load_key<0, DK, DV>(n_, nrec, i, l);
         __syncthreads();  // A: Delta complete
-        f16x8 dfr[2][NT];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            dfr[s2][nt] = *reinterpret_cast<const f16x8*>(db + (((size_t)s2 * NT + nt) * 64 + l) * 16);
+
+        float lam[TPK][4];
+        int ue4[TPK][4];
 #pragma unroll
         for (int p = 0; p < TPK; ++p) {
-          const float lam[4] = {row_bcast<0>(c_.lam[p]), row_bcast<1>(c_.lam[p]), row_bcast<2>(c_.lam[p]),
-                                row_bcast<3>(c_.lam[p])};
+          lam[p][0] = row_bcast<0>(c_.lam[p]); lam[p][1] = row_bcast<1>(c_.lam[p]);
+          lam[p][2] = row_bcast<2>(c_.lam[p]); lam[p][3] = row_bcast<3>(c_.lam[p]);
           const float ecf = __int_as_float(c_.ec[p]);
-          const int ue4[4] = {__float_as_int(row_bcast<0>(ecf)) - es, __float_as_int(row_bcast<1>(ecf)) - es,
-                              __float_as_int(row_bcast<2>(ecf)) - es, __float_as_int(row_bcast<3>(ecf)) - es};
+          ue4[p][0] = __float_as_int(row_bcast<0>(ecf)) - es; ue4[p][1] = __float_as_int(row_bcast<1>(ecf)) - es;
+          ue4[p][2] = __float_as_int(row_bcast<2>(ecf)) - es; ue4[p][3] = __float_as_int(row_bcast<3>(ecf)) - es;
+        }
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            f32x4 u = zero4();
+        for (int hh = 0; hh < NH; ++hh) {
+          f16x8 dfr[2][4];
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) u = mfma16(c_.kt[p][s2], dfr[s2][nt], u);
+          for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) S[p][nt][r] = fmaf(lam[r], S[p][nt][r], ldexpf(u[r], ue4[r]));
-          }
+            for (int nt = 0; nt < 4; ++nt)
+              dfr[s2][nt] = *reinterpret_cast<const f16x8*>(db + (((size_t)s2 * NT + 4 * hh + nt) * 64 + l) * 16);
+#pragma unroll
+          for (int p = 0; p < TPK; ++p)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+              f32x4 u = zero4();
+#pragma unroll
+              for (int s2 = 0; s2 < 2; ++s2) u = mfma16(c_.kt[p][s2], dfr[s2][nt], u);
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                S[p][4 * hh + nt][r] = fmaf(lam[p][r], S[p][4 * hh + nt][r], ldexpf(u[r], ue4[p][r]));
+            }
         }
         if (SAME) load_key<0, DK, DV>(n_, nrec, i, l);
         load_key<1, DK, DV>(n_, nrec, i, l);
         write_state((int)((k + 1) & 1));
         __syncthreads();  // B: next S0 complete
       };
-      {
-        int64_t k = 0;
+      auto walk_step = [&](int64_t k) __attribute__((always_inline)) {
         int sl;
-        for (; k + 2 <= nk; k += 2) {
-          step(kb[0], kb[1], vrec(k + 1, cur, nxt, nx_pre, sl), k, IntC<0>{});
-          step(kb[1], kb[0], vrec(k + 2, cur, nxt, nx_pre, sl), k + 1, IntC<0>{});
-        }
-        if (k < nk) step(kb[0], kb[0], vrec(k + 1, cur, nxt, nx_pre, sl), k, IntC<1>{});
-      }
-      if (a.ht) {
-        const size_t sbase = ((size_t)cur.n * a.H + cur.h) * DK * DV;
-        const int col0 = cur.slice * NV;
-#pragma unroll
-        for (int p = 0; p < TPK; ++p)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int row = 16 * (TPK * i + p) + 4 * gq + r;
-              a.ht[sbase + (size_t)row * DV + col0 + 16 * nt + t] = S[p][nt][r];
-            }
-      }
+        step(kb[0], kb[0], vrec(k + 1, cur, nxt, nx_pre, sl), k, IntC<1>{});
+      };
+      if (nk > 0) walk_step(0);  // on its own, as in the token role
+      for (int64_t k = 1; k < nk; ++k) walk_step(k);
+      if (a.ht) store_state(cur);
       ring_ok = nk > 0 && nx_pre;
       have_pre = nxt.ok;
       if (!nxt.ok) return;
@@ -445,14 +516,23 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
   }
 }
 
+// Dynamic LDS of the kernel below: the largest of its three scan layouts (the short one with
+// the key waves' state stage), then the id slots.
+template <int DK, int DV, int NVL, int NVW>
+constexpr size_t scan_tasks_smem() {
+  constexpr size_t A = ScanSmem<DK, DV, NVL>::BYTES, B = ScanSmem<DK, DV, NVW>::BYTES;
+  constexpr size_t C = ((ScanSmem<DK, DV, DV>::BYTES + 15) & ~(size_t)15) + (size_t)DK * (DV + 4) * 4;
+  constexpr size_t M = A > B ? (A > C ? A : C) : (B > C ? B : C);
+  return ((M + 15) & ~(size_t)15) + 32;
+}
+
 // One resident workgroup per compute unit (gridDim.x of them): long tasks one at a time,
 // then short tasks pipelined, each from this workgroup's queue.
-template <int DK, int DV, int NVL, int NVS, typename OutT>
+template <int DK, int DV, int NVL, int NVW, typename OutT>
 __global__ __launch_bounds__(kScanThreads) void state_scan_tasks_kernel(ScanArgs a, TaskArgs ta) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int DL = 2;  // ring depth of the narrow long walk (three deep spills)
-  constexpr size_t SL = ScanSmem<DK, DV, NVL>::BYTES, SS = ScanSmem<DK, DV, NVS>::BYTES;
-  constexpr size_t SMB = SL > SS ? SL : SS;
+  constexpr size_t SMB = scan_tasks_smem<DK, DV, NVL, NVW>() - 32;  // the id slots follow
   int32_t* qs = reinterpret_cast<int32_t*>(smem + ((SMB + 15) & ~(size_t)15));
   QueueCtx q;
   q.nq = gridDim.x >= kQueueSlots ? kQueueSlots : 1;
@@ -462,9 +542,9 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_tasks_kernel(ScanArgs
   // narrow slices for the long class only when its chains on wide slices would leave
   // compute units without a task
   const int lp = *ta.n_long * (int)a.H;
-  const bool narrow = (int64_t)lp * (DV / NVS) < (int64_t)gridDim.x;
+  const bool narrow = (int64_t)lp * (DV / NVW) < (int64_t)gridDim.x;
   q.long_pairs = lp;
-  q.long_slices = narrow ? DV / NVL : DV / NVS;
+  q.long_slices = narrow ? DV / NVL : DV / NVW;
   const int lcnt = lp > q.x ? (lp - q.x + q.nq - 1) / q.nq : 0;
   q.long_tasks = lcnt * q.long_slices;
   q.qs = qs;
@@ -481,7 +561,7 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_tasks_kernel(ScanArgs
     if (!k.ok) break;
     const int64_t n = a.seq_order[k.rank];
     if (narrow) scan_walk<DK, DV, NVL, OutT, false, DL>(a, FuseArgs{}, n, k.h, k.slice, mark, smem);
-    else scan_walk<DK, DV, NVS, OutT, false>(a, FuseArgs{}, n, k.h, k.slice, mark, smem);
+    else scan_walk<DK, DV, NVW, OutT, false>(a, FuseArgs{}, n, k.h, k.slice, mark, smem);
     mark = false;
   }
   if (mark && tid == 0 && a.ctl)
@@ -489,14 +569,7 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_tasks_kernel(ScanArgs
   // short tasks: `u` is the first one (or past the queue's end); request the one after it
   int pending = 0;
   if (tid == 0) pending = queue_request(q.ctr);
-  scan_short_tasks<DK, DV, NVS, OutT>(a, q, ta.rank_desc, u, pending, smem);
-}
-
-template <int DK, int DV, int NVL, int NVS>
-constexpr size_t scan_tasks_smem() {
-  constexpr size_t SL = ScanSmem<DK, DV, NVL>::BYTES, SS = ScanSmem<DK, DV, NVS>::BYTES;
-  constexpr size_t SMB = SL > SS ? SL : SS;
-  return ((SMB + 15) & ~(size_t)15) + 16;
+  scan_short_tasks<DK, DV, OutT>(a, q, ta.rank_desc, u, pending, smem);
 }
 
 }  // namespace kda
