@@ -1122,7 +1122,10 @@ __global__ __launch_bounds__(DK * 4) void cb_grad_a_kernel(CbArgs a) {
     for (int J = 0; J < 4; ++J)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 av = *reinterpret_cast<const float4*>(dAs + t * 64 + 16 * J + 4 * q);
+        // only the lower blocks of dA are written: the others hold whatever an earlier
+        // kernel left in LDS, so they are selected away, not multiplied by zero
+        const float4 ar = *reinterpret_cast<const float4*>(dAs + t * 64 + 16 * J + 4 * q);
+        const float4 av = J <= I ? ar : make_float4(0.f, 0.f, 0.f, 0.f);
         s = fmaf(av.x, lv[J][q].x, fmaf(av.y, lv[J][q].y, fmaf(av.z, lv[J][q].z, fmaf(av.w, lv[J][q].w, s))));
       }
     float y = dyv[t];
