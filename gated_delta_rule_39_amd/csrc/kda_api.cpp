@@ -186,6 +186,10 @@ extern "C" {
 
 int kda_version(void) { return 104; }
 
+kda_status_t kda_test_fill_lds(uint32_t bits, void* stream) {
+  return kda::fill_lds(bits, static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 const char* kda_status_string(kda_status_t s) {
   switch (s) {
     case KDA_OK: return "KDA_OK";

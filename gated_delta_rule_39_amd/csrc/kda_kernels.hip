@@ -2,6 +2,7 @@
 #include "kda_launch.h"
 
 #include <atomic>
+#include <cstdlib>
 #include <mutex>
 #include <utility>
 #include <vector>
@@ -49,6 +50,37 @@ static hipError_t allow_smem(K kern, size_t smem) {
   return hipSuccess;
 }
 
+// Test hook: with KDA_TEST_LDS_FILL=<32-bit pattern> set, every kernel of a call is preceded
+// by a fill of the whole LDS of every compute unit with that pattern.  No kernel here may
+// read an LDS word it has not written in the same launch (LDS keeps what the previous
+// kernel on the compute unit left); a NaN or Inf pattern makes any such read visible in
+// the outputs.
+__global__ __launch_bounds__(1024) void lds_fill_kernel(uint32_t bits, uint32_t words) {
+  extern __shared__ __align__(16) uint32_t lds_words[];
+  volatile uint32_t* v = lds_words;  // stores the compiler must keep
+  for (uint32_t i = threadIdx.x; i < words; i += blockDim.x) v[i] = bits;
+}
+
+hipError_t fill_lds(uint32_t bits, hipStream_t stream) {
+  int dev = 0, bytes = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev)) != hipSuccess)
+    return e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  if (bytes <= 0 || cus <= 0) return hipErrorInvalidValue;
+  if ((e = allow_smem(lds_fill_kernel, (size_t)bytes)) != hipSuccess) return e;
+  hipLaunchKernelGGL(lds_fill_kernel, dim3((unsigned)(4 * cus)), dim3(1024), (size_t)bytes, stream, bits,
+                     (uint32_t)(bytes / 4));
+  return hipGetLastError();
+}
+
+static hipError_t stale_lds(hipStream_t stream) {
+  const char* env = std::getenv("KDA_TEST_LDS_FILL");
+  if (!env || !env[0]) return hipSuccess;
+  return fill_lds((uint32_t)std::strtoul(env, nullptr, 0), stream);
+}
+
 static void mark(const ForwardPlan& p, int i, hipStream_t stream) {
   if (p.marks[i]) (void)hipEventRecord(p.marks[i], stream);
 }
@@ -86,6 +118,7 @@ static hipError_t launch_prep(const ForwardPlan& p, hipStream_t stream) {
   int64_t grid = p.chunk_wgs > 0 ? p.chunk_wgs : 256;
   const int64_t items = p.n_chunk_ub * (int64_t)p.H;
   if (grid > items) grid = items;
+  if (hipError_t ep = stale_lds(stream); ep != hipSuccess) return ep;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kPrepThreads), smem, stream, a);
   return hipGetLastError();
 }
@@ -96,6 +129,7 @@ static hipError_t launch_scan_nv(const ForwardPlan& p, hipStream_t stream) {
   const size_t smem = ScanSmem<DK, DV, NV>::BYTES;
   auto kern = state_scan_kernel<DK, DV, NV, OutT>;
   const int64_t blocks = p.N * (int64_t)p.H * (DV / NV);
+  if (hipError_t ep = stale_lds(stream); ep != hipSuccess) return ep;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kScanThreads), smem, stream, a);
   return hipGetLastError();
 }
@@ -112,6 +146,7 @@ static hipError_t launch_scan_tasks(const ForwardPlan& p, hipStream_t stream) {
   auto kern = state_scan_tasks_kernel<DK, DV, NVL, NVW, OutT>;
   hipError_t ea = allow_smem(kern, smem);
   if (ea != hipSuccess) return ea;
+  if (hipError_t ep = stale_lds(stream); ep != hipSuccess) return ep;
   hipLaunchKernelGGL(kern, dim3((unsigned)p.task_scan), dim3(kScanThreads), smem, stream, a, ta);
   return hipGetLastError();
 }
@@ -157,6 +192,7 @@ static hipError_t launch_fused(const ForwardPlan& p, hipStream_t stream) {
   hipError_t ea = allow_smem(kern, smem);
   if (ea != hipSuccess) return ea;
   const int64_t chains = p.N * (int64_t)p.H * (DV / 64);
+  if (hipError_t ep = stale_lds(stream); ep != hipSuccess) return ep;
   hipLaunchKernelGGL(kern, dim3((unsigned)(p.fuse_producers + chains)), dim3(kPrepThreads), smem, stream,
                      prep_args(p), scan_args(p), fz);
   return hipGetLastError();
@@ -187,6 +223,7 @@ hipError_t launch_forward(const ForwardPlan& p, hipStream_t stream) {
   // packed sequences: chunk table, sequence offsets and order from cu_seqlens on the device;
   // fixed-length rows need none of it (the kernels derive every chunk from its index)
   if (p.cu) {
+    if (hipError_t ep = stale_lds(stream); ep != hipSuccess) return ep;
     hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kMapThreads), 0, stream, p.cu, p.T, p.N, p.n_chunk_ub,
                        p.info, reinterpret_cast<ChunkEntry*>(p.table), p.seq_off, p.seq_order,
                        reinterpret_cast<int4*>(p.rank_desc), p.long_chunks);
@@ -209,6 +246,7 @@ static hipError_t launch_recurrent_dkdv(const ForwardPlan& p, hipStream_t stream
   const int64_t per_block = kRecThreads / 64;
   const int64_t blocks = (a.waves + per_block - 1) / per_block;
   auto kern = recurrent_kernel<DK, DV, InT>;
+  if (hipError_t ep = stale_lds(stream); ep != hipSuccess) return ep;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kRecThreads), 0, stream, a);
   return hipGetLastError();
 }
@@ -258,6 +296,7 @@ static hipError_t launch_chunk_backward_t(const BackwardPlan& p, hipStream_t str
     auto fac = cb_factor_kernel<DK, DV, InT>;
     const size_t smem = CbFacSmem<DK>::BYTES;
     if ((e = allow_smem(fac, smem)) != hipSuccess) return e;
+    if (hipError_t ep = stale_lds(stream); ep != hipSuccess) return ep;
     hipLaunchKernelGGL(fac, dim3((unsigned)items), dim3(DK * 4), smem, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -265,17 +304,20 @@ static hipError_t launch_chunk_backward_t(const BackwardPlan& p, hipStream_t str
   const size_t ssm = CbScanSmem<DK>::BYTES;
   auto sc = cb_state_scan_kernel<DK, DV, InT>;
   if ((e = allow_smem(sc, ssm)) != hipSuccess) return e;
+  if (hipError_t ep = stale_lds(stream); ep != hipSuccess) return ep;
   hipLaunchKernelGGL(sc, dim3((unsigned)chains), dim3(DK * 4), ssm, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (items > 0) {
     auto ga = cb_grad_a_kernel<DK, DV, InT>;
     const size_t gsm = CbGradASmem<DK, DV>::BYTES;
     if ((e = allow_smem(ga, gsm)) != hipSuccess) return e;
+    if (hipError_t ep = stale_lds(stream); ep != hipSuccess) return ep;
     hipLaunchKernelGGL(ga, dim3((unsigned)items), dim3(DK * 4), gsm, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     auto gb = cb_grad_b_kernel<DK, DV, InT>;
     const size_t smem = CbGradSmem<DK>::BYTES;
     if ((e = allow_smem(gb, smem)) != hipSuccess) return e;
+    if (hipError_t ep = stale_lds(stream); ep != hipSuccess) return ep;
     hipLaunchKernelGGL(gb, dim3((unsigned)items), dim3(DK * 4), smem, stream, a);
     e = hipGetLastError();
   }
@@ -305,6 +347,7 @@ size_t chunk_bwd_state_floats(int dk, int dv) {
 hipError_t launch_backward(const BackwardPlan& p, hipStream_t stream) {
   if (p.N <= 0) return hipSuccess;
   if (p.cu) {
+    if (hipError_t ep = stale_lds(stream); ep != hipSuccess) return ep;
     hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kMapThreads), 0, stream, p.cu, p.T, p.N, p.n_chunk_ub,
                        p.info, reinterpret_cast<ChunkEntry*>(p.table), p.seq_off, p.seq_order, nullptr, 0);
     hipError_t e = hipGetLastError();

@@ -74,4 +74,7 @@ hipError_t launch_backward(const BackwardPlan& p, hipStream_t stream);
 // scale of `p`; no workspace).
 hipError_t launch_recurrent(const ForwardPlan& p, hipStream_t stream);
 
+// Fill the whole LDS of every compute unit with a 32-bit pattern (a test hook).
+hipError_t fill_lds(uint32_t bits, hipStream_t stream);
+
 }  // namespace kda

@@ -53,6 +53,8 @@ _lib.kda_bwd.argtypes = [ctypes.POINTER(Problem)] + [_P] * 7 + [ctypes.c_float] 
 _lib.kda_bwd.restype = ctypes.c_int
 _lib.kda_status_string.argtypes = [ctypes.c_int]
 _lib.kda_status_string.restype = ctypes.c_char_p
+_lib.kda_test_fill_lds.argtypes = [ctypes.c_uint32, _P]
+_lib.kda_test_fill_lds.restype = ctypes.c_int
 _lib.kda_version.argtypes = []
 _lib.kda_version.restype = ctypes.c_int
 
@@ -75,6 +77,15 @@ def library():
 
 def version():
     return _lib.kda_version()
+
+
+def test_fill_lds(bits, stream=None):
+    """Test hook: fill every compute unit's LDS with the 32-bit pattern `bits` (kda_test_fill_lds)."""
+    import torch
+    st = stream if stream is not None else torch.cuda.current_stream()
+    rc = _lib.kda_test_fill_lds(ctypes.c_uint32(bits & 0xFFFFFFFF), ctypes.c_void_p(st.cuda_stream))
+    if rc != 0:
+        raise RuntimeError("kda_test_fill_lds: %s" % _lib.kda_status_string(rc).decode())
 
 
 def make_problem(B, T, H, dk, dv, dtype, num_seqs=0):

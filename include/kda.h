@@ -276,6 +276,16 @@ kda_status_t kda_bwd(const kda_problem_t* prob, const void* q, const void* k, co
                      float* dg, void* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* Test hook, not part of the method: fills the whole LDS of every compute unit with the
+ * 32-bit pattern `bits`, asynchronously on `stream` (a HIP stream, NULL for the default
+ * stream).  LDS keeps what the previous kernel on a compute unit left there, and no kernel
+ * of this library may read an LDS word it has not written in the same launch; a call made
+ * right after this fill with a NaN or Inf pattern shows any such read in its outputs.
+ * With the environment variable KDA_TEST_LDS_FILL set to a pattern (decimal or 0x hex),
+ * every kernel that kda_fwd, kda_decode and kda_bwd launch is preceded by this fill.
+ * Returns KDA_ERR_HIP when the launch fails. */
+kda_status_t kda_test_fill_lds(uint32_t bits, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* kda_status_string(kda_status_t status);
 
