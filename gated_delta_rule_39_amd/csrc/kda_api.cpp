@@ -20,7 +20,7 @@ constexpr int64_t kChunkTokens = 64;
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct Carve {
-  size_t info, table, seq_off, seq_order, rank_desc, defer, flags, rec, total;
+  size_t info, table, seq_off, seq_order, rank_desc, passes, small_list, defer, flags, rec, total;
 };
 
 bool sizes_ok(const kda_problem_t* p, bool packed, int64_t* N, int64_t* n_chunk_ub) {
@@ -54,7 +54,9 @@ Carve carve(const kda_problem_t* p, int64_t N, int64_t n_chunk_ub) {
   c.seq_off = c.table + align256((size_t)n_chunk_ub * 16);
   c.seq_order = c.seq_off + align256((size_t)(N + 1) * 4);
   c.rank_desc = c.seq_order + align256((size_t)N * 4);
-  c.defer = c.rank_desc + align256((size_t)N * 16);
+  c.passes = c.rank_desc + align256((size_t)N * 16);
+  c.small_list = c.passes + align256((size_t)n_chunk_ub * 8);
+  c.defer = c.small_list + align256((size_t)n_chunk_ub * 4);
   c.flags = c.defer + align256((size_t)n_chunk_ub * (size_t)p->heads * 4);
   c.rec = c.flags + align256((size_t)n_chunk_ub * (size_t)p->heads * 8 * 2);  // a flag per 64-column slice
   c.total = c.rec + (size_t)n_chunk_ub * (size_t)p->heads * kda::record_bytes(p->dk, p->dv);
@@ -311,6 +313,8 @@ static kda_status_t forward(const kda_problem_t* prob, const void* q, const void
   p.seq_off = reinterpret_cast<int32_t*>(ws + c.seq_off);
   p.seq_order = reinterpret_cast<int32_t*>(ws + c.seq_order);
   p.rank_desc = ws + c.rank_desc;
+  p.passes = ws + c.passes;
+  p.small_list = reinterpret_cast<int32_t*>(ws + c.small_list);
   p.rec = ws + c.rec;
   p.defer = reinterpret_cast<int32_t*>(ws + c.defer);
   p.flags = reinterpret_cast<uint64_t*>(ws + c.flags);

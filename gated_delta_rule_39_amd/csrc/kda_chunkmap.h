@@ -19,6 +19,10 @@
 //   info[2]           sequences of at least `long_chunks` chunks (a power of two, so they
 //                     are exactly the first ones of seq_order); 0 when long_chunks is 0
 //   info[8..15]       task counters of the persistent state scan, zeroed here
+//   passes[p]         (optional) the chunk kernel's passes: {chunk, partner or -1}; a chunk of
+//                     at most 32 tokens shares its 64-row pass with the next such chunk (rows
+//                     0..31 and 32..63), every other chunk has a pass of its own;
+//                     info[3] = number of passes (small_list[]: scratch, the short chunks in order)
 #pragma once
 
 #include "kda_device.h"
@@ -27,6 +31,28 @@ namespace kda {
 
 constexpr int kMapThreads = 1024;
 constexpr int kMapBuckets = 128;
+
+// Inclusive prefix sum over the workgroup's 1024 threads in thread order: a scan inside each
+// wave, then the waves' totals through LDS (`wsum`, 16 words).  `total` gets the sum of all.
+__device__ inline int32_t block_incl_scan(int32_t v, int32_t* wsum, int32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t x = __shfl_up(v, o, 64);
+    if (lane >= o) v += x;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  int32_t off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kMapThreads / 64; ++w) {
+    const int32_t x = wsum[w];
+    off += w < wave ? x : 0;
+    tot += x;
+  }
+  __syncthreads();  // wsum is free again
+  total = tot;
+  return v + off;
+}
 
 // Order bucket of a chunk count: 0 for none, else 1 + 4 floor(log2 c) + the next two bits
 // of c (monotone in c; a power of two starts its bucket).
@@ -44,16 +70,17 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* _
                                                                 int32_t* __restrict__ seq_off,
                                                                 int32_t* __restrict__ seq_order,
                                                                 int4* __restrict__ rank_desc,
-                                                                int32_t long_chunks) {
-  __shared__ int32_t scan[kMapThreads];
+                                                                int32_t long_chunks,
+                                                                int2* __restrict__ passes,
+                                                                int32_t* __restrict__ small_list) {
   __shared__ int32_t hist[kMapBuckets];
-  __shared__ int32_t carry_s;
+  __shared__ int32_t wsum[kMapThreads / 64];
   const int tid = threadIdx.x;
-  if (tid == 0) carry_s = 0;
   if (tid < kMapBuckets) hist[tid] = 0;
   __syncthreads();
 
   // 1. chunk counts, exclusive prefix -> seq_off; bucket histogram
+  int32_t carry = 0;  // chunks of the sequences before this batch (the same in every thread)
   for (int64_t base = 0; base < N; base += kMapThreads) {
     int64_t n = base + tid;
     int32_t cnt = 0;
@@ -63,26 +90,17 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* _
       cnt = (int32_t)(c < n_chunk_ub ? c : n_chunk_ub);
       atomicAdd(&hist[order_bucket(cnt)], 1);
     }
-    scan[tid] = cnt;
-    __syncthreads();
-    for (int o = 1; o < kMapThreads; o <<= 1) {
-      int32_t add = tid >= o ? scan[tid - o] : 0;
-      __syncthreads();
-      scan[tid] += add;
-      __syncthreads();
-    }
-    int32_t carry = carry_s;
-    if (n < N) seq_off[n] = carry + scan[tid] - cnt;
-    __syncthreads();
-    if (tid == kMapThreads - 1) carry_s = carry + scan[tid];
-    __syncthreads();
+    int32_t batch;
+    const int32_t incl = block_incl_scan(cnt, wsum, batch);
+    if (n < N) seq_off[n] = carry + incl - cnt;
+    carry += batch;
   }
-  int32_t total = carry_s;
+  int32_t total = carry;
   if (total > n_chunk_ub) total = (int32_t)n_chunk_ub;  // only on invalid cu_seqlens
   if (tid == 0) {
     info[0] = total;
-    info[1] = (carry_s > n_chunk_ub) ? 1 : 0;
-    seq_off[N] = carry_s;
+    info[1] = (carry > n_chunk_ub) ? 1 : 0;
+    seq_off[N] = carry;
   }
   if (tid < 8) info[8 + tid] = 0;
   __syncthreads();
@@ -137,6 +155,39 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* _
       if (rank_desc) rank_desc[pos] = make_int4((int)n, seq_off[n], (int)seq_start(cu, T, n), (int)L);
     }
   }
+
+  // 4. passes of the chunk kernel (the chunk table is complete: barriers since step 2).
+  //    Rank of each short chunk among the short ones, then the pass heads (other chunks and
+  //    short chunks of even rank) numbered in chunk order.
+  if (!passes) return;
+  __syncthreads();
+  auto is_short = [&](int64_t c) { return c < total && table[c].len <= 32; };
+  int32_t n_short = 0;
+  for (int64_t base = 0; base < total; base += kMapThreads) {
+    const int64_t c = base + tid;
+    const int32_t f = is_short(c) ? 1 : 0;
+    int32_t batch;
+    const int32_t incl = block_incl_scan(f, wsum, batch);
+    if (f) small_list[n_short + incl - 1] = (int32_t)c;
+    n_short += batch;
+  }
+  __syncthreads();  // small_list complete
+  int32_t n_short_seen = 0, n_pass = 0;
+  for (int64_t base = 0; base < total; base += kMapThreads) {
+    const int64_t c = base + tid;
+    const bool sh = is_short(c);
+    int32_t shorts, heads;
+    const int32_t rank = n_short_seen + block_incl_scan(sh ? 1 : 0, wsum, shorts) - 1;  // for short chunks
+    const bool head = c < total && (!sh || (rank & 1) == 0);
+    const int32_t hpos = block_incl_scan(head ? 1 : 0, wsum, heads);
+    if (head) {
+      const int32_t partner = (sh && rank + 1 < n_short) ? small_list[rank + 1] : -1;
+      passes[n_pass + hpos - 1] = make_int2((int32_t)c, partner);
+    }
+    n_short_seen += shorts;
+    n_pass += heads;
+  }
+  if (tid == 0) info[3] = n_pass;
 }
 
 }  // namespace kda

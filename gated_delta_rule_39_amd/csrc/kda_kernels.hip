@@ -92,6 +92,7 @@ static PrepArgs prep_args(const ForwardPlan& p) {
   a.info = p.info;
   a.nc = p.cu ? 0 : (p.T + kChunk - 1) / kChunk;
   a.table = reinterpret_cast<const ChunkEntry*>(p.table);
+  a.passes = reinterpret_cast<const int2*>(p.passes);
   a.rec = p.rec;
   a.defer = p.defer;
   return a;
@@ -226,7 +227,8 @@ hipError_t launch_forward(const ForwardPlan& p, hipStream_t stream) {
     if (hipError_t ep = stale_lds(stream); ep != hipSuccess) return ep;
     hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kMapThreads), 0, stream, p.cu, p.T, p.N, p.n_chunk_ub,
                        p.info, reinterpret_cast<ChunkEntry*>(p.table), p.seq_off, p.seq_order,
-                       reinterpret_cast<int4*>(p.rank_desc), p.long_chunks);
+                       reinterpret_cast<int4*>(p.rank_desc), p.long_chunks, reinterpret_cast<int2*>(p.passes),
+                       p.small_list);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -349,7 +351,8 @@ hipError_t launch_backward(const BackwardPlan& p, hipStream_t stream) {
   if (p.cu) {
     if (hipError_t ep = stale_lds(stream); ep != hipSuccess) return ep;
     hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kMapThreads), 0, stream, p.cu, p.T, p.N, p.n_chunk_ub,
-                       p.info, reinterpret_cast<ChunkEntry*>(p.table), p.seq_off, p.seq_order, nullptr, 0);
+                       p.info, reinterpret_cast<ChunkEntry*>(p.table), p.seq_off, p.seq_order, nullptr, 0,
+                       nullptr, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -28,6 +28,8 @@ struct ForwardPlan {
   int32_t* seq_off;
   int32_t* seq_order;
   void* rank_desc;  // packed: per rank of seq_order, {sequence, first chunk, first token, length}
+  void* passes;     // packed: the chunk kernel's passes {chunk, partner chunk or -1}
+  int32_t* small_list;  // packed: chunk map scratch (the chunks of at most 32 tokens)
   uint8_t* rec;
   int32_t* defer;  // per (chunk, head): the item needs the exact diagonal tiles (chunk kernel scratch)
   uint64_t* flags;        // per (chunk, head): record-ready flags of the fused kernel

@@ -89,8 +89,8 @@ struct PrepSmem {
   static constexpr size_t X = 0;                  // btot -> column operands | Bu fragments -> Bw^T | Bu
   static constexpr size_t Y = X + X_BYTES;        // L (strict lower) + inverse temporaries (upper)
   static constexpr size_t Z = Y + MAT;            // decay-factor table -> Tinv
-  static constexpr size_t GE = Z + Z_BYTES;       // G (log2 units) at the 16 group ends, then at token j*
-  static constexpr size_t GP = GE + 17 * DK * 4;  // Gram partial tiles: [L | Aqk^T][block w][tile b][lane] x 4 fp32
+  static constexpr size_t GE = Z + Z_BYTES;       // G (log2 units) at the 16 group ends, then at token j* (x2)
+  static constexpr size_t GP = GE + 18 * DK * 4;  // Gram partial tiles: [L | Aqk^T][block w][tile b][lane] x 4 fp32
   static constexpr size_t NRM = GP + 2 * 16 * 64 * 16;  // norm partials: [exp | sum][tensor 2][half 2][token 64]
   static constexpr size_t BETA = NRM + 2 * 2 * 2 * 64 * 4;
   static constexpr size_t RED = BETA + 64 * 4;    // [8] max |v| per wave, then the guard flag
@@ -110,6 +110,7 @@ struct PrepArgs {
   int32_t H;
   const int32_t* info;       // packed mode: info[0] = number of chunks
   const ChunkEntry* table;   // packed mode: the chunk table
+  const int2* passes;        // packed mode: passes {chunk, partner or -1}; info[3] = their number
   int64_t nc;                // fixed-length mode (cu == NULL): chunks per row; no table is built
   uint8_t* rec;     // records [n_chunk_ub][H]
   int32_t* defer;   // [chunk * H + head]: 1 if the item needs the exact diagonal tiles (written for every item)
@@ -195,16 +196,20 @@ struct RawAt {
   bool valid;
 };
 
-// `start`: first token of the chunk in the flattened order, `len`: its valid tokens.
+// `start`: first token of the chunk in the flattened order, `len`: its valid tokens.  A pass
+// of two chunks (`start2` >= 0): rows 32..63 are the second chunk's rows 0..31.
 template <int DK, int DV>
-__device__ __forceinline__ RawAt raw_at_tok(const PrepArgs& a, int64_t start, int len, int h) {
+__device__ __forceinline__ RawAt raw_at_tok(const PrepArgs& a, int64_t start, int len, int h,
+                                            int64_t start2 = -1, int len2 = 0) {
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int w = wv & 3, hf = wv >> 2, l = tid & 63, t = l & 15, gq = l >> 4;
   const int i_loc = 16 * w + t;
-  const int64_t tok = start + i_loc;
+  const bool second = start2 >= 0 && w >= 2;  // wave-uniform
+  const int row = second ? i_loc - 32 : i_loc;
+  const int64_t tok = (second ? start2 : start) + row;
   RawAt at;
-  at.valid = (i_loc < len) && (tok >= 0) && (tok < a.T_total);
+  at.valid = (row < (second ? len2 : len)) && (tok >= 0) && (tok < a.T_total);
   const int64_t tk = at.valid ? tok : 0;
   at.rowk = ((size_t)tk * a.H + h) * DK + hf * (DK / 2) + 4 * gq;
   at.rowv = ((size_t)tk * a.H + h) * DV + hf * (DV / 2) + 4 * gq;
@@ -331,9 +336,15 @@ __device__ __forceinline__ void rec_store(uint8_t* rec, size_t off, const V& v) 
 // every diagonal tile.  Every wave of the workgroup calls it (it holds barriers).
 // `mid(1)`, `mid(2)` and `mid(3)` run right after barriers #1, #2 and #4 (the persistent kernel
 // issues the next item's remaining loads there).
+//
+// Two chunks in one pass (`chunk2` >= 0, both of at most 32 tokens): rows 0..31 hold
+// `chunk`, rows 32..63 hold `chunk2`.  The pass is then block diagonal in its two halves:
+// the gate sum restarts at row 32, the Gram tiles across the halves are zero (so is Tinv
+// across them), G_last and j* are taken per half, and each half goes to its own record
+// (rows 0..31 there, the rest zero).
 template <int DK, int DV, bool EXACT, bool WT, typename Mid>
-__device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, const int h, ItemIn<DK, DV>& in,
-                                          uint8_t* smem, Mid&& mid) {
+__device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, const int chunk2, const int h,
+                                          ItemIn<DK, DV>& in, uint8_t* smem, Mid&& mid) {
   using R = Rec<DK, DV>;
   using SM = PrepSmem<DK, DV>;
   constexpr int KSK = DK / 32;   // contraction steps over key channels
@@ -375,7 +386,12 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   const int i_loc = 16 * w + t;  // this lane's token row inside the chunk
   const int cb = hf * (DK / 2);  // first key channel of the half
   const int sb = hf * KH;        // first key step of the half
+  const bool paired = chunk2 >= 0;                 // workgroup-uniform
+  const bool hi_half = paired && w >= 2;           // this wave's rows belong to chunk2
   uint8_t* rec = a.rec + ((size_t)chunk * a.H + h) * R::BYTES;
+  uint8_t* rec2 = paired ? a.rec + ((size_t)chunk2 * a.H + h) * R::BYTES : rec;
+  uint8_t* recw = hi_half ? rec2 : rec;            // this wave's record
+  const int wr = hi_half ? w - 2 : w;              // this wave's row block there
 
   // reads the lane's NE channels (of this half) of row `row` of a [*][DK] fp32 array in LDS
   auto lane_row = [&](const float* base, int row, float* out) {
@@ -479,7 +495,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
 #pragma unroll
     for (int b = 0; b < 3; ++b) {
       const float4 bt4 = *reinterpret_cast<const float4*>(btot + b * DK + cb + 16 * j + 4 * gq);
-      const bool use = b < w;
+      const bool use = b < w && (!hi_half || b >= 2);  // a second chunk's sum starts at its row 0
       off.x += use ? bt4.x : 0.f; off.y += use ? bt4.y : 0.f;
       off.z += use ? bt4.z : 0.f; off.w += use ? bt4.w : 0.f;
     }
@@ -506,12 +522,16 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   // Khat*exp(G_last - G) are scaled by the largest factor that still multiplies a nonzero
   // Delta row, exp(G_last - G_j*) per channel: with deep decays and beta = 0 at the end of
   // a chunk, the entries that carry the new state would otherwise fall below fp16's range.
+  // (two chunks in the pass: j* of each, the second's in gend row 17)
   const uint64_t bmask = __ballot(sbeta[l] > 0.f);
-  const int jstar = bmask ? 63 - __builtin_clzll(bmask) : -1;  // wave-uniform
-  if (i_loc == jstar) {
+  const uint64_t bm1 = paired ? (bmask & 0xffffffffull) : bmask, bm2 = paired ? (bmask >> 32) : 0;
+  const int jstar = bm1 ? 63 - __builtin_clzll(bm1) : -1;          // wave-uniform
+  const int jstar2 = bm2 ? 32 + 63 - __builtin_clzll(bm2) : -1;    // wave-uniform
+  const int jrow = hi_half ? jstar2 : jstar;                          // j* of this wave's chunk
+  if (i_loc == jrow) {
 #pragma unroll
     for (int j = 0; j < 2 * KH; ++j)
-      *reinterpret_cast<float4*>(gend + 16 * DK + cb + 16 * j + 4 * gq) =
+      *reinterpret_cast<float4*>(gend + (hi_half ? 17 : 16) * DK + cb + 16 * j + 4 * gq) =
           make_float4(G[4 * j], G[4 * j + 1], G[4 * j + 2], G[4 * j + 3]);
   }
   __syncthreads();  // #2: group-end gates visible, block totals and norm partials consumed
@@ -521,16 +541,19 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   if (tid < DK) {
     const int c = tid;
     auto ge = [&](int p) { return p < 0 ? 0.f : gend[p * DK + c]; };
-    const float glast = ge(15);
+    // G_last of the chunk (of each chunk of a pair: end of row 31, end of row 63)
+    const float glast = paired ? ge(7) : ge(15), glast2 = ge(15);
     // row exponent of Khat*exp(G_last - G): 2^-ec times every entry up to token j* stays
     // below 2 (|khat| <= 1, exp(G_last - G_j) <= exp(G_last - G_j*) for j <= j*)
     const int ec = jstar >= 0 ? max(-126, (int)floorf(glast - gend[16 * DK + c])) : 0;
+    const int ec2 = jstar2 >= 0 ? max(-126, (int)floorf(glast2 - gend[17 * DK + c])) : 0;
     int bad = 0;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
-      const float gp = ge(4 * ww - 1), gn = ge(4 * ww + 3), gm = ge(4 * ww + 1);
+      const bool second = paired && ww >= 2;  // a block of the pair's second chunk
+      const float gp = (paired && ww == 2) ? 0.f : ge(4 * ww - 1), gn = ge(4 * ww + 3), gm = ge(4 * ww + 1);
       et[ww * DK + c] = exp2_hw(gp);
-      et[(4 + ww) * DK + c] = exp2_hw(glast - gn - (float)ec);
+      et[(4 + ww) * DK + c] = exp2_hw((second ? glast2 : glast) - gn - (float)(second ? ec2 : ec));
       const float d1 = gp - gm, d2 = gm - gn;
       if (!(d1 <= kGuardLog2 && d2 <= kGuardLog2)) bad = 1;
       et[(11 + ww) * DK + c] = exp2_hw(fminf(d1, kGuardLog2));
@@ -541,6 +564,8 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     et[10 * DK + c] = exp2_hw(ge(11) - ge(7));
     if (bad) atomicOr(guard, 1);
     rec_store<WT, R::BYTES>(rec, R::LAM + (size_t)c * 8, uint2_v{__float_as_uint(exp2_hw(glast)), (uint32_t)ec});
+    if (paired)
+      rec_store<WT, R::BYTES>(rec2, R::LAM + (size_t)c * 8, uint2_v{__float_as_uint(exp2_hw(glast2)), (uint32_t)ec2});
   }
   // operand bases: rows khat_i exp(G_i - Gprev(w)) and qhat_i exp(G_i - Gprev(w)),
   // columns khat_j exp(Gnext(w) - G_j); all factors <= 1
@@ -548,9 +573,10 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   {
     float gp[NE], gn[NE];
     lane_row(gend, 4 * w + 3, gn);
-    lane_row(gend, w > 0 ? 4 * w - 1 : 0, gp);  // read always, zero for block 0: no branch
+    lane_row(gend, w > 0 ? 4 * w - 1 : 0, gp);  // read always, zero for a chunk's block 0: no branch
+    const bool first_block = w == 0 || (paired && w == 2);
 #pragma unroll
-    for (int e = 0; e < NE; ++e) gp[e] = (w > 0) ? gp[e] : 0.f;
+    for (int e = 0; e < NE; ++e) gp[e] = first_block ? 0.f : gp[e];
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
       const float fb = exp2_hw(G[e] - gp[e]);
@@ -565,7 +591,10 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     // A diagonal tile spans more decay than the fp32 path covers: the item is flagged
     // and redone by the exact variant, which rewrites its record.  This variant still
     // runs to the end, so every item issues the same memory operations.
-    if (tid == 0) a.defer[(size_t)chunk * a.H + h] = *guard;
+    if (tid == 0) {
+      a.defer[(size_t)chunk * a.H + h] = *guard;
+      if (paired) a.defer[(size_t)chunk2 * a.H + h] = *guard;
+    }
   }
 
   // identity fragments: B[k][n] = 1 iff the channel of slot k is 16*hh + n of the step
@@ -589,11 +618,12 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         qf[e] = (_Float16)(QB[8 * sl + e] * eS[e]);          // qhat exp(G)
-        kf[e] = (_Float16)(i_loc <= jstar ? YC[8 * sl + e] * eE[e] : 0.f);  // khat exp(G_last - G) 2^-ec
+        kf[e] = (_Float16)(i_loc <= jrow ? YC[8 * sl + e] * eE[e] : 0.f);  // khat exp(G_last - G) 2^-ec
         bwr[sl][e] = (_Float16)(bt * XB[8 * sl + e] * eS[e]); // beta khat exp(G)
         y[e] = (_Float16)YC[8 * sl + e];
       }
-      rec_store<WT, R::BYTES>(rec, R::Q + ((size_t)(w * KSK + s) * 64 + l) * 16, qf);
+      rec_store<WT, R::BYTES>(recw, R::Q + ((size_t)(wr * KSK + s) * 64 + l) * 16, qf);
+      if (paired) rec_store<WT, R::BYTES>(recw, R::Q + ((size_t)((wr + 2) * KSK + s) * 64 + l) * 16, f16x8{});
       // K~^T fragments: (K~ I) holds, per lane, key channel 16 ct + t at tokens 16 w + 4 gq + r,
       // ct = 2 s + hh.  The 16-byte record fragment of (ct, token pair w / 2) joins the halves of
       // token blocks 2 (w / 2) and 2 (w / 2) + 1: both go to LDS here, and after barrier #4 each
@@ -622,6 +652,10 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     if (tid == 0) {
       rec_store<WT, R::BYTES>(rec, R::HDR, vmax);
       rec_store<WT, R::BYTES>(rec, R::HDR + 4, ue);
+      if (paired) {  // the pair's max |v| bounds both chunks; U of both uses the same ue
+        rec_store<WT, R::BYTES>(rec2, R::HDR, vmax);
+        rec_store<WT, R::BYTES>(rec2, R::HDR + 4, ue);
+      }
     }
   }
   __syncthreads();  // #4: column operands visible
@@ -635,7 +669,9 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     const f16x4 lo = ktx[((((hf * 2 + (w >> 1)) * 2 + 0) * (2 * KH) + j) * 64) + l];
     const f16x4 hi = ktx[((((hf * 2 + (w >> 1)) * 2 + 1) * (2 * KH) + j) * 64) + l];
     const f16x8 frag = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    rec_store<WT, R::BYTES>(rec, R::KT + ((size_t)(ct * 2 + (w >> 1)) * 64 + l) * 16, frag);
+    // (a pair: token half w / 2 is a whole chunk, its record's first half; the second is zero)
+    rec_store<WT, R::BYTES>(recw, R::KT + ((size_t)(ct * 2 + (paired ? 0 : (w >> 1))) * 64 + l) * 16, frag);
+    if (paired) rec_store<WT, R::BYTES>(recw, R::KT + ((size_t)(ct * 2 + 1) * 64 + l) * 16, f16x8{});
   }
 
   // ---------------- (b) Gram matrices L (row block w) and Aqk^T (column block w) ----------------
@@ -649,7 +685,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   // Row factor exp(G_i - Gnext(b)) = exp(G_i - Gprev(w)) * exp(Gprev(w) - Gnext(b)).
 #pragma unroll
   for (int b = 0; b < 3; ++b) {
-    if (b < w) {
+    if (b < w && !(hi_half && b < 2)) {  // tiles across a pair's two chunks stay zero
       const int trow = 8 + (b == 0 ? (w == 2 ? 0 : 1) : 2);
 #pragma unroll
       for (int sl = 0; sl < KH; ++sl) {
@@ -858,7 +894,8 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
         f[r] = (_Float16)full[2 * s2][r];
         f[4 + r] = (_Float16)full[2 * s2 + 1][r];
       }
-      rec_store<WT, R::BYTES>(rec, R::A + ((size_t)(w * 2 + s2) * 64 + l) * 16, f);
+      // a pair's second chunk: its columns are the second half (s2 = 1), the first is zero
+      rec_store<WT, R::BYTES>(recw, R::A + ((size_t)(wr * 2 + (hi_half ? s2 ^ 1 : s2)) * 64 + l) * 16, f);
     }
   }
   // Bw^T fragments through identity products (rows = key channels, tokens in pi order)
@@ -979,7 +1016,8 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
       }
       f16x8 wf = {(_Float16)c0[0], (_Float16)c0[1], (_Float16)c0[2], (_Float16)c0[3],
                   (_Float16)c1[0], (_Float16)c1[1], (_Float16)c1[2], (_Float16)c1[3]};
-      rec_store<WT, R::BYTES>(rec, R::W + ((size_t)(w * KSK + sk) * 64 + l) * 16, wf);
+      rec_store<WT, R::BYTES>(recw, R::W + ((size_t)(wr * KSK + sk) * 64 + l) * 16, wf);
+      if (paired) rec_store<WT, R::BYTES>(recw, R::W + ((size_t)((wr + 2) * KSK + sk) * 64 + l) * 16, f16x8{});
     }
 #pragma unroll
     for (int ntl = 0; ntl < NTV / 2; ++ntl) {
@@ -991,7 +1029,8 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
         c = mfma16(tf[s], bfr, c);
       }
       f16x4 uf = {(_Float16)c[0], (_Float16)c[1], (_Float16)c[2], (_Float16)c[3]};
-      rec_store<WT, R::BYTES>(rec, R::U + ((size_t)(w * NTV + nt) * 64 + l) * 8, uf);
+      rec_store<WT, R::BYTES>(recw, R::U + ((size_t)(wr * NTV + nt) * 64 + l) * 8, uf);
+      if (paired) rec_store<WT, R::BYTES>(recw, R::U + ((size_t)((wr + 2) * NTV + nt) * 64 + l) * 8, f16x4{});
     }
   }
 }
@@ -1018,19 +1057,26 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
 template <int DK, int DV, typename InT, bool FUSED>
 __device__ __forceinline__ void chunk_walk(const PrepArgs& a, const FuseArgs& fz, const int wg, const int n_wg,
                                            uint8_t* smem) {
-  // items (fewer than 2^31), kept in scalar registers
+  // items (fewer than 2^31), kept in scalar registers; packed batches walk the passes
+  // (a pass: one chunk, or two chunks of at most 32 tokens)
   const int n_rows = (int)(a.T_total / (a.T > 0 ? a.T : 1));
-  const int n_items = (a.cu ? (int)sload_u32(a.info) : (int)(a.nc * n_rows)) * a.H;
+  const int n_items = (a.cu ? (int)sload_u32(a.info + 3) : (int)(a.nc * n_rows)) * a.H;
   int it = wg;
   if (it >= n_items) return;  // uniform for the workgroup
   auto entry = [&](int c) { return a.cu ? ld_entry(a.table + c) : entry_fixed(a, c); };
   // chunks from the last to the first: the records the scan reads first are written last
   // and are still in the caches (L2, MALL) when it starts.  Fused: position p holds chunk
   // p / rows of row p % rows.
-  const int n_chunks = n_items / a.H;
+  const int n_chunks = n_items / a.H;  // passes, for packed batches
   auto chunk_of = [&](int x) {
     const int pos = x / a.H;
     return FUSED ? (pos % n_rows) * (int)a.nc + pos / n_rows : n_chunks - 1 - pos;
+  };
+  // the chunks of item x's pass: {chunk, second chunk or -1}
+  auto pass_of = [&](int x) {
+    if (!a.cu) return make_int2(chunk_of(x), -1);
+    const uint64_t pc = sload_u64(a.passes + chunk_of(x));
+    return make_int2((int32_t)(uint32_t)pc, (int32_t)(uint32_t)(pc >> 32));
   };
   // every wave's record stores (written through at device scope) complete, then the flags
   // (device-scope stores), one per 64-column scan slice that reads the record
@@ -1046,15 +1092,27 @@ __device__ __forceinline__ void chunk_walk(const PrepArgs& a, const FuseArgs& fz
   // Where the chunks of this workgroup's first 64 items start and how many tokens they
   // hold, staged in LDS (entry j: item blockIdx.x + j * gridDim.x) with one batch of
   // vector loads: the next item's input loads then never wait behind dependent scalar
-  // metadata loads.  Later items (more than 64 per workgroup) read the chunk table.
+  // metadata loads.  Later items (more than 64 per workgroup) read the tables.  Entry:
+  // {first token lo, hi, valid tokens | second chunk's valid tokens << 16, second chunk's
+  // first token or -1} (a second chunk exists in packed batches, whose token offsets fit
+  // 31 bits).
   int4* meta = reinterpret_cast<int4*>(smem + PrepSmem<DK, DV>::META);
+  auto start_of = [&](const ChunkEntry& e) { return seq_start(a.cu, a.T, e.seq) + (int64_t)e.idx * kChunk; };
   if (threadIdx.x < 64) {
     const int64_t item = (int64_t)wg + (int64_t)threadIdx.x * n_wg;
-    int4 m = make_int4(0, 0, 0, 0);
+    int4 m = make_int4(0, 0, 0, -1);
     if (item < n_items) {
-      const ChunkEntry e = a.cu ? a.table[chunk_of((int)item)] : entry_fixed(a, chunk_of((int)item));
-      const int64_t st = seq_start(a.cu, a.T, e.seq) + (int64_t)e.idx * kChunk;
-      m = make_int4((int32_t)(uint32_t)st, (int32_t)(st >> 32), e.len, 0);
+      int2 pc = make_int2(chunk_of((int)item), -1);
+      if (a.cu) pc = a.passes[pc.x];
+      const ChunkEntry e = a.cu ? a.table[pc.x] : entry_fixed(a, pc.x);
+      const int64_t st = start_of(e);
+      int len2 = 0, st2 = -1;
+      if (pc.y >= 0) {
+        const ChunkEntry e2 = a.table[pc.y];
+        len2 = e2.len;
+        st2 = (int32_t)start_of(e2);
+      }
+      m = make_int4((int32_t)(uint32_t)st, (int32_t)(st >> 32), e.len | (len2 << 16), st2);
     }
     meta[threadIdx.x] = m;
   }
@@ -1064,10 +1122,15 @@ __device__ __forceinline__ void chunk_walk(const PrepArgs& a, const FuseArgs& fz
       const int4 m = meta[j];  // same address in every lane
       const uint32_t lo = __builtin_amdgcn_readfirstlane(m.x);
       const int32_t hi = __builtin_amdgcn_readfirstlane(m.y);
-      const int len = __builtin_amdgcn_readfirstlane(m.z);
-      return raw_at_tok<DK, DV>(a, (int64_t)(((uint64_t)(uint32_t)hi << 32) | lo), len, head_of(item));
+      const int lens = __builtin_amdgcn_readfirstlane(m.z);
+      const int st2 = __builtin_amdgcn_readfirstlane(m.w);
+      return raw_at_tok<DK, DV>(a, (int64_t)(((uint64_t)(uint32_t)hi << 32) | lo), lens & 0xffff, head_of(item),
+                                st2, lens >> 16);
     }
-    return raw_at<DK, DV>(a, entry(chunk_of(item)), head_of(item));
+    const int2 pc = pass_of(item);
+    if (pc.y < 0) return raw_at<DK, DV>(a, entry(pc.x), head_of(item));
+    const ChunkEntry e = entry(pc.x), e2 = entry(pc.y);
+    return raw_at_tok<DK, DV>(a, start_of(e), e.len, head_of(item), start_of(e2), e2.len);
   };
   {
     RawIn<DK, DV, InT> raw;
@@ -1085,7 +1148,8 @@ __device__ __forceinline__ void chunk_walk(const PrepArgs& a, const FuseArgs& fz
       const bool more = nx < n_items;
       const RawAt at = at_of(more ? j + 1 : j, more ? nx : it);
       load_part<0>(raw, a, at);
-      prep_item<DK, DV, false, FUSED>(a, chunk_of(it), head_of(it), in, smem, [&](int phase) {
+      const int2 pc = pass_of(it);
+      prep_item<DK, DV, false, FUSED>(a, pc.x, pc.y, head_of(it), in, smem, [&](int phase) {
         if (phase == 1) load_part<1>(raw, a, at);
         if (phase == 2) load_part<2>(raw, a, at);
         if (phase == 3) load_part<3>(raw, a, at);
@@ -1106,29 +1170,35 @@ __device__ __forceinline__ void chunk_walk(const PrepArgs& a, const FuseArgs& fz
   }
   __syncthreads();  // LDS is rewritten below; this workgroup's flags are visible to it
 
-  // exact pass over this workgroup's flagged items, 64 items per batch of flag loads
+  // exact pass over this workgroup's flagged items, 64 items per batch of flag loads; each
+  // flagged chunk of a pass is redone on its own
   const int n_own = (n_items - wg + n_wg - 1) / n_wg;
   const int lane = threadIdx.x & 63;
   for (int kb = 0; kb < n_own; kb += 64) {
     int f = 0;
     if (kb + lane < n_own) {
       const int x = wg + (kb + lane) * n_wg;
-      f = a.defer[(size_t)chunk_of(x) * a.H + head_of(x)];
+      const int2 pc = a.cu ? a.passes[chunk_of(x)] : make_int2(chunk_of(x), -1);
+      f = a.defer[(size_t)pc.x * a.H + head_of(x)] != 0;  // both chunks of a pass share the flag
     }
     uint64_t bits = __ballot(f != 0);  // the same in every wave
     while (bits) {
       const int b = __builtin_ctzll(bits);
       bits &= bits - 1;
       const int x = __builtin_amdgcn_readfirstlane(wg + (kb + b) * n_wg);
-      RawIn<DK, DV, InT> raw;
-      load_raw(raw, a, entry(chunk_of(x)), head_of(x));
-      ItemIn<DK, DV> in;
-      unpack_raw(in, raw);
-      prep_item<DK, DV, true, FUSED>(a, chunk_of(x), head_of(x), in, smem, [](int) {});
-      if (FUSED) {
-        publish(chunk_of(x), head_of(x), true);
-      } else {
-        __syncthreads();  // LDS is rewritten by the next item
+      const int2 pc = pass_of(x);
+      for (int k = 0; k < (pc.y >= 0 ? 2 : 1); ++k) {
+        const int c = k ? pc.y : pc.x;
+        RawIn<DK, DV, InT> raw;
+        load_raw(raw, a, entry(c), head_of(x));
+        ItemIn<DK, DV> in;
+        unpack_raw(in, raw);
+        prep_item<DK, DV, true, FUSED>(a, c, -1, head_of(x), in, smem, [](int) {});
+        if (FUSED) {
+          publish(c, head_of(x), true);
+        } else {
+          __syncthreads();  // LDS is rewritten by the next item
+        }
       }
     }
   }

@@ -356,3 +356,27 @@ def test_persistent_scan_head_sizes(dk, dv):
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     x = make_inputs(1, int(cu[-1]), 5, dk, dv, seed=dk * 3 + dv, dtype="bf16", cu_seqlens=cu)
     _check(x, "persistent scan dk=%d dv=%d" % (dk, dv))
+
+
+# Chunks of at most 32 tokens (short sequences, short last chunks) share one 64-row pass of the
+# chunk kernel two by two in chunk order, across sequence boundaries; with an odd count the
+# last one runs alone.  Deep gates send every pass to the exact variant, which redoes each
+# chunk of a pair on its own; three chunk workgroups walk many passes each.
+@pytest.mark.parametrize("gate_kind", ["base", "mid", "deep"])
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 128, 128), ("f32", 128, 128), ("bf16", 64, 128),
+                                         ("f32", 128, 64)])
+def test_paired_short_chunks(dtype, dk, dv, gate_kind, monkeypatch):
+    monkeypatch.setenv("KDA_CHUNK_WGS", "3")
+    rng = np.random.default_rng(dk + 7 * dv)
+    lens = [32, 1, 33, 96, 0, 31, 2, 200] + [int(v) for v in rng.integers(1, 33, size=20)] + [64, 17]
+    tails = [L - 64 * ((L - 1) // 64) for L in lens if L > 0]
+    n_short = sum(1 for t in tails if t <= 32)
+    if n_short % 2 == 0:
+        lens.append(5)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    x = make_inputs(1, int(cu[-1]), 3, dk, dv, seed=dk + dv, dtype=dtype, cu_seqlens=cu,
+                    gate=gate_kind)
+    o, h, ro, rh = _check(x, "paired short chunks %s dk=%d dv=%d gate=%s" % (dtype, dk, dv, gate_kind))
+    for n, L in enumerate(lens):
+        if L == 0:
+            np.testing.assert_array_equal(h[n], x.h0[n])
