@@ -146,6 +146,14 @@ int long_chunks() {
   return p;
 }
 
+// KDA_LONG_SLICE=32|64: value columns of a long task of the persistent scan (tuning and
+// tests); unset or anything else: the scan chooses.
+int long_width() {
+  const char* env = std::getenv("KDA_LONG_SLICE");
+  const int v = env ? std::atoi(env) : 0;
+  return v == 32 || v == 64 ? v : 0;
+}
+
 // Workgroups of the persistent chunk kernel: one per compute unit, or fewer when
 // KDA_CHUNK_WGS=n (n >= 1) asks for it (tuning, and tests of long per-workgroup walks).
 int chunk_workgroups() {
@@ -332,6 +340,7 @@ static kda_status_t forward(const kda_problem_t* prob, const void* q, const void
   p.chunk_wgs = chunk_workgroups();
   p.task_scan = task_scan_workgroups(packed);
   p.long_chunks = long_chunks();
+  p.long_width = long_width();
   for (int i = 0; i < 4; ++i) p.marks[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
   hipError_t e = kda::launch_forward(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;

@@ -87,6 +87,15 @@ __device__ inline void store4(uint16_t* p, const float* x) {
 __device__ inline void store4(float* p, const float* x) {
   *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
 }
+// The same, as streaming stores (outputs that no kernel of the call reads again)
+__device__ inline void store4_nt(uint16_t* p, const float* x) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 r = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+  __builtin_nontemporal_store(r, reinterpret_cast<u32x2*>(p));
+}
+__device__ inline void store4_nt(float* p, const float* x) {
+  __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(p));
+}
 __device__ inline void store1(uint16_t* p, float x) { *p = (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu); }
 __device__ inline void store1(float* p, float x) { *p = x; }
 
@@ -149,28 +158,39 @@ struct Rec {
   static constexpr size_t BYTES = (HDR + 16 + 255) / 256 * 256;
 };
 
-// Raw buffer resources (record stores and loads of the fused kernel): dword 3 with a 32-bit
-// data format, byte offsets, no swizzle; accesses past num_records are dropped.
+// The parts of a record that hold data for a chunk of `rows` valid tokens.  Tokens past the
+// chunk's end would give zero rows of W, Qhat exp(G), U and Aqk and zero token columns of
+// K~^T and Aqk, so those parts are neither stored nor loaded: a load of a missing part
+// returns zeros.  Row block b (tokens 16 b .. 16 b + 15) of W, Qhat exp(G), U and Aqk;
+// token half s2 (32 s2 .. 32 s2 + 31: pi stays inside a 32-wide step) of K~^T and Aqk; the
+// per-channel and header words of any chunk.  rows = 0 (a load past the end of a walk, never
+// used) fetches nothing.
+__device__ __forceinline__ bool rec_rows_present(int rows, int b) { return 16 * b < rows; }
+__device__ __forceinline__ bool rec_half_present(int rows, int s2) { return 32 * s2 < rows; }
+
+// Raw buffer resources (record stores and loads): dword 3 with a 32-bit data format, byte
+// offsets, no swizzle; accesses past num_records are dropped (loads return zeros).  A missing
+// part of a record is accessed through a resource with num_records = 0, so the instruction
+// stream (and the memory-counter waits the compiler derives from it) is the same for every
+// chunk length.
 constexpr int kBufferFlags = 0x00020000;
 typedef uint32_t uint4_v __attribute__((ext_vector_type(4)));
 typedef uint32_t uint2_v __attribute__((ext_vector_type(2)));
 
-// Record loads.  COHERENT (the scan role of the fused kernel): device-scope (sc1) buffer
-// loads, which see records that another compute die wrote through; otherwise plain loads.
+// Record loads of `bytes` (the record's size, or 0 for a missing part).  COHERENT (the scan
+// role of the fused kernel): device-scope (sc1) loads, which see records that another compute
+// die wrote through; otherwise plain loads.
 template <typename V, bool COHERENT>
 __device__ __forceinline__ V rec_load(const uint8_t* rec, int bytes, size_t off) {
-  if constexpr (COHERENT) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(rec), 0, bytes, kBufferFlags);
-    if constexpr (sizeof(V) == 16) {
-      return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 16));
-    } else if constexpr (sizeof(V) == 8) {
-      return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, 16));
-    } else {
-      static_assert(sizeof(V) == 4, "record loads are 4, 8 or 16 bytes");
-      return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, 16));
-    }
+  constexpr int aux = COHERENT ? 16 : 0;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(rec), 0, bytes, kBufferFlags);
+  if constexpr (sizeof(V) == 16) {
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, aux));
+  } else if constexpr (sizeof(V) == 8) {
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, aux));
   } else {
-    return *reinterpret_cast<const V*>(rec + off);
+    static_assert(sizeof(V) == 4, "record loads are 4, 8 or 16 bytes");
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, aux));
   }
 }
 

@@ -143,6 +143,7 @@ static hipError_t launch_scan_tasks(const ForwardPlan& p, hipStream_t stream) {
   ta.queue = p.info + 8;
   ta.n_long = p.info + 2;
   ta.rank_desc = reinterpret_cast<const int4*>(p.rank_desc);
+  ta.long_width = p.long_width == NVL || p.long_width == NVW ? p.long_width : 0;
   const size_t smem = scan_tasks_smem<DK, DV, NVL, NVW>();
   auto kern = state_scan_tasks_kernel<DK, DV, NVL, NVW, OutT>;
   hipError_t ea = allow_smem(kern, smem);

@@ -41,6 +41,7 @@ struct ForwardPlan {
   int32_t slice;  // value columns per scan workgroup (16, 32 or 64)
   int32_t task_scan;    // packed: > 0 runs the persistent state scan on this many workgroups
   int32_t long_chunks;  // packed: sequences of at least this many chunks form the long class (power of two; 0: none)
+  int32_t long_width;   // packed: value columns of a long task (32 or 64; 0: chosen by the scan)
   int32_t chunk_wgs;  // workgroups of the persistent chunk kernel (>= 1)
   hipEvent_t marks[4];  // optional timing marks around the kernels (may be null)
 };

@@ -311,24 +311,33 @@ __device__ __forceinline__ void subst_rows(float (&x)[4], const float (&am)[16])
   if constexpr (J + 1 < 15) subst_rows<J + 1>(x, am);
 }
 
-// Record stores.  WT (the fused kernel): device-scope stores (sc1), which write through
-// the L2 of the compute die, so that once they complete the record is visible to the scan
-// workgroups on every die; otherwise plain stores, kept in L2 for the scan kernel.
+// Record stores.  `present` = false: a part of the record that the chunk's length leaves
+// empty (rec_rows_present), dropped by the buffer's range check: no bytes are written and
+// the instruction stream is the same for every length.  WT (the fused kernel): device-scope
+// stores (sc1), which write through the L2 of the compute die, so that once they complete the
+// record is visible to the scan workgroups on every die; otherwise plain stores, kept in L2
+// for the scan kernel.
 template <bool WT, int BYTES, typename V>
-__device__ __forceinline__ void rec_store(uint8_t* rec, size_t off, const V& v) {
-  if constexpr (WT) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(rec, 0, BYTES, kBufferFlags);
-    if constexpr (sizeof(V) == 16) {
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4_v, v), rs, (int)off, 0, 16);
-    } else if constexpr (sizeof(V) == 8) {
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2_v, v), rs, (int)off, 0, 16);
-    } else {
-      static_assert(sizeof(V) == 4, "record stores are 4, 8 or 16 bytes");
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, (int)off, 0, 16);
-    }
+__device__ __forceinline__ void rec_store(uint8_t* rec, size_t off, const V& v, bool present = true) {
+  constexpr int aux = WT ? 16 : 0;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(rec, 0, present ? BYTES : 0, kBufferFlags);
+  if constexpr (sizeof(V) == 16) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4_v, v), rs, (int)off, 0, aux);
+  } else if constexpr (sizeof(V) == 8) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2_v, v), rs, (int)off, 0, aux);
   } else {
-    *reinterpret_cast<V*>(rec + off) = v;
+    static_assert(sizeof(V) == 4, "record stores are 4, 8 or 16 bytes");
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, (int)off, 0, aux);
   }
+}
+
+// Valid tokens of chunk c (1..64; fewer only in a sequence's last chunk).  Chunk numbers
+// fit 31 bits (items are counted in int).
+__device__ __forceinline__ int chunk_rows(const PrepArgs& a, int c) {
+  if (a.cu) return (int)sload_u32(reinterpret_cast<const int32_t*>(a.table + c) + 1);
+  const int nc = (int)a.nc, idx = c - (c / nc) * nc;
+  const int64_t rem = a.T - (int64_t)idx * kChunk;
+  return rem < kChunk ? (int)rem : kChunk;
 }
 
 // One (chunk, head) from its fp32 inputs.  EXACT = false: guarded fp32 diagonal tiles,
@@ -392,6 +401,8 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   uint8_t* rec2 = paired ? a.rec + ((size_t)chunk2 * a.H + h) * R::BYTES : rec;
   uint8_t* recw = hi_half ? rec2 : rec;            // this wave's record
   const int wr = hi_half ? w - 2 : w;              // this wave's row block there
+  // valid tokens of this wave's chunk: the parts of its record past them are not stored
+  const int rows_w = chunk_rows(a, hi_half ? chunk2 : chunk);
 
   // reads the lane's NE channels (of this half) of row `row` of a [*][DK] fp32 array in LDS
   auto lane_row = [&](const float* base, int row, float* out) {
@@ -622,8 +633,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
         bwr[sl][e] = (_Float16)(bt * XB[8 * sl + e] * eS[e]); // beta khat exp(G)
         y[e] = (_Float16)YC[8 * sl + e];
       }
-      rec_store<WT, R::BYTES>(recw, R::Q + ((size_t)(wr * KSK + s) * 64 + l) * 16, qf);
-      if (paired) rec_store<WT, R::BYTES>(recw, R::Q + ((size_t)((wr + 2) * KSK + s) * 64 + l) * 16, f16x8{});
+      rec_store<WT, R::BYTES>(recw, R::Q + ((size_t)(wr * KSK + s) * 64 + l) * 16, qf, rec_rows_present(rows_w, wr));
       // K~^T fragments: (K~ I) holds, per lane, key channel 16 ct + t at tokens 16 w + 4 gq + r,
       // ct = 2 s + hh.  The 16-byte record fragment of (ct, token pair w / 2) joins the halves of
       // token blocks 2 (w / 2) and 2 (w / 2) + 1: both go to LDS here, and after barrier #4 each
@@ -669,9 +679,9 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
     const f16x4 lo = ktx[((((hf * 2 + (w >> 1)) * 2 + 0) * (2 * KH) + j) * 64) + l];
     const f16x4 hi = ktx[((((hf * 2 + (w >> 1)) * 2 + 1) * (2 * KH) + j) * 64) + l];
     const f16x8 frag = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    // (a pair: token half w / 2 is a whole chunk, its record's first half; the second is zero)
-    rec_store<WT, R::BYTES>(recw, R::KT + ((size_t)(ct * 2 + (paired ? 0 : (w >> 1))) * 64 + l) * 16, frag);
-    if (paired) rec_store<WT, R::BYTES>(recw, R::KT + ((size_t)(ct * 2 + 1) * 64 + l) * 16, f16x8{});
+    // (a pair: token half w / 2 is a whole chunk, its record's first half)
+    const int s2k = paired ? 0 : (w >> 1);
+    rec_store<WT, R::BYTES>(recw, R::KT + ((size_t)(ct * 2 + s2k) * 64 + l) * 16, frag, rec_half_present(rows_w, s2k));
   }
 
   // ---------------- (b) Gram matrices L (row block w) and Aqk^T (column block w) ----------------
@@ -894,8 +904,10 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
         f[r] = (_Float16)full[2 * s2][r];
         f[4 + r] = (_Float16)full[2 * s2 + 1][r];
       }
-      // a pair's second chunk: its columns are the second half (s2 = 1), the first is zero
-      rec_store<WT, R::BYTES>(recw, R::A + ((size_t)(wr * 2 + (hi_half ? s2 ^ 1 : s2)) * 64 + l) * 16, f);
+      // a pair's second chunk: its columns are the pass's second half (s2 = 1), its record's first
+      const int s2r = hi_half ? s2 ^ 1 : s2;
+      rec_store<WT, R::BYTES>(recw, R::A + ((size_t)(wr * 2 + s2r) * 64 + l) * 16, f,
+                              rec_rows_present(rows_w, wr) && rec_half_present(rows_w, s2r));
     }
   }
   // Bw^T fragments through identity products (rows = key channels, tokens in pi order)
@@ -1016,8 +1028,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
       }
       f16x8 wf = {(_Float16)c0[0], (_Float16)c0[1], (_Float16)c0[2], (_Float16)c0[3],
                   (_Float16)c1[0], (_Float16)c1[1], (_Float16)c1[2], (_Float16)c1[3]};
-      rec_store<WT, R::BYTES>(recw, R::W + ((size_t)(wr * KSK + sk) * 64 + l) * 16, wf);
-      if (paired) rec_store<WT, R::BYTES>(recw, R::W + ((size_t)((wr + 2) * KSK + sk) * 64 + l) * 16, f16x8{});
+      rec_store<WT, R::BYTES>(recw, R::W + ((size_t)(wr * KSK + sk) * 64 + l) * 16, wf, rec_rows_present(rows_w, wr));
     }
 #pragma unroll
     for (int ntl = 0; ntl < NTV / 2; ++ntl) {
@@ -1029,8 +1040,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
         c = mfma16(tf[s], bfr, c);
       }
       f16x4 uf = {(_Float16)c[0], (_Float16)c[1], (_Float16)c[2], (_Float16)c[3]};
-      rec_store<WT, R::BYTES>(recw, R::U + ((size_t)(wr * NTV + nt) * 64 + l) * 8, uf);
-      if (paired) rec_store<WT, R::BYTES>(recw, R::U + ((size_t)((wr + 2) * NTV + nt) * 64 + l) * 8, f16x4{});
+      rec_store<WT, R::BYTES>(recw, R::U + ((size_t)(wr * NTV + nt) * 64 + l) * 8, uf, rec_rows_present(rows_w, wr));
     }
   }
 }

@@ -110,50 +110,56 @@ struct KeyRegs {
 // step, so that the eight waves never queue all of them on the vector-memory path at
 // once.  Token waves: 0 = W, 1 = Qhat*exp(G), 2 = Aqk, U and ue (or 3 = U and ue, 4 = Aqk,
 // for a walk that reuses its slot and so requests each factor after its last use).  Key
-// waves: 0 = K~^T, 1 = exp(G_last).
+// waves: 0 = K~^T, 1 = exp(G_last).  `rows`: the chunk's valid tokens (0 past a walk's
+// end); the parts of the record past them are not fetched and read as zeros.
 template <int PART, int DK, int DV, int NV, bool FUSED = false>
-__device__ __forceinline__ void load_tok(TokRegs<DK, NV>& c, const uint8_t* rec, int i, int l, int slice) {
+__device__ __forceinline__ void load_tok(TokRegs<DK, NV>& c, const uint8_t* rec, int rows, int i, int l, int slice) {
   using R = Rec<DK, DV>;
   using TR = TokRegs<DK, NV>;
+  const int nb = rec_rows_present(rows, i) ? (int)R::BYTES : 0;  // row block i
   if (PART == 0) {
 #pragma unroll
     for (int s = 0; s < TR::KSK; ++s)
-      c.wf[s] = rec_load<f16x8, FUSED>(rec, R::BYTES, R::W + ((size_t)(i * TR::KSK + s) * 64 + l) * 16);
+      c.wf[s] = rec_load<f16x8, FUSED>(rec, nb, R::W + ((size_t)(i * TR::KSK + s) * 64 + l) * 16);
   } else if (PART == 1) {
 #pragma unroll
     for (int s = 0; s < TR::KSK; ++s)
-      c.qf[s] = rec_load<f16x8, FUSED>(rec, R::BYTES, R::Q + ((size_t)(i * TR::KSK + s) * 64 + l) * 16);
+      c.qf[s] = rec_load<f16x8, FUSED>(rec, nb, R::Q + ((size_t)(i * TR::KSK + s) * 64 + l) * 16);
   } else {
     if (PART == 2 || PART == 4) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
-        c.af[s2] = rec_load<f16x8, FUSED>(rec, R::BYTES, R::A + ((size_t)(i * 2 + s2) * 64 + l) * 16);
+        c.af[s2] = rec_load<f16x8, FUSED>(rec, rec_half_present(rows, s2) ? nb : 0,
+                                          R::A + ((size_t)(i * 2 + s2) * 64 + l) * 16);
     }
     if (PART == 2 || PART == 3) {
+      const int nh = rows > 0 ? (int)R::BYTES : 0;
 #pragma unroll
       for (int nt = 0; nt < TR::NT; ++nt)
-        c.uf[nt] = rec_load<f16x4, FUSED>(rec, R::BYTES, R::U + ((size_t)(i * R::NTV + slice * TR::NT + nt) * 64 + l) * 8);
-      c.ue = rec_load<int32_t, FUSED>(rec, R::BYTES, R::HDR + 4);
-      if (FUSED) c.vmax = rec_load<float, true>(rec, R::BYTES, R::HDR);
+        c.uf[nt] = rec_load<f16x4, FUSED>(rec, nb, R::U + ((size_t)(i * R::NTV + slice * TR::NT + nt) * 64 + l) * 8);
+      c.ue = rec_load<int32_t, FUSED>(rec, nh, R::HDR + 4);
+      if (FUSED) c.vmax = rec_load<float, true>(rec, nh, R::HDR);
     }
   }
 }
 
 template <int PART, int DK, int DV, bool FUSED = false>
-__device__ __forceinline__ void load_key(KeyRegs<DK>& c, const uint8_t* rec, int m, int l) {
+__device__ __forceinline__ void load_key(KeyRegs<DK>& c, const uint8_t* rec, int rows, int m, int l) {
   using R = Rec<DK, DV>;
   using KR = KeyRegs<DK>;
   const int gq = l >> 4;
-  if (FUSED && PART == 0) c.vmax = rec_load<float, true>(rec, R::BYTES, R::HDR);
+  const int nh = rows > 0 ? (int)R::BYTES : 0;
+  if (FUSED && PART == 0) c.vmax = rec_load<float, true>(rec, nh, R::HDR);
 #pragma unroll
   for (int p = 0; p < KR::TPK; ++p) {
     const int ct = KR::TPK * m + p;
     if (PART == 0) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
-        c.kt[p][s2] = rec_load<f16x8, FUSED>(rec, R::BYTES, R::KT + ((size_t)(ct * 2 + s2) * 64 + l) * 16);
+        c.kt[p][s2] = rec_load<f16x8, FUSED>(rec, rec_half_present(rows, s2) ? (int)R::BYTES : 0,
+                                             R::KT + ((size_t)(ct * 2 + s2) * 64 + l) * 16);
     } else {
-      const uint2_v le = rec_load<uint2_v, FUSED>(rec, R::BYTES, R::LAM + (size_t)(16 * ct + 4 * gq + (l & 3)) * 8);
+      const uint2_v le = rec_load<uint2_v, FUSED>(rec, nh, R::LAM + (size_t)(16 * ct + 4 * gq + (l & 3)) * 8);
       c.lam[p] = __uint_as_float(le[0]);
       c.ec[p] = (int)le[1];
     }
@@ -332,16 +338,21 @@ __device__ __forceinline__ void scan_walk(const ScanArgs& a, const FuseArgs& fz,
     const int64_t cc = c < c1 ? c : c1 - 1;  // past the end: the last chunk again (loaded, never used)
     return a.rec + ((size_t)cc * a.H + h) * R::BYTES;
   };
+  // valid tokens of chunk c (only a sequence's last chunk has fewer than 64); 0 past the end
+  auto rows_of = [&](int64_t c) {
+    const int64_t rem = L - (c - c0) * kChunk;
+    return c >= c1 ? 0 : (rem < kChunk ? (int)rem : kChunk);
+  };
 
   if (tok_wave) {
     // ---- token block i: Delta rows, then the output rows ----
-    auto step = [&](const TR& cur, TR& nxt, const uint8_t* nrec, int64_t c) {
+    auto step = [&](const TR& cur, TR& nxt, const uint8_t* nrec, int nrows, int64_t c) {
       if (FUSED) {
         es = es_at(c, cur.vmax);
         await_chunk(c + kScanDepth - 1);
         prepoll(c + kScanDepth);
       }
-      load_tok<0, DK, DV, NV, FUSED>(nxt, nrec, i, l, slice);
+      load_tok<0, DK, DV, NV, FUSED>(nxt, nrec, nrows, i, l, slice);
       const f16x8* sb = reinterpret_cast<const f16x8*>(sbb + (size_t)((c - c0) & 1) * SM::SBUF);
       // all S0 fragments at once, so that the MFMA chains below never wait on LDS one by one
       f16x8 sf[KSK][NT];
@@ -364,7 +375,7 @@ __device__ __forceinline__ void scan_walk(const ScanArgs& a, const FuseArgs& fz,
         for (int r = 0; r < 4; ++r) df[r] = (_Float16)(ldexpf((float)cur.uf[nt][r], es - cur.ue) - d[nt][r]);
         *reinterpret_cast<f16x4*>(db + (((size_t)(i >> 1) * NT + nt) * 64 + l) * 16 + (i & 1) * 8) = df;
       }
-      load_tok<1, DK, DV, NV, FUSED>(nxt, nrec, i, l, slice);
+      load_tok<1, DK, DV, NV, FUSED>(nxt, nrec, nrows, i, l, slice);
       // o^T, inter-chunk part: S0^T (Qhat exp(G))^T
       f32x4 o[NT];
 #pragma unroll
@@ -374,7 +385,7 @@ __device__ __forceinline__ void scan_walk(const ScanArgs& a, const FuseArgs& fz,
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) o[nt] = mfma16(sf[s][nt], cur.qf[s], o[nt]);
       __syncthreads();  // A: Delta complete
-      load_tok<2, DK, DV, NV, FUSED>(nxt, nrec, i, l, slice);
+      load_tok<2, DK, DV, NV, FUSED>(nxt, nrec, nrows, i, l, slice);
       // o^T, intra-chunk part: Delta^T Aqk^T; then 4 consecutive value columns per lane
       f16x8 dfr[2][NT];
 #pragma unroll
@@ -410,9 +421,9 @@ __device__ __forceinline__ void scan_walk(const ScanArgs& a, const FuseArgs& fz,
 #pragma unroll
       for (int j = 0; j < kScanDepth - 1; ++j) {
         await_chunk(c0 + j);
-        load_tok<0, DK, DV, NV, FUSED>(buf[j], rec_of(c0 + j), i, l, slice);
-        load_tok<1, DK, DV, NV, FUSED>(buf[j], rec_of(c0 + j), i, l, slice);
-        load_tok<2, DK, DV, NV, FUSED>(buf[j], rec_of(c0 + j), i, l, slice);
+        load_tok<0, DK, DV, NV, FUSED>(buf[j], rec_of(c0 + j), rows_of(c0 + j), i, l, slice);
+        load_tok<1, DK, DV, NV, FUSED>(buf[j], rec_of(c0 + j), rows_of(c0 + j), i, l, slice);
+        load_tok<2, DK, DV, NV, FUSED>(buf[j], rec_of(c0 + j), rows_of(c0 + j), i, l, slice);
       }
       if (FUSED) __syncthreads();  // S0 of the first chunk visible
       // whole groups of kScanDepth steps (no conditional step: the compiler's memory-counter
@@ -421,20 +432,23 @@ __device__ __forceinline__ void scan_walk(const ScanArgs& a, const FuseArgs& fz,
       for (; c + kScanDepth <= c1; c += kScanDepth) {
 #pragma unroll
         for (int j = 0; j < kScanDepth; ++j)
-          step(buf[j], buf[(j + kScanDepth - 1) % kScanDepth], rec_of(c + j + kScanDepth - 1), c + j);
+          step(buf[j], buf[(j + kScanDepth - 1) % kScanDepth], rec_of(c + j + kScanDepth - 1),
+               rows_of(c + j + kScanDepth - 1), c + j);
       }
 #pragma unroll
       for (int j = 0; j < kScanDepth - 1; ++j)
-        if (c + j < c1) step(buf[j], buf[(j + kScanDepth - 1) % kScanDepth], rec_of(c + j + kScanDepth - 1), c + j);
+        if (c + j < c1)
+          step(buf[j], buf[(j + kScanDepth - 1) % kScanDepth], rec_of(c + j + kScanDepth - 1),
+               rows_of(c + j + kScanDepth - 1), c + j);
     }
   } else {
     // ---- key block i: S_next = Diag(exp(G_last)) S0 + K~^T Delta ----
-    auto step = [&](const KR& cur, KR& nxt, const uint8_t* nrec, int64_t c) {
+    auto step = [&](const KR& cur, KR& nxt, const uint8_t* nrec, int nrows, int64_t c) {
       if (FUSED) {
         await_chunk(c + kScanDepth - 1);
         prepoll(c + kScanDepth);
       }
-      load_key<0, DK, DV, FUSED>(nxt, nrec, i, l);
+      load_key<0, DK, DV, FUSED>(nxt, nrec, nrows, i, l);
       __syncthreads();  // A: Delta complete
       f16x8 dfr[2][NT];
 #pragma unroll
@@ -459,7 +473,7 @@ __device__ __forceinline__ void scan_walk(const ScanArgs& a, const FuseArgs& fz,
         }
       }
 
-      load_key<1, DK, DV, FUSED>(nxt, nrec, i, l);
+      load_key<1, DK, DV, FUSED>(nxt, nrec, nrows, i, l);
       // the next chunk's copy exponent (the same value its token waves derive)
       if (FUSED && c + 1 < c1) es = es_at(c + 1, nxt.vmax);
       write_state((int)((c - c0 + 1) & 1));
@@ -474,8 +488,8 @@ __device__ __forceinline__ void scan_walk(const ScanArgs& a, const FuseArgs& fz,
 #pragma unroll
       for (int j = 0; j < kScanDepth - 1; ++j) {
         await_chunk(c0 + j);
-        load_key<0, DK, DV, FUSED>(buf[j], rec_of(c0 + j), i, l);
-        load_key<1, DK, DV, FUSED>(buf[j], rec_of(c0 + j), i, l);
+        load_key<0, DK, DV, FUSED>(buf[j], rec_of(c0 + j), rows_of(c0 + j), i, l);
+        load_key<1, DK, DV, FUSED>(buf[j], rec_of(c0 + j), rows_of(c0 + j), i, l);
       }
       if (FUSED) {
         es = es_at(c0, buf[0].vmax);
@@ -486,11 +500,14 @@ __device__ __forceinline__ void scan_walk(const ScanArgs& a, const FuseArgs& fz,
       for (; c + kScanDepth <= c1; c += kScanDepth) {
 #pragma unroll
         for (int j = 0; j < kScanDepth; ++j)
-          step(buf[j], buf[(j + kScanDepth - 1) % kScanDepth], rec_of(c + j + kScanDepth - 1), c + j);
+          step(buf[j], buf[(j + kScanDepth - 1) % kScanDepth], rec_of(c + j + kScanDepth - 1),
+               rows_of(c + j + kScanDepth - 1), c + j);
       }
 #pragma unroll
       for (int j = 0; j < kScanDepth - 1; ++j)
-        if (c + j < c1) step(buf[j], buf[(j + kScanDepth - 1) % kScanDepth], rec_of(c + j + kScanDepth - 1), c + j);
+        if (c + j < c1)
+          step(buf[j], buf[(j + kScanDepth - 1) % kScanDepth], rec_of(c + j + kScanDepth - 1),
+               rows_of(c + j + kScanDepth - 1), c + j);
     }
     if (a.ht) {
       // (fused) a token wave's wait gave up: the final state is not valid (every wave is past

@@ -46,6 +46,7 @@ struct TaskArgs {
   int32_t* queue;          // kQueueSlots counters, zeroed by the chunk map before the launch
   const int32_t* n_long;   // sequences of at least long_chunks chunks (the first ones of seq_order)
   const int4* rank_desc;   // per rank of seq_order: {sequence, first chunk, first token, length}
+  int32_t long_width;      // value columns of a long task: NVL, NVW, or 0 (chosen here)
 };
 
 // Task u of queue x among the (sequence, head) pairs [p_lo, p_hi) with p = x (mod nq),
@@ -157,19 +158,21 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
     return reinterpret_cast<const float*>(a.rec + ((size_t)c * a.H + h) * R::BYTES + R::HDR);
   };
   // record of virtual chunk v of the stream "this task's chunks, then the next task's"
-  auto vrec = [&](int64_t v, const ScanTask& k, const ScanTask& nx, bool nx_ok, int& sl) __attribute__((always_inline)) {
-    int64_t c;
+  auto vrec = [&](int64_t v, const ScanTask& k, const ScanTask& nx, bool nx_ok, int& sl, int& rows)
+                  __attribute__((always_inline)) {
+    int64_t c, rem;
     int hh;
     const int64_t nk = k.c1 - k.c0;
     if (v < nk) {
-      c = k.c0 + v; hh = k.h; sl = k.slice;
+      c = k.c0 + v; rem = k.L - v * kChunk; hh = k.h; sl = k.slice;
     } else if (nx_ok) {
-      const int64_t w = v - nk, nn = nx.c1 - nx.c0;
-      c = nx.c0 + (w < nn ? w : nn - 1); hh = nx.h; sl = nx.slice;
+      const int64_t w = v - nk, nn = nx.c1 - nx.c0, j = w < nn ? w : nn - 1;
+      c = nx.c0 + j; rem = nx.L - j * kChunk; hh = nx.h; sl = nx.slice;
     } else {
-      c = k.c1 - 1; hh = k.h; sl = k.slice;  // past the end: loaded, never used
+      c = k.c1 - 1; rem = 0; hh = k.h; sl = k.slice;  // past the end: nothing is fetched
     }
     if (c < 0) c = 0;
+    rows = rem <= 0 ? 0 : (rem < kChunk ? (int)rem : kChunk);
     return a.rec + ((size_t)c * a.H + hh) * R::BYTES;
   };
 
@@ -250,11 +253,11 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
       after_barrier0(cur, nxt, es);
       const int64_t nk = cur.c1 - cur.c0;
       if (!ring_ok && nk > 0) {
-        int sl;
-        const uint8_t* r0 = vrec(0, cur, nxt, false, sl);
-        load_tok<0, DK, DV, NV>(tb[0], r0, i, l, sl);
-        load_tok<1, DK, DV, NV>(tb[0], r0, i, l, sl);
-        load_tok<2, DK, DV, NV>(tb[0], r0, i, l, sl);
+        int sl, nr;
+        const uint8_t* r0 = vrec(0, cur, nxt, false, sl, nr);
+        load_tok<0, DK, DV, NV>(tb[0], r0, nr, i, l, sl);
+        load_tok<1, DK, DV, NV>(tb[0], r0, nr, i, l, sl);
+        load_tok<2, DK, DV, NV>(tb[0], r0, nr, i, l, sl);
       }
       __syncthreads();  // 1
       const bool nx_pre = nxt.ok && nxt.c1 > nxt.c0;  // the ring may run on into the next task
@@ -262,10 +265,10 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
 
       // Delta for both halves before barrier A (the key waves wait for it); the output rows
       // after it, half by half (S0 stays in its buffer until the step after)
-      auto step = [&](const TR& c_, TR& n_, const uint8_t* nrec, int nsl, int64_t k, auto same, auto first)
+      auto step = [&](const TR& c_, TR& n_, const uint8_t* nrec, int nsl, int nr, int64_t k, auto same, auto first)
                       __attribute__((always_inline)) {
         constexpr bool SAME = decltype(same)::value != 0;
-        if (!SAME) load_tok<0, DK, DV, NV>(n_, nrec, i, l, nsl);
+        if (!SAME) load_tok<0, DK, DV, NV>(n_, nrec, nr, i, l, nsl);
         const f16x8* sb = reinterpret_cast<const f16x8*>(sbb + (size_t)(k & 1) * SM::SBUF);
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
@@ -293,13 +296,13 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
         // the descriptor of the id held in reserve (its request has returned by now)
         if (decltype(first)::value && tid == 0) pend_desc = fetch_desc(pending);
         if (SAME) {
-          load_tok<0, DK, DV, NV>(n_, nrec, i, l, nsl);  // W, U and ue are spent
-          load_tok<3, DK, DV, NV>(n_, nrec, i, l, nsl);
+          load_tok<0, DK, DV, NV>(n_, nrec, nr, i, l, nsl);  // W, U and ue are spent
+          load_tok<3, DK, DV, NV>(n_, nrec, nr, i, l, nsl);
         } else {
-          load_tok<1, DK, DV, NV>(n_, nrec, i, l, nsl);
+          load_tok<1, DK, DV, NV>(n_, nrec, nr, i, l, nsl);
         }
         __syncthreads();  // A: Delta complete
-        if (!SAME) load_tok<2, DK, DV, NV>(n_, nrec, i, l, nsl);
+        if (!SAME) load_tok<2, DK, DV, NV>(n_, nrec, nr, i, l, nsl);
         const int64_t rem = cur.L - k * kChunk;
         const int len = rem < kChunk ? (int)rem : kChunk;
         const int i_loc = 16 * i + t;
@@ -336,13 +339,13 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
               float v4[4];
 #pragma unroll
               for (int r = 0; r < 4; ++r) v4[r] = ldexpf(o[nt][r], -es) * oscale;
-              store4(out + ((size_t)tok * a.H + cur.h) * DV + 64 * hh + 16 * nt + 4 * gq, v4);
+              store4_nt(out + ((size_t)tok * a.H + cur.h) * DV + 64 * hh + 16 * nt + 4 * gq, v4);
             }
           }
         }
         if (SAME) {
-          load_tok<1, DK, DV, NV>(n_, nrec, i, l, nsl);
-          load_tok<4, DK, DV, NV>(n_, nrec, i, l, nsl);
+          load_tok<1, DK, DV, NV>(n_, nrec, nr, i, l, nsl);
+          load_tok<4, DK, DV, NV>(n_, nrec, nr, i, l, nsl);
         }
         __syncthreads();  // B: next S0 complete
       };
@@ -351,9 +354,9 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
       // the first step on its own: a loop's memory-counter waits are set for its later
       // iterations and would make this one wait for the prefetches issued just before it
       auto walk_step = [&](int64_t k, auto first) __attribute__((always_inline)) {
-        int sl;
-        const uint8_t* n1 = vrec(k + 1, cur, nxt, nx_pre, sl);
-        step(tb[0], tb[0], n1, sl, k, IntC<1>{}, first);
+        int sl, nr;
+        const uint8_t* n1 = vrec(k + 1, cur, nxt, nx_pre, sl, nr);
+        step(tb[0], tb[0], n1, sl, nr, k, IntC<1>{}, first);
       };
       if (nk > 0) walk_step(0, IntC<1>{});
       else if (tid == 0) pend_desc = fetch_desc(pending);
@@ -389,7 +392,10 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
       if (a.h0) {
         const float* src = a.h0 + ((size_t)k.n * a.H + k.h) * DK * DV + (size_t)RW * i * DV + 4 * l;
 #pragma unroll
-        for (int j = 0; j < PCS; ++j) Sv[j] = *reinterpret_cast<const float4*>(src + 256 * j);
+        for (int j = 0; j < PCS; ++j) {
+          const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + 256 * j));
+          Sv[j] = make_float4(v[0], v[1], v[2], v[3]);
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < PCS; ++j) Sv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -415,7 +421,8 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
       float* dst = a.ht + ((size_t)k.n * a.H + k.h) * DK * DV + (size_t)RW * i * DV + 4 * l;
 #pragma unroll
       for (int j = 0; j < PCS; ++j)
-        *reinterpret_cast<float4*>(dst + 256 * j) = *reinterpret_cast<const float4*>(stage_l + RPJ * SP * j);
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(stage_l + RPJ * SP * j),
+                                    reinterpret_cast<f32x4*>(dst + 256 * j));
     };
     for (;;) {
       if (!have_pre) load_state(cur);
@@ -437,10 +444,10 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
       after_barrier0(cur, nxt, es);
       const int64_t nk = cur.c1 - cur.c0;
       if (!ring_ok && nk > 0) {
-        int sl;
-        const uint8_t* r0 = vrec(0, cur, nxt, false, sl);
-        load_key<0, DK, DV>(kb[0], r0, i, l);
-        load_key<1, DK, DV>(kb[0], r0, i, l);
+        int sl, nr;
+        const uint8_t* r0 = vrec(0, cur, nxt, false, sl, nr);
+        load_key<0, DK, DV>(kb[0], r0, nr, i, l);
+        load_key<1, DK, DV>(kb[0], r0, nr, i, l);
       }
       auto write_state = [&](int buf) __attribute__((always_inline)) {
         uint8_t* sb = sbb + (size_t)buf * SM::SBUF;
@@ -461,9 +468,10 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
       const bool nx_pre = nxt.ok && nxt.c1 > nxt.c0;
       if (nxt.ok) load_state(nxt);  // under this task's steps
 
-      auto step = [&](const KR& c_, KR& n_, const uint8_t* nrec, int64_t k, auto same) __attribute__((always_inline)) {
+      auto step = [&](const KR& c_, KR& n_, const uint8_t* nrec, int nr, int64_t k, auto same)
+                      __attribute__((always_inline)) {
         constexpr bool SAME = decltype(same)::value != 0;
-        if (!SAME) load_key<0, DK, DV>(n_, nrec, i, l);
+        if (!SAME) load_key<0, DK, DV>(n_, nrec, nr, i, l);
         __syncthreads();  // A: Delta complete
 
         float lam[TPK][4];
@@ -496,14 +504,15 @@ __device__ __forceinline__ void scan_short_tasks(const ScanArgs& a, const QueueC
                 S[p][4 * hh + nt][r] = fmaf(lam[p][r], S[p][4 * hh + nt][r], ldexpf(u[r], ue4[p][r]));
             }
         }
-        if (SAME) load_key<0, DK, DV>(n_, nrec, i, l);
-        load_key<1, DK, DV>(n_, nrec, i, l);
+        if (SAME) load_key<0, DK, DV>(n_, nrec, nr, i, l);
+        load_key<1, DK, DV>(n_, nrec, nr, i, l);
         write_state((int)((k + 1) & 1));
         __syncthreads();  // B: next S0 complete
       };
       auto walk_step = [&](int64_t k) __attribute__((always_inline)) {
-        int sl;
-        step(kb[0], kb[0], vrec(k + 1, cur, nxt, nx_pre, sl), k, IntC<1>{});
+        int sl, nr;
+        const uint8_t* n1 = vrec(k + 1, cur, nxt, nx_pre, sl, nr);
+        step(kb[0], kb[0], n1, nr, k, IntC<1>{});
       };
       if (nk > 0) walk_step(0);  // on its own, as in the token role
       for (int64_t k = 1; k < nk; ++k) walk_step(k);
@@ -542,7 +551,7 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_tasks_kernel(ScanArgs
   // narrow slices for the long class only when its chains on wide slices would leave
   // compute units without a task
   const int lp = *ta.n_long * (int)a.H;
-  const bool narrow = (int64_t)lp * (DV / NVW) < (int64_t)gridDim.x;
+  const bool narrow = ta.long_width ? ta.long_width == NVL : (int64_t)lp * (DV / NVW) < (int64_t)gridDim.x;
   q.long_pairs = lp;
   q.long_slices = narrow ? DV / NVL : DV / NVW;
   const int lcnt = lp > q.x ? (lp - q.x + q.nq - 1) / q.nq : 0;

@@ -334,8 +334,9 @@ def test_validate_cu_seqlens_rejects_bad_offsets(bad, monkeypatch):
 @pytest.mark.parametrize("env", [{}, {"KDA_LONG_CHUNKS": "1"}, {"KDA_LONG_CHUNKS": "0"},
                                  {"KDA_LONG_CHUNKS": "1024"}, {"KDA_TASK_SCAN": "3"},
                                  {"KDA_TASK_SCAN": "8"}, {"KDA_TASK_SCAN": "13", "KDA_LONG_CHUNKS": "2"},
-                                 {"KDA_TASK_SCAN": "0"}],
-                         ids=["default", "all-long", "no-long", "all-short", "3wg", "8wg", "13wg-long2", "off"])
+                                 {"KDA_TASK_SCAN": "0"}, {"KDA_LONG_SLICE": "64"}, {"KDA_LONG_SLICE": "32", "KDA_LONG_CHUNKS": "2"}],
+                         ids=["default", "all-long", "no-long", "all-short", "3wg", "8wg", "13wg-long2", "off", "long-wide",
+                              "long-narrow"])
 def test_persistent_scan_task_classes(env, monkeypatch):
     for k, v in env.items():
         monkeypatch.setenv(k, v)
@@ -380,3 +381,29 @@ def test_paired_short_chunks(dtype, dk, dv, gate_kind, monkeypatch):
     for n, L in enumerate(lens):
         if L == 0:
             np.testing.assert_array_equal(h[n], x.h0[n])
+
+
+# A record holds only what its chunk's tokens fill: the row blocks and token halves past a
+# chunk's end are neither stored by the chunk kernel nor loaded by the scan (a load of them
+# reads zeros).  A workspace whose every byte is 0xFF (NaN in fp16 and fp32) before the call
+# shows that nothing reads a part that was never written: partial last chunks on the fused
+# path, the two-kernel path and in packed batches, where pairs of short chunks share a pass.
+@pytest.mark.parametrize("path", ["fused", "two-kernel", "packed"])
+def test_unwritten_record_parts_are_never_read(path, monkeypatch):
+    import torch
+    import gated_delta_rule_39_amd.kda as kda
+    if path == "packed":
+        lens = [1, 17, 33, 48, 64, 100, 5, 130, 16, 32, 0, 2]
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        x = make_inputs(1, int(cu[-1]), 3, 128, 128, seed=97, dtype="bf16", cu_seqlens=cu)
+    else:
+        x = make_inputs(2, 177, 3, 128, 128, seed=98, dtype="bf16")  # last chunk: 49 tokens
+    if path == "two-kernel":
+        monkeypatch.setenv("KDA_FUSED", "0")
+    B, T, H, dk, dv = x.shape
+    n = 0 if x.cu_seqlens is None else x.num_seqs
+    wsb = kda.workspace_size(B, T, H, dk, dv, kda.KDA_BF16, n)
+    ws = torch.full((wsb,), 255, dtype=torch.uint8, device="cuda:0")
+    o, h = run_gpu(x, workspace=ws)
+    ro, rh = run_oracle(x)
+    gate(x, o, h, ro, rh, "NaN-filled workspace, %s" % path)
