@@ -15,12 +15,16 @@ the library's kernels on the stream they run on, in a second pass over the same
 steps (the headline timing has no events between the kernels).
 
 Beside the headline workload the line also carries the two 8,192-token varlen
-batches (uniform and skewed lengths), timed the same way and checked against the
-oracle, the geomean of the three, the headline workload with cold caches, a
-decode step (kda_decode) over 256 sequences with its HBM roofline, the backward
-pass, and the serial bound of the state pass (the chain-latency bound: the
-longest chain's chunks times the step latency of a lone chain); --no-extra skips
-these, for profiling runs.
+batches (uniform and skewed lengths), timed the same way (W untimed calls, then K
+timed calls) and checked against the oracle, and the geomean of the three.  Their inputs
+are drawn and uploaded before any timing and their legs run right after the
+headline one's, with their oracle checks afterwards: the GPU then runs all timed
+legs without idling while the host draws inputs or runs the oracle (an idle GPU
+drops its clock, and W = 5 calls do not bring it back).  The line further carries
+the headline workload with cold caches, a decode step (kda_decode) over 256
+sequences with its HBM roofline, the backward pass, and the serial bound of the
+state pass (the chain-latency bound: the longest chain's chunks times the step
+latency of a lone chain); --no-extra skips these, for profiling runs.
 
 The roofline of the fused kernel counts the method minimum as its algorithmic
 bytes (every input read once, the output written once, h0 and ht once); the
@@ -164,16 +168,11 @@ def kernel_source_hash(kernel):
     return h.hexdigest()
 
 
-def extra_measurements(args, lib, kda, make_config, upload, dev, torch, argv1, out1, ht1, x1):
-    """The other two 8,192-token workloads (uniform and skewed varlen batches), each timed
-    like the headline one and checked against the oracle, their geomean with the headline
-    workload, and the headline workload with cold caches (a 512 MiB buffer written before
-    every call, outside the timed call)."""
-    from oracle import oracle_fwd
-    rel = lambda a, b: float(np.linalg.norm(a.astype(np.float64) - b) / np.linalg.norm(b))
-    res = {"ok": True}
-    per = {}
-    K, W = args.steps, args.warmup
+def prepare_varlen_legs(lib, kda, make_config, upload, dev, torch):
+    """Inputs, outputs and workspaces of the other two 8,192-token workloads (uniform and
+    skewed varlen batches), made and uploaded before any timing, so that the GPU runs the
+    timed legs back to back instead of idling while the host draws the next inputs."""
+    legs = []
     for idx in (2, 3):
         y = make_config(idx)
         B, T, H, dk, dv = y.shape
@@ -190,6 +189,14 @@ def extra_measurements(args, lib, kda, make_config, upload, dev, torch, argv1, o
         argv = [ctypes.byref(prob), P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["h0"]),
                 P(d["cu"]), ctypes.c_float(y.scale), P(o), P(h), P(ws), ctypes.c_size_t(wsb),
                 ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)]
+        legs.append({"y": y, "d": d, "o": o, "h": h, "ws": ws, "prob": prob, "argv": argv})
+    return legs
+
+
+def time_varlen_legs(legs, lib, W, K, torch):
+    """Each varlen leg as the headline one: W untimed calls, then K timed calls."""
+    for leg in legs:
+        argv = leg["argv"]
         for _ in range(W):
             if lib.kda_fwd(*argv):
                 raise RuntimeError("kda_fwd failed")
@@ -200,17 +207,30 @@ def extra_measurements(args, lib, kda, make_config, upload, dev, torch, argv1, o
             lib.kda_fwd(*argv)
         e1.record()
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / K
+        leg["ms"] = e0.elapsed_time(e1) / K
+
+
+def extra_measurements(args, lib, kda, legs, upload, dev, torch, argv1, out1, ht1, x1):
+    """The varlen legs' parity against the oracle (their outputs are those of the last timed
+    call), their geomean with the headline workload, and the headline workload with cold
+    caches (a 512 MiB buffer written before every call, outside the timed call)."""
+    from oracle import oracle_fwd
+    rel = lambda a, b: float(np.linalg.norm(a.astype(np.float64) - b) / np.linalg.norm(b))
+    res = {"ok": True}
+    per = {}
+    for leg in legs:
+        y, o, h, ms = leg["y"], leg["o"], leg["h"], leg["ms"]
+        B, T = y.shape[0], y.shape[1]
         ro, rh = oracle_fwd(y.q, y.k, y.v, y.g, y.beta, y.h0, y.cu_seqlens, y.scale)
         eo, eh = rel(o.float().cpu().numpy(), ro), rel(h.cpu().numpy(), rh)
         good = eo <= TOL and eh <= TOL
         res["ok"] = res["ok"] and good
         per[y.name] = {"tokens_per_s": round(B * T / (ms * 1e-3), 1) if good else None,
-                       "ms_per_step": round(ms, 5), "sequences": int(N),
+                       "ms_per_step": round(ms, 5), "sequences": int(y.num_seqs),
                        "out_rel_rmse": eo, "state_rel_rmse": eh}
         log("workload %s: %.4f ms/step, parity out %.2e state %.2e" % (y.name, ms, eo, eh))
-        del d, o, h, ws
     res["workloads"] = per
+    legs.clear()  # their buffers are no longer needed
 
     # headline workload with cold caches
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -538,6 +558,13 @@ def main():
     lib.kda_fwd_timed.argtypes = list(lib.kda_fwd.argtypes) + [ctypes.c_void_p]
     lib.kda_fwd_timed.restype = ctypes.c_int
 
+    # the other workloads' inputs, ready before any timing (their legs run right after this one)
+    legs = []
+    if not args.no_extra and not args.no_verify:
+        t0 = time.time()
+        legs = prepare_varlen_legs(lib, kda, make_config, upload, dev, torch)
+        log("varlen workloads generated and uploaded in %.1fs" % (time.time() - t0))
+
     hip = hip_runtime()
     K, W = args.steps, args.warmup
     marks = []
@@ -575,6 +602,10 @@ def main():
         if rc:
             raise kda.KDAError(rc)
     torch.cuda.synchronize()
+    # the varlen legs right after this one, with no host work in between (their parity is
+    # checked afterwards, from the outputs of their last timed call)
+    if legs:
+        time_varlen_legs(legs, lib, W, K, torch)
 
     def elapsed(a, b):
         f = ctypes.c_float()
@@ -651,7 +682,7 @@ def main():
 
     extra = {}
     if not args.no_extra and not args.no_verify:
-        extra = extra_measurements(args, lib, kda, make_config, upload, dev, torch, argv, out, ht, x)
+        extra = extra_measurements(args, lib, kda, legs, upload, dev, torch, argv, out, ht, x)
         ok = ok and extra.pop("ok")
 
     nch = n_chunks_of(x)
