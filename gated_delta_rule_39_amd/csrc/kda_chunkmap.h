@@ -31,6 +31,13 @@ namespace kda {
 
 constexpr int kMapThreads = 1024;
 constexpr int kMapBuckets = 128;
+// Batches of at most kMapLdsSeqs sequences keep their offsets, starts and lengths in LDS, and
+// at most kMapLdsChunks chunks their lengths and the list of short chunks: the later steps
+// then read what the earlier ones computed from LDS instead of through L2 (a binary search
+// over the offsets is otherwise a chain of dependent global loads).  Larger batches use the
+// global arrays.
+constexpr int kMapLdsSeqs = 2048;
+constexpr int kMapLdsChunks = 4096;
 
 // Inclusive prefix sum over the workgroup's 1024 threads in thread order: a scan inside each
 // wave, then the waves' totals through LDS (`wsum`, 16 words).  `total` gets the sum of all.
@@ -75,9 +82,17 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* _
                                                                 int32_t* __restrict__ small_list) {
   __shared__ int32_t hist[kMapBuckets];
   __shared__ int32_t wsum[kMapThreads / 64];
+  __shared__ int32_t s_off[kMapLdsSeqs], s_start[kMapLdsSeqs], s_len[kMapLdsSeqs];
+  __shared__ uint8_t s_clen[kMapLdsChunks];
+  __shared__ int32_t s_small[kMapLdsChunks];
   const int tid = threadIdx.x;
   if (tid < kMapBuckets) hist[tid] = 0;
   __syncthreads();
+  // packed offsets and lengths fit 31 bits (the host bounds the total tokens)
+  const bool lds_seq = cu != nullptr && N <= kMapLdsSeqs;
+  auto off_of = [&](int64_t m) { return lds_seq ? (int64_t)s_off[m] : (int64_t)seq_off[m]; };
+  auto start_of = [&](int64_t m) { return lds_seq ? (int64_t)s_start[m] : seq_start(cu, T, m); };
+  auto len_of = [&](int64_t m) { return lds_seq ? (int64_t)s_len[m] : seq_len(cu, T, m); };
 
   // 1. chunk counts, exclusive prefix -> seq_off; bucket histogram
   int32_t carry = 0;  // chunks of the sequences before this batch (the same in every thread)
@@ -89,10 +104,17 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* _
       int64_t c = (L + kChunk - 1) / kChunk;
       cnt = (int32_t)(c < n_chunk_ub ? c : n_chunk_ub);
       atomicAdd(&hist[order_bucket(cnt)], 1);
+      if (lds_seq) {
+        s_start[n] = (int32_t)seq_start(cu, T, n);
+        s_len[n] = (int32_t)L;
+      }
     }
     int32_t batch;
     const int32_t incl = block_incl_scan(cnt, wsum, batch);
-    if (n < N) seq_off[n] = carry + incl - cnt;
+    if (n < N) {
+      seq_off[n] = carry + incl - cnt;
+      if (lds_seq) s_off[n] = carry + incl - cnt;
+    }
     carry += batch;
   }
   int32_t total = carry;
@@ -106,15 +128,16 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* _
   __syncthreads();
 
   // 2. table: chunk c belongs to the last sequence n with seq_off[n] <= c
+  const bool lds_chunks = total <= kMapLdsChunks;
   for (int64_t c = tid; c < total; c += kMapThreads) {
     int64_t lo = 0, hi = N - 1;
     while (lo < hi) {
       int64_t mid = (lo + hi + 1) >> 1;
-      if (seq_off[mid] <= c) lo = mid; else hi = mid - 1;
+      if (off_of(mid) <= c) lo = mid; else hi = mid - 1;
     }
     int64_t n = lo;
-    int32_t idx = (int32_t)(c - seq_off[n]);
-    int64_t L = seq_len(cu, T, n);
+    int32_t idx = (int32_t)(c - off_of(n));
+    int64_t L = len_of(n);
     int64_t rem = L - (int64_t)idx * kChunk;
     ChunkEntry e;
     e.seq = (int32_t)n;
@@ -122,6 +145,7 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* _
     e.idx = idx;
     e.pad = 0;
     table[c] = e;
+    if (lds_chunks) s_clen[c] = (uint8_t)e.len;
   }
 
   // 3. longest-first order of sequences (order buckets, descending): each bucket's first
@@ -147,12 +171,12 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* _
   for (int64_t base = 0; base < N; base += kMapThreads) {
     int64_t n = base + tid;
     if (n < N) {
-      int64_t L = seq_len(cu, T, n);
+      int64_t L = len_of(n);
       int64_t c = (L + kChunk - 1) / kChunk;
       int32_t cnt = (int32_t)(c < n_chunk_ub ? c : n_chunk_ub);
       int32_t pos = atomicAdd(&hist[order_bucket(cnt)], 1);
       seq_order[pos] = (int32_t)n;
-      if (rank_desc) rank_desc[pos] = make_int4((int)n, seq_off[n], (int)seq_start(cu, T, n), (int)L);
+      if (rank_desc) rank_desc[pos] = make_int4((int)n, (int)off_of(n), (int)start_of(n), (int)L);
     }
   }
 
@@ -161,14 +185,17 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* _
   //    short chunks of even rank) numbered in chunk order.
   if (!passes) return;
   __syncthreads();
-  auto is_short = [&](int64_t c) { return c < total && table[c].len <= 32; };
+  auto is_short = [&](int64_t c) { return c < total && (lds_chunks ? s_clen[c] : table[c].len) <= 32; };
   int32_t n_short = 0;
   for (int64_t base = 0; base < total; base += kMapThreads) {
     const int64_t c = base + tid;
     const int32_t f = is_short(c) ? 1 : 0;
     int32_t batch;
     const int32_t incl = block_incl_scan(f, wsum, batch);
-    if (f) small_list[n_short + incl - 1] = (int32_t)c;
+    if (f) {
+      if (lds_chunks) s_small[n_short + incl - 1] = (int32_t)c;
+      else small_list[n_short + incl - 1] = (int32_t)c;
+    }
     n_short += batch;
   }
   __syncthreads();  // small_list complete
@@ -181,7 +208,8 @@ __global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t* _
     const bool head = c < total && (!sh || (rank & 1) == 0);
     const int32_t hpos = block_incl_scan(head ? 1 : 0, wsum, heads);
     if (head) {
-      const int32_t partner = (sh && rank + 1 < n_short) ? small_list[rank + 1] : -1;
+      const int32_t partner =
+          (sh && rank + 1 < n_short) ? (lds_chunks ? s_small[rank + 1] : small_list[rank + 1]) : -1;
       passes[n_pass + hpos - 1] = make_int2((int32_t)c, partner);
     }
     n_short_seen += shorts;
