@@ -401,8 +401,11 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
   uint8_t* rec2 = paired ? a.rec + ((size_t)chunk2 * a.H + h) * R::BYTES : rec;
   uint8_t* recw = hi_half ? rec2 : rec;            // this wave's record
   const int wr = hi_half ? w - 2 : w;              // this wave's row block there
-  // valid tokens of this wave's chunk: the parts of its record past them are not stored
-  const int rows_w = chunk_rows(a, hi_half ? chunk2 : chunk);
+  // valid tokens of this wave's chunk: the parts of its record past them are not stored.  The
+  // fused kernel (fixed-length rows: at most one partial chunk per row) stores every part: its
+  // walk bounds the launch, and the length lookup per item cost it more (about 1.5 %) than the
+  // few empty parts it would drop (the scan may skip loading a part that was stored: it is zero)
+  const int rows_w = WT ? kChunk : chunk_rows(a, hi_half ? chunk2 : chunk);
 
   // reads the lane's NE channels (of this half) of row `row` of a [*][DK] fp32 array in LDS
   auto lane_row = [&](const float* base, int row, float* out) {
