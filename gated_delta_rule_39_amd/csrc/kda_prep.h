@@ -320,14 +320,17 @@ __device__ __forceinline__ void subst_rows(float (&x)[4], const float (&am)[16])
 template <bool WT, int BYTES, typename V>
 __device__ __forceinline__ void rec_store(uint8_t* rec, size_t off, const V& v, bool present = true) {
   constexpr int aux = WT ? 16 : 0;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(rec, 0, present ? BYTES : 0, kBufferFlags);
+  // one resource per record; a missing part's offset lies past the record's range, so the
+  // store is dropped
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(rec, 0, BYTES, kBufferFlags);
+  const int o = (int)off + (present ? 0 : (1 << 30));
   if constexpr (sizeof(V) == 16) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4_v, v), rs, (int)off, 0, aux);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4_v, v), rs, o, 0, aux);
   } else if constexpr (sizeof(V) == 8) {
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2_v, v), rs, (int)off, 0, aux);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2_v, v), rs, o, 0, aux);
   } else {
     static_assert(sizeof(V) == 4, "record stores are 4, 8 or 16 bytes");
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, (int)off, 0, aux);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, o, 0, aux);
   }
 }
 
