@@ -108,9 +108,10 @@ struct KeyRegs {
 
 // The loads of a chunk's factors are issued in groups spread over the previous chunk's
 // step, so that the eight waves never queue all of them on the vector-memory path at
-// once.  Token waves: 0 = W, 1 = Qhat*exp(G), 2 = Aqk, U and ue, 3 = U and ue (with the
-// header's max |v| in the fused kernel), 4 = Aqk.  A walk requests the next chunk's W and U
-// first (the next Delta needs both), Qhat*exp(G) after its Delta, Aqk after barrier A.  Key
+// once.  Token waves: 0 = W, 1 = Qhat*exp(G), 2 = Aqk, U and ue (or 3 = U and ue, 4 = Aqk,
+// for a walk that reuses its slot and so requests each factor after its last use).  Requesting
+// U together with W instead (the next Delta needs both) was slower: the walk's loads then
+// bunch at the start of the step.  Key
 // waves: 0 = K~^T, 1 = exp(G_last).  `rows`: the chunk's valid tokens (0 past a walk's
 // end); the parts of the record past them are not fetched and read as zeros.
 template <int PART, int DK, int DV, int NV, bool FUSED = false>
@@ -365,10 +366,7 @@ __device__ __forceinline__ void scan_walk(const ScanArgs& a, const FuseArgs& fz,
         await_chunk(c + kScanDepth - 1);
         prepoll(c + kScanDepth);
       }
-      // the next chunk's factors in the order this step's products use them: W and U (Delta)
-      // first, then Qhat exp(G) (output), then Aqk (after barrier A)
       load_tok<0, DK, DV, NV, FUSED>(nxt, nrec, nrows, i, l, slice);
-      load_tok<3, DK, DV, NV, FUSED>(nxt, nrec, nrows, i, l, slice);
       const f16x8* sb = reinterpret_cast<const f16x8*>(sbb + (size_t)((c - c0) & 1) * SM::SBUF);
       // all S0 fragments at once, so that the MFMA chains below never wait on LDS one by one
       f16x8 sf[KSK][NT];
@@ -401,7 +399,7 @@ __device__ __forceinline__ void scan_walk(const ScanArgs& a, const FuseArgs& fz,
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) o[nt] = mfma16(sf[s][nt], cur.qf[s], o[nt]);
       __syncthreads();  // A: Delta complete
-      load_tok<4, DK, DV, NV, FUSED>(nxt, nrec, nrows, i, l, slice);
+      load_tok<2, DK, DV, NV, FUSED>(nxt, nrec, nrows, i, l, slice);
       // o^T, intra-chunk part: Delta^T Aqk^T; then 4 consecutive value columns per lane
       f16x8 dfr[2][NT];
 #pragma unroll
@@ -438,9 +436,8 @@ __device__ __forceinline__ void scan_walk(const ScanArgs& a, const FuseArgs& fz,
       for (int j = 0; j < kScanDepth - 1; ++j) {
         await_chunk(c0 + j);
         load_tok<0, DK, DV, NV, FUSED>(buf[j], rec_of(c0 + j), rows_of(c0 + j), i, l, slice);
-        load_tok<3, DK, DV, NV, FUSED>(buf[j], rec_of(c0 + j), rows_of(c0 + j), i, l, slice);
         load_tok<1, DK, DV, NV, FUSED>(buf[j], rec_of(c0 + j), rows_of(c0 + j), i, l, slice);
-        load_tok<4, DK, DV, NV, FUSED>(buf[j], rec_of(c0 + j), rows_of(c0 + j), i, l, slice);
+        load_tok<2, DK, DV, NV, FUSED>(buf[j], rec_of(c0 + j), rows_of(c0 + j), i, l, slice);
       }
       if (FUSED) __syncthreads();  // S0 of the first chunk visible
       // whole groups of kScanDepth steps (no conditional step: the compiler's memory-counter
