@@ -182,6 +182,15 @@ int fused_producers(const kda_problem_t* p, int64_t N, bool packed) {
   return (int)(walk < cap ? walk : cap);
 }
 
+// Fused: chunk-walk rounds that every workgroup of the launch takes (the scan workgroups one
+// item per round before their chains start), KDA_FUSE_ROUNDS=n overrides (0: none).
+int fuse_rounds() {
+  const char* env = std::getenv("KDA_FUSE_ROUNDS");
+  if (!env) return 1;
+  const int v = std::atoi(env);
+  return v < 0 ? 0 : (v > 64 ? 64 : v);
+}
+
 // Flag value of a fused call: a process-wide counter from a time-derived start, so that
 // flags left by earlier calls (or uninitialised workspace) do not match.
 uint64_t next_epoch() {
@@ -330,6 +339,7 @@ static kda_status_t forward(const kda_problem_t* prob, const void* q, const void
   p.fuse_producers = fused_producers(prob, N, packed);
   p.epoch = p.fuse_producers > 0 ? next_epoch() : 0;
   p.spin_limit = spin_limit_override();
+  p.fuse_rounds = p.fuse_producers > 0 ? fuse_rounds() : 0;
   p.captured = false;
   if (p.fuse_producers > 0) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;

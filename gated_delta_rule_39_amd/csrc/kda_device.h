@@ -220,6 +220,7 @@ struct FuseArgs {
   uint64_t* ctl;              // [0] flag value of the most recent launch, [1] value of a failed one
   int32_t producers;          // workgroups 0 .. producers-1 run the chunk walk, the rest the scan
   int32_t spin_limit;         // polls (about 130 cycles each) before a wait gives up
+  int32_t scan_rounds;        // chunk-walk rounds every workgroup takes (scan ones before their chains)
 };
 
 // The flag value of this launch (the same in every workgroup: the counter is written by

@@ -19,11 +19,14 @@ __global__ __launch_bounds__(kPrepThreads, 1) void fused_fwd_kernel(PrepArgs pa,
   extern __shared__ __align__(16) uint8_t smem[];
   FuseArgs f = fz;
   f.epoch = launch_epoch(fz);
-  if ((int)blockIdx.x < f.producers)
-    chunk_walk<DK, DV, InT, true>(pa, f, (int)blockIdx.x, f.producers, smem);
-  else
+  const bool producer = (int)blockIdx.x < f.producers;
+  if (producer || f.scan_rounds > 0)
+    chunk_walk<DK, DV, InT, true>(pa, f, (int)blockIdx.x, f.producers, smem, (int)gridDim.x, f.scan_rounds);
+  if (!producer) {
+    __syncthreads();  // the chunk items' LDS is free
     scan_chain<DK, DV, 64, InT, true>(sa, f, (int64_t)blockIdx.x - f.producers,
                                       (int64_t)gridDim.x - f.producers, smem);
+  }
 }
 
 }  // namespace kda

@@ -171,6 +171,7 @@ static hipError_t launch_fused(const ForwardPlan& p, hipStream_t stream) {
   fz.ctl = p.ctl;
   fz.dev_epoch = nullptr;
   fz.producers = p.fuse_producers;
+  fz.scan_rounds = p.fuse_rounds;
   if (p.spin_limit > 0) {
     fz.spin_limit = p.spin_limit;
   } else {

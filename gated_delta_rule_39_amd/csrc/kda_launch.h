@@ -38,6 +38,7 @@ struct ForwardPlan {
   bool captured;          // the stream is capturing a graph: flag values come from the device counter
   int32_t spin_limit;     // polls before a fused-kernel wait gives up
   int32_t fuse_producers;  // > 0: one fused kernel, this many workgroups run the chunk walk
+  int32_t fuse_rounds;     // fused: chunk-walk rounds shared by every workgroup (scan ones included)
   int32_t slice;  // value columns per scan workgroup (16, 32 or 64)
   int32_t task_scan;    // packed: > 0 runs the persistent state scan on this many workgroups
   int32_t long_chunks;  // packed: sequences of at least this many chunks form the long class (power of two; 0: none)

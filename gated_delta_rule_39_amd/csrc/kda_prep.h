@@ -1070,15 +1070,35 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
 // goes in the order the scan consumes, every row's first chunk first, and each record is
 // published (device-scope release, then its flag) as soon as it is final: right after
 // its item, or after the exact pass for a flagged item.
+//
+// Schedule: workgroup wg takes items wg + j n_wg.  With `rounds` > 0 (the fused kernel) the
+// first `rounds` rounds go over all n_all workgroups of the launch, the scan workgroups
+// (wg >= n_wg) included, which walk only those rounds before their chains start (their
+// chains would wait that long for the first records anyway); the later rounds go over the
+// n_wg chunk workgroups.  4,096 items on 192 + 64 workgroups: one item each in the first
+// round, then 20 more for each chunk workgroup (instead of 21 or 22).
 template <int DK, int DV, typename InT, bool FUSED>
 __device__ __forceinline__ void chunk_walk(const PrepArgs& a, const FuseArgs& fz, const int wg, const int n_wg,
-                                           uint8_t* smem) {
+                                           uint8_t* smem, const int n_all = 0, const int rounds = 0) {
   // items (fewer than 2^31), kept in scalar registers; packed batches walk the passes
   // (a pass: one chunk, or two chunks of at most 32 tokens)
   const int n_rows = (int)(a.T_total / (a.T > 0 ? a.T : 1));
   const int n_items = (a.cu ? (int)sload_u32(a.info + 3) : (int)(a.nc * n_rows)) * a.H;
-  int it = wg;
-  if (it >= n_items) return;  // uniform for the workgroup
+  const int R = n_all > n_wg ? n_all : n_wg;
+  auto item_of = [&](int j) { return j < rounds ? j * R + wg : rounds * R + wg + (j - rounds) * n_wg; };
+  // this workgroup's items: item_of(0) .. item_of(n_own - 1)
+  int n_own;
+  {
+    const int k1 = n_items > wg ? (n_items - wg + R - 1) / R : 0;  // shared rounds with an item
+    if (wg >= n_wg || k1 < rounds) {
+      n_own = k1 < rounds ? k1 : rounds;
+    } else {
+      const int rem = n_items - (rounds * R + wg);
+      n_own = rounds + (rem > 0 ? (rem + n_wg - 1) / n_wg : 0);
+    }
+  }
+  int it = wg;  // item_of(0)
+  if (n_own <= 0) return;  // uniform for the workgroup
   auto entry = [&](int c) { return a.cu ? ld_entry(a.table + c) : entry_fixed(a, c); };
   // chunks from the last to the first: the records the scan reads first are written last
   // and are still in the caches (L2, MALL) when it starts.  Fused: position p holds chunk
@@ -1115,10 +1135,10 @@ __device__ __forceinline__ void chunk_walk(const PrepArgs& a, const FuseArgs& fz
   int4* meta = reinterpret_cast<int4*>(smem + PrepSmem<DK, DV>::META);
   auto start_of = [&](const ChunkEntry& e) { return seq_start(a.cu, a.T, e.seq) + (int64_t)e.idx * kChunk; };
   if (threadIdx.x < 64) {
-    const int64_t item = (int64_t)wg + (int64_t)threadIdx.x * n_wg;
     int4 m = make_int4(0, 0, 0, -1);
-    if (item < n_items) {
-      int2 pc = make_int2(chunk_of((int)item), -1);
+    if ((int)threadIdx.x < n_own) {
+      const int item = item_of((int)threadIdx.x);
+      int2 pc = make_int2(chunk_of(item), -1);
       if (a.cu) pc = a.passes[pc.x];
       const ChunkEntry e = a.cu ? a.table[pc.x] : entry_fixed(a, pc.x);
       const int64_t st = start_of(e);
@@ -1160,8 +1180,8 @@ __device__ __forceinline__ void chunk_walk(const PrepArgs& a, const FuseArgs& fz
     }
     unpack_raw(in, raw);
     for (int j = 0;; ++j) {
-      const int nx = __builtin_amdgcn_readfirstlane(it + n_wg);
-      const bool more = nx < n_items;
+      const bool more = j + 1 < n_own;
+      const int nx = __builtin_amdgcn_readfirstlane(more ? item_of(j + 1) : it);
       const RawAt at = at_of(more ? j + 1 : j, more ? nx : it);
       load_part<0>(raw, a, at);
       const int2 pc = pass_of(it);
@@ -1188,12 +1208,11 @@ __device__ __forceinline__ void chunk_walk(const PrepArgs& a, const FuseArgs& fz
 
   // exact pass over this workgroup's flagged items, 64 items per batch of flag loads; each
   // flagged chunk of a pass is redone on its own
-  const int n_own = (n_items - wg + n_wg - 1) / n_wg;
   const int lane = threadIdx.x & 63;
   for (int kb = 0; kb < n_own; kb += 64) {
     int f = 0;
     if (kb + lane < n_own) {
-      const int x = wg + (kb + lane) * n_wg;
+      const int x = item_of(kb + lane);
       const int2 pc = a.cu ? a.passes[chunk_of(x)] : make_int2(chunk_of(x), -1);
       f = a.defer[(size_t)pc.x * a.H + head_of(x)] != 0;  // both chunks of a pass share the flag
     }
@@ -1201,7 +1220,7 @@ __device__ __forceinline__ void chunk_walk(const PrepArgs& a, const FuseArgs& fz
     while (bits) {
       const int b = __builtin_ctzll(bits);
       bits &= bits - 1;
-      const int x = __builtin_amdgcn_readfirstlane(wg + (kb + b) * n_wg);
+      const int x = __builtin_amdgcn_readfirstlane(item_of(kb + b));
       const int2 pc = pass_of(x);
       for (int k = 0; k < (pc.y >= 0 ? 2 : 1); ++k) {
         const int c = k ? pc.y : pc.x;

@@ -154,6 +154,9 @@ kda_status_t kda_fwd_validate(const kda_problem_t* prob, const void* q, const vo
  *                            unit a workgroup)
  *   KDA_CHUNK_WGS=n          at most n workgroups compute chunk factors (default: one
  *                            per compute unit, minus the chain workgroups when fused)
+ *   KDA_FUSE_ROUNDS=n        fused kernel: rounds of chunk items that the chain
+ *                            workgroups take too, before their chains start (default 1;
+ *                            0..64; the results are the same bits for every n)
  *   KDA_SPIN_LIMIT=n         polls before a wait of the fused kernel gives up (default:
  *                            several times the whole chunk walk); a small n forces the
  *                            failure path that kda_fwd_status reports

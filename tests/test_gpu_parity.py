@@ -226,6 +226,28 @@ def test_fused_deferred_items_on_long_walks(monkeypatch):
     _check(x, "fused, deep gates, 3 chunk workgroups")
 
 
+@pytest.mark.parametrize("gate_kind", ["base", "deep"])
+def test_fused_scan_workgroups_take_chunk_items(gate_kind, monkeypatch):
+    """The fused kernel's scan workgroups walk the first KDA_FUSE_ROUNDS rounds of chunk items
+    (redoing their own deferred ones: deep gates) before their chains start.  Three chunk
+    workgroups and eight chains: with five rounds the scan workgroups produce most records.
+    Which workgroup computes an item must not change a bit of the result."""
+    monkeypatch.setenv("KDA_CHUNK_WGS", "3")
+    x = make_inputs(1, 1000, 4, 128, 128, seed=44, dtype="bf16", gate=gate_kind)
+    d = to_device(x)
+    ref = None
+    for rounds in ("0", "1", "2", "5"):
+        monkeypatch.setenv("KDA_FUSE_ROUNDS", rounds)
+        o, h = run_gpu(x, d)
+        if ref is None:
+            ro, rh = run_oracle(x)
+            gate(x, o, h, ro, rh, "fused, %s gates, no shared rounds" % gate_kind)
+            ref = (o, h)
+        else:
+            np.testing.assert_array_equal(o, ref[0])
+            np.testing.assert_array_equal(h, ref[1])
+
+
 def test_fused_forward_in_a_captured_graph():
     # kda_fwd captured once and replayed with new inputs copied into the captured buffers:
     # every replay must match an eager call on the same inputs (a captured fused call derives
