@@ -912,8 +912,9 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, const int chunk, co
       }
       // a pair's second chunk: its columns are the pass's second half (s2 = 1), its record's first
       const int s2r = hi_half ? s2 ^ 1 : s2;
+      // (row blocks 0 and 1 are zero in the second column half: not stored, never read)
       rec_store<WT, R::BYTES>(recw, R::A + ((size_t)(wr * 2 + s2r) * 64 + l) * 16, f,
-                              rec_rows_present(rows_w, wr) && rec_half_present(rows_w, s2r));
+                              rec_rows_present(rows_w, wr) && rec_half_present(rows_w, s2r) && (s2r == 0 || wr >= 2));
     }
   }
   // Bw^T fragments through identity products (rows = key channels, tokens in pi order)

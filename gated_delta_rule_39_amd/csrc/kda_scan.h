@@ -129,9 +129,11 @@ __device__ __forceinline__ void load_tok(TokRegs<DK, NV>& c, const uint8_t* rec,
       c.qf[s] = rec_load<f16x8, FUSED>(rec, nb, R::Q + ((size_t)(i * TR::KSK + s) * 64 + l) * 16);
   } else {
     if (PART == 2 || PART == 4) {
+      // Aqk is lower triangular: token blocks 0 and 1 have nothing in the second 32-token
+      // half of the columns (never stored), which reads as zeros
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
-        c.af[s2] = rec_load<f16x8, FUSED>(rec, rec_half_present(rows, s2) ? nb : 0,
+        c.af[s2] = rec_load<f16x8, FUSED>(rec, rec_half_present(rows, s2) && (s2 == 0 || i >= 2) ? nb : 0,
                                           R::A + ((size_t)(i * 2 + s2) * 64 + l) * 16);
     }
     if (PART == 2 || PART == 3) {
