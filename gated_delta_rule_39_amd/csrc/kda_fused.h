@@ -10,9 +10,11 @@
 namespace kda {
 
 // Fused forward: workgroups 0 .. producers-1 walk the chunks (in the order the scan
-// consumes them) and publish each record; the others each walk one (row, head, 64-column
-// slice) chain, waiting for each record before loading it.  The chunk workgroups never
-// wait on anything, and they have the lower block ids, so they are dispatched first.
+// consumes them) and publish each record; the others first take the first `scan_rounds`
+// rounds of items with them (publishing those records too, their deferred ones included),
+// then each walk one (row, head, 64-column slice) chain, waiting for each record before
+// loading it.  Every record is published by a workgroup before it waits on anything; the
+// chunk workgroups never wait and have the lower block ids, so they are dispatched first.
 template <int DK, int DV, typename InT>
 __global__ __launch_bounds__(kPrepThreads, 1) void fused_fwd_kernel(PrepArgs pa, ScanArgs sa, FuseArgs fz) {
   static_assert(kPrepThreads == kScanThreads, "one block size for both roles");
